@@ -1,0 +1,280 @@
+"""fp64 CPU oracle for the causal video-VAE hot path.
+
+TEST INFRASTRUCTURE ONLY.  Only the test suite, ``__graft_entry__.smoke()`` and
+the CPU-baseline leg of ``bench.py`` may import this package.  The product path
+(``video_vae_causal_amd``) never imports, links or runs anything here, and this
+package imports nothing from it: the two share no code.
+
+Tensors are numpy float64 arrays in the pages' logical layout NCTHW
+("Cosmos3 Wan VAE -- engine size vs runtime context memory", section 10.1).
+The arithmetic lives in ``oracle.c`` (plain C, fp64); this module only marshals
+arrays and composes the documented operations in the pages' order.
+
+Pins (what each function is checked against) are listed in the test files
+``tests/test_oracle_*.py``.  Nothing in this module is "parity unpinned".
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Optional, Sequence
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+# The divisor clamp of the channel RMS norm.  The page names an L2 normalise
+# with a max-clamp but prints no epsilon; 1e-12 is the documented default of
+# the normalise call the page names.
+DEFAULT_EPS = 1e-12
+# Past frames a 3x3x3 causal conv with temporal dilation 1 keeps (the page's
+# CACHE_T = 2, "Cosmos3 Wan VAE ...", section 8.5).
+CACHE_T = 2
+
+
+def build() -> str:
+    """Compile oracle.c into liboracle.so with gcc (fp64, OpenMP)."""
+    tmp = _LIB_PATH + ".tmp"
+    subprocess.check_call(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11",
+                           _SRC, "-o", tmp, "-lm"])
+    os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+        build()
+    lib = ctypes.CDLL(_LIB_PATH)
+    dp = ctypes.POINTER(ctypes.c_double)
+    i = ctypes.c_int
+    lib.oracle_causal_conv3d.restype = ctypes.c_int
+    lib.oracle_causal_conv3d.argtypes = [dp, i, i, i, i, i, dp, i, dp, i, i, i, i, dp,
+                                         i, i, i, i, i, i, i, dp]
+    lib.oracle_causal_conv3d_points.restype = ctypes.c_int
+    lib.oracle_causal_conv3d_points.argtypes = [dp, i, i, i, i, i, dp, i, dp, i, i, i, i, dp,
+                                                i, i, i, i, i, i, i,
+                                                ctypes.POINTER(ctypes.c_int64), ctypes.c_long, dp]
+    lib.oracle_rms_norm.restype = ctypes.c_int
+    lib.oracle_rms_norm.argtypes = [dp, i, i, i, i, i, dp, dp, ctypes.c_double, dp]
+    lib.oracle_silu.restype = None
+    lib.oracle_silu.argtypes = [dp, ctypes.c_long, dp]
+    lib.oracle_upsample_nearest2x.restype = None
+    lib.oracle_upsample_nearest2x.argtypes = [dp, i, i, i, i, i, dp]
+    lib.oracle_round_bf16.restype = None
+    lib.oracle_round_bf16.argtypes = [dp, ctypes.c_long, dp]
+    lib.oracle_conv_out_size.restype = ctypes.c_int
+    lib.oracle_conv_out_size.argtypes = [i, i, i, i, i]
+    _lib = lib
+    return lib
+
+
+def _f64(a) -> np.ndarray:
+    return np.ascontiguousarray(np.asarray(a, dtype=np.float64))
+
+
+def _ptr(a: Optional[np.ndarray]):
+    if a is None:
+        return None
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+
+
+def conv_out_size(n: int, k: int, stride: int, pad: int, dil: int) -> int:
+    return int(_load().oracle_conv_out_size(n, k, stride, pad, dil))
+
+
+def _conv_args(x, w, bias, cache, stride, pad, dil):
+    x = _f64(x)
+    w = _f64(w)
+    if x.ndim != 5 or w.ndim != 5:
+        raise ValueError("x must be [N,C,T,H,W] and w [Cout,Cin,kT,kH,kW]")
+    N, C, T, H, W = x.shape
+    Cout, Cin, kT, kH, kW = w.shape
+    if Cin != C:
+        raise ValueError("channel mismatch")
+    sh, sw = stride
+    ph, pw = pad
+    dt, dh, dw = dil
+    past = dt * (kT - 1)
+    b = None if bias is None else _f64(bias).reshape(Cout)
+    c = None
+    if cache is not None:
+        c = _f64(cache)
+        if c.shape != (N, C, past, H, W):
+            raise ValueError(f"cache must be {(N, C, past, H, W)}, got {c.shape}")
+    return x, w, b, c, (N, C, T, H, W), (Cout, kT, kH, kW), (sh, sw, ph, pw, dt, dh, dw), past
+
+
+def causal_conv3d(x, w, bias=None, cache=None, stride=(1, 1), pad=(1, 1),
+                  dil=(1, 1, 1)) -> np.ndarray:
+    """Causal Conv3D (temporal stride 1), fp64, whole chunk at once.
+
+    "Cosmos3 Wan VAE ...", section 10.3: standard Conv3D sum with the temporal
+    padding moved entirely to the past (dil_t*(kT-1) frames, zeros or the
+    cache), symmetric spatial zero padding, bias added once after the sum.
+    ``cache`` is [N, C_in, dil_t*(kT-1), H, W] (the past frames, oldest first)
+    or None for zero causal padding.
+    """
+    x, w, b, c, (N, C, T, H, W), (Cout, kT, kH, kW), (sh, sw, ph, pw, dt, dh, dw), past = \
+        _conv_args(x, w, bias, cache, stride, pad, dil)
+    Ho = conv_out_size(H, kH, sh, ph, dh)
+    Wo = conv_out_size(W, kW, sw, pw, dw)
+    y = np.empty((N, Cout, T, Ho, Wo), dtype=np.float64)
+    if N * T == 0:
+        return y
+    rc = _load().oracle_causal_conv3d(_ptr(x), N, C, T, H, W, _ptr(c), past if c is not None else 0,
+                                      _ptr(w), Cout, kT, kH, kW, _ptr(b),
+                                      sh, sw, ph, pw, dt, dh, dw, _ptr(y))
+    if rc != 0:
+        raise ValueError("oracle_causal_conv3d rejected its arguments")
+    return y
+
+
+def causal_conv3d_points(x, w, flat_idx, bias=None, cache=None, stride=(1, 1), pad=(1, 1),
+                         dil=(1, 1, 1)) -> np.ndarray:
+    """Same definition as :func:`causal_conv3d`, evaluated only at the given
+    flat indices of the NCTHW output."""
+    x, w, b, c, (N, C, T, H, W), (Cout, kT, kH, kW), (sh, sw, ph, pw, dt, dh, dw), past = \
+        _conv_args(x, w, bias, cache, stride, pad, dil)
+    idx = np.ascontiguousarray(np.asarray(flat_idx, dtype=np.int64).ravel())
+    out = np.empty(idx.shape[0], dtype=np.float64)
+    rc = _load().oracle_causal_conv3d_points(
+        _ptr(x), N, C, T, H, W, _ptr(c), past if c is not None else 0,
+        _ptr(w), Cout, kT, kH, kW, _ptr(b), sh, sw, ph, pw, dt, dh, dw,
+        idx.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), idx.shape[0], _ptr(out))
+    if rc != 0:
+        raise ValueError("oracle_causal_conv3d_points rejected its arguments")
+    return out
+
+
+def rms_norm(x, gamma, beta=None, eps: float = DEFAULT_EPS) -> np.ndarray:
+    """Channel L2/RMS norm, "Cosmos3 Wan VAE ...", section 10.2:
+    v / max(||v||_2, eps) * sqrt(C) * gamma + beta over dim C of NCTHW."""
+    x = _f64(x)
+    N, C, T, H, W = x.shape
+    g = _f64(gamma).reshape(C)
+    b = None if beta is None else _f64(beta).reshape(C)
+    y = np.empty_like(x)
+    if x.size == 0:
+        return y
+    rc = _load().oracle_rms_norm(_ptr(x), N, C, T, H, W, _ptr(g), _ptr(b), float(eps), _ptr(y))
+    if rc != 0:
+        raise ValueError("oracle_rms_norm rejected its arguments")
+    return y
+
+
+def silu(x) -> np.ndarray:
+    """x * sigmoid(x), "Cosmos3 Wan VAE ...", section 10.4."""
+    x = _f64(x)
+    y = np.empty_like(x)
+    _load().oracle_silu(_ptr(x), x.size, _ptr(y))
+    return y
+
+
+def upsample_nearest2x(x) -> np.ndarray:
+    """Nearest 2x upsample in H and W, none in T (plainest reading)."""
+    x = _f64(x)
+    N, C, T, H, W = x.shape
+    y = np.empty((N, C, T, 2 * H, 2 * W), dtype=np.float64)
+    _load().oracle_upsample_nearest2x(_ptr(x), N, C, T, H, W, _ptr(y))
+    return y
+
+
+def round_bf16(x) -> np.ndarray:
+    """Round to the nearest bfloat16 value (ties to even), returned as fp64."""
+    x = _f64(x)
+    y = np.empty_like(x)
+    _load().oracle_round_bf16(_ptr(x), x.size, _ptr(y))
+    return y
+
+
+def next_cache(cache_in, x, frames: int = CACHE_T) -> np.ndarray:
+    """The cache a causal conv leaves behind: the last ``frames`` frames of
+    concat_T(cache_in, x) ("Cosmos3 Wan VAE ...", sections 8.5 and 10.3: the
+    cached frames are concatenated in front of the chunk).  ``cache_in`` None
+    means a fresh sequence (all-zero past)."""
+    x = _f64(x)
+    N, C, T, H, W = x.shape
+    if cache_in is None:
+        cache_in = np.zeros((N, C, frames, H, W))
+    full = np.concatenate([_f64(cache_in), x], axis=2)
+    return np.ascontiguousarray(full[:, :, full.shape[2] - frames:])
+
+
+def _maybe_round(a, bf16: bool):
+    return round_bf16(a) if bf16 else a
+
+
+def norm_silu(x, gamma, beta=None, eps=DEFAULT_EPS, bf16: bool = False):
+    """RMS norm then SiLU; in bf16 mode rounded once where the GPU stores it."""
+    return _maybe_round(silu(rms_norm(x, gamma, beta, eps)), bf16)
+
+
+def resblock(x, p: dict, cache1=None, cache2=None, bf16: bool = False, eps=DEFAULT_EPS):
+    """Wan residual block, "Cosmos3 Wan VAE ...", section 10.4:
+    norm1 -> SiLU -> conv1 (3x3x3 causal) -> norm2 -> SiLU -> Dropout (identity at
+    inference) -> conv2 (3x3x3 causal), plus the shortcut (identity when
+    C_in == C_out, else a 1x1x1 causal conv), added after conv2.
+
+    ``p`` holds gamma1, beta1, w1, b1, gamma2, beta2, w2, b2 and optionally
+    w_short, b_short.  ``cache1``/``cache2`` are the 2-frame caches of the two
+    3x3x3 convs (their inputs, i.e. post norm+SiLU), None for a fresh sequence.
+    In bf16 mode every stored tensor (norm outputs, conv1 output, block
+    output) is rounded to bf16, as the GPU stores them.
+    Returns (y, next_cache1, next_cache2).
+    """
+    h1 = norm_silu(x, p["gamma1"], p.get("beta1"), eps, bf16)
+    a1 = _maybe_round(causal_conv3d(h1, p["w1"], p.get("b1"), cache=_zero_if_none(cache1, h1)), bf16)
+    h2 = norm_silu(a1, p["gamma2"], p.get("beta2"), eps, bf16)
+    if p.get("w_short") is not None:
+        sc = _maybe_round(causal_conv3d(x, p["w_short"], p.get("b_short"), pad=(0, 0)), bf16)
+    else:
+        sc = _f64(x)
+    a2 = causal_conv3d(h2, p["w2"], p.get("b2"), cache=_zero_if_none(cache2, h2))
+    y = _maybe_round(a2 + sc, bf16)
+    return y, next_cache(cache1, h1), next_cache(cache2, h2)
+
+
+def _zero_if_none(cache, like):
+    if cache is not None:
+        return cache
+    N, C, T, H, W = np.shape(like)
+    return np.zeros((N, C, CACHE_T, H, W))
+
+
+def decoder_stack(latent, p: dict, bf16: bool = False, eps=DEFAULT_EPS):
+    """Decoder-shaped stack over a whole latent sequence (causal, so the whole
+    sequence equals frame-by-frame streaming with per-layer caches):
+    conv_in (3x3x3) -> resblock -> resblock -> nearest 2x spatial upsample ->
+    conv_up (3x3x3) -> resblock -> resblock.
+
+    ``p``: w_in, b_in, rb0..rb3 (resblock dicts), w_up, b_up.
+    """
+    h = _maybe_round(causal_conv3d(latent, p["w_in"], p.get("b_in")), bf16)
+    for k in (0, 1):
+        h, _, _ = resblock(h, p[f"rb{k}"], bf16=bf16, eps=eps)
+    h = upsample_nearest2x(h)
+    h = _maybe_round(causal_conv3d(h, p["w_up"], p.get("b_up")), bf16)
+    for k in (2, 3):
+        h, _, _ = resblock(h, p[f"rb{k}"], bf16=bf16, eps=eps)
+    return h
+
+
+def rel_l2(y, ref) -> float:
+    """||y - ref||_2 / ||ref||_2 in fp64."""
+    y = np.asarray(y, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    den = np.linalg.norm(ref.ravel())
+    num = np.linalg.norm((y - ref).ravel())
+    return float(num / den) if den > 0 else float(num)
+
+
+def max_abs(y, ref) -> float:
+    return float(np.max(np.abs(np.asarray(y, np.float64) - np.asarray(ref, np.float64)))) \
+        if np.size(ref) else 0.0
