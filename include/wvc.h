@@ -1,0 +1,214 @@
+/*
+ * wvc.h -- C ABI of libwvc: the causal video-VAE hot path on MI355X (gfx950).
+ *
+ * The library computes the causal 3-D convolution of the Wan video VAE with
+ * its rolling past-frame cache, the channel RMS norm + SiLU around it, and the
+ * residual block that chains them.  Sources of each definition are named at
+ * every entry point:
+ *   [P1] "Cosmos3 Wan VAE -- engine size vs runtime context memory"
+ *        (devpress.csdn.net), sections 8.5, 10.1-10.4.
+ *   [P3] "cache-aware video decoder lowering" (rit.work), section on turning
+ *        Conv3D into batched Conv2D.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Pointers.  Every tensor pointer is a DEVICE pointer owned by the caller.
+ *   The library never allocates, frees or keeps a pointer past the call.
+ * Streams.  `stream` is a hipStream_t passed as void* (NULL = the null
+ *   stream).  Every call only enqueues work on that stream and returns; the
+ *   library never synchronises.  Results are ready when the stream is.
+ * Layout.  Activations are logically [N, C, T, H, W] (the pages' NCTHW,
+ *   [P1] 10.1) and stored channels-last: physical [N][T][H][W][C], C fastest
+ *   (PyTorch's channels_last_3d).  Conv weights are logically
+ *   [C_out, C_in, kT, kH, kW] ([P1] 10.3) stored [C_out][kT][kH][kW][C_in].
+ *   Bias, gamma, beta are [C].  All tensors of one call share one dtype.
+ * Caches.  A past-frame cache of a causal conv is [N, C_in, F, H, W]
+ *   (physical [N][F][H][W][C_in]) with F = wvc_conv3d_cache_frames() (2 for
+ *   the 3x3x3 conv: the page's CACHE_T = 2, [P1] 8.5).  Frame 0 is the oldest.
+ *   An all-zero cache is exactly the zero causal padding before frame 0.
+ * Errors.  Every function returning int returns WVC_OK (0) or one WVC_ERR_*.
+ *   Argument errors are detected before anything is enqueued, so a failed call
+ *   has no side effect.  wvc_last_error() gives text for the calling thread's
+ *   last failure.  No C++ exception crosses this boundary.
+ * Threads.  Calls on different streams or threads are independent; the route
+ *   counters and the strict flag are process-wide.
+ */
+#ifndef WVC_H
+#define WVC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+    WVC_OK = 0,
+    WVC_ERR_ARG = 1,         /* null / negative / inconsistent argument        */
+    WVC_ERR_UNSUPPORTED = 2, /* temporal stride != 1, groups != 1, bad dtype   */
+    WVC_ERR_ALIAS = 3,       /* a written buffer overlaps another buffer       */
+    WVC_ERR_WORKSPACE = 4,   /* workspace missing or too small                 */
+    WVC_ERR_STRICT = 5,      /* strict mode on and the call needs the generic route */
+    WVC_ERR_HIP = 6          /* the HIP runtime reported an error at launch    */
+};
+
+enum { WVC_F32 = 0, WVC_BF16 = 1 };
+
+/* Descriptor of one causal Conv3D call over a chunk of `t` frames. */
+typedef struct wvc_conv3d_desc {
+    int n, c_in, c_out, t, h, w; /* batch, channels, frames in this chunk, spatial  */
+    int kt, kh, kw;              /* kernel extent                                   */
+    int stride_t;                /* must be 1                                       */
+    int stride_h, stride_w;
+    int pad_h, pad_w;            /* symmetric zero padding; temporal pad is causal  */
+    int dil_t, dil_h, dil_w;
+    int groups;                  /* must be 1                                       */
+    int dtype;                   /* WVC_F32 or WVC_BF16                             */
+} wvc_conv3d_desc;
+
+/* Route counters ([P3]: counters show which route every call took). */
+typedef struct wvc_counters {
+    uint64_t fast_3x3x3; /* MFMA implicit-GEMM 3x3x3 route       */
+    uint64_t fast_1x1x1; /* MFMA 1x1x1 channel-projection route  */
+    uint64_t generic;    /* direct-convolution route             */
+    uint64_t rejected;   /* calls refused with WVC_ERR_UNSUPPORTED or WVC_ERR_STRICT */
+} wvc_counters;
+
+/*
+ * Causal 3-D convolution of one chunk, with an explicit cache in and out.
+ * Implements [P1] 10.3: y = b + sum_{ci,kt,kh,kw} W * X', where X' is the
+ * chunk with the F cached past frames concatenated in front along T ([P1] 8.5,
+ * 10.3), then zero padded pad_h/pad_w in space; no future frame is read, so
+ * kernel slice kt = kT-1 multiplies the current frame and slice kt multiplies
+ * frame t - (kT-1-kt)*dil_t.  The bias is added once after the sum over all
+ * slices, and stride, padding and dilation are honoured as given ([P3]).
+ * The output has t frames and h_out = (h + 2 pad_h - dil_h (kh-1) - 1)/stride_h + 1
+ * rows (w_out likewise).
+ *
+ *   x         [N, C_in, t, H, W]          read
+ *   cache_in  [N, C_in, F, H, W] or NULL  read; NULL = zero causal padding
+ *                                          (start of a sequence)
+ *   cache_out [N, C_in, F, H, W] or NULL  written: the last F frames of
+ *                                          concat_T(cache_in, x); NULL = skip
+ *   weight    [C_out, C_in, kT, kH, kW]   read
+ *   bias      [C_out] or NULL             read
+ *   residual  [N, C_out, t, h_out, w_out] or NULL; added after the bias
+ *                                          (fused residual of the block)
+ *   y         [N, C_out, t, h_out, w_out] written
+ *   workspace / workspace_bytes: scratch of at least
+ *             wvc_causal_conv3d_workspace_bytes(d) bytes (may be NULL if 0).
+ *
+ * Routes: bf16 3x3x3 / stride 1 / pad 1 / dilation 1 with C_in % 8 == 0 and
+ * C_out % 16 == 0 takes the MFMA implicit-GEMM kernel; bf16 1x1x1 / stride 1 /
+ * pad 0 with the same channel rules takes the MFMA projection kernel; every
+ * other legal call takes the direct-convolution route (counted as generic,
+ * refused with WVC_ERR_STRICT in strict mode).  stride_t != 1 or groups != 1
+ * is WVC_ERR_UNSUPPORTED ([P3]: the fast path covers 5-D tensors, unit
+ * temporal stride and one group).
+ * Aliasing: y, cache_out and workspace may not overlap any other buffer of the
+ * call (WVC_ERR_ALIAS); read-only buffers may overlap each other (residual ==
+ * x is legal).  cache_in and cache_out must therefore be distinct buffers.
+ */
+int wvc_causal_conv3d_fwd(const wvc_conv3d_desc *d, const void *x, const void *cache_in,
+                          void *cache_out, const void *weight, const void *bias,
+                          const void *residual, void *y, void *workspace,
+                          size_t workspace_bytes, void *stream);
+
+/* Bytes of workspace wvc_causal_conv3d_fwd needs for this descriptor
+ * (0 when none; (size_t)-1 for an invalid descriptor). */
+size_t wvc_causal_conv3d_workspace_bytes(const wvc_conv3d_desc *d);
+
+/* Past frames F a causal conv keeps: dil_t * (kT - 1) ([P1] 10.3, the causal
+ * pad tuple puts all temporal padding before frame 0).  -1 if d is invalid. */
+int wvc_conv3d_cache_frames(const wvc_conv3d_desc *d);
+
+/*
+ * Channel RMS norm, optionally followed by SiLU, [P1] 10.2 and 10.4:
+ * for each (n, t, h, w), with v the C channel values,
+ *   u_c = v_c / max(||v||_2, eps) * sqrt(C) * gamma_c + beta_c
+ *   y_c = apply_silu ? u_c * sigmoid(u_c) : u_c
+ * computed in fp32 and rounded once to the storage type.
+ *   x, y   [N, C, T, H, W] channels-last; y may not overlap x (WVC_ERR_ALIAS)
+ *   gamma  [C]; beta [C] or NULL (zero)
+ * eps must be > 0 (the pages print none; 1e-12 matches the L2-normalise call
+ * the page names).
+ */
+int wvc_rmsnorm_silu(const void *x, const void *gamma, const void *beta, void *y, int n, int c,
+                     int t, int h, int w, int dtype, float eps, int apply_silu, void *stream);
+
+/* Descriptor of one residual-block call over a chunk of t frames. */
+typedef struct wvc_resblock_desc {
+    int n, c_in, c_out, t, h, w;
+    int dtype;
+    float eps; /* RMS-norm clamp, > 0 */
+} wvc_resblock_desc;
+
+/* Parameters of one residual block ([P1] 10.4).  All device pointers. */
+typedef struct wvc_resblock_params {
+    const void *gamma1, *beta1; /* norm1 over C_in; beta1 may be NULL   */
+    const void *w1, *b1;        /* conv1 3x3x3 C_in -> C_out; b1 may be NULL */
+    const void *gamma2, *beta2; /* norm2 over C_out; beta2 may be NULL  */
+    const void *w2, *b2;        /* conv2 3x3x3 C_out -> C_out           */
+    const void *w_short, *b_short; /* 1x1x1 shortcut C_in -> C_out; must be
+                                      given when C_in != C_out, NULL otherwise
+                                      (identity shortcut) */
+} wvc_resblock_params;
+
+/*
+ * Wan residual block on one chunk, [P1] 10.4:
+ *   h1 = SiLU(norm1(x)); a1 = conv1(h1 | cache1); h2 = SiLU(norm2(a1));
+ *   y  = conv2(h2 | cache2) + shortcut(x)
+ * (Dropout is the identity at inference.)  The caches hold the conv inputs
+ * h1 and h2 (post norm + SiLU): cache1 is [N, C_in, 2, H, W], cache2
+ * [N, C_out, 2, H, W]; the *_in ones may be NULL (sequence start), the *_out
+ * ones receive the last 2 frames of concat(cache_in, h) and may be NULL.
+ * The residual is added in conv2's epilogue, before the single rounding.
+ *   x [N, C_in, t, H, W] read; y [N, C_out, t, H, W] written.
+ * Workspace: wvc_resblock_workspace_bytes(d) bytes (intermediates h1, a1, h2
+ * and the shortcut output); it may not overlap any other buffer.
+ */
+int wvc_resblock_fwd(const wvc_resblock_desc *d, const void *x, void *y,
+                     const wvc_resblock_params *p, const void *cache1_in, void *cache1_out,
+                     const void *cache2_in, void *cache2_out, void *workspace,
+                     size_t workspace_bytes, void *stream);
+
+size_t wvc_resblock_workspace_bytes(const wvc_resblock_desc *d);
+
+/*
+ * Zero-fills `bytes` bytes of a cache (a fill kernel, never a memset node, so
+ * it can be recorded in a graph).  A zeroed cache is exactly the zero causal
+ * padding before frame 0, so this restarts a stream.  bytes % 4 == 0.
+ */
+int wvc_cache_reset(void *cache, size_t bytes, void *stream);
+
+/*
+ * Nearest-neighbour 2x spatial upsample, per frame, no temporal change:
+ * y[n, c, t, 2h+i, 2w+j] = x[n, c, t, h, w], i, j in {0, 1}.  The decoder
+ * upsamples back towards pixels; the pages give no operator detail, so this is
+ * the plainest reading.  x [N,C,T,H,W], y [N,C,T,2H,2W]; y may not overlap x.
+ */
+int wvc_upsample_nearest2x(const void *x, void *y, int n, int c, int t, int h, int w, int dtype,
+                           void *stream);
+
+/* Strict mode ([P3]: a strict mode stops on an unexpected fallback): when on,
+ * a call that would take the generic route fails with WVC_ERR_STRICT.
+ * Initialised from the environment variable WVC_STRICT (=1 turns it on). */
+void wvc_set_strict(int on);
+int wvc_get_strict(void);
+
+/* Route counters, process-wide, atomically updated. */
+void wvc_get_counters(wvc_counters *out);
+void wvc_reset_counters(void);
+
+/* Text of the calling thread's last failure ("" if none).  Valid until the
+ * thread's next failing call. */
+const char *wvc_last_error(void);
+
+/* Library version string. */
+const char *wvc_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* WVC_H */

@@ -1,0 +1,181 @@
+"""C-ABI tests that need no GPU: the library loads, exports every symbol the
+header declares, and rejects bad calls with the documented status code before
+enqueueing anything (so fake, never-dereferenced pointers are safe here).
+
+Route guard semantics follow "cache-aware video decoder lowering" (section on
+turning Conv3D into batched Conv2D): the fast path covers unit temporal stride
+and one group; counters record each call's route; strict mode stops on an
+unexpected fallback.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from video_vae_causal_amd import _lib as L
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "wvc.h")
+
+# Fake device addresses: validation compares them but never dereferences them.
+X, CIN, COUT, W, B, Y, WS = (0x10000000 + i * 0x01000000 for i in range(7))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(L.LIB_PATH):
+        pytest.skip("libwvc.so not built")
+    return L.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(wvc_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_and_binding_agree():
+    assert sorted(L.EXPORTED) == declared_functions()
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    assert L.wvc_version().startswith("libwvc")
+
+
+def desc(**kw):
+    base = dict(x_shape=(1, 16, 2, 8, 8), w_shape=(16, 16, 3, 3, 3), dtype=L.WVC_BF16)
+    base.update(kw)
+    return L.conv_desc(base["x_shape"], base["w_shape"], base["dtype"],
+                       base.get("stride", (1, 1, 1)), base.get("padding", (1, 1)),
+                       base.get("dilation", (1, 1, 1)), base.get("groups", 1))
+
+
+def call(lib, d, x=X, cin=CIN, cout=COUT, w=W, b=B, res=None, y=Y, ws=None, wsb=0):
+    return lib.wvc_causal_conv3d_fwd(ctypes.byref(d) if d is not None else None, x, cin, cout, w,
+                                     b, res, y, ws, wsb, None)
+
+
+def test_unsupported_guard_and_rejected_counter(lib):
+    L.wvc_reset_counters()
+    assert call(lib, desc(stride=(2, 1, 1))) == L.WVC_ERR_UNSUPPORTED
+    assert "temporal stride" in L.wvc_last_error()
+    assert call(lib, desc(groups=2)) == L.WVC_ERR_UNSUPPORTED
+    assert call(lib, desc(dtype=7)) == L.WVC_ERR_UNSUPPORTED
+    c = L.wvc_get_counters()
+    assert c["rejected"] == 3 and c["fast_3x3x3"] == c["generic"] == 0
+
+
+def test_bad_arguments(lib):
+    assert call(lib, None) == L.WVC_ERR_ARG
+    assert call(lib, desc(x_shape=(0, 16, 2, 8, 8))) == L.WVC_ERR_ARG
+    assert call(lib, desc(x_shape=(1, 16, -1, 8, 8))) == L.WVC_ERR_ARG
+    assert call(lib, desc(padding=(-1, 1))) == L.WVC_ERR_ARG
+    assert call(lib, desc(dilation=(0, 1, 1))) == L.WVC_ERR_ARG
+    assert call(lib, desc(x_shape=(1, 16, 2, 1, 1), padding=(0, 0))) == L.WVC_ERR_ARG
+    assert call(lib, desc(), w=None) == L.WVC_ERR_ARG
+    assert call(lib, desc(), x=None) == L.WVC_ERR_ARG
+    assert call(lib, desc(), ws=None, wsb=64) == L.WVC_ERR_ARG
+    assert L.wvc_last_error()
+
+
+def test_aliasing_of_written_buffers(lib):
+    assert call(lib, desc(), y=X) == L.WVC_ERR_ALIAS                 # in place
+    assert "'y'" in L.wvc_last_error()
+    assert call(lib, desc(), cout=CIN) == L.WVC_ERR_ALIAS            # cache not ping-ponged
+    assert call(lib, desc(), y=X + 64) == L.WVC_ERR_ALIAS            # partial overlap
+    assert call(lib, desc(), ws=W, wsb=16) == L.WVC_ERR_ALIAS         # workspace on weights
+    assert call(lib, desc(), cout=Y + 2048) == L.WVC_ERR_ALIAS       # cache_out inside y
+
+
+def test_read_only_buffers_may_overlap_until_a_launch(lib):
+    """residual == x is legal; with strict mode on, an fp32 call (generic route)
+    is refused before any launch, proving validation passed the aliasing."""
+    L.wvc_set_strict(True)
+    try:
+        d = desc(dtype=L.WVC_F32)
+        assert call(lib, d, res=X) != L.WVC_ERR_ALIAS
+        assert call(lib, d, res=X) == L.WVC_ERR_STRICT
+    finally:
+        L.wvc_set_strict(False)
+
+
+def test_strict_mode_refuses_generic_route(lib):
+    L.wvc_reset_counters()
+    L.wvc_set_strict(True)
+    try:
+        assert L.wvc_get_strict()
+        assert call(lib, desc(dtype=L.WVC_F32)) == L.WVC_ERR_STRICT
+        assert call(lib, desc(stride=(1, 2, 2))) == L.WVC_ERR_STRICT
+        assert call(lib, desc(w_shape=(16, 16, 3, 5, 5), padding=(2, 2))) == L.WVC_ERR_STRICT
+        # misaligned pointers fall to the generic route as well
+        assert call(lib, desc(), x=X + 2) == L.WVC_ERR_STRICT
+        assert "strict" in L.wvc_last_error()
+        assert L.wvc_get_counters()["rejected"] == 4
+    finally:
+        L.wvc_set_strict(False)
+    assert not L.wvc_get_strict()
+
+
+def test_cache_frames_and_workspace_queries(lib):
+    assert lib.wvc_conv3d_cache_frames(ctypes.byref(desc())) == 2
+    assert lib.wvc_conv3d_cache_frames(ctypes.byref(desc(w_shape=(16, 16, 1, 1, 1)))) == 0
+    assert lib.wvc_conv3d_cache_frames(ctypes.byref(desc(dilation=(3, 1, 1)))) == 6
+    assert lib.wvc_conv3d_cache_frames(None) == -1
+    L.wvc_reset_counters()
+    assert L.wvc_causal_conv3d_workspace_bytes(desc()) == 0
+    with pytest.raises(L.WvcError):
+        L.wvc_causal_conv3d_workspace_bytes(desc(stride=(2, 1, 1)))
+    assert L.wvc_get_counters()["rejected"] == 0   # a size query is not a call
+
+
+def rb_desc(c_in=16, c_out=16, t=1, eps=1e-12):
+    return L.resblock_desc((1, c_in, t, 8, 8), c_out, L.WVC_BF16, eps)
+
+
+def test_resblock_validation(lib):
+    d = rb_desc()
+    need = L.wvc_resblock_workspace_bytes(d)
+    assert need >= 3 * 8 * 8 * 16 * 2
+    assert L.wvc_resblock_workspace_bytes(rb_desc(c_out=32)) > need   # shortcut output too
+    p = L.ResblockParams()
+    p.gamma1, p.w1, p.gamma2, p.w2 = 0x50000000, 0x51000000, 0x52000000, 0x53000000
+
+    def rcall(d, x=X, y=Y, params=p, ws=WS, wsb=None, c1i=None, c1o=None):
+        return lib.wvc_resblock_fwd(ctypes.byref(d), x, y, ctypes.byref(params) if params else None,
+                                    c1i, c1o, None, None, ws, need if wsb is None else wsb, None)
+
+    assert rcall(d, wsb=need - 1) == L.WVC_ERR_WORKSPACE
+    assert rcall(d, params=None) == L.WVC_ERR_ARG
+    assert rcall(rb_desc(eps=0.0)) == L.WVC_ERR_ARG
+    assert rcall(rb_desc(c_out=32)) == L.WVC_ERR_ARG       # C_in != C_out needs w_short
+    assert rcall(d, y=X) == L.WVC_ERR_ALIAS
+    assert rcall(d, ws=Y) == L.WVC_ERR_ALIAS
+    assert rcall(d, c1i=CIN, c1o=CIN) == L.WVC_ERR_ALIAS
+    q = L.ResblockParams()
+    q.gamma1 = 0x50000000
+    assert rcall(d, params=q) == L.WVC_ERR_ARG
+
+
+def test_norm_and_upsample_validation(lib):
+    assert lib.wvc_rmsnorm_silu(X, B, None, Y, 1, 0, 1, 4, 4, L.WVC_BF16, 1e-12, 1, None) == L.WVC_ERR_ARG
+    assert lib.wvc_rmsnorm_silu(X, B, None, Y, 1, 8, 1, 4, 4, L.WVC_BF16, 0.0, 1, None) == L.WVC_ERR_ARG
+    assert lib.wvc_rmsnorm_silu(X, None, None, Y, 1, 8, 1, 4, 4, L.WVC_BF16, 1e-12, 1, None) == L.WVC_ERR_ARG
+    assert lib.wvc_rmsnorm_silu(X, B, None, X, 1, 8, 1, 4, 4, L.WVC_BF16, 1e-12, 1, None) == L.WVC_ERR_ALIAS
+    assert lib.wvc_rmsnorm_silu(X, B, None, Y, 1, 8, 1, 4, 4, 9, 1e-12, 1, None) == L.WVC_ERR_UNSUPPORTED
+    assert lib.wvc_upsample_nearest2x(X, X + 16, 1, 8, 1, 4, 4, L.WVC_BF16, None) == L.WVC_ERR_ALIAS
+    assert lib.wvc_upsample_nearest2x(X, Y, 1, 8, 1, 0, 4, L.WVC_BF16, None) == L.WVC_ERR_ARG
+    assert lib.wvc_cache_reset(None, 64, None) == L.WVC_ERR_ARG
+    assert lib.wvc_cache_reset(X + 2, 64, None) == L.WVC_ERR_ARG
+    assert lib.wvc_cache_reset(X, 6, None) == L.WVC_ERR_ARG
+    assert lib.wvc_cache_reset(X, 0, None) == L.WVC_OK
+
+
+def test_binding_refuses_host_tensors(lib):
+    import torch
+    x = torch.zeros((1, 16, 1, 4, 4), dtype=torch.bfloat16)
+    w = torch.zeros((16, 16, 3, 3, 3), dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        L.wvc_causal_conv3d_fwd(x, w)

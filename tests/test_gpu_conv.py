@@ -1,0 +1,200 @@
+"""GPU parity of the causal conv (both MFMA routes and the direct route)
+against the fp64 oracle, through the C ABI.
+
+Definitions: "Cosmos3 Wan VAE -- engine size vs runtime context memory",
+section 10.3 (conv, causal padding, cache concatenation) and "cache-aware video
+decoder lowering" (bias once, stride/padding/dilation honoured, causal order,
+route counters and strict mode).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from video_vae_causal_amd import _lib as L
+from video_vae_causal_amd import inputs
+from _gpu_util import check_bf16, check_f32, f64, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+
+def cl(t):
+    return t.contiguous(memory_format=torch.channels_last_3d)
+
+
+def conv_case(cin, cout, t, h, w, seed, k=(3, 3, 3), dtype="bf16"):
+    x = inputs.quantize(inputs.normal((1, cin, t, h, w), seed, "x"), dtype)
+    wt = inputs.conv_weight(cout, cin, k, seed, "w", dtype)
+    b = inputs.conv_bias(cout, seed, "b", dtype)
+    cache = inputs.quantize(inputs.normal((1, cin, 2, h, w), seed, "cache"), dtype)
+    return x, wt, b, cache
+
+
+@pytest.mark.parametrize("cin,cout,t,h,w", [
+    (64, 64, 3, 20, 37),     # ragged tiles in both directions
+    (48, 384, 2, 9, 13),     # partial 32-channel block, 3 channel tiles
+    (96, 96, 2, 17, 33),     # 96-channel tile variant
+    (32, 128, 1, 8, 8),
+    (16, 16, 2, 1, 70),      # one-row frames
+    (384, 384, 1, 30, 52),   # decoder low-res frame
+])
+def test_conv3x3x3_bf16_vs_oracle(cin, cout, t, h, w):
+    x, wt, b, cache = conv_case(cin, cout, t, h, w, seed=cin + cout + h)
+    print(f"[case] conv3 cin={cin} cout={cout} t={t} {h}x{w}", flush=True)
+    L.wvc_reset_counters()
+    y = L.wvc_causal_conv3d_fwd(to_dev(x), to_dev(wt), to_dev(b), cache_in=to_dev(cache))
+    ref = oracle.causal_conv3d(f64(x), f64(wt), f64(b), cache=f64(cache))
+    check_bf16(to_host(y), ref, f"conv3 {cin}->{cout} {h}x{w}")
+    assert L.wvc_get_counters()["fast_3x3x3"] == 1
+
+
+def test_conv_residual_and_no_bias():
+    x, wt, b, cache = conv_case(64, 64, 2, 11, 19, seed=7)
+    res = inputs.quantize(inputs.normal((1, 64, 2, 11, 19), 7, "res"), "bf16")
+    y = L.wvc_causal_conv3d_fwd(to_dev(x), to_dev(wt), None, residual=to_dev(res))
+    ref = oracle.causal_conv3d(f64(x), f64(wt), None) + f64(res)
+    check_bf16(to_host(y), ref, "conv3 + residual, no bias")
+
+
+def test_cache_out_is_last_two_frames_exactly():
+    for t in (1, 2, 4):
+        x, wt, b, cache = conv_case(32, 32, t, 6, 10, seed=20 + t)
+        cin, cout = to_dev(cache), L.empty_cl((1, 32, 2, 6, 10))
+        L.wvc_causal_conv3d_fwd(to_dev(x), to_dev(wt), to_dev(b), cache_in=cin, cache_out=cout)
+        expect = oracle.next_cache(f64(cache), f64(x))
+        np.testing.assert_array_equal(to_host(cout), expect)
+    # no cache_in: the past is zero
+    x, wt, b, _ = conv_case(32, 32, 1, 6, 10, seed=30)
+    cout = L.empty_cl((1, 32, 2, 6, 10))
+    L.wvc_causal_conv3d_fwd(to_dev(x), to_dev(wt), to_dev(b), cache_out=cout)
+    np.testing.assert_array_equal(to_host(cout), oracle.next_cache(None, f64(x)))
+
+
+def test_tiny_f32_config_whole_and_frame_chunks():
+    """fp32 causal conv 16->16 on [1,16,5,32,32] (direct route): whole sequence
+    and 1-frame chunks with the cache, rel L2 <= 1e-5; chunked == whole bitwise."""
+    d = inputs.tiny_conv_inputs(seed=1)
+    ref = oracle.causal_conv3d(f64(d["x"]), f64(d["w"]), f64(d["b"]))
+    xd, wd, bd = (to_dev(d[k], torch.float32) for k in ("x", "w", "b"))
+    L.wvc_reset_counters()
+    whole = L.wvc_causal_conv3d_fwd(xd, wd, bd)
+    check_f32(to_host(whole), ref, "tiny fp32 whole")
+    caches = [L.empty_cl((1, 16, 2, 32, 32), torch.float32) for _ in range(2)]
+    L.wvc_cache_reset(caches[0])
+    outs = []
+    for t in range(5):
+        outs.append(L.wvc_causal_conv3d_fwd(cl(xd[:, :, t:t + 1]), wd, bd, caches[t % 2],
+                                            caches[(t + 1) % 2]))
+    chunked = torch.cat(outs, dim=2)
+    check_f32(to_host(chunked), ref, "tiny fp32 1-frame chunks")
+    assert torch.equal(chunked, whole)
+    assert L.wvc_get_counters()["generic"] == 6
+
+
+@pytest.mark.parametrize("k,stride,pad,dil", [
+    ((3, 3, 3), (1, 2, 2), (1, 1), (1, 1, 1)),
+    ((3, 3, 3), (1, 1, 1), (2, 2), (2, 2, 2)),
+    ((2, 5, 3), (1, 1, 2), (2, 0), (1, 1, 3)),
+    ((3, 3, 3), (1, 1, 1), (1, 1), (1, 1, 1)),
+])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_direct_route_stride_pad_dilation(k, stride, pad, dil, dtype):
+    cin, cout = 12, 10          # channel counts the MFMA routes do not take
+    x = inputs.quantize(inputs.normal((2, cin, 4, 13, 15), 3, "x"), dtype)
+    wt = inputs.conv_weight(cout, cin, k, 3, "w", dtype)
+    b = inputs.conv_bias(cout, 3, "b", dtype)
+    past = dil[0] * (k[0] - 1)
+    cache = inputs.quantize(inputs.normal((2, cin, past, 13, 15), 3, "c"), dtype)
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    y = L.wvc_causal_conv3d_fwd(to_dev(x, tdt), to_dev(wt, tdt), to_dev(b, tdt),
+                                cache_in=to_dev(cache, tdt) if past else None,
+                                stride=stride, padding=pad, dilation=dil)
+    ref = oracle.causal_conv3d(f64(x), f64(wt), f64(b), cache=f64(cache) if past else None,
+                               stride=stride[1:], pad=pad, dil=dil)
+    (check_bf16 if dtype == "bf16" else check_f32)(to_host(y), ref, f"direct {k} {stride} {pad} {dil}")
+
+
+@pytest.mark.parametrize("cin,cout,h,w", [(64, 32, 9, 13), (384, 192, 12, 40), (48, 96, 5, 7)])
+def test_conv1x1x1_projection(cin, cout, h, w):
+    x = inputs.quantize(inputs.normal((1, cin, 2, h, w), 9, "x"), "bf16")
+    wt = inputs.conv_weight(cout, cin, (1, 1, 1), 9, "w", "bf16")
+    b = inputs.conv_bias(cout, 9, "b", "bf16")
+    L.wvc_reset_counters()
+    y = L.wvc_causal_conv3d_fwd(to_dev(x), to_dev(wt), to_dev(b), padding=(0, 0))
+    ref = oracle.causal_conv3d(f64(x), f64(wt), f64(b), pad=(0, 0))
+    check_bf16(to_host(y), ref, f"conv1x1 {cin}->{cout}")
+    assert L.wvc_get_counters()["fast_1x1x1"] == 1
+
+
+@pytest.mark.parametrize("sizes", [[1, 1, 1, 1, 1], [2, 3], [4, 1], [1, 4]])
+def test_chunked_equals_whole_bitwise(sizes):
+    x, wt, b, _ = conv_case(64, 128, 5, 14, 22, seed=41)
+    xd, wd, bd = to_dev(x), to_dev(wt), to_dev(b)
+    whole = L.wvc_causal_conv3d_fwd(xd, wd, bd)
+    caches = [L.empty_cl((1, 64, 2, 14, 22)) for _ in range(2)]
+    L.wvc_cache_reset(caches[0])
+    outs, t0 = [], 0
+    for i, s in enumerate(sizes):
+        outs.append(L.wvc_causal_conv3d_fwd(cl(xd[:, :, t0:t0 + s]), wd, bd, caches[i % 2],
+                                            caches[(i + 1) % 2]))
+        t0 += s
+    assert torch.equal(torch.cat(outs, dim=2), whole)
+
+
+@pytest.mark.parametrize("t0", [0, 2, 4])
+def test_causality_bitwise(t0):
+    x, wt, b, _ = conv_case(32, 64, 6, 10, 18, seed=50)
+    y0 = L.wvc_causal_conv3d_fwd(to_dev(x), to_dev(wt), to_dev(b))
+    x2 = x.copy()
+    x2[:, :, t0] = inputs.quantize(inputs.normal((1, 32, 10, 18), 51, "p"), "bf16")
+    y1 = L.wvc_causal_conv3d_fwd(to_dev(x2), to_dev(wt), to_dev(b))
+    assert torch.equal(y1[:, :, :t0], y0[:, :, :t0])
+    for t in range(t0, min(t0 + 3, 6)):
+        assert not torch.equal(y1[:, :, t], y0[:, :, t])
+    assert torch.equal(y1[:, :, t0 + 3:], y0[:, :, t0 + 3:])
+
+
+def test_bias_added_exactly_once():
+    for cin, cout, dtype in ((64, 128, "bf16"), (12, 10, "f32")):
+        _, wt, b, _ = conv_case(cin, cout, 2, 7, 9, seed=60, dtype=dtype)
+        tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+        x = torch.zeros((1, cin, 3, 7, 9), dtype=tdt, device="cuda").contiguous(
+            memory_format=torch.channels_last_3d)
+        y = L.wvc_causal_conv3d_fwd(x, to_dev(wt, tdt), to_dev(b, tdt))
+        expect = np.broadcast_to(f64(b)[None, :, None, None, None], y.shape)
+        np.testing.assert_array_equal(to_host(y), expect)
+
+
+def test_determinism_bitwise():
+    x, wt, b, cache = conv_case(96, 96, 3, 25, 31, seed=70)
+    args = (to_dev(x), to_dev(wt), to_dev(b), to_dev(cache))
+    y0 = L.wvc_causal_conv3d_fwd(*args)
+    y1 = L.wvc_causal_conv3d_fwd(*args)
+    assert torch.equal(y0, y1)
+
+
+def test_output_canaries_untouched():
+    """Outputs are written into the front of a larger buffer whose tail holds a
+    sentinel; the tail must be untouched (no out-of-bounds stores)."""
+    cin, cout, t, h, w = 64, 128, 2, 9, 21
+    x, wt, b, _ = conv_case(cin, cout, t, h, w, seed=80)
+    numel = t * h * w * cout
+    flat = torch.full((numel + 4096,), 0x7FC1, dtype=torch.int16, device="cuda")
+    y = flat[:numel].view(torch.bfloat16).view(1, t, h, w, cout).permute(0, 4, 1, 2, 3)
+    assert y.is_contiguous(memory_format=torch.channels_last_3d)
+    L.wvc_causal_conv3d_fwd(to_dev(x), to_dev(wt), to_dev(b), y=y)
+    assert torch.all(flat[numel:] == 0x7FC1)
+    ref = oracle.causal_conv3d(f64(x), f64(wt), f64(b))
+    check_bf16(to_host(y), ref, "canary run")
+
+
+def test_strict_mode_allows_fast_route_and_refuses_generic():
+    x, wt, b, _ = conv_case(32, 32, 1, 6, 6, seed=90)
+    L.wvc_set_strict(True)
+    try:
+        L.wvc_causal_conv3d_fwd(to_dev(x), to_dev(wt), to_dev(b))
+        with pytest.raises(L.WvcError) as e:
+            L.wvc_causal_conv3d_fwd(to_dev(x, torch.float32), to_dev(wt, torch.float32))
+        assert e.value.code == L.WVC_ERR_STRICT
+    finally:
+        L.wvc_set_strict(False)

@@ -1,0 +1,333 @@
+"""ctypes binding of libwvc (include/wvc.h).
+
+Argument marshalling only: every step of the path runs in the library's HIP
+kernels.  PyTorch supplies device memory and the current HIP stream.  Tensors
+use the logical NCTHW shapes with PyTorch's channels_last_3d memory format
+(physical N,T,H,W,C), which is what the library expects; weights are
+[C_out, C_in, kT, kH, kW] in channels_last_3d (physical C_out,kT,kH,kW,C_in).
+
+There is no fallback: if libwvc.so is missing or fails to load, every entry
+point raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libwvc.so")
+
+WVC_OK, WVC_ERR_ARG, WVC_ERR_UNSUPPORTED, WVC_ERR_ALIAS, WVC_ERR_WORKSPACE, WVC_ERR_STRICT, \
+    WVC_ERR_HIP = range(7)
+WVC_F32, WVC_BF16 = 0, 1
+ERROR_NAMES = {0: "WVC_OK", 1: "WVC_ERR_ARG", 2: "WVC_ERR_UNSUPPORTED", 3: "WVC_ERR_ALIAS",
+               4: "WVC_ERR_WORKSPACE", 5: "WVC_ERR_STRICT", 6: "WVC_ERR_HIP"}
+
+# Every symbol include/wvc.h declares.
+EXPORTED = (
+    "wvc_causal_conv3d_fwd", "wvc_causal_conv3d_workspace_bytes", "wvc_conv3d_cache_frames",
+    "wvc_rmsnorm_silu", "wvc_resblock_fwd", "wvc_resblock_workspace_bytes", "wvc_cache_reset",
+    "wvc_upsample_nearest2x", "wvc_set_strict", "wvc_get_strict", "wvc_get_counters",
+    "wvc_reset_counters", "wvc_last_error", "wvc_version",
+)
+
+
+class ConvDesc(ctypes.Structure):
+    _fields_ = [(f, ctypes.c_int) for f in (
+        "n", "c_in", "c_out", "t", "h", "w", "kt", "kh", "kw", "stride_t", "stride_h",
+        "stride_w", "pad_h", "pad_w", "dil_t", "dil_h", "dil_w", "groups", "dtype")]
+
+
+class ResblockDesc(ctypes.Structure):
+    _fields_ = [(f, ctypes.c_int) for f in ("n", "c_in", "c_out", "t", "h", "w", "dtype")] + \
+        [("eps", ctypes.c_float)]
+
+
+class ResblockParams(ctypes.Structure):
+    _fields_ = [(f, ctypes.c_void_p) for f in (
+        "gamma1", "beta1", "w1", "b1", "gamma2", "beta2", "w2", "b2", "w_short", "b_short")]
+
+
+class Counters(ctypes.Structure):
+    _fields_ = [(f, ctypes.c_uint64) for f in ("fast_3x3x3", "fast_1x1x1", "generic", "rejected")]
+
+
+class WvcError(RuntimeError):
+    def __init__(self, code: int, text: str):
+        super().__init__(f"{ERROR_NAMES.get(code, code)}: {text}")
+        self.code = code
+
+
+_lib = None
+
+
+def load(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libwvc.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with __graft_entry__.build() "
+                          "(hipcc, gfx950); there is no fallback path")
+    lib = ctypes.CDLL(path)
+    vp, sz, i, f = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_float
+    dptr = ctypes.POINTER(ConvDesc)
+    lib.wvc_causal_conv3d_fwd.argtypes = [dptr, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.wvc_causal_conv3d_fwd.restype = i
+    lib.wvc_causal_conv3d_workspace_bytes.argtypes = [dptr]
+    lib.wvc_causal_conv3d_workspace_bytes.restype = sz
+    lib.wvc_conv3d_cache_frames.argtypes = [dptr]
+    lib.wvc_conv3d_cache_frames.restype = i
+    lib.wvc_rmsnorm_silu.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp]
+    lib.wvc_rmsnorm_silu.restype = i
+    lib.wvc_resblock_fwd.argtypes = [ctypes.POINTER(ResblockDesc), vp, vp,
+                                     ctypes.POINTER(ResblockParams), vp, vp, vp, vp, vp, sz, vp]
+    lib.wvc_resblock_fwd.restype = i
+    lib.wvc_resblock_workspace_bytes.argtypes = [ctypes.POINTER(ResblockDesc)]
+    lib.wvc_resblock_workspace_bytes.restype = sz
+    lib.wvc_cache_reset.argtypes = [vp, sz, vp]
+    lib.wvc_cache_reset.restype = i
+    lib.wvc_upsample_nearest2x.argtypes = [vp, vp, i, i, i, i, i, i, vp]
+    lib.wvc_upsample_nearest2x.restype = i
+    lib.wvc_set_strict.argtypes = [i]
+    lib.wvc_set_strict.restype = None
+    lib.wvc_get_strict.argtypes = []
+    lib.wvc_get_strict.restype = i
+    lib.wvc_get_counters.argtypes = [ctypes.POINTER(Counters)]
+    lib.wvc_get_counters.restype = None
+    lib.wvc_reset_counters.argtypes = []
+    lib.wvc_reset_counters.restype = None
+    lib.wvc_last_error.argtypes = []
+    lib.wvc_last_error.restype = ctypes.c_char_p
+    lib.wvc_version.argtypes = []
+    lib.wvc_version.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def _check(rc: int):
+    if rc != WVC_OK:
+        raise WvcError(rc, load().wvc_last_error().decode())
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(t: Optional[torch.Tensor] = None):
+    dev = t.device if t is not None and t.is_cuda else None
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def _dtype_code(dt: torch.dtype) -> int:
+    if dt == torch.bfloat16:
+        return WVC_BF16
+    if dt == torch.float32:
+        return WVC_F32
+    raise TypeError(f"unsupported dtype {dt}: bfloat16 or float32")
+
+
+def _need_cl(t: Optional[torch.Tensor], name: str, ndim: int = 5):
+    if t is None:
+        return
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got {tuple(t.shape)}")
+    if ndim == 5 and not t.is_contiguous(memory_format=torch.channels_last_3d):
+        raise ValueError(f"{name} must be channels_last_3d contiguous")
+
+
+def _need_vec(t: Optional[torch.Tensor], name: str, c: int):
+    if t is None:
+        return
+    if not t.is_cuda or t.dim() != 1 or t.shape[0] != c or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous device vector of {c} elements")
+
+
+def empty_cl(shape: Sequence[int], dtype=torch.bfloat16, device="cuda") -> torch.Tensor:
+    """Uninitialised [N,C,T,H,W] tensor in channels_last_3d memory."""
+    return torch.empty(tuple(shape), dtype=dtype, device=device,
+                       memory_format=torch.channels_last_3d)
+
+
+def conv_desc(x_shape, w_shape, dtype: int, stride=(1, 1, 1), padding=(1, 1),
+              dilation=(1, 1, 1), groups: int = 1) -> ConvDesc:
+    n, c, t, h, w = x_shape
+    co, ci, kt, kh, kw = w_shape
+    d = ConvDesc()
+    d.n, d.c_in, d.c_out, d.t, d.h, d.w = n, ci, co, t, h, w
+    d.kt, d.kh, d.kw = kt, kh, kw
+    d.stride_t, d.stride_h, d.stride_w = stride
+    d.pad_h, d.pad_w = padding
+    d.dil_t, d.dil_h, d.dil_w = dilation
+    d.groups = groups
+    d.dtype = dtype
+    return d
+
+
+def conv_out_hw(h, w, k, stride, padding, dilation):
+    ho = (h + 2 * padding[0] - dilation[1] * (k[1] - 1) - 1) // stride[1] + 1
+    wo = (w + 2 * padding[1] - dilation[2] * (k[2] - 1) - 1) // stride[2] + 1
+    return ho, wo
+
+
+def wvc_conv3d_cache_frames(weight_shape, dilation=(1, 1, 1)) -> int:
+    d = conv_desc((1, weight_shape[1], 1, 1, 1), weight_shape, WVC_BF16, dilation=dilation)
+    return load().wvc_conv3d_cache_frames(ctypes.byref(d))
+
+
+def wvc_causal_conv3d_workspace_bytes(d: ConvDesc) -> int:
+    v = load().wvc_causal_conv3d_workspace_bytes(ctypes.byref(d))
+    if v == ctypes.c_size_t(-1).value:
+        raise WvcError(WVC_ERR_ARG, load().wvc_last_error().decode())
+    return v
+
+
+def wvc_causal_conv3d_fwd(x: torch.Tensor, weight: torch.Tensor, bias: Optional[torch.Tensor] = None,
+                          cache_in: Optional[torch.Tensor] = None,
+                          cache_out: Optional[torch.Tensor] = None,
+                          residual: Optional[torch.Tensor] = None,
+                          y: Optional[torch.Tensor] = None, stride=(1, 1, 1), padding=(1, 1),
+                          dilation=(1, 1, 1), groups: int = 1,
+                          workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Causal Conv3D of one chunk (see wvc_causal_conv3d_fwd in include/wvc.h).
+    Returns y (allocated if not given)."""
+    lib = load()
+    _need_cl(x, "x")
+    _need_cl(weight, "weight")
+    for name, t in (("cache_in", cache_in), ("cache_out", cache_out), ("residual", residual),
+                    ("y", y)):
+        _need_cl(t, name)
+    _need_vec(bias, "bias", weight.shape[0])
+    code = _dtype_code(x.dtype)
+    d = conv_desc(tuple(x.shape), tuple(weight.shape), code, stride, padding, dilation, groups)
+    if y is None:
+        ho, wo = conv_out_hw(x.shape[3], x.shape[4], weight.shape[2:], stride, padding, dilation)
+        if ho < 1 or wo < 1:
+            raise WvcError(WVC_ERR_ARG, "kernel larger than the padded frame")
+        y = empty_cl((x.shape[0], weight.shape[0], x.shape[2], ho, wo), x.dtype, x.device)
+    ws_bytes = 0
+    if workspace is None:
+        need = wvc_causal_conv3d_workspace_bytes(d)
+        if need:
+            workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    if workspace is not None:
+        ws_bytes = workspace.numel() * workspace.element_size()
+    _check(lib.wvc_causal_conv3d_fwd(ctypes.byref(d), _ptr(x), _ptr(cache_in), _ptr(cache_out),
+                                      _ptr(weight), _ptr(bias), _ptr(residual), _ptr(y),
+                                      _ptr(workspace), ws_bytes, _stream(x)))
+    return y
+
+
+def wvc_rmsnorm_silu(x: torch.Tensor, gamma: torch.Tensor, beta: Optional[torch.Tensor] = None,
+                     y: Optional[torch.Tensor] = None, eps: float = 1e-12,
+                     apply_silu: bool = True) -> torch.Tensor:
+    """Channel RMS norm (+ SiLU) (see wvc_rmsnorm_silu in include/wvc.h)."""
+    lib = load()
+    _need_cl(x, "x")
+    _need_cl(y, "y")
+    n, c, t, h, w = x.shape
+    _need_vec(gamma, "gamma", c)
+    _need_vec(beta, "beta", c)
+    if y is None:
+        y = empty_cl(x.shape, x.dtype, x.device)
+    _check(lib.wvc_rmsnorm_silu(_ptr(x), _ptr(gamma), _ptr(beta), _ptr(y), n, c, t, h, w,
+                                _dtype_code(x.dtype), float(eps), int(bool(apply_silu)),
+                                _stream(x)))
+    return y
+
+
+def resblock_desc(x_shape, c_out: int, dtype: int, eps: float = 1e-12) -> ResblockDesc:
+    d = ResblockDesc()
+    d.n, d.c_in, d.t, d.h, d.w = x_shape[0], x_shape[1], x_shape[2], x_shape[3], x_shape[4]
+    d.c_out = c_out
+    d.dtype = dtype
+    d.eps = eps
+    return d
+
+
+def wvc_resblock_workspace_bytes(d: ResblockDesc) -> int:
+    v = load().wvc_resblock_workspace_bytes(ctypes.byref(d))
+    if v == ctypes.c_size_t(-1).value:
+        raise WvcError(WVC_ERR_ARG, load().wvc_last_error().decode())
+    return v
+
+
+def wvc_resblock_fwd(x: torch.Tensor, params: dict, cache1_in=None, cache1_out=None,
+                     cache2_in=None, cache2_out=None, y: Optional[torch.Tensor] = None,
+                     eps: float = 1e-12, workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Wan residual block on one chunk (see wvc_resblock_fwd in include/wvc.h).
+    ``params``: gamma1, beta1, w1, b1, gamma2, beta2, w2, b2[, w_short, b_short]."""
+    lib = load()
+    _need_cl(x, "x")
+    c_out = params["w1"].shape[0]
+    for name in ("w1", "w2", "w_short"):
+        _need_cl(params.get(name), name)
+    for name, t in (("cache1_in", cache1_in), ("cache1_out", cache1_out),
+                    ("cache2_in", cache2_in), ("cache2_out", cache2_out), ("y", y)):
+        _need_cl(t, name)
+    code = _dtype_code(x.dtype)
+    d = resblock_desc(tuple(x.shape), c_out, code, eps)
+    if y is None:
+        y = empty_cl((x.shape[0], c_out) + tuple(x.shape[2:]), x.dtype, x.device)
+    need = wvc_resblock_workspace_bytes(d)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    p = ResblockParams()
+    for f, _ in ResblockParams._fields_:
+        t = params.get(f)
+        setattr(p, f, None if t is None else t.data_ptr())
+    _check(lib.wvc_resblock_fwd(ctypes.byref(d), _ptr(x), _ptr(y), ctypes.byref(p),
+                                _ptr(cache1_in), _ptr(cache1_out), _ptr(cache2_in),
+                                _ptr(cache2_out), _ptr(workspace), ws_bytes, _stream(x)))
+    return y
+
+
+def wvc_cache_reset(cache: torch.Tensor):
+    """Zero a cache in place (the zero causal padding of a fresh sequence)."""
+    _check(load().wvc_cache_reset(_ptr(cache), cache.numel() * cache.element_size(),
+                                  _stream(cache)))
+    return cache
+
+
+def wvc_upsample_nearest2x(x: torch.Tensor, y: Optional[torch.Tensor] = None) -> torch.Tensor:
+    lib = load()
+    _need_cl(x, "x")
+    _need_cl(y, "y")
+    n, c, t, h, w = x.shape
+    if y is None:
+        y = empty_cl((n, c, t, 2 * h, 2 * w), x.dtype, x.device)
+    _check(lib.wvc_upsample_nearest2x(_ptr(x), _ptr(y), n, c, t, h, w, _dtype_code(x.dtype),
+                                      _stream(x)))
+    return y
+
+
+def wvc_set_strict(on: bool):
+    load().wvc_set_strict(int(bool(on)))
+
+
+def wvc_get_strict() -> bool:
+    return bool(load().wvc_get_strict())
+
+
+def wvc_get_counters() -> dict:
+    c = Counters()
+    load().wvc_get_counters(ctypes.byref(c))
+    return {f: int(getattr(c, f)) for f, _ in Counters._fields_}
+
+
+def wvc_reset_counters():
+    load().wvc_reset_counters()
+
+
+def wvc_last_error() -> str:
+    return load().wvc_last_error().decode()
+
+
+def wvc_version() -> str:
+    return load().wvc_version().decode()

@@ -1,0 +1,430 @@
+// wvc_api.hip -- the C ABI of libwvc (declared in include/wvc.h): argument
+// validation, route selection, aliasing checks, route counters, strict mode
+// and per-thread error text.  Every argument error is reported before any
+// work is enqueued.
+#include <atomic>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+
+#include "wvc.h"
+#include "wvc_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+std::atomic<int> g_strict{-1};
+std::atomic<uint64_t> g_fast3{0}, g_fast1{0}, g_generic{0}, g_rejected{0};
+
+int fail(int code, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+int strict_on() {
+    int s = g_strict.load();
+    if (s < 0) {
+        const char *e = std::getenv("WVC_STRICT");
+        int want = (e && std::atoi(e) != 0) ? 1 : 0;
+        int expected = -1;
+        g_strict.compare_exchange_strong(expected, want);
+        s = g_strict.load();
+    }
+    return s;
+}
+
+int elem_bytes(int dtype) { return dtype == WVC_F32 ? 4 : dtype == WVC_BF16 ? 2 : 0; }
+
+struct Buf {
+    const void *p;
+    size_t bytes;
+    bool written;
+    const char *name;
+};
+
+// Every written buffer must be disjoint from every other buffer of the call.
+int check_aliasing(const Buf *b, int nb) {
+    for (int i = 0; i < nb; ++i) {
+        if (!b[i].written || !b[i].p || b[i].bytes == 0) continue;
+        const uintptr_t lo = (uintptr_t)b[i].p, hi = lo + b[i].bytes;
+        for (int j = 0; j < nb; ++j) {
+            if (j == i || !b[j].p || b[j].bytes == 0) continue;
+            const uintptr_t lo2 = (uintptr_t)b[j].p, hi2 = lo2 + b[j].bytes;
+            if (lo < hi2 && lo2 < hi)
+                return fail(WVC_ERR_ALIAS, "written buffer '%s' overlaps buffer '%s'", b[i].name,
+                            b[j].name);
+        }
+    }
+    return WVC_OK;
+}
+
+bool mul_ok(size_t a, size_t b, size_t *out) {
+    if (a != 0 && b > (SIZE_MAX >> 2) / a) return false;
+    *out = a * b;
+    return true;
+}
+
+int out_size(int in, int k, int s, int p, int d) {
+    const long span = (long)d * (k - 1) + 1;
+    if ((long)in + 2L * p < span) return 0;
+    return (int)(((long)in + 2L * p - span) / s + 1);
+}
+
+bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
+
+struct ConvPlan {
+    wvc::ConvCall call;
+    wvc::ConvRoute route;
+    size_t x_bytes, cache_bytes, w_bytes, b_bytes, y_bytes;
+};
+
+// Validates the descriptor (not the pointers) and fills the sizes.
+int plan_conv(const wvc_conv3d_desc *d, ConvPlan *pl, bool count = true) {
+    if (!d) return fail(WVC_ERR_ARG, "conv descriptor is NULL");
+    if (d->stride_t != 1) {
+        if (count) g_rejected++;
+        return fail(WVC_ERR_UNSUPPORTED, "temporal stride %d: only temporal stride 1 is supported",
+                    d->stride_t);
+    }
+    if (d->groups != 1) {
+        if (count) g_rejected++;
+        return fail(WVC_ERR_UNSUPPORTED, "groups=%d: only one group is supported", d->groups);
+    }
+    const int e = elem_bytes(d->dtype);
+    if (!e) {
+        if (count) g_rejected++;
+        return fail(WVC_ERR_UNSUPPORTED, "dtype %d is neither WVC_F32 nor WVC_BF16", d->dtype);
+    }
+    if (d->n < 1 || d->c_in < 1 || d->c_out < 1 || d->t < 0 || d->h < 1 || d->w < 1)
+        return fail(WVC_ERR_ARG, "bad shape n=%d c_in=%d c_out=%d t=%d h=%d w=%d", d->n, d->c_in,
+                    d->c_out, d->t, d->h, d->w);
+    if (d->kt < 1 || d->kh < 1 || d->kw < 1 || d->stride_h < 1 || d->stride_w < 1 ||
+        d->pad_h < 0 || d->pad_w < 0 || d->dil_t < 1 || d->dil_h < 1 || d->dil_w < 1)
+        return fail(WVC_ERR_ARG, "bad kernel/stride/pad/dilation");
+    const int ho = out_size(d->h, d->kh, d->stride_h, d->pad_h, d->dil_h);
+    const int wo = out_size(d->w, d->kw, d->stride_w, d->pad_w, d->dil_w);
+    if (ho < 1 || wo < 1) return fail(WVC_ERR_ARG, "kernel larger than the padded frame");
+    const long frames = (long)d->dil_t * (d->kt - 1);
+    if (frames > 1024) return fail(WVC_ERR_ARG, "temporal receptive field too large");
+
+    wvc::ConvCall &c = pl->call;
+    std::memset(&c, 0, sizeof(c));
+    c.n = d->n; c.cin = d->c_in; c.cout = d->c_out; c.t = d->t; c.h = d->h; c.w = d->w;
+    c.ho = ho; c.wo = wo;
+    c.kt = d->kt; c.kh = d->kh; c.kw = d->kw;
+    c.sh = d->stride_h; c.sw = d->stride_w; c.ph = d->pad_h; c.pw = d->pad_w;
+    c.dt = d->dil_t; c.dh = d->dil_h; c.dw = d->dil_w;
+    c.frames = (int)frames;
+    c.dtype = d->dtype;
+
+    size_t plane_in, plane_out, v;
+    bool ok = mul_ok((size_t)d->h, (size_t)d->w, &plane_in) && mul_ok(plane_in, d->c_in, &plane_in);
+    ok = ok && mul_ok((size_t)ho, (size_t)wo, &plane_out) && mul_ok(plane_out, d->c_out, &plane_out);
+    ok = ok && mul_ok(plane_in, (size_t)d->n * d->t, &v) && mul_ok(v, e, &pl->x_bytes);
+    ok = ok && mul_ok(plane_in, (size_t)d->n * frames, &v) && mul_ok(v, e, &pl->cache_bytes);
+    ok = ok && mul_ok((size_t)d->c_out * d->c_in, (size_t)d->kt * d->kh * d->kw, &v) &&
+         mul_ok(v, e, &pl->w_bytes);
+    ok = ok && mul_ok(plane_out, (size_t)d->n * d->t, &v) && mul_ok(v, e, &pl->y_bytes);
+    if (!ok) return fail(WVC_ERR_ARG, "tensor size overflows");
+    pl->b_bytes = (size_t)d->c_out * e;
+
+    const bool chan_ok = d->c_in % 8 == 0 && d->c_out % 16 == 0;
+    const bool unit = d->stride_h == 1 && d->stride_w == 1;
+    if (d->dtype == WVC_BF16 && chan_ok && unit && d->kt == 3 && d->kh == 3 && d->kw == 3 &&
+        d->pad_h == 1 && d->pad_w == 1 && d->dil_t == 1 && d->dil_h == 1 && d->dil_w == 1)
+        pl->route = wvc::ConvRoute::Fast3x3x3;
+    else if (d->dtype == WVC_BF16 && chan_ok && unit && d->kt == 1 && d->kh == 1 && d->kw == 1 &&
+             d->pad_h == 0 && d->pad_w == 0)
+        pl->route = wvc::ConvRoute::Fast1x1x1;
+    else
+        pl->route = wvc::ConvRoute::Generic;
+    return WVC_OK;
+}
+
+int hip_status(hipError_t err, const char *what) {
+    if (err == hipSuccess) return WVC_OK;
+    return fail(WVC_ERR_HIP, "%s: %s", what, hipGetErrorString(err));
+}
+
+// Validated conv call shared by wvc_causal_conv3d_fwd and wvc_resblock_fwd.
+int conv_fwd(const wvc_conv3d_desc *d, const void *x, const void *cache_in, void *cache_out,
+             const void *weight, const void *bias, const void *residual, void *y, void *ws,
+             size_t ws_bytes, hipStream_t s) {
+    ConvPlan pl;
+    int rc = plan_conv(d, &pl);
+    if (rc) return rc;
+    if (!weight) return fail(WVC_ERR_ARG, "weight is NULL");
+    if (d->t > 0 && (!x || !y)) return fail(WVC_ERR_ARG, "x or y is NULL");
+    if (pl.call.frames == 0) {
+        cache_in = nullptr;
+        cache_out = nullptr;
+    }
+    if (!ws && ws_bytes) return fail(WVC_ERR_ARG, "workspace is NULL but workspace_bytes > 0");
+
+    // Fast routes read 16-byte vectors; anything not aligned takes the generic route.
+    if (pl.route != wvc::ConvRoute::Generic) {
+        const bool al = aligned(x, 16) && aligned(cache_in, 16) && aligned(weight, 16) &&
+                        aligned(y, 16) && aligned(residual, 16) && aligned(bias, 8);
+        if (!al) pl.route = wvc::ConvRoute::Generic;
+    }
+    size_t need = pl.route == wvc::ConvRoute::Generic ? 0 : wvc::igemm_workspace_bytes(pl.call, pl.route);
+    if (ws_bytes < need)
+        return fail(WVC_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", ws_bytes, need);
+
+    const Buf bufs[] = {
+        {x, pl.x_bytes, false, "x"},
+        {cache_in, pl.cache_bytes, false, "cache_in"},
+        {cache_out, pl.cache_bytes, true, "cache_out"},
+        {weight, pl.w_bytes, false, "weight"},
+        {bias, pl.b_bytes, false, "bias"},
+        {residual, pl.y_bytes, false, "residual"},
+        {y, pl.y_bytes, true, "y"},
+        {ws, ws_bytes, true, "workspace"},
+    };
+    rc = check_aliasing(bufs, 8);
+    if (rc) return rc;
+
+    if (pl.route == wvc::ConvRoute::Generic && strict_on()) {
+        g_rejected++;
+        return fail(WVC_ERR_STRICT, "strict mode: call would take the generic direct route");
+    }
+
+    wvc::ConvCall &c = pl.call;
+    c.x = x;
+    c.cache_in = cache_in;
+    c.weight = weight;
+    c.bias = bias;
+    c.residual = residual;
+    c.y = y;
+    hipError_t err = hipSuccess;
+    if (d->t > 0) {
+        if (pl.route == wvc::ConvRoute::Generic)
+            err = wvc::launch_conv_direct(c, s);
+        else
+            err = wvc::launch_conv_igemm(c, pl.route, ws, ws_bytes, s);
+        if (err != hipSuccess) return hip_status(err, "conv launch");
+    }
+    if (cache_out) {
+        const size_t frame_elems = (size_t)d->h * d->w * d->c_in;
+        err = wvc::launch_cache_update(x, cache_in, cache_out, d->n, d->t, c.frames, frame_elems,
+                                       elem_bytes(d->dtype), s);
+        if (err != hipSuccess) return hip_status(err, "cache update launch");
+    }
+    if (pl.route == wvc::ConvRoute::Fast3x3x3)
+        g_fast3++;
+    else if (pl.route == wvc::ConvRoute::Fast1x1x1)
+        g_fast1++;
+    else
+        g_generic++;
+    return WVC_OK;
+}
+
+int norm_fwd(const void *x, const void *gamma, const void *beta, void *y, int n, int c, int t,
+             int h, int w, int dtype, float eps, int apply_silu, hipStream_t s) {
+    const int e = elem_bytes(dtype);
+    if (!e) return fail(WVC_ERR_UNSUPPORTED, "dtype %d is neither WVC_F32 nor WVC_BF16", dtype);
+    if (n < 1 || c < 1 || t < 0 || h < 1 || w < 1)
+        return fail(WVC_ERR_ARG, "bad shape n=%d c=%d t=%d h=%d w=%d", n, c, t, h, w);
+    if (!(eps > 0.f)) return fail(WVC_ERR_ARG, "eps must be > 0");
+    if (!gamma) return fail(WVC_ERR_ARG, "gamma is NULL");
+    const long positions = (long)n * t * h * w;
+    if (positions > 0 && (!x || !y)) return fail(WVC_ERR_ARG, "x or y is NULL");
+    const size_t bytes = (size_t)positions * c * e;
+    const Buf bufs[] = {{x, bytes, false, "x"},
+                        {y, bytes, true, "y"},
+                        {gamma, (size_t)c * e, false, "gamma"},
+                        {beta, (size_t)c * e, false, "beta"}};
+    int rc = check_aliasing(bufs, 4);
+    if (rc) return rc;
+    return hip_status(wvc::launch_rmsnorm_silu(x, gamma, beta, y, positions, c, dtype, eps,
+                                               apply_silu, s),
+                      "rmsnorm launch");
+}
+
+size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+struct BlockLayout {
+    size_t h1, a1, h2, sc, total;
+};
+
+int plan_block(const wvc_resblock_desc *d, BlockLayout *L) {
+    if (!d) return fail(WVC_ERR_ARG, "resblock descriptor is NULL");
+    const int e = elem_bytes(d->dtype);
+    if (!e) return fail(WVC_ERR_UNSUPPORTED, "dtype %d is neither WVC_F32 nor WVC_BF16", d->dtype);
+    if (d->n < 1 || d->c_in < 1 || d->c_out < 1 || d->t < 0 || d->h < 1 || d->w < 1)
+        return fail(WVC_ERR_ARG, "bad resblock shape");
+    if (!(d->eps > 0.f)) return fail(WVC_ERR_ARG, "eps must be > 0");
+    const size_t pos = (size_t)d->n * d->t * d->h * d->w;
+    L->h1 = 0;
+    L->a1 = align256(pos * d->c_in * e);
+    L->h2 = L->a1 + align256(pos * d->c_out * e);
+    L->sc = L->h2 + align256(pos * d->c_out * e);
+    L->total = L->sc + (d->c_in != d->c_out ? align256(pos * d->c_out * e) : 0);
+    return WVC_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int wvc_causal_conv3d_fwd(const wvc_conv3d_desc *d, const void *x, const void *cache_in,
+                          void *cache_out, const void *weight, const void *bias,
+                          const void *residual, void *y, void *workspace, size_t workspace_bytes,
+                          void *stream) {
+    return conv_fwd(d, x, cache_in, cache_out, weight, bias, residual, y, workspace,
+                    workspace_bytes, static_cast<hipStream_t>(stream));
+}
+
+size_t wvc_causal_conv3d_workspace_bytes(const wvc_conv3d_desc *d) {
+    ConvPlan pl;
+    if (plan_conv(d, &pl, /*count=*/false)) return (size_t)-1;  // a size query is not a call
+    if (pl.route == wvc::ConvRoute::Generic) return 0;
+    return wvc::igemm_workspace_bytes(pl.call, pl.route);
+}
+
+int wvc_conv3d_cache_frames(const wvc_conv3d_desc *d) {
+    if (!d || d->kt < 1 || d->dil_t < 1) return -1;
+    return d->dil_t * (d->kt - 1);
+}
+
+int wvc_rmsnorm_silu(const void *x, const void *gamma, const void *beta, void *y, int n, int c,
+                     int t, int h, int w, int dtype, float eps, int apply_silu, void *stream) {
+    return norm_fwd(x, gamma, beta, y, n, c, t, h, w, dtype, eps, apply_silu,
+                    static_cast<hipStream_t>(stream));
+}
+
+size_t wvc_resblock_workspace_bytes(const wvc_resblock_desc *d) {
+    BlockLayout L;
+    if (plan_block(d, &L)) return (size_t)-1;
+    return L.total;
+}
+
+int wvc_resblock_fwd(const wvc_resblock_desc *d, const void *x, void *y,
+                     const wvc_resblock_params *p, const void *cache1_in, void *cache1_out,
+                     const void *cache2_in, void *cache2_out, void *workspace,
+                     size_t workspace_bytes, void *stream) {
+    BlockLayout L;
+    int rc = plan_block(d, &L);
+    if (rc) return rc;
+    if (!p) return fail(WVC_ERR_ARG, "params is NULL");
+    if (!p->gamma1 || !p->w1 || !p->gamma2 || !p->w2)
+        return fail(WVC_ERR_ARG, "gamma1, w1, gamma2 and w2 are required");
+    const bool proj = d->c_in != d->c_out;
+    if (proj && !p->w_short) return fail(WVC_ERR_ARG, "C_in != C_out needs w_short");
+    if (!proj && p->w_short) return fail(WVC_ERR_ARG, "w_short given but C_in == C_out");
+    if (d->t > 0 && (!x || !y)) return fail(WVC_ERR_ARG, "x or y is NULL");
+    if (workspace_bytes < L.total || (!workspace && L.total))
+        return fail(WVC_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes,
+                    L.total);
+    const int e = elem_bytes(d->dtype);
+    const size_t pos = (size_t)d->n * d->t * d->h * d->w;
+    const size_t plane_in = (size_t)d->n * 2 * d->h * d->w;
+    const Buf bufs[] = {
+        {x, pos * d->c_in * e, false, "x"},
+        {y, pos * d->c_out * e, true, "y"},
+        {cache1_in, plane_in * d->c_in * e, false, "cache1_in"},
+        {cache1_out, plane_in * d->c_in * e, true, "cache1_out"},
+        {cache2_in, plane_in * d->c_out * e, false, "cache2_in"},
+        {cache2_out, plane_in * d->c_out * e, true, "cache2_out"},
+        {workspace, workspace_bytes, true, "workspace"},
+    };
+    rc = check_aliasing(bufs, 7);
+    if (rc) return rc;
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    char *ws = static_cast<char *>(workspace);
+    void *h1 = ws + L.h1, *a1 = ws + L.a1, *h2 = ws + L.h2, *sc = ws + L.sc;
+
+    wvc_conv3d_desc c1{};
+    c1.n = d->n; c1.c_in = d->c_in; c1.c_out = d->c_out; c1.t = d->t; c1.h = d->h; c1.w = d->w;
+    c1.kt = c1.kh = c1.kw = 3;
+    c1.stride_t = c1.stride_h = c1.stride_w = 1;
+    c1.pad_h = c1.pad_w = 1;
+    c1.dil_t = c1.dil_h = c1.dil_w = 1;
+    c1.groups = 1;
+    c1.dtype = d->dtype;
+    wvc_conv3d_desc c2 = c1;
+    c2.c_in = d->c_out;
+
+    // Validate both convs (and strict mode) before enqueueing anything.
+    ConvPlan pl1, pl2;
+    if ((rc = plan_conv(&c1, &pl1)) || (rc = plan_conv(&c2, &pl2))) return rc;
+    if (strict_on() &&
+        (pl1.route == wvc::ConvRoute::Generic || pl2.route == wvc::ConvRoute::Generic)) {
+        g_rejected++;
+        return fail(WVC_ERR_STRICT, "strict mode: a block conv would take the generic route");
+    }
+
+    if ((rc = norm_fwd(x, p->gamma1, p->beta1, h1, d->n, d->c_in, d->t, d->h, d->w, d->dtype,
+                       d->eps, 1, s)))
+        return rc;
+    if ((rc = conv_fwd(&c1, h1, cache1_in, cache1_out, p->w1, p->b1, nullptr, a1, nullptr, 0, s)))
+        return rc;
+    if ((rc = norm_fwd(a1, p->gamma2, p->beta2, h2, d->n, d->c_out, d->t, d->h, d->w, d->dtype,
+                       d->eps, 1, s)))
+        return rc;
+    const void *shortcut = x;
+    if (proj) {
+        wvc_conv3d_desc cs = c1;
+        cs.kt = cs.kh = cs.kw = 1;
+        cs.pad_h = cs.pad_w = 0;
+        if ((rc = conv_fwd(&cs, x, nullptr, nullptr, p->w_short, p->b_short, nullptr, sc, nullptr,
+                           0, s)))
+            return rc;
+        shortcut = sc;
+    }
+    return conv_fwd(&c2, h2, cache2_in, cache2_out, p->w2, p->b2, shortcut, y, nullptr, 0, s);
+}
+
+int wvc_cache_reset(void *cache, size_t bytes, void *stream) {
+    if (bytes == 0) return WVC_OK;
+    if (!cache) return fail(WVC_ERR_ARG, "cache is NULL");
+    if (bytes % 4 != 0 || !aligned(cache, 4))
+        return fail(WVC_ERR_ARG, "cache reset needs 4-byte aligned pointer and size");
+    return hip_status(wvc::launch_fill_zero(cache, bytes, static_cast<hipStream_t>(stream)),
+                      "cache reset launch");
+}
+
+int wvc_upsample_nearest2x(const void *x, void *y, int n, int c, int t, int h, int w, int dtype,
+                           void *stream) {
+    const int e = elem_bytes(dtype);
+    if (!e) return fail(WVC_ERR_UNSUPPORTED, "dtype %d is neither WVC_F32 nor WVC_BF16", dtype);
+    if (n < 1 || c < 1 || t < 0 || h < 1 || w < 1) return fail(WVC_ERR_ARG, "bad upsample shape");
+    const long planes = (long)n * t;
+    if (planes > 0 && (!x || !y)) return fail(WVC_ERR_ARG, "x or y is NULL");
+    const size_t in_bytes = (size_t)planes * h * w * c * e;
+    const Buf bufs[] = {{x, in_bytes, false, "x"}, {y, in_bytes * 4, true, "y"}};
+    int rc = check_aliasing(bufs, 2);
+    if (rc) return rc;
+    return hip_status(
+        wvc::launch_upsample2x(x, y, planes, h, w, c, e, static_cast<hipStream_t>(stream)),
+        "upsample launch");
+}
+
+void wvc_set_strict(int on) { g_strict.store(on ? 1 : 0); }
+int wvc_get_strict(void) { return strict_on(); }
+
+void wvc_get_counters(wvc_counters *out) {
+    if (!out) return;
+    out->fast_3x3x3 = g_fast3.load();
+    out->fast_1x1x1 = g_fast1.load();
+    out->generic = g_generic.load();
+    out->rejected = g_rejected.load();
+}
+
+void wvc_reset_counters(void) {
+    g_fast3 = 0;
+    g_fast1 = 0;
+    g_generic = 0;
+    g_rejected = 0;
+}
+
+const char *wvc_last_error(void) { return g_err; }
+
+const char *wvc_version(void) { return "libwvc 0.1 (gfx950)"; }
+
+}  // extern "C"

@@ -1,0 +1,67 @@
+// wvc_internal.h -- declarations shared by libwvc's own translation units.
+// Nothing here is part of the C ABI (that is include/wvc.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+
+namespace wvc {
+
+// ---------------------------------------------------------------------------
+// bf16 storage helpers (bf16 is carried as raw 16-bit patterns in memory).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+    return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// float -> bf16, round to nearest, ties to even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return static_cast<uint16_t>(u >> 16);
+}
+
+// ---------------------------------------------------------------------------
+// Conv launch description (already validated by the API layer).
+// Tensor layouts are channels-last, see include/wvc.h.
+// ---------------------------------------------------------------------------
+struct ConvCall {
+    const void *x;         // [N][T][H][W][Cin]
+    const void *cache_in;  // [N][F][H][W][Cin] or nullptr (zeros)
+    const void *weight;    // [Cout][kT][kH][kW][Cin]
+    const void *bias;      // [Cout] or nullptr
+    const void *residual;  // [N][T][Ho][Wo][Cout] or nullptr
+    void *y;               // [N][T][Ho][Wo][Cout]
+    int n, cin, cout, t, h, w, ho, wo;
+    int kt, kh, kw, sh, sw, ph, pw, dt, dh, dw;
+    int frames;            // F = dt*(kt-1)
+    int dtype;             // WVC_F32 / WVC_BF16
+};
+
+enum class ConvRoute { Fast3x3x3, Fast1x1x1, Generic };
+
+// MFMA implicit-GEMM route (bf16 only).
+size_t igemm_workspace_bytes(const ConvCall &c, ConvRoute r);
+hipError_t launch_conv_igemm(const ConvCall &c, ConvRoute r, void *ws, size_t ws_bytes,
+                             hipStream_t s);
+// Direct-convolution route (any stride/pad/dilation, fp32 or bf16).
+hipError_t launch_conv_direct(const ConvCall &c, hipStream_t s);
+
+// cache_out = last F frames of concat_T(cache_in, x) (cache_in nullptr = zeros).
+hipError_t launch_cache_update(const void *x, const void *cache_in, void *cache_out, int n,
+                               int t, int frames, size_t frame_elems, int elem_bytes,
+                               hipStream_t s);
+
+hipError_t launch_rmsnorm_silu(const void *x, const void *gamma, const void *beta, void *y,
+                               long positions, int c, int dtype, float eps, int apply_silu,
+                               hipStream_t s);
+
+hipError_t launch_upsample2x(const void *x, void *y, long planes, int h, int w, int c,
+                             int elem_bytes, hipStream_t s);
+
+hipError_t launch_fill_zero(void *p, size_t bytes, hipStream_t s);
+
+}  // namespace wvc
