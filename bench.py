@@ -1,0 +1,369 @@
+"""Benchmark of the causal video-VAE hot path on one MI355X.
+
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+A step is one pass of the whole hot path over one batch of synthetic input:
+
+  resblock_384_60x104 (default): the Wan residual block, C=384, 60x104, 5
+      latent frames fed one frame at a time through the 2-frame caches (caches
+      reset at the start of each step): per frame RMSNorm+SiLU -> causal conv
+      3x3x3 -> RMSNorm+SiLU -> causal conv 3x3x3 + residual, plus the cache
+      updates.
+  layer_384_240x416: causal conv 3x3x3 384->384 over x[1,384,17,240,416]
+      (whole sequence), then the 1x1x1 384->192 projection.
+  layer_96_480x832: RMSNorm+SiLU then causal conv 3x3x3 96->96 over
+      x[1,96,17,480,832] in chunks 1+4+4+4+4 with the cache.
+  decoder_stack_48_30x52: latent[1,48,21,30,52] -> conv_in -> 2 resblocks ->
+      up 2x -> conv -> 2 resblocks, streamed one latent frame at a time.
+
+Prints one JSON line.  ``value`` is the conv throughput of the whole step
+(conv FLOPs counted as 2*M*K*N over all taps, divided by the step time) in
+TFLOP/s; ``ms_per_latent_frame`` is the step time per latent frame.  The
+``roofline`` object covers the dominant kernel (the 3x3x3 conv, or the norm
+where stated), timed live with HIP events on the stream it runs on; the
+``cpu_baseline`` object times the fp64 CPU oracle on a bounded sample.
+Inputs are seeded synthetic tensors already resident in HBM when timing starts.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
+METRIC = "causal Conv3D bf16 TFLOP/s (% MFMA peak) + ms per decoded latent frame"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="resblock_384_60x104",
+                    choices=["resblock_384_60x104", "layer_384_240x416", "layer_96_480x832",
+                             "decoder_stack_48_30x52"])
+    ap.add_argument("--kernel-reps", type=int, default=50,
+                    help="launches of the dominant kernel timed for the roofline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "traffic.json"),
+                    help="measured HBM bytes per launch (from rocprofv3 --pmc), if present")
+    return ap.parse_args()
+
+
+def cl(t):
+    import torch
+    return t.contiguous(memory_format=torch.channels_last_3d)
+
+
+def to_dev(a, dtype=None):
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to("cuda")
+    t = t.to(dtype or torch.bfloat16)
+    return cl(t) if t.dim() == 5 else t
+
+
+def conv_workspace(x, w, padding=(1, 1)):
+    """Zero-filled conv workspace allocated once, outside any timed region."""
+    import torch
+    from video_vae_causal_amd import _lib as L
+    d = L.conv_desc(tuple(x.shape), tuple(w.shape), L.WVC_BF16, padding=padding)
+    need = L.wvc_causal_conv3d_workspace_bytes(d)
+    return torch.zeros(need, dtype=torch.uint8, device="cuda") if need else None
+
+
+def time_region(fn, steps, warmup):
+    """Warm up, then time exactly ``steps`` calls between two events on the
+    current stream, synchronised on both sides.  Returns (ms per call, wall s)."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    w0 = time.perf_counter()
+    start.record()
+    for _ in range(steps):
+        fn()
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    return start.elapsed_time(end) / steps, wall
+
+
+# ---------------------------------------------------------------------------
+# Workloads: each returns (step_fn, info) where info describes FLOPs, frames,
+# the dominant kernel and how to time it alone.
+# ---------------------------------------------------------------------------
+
+def wl_resblock():
+    import torch
+    from video_vae_causal_amd import _lib as L, accounting as acc, inputs, stream
+    r = inputs.resblock_inputs(seed=2)
+    n, c, t, h, w = r["x"].shape
+    x = to_dev(r["x"])
+    p = {k: to_dev(v) for k, v in r["p"].items()}
+    frames = [cl(x[:, :, i:i + 1]) for i in range(t)]
+    out = L.empty_cl(x.shape)
+    outs = [out[:, :, i:i + 1] for i in range(t)]
+    rb = stream.ResBlock(p)
+    rb.start(n, h, w)
+
+    def step():
+        rb.c1.reset()
+        rb.c2.reset()
+        for i in range(t):
+            rb(frames[i], y=outs[i])
+
+    conv_flops = 2 * t * acc.conv_flops(n, 1, h, w, c, c)
+    # dominant kernel alone: the 3x3x3 conv of one 60x104 frame (no cache update)
+    cache = L.empty_cl((n, c, 2, h, w))
+    L.wvc_cache_reset(cache)
+    ky = L.empty_cl((n, c, 1, h, w))
+    kws = conv_workspace(frames[0], p["w1"])
+
+    def kernel():
+        L.wvc_causal_conv3d_fwd(frames[0], p["w1"], p["b1"], cache, None, None, ky, workspace=kws)
+
+    info = dict(workload="resblock_384_60x104", conv_flops=conv_flops, latent_frames=t,
+                config={"workload": "resblock_384_60x104", "channels": c, "frames": t,
+                        "height": h, "width": w, "chunk_frames": 1, "cache_frames": 2,
+                        "batch": n},
+                kernel=kernel, kernel_name="igemm_kernel<3, 96, 16, 2, true>",
+                kernel_units=acc.conv_flops(n, 1, h, w, c, c), kernel_bound="mfma",
+                kernel_bytes=acc.conv_launch_bytes(n, 1, h, w, c, c))
+    return step, info
+
+
+def wl_layer384():
+    import torch
+    from video_vae_causal_amd import _lib as L, accounting as acc, inputs
+    d = inputs.layer384_inputs()
+    n, c, t, h, w = d["x"].shape
+    x, wt, b = to_dev(d["x"]), to_dev(d["w"]), to_dev(d["b"])
+    wp, bp = to_dev(d["wp"]), to_dev(d["bp"])
+    y = L.empty_cl((n, c, t, h, w))
+    proj = L.empty_cl((n, wp.shape[0], t, h, w))
+
+    ws3 = conv_workspace(x, wt)
+    ws1 = conv_workspace(y, wp, padding=(0, 0))
+
+    def step():
+        L.wvc_causal_conv3d_fwd(x, wt, b, y=y, workspace=ws3)
+        L.wvc_causal_conv3d_fwd(y, wp, bp, y=proj, padding=(0, 0), workspace=ws1)
+
+    f3 = acc.conv_flops(n, t, h, w, c, c)
+    f1 = acc.conv_flops(n, t, h, w, c, wp.shape[0], (1, 1, 1))
+
+    def kernel():
+        L.wvc_causal_conv3d_fwd(x, wt, b, y=y, workspace=ws3)
+
+    info = dict(workload="layer_384_240x416", conv_flops=f3 + f1, latent_frames=t,
+                config={"workload": "layer_384_240x416", "channels": c, "frames": t,
+                        "height": h, "width": w, "chunk_frames": t, "projection_out": int(wp.shape[0]),
+                        "batch": n},
+                kernel=kernel, kernel_name="igemm_kernel<3, 128, 32, 2, false>", kernel_units=f3,
+                kernel_bound="mfma", kernel_bytes=acc.conv_launch_bytes(n, t, h, w, c, c, cache_frames=0))
+    return step, info
+
+
+def wl_layer96():
+    import torch
+    from video_vae_causal_amd import _lib as L, accounting as acc, inputs
+    d = inputs.layer96_inputs()
+    n, c, t, h, w = d["x"].shape
+    x, g, wt, b = to_dev(d["x"]), to_dev(d["gamma"]), to_dev(d["w"]), to_dev(d["b"])
+    hbuf = L.empty_cl(x.shape)
+    y = L.empty_cl(x.shape)
+    caches = [L.empty_cl((n, c, 2, h, w)) for _ in range(2)]
+    sizes = [1, 4, 4, 4, 4]
+    starts = np.cumsum([0] + sizes[:-1])
+    hs = [cl(hbuf[:, :, s:s + k]) for s, k in zip(starts, sizes)]
+    ys = [y[:, :, s:s + k] for s, k in zip(starts, sizes)]
+
+    wss = [conv_workspace(hs[i], wt) for i in range(len(sizes))]
+
+    def step():
+        L.wvc_rmsnorm_silu(x, g, y=hbuf)
+        L.wvc_cache_reset(caches[0])
+        for i in range(len(sizes)):
+            L.wvc_causal_conv3d_fwd(hs[i], wt, b, caches[i % 2], caches[(i + 1) % 2], y=ys[i],
+                                    workspace=wss[i])
+
+    conv_flops = acc.conv_flops(n, t, h, w, c, c)
+
+    def kernel():
+        L.wvc_causal_conv3d_fwd(hs[1], wt, b, caches[0], None, None, ys[1], workspace=wss[1])
+
+    def norm_kernel():
+        L.wvc_rmsnorm_silu(x, g, y=hbuf)
+
+    info = dict(workload="layer_96_480x832", conv_flops=conv_flops, latent_frames=t,
+                config={"workload": "layer_96_480x832", "channels": c, "frames": t,
+                        "height": h, "width": w, "chunks": sizes, "batch": n},
+                kernel=kernel, kernel_name="igemm_kernel<3, 96, 16, 2, false>",
+                kernel_units=acc.conv_flops(n, 4, h, w, c, c), kernel_bound="mfma",
+                kernel_bytes=acc.conv_launch_bytes(n, 4, h, w, c, c),
+                norm_kernel=norm_kernel, norm_bytes=acc.norm_bytes(n * c * t * h * w))
+    return step, info
+
+
+def wl_decoder():
+    import torch
+    from video_vae_causal_amd import _lib as L, accounting as acc, inputs, stream
+    d = inputs.decoder_inputs(seed=5)
+    n, cl_, t, h, w = d["latent"].shape
+    width = d["p"]["w_in"].shape[0]
+    lat = to_dev(d["latent"])
+    p = {k: ({kk: to_dev(vv) for kk, vv in v.items()} if isinstance(v, dict) else to_dev(v))
+         for k, v in d["p"].items()}
+    frames = [cl(lat[:, :, i:i + 1]) for i in range(t)]
+    stack = stream.DecoderStack(p)
+    stack.start(n, h, w)
+    out = L.empty_cl((n, width, t, 2 * h, 2 * w))
+    outs = [out[:, :, i:i + 1] for i in range(t)]
+
+    def step():
+        stack.start(n, h, w)
+        for i in range(t):
+            stack.chunk(frames[i], out=outs[i])
+
+    per_frame = (acc.conv_flops(n, 1, h, w, cl_, width) + 4 * acc.conv_flops(n, 1, h, w, width, width)
+                 + 5 * acc.conv_flops(n, 1, 2 * h, 2 * w, width, width))
+    cache = L.empty_cl((n, width, 2, 2 * h, 2 * w))
+    L.wvc_cache_reset(cache)
+    kx = cl(torch.randn((n, width, 1, 2 * h, 2 * w), device="cuda").to(torch.bfloat16))
+    ky = L.empty_cl((n, width, 1, 2 * h, 2 * w))
+
+    kws = conv_workspace(kx, p["w_up"])
+
+    def kernel():
+        L.wvc_causal_conv3d_fwd(kx, p["w_up"], p["b_up"], cache, None, None, ky, workspace=kws)
+
+    info = dict(workload="decoder_stack_48_30x52", conv_flops=per_frame * t, latent_frames=t,
+                config={"workload": "decoder_stack_48_30x52", "latent_channels": cl_, "channels": width,
+                        "frames": t, "height": h, "width": w, "chunk_frames": 1, "batch": n},
+                kernel=kernel, kernel_name="igemm_kernel<3, 96, 16, 2, true>",
+                kernel_units=acc.conv_flops(n, 1, 2 * h, 2 * w, width, width), kernel_bound="mfma",
+                kernel_bytes=acc.conv_launch_bytes(n, 1, 2 * h, 2 * w, width, width))
+    return step, info
+
+
+WORKLOADS = {"resblock_384_60x104": wl_resblock, "layer_384_240x416": wl_layer384,
+             "layer_96_480x832": wl_layer96, "decoder_stack_48_30x52": wl_decoder}
+
+
+# ---------------------------------------------------------------------------
+# CPU baseline: the fp64 oracle on a bounded sample of the same workload.
+# ---------------------------------------------------------------------------
+
+def cpu_baseline(workload: str):
+    import oracle
+    from video_vae_causal_amd import accounting as acc, inputs
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    if workload == "decoder_stack_48_30x52":
+        d = inputs.decoder_inputs(seed=5)
+        lat = d["latent"][:, :, :1].astype(np.float64)
+        p = {k: ({kk: vv.astype(np.float64) for kk, vv in v.items()} if isinstance(v, dict)
+                 else v.astype(np.float64)) for k, v in d["p"].items()}
+        n, cl_, t, h, w = lat.shape
+        width = p["w_in"].shape[0]
+        flops = (acc.conv_flops(n, 1, h, w, cl_, width) + 4 * acc.conv_flops(n, 1, h, w, width, width)
+                 + 5 * acc.conv_flops(n, 1, 2 * h, 2 * w, width, width))
+        t0 = time.perf_counter()
+        oracle.decoder_stack(lat, p, bf16=True)
+        dt = time.perf_counter() - t0
+        sample = "latent frame 0 of 21 through the whole stack (bf16-boundary oracle)"
+    elif workload == "resblock_384_60x104":
+        r = inputs.resblock_inputs(seed=2)
+        x = r["x"][:, :, 2:3].astype(np.float64)
+        p = {k: v.astype(np.float64) for k, v in r["p"].items()}
+        n, c, _, h, w = x.shape
+        past = r["x"][:, :, 0:2].astype(np.float64)   # non-zero caches: every tap is computed
+        flops = 2 * acc.conv_flops(n, 1, h, w, c, c)
+        t0 = time.perf_counter()
+        oracle.resblock(x, p, past, past, bf16=True)
+        dt = time.perf_counter() - t0
+        sample = "1 of 5 latent frames (frame 2, non-zero caches) through the block"
+    else:
+        d = inputs.layer384_inputs() if workload == "layer_384_240x416" else inputs.layer96_inputs()
+        x = d["x"][:, :, :3]
+        n, c, _, h, w = x.shape
+        rows = 24 if c == 384 else 48
+        xs = x[:, :, :, :rows].astype(np.float64)    # frames 0..2, first rows of the frame
+        past = np.zeros((n, c, 2, rows, w))
+        flops = acc.conv_flops(n, 3, rows, w, c, c)
+        t0 = time.perf_counter()
+        oracle.causal_conv3d(xs, d["w"].astype(np.float64), d["b"].astype(np.float64), cache=past)
+        dt = time.perf_counter() - t0
+        sample = f"frames 0-2, rows 0-{rows - 1} of the 3x3x3 conv"
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": sample, "seconds": round(dt, 3), "flops": flops}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported "
+              "(the path has no multi-GPU sharding in this build)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from video_vae_causal_amd import _lib as L
+    L.load()
+    torch.cuda.set_device(0)
+
+    step, info = WORKLOADS[args.workload]()
+    ms_step, wall = time_region(step, args.steps, args.warmup)
+    value = info["conv_flops"] / (ms_step * 1e-3) / 1e12
+
+    # dominant kernel, timed alone with events on the stream it is launched on
+    k_ms, _ = time_region(info["kernel"], args.kernel_reps, 3)
+    achieved = info["kernel_units"] / (k_ms * 1e-3) / 1e12
+    traffic = None
+    if os.path.exists(args.traffic_json):
+        try:
+            tj = json.load(open(args.traffic_json))
+            entry = tj.get(args.workload)
+            if entry and entry.get("kernel") == info["kernel_name"]:
+                traffic = entry.get("bytes_per_launch")
+        except (OSError, ValueError):
+            traffic = None
+    roofline = {"bound": info["kernel_bound"], "achieved": round(achieved, 2),
+                "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": traffic,
+                "kernel": info["kernel_name"], "kernel_ms": round(k_ms, 5),
+                "flops_per_launch": info["kernel_units"],
+                "algorithmic_bytes_per_launch": info["kernel_bytes"]}
+
+    line = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded Philox normals, random-init weights)",
+        "config": info["config"],
+        "pct_mfma_peak": round(100 * value / MFMA_BF16_PEAK_TFLOPS, 2),
+        "ms_per_latent_frame": round(ms_step / info["latent_frames"], 4),
+        "conv_flops_per_step": info["conv_flops"],
+        "wall_s_timed": round(wall, 3),
+        "roofline": roofline,
+    }
+    if "norm_kernel" in info:
+        n_ms, _ = time_region(info["norm_kernel"], 20, 3)
+        gbs = info["norm_bytes"] / (n_ms * 1e-3) / 1e9
+        line["roofline_norm"] = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                                 "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                                 "traffic": None, "kernel": "rmsnorm_vec_kernel",
+                                 "kernel_ms": round(n_ms, 5), "bytes_per_launch": info["norm_bytes"]}
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(args.workload)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

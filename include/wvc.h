@@ -98,10 +98,17 @@ typedef struct wvc_counters {
  *   y         [N, C_out, t, h_out, w_out] written
  *   workspace / workspace_bytes: scratch of at least
  *             wvc_causal_conv3d_workspace_bytes(d) bytes (may be NULL if 0).
+ *             It holds split-K partial sums and per-tile arrival counters:
+ *             it must be zero-filled before its first use (wvc_cache_reset
+ *             does that), and every successful call leaves it ready for the
+ *             next one.  Calls that share a workspace must not overlap in
+ *             time (use one stream, or one workspace per stream).
  *
- * Routes: bf16 3x3x3 / stride 1 / pad 1 / dilation 1 with C_in % 8 == 0 and
- * C_out % 16 == 0 takes the MFMA implicit-GEMM kernel; bf16 1x1x1 / stride 1 /
- * pad 0 with the same channel rules takes the MFMA projection kernel; every
+ * Routes: bf16 3x3x3 / stride 1 / pad 1 / dilation 1 with C_in % 8 == 0,
+ * C_out % 32 == 0 and 16-byte aligned tensors takes the MFMA implicit-GEMM
+ * kernel (which also writes cache_out, in the same pass); bf16 1x1x1 /
+ * stride 1 / pad 0 with the same channel rules takes the MFMA projection
+ * kernel; every
  * other legal call takes the direct-convolution route (counted as generic,
  * refused with WVC_ERR_STRICT in strict mode).  stride_t != 1 or groups != 1
  * is WVC_ERR_UNSUPPORTED ([P3]: the fast path covers 5-D tensors, unit
@@ -165,8 +172,10 @@ typedef struct wvc_resblock_params {
  * ones receive the last 2 frames of concat(cache_in, h) and may be NULL.
  * The residual is added in conv2's epilogue, before the single rounding.
  *   x [N, C_in, t, H, W] read; y [N, C_out, t, H, W] written.
- * Workspace: wvc_resblock_workspace_bytes(d) bytes (intermediates h1, a1, h2
- * and the shortcut output); it may not overlap any other buffer.
+ * Workspace: wvc_resblock_workspace_bytes(d) bytes (intermediates h1, a1, h2,
+ * the shortcut output and the convs' scratch); it may not overlap any other
+ * buffer, and like the conv workspace it must be zero-filled before its first
+ * use and is left ready for the next call.
  */
 int wvc_resblock_fwd(const wvc_resblock_desc *d, const void *x, void *y,
                      const wvc_resblock_params *p, const void *cache1_in, void *cache1_out,

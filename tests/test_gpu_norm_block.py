@@ -106,9 +106,24 @@ def test_resblock_384_60x104_five_frames_one_at_a_time():
     exact, _, _ = oracle.resblock(f64(r["x"]), block_params_f64(r["p"]), bf16=False)
     print(f"[parity] resblock 384 distance to pure fp64 chain: rel_l2={oracle.rel_l2(yh, exact):.3e}",
           flush=True)
-    # whole sequence at once equals the frame-by-frame stream bitwise
+    # whole sequence at once agrees with the frame-by-frame stream (the two
+    # launch shapes may split K differently, so the bar is the parity bar)
     yw, _ = run_block_stream(xd, block_params_dev(r["p"]), [5])
-    assert torch.equal(yw, y)
+    check_bf16(to_host(yw), yh, "resblock 384 whole vs streamed")
+
+
+def test_resblock_mixed_chunk_lengths_share_one_workspace():
+    """Chunks of different lengths through one block (one workspace): at 384
+    channels and 30x52 a 4-frame chunk runs unsplit while a 1-frame chunk
+    splits K, so the workspace's split-K counters must survive the longer
+    chunk's activations.  Regression test for a layout that placed them after
+    the chunk-length-dependent intermediates."""
+    r = inputs.resblock_inputs(seed=31, shape=(1, 384, 8, 30, 52))
+    xd = to_dev(r["x"])
+    ref, _, _ = oracle.resblock(f64(r["x"]), block_params_f64(r["p"]), bf16=True)
+    for sizes in ([4, 1, 2, 1], [1, 4, 1, 2], [1, 1, 4, 2]):
+        y, _ = run_block_stream(xd, block_params_dev(r["p"]), sizes)
+        check_bf16(to_host(y), ref, f"resblock 384 30x52 chunks {sizes}")
 
 
 def test_resblock_checkpoint_resume_bitwise():
@@ -154,7 +169,8 @@ def test_decoder_stack_full_width_two_frames_vs_oracle():
 
 def test_decoder_stack_21_frames_chunking_invariant():
     """All 21 latent frames: frame-by-frame streaming, 4-frame chunks and one
-    whole-sequence pass agree bitwise, and two runs are bitwise equal."""
+    whole-sequence pass agree (parity bar: chunk lengths may change the split-K
+    grouping), and two runs of the same chunking are bitwise equal."""
     d = inputs.decoder_inputs(seed=5)
     pd = stack_dev(d["p"])
     lat = to_dev(d["latent"])
@@ -163,5 +179,7 @@ def test_decoder_stack_21_frames_chunking_invariant():
     b = stream.DecoderStack(pd).run(lat, chunk_frames=4)
     c = stream.DecoderStack(pd).run(lat, chunk_frames=21)
     a2 = stream.DecoderStack(pd).run(lat, chunk_frames=1)
-    assert torch.equal(a, b) and torch.equal(a, c) and torch.equal(a, a2)
+    assert torch.equal(a, a2)
     assert torch.isfinite(a.float()).all()
+    check_bf16(to_host(b), to_host(a), "decoder 4-frame chunks vs frame by frame")
+    check_bf16(to_host(c), to_host(a), "decoder whole vs frame by frame")

@@ -11,28 +11,48 @@
 // GEMM view (same page, Conv3D as GEMM): rows = output channels (MFMA A
 // operand = weights, K contiguous in the channels-last weight layout),
 // columns = output positions (MFMA B operand = input patches), K = 27 taps x
-// C_in.  Nothing is materialised: the patch matrix is read straight out of a
-// spatial halo tile held in LDS.
+// C_in.  Nothing is materialised: the patch matrix is read out of a spatial
+// halo tile held in LDS.
 //
 // Work decomposition
-//   workgroup : 256 threads (4 waves), CO_T output channels x POS_T output
-//               positions of one output frame; positions form a TH x TW
-//               spatial tile chosen by the host (TH*TW == POS_T).
-//   K loop    : over 32-channel blocks of C_in.  Per block the halo of the
-//               three input frames t-2, t-1, t (cache or chunk) is staged in
-//               LDS as [frame][k-group(4)][(TH+2)(TW+2)][8 channels], 16 B per
-//               entry, so the 16 lanes of one k-group read 16 neighbouring
-//               positions as one contiguous run.  The 27 taps then read their
-//               B fragments from the same tile at a shifted offset: the
-//               temporal taps are accumulated in registers, never as
-//               per-slice batches.
-//   waves     : 2 (channels) x 2 (positions); a wave owns CO_T/2 x POS_T/2
-//               outputs as 16x16 MFMA tiles (v_mfma_f32_16x16x32_bf16).
+//   workgroup : 256 threads (4 waves), CO_T output channels x 256 output
+//               positions of one output frame; the positions form a TH x TW
+//               spatial tile chosen by the host (TH*TW == 256).
+//   K loop    : over work units (kt, 32-channel block).  A unit stages the
+//               halo of ONE input frame (t-2+kt: cache or chunk) for 32 input
+//               channels in LDS as [k-group(4)][(TH+2)(TW+2)][8 channels]
+//               (16 B entries, so the 16 lanes of one k-group read 16
+//               neighbouring positions as one contiguous run), then runs its
+//               9 spatial taps, each reading its B fragments from the same tile
+//               at a shifted offset.  The three temporal taps accumulate into
+//               the same registers: no per-slice batches exist.
+//   waves     : 2 (channels) x 2 (positions); a wave owns CO_T/2 x 128 outputs
+//               as 16x16 MFMA tiles (v_mfma_f32_16x16x32_bf16).  Within a unit
+//               the A (weights, global) and B (LDS) fragments of tap k+1 are
+//               fetched while the MFMAs of tap k run (register ping-pong).
+//               Two workgroups share a CU, so one stages while the other
+//               computes.
+//   loads     : buffer loads with the frame as the buffer range: positions
+//               outside the frame and channels past C_in read as zero in
+//               hardware, so staging has no branches.
+//   split-K   : small grids (one 60x104 or 30x52 frame) split the units of a
+//               tile over S workgroups.  Each writes fp32 partials in MFMA
+//               fragment order; the last to arrive (atomic counter) sums the S
+//               partials in split order -- deterministic, no float atomics --
+//               and runs the epilogue, then re-arms the counter for the next
+//               call.  Counters sit at a fixed offset (the workspace's first
+//               CTR_CAP words), partials after them.
 //   epilogue  : + bias, + residual (fused block shortcut), one rounding to
 //               bf16, 8-byte stores of 4 consecutive channels.
+//   cache     : the workgroups of the chunk's last output frame (channel tile
+//               0) also write the interior of the halos they stage for frames
+//               T-2 and T-1 to cache_out: the rolling cache update costs no
+//               extra pass over the frames.
 //   mapping   : workgroup ids are remapped so each XCD (own L2) receives a
-//               contiguous run of tiles: the channel tiles of one spatial tile
-//               and its neighbours share the halo in that XCD's L2.
+//               contiguous run of tiles: splits and channel tiles of one
+//               spatial tile, then its neighbours, share that XCD's L2.
+#include <type_traits>
+
 #include "wvc_internal.h"
 #include "wvc.h"
 
@@ -41,6 +61,16 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int POS_T = 256;
+// Split-K arrival counters live at a fixed place -- the first CTR_CAP words of
+// the workspace -- so that a workspace reused by calls of different shapes
+// never finds partial sums where a later call expects a zeroed counter.
+constexpr int CTR_CAP = 4096;
+constexpr size_t CTR_BYTES = CTR_CAP * sizeof(uint32_t);
+constexpr uint32_t OOB = 0x80000000u;  // an offset past every buffer range used here
+constexpr int RSRC_WORD3 = 0x00020000;  // raw buffer, range-checked (CDNA data format)
 
 struct IgParams {
     const uint16_t *x;
@@ -49,10 +79,16 @@ struct IgParams {
     const uint16_t *bias;
     const uint16_t *res;
     uint16_t *y;
+    uint16_t *cache_out;
+    float *part;
+    uint32_t *ctr;
     int T, H, W, Cin, Cout, F;
     int TH, TW, HC, HP;
     int tiles_w, tiles_h, co_tiles;
+    int S, U;
     int total;
+    int co_major;  // channel tile slowest in the workgroup order (small grids)
+    uint32_t frame_bytes, w_bytes;
 };
 
 __device__ __forceinline__ int xcd_remap(int bid, int total) {
@@ -65,27 +101,103 @@ __device__ __forceinline__ int xcd_remap(int bid, int total) {
     return start + local;
 }
 
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
+                                             RSRC_WORD3);
+}
+
+__device__ __forceinline__ uint4 bload(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
 
-template <int KS, int CO_T, int POS_T, int HP_MAX>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) igemm_kernel(IgParams p) {
-    constexpr int KT = KS;
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// MFMA shapes used here: M x M output tiles, 512/M deep in K.
+template <int M>
+struct Mfma;
+template <>
+struct Mfma<16> {
+    typedef f32x4 acc_t;
+    static constexpr int ACC = 4;
+    __device__ static acc_t run(bf16x8 a, bf16x8 b, acc_t c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+    }
+};
+template <>
+struct Mfma<32> {
+    typedef f32x16 acc_t;
+    static constexpr int ACC = 16;
+    __device__ static acc_t run(bf16x8 a, bf16x8 b, acc_t c) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+    }
+};
+
+template <int N>
+using Int = std::integral_constant<int, N>;
+
+// One workgroup = 256 threads = 4 waves laid out WAVES_CO (channels) x
+// 4/WAVES_CO (positions).  M is the MFMA tile edge (16: 16x16x32, 32: 32x32x16).
+//
+// Pipeline (one workgroup per CU, up to 512 registers per lane):
+//   * a stage is one work unit (kt, 32-channel block); its halo tile lives in
+//     one half of a double-buffered LDS array.  The next stage's halo is loaded
+//     into registers while the current stage computes and is written to the
+//     other half at the end of the stage, followed by one barrier.
+//   * a row is one kernel row kh of a stage: KS taps.  The weights (A
+//     fragments) of a whole row are fetched as one batch two rows ahead into
+//     one of three register sets (row r uses set r % 3).
+//   * the input patches (B fragments) of tap k+1 are read from LDS right after
+//     the last MFMA of tap k that used the same registers.
+//   Global loads complete in issue order, so the issue order (row batch, then
+//   the next halo) is chosen such that every wait covers only loads issued at
+//   least one full row earlier.
+template <int KS, int CO_T, int M, int WAVES_CO, bool SPLIT>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+igemm_kernel(IgParams p) {
+    using MF = Mfma<M>;
+    using acc_t = typename MF::acc_t;
+    constexpr int ACC = MF::ACC;
     constexpr int TAPS = KS * KS * KS;
     constexpr int PAD = KS / 2;
-    constexpr int WCO = CO_T / 2, WPOS = POS_T / 2;
-    constexpr int FCO = WCO / 16, FPOS = WPOS / 16;
-    static_assert(WCO % 16 == 0 && WPOS % 16 == 0, "wave tile must be whole 16x16 MFMA tiles");
+    constexpr int HPM = KS == 3 ? 340 : 256;
+    constexpr int NIT = (4 * HPM + 255) / 256;
+    constexpr int WAVES_POS = 4 / WAVES_CO;
+    constexpr int WCO = CO_T / WAVES_CO, WPOS = POS_T / WAVES_POS;
+    constexpr int FCO = WCO / M, FPOS = WPOS / M;
+    constexpr int KSTEPS = M / 16;  // MFMA K-steps per 32-channel block
+    constexpr int GPL = 64 / M;     // 8-channel groups spanned by one K-step
+    static_assert(WCO % M == 0 && WPOS % M == 0, "wave tile must be whole MFMA tiles");
+    static_assert(NIT <= 32, "staging mask");
 
-    __shared__ uint4 halo[KT * 4 * HP_MAX];
+    __shared__ uint4 halo[2][4 * HPM];
+    __shared__ int s_last;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
-    const int wco = wave & 1, wpos = wave >> 1;
-    const int kg = lane >> 4, l16 = lane & 15;
+    const int wco = wave % WAVES_CO, wpos = wave / WAVES_CO;
+    const int lr = lane % M;  // A row / B column of this lane inside an MFMA tile
+    const int lg = lane / M;  // 8-channel group of this lane inside a K-step
+    const int g = tid & 3;    // staging: 8-channel group
 
     int L = xcd_remap(blockIdx.x, p.total);
-    const int co_tile = L % p.co_tiles;
-    L /= p.co_tiles;
+    const int s = SPLIT ? L % p.S : 0;
+    if (SPLIT) L /= p.S;
+    const int tile_id = L;
+    // Order of the logical tiles: channel tile fastest (large grids: the tiles
+    // of one spatial block share its halo in L2) or slowest (small grids: each
+    // XCD then works on one channel tile, so its weight slice stays in L2).
+    int ct;
+    if (p.co_major) {
+        const int per_ct = (int)(p.total / p.S) / p.co_tiles;
+        ct = L / per_ct;
+        L -= ct * per_ct;
+    } else {
+        ct = L % p.co_tiles;
+        L /= p.co_tiles;
+    }
     const int tw = L % p.tiles_w;
     L /= p.tiles_w;
     const int th = L % p.tiles_h;
@@ -93,199 +205,434 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) i
     const int t = L % p.T;
     const int n = L / p.T;
     const int h0 = th * p.TH, w0 = tw * p.TW;
-    const int co0 = co_tile * CO_T + wco * WCO;
+    const int co0 = ct * CO_T + wco * WCO;
+    const int u0 = SPLIT ? (s * p.U) / p.S : 0;
+    const int u1 = SPLIT ? ((s + 1) * p.U) / p.S : p.U;
 
-    // LDS entry (in 16-byte units) of this lane's B-fragment positions at tap (0,0,0).
+    // Staging: item k of this thread is halo position (tid>>2) + 64k, group g;
+    // its LDS entry is lbase + 64k when (tid>>2) + 64k < HP.
+    uint32_t soff[NIT];  // byte offset of the 16-byte chunk inside a frame, or OOB
+    uint32_t interior = 0, lvalid = 0;
+    const int lbase = g * p.HP + (tid >> 2);
+#pragma unroll
+    for (int k = 0; k < NIT; ++k) {
+        const int hp = (tid >> 2) + 64 * k;
+        const bool valid = hp < p.HP;
+        const int r = hp / p.HC, c = hp - r * p.HC;
+        const int hs = h0 + r - PAD, ws = w0 + c - PAD;
+        const bool inframe = valid && hs >= 0 && hs < p.H && ws >= 0 && ws < p.W;
+        soff[k] = inframe ? (uint32_t)(((hs * p.W + ws) * p.Cin + g * 8) * 2) : OOB;
+        if (valid) lvalid |= 1u << k;
+        if (inframe && r >= PAD && r < PAD + p.TH && c >= PAD && c < PAD + p.TW) interior |= 1u << k;
+    }
+    // B fragments: LDS entry of this lane's position at spatial tap (0,0),
+    // K-step 0; K-step ks adds ks*GPL*HP.
     int boff[FPOS];
 #pragma unroll
     for (int f = 0; f < FPOS; ++f) {
-        const int q = wpos * WPOS + f * 16 + l16;
+        const int q = wpos * WPOS + f * M + lr;
         const int r = q / p.TW, c = q - r * p.TW;
-        boff[f] = kg * p.HP + r * p.HC + c;
+        boff[f] = lg * p.HP + r * p.HC + c;
     }
-    // This lane's weight rows (A fragments): channel co, k-group kg.
-    const uint16_t *wrow[FCO];
-    bool wok[FCO];
+    // A fragments: byte offset of (channel co, tap 0, input channel 8*lg).
+    uint32_t aoff[FCO];
 #pragma unroll
-    for (int f = 0; f < FCO; ++f) {
-        const int co = co0 + f * 16 + l16;
-        wok[f] = co < p.Cout;
-        wrow[f] = p.w + (size_t)(wok[f] ? co : 0) * TAPS * p.Cin + kg * 8;
-    }
+    for (int f = 0; f < FCO; ++f)
+        aoff[f] = (uint32_t)(((co0 + f * M + lr) * TAPS * p.Cin + lg * 8) * 2);
+    const __amdgpu_buffer_rsrc_t wr = rsrc(p.w, p.w_bytes);
+    const size_t frame_elems = (size_t)p.frame_bytes / 2;
+    const bool write_cache = KS == 3 && p.cache_out != nullptr && t == p.T - 1 && ct == 0;
 
-    f32x4 acc[FCO][FPOS];
+    acc_t acc[FCO][FPOS];
 #pragma unroll
     for (int i = 0; i < FCO; ++i)
 #pragma unroll
-        for (int j = 0; j < FPOS; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < FPOS; ++j)
+#pragma unroll
+            for (int e = 0; e < ACC; ++e) acc[i][j][e] = 0.f;
 
-    const size_t row_elems = (size_t)p.W * p.Cin;
-    const size_t frame_elems = (size_t)p.H * row_elems;
-    const int items = KT * p.HP * 4;
+    bf16x8 A[3][KS][FCO][KSTEPS];  // three row sets: [set][kw][co tile][K-step]
+    bf16x8 B[2][FPOS][KSTEPS];     // two tap sets: tap k reads B[k & 1]
+    uint4 hv[NIT];
 
-    for (int cb = 0; cb < p.Cin; cb += 32) {
-        __syncthreads();  // every wave is done reading the previous block
-        for (int it = tid; it < items; it += 256) {
-            const int g = it & 3;
-            const int pi = it >> 2;
-            const int fr = pi / p.HP;
-            const int hp = pi - fr * p.HP;
-            const int r = hp / p.HC;
-            const int c = hp - r * p.HC;
-            const int hs = h0 + r - PAD, ws = w0 + c - PAD;
-            const int ts = t - (KT - 1) + fr;
-            const int ci = cb + g * 8;
-            uint4 v = make_uint4(0u, 0u, 0u, 0u);
-            if (hs >= 0 && hs < p.H && ws >= 0 && ws < p.W && ci < p.Cin) {
-                const uint16_t *src = nullptr;
-                const size_t off = (size_t)hs * row_elems + (size_t)ws * p.Cin + ci;
-                if (ts >= 0)
-                    src = p.x + (size_t)(n * p.T + ts) * frame_elems + off;
-                else if (p.cache)
-                    src = p.cache + (size_t)(n * p.F + p.F + ts) * frame_elems + off;
-                if (src) v = *reinterpret_cast<const uint4 *>(src);
+    auto load_row = [&](auto set_tag, int rho) {
+        constexpr int SET = decltype(set_tag)::value;
+        const int u = u0 + rho / KS, kh = rho % KS;
+        const int kt = u % KS, cb = (u / KS) * 32;
+#pragma unroll
+        for (int kw = 0; kw < KS; ++kw) {
+            const int tap = (kt * KS + kh) * KS + kw;
+#pragma unroll
+            for (int ks = 0; ks < KSTEPS; ++ks) {
+                const int ch = cb + ks * GPL * 8;
+                const bool ok = ch + lg * 8 < p.Cin;
+                const uint32_t o = (uint32_t)(tap * p.Cin + ch) * 2;
+#pragma unroll
+                for (int f = 0; f < FCO; ++f)
+                    A[SET][kw][f][ks] = as_bf16x8(bload(wr, ok ? aoff[f] + o : OOB));
             }
-            halo[(fr * 4 + g) * p.HP + hp] = v;
         }
+    };
+    auto load_halo = [&](int u) {
+        const int kt = u % KS, cb = (u / KS) * 32;
+        const int ts = t - (KS - 1) + kt;
+        __amdgpu_buffer_rsrc_t fr;
+        if (ts >= 0)
+            fr = rsrc(p.x + (size_t)(n * p.T + ts) * frame_elems, p.frame_bytes);
+        else if (p.cache)
+            fr = rsrc(p.cache + (size_t)(n * p.F + p.F + ts) * frame_elems, p.frame_bytes);
+        else
+            fr = rsrc(p.x, 0u);  // zero causal padding: every load reads zero
+        const bool gok = cb + g * 8 < p.Cin;
+#pragma unroll
+        for (int k = 0; k < NIT; ++k)
+            hv[k] = bload(fr, (gok && soff[k] != OOB) ? soff[k] + (uint32_t)cb * 2 : OOB);
+    };
+    auto store_halo = [&](int u, int buf) {
+#pragma unroll
+        for (int k = 0; k < NIT; ++k)
+            if (lvalid & (1u << k)) halo[buf][lbase + 64 * k] = hv[k];
+        const int kt = u % KS, cb = (u / KS) * 32;
+        if (write_cache && kt >= 1 && cb + g * 8 < p.Cin) {
+            uint16_t *dst = p.cache_out + (size_t)(n * 2 + kt - 1) * frame_elems + cb;
+#pragma unroll
+            for (int k = 0; k < NIT; ++k)
+                if (interior & (1u << k))
+                    *reinterpret_cast<uint4 *>(reinterpret_cast<char *>(dst) + soff[k]) = hv[k];
+        }
+    };
+    auto load_b = [&](auto set_tag, int buf, int j, int kh, int kw) {
+        constexpr int BS = decltype(set_tag)::value;
+        const int toff = kh * p.HC + kw;
+#pragma unroll
+        for (int ks = 0; ks < KSTEPS; ++ks)
+            B[BS][j][ks] = as_bf16x8(halo[buf][boff[j] + ks * GPL * p.HP + toff]);
+    };
+
+    const int R = (u1 - u0) * KS;  // rows this workgroup runs
+    // One row: KS taps of stage u = u0 + rho/KS, kernel row kh = rho % KS.
+    // The prefetches are unconditional (indices clamped to the last row or
+    // stage; the surplus loads at the very end are never used) so the loads
+    // stay where they are issued instead of moving next to their first use.
+    auto row = [&](auto set_tag, int rho) {
+        constexpr int SET = decltype(set_tag)::value;
+        constexpr int kh = SET % KS;  // rows are visited in groups of 3 == KS (or KS == 1)
+        const int u = u0 + rho / KS;
+        const int buf = (u - u0) & 1;
+        const bool last_stage = u + 1 >= u1;
+        load_row(Int<(SET + 2) % 3>{}, rho + 2 < R ? rho + 2 : R - 1);
+        if (kh == 0) load_halo(last_stage ? u : u + 1);
+        __builtin_amdgcn_sched_barrier(0);
+        // Tap tp = kh*KS + kw of the stage reads B[tp & 1]; the next tap's set is
+        // filled while this tap's MFMAs run, so no LDS read ever overwrites
+        // registers an in-flight MFMA is still reading.
+        auto tap = [&](auto kw_tag) {
+            constexpr int kw = decltype(kw_tag)::value;
+            constexpr int tp = kh * KS + kw;
+            constexpr int cur = tp & 1;
+            constexpr bool next_in_stage = tp + 1 < KS * KS;
+            constexpr int nkh = (tp + 1) / KS, nkw = (tp + 1) % KS;
+#pragma unroll
+            for (int ks = 0; ks < KSTEPS; ++ks) {
+#pragma unroll
+                for (int j = 0; j < FPOS; ++j) {
+#pragma unroll
+                    for (int i = 0; i < FCO; ++i)
+                        acc[i][j] = MF::run(A[SET][kw][i][ks], B[cur][j][ks], acc[i][j]);
+                    if (ks == 0 && next_in_stage) load_b(Int<cur ^ 1>{}, buf, j, nkh, nkw);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+        };
+        tap(Int<0>{});
+        if constexpr (KS > 1) {
+            tap(Int<1>{});
+            tap(Int<2>{});
+        }
+        if (kh == KS - 1 && !last_stage) {
+            store_halo(u + 1, buf ^ 1);
+            __syncthreads();
+#pragma unroll
+            for (int j = 0; j < FPOS; ++j) load_b(Int<0>{}, buf ^ 1, j, 0, 0);
+        }
+    };
+
+    if (R > 0) {
+        load_halo(u0);
+        load_row(Int<0>{}, 0);
+        load_row(Int<1>{}, R > 1 ? 1 : 0);
+        store_halo(u0, 0);
         __syncthreads();
-
-        const bool kok = (cb + kg * 8) < p.Cin;
-        // Weights (A fragments) come from global memory and are prefetched one
-        // tap ahead; input patches (B fragments) are read from the LDS tile.
-        bf16x8 a_cur[FCO], a_nxt[FCO];
 #pragma unroll
-        for (int f = 0; f < FCO; ++f) {
-            uint4 v = make_uint4(0u, 0u, 0u, 0u);
-            if (wok[f] && kok) v = *reinterpret_cast<const uint4 *>(wrow[f] + cb);
-            a_cur[f] = as_bf16x8(v);
-        }
-#pragma unroll 1
-        for (int tap = 0; tap < TAPS; ++tap) {
-            const int tn = tap + 1 < TAPS ? tap + 1 : tap;
-#pragma unroll
-            for (int f = 0; f < FCO; ++f) {
-                uint4 v = make_uint4(0u, 0u, 0u, 0u);
-                if (wok[f] && kok)
-                    v = *reinterpret_cast<const uint4 *>(wrow[f] + (size_t)tn * p.Cin + cb);
-                a_nxt[f] = as_bf16x8(v);
+        for (int j = 0; j < FPOS; ++j) load_b(Int<0>{}, 0, j, 0, 0);
+        if (KS == 3) {
+            // R is a multiple of 3: one stage per iteration, no row guards.
+            for (int rho = 0; rho < R; rho += 3) {
+                row(Int<0>{}, rho);
+                row(Int<1>{}, rho + 1);
+                row(Int<2>{}, rho + 2);
             }
-            const int kt = tap / (KS * KS), kh = (tap / KS) % KS, kw = tap % KS;
-            const int toff = kt * 4 * p.HP + kh * p.HC + kw;
-            bf16x8 b[FPOS];
-#pragma unroll
-            for (int f = 0; f < FPOS; ++f) b[f] = as_bf16x8(halo[boff[f] + toff]);
-#pragma unroll
-            for (int i = 0; i < FCO; ++i)
-#pragma unroll
-                for (int j = 0; j < FPOS; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_cur[i], b[j], acc[i][j], 0, 0, 0);
-#pragma unroll
-            for (int f = 0; f < FCO; ++f) a_cur[f] = a_nxt[f];
+        } else {
+            for (int rho = 0; rho < R; rho += 3) {
+                row(Int<0>{}, rho);
+                if (rho + 1 < R) row(Int<1>{}, rho + 1);
+                if (rho + 2 < R) row(Int<2>{}, rho + 2);
+            }
         }
     }
 
-    // Epilogue.  Lane holds D[co = 4*kg + e][pos = l16] of each 16x16 tile.
+    if (SPLIT) {
+        // Partials in MFMA fragment order: lane-contiguous 16-byte stores.
+        constexpr int TILE_F = POS_T * CO_T;
+        constexpr int WAVE_F = FCO * FPOS * 64 * ACC;
+        float *mine = p.part + ((size_t)tile_id * p.S + s) * TILE_F + (size_t)wave * WAVE_F;
+#pragma unroll
+        for (int i = 0; i < FCO; ++i)
+#pragma unroll
+            for (int j = 0; j < FPOS; ++j)
+#pragma unroll
+                for (int e = 0; e < ACC; e += 4)
+                    *reinterpret_cast<f32x4 *>(mine + ((i * FPOS + j) * 64 + lane) * ACC + e) =
+                        f32x4{acc[i][j][e], acc[i][j][e + 1], acc[i][j][e + 2], acc[i][j][e + 3]};
+        __threadfence();
+        __syncthreads();
+        if (tid == 0) s_last = (atomicAdd(p.ctr + tile_id, 1u) == (unsigned)(p.S - 1));
+        __syncthreads();
+        if (!s_last) return;
+        __threadfence();
+        const float *base = p.part + (size_t)tile_id * p.S * TILE_F + (size_t)wave * WAVE_F;
+#pragma unroll
+        for (int i = 0; i < FCO; ++i)
+#pragma unroll
+            for (int j = 0; j < FPOS; ++j)
+#pragma unroll
+                for (int e = 0; e < ACC; e += 4) {
+                    f32x4 sum = f32x4{0.f, 0.f, 0.f, 0.f};
+                    for (int ss = 0; ss < p.S; ++ss) {
+                        const f32x4 pv =
+                            ss == s ? f32x4{acc[i][j][e], acc[i][j][e + 1], acc[i][j][e + 2], acc[i][j][e + 3]}
+                                    : *reinterpret_cast<const f32x4 *>(
+                                          base + (size_t)ss * TILE_F + ((i * FPOS + j) * 64 + lane) * ACC + e);
+                        sum += pv;
+                    }
+                    acc[i][j][e] = sum[0];
+                    acc[i][j][e + 1] = sum[1];
+                    acc[i][j][e + 2] = sum[2];
+                    acc[i][j][e + 3] = sum[3];
+                }
+        if (tid == 0) p.ctr[tile_id] = 0u;  // re-armed for the next call
+    }
+
+    // Epilogue.  Accumulator element e of tile (i, j) is output channel
+    // co0 + i*M + (e/4)*8 + lg*4 + e%4 at position wpos*WPOS + j*M + lr.
 #pragma unroll
     for (int j = 0; j < FPOS; ++j) {
-        const int q = wpos * WPOS + j * 16 + l16;
+        const int q = wpos * WPOS + j * M + lr;
         const int r = q / p.TW, c = q - r * p.TW;
         const int h = h0 + r, w = w0 + c;
         if (h >= p.H || w >= p.W) continue;
         const size_t obase = (((size_t)(n * p.T + t) * p.H + h) * p.W + w) * p.Cout;
 #pragma unroll
-        for (int i = 0; i < FCO; ++i) {
-            const int co = co0 + i * 16 + kg * 4;
-            if (co >= p.Cout) continue;
-            float v[4] = {acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]};
-            if (p.bias) {
-                const uint2 bb = *reinterpret_cast<const uint2 *>(p.bias + co);
-                v[0] += bf16_to_f32(bb.x & 0xffffu);
-                v[1] += bf16_to_f32(bb.x >> 16);
-                v[2] += bf16_to_f32(bb.y & 0xffffu);
-                v[3] += bf16_to_f32(bb.y >> 16);
+        for (int i = 0; i < FCO; ++i)
+#pragma unroll
+            for (int e4 = 0; e4 < ACC / 4; ++e4) {
+                const int co = co0 + i * M + e4 * 8 + lg * 4;
+                float v[4] = {acc[i][j][e4 * 4], acc[i][j][e4 * 4 + 1], acc[i][j][e4 * 4 + 2],
+                              acc[i][j][e4 * 4 + 3]};
+                if (p.bias) {
+                    const uint2 bb = *reinterpret_cast<const uint2 *>(p.bias + co);
+                    v[0] += bf16_to_f32(bb.x & 0xffffu);
+                    v[1] += bf16_to_f32(bb.x >> 16);
+                    v[2] += bf16_to_f32(bb.y & 0xffffu);
+                    v[3] += bf16_to_f32(bb.y >> 16);
+                }
+                if (p.res) {
+                    const uint2 rr = *reinterpret_cast<const uint2 *>(p.res + obase + co);
+                    v[0] += bf16_to_f32(rr.x & 0xffffu);
+                    v[1] += bf16_to_f32(rr.x >> 16);
+                    v[2] += bf16_to_f32(rr.y & 0xffffu);
+                    v[3] += bf16_to_f32(rr.y >> 16);
+                }
+                uint2 o;
+                o.x = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
+                o.y = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
+                *reinterpret_cast<uint2 *>(p.y + obase + co) = o;
             }
-            if (p.res) {
-                const uint2 rr = *reinterpret_cast<const uint2 *>(p.res + obase + co);
-                v[0] += bf16_to_f32(rr.x & 0xffffu);
-                v[1] += bf16_to_f32(rr.x >> 16);
-                v[2] += bf16_to_f32(rr.y & 0xffffu);
-                v[3] += bf16_to_f32(rr.y >> 16);
-            }
-            uint2 o;
-            o.x = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
-            o.y = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
-            *reinterpret_cast<uint2 *>(p.y + obase + co) = o;
-        }
     }
 }
 
-struct TileChoice {
-    int th, tw;
+struct Plan {
+    int th, tw, hc, hp, tiles_h, tiles_w, co_t, co_tiles, S, U, co_major;
+    long tiles;  // n * t * tiles_h * tiles_w * co_tiles
 };
 
-// Pick a TH x TW tile (TH*TW == pos_t) that wastes the fewest positions on
-// ragged edges; ties go to the wider tile (longer contiguous runs).
-TileChoice choose_tile(int h, int w, int pos_t, int ks, int hp_max) {
-    TileChoice best{0, 0};
-    long best_cost = -1;
-    for (int tw = 1; tw <= pos_t; tw *= 2) {
-        const int th = pos_t / tw;
-        if ((th + ks - 1) * (tw + ks - 1) > hp_max) continue;
-        const long tiles = (long)((h + th - 1) / th) * ((w + tw - 1) / tw);
-        const long cost = tiles * pos_t;
-        if (best_cost < 0 || cost < best_cost || (cost == best_cost && tw > best.tw)) {
-            best_cost = cost;
-            best = {th, tw};
-        }
+int num_cus() {
+    static int cached = 0;
+    if (!cached) {
+        int dev = 0, cus = 0;
+        if (hipGetDevice(&dev) == hipSuccess &&
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+            cus > 0)
+            cached = cus;
+        else
+            cached = 256;
     }
-    return best;
+    return cached;
 }
 
-template <int KS, int CO_T, int POS_T, int HP_MAX>
-hipError_t launch_variant(const ConvCall &c, hipStream_t s) {
-    IgParams p;
+// Pick a TH x TW tile (TH*TW == 256) that wastes the fewest positions on
+// ragged edges; ties go to the wider tile (longer contiguous runs).
+void choose_tile(int h, int w, int ks, int hp_max, int *th_out, int *tw_out) {
+    int bth = 0, btw = 0;
+    long best = -1;
+    for (int tw = 1; tw <= POS_T; tw *= 2) {
+        const int th = POS_T / tw;
+        if ((th + ks - 1) * (tw + ks - 1) > hp_max) continue;
+        // tiles narrower than 16 columns split a 16-lane LDS read over rows
+        // 2*(tw+2) bytes * 8 apart, which collide in the LDS banks: count them
+        // as 25% more expensive
+        const long tiles = (long)((h + th - 1) / th) * ((w + tw - 1) / tw);
+        const long cost = tw < 16 ? tiles * 5 : tiles * 4;
+        if (best < 0 || cost < best || (cost == best && tw > btw)) {
+            best = cost;
+            bth = th;
+            btw = tw;
+        }
+    }
+    *th_out = bth;
+    *tw_out = btw;
+}
+
+int co_tile_for(int cout) {
+    if (cout % 128 == 0) return 128;
+    if (cout % 96 == 0) return 96;
+    if (cout % 64 == 0) return 64;
+    return 32;  // the route requires cout % 32 == 0
+}
+
+Plan make_plan(const ConvCall &c, ConvRoute r) {
+    Plan pl{};
+    const int ks = r == ConvRoute::Fast3x3x3 ? 3 : 1;
+    const int hp_max = ks == 3 ? 340 : 256;
+    choose_tile(c.h, c.w, ks, hp_max, &pl.th, &pl.tw);
+    pl.hc = pl.tw + ks - 1;
+    pl.hp = (pl.th + ks - 1) * pl.hc;
+    pl.tiles_h = (c.h + pl.th - 1) / pl.th;
+    pl.tiles_w = (c.w + pl.tw - 1) / pl.tw;
+    pl.co_t = co_tile_for(c.cout);
+    pl.U = ks * ((c.cin + 31) / 32);
+    const long spatial = (long)c.n * c.t * pl.tiles_h * pl.tiles_w;
+    const long slots = num_cus();  // one workgroup per CU
+    // Small grid (fewer tiles than resident slots): order channel tiles
+    // slowest, and prefer 96-channel tiles when they split C_out into a
+    // multiple of 4 tiles -- with 8 XCDs, two XCDs then share each channel tile
+    // and hold 1/4 of the weights each in L2.
+    pl.co_major = spatial * (c.cout / pl.co_t) < slots;
+    if (pl.co_major && c.cout % 96 == 0 && (c.cout / 96) % 4 == 0) pl.co_t = 96;
+    pl.co_tiles = c.cout / pl.co_t;
+    pl.tiles = spatial * pl.co_tiles;
+    // Split K when the tiles alone leave CUs idle: minimise
+    // (rounds of resident workgroups) * (units per split + fixed cost).
+    int best_s = 1;
+    double best_cost = -1.0;
+    const int s_max = pl.tiles <= CTR_CAP ? pl.U : 1;
+    for (int s = 1; s <= s_max && s <= 64; ++s) {
+        const long wgs = pl.tiles * s;
+        const double rounds = (double)((wgs + slots - 1) / slots);
+        const double cost = rounds * ((double)((pl.U + s - 1) / s) + 1.0 + (s > 1 ? 0.5 : 0.0));
+        if (best_cost < 0 || cost < best_cost - 1e-9) {
+            best_cost = cost;
+            best_s = s;
+        }
+    }
+    pl.S = best_s;
+    return pl;
+}
+
+size_t part_bytes(const Plan &pl) {
+    if (pl.S <= 1) return 0;
+    return (size_t)pl.tiles * pl.S * POS_T * pl.co_t * sizeof(float);
+}
+
+size_t ws_bytes_for(const Plan &pl) {
+    if (pl.S <= 1) return 0;
+    return CTR_BYTES + part_bytes(pl);
+}
+
+template <int KS, int CO_T, int M, int WAVES_CO>
+hipError_t launch_variant(const IgParams &p, hipStream_t s) {
+    if (p.S > 1)
+        hipLaunchKernelGGL((igemm_kernel<KS, CO_T, M, WAVES_CO, true>), dim3(p.total), dim3(256), 0, s, p);
+    else
+        hipLaunchKernelGGL((igemm_kernel<KS, CO_T, M, WAVES_CO, false>), dim3(p.total), dim3(256), 0, s, p);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+size_t igemm_counter_bytes() { return CTR_BYTES; }
+
+size_t igemm_workspace_bytes(const ConvCall &c, ConvRoute r) {
+    if (c.t <= 0) return 0;
+    return ws_bytes_for(make_plan(c, r));
+}
+
+bool igemm_supports(const ConvCall &c) {
+    // 32-bit buffer offsets: one frame and the weights must stay below 2 GiB.
+    const size_t frame = (size_t)c.h * c.w * c.cin * 2;
+    const size_t wbytes = (size_t)c.cout * c.cin * c.kt * c.kh * c.kw * 2;
+    return frame < ((size_t)1 << 31) && wbytes < ((size_t)1 << 31) && c.cout % 32 == 0;
+}
+
+hipError_t launch_conv_igemm(const ConvCall &c, ConvRoute r, void *ws, size_t ws_bytes,
+                             void *cache_out, hipStream_t s) {
+    const Plan pl = make_plan(c, r);
+    if (pl.th == 0) return hipErrorInvalidValue;
+    IgParams p{};
     p.x = static_cast<const uint16_t *>(c.x);
     p.cache = static_cast<const uint16_t *>(c.cache_in);
     p.w = static_cast<const uint16_t *>(c.weight);
     p.bias = static_cast<const uint16_t *>(c.bias);
     p.res = static_cast<const uint16_t *>(c.residual);
     p.y = static_cast<uint16_t *>(c.y);
+    p.cache_out = r == ConvRoute::Fast3x3x3 ? static_cast<uint16_t *>(cache_out) : nullptr;
     p.T = c.t;
     p.H = c.h;
     p.W = c.w;
     p.Cin = c.cin;
     p.Cout = c.cout;
     p.F = c.frames;
-    const TileChoice tc = choose_tile(c.h, c.w, POS_T, KS, HP_MAX);
-    if (tc.th == 0) return hipErrorInvalidValue;
-    p.TH = tc.th;
-    p.TW = tc.tw;
-    p.HC = tc.tw + KS - 1;
-    p.HP = (tc.th + KS - 1) * p.HC;
-    p.tiles_w = (c.w + tc.tw - 1) / tc.tw;
-    p.tiles_h = (c.h + tc.th - 1) / tc.th;
-    p.co_tiles = (c.cout + CO_T - 1) / CO_T;
-    const long total = (long)c.n * c.t * p.tiles_h * p.tiles_w * p.co_tiles;
+    p.TH = pl.th;
+    p.TW = pl.tw;
+    p.HC = pl.hc;
+    p.HP = pl.hp;
+    p.tiles_w = pl.tiles_w;
+    p.tiles_h = pl.tiles_h;
+    p.co_tiles = pl.co_tiles;
+    p.S = pl.S;
+    p.U = pl.U;
+    p.co_major = pl.co_major;
+    p.frame_bytes = (uint32_t)((size_t)c.h * c.w * c.cin * 2);
+    p.w_bytes = (uint32_t)((size_t)c.cout * c.cin * c.kt * c.kh * c.kw * 2);
+    if (pl.S > 1) {
+        if (ws_bytes < ws_bytes_for(pl) || !ws) return hipErrorInvalidValue;
+        p.ctr = static_cast<uint32_t *>(ws);
+        p.part = reinterpret_cast<float *>(static_cast<char *>(ws) + CTR_BYTES);
+    }
+    const long total = pl.tiles * pl.S;
     if (total <= 0) return hipSuccess;
     if (total > 0x7fffffffL) return hipErrorInvalidValue;
     p.total = (int)total;
-    hipLaunchKernelGGL((igemm_kernel<KS, CO_T, POS_T, HP_MAX>), dim3(p.total), dim3(256), 0, s, p);
-    return hipGetLastError();
-}
-
-}  // namespace
-
-size_t igemm_workspace_bytes(const ConvCall &, ConvRoute) { return 0; }
-
-hipError_t launch_conv_igemm(const ConvCall &c, ConvRoute r, void *, size_t, hipStream_t s) {
-    if (r == ConvRoute::Fast3x3x3) {
-        if (c.cout % 128 == 0) return launch_variant<3, 128, 256, 340>(c, s);
-        if (c.cout % 96 == 0) return launch_variant<3, 96, 256, 340>(c, s);
-        return launch_variant<3, 64, 256, 340>(c, s);
+    const bool k3 = r == ConvRoute::Fast3x3x3;
+    // 128 channels: 32x32x16 MFMAs on 2 x 2 waves of 64 x 128.  96 and 64:
+    // 16x16x32 MFMAs on 2 x 2 waves (48 or 32 channels x 128 positions).
+    // 32: 32x32x16 on 1 x 4 waves of 32 x 64.
+    switch (pl.co_t) {
+        case 128: return k3 ? launch_variant<3, 128, 32, 2>(p, s) : launch_variant<1, 128, 32, 2>(p, s);
+        case 96: return k3 ? launch_variant<3, 96, 16, 2>(p, s) : launch_variant<1, 96, 16, 2>(p, s);
+        case 64: return k3 ? launch_variant<3, 64, 16, 2>(p, s) : launch_variant<1, 64, 16, 2>(p, s);
+        default: return k3 ? launch_variant<3, 32, 32, 1>(p, s) : launch_variant<1, 32, 32, 1>(p, s);
     }
-    if (c.cout % 128 == 0) return launch_variant<1, 128, 256, 256>(c, s);
-    if (c.cout % 96 == 0) return launch_variant<1, 96, 256, 256>(c, s);
-    return launch_variant<1, 64, 256, 256>(c, s);
 }
 
 }  // namespace wvc

@@ -132,7 +132,7 @@ int plan_conv(const wvc_conv3d_desc *d, ConvPlan *pl, bool count = true) {
     if (!ok) return fail(WVC_ERR_ARG, "tensor size overflows");
     pl->b_bytes = (size_t)d->c_out * e;
 
-    const bool chan_ok = d->c_in % 8 == 0 && d->c_out % 16 == 0;
+    const bool chan_ok = d->c_in % 8 == 0 && d->c_out % 32 == 0;
     const bool unit = d->stride_h == 1 && d->stride_w == 1;
     if (d->dtype == WVC_BF16 && chan_ok && unit && d->kt == 3 && d->kh == 3 && d->kw == 3 &&
         d->pad_h == 1 && d->pad_w == 1 && d->dil_t == 1 && d->dil_h == 1 && d->dil_w == 1)
@@ -141,6 +141,8 @@ int plan_conv(const wvc_conv3d_desc *d, ConvPlan *pl, bool count = true) {
              d->pad_h == 0 && d->pad_w == 0)
         pl->route = wvc::ConvRoute::Fast1x1x1;
     else
+        pl->route = wvc::ConvRoute::Generic;
+    if (pl->route != wvc::ConvRoute::Generic && !wvc::igemm_supports(c))
         pl->route = wvc::ConvRoute::Generic;
     return WVC_OK;
 }
@@ -201,14 +203,17 @@ int conv_fwd(const wvc_conv3d_desc *d, const void *x, const void *cache_in, void
     c.residual = residual;
     c.y = y;
     hipError_t err = hipSuccess;
+    bool cache_done = false;
     if (d->t > 0) {
-        if (pl.route == wvc::ConvRoute::Generic)
+        if (pl.route == wvc::ConvRoute::Generic) {
             err = wvc::launch_conv_direct(c, s);
-        else
-            err = wvc::launch_conv_igemm(c, pl.route, ws, ws_bytes, s);
+        } else {
+            err = wvc::launch_conv_igemm(c, pl.route, ws, ws_bytes, cache_out, s);
+            cache_done = pl.route == wvc::ConvRoute::Fast3x3x3;  // written by the conv itself
+        }
         if (err != hipSuccess) return hip_status(err, "conv launch");
     }
-    if (cache_out) {
+    if (cache_out && !cache_done) {
         const size_t frame_elems = (size_t)d->h * d->w * d->c_in;
         err = wvc::launch_cache_update(x, cache_in, cache_out, d->n, d->t, c.frames, frame_elems,
                                        elem_bytes(d->dtype), s);
@@ -248,7 +253,7 @@ int norm_fwd(const void *x, const void *gamma, const void *beta, void *y, int n,
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 struct BlockLayout {
-    size_t h1, a1, h2, sc, total;
+    size_t h1, a1, h2, sc, conv, conv_bytes, total;
 };
 
 int plan_block(const wvc_resblock_desc *d, BlockLayout *L) {
@@ -259,8 +264,37 @@ int plan_block(const wvc_resblock_desc *d, BlockLayout *L) {
         return fail(WVC_ERR_ARG, "bad resblock shape");
     if (!(d->eps > 0.f)) return fail(WVC_ERR_ARG, "eps must be > 0");
     const size_t pos = (size_t)d->n * d->t * d->h * d->w;
-    L->h1 = 0;
-    L->a1 = align256(pos * d->c_in * e);
+    // The convs' scratch comes first and always reserves the split-K counter
+    // words at offset 0, whatever this chunk length needs: a later call with a
+    // different chunk length (and split) then still finds its counters zeroed
+    // instead of an earlier call's activations.
+    wvc_conv3d_desc c{};
+    c.n = d->n; c.c_in = d->c_in; c.c_out = d->c_out; c.t = d->t; c.h = d->h; c.w = d->w;
+    c.kt = c.kh = c.kw = 3;
+    c.stride_t = c.stride_h = c.stride_w = 1;
+    c.pad_h = c.pad_w = 1;
+    c.dil_t = c.dil_h = c.dil_w = 1;
+    c.groups = 1;
+    c.dtype = d->dtype;
+    size_t need = wvc::igemm_counter_bytes();
+    for (int k = 0; k < 3; ++k) {
+        if (k == 1) c.c_in = d->c_out;
+        if (k == 2) {  // the 1x1x1 shortcut, when there is one
+            if (d->c_in == d->c_out) break;
+            c.c_in = d->c_in;
+            c.kt = c.kh = c.kw = 1;
+            c.pad_h = c.pad_w = 0;
+        }
+        ConvPlan pl;
+        if (plan_conv(&c, &pl, false) == WVC_OK && pl.route != wvc::ConvRoute::Generic) {
+            const size_t b = wvc::igemm_workspace_bytes(pl.call, pl.route);
+            if (b > need) need = b;
+        }
+    }
+    L->conv = 0;
+    L->conv_bytes = align256(need);
+    L->h1 = L->conv_bytes;
+    L->a1 = L->h1 + align256(pos * d->c_in * e);
     L->h2 = L->a1 + align256(pos * d->c_out * e);
     L->sc = L->h2 + align256(pos * d->c_out * e);
     L->total = L->sc + (d->c_in != d->c_out ? align256(pos * d->c_out * e) : 0);
@@ -362,7 +396,9 @@ int wvc_resblock_fwd(const wvc_resblock_desc *d, const void *x, void *y,
     if ((rc = norm_fwd(x, p->gamma1, p->beta1, h1, d->n, d->c_in, d->t, d->h, d->w, d->dtype,
                        d->eps, 1, s)))
         return rc;
-    if ((rc = conv_fwd(&c1, h1, cache1_in, cache1_out, p->w1, p->b1, nullptr, a1, nullptr, 0, s)))
+    void *cws = ws + L.conv;
+    if ((rc = conv_fwd(&c1, h1, cache1_in, cache1_out, p->w1, p->b1, nullptr, a1, cws, L.conv_bytes,
+                       s)))
         return rc;
     if ((rc = norm_fwd(a1, p->gamma2, p->beta2, h2, d->n, d->c_out, d->t, d->h, d->w, d->dtype,
                        d->eps, 1, s)))
@@ -372,12 +408,12 @@ int wvc_resblock_fwd(const wvc_resblock_desc *d, const void *x, void *y,
         wvc_conv3d_desc cs = c1;
         cs.kt = cs.kh = cs.kw = 1;
         cs.pad_h = cs.pad_w = 0;
-        if ((rc = conv_fwd(&cs, x, nullptr, nullptr, p->w_short, p->b_short, nullptr, sc, nullptr,
-                           0, s)))
+        if ((rc = conv_fwd(&cs, x, nullptr, nullptr, p->w_short, p->b_short, nullptr, sc, cws,
+                           L.conv_bytes, s)))
             return rc;
         shortcut = sc;
     }
-    return conv_fwd(&c2, h2, cache2_in, cache2_out, p->w2, p->b2, shortcut, y, nullptr, 0, s);
+    return conv_fwd(&c2, h2, cache2_in, cache2_out, p->w2, p->b2, shortcut, y, cws, L.conv_bytes, s);
 }
 
 int wvc_cache_reset(void *cache, size_t bytes, void *stream) {

@@ -43,10 +43,16 @@ struct ConvCall {
 
 enum class ConvRoute { Fast3x3x3, Fast1x1x1, Generic };
 
-// MFMA implicit-GEMM route (bf16 only).
+// MFMA implicit-GEMM route (bf16 only).  The workspace holds split-K partials
+// and per-tile arrival counters; the counters must be zero before the first
+// call and every call leaves them zero.  The 3x3x3 route also writes
+// cache_out (may be nullptr) when t > 0.
 size_t igemm_workspace_bytes(const ConvCall &c, ConvRoute r);
+// Bytes at the start of every conv workspace that hold the arrival counters.
+size_t igemm_counter_bytes();
+bool igemm_supports(const ConvCall &c);
 hipError_t launch_conv_igemm(const ConvCall &c, ConvRoute r, void *ws, size_t ws_bytes,
-                             hipStream_t s);
+                             void *cache_out, hipStream_t s);
 // Direct-convolution route (any stride/pad/dilation, fp32 or bf16).
 hipError_t launch_conv_direct(const ConvCall &c, hipStream_t s);
 

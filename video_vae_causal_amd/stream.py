@@ -57,6 +57,7 @@ class CausalConv3d:
         self.bias = bias
         self.frames = L.wvc_conv3d_cache_frames(tuple(weight.shape))
         self.cache: Optional[_PingPong] = None
+        self.ws: Optional[torch.Tensor] = None
 
     def start(self, n: int, h: int, w: int):
         c = self.weight.shape[1]
@@ -73,7 +74,13 @@ class CausalConv3d:
             self.start(x.shape[0], x.shape[3], x.shape[4])
         cin = self.cache.cin if self.frames else None
         cout = self.cache.cout if self.frames else None
-        y = L.wvc_causal_conv3d_fwd(x, self.weight, self.bias, cin, cout, residual, y)
+        d = L.conv_desc(tuple(x.shape), tuple(self.weight.shape), L._dtype_code(x.dtype),
+                        padding=(1, 1) if self.weight.shape[3] == 3 else (0, 0))
+        need = L.wvc_causal_conv3d_workspace_bytes(d)
+        if need and (self.ws is None or self.ws.numel() < need):
+            self.ws = torch.zeros(need, dtype=torch.uint8, device=x.device)
+        y = L.wvc_causal_conv3d_fwd(x, self.weight, self.bias, cin, cout, residual, y,
+                                    workspace=self.ws if need else None)
         if self.frames:
             self.cache.flip()
         return y
@@ -105,7 +112,8 @@ class ResBlock:
         d = L.resblock_desc(tuple(x.shape), self.p["w1"].shape[0], L._dtype_code(x.dtype), self.eps)
         need = L.wvc_resblock_workspace_bytes(d)
         if self.ws is None or self.ws.numel() < need:
-            self.ws = torch.empty(need, dtype=torch.uint8, device=x.device)
+            # zero-filled once: split-K counters start at zero, calls leave them so
+            self.ws = torch.zeros(need, dtype=torch.uint8, device=x.device)
         y = L.wvc_resblock_fwd(x, self.p, self.c1.cin, self.c1.cout, self.c2.cin, self.c2.cout,
                                y=y, eps=self.eps, workspace=self.ws)
         self.c1.flip()
