@@ -70,11 +70,12 @@ def to_dev(a, dtype=None):
     return cl(t) if t.dim() == 5 else t
 
 
-def conv_workspace(x, w, padding=(1, 1)):
+def conv_workspace(x, w, padding=(1, 1), packed=False):
     """Zero-filled conv workspace allocated once, outside any timed region."""
     import torch
     from video_vae_causal_amd import _lib as L
-    d = L.conv_desc(tuple(x.shape), tuple(w.shape), L.WVC_BF16, padding=padding)
+    d = L.conv_desc(tuple(x.shape), tuple(w.shape), L.WVC_BF16, padding=padding,
+                    weight_layout=L.WVC_WEIGHT_PACKED if packed else L.WVC_WEIGHT_STANDARD)
     need = L.wvc_causal_conv3d_workspace_bytes(d)
     return torch.zeros(need, dtype=torch.uint8, device="cuda") if need else None
 
@@ -126,16 +127,18 @@ def wl_resblock():
     cache = L.empty_cl((n, c, 2, h, w))
     L.wvc_cache_reset(cache)
     ky = L.empty_cl((n, c, 1, h, w))
-    kws = conv_workspace(frames[0], p["w1"])
+    kws = conv_workspace(frames[0], p["w1"], packed=True)
+    w1p = L.wvc_conv3d_pack_weights(p["w1"])
 
     def kernel():
-        L.wvc_causal_conv3d_fwd(frames[0], p["w1"], p["b1"], cache, None, None, ky, workspace=kws)
+        L.wvc_causal_conv3d_fwd(frames[0], p["w1"], p["b1"], cache, None, None, ky, workspace=kws,
+                                packed_weight=w1p)
 
     info = dict(workload="resblock_384_60x104", conv_flops=conv_flops, latent_frames=t,
                 config={"workload": "resblock_384_60x104", "channels": c, "frames": t,
                         "height": h, "width": w, "chunk_frames": 1, "cache_frames": 2,
                         "batch": n},
-                kernel=kernel, kernel_name="igemm_kernel<3, 96, 16, 2, true>",
+                kernel=kernel, kernel_name="igemm_kernel<3, 128, 32, 2, true>",
                 kernel_units=acc.conv_flops(n, 1, h, w, c, c), kernel_bound="mfma",
                 kernel_bytes=acc.conv_launch_bytes(n, 1, h, w, c, c))
     return step, info
@@ -151,18 +154,20 @@ def wl_layer384():
     y = L.empty_cl((n, c, t, h, w))
     proj = L.empty_cl((n, wp.shape[0], t, h, w))
 
-    ws3 = conv_workspace(x, wt)
-    ws1 = conv_workspace(y, wp, padding=(0, 0))
+    ws3 = conv_workspace(x, wt, packed=True)
+    ws1 = conv_workspace(y, wp, padding=(0, 0), packed=True)
+    wtp = L.wvc_conv3d_pack_weights(wt)
+    wpp = L.wvc_conv3d_pack_weights(wp, padding=(0, 0))
 
     def step():
-        L.wvc_causal_conv3d_fwd(x, wt, b, y=y, workspace=ws3)
-        L.wvc_causal_conv3d_fwd(y, wp, bp, y=proj, padding=(0, 0), workspace=ws1)
+        L.wvc_causal_conv3d_fwd(x, wt, b, y=y, workspace=ws3, packed_weight=wtp)
+        L.wvc_causal_conv3d_fwd(y, wp, bp, y=proj, padding=(0, 0), workspace=ws1, packed_weight=wpp)
 
     f3 = acc.conv_flops(n, t, h, w, c, c)
     f1 = acc.conv_flops(n, t, h, w, c, wp.shape[0], (1, 1, 1))
 
     def kernel():
-        L.wvc_causal_conv3d_fwd(x, wt, b, y=y, workspace=ws3)
+        L.wvc_causal_conv3d_fwd(x, wt, b, y=y, workspace=ws3, packed_weight=wtp)
 
     info = dict(workload="layer_384_240x416", conv_flops=f3 + f1, latent_frames=t,
                 config={"workload": "layer_384_240x416", "channels": c, "frames": t,
@@ -187,19 +192,21 @@ def wl_layer96():
     hs = [cl(hbuf[:, :, s:s + k]) for s, k in zip(starts, sizes)]
     ys = [y[:, :, s:s + k] for s, k in zip(starts, sizes)]
 
-    wss = [conv_workspace(hs[i], wt) for i in range(len(sizes))]
+    wss = [conv_workspace(hs[i], wt, packed=True) for i in range(len(sizes))]
+    wtp = L.wvc_conv3d_pack_weights(wt)
 
     def step():
         L.wvc_rmsnorm_silu(x, g, y=hbuf)
         L.wvc_cache_reset(caches[0])
         for i in range(len(sizes)):
             L.wvc_causal_conv3d_fwd(hs[i], wt, b, caches[i % 2], caches[(i + 1) % 2], y=ys[i],
-                                    workspace=wss[i])
+                                    workspace=wss[i], packed_weight=wtp)
 
     conv_flops = acc.conv_flops(n, t, h, w, c, c)
 
     def kernel():
-        L.wvc_causal_conv3d_fwd(hs[1], wt, b, caches[0], None, None, ys[1], workspace=wss[1])
+        L.wvc_causal_conv3d_fwd(hs[1], wt, b, caches[0], None, None, ys[1], workspace=wss[1],
+                                packed_weight=wtp)
 
     def norm_kernel():
         L.wvc_rmsnorm_silu(x, g, y=hbuf)
@@ -241,15 +248,17 @@ def wl_decoder():
     kx = cl(torch.randn((n, width, 1, 2 * h, 2 * w), device="cuda").to(torch.bfloat16))
     ky = L.empty_cl((n, width, 1, 2 * h, 2 * w))
 
-    kws = conv_workspace(kx, p["w_up"])
+    kws = conv_workspace(kx, p["w_up"], packed=True)
+    wup = L.wvc_conv3d_pack_weights(p["w_up"])
 
     def kernel():
-        L.wvc_causal_conv3d_fwd(kx, p["w_up"], p["b_up"], cache, None, None, ky, workspace=kws)
+        L.wvc_causal_conv3d_fwd(kx, p["w_up"], p["b_up"], cache, None, None, ky, workspace=kws,
+                                packed_weight=wup)
 
     info = dict(workload="decoder_stack_48_30x52", conv_flops=per_frame * t, latent_frames=t,
                 config={"workload": "decoder_stack_48_30x52", "latent_channels": cl_, "channels": width,
                         "frames": t, "height": h, "width": w, "chunk_frames": 1, "batch": n},
-                kernel=kernel, kernel_name="igemm_kernel<3, 96, 16, 2, true>",
+                kernel=kernel, kernel_name="igemm_kernel<3, 128, 32, 2, true>",
                 kernel_units=acc.conv_flops(n, 1, 2 * h, 2 * w, width, width), kernel_bound="mfma",
                 kernel_bytes=acc.conv_launch_bytes(n, 1, 2 * h, 2 * w, width, width))
     return step, info

@@ -55,6 +55,10 @@ enum {
 
 enum { WVC_F32 = 0, WVC_BF16 = 1 };
 
+/* Weight layouts: the standard [C_out][kT][kH][kW][C_in] one, or the packed
+ * MFMA fragment order written by wvc_conv3d_pack_weights (fast routes only). */
+enum { WVC_WEIGHT_STANDARD = 0, WVC_WEIGHT_PACKED = 1 };
+
 /* Descriptor of one causal Conv3D call over a chunk of `t` frames. */
 typedef struct wvc_conv3d_desc {
     int n, c_in, c_out, t, h, w; /* batch, channels, frames in this chunk, spatial  */
@@ -65,6 +69,7 @@ typedef struct wvc_conv3d_desc {
     int dil_t, dil_h, dil_w;
     int groups;                  /* must be 1                                       */
     int dtype;                   /* WVC_F32 or WVC_BF16                             */
+    int weight_layout;           /* WVC_WEIGHT_STANDARD or WVC_WEIGHT_PACKED        */
 } wvc_conv3d_desc;
 
 /* Route counters ([P3]: counters show which route every call took). */
@@ -91,7 +96,8 @@ typedef struct wvc_counters {
  *                                          (start of a sequence)
  *   cache_out [N, C_in, F, H, W] or NULL  written: the last F frames of
  *                                          concat_T(cache_in, x); NULL = skip
- *   weight    [C_out, C_in, kT, kH, kW]   read
+ *   weight    [C_out, C_in, kT, kH, kW]   read (or its packed form when
+ *                                          d->weight_layout is WVC_WEIGHT_PACKED)
  *   bias      [C_out] or NULL             read
  *   residual  [N, C_out, t, h_out, w_out] or NULL; added after the bias
  *                                          (fused residual of the block)
@@ -123,8 +129,27 @@ int wvc_causal_conv3d_fwd(const wvc_conv3d_desc *d, const void *x, const void *c
                           size_t workspace_bytes, void *stream);
 
 /* Bytes of workspace wvc_causal_conv3d_fwd needs for this descriptor
- * (0 when none; (size_t)-1 for an invalid descriptor). */
+ * (0 when none; (size_t)-1 for an invalid descriptor).  A call with
+ * standard-layout weights on a fast route needs room to pack them. */
 size_t wvc_causal_conv3d_workspace_bytes(const wvc_conv3d_desc *d);
+
+/*
+ * Weights in MFMA fragment order.  The fast routes read each wave's weight
+ * fragment (M output channels x one MFMA K-step, M = 32 or 16 by C_out) as
+ * one contiguous 1 KiB block; wvc_conv3d_pack_weights writes that order once,
+ * so repeated calls with the same weights (a streamed layer) skip the packing
+ * pass.  The packed tensor depends only on C_out, C_in and the kernel size of
+ * the descriptor (not on t, h or w).
+ *   wvc_conv3d_packed_weight_bytes: size of the packed tensor, (size_t)-1 if
+ *     the descriptor does not take a fast route (bf16, 3x3x3 or 1x1x1 as above).
+ *   wvc_conv3d_pack_weights: weight (standard layout, read) -> packed
+ *     (written, wvc_conv3d_packed_weight_bytes(d) bytes, must not overlap
+ *     weight), enqueued on stream.  Channels past C_in are zero-filled.
+ * Use the result with d->weight_layout = WVC_WEIGHT_PACKED.
+ */
+size_t wvc_conv3d_packed_weight_bytes(const wvc_conv3d_desc *d);
+int wvc_conv3d_pack_weights(const wvc_conv3d_desc *d, const void *weight, void *packed,
+                            void *stream);
 
 /* Past frames F a causal conv keeps: dil_t * (kT - 1) ([P1] 10.3, the causal
  * pad tuple puts all temporal padding before frame 0).  -1 if d is invalid. */
@@ -148,7 +173,8 @@ int wvc_rmsnorm_silu(const void *x, const void *gamma, const void *beta, void *y
 typedef struct wvc_resblock_desc {
     int n, c_in, c_out, t, h, w;
     int dtype;
-    float eps; /* RMS-norm clamp, > 0 */
+    float eps;          /* RMS-norm clamp, > 0 */
+    int weights_packed; /* 1: w1, w2, w_short were packed by wvc_conv3d_pack_weights */
 } wvc_resblock_desc;
 
 /* Parameters of one residual block ([P1] 10.4).  All device pointers. */

@@ -131,6 +131,30 @@ def test_cache_frames_and_workspace_queries(lib):
     assert L.wvc_get_counters()["rejected"] == 0   # a size query is not a call
 
 
+def test_packed_weight_layout_validation(lib):
+    L.wvc_reset_counters()
+    d = desc(dtype=L.WVC_F32)
+    assert lib.wvc_conv3d_packed_weight_bytes(ctypes.byref(d)) == ctypes.c_size_t(-1).value
+    assert lib.wvc_conv3d_pack_weights(ctypes.byref(d), W, WS, None) == L.WVC_ERR_UNSUPPORTED
+    d = desc(dtype=L.WVC_F32)
+    d.weight_layout = L.WVC_WEIGHT_PACKED
+    assert call(lib, d) == L.WVC_ERR_UNSUPPORTED
+    d = desc(x_shape=(1, 32, 2, 8, 8), w_shape=(32, 32, 3, 3, 3))
+    d.weight_layout = 7
+    assert call(lib, d) == L.WVC_ERR_ARG
+    # 384 -> 384 3x3x3: 384 * 27 * 384 * 2 bytes, channels padded to 32
+    d = desc(x_shape=(1, 384, 1, 8, 8), w_shape=(384, 384, 3, 3, 3))
+    assert lib.wvc_conv3d_packed_weight_bytes(ctypes.byref(d)) == 384 * 27 * 384 * 2
+    d = desc(x_shape=(1, 48, 1, 8, 8), w_shape=(384, 48, 3, 3, 3))
+    assert lib.wvc_conv3d_packed_weight_bytes(ctypes.byref(d)) == 384 * 27 * 64 * 2
+    assert lib.wvc_conv3d_pack_weights(ctypes.byref(d), W, W + 64, None) == L.WVC_ERR_ALIAS
+    assert lib.wvc_conv3d_pack_weights(ctypes.byref(d), W, None, None) == L.WVC_ERR_ARG
+    # a packed call whose tensors are not 16-byte aligned cannot fall back
+    d = desc(x_shape=(1, 32, 2, 8, 8), w_shape=(32, 32, 3, 3, 3))
+    d.weight_layout = L.WVC_WEIGHT_PACKED
+    assert call(lib, d, x=X + 2) == L.WVC_ERR_ARG
+
+
 def rb_desc(c_in=16, c_out=16, t=1, eps=1e-12):
     return L.resblock_desc((1, c_in, t, 8, 8), c_out, L.WVC_BF16, eps)
 

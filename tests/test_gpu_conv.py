@@ -69,6 +69,22 @@ def test_split_k_workspace_reused_across_shapes():
             check_bf16(to_host(y), ref, f"split-K {ci}->{co} {h}x{w}")
 
 
+@pytest.mark.parametrize("cin,cout,t,h,w", [(384, 384, 2, 12, 40), (48, 384, 1, 9, 13),
+                                             (96, 96, 2, 17, 33), (64, 64, 1, 10, 10)])
+def test_packed_weights_equal_standard_layout_bitwise(cin, cout, t, h, w):
+    """A call with weights packed once by wvc_conv3d_pack_weights runs the same
+    kernel on the same numbers as a call that packs them itself: bitwise."""
+    x, wt, b, cache = conv_case(cin, cout, t, h, w, seed=300 + cin)
+    xd, wd, bd, cd = to_dev(x), to_dev(wt), to_dev(b), to_dev(cache)
+    packed = L.wvc_conv3d_pack_weights(wd)
+    assert packed.numel() == L.wvc_conv3d_packed_weight_bytes(tuple(wd.shape))
+    y_std = L.wvc_causal_conv3d_fwd(xd, wd, bd, cd)
+    y_pk = L.wvc_causal_conv3d_fwd(xd, wd, bd, cd, packed_weight=packed)
+    assert torch.equal(y_std, y_pk)
+    check_bf16(to_host(y_pk), oracle.causal_conv3d(f64(x), f64(wt), f64(b), cache=f64(cache)),
+               f"packed weights {cin}->{cout}")
+
+
 def test_conv_residual_and_no_bias():
     x, wt, b, cache = conv_case(64, 64, 2, 11, 19, seed=7)
     res = inputs.quantize(inputs.normal((1, 64, 2, 11, 19), 7, "res"), "bf16")

@@ -126,6 +126,15 @@ def test_resblock_mixed_chunk_lengths_share_one_workspace():
         check_bf16(to_host(y), ref, f"resblock 384 30x52 chunks {sizes}")
 
 
+def test_resblock_packed_and_standard_weights_agree_bitwise():
+    r = inputs.resblock_inputs(seed=41, shape=(1, 96, 2, 9, 17))
+    xd, pd = to_dev(r["x"]), block_params_dev(r["p"])
+    packed = {k: L.wvc_conv3d_pack_weights(pd[k]) for k in ("w1", "w2")}
+    y_std = L.wvc_resblock_fwd(xd, pd)
+    y_pk = L.wvc_resblock_fwd(xd, pd, packed=packed)
+    assert torch.equal(y_std, y_pk)
+
+
 def test_resblock_checkpoint_resume_bitwise():
     r = inputs.resblock_inputs(seed=9, shape=(1, 64, 4, 8, 12))
     xd, pd = to_dev(r["x"]), block_params_dev(r["p"])

@@ -23,12 +23,14 @@ LIB_PATH = os.path.join(_HERE, "libwvc.so")
 WVC_OK, WVC_ERR_ARG, WVC_ERR_UNSUPPORTED, WVC_ERR_ALIAS, WVC_ERR_WORKSPACE, WVC_ERR_STRICT, \
     WVC_ERR_HIP = range(7)
 WVC_F32, WVC_BF16 = 0, 1
+WVC_WEIGHT_STANDARD, WVC_WEIGHT_PACKED = 0, 1
 ERROR_NAMES = {0: "WVC_OK", 1: "WVC_ERR_ARG", 2: "WVC_ERR_UNSUPPORTED", 3: "WVC_ERR_ALIAS",
                4: "WVC_ERR_WORKSPACE", 5: "WVC_ERR_STRICT", 6: "WVC_ERR_HIP"}
 
 # Every symbol include/wvc.h declares.
 EXPORTED = (
     "wvc_causal_conv3d_fwd", "wvc_causal_conv3d_workspace_bytes", "wvc_conv3d_cache_frames",
+    "wvc_conv3d_packed_weight_bytes", "wvc_conv3d_pack_weights",
     "wvc_rmsnorm_silu", "wvc_resblock_fwd", "wvc_resblock_workspace_bytes", "wvc_cache_reset",
     "wvc_upsample_nearest2x", "wvc_set_strict", "wvc_get_strict", "wvc_get_counters",
     "wvc_reset_counters", "wvc_last_error", "wvc_version",
@@ -38,12 +40,13 @@ EXPORTED = (
 class ConvDesc(ctypes.Structure):
     _fields_ = [(f, ctypes.c_int) for f in (
         "n", "c_in", "c_out", "t", "h", "w", "kt", "kh", "kw", "stride_t", "stride_h",
-        "stride_w", "pad_h", "pad_w", "dil_t", "dil_h", "dil_w", "groups", "dtype")]
+        "stride_w", "pad_h", "pad_w", "dil_t", "dil_h", "dil_w", "groups", "dtype",
+        "weight_layout")]
 
 
 class ResblockDesc(ctypes.Structure):
     _fields_ = [(f, ctypes.c_int) for f in ("n", "c_in", "c_out", "t", "h", "w", "dtype")] + \
-        [("eps", ctypes.c_float)]
+        [("eps", ctypes.c_float), ("weights_packed", ctypes.c_int)]
 
 
 class ResblockParams(ctypes.Structure):
@@ -81,6 +84,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.wvc_causal_conv3d_workspace_bytes.restype = sz
     lib.wvc_conv3d_cache_frames.argtypes = [dptr]
     lib.wvc_conv3d_cache_frames.restype = i
+    lib.wvc_conv3d_packed_weight_bytes.argtypes = [dptr]
+    lib.wvc_conv3d_packed_weight_bytes.restype = sz
+    lib.wvc_conv3d_pack_weights.argtypes = [dptr, vp, vp, vp]
+    lib.wvc_conv3d_pack_weights.restype = i
     lib.wvc_rmsnorm_silu.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp]
     lib.wvc_rmsnorm_silu.restype = i
     lib.wvc_resblock_fwd.argtypes = [ctypes.POINTER(ResblockDesc), vp, vp,
@@ -155,7 +162,8 @@ def empty_cl(shape: Sequence[int], dtype=torch.bfloat16, device="cuda") -> torch
 
 
 def conv_desc(x_shape, w_shape, dtype: int, stride=(1, 1, 1), padding=(1, 1),
-              dilation=(1, 1, 1), groups: int = 1) -> ConvDesc:
+              dilation=(1, 1, 1), groups: int = 1,
+              weight_layout: int = WVC_WEIGHT_STANDARD) -> ConvDesc:
     n, c, t, h, w = x_shape
     co, ci, kt, kh, kw = w_shape
     d = ConvDesc()
@@ -166,6 +174,7 @@ def conv_desc(x_shape, w_shape, dtype: int, stride=(1, 1, 1), padding=(1, 1),
     d.dil_t, d.dil_h, d.dil_w = dilation
     d.groups = groups
     d.dtype = dtype
+    d.weight_layout = weight_layout
     return d
 
 
@@ -187,14 +196,40 @@ def wvc_causal_conv3d_workspace_bytes(d: ConvDesc) -> int:
     return v
 
 
+def wvc_conv3d_packed_weight_bytes(w_shape, dtype=torch.bfloat16, padding=(1, 1)) -> int:
+    d = conv_desc((1, w_shape[1], 1, 1, 1), tuple(w_shape), _dtype_code(dtype), padding=padding)
+    v = load().wvc_conv3d_packed_weight_bytes(ctypes.byref(d))
+    if v == ctypes.c_size_t(-1).value:
+        raise WvcError(WVC_ERR_UNSUPPORTED, load().wvc_last_error().decode())
+    return v
+
+
+def wvc_conv3d_pack_weights(weight: torch.Tensor, padding=(1, 1)) -> torch.Tensor:
+    """Weights [C_out, C_in, kT, kH, kW] (channels_last_3d) -> their packed MFMA
+    fragment order (a flat uint8 device tensor), for calls with
+    weight_layout=WVC_WEIGHT_PACKED (see wvc_conv3d_pack_weights in
+    include/wvc.h)."""
+    _need_cl(weight, "weight")
+    shape = tuple(weight.shape)
+    d = conv_desc((1, shape[1], 1, 1, 1), shape, _dtype_code(weight.dtype), padding=padding)
+    packed = torch.empty(wvc_conv3d_packed_weight_bytes(shape, weight.dtype, padding),
+                         dtype=torch.uint8, device=weight.device)
+    _check(load().wvc_conv3d_pack_weights(ctypes.byref(d), _ptr(weight), _ptr(packed),
+                                          _stream(weight)))
+    return packed
+
+
 def wvc_causal_conv3d_fwd(x: torch.Tensor, weight: torch.Tensor, bias: Optional[torch.Tensor] = None,
                           cache_in: Optional[torch.Tensor] = None,
                           cache_out: Optional[torch.Tensor] = None,
                           residual: Optional[torch.Tensor] = None,
                           y: Optional[torch.Tensor] = None, stride=(1, 1, 1), padding=(1, 1),
                           dilation=(1, 1, 1), groups: int = 1,
-                          workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+                          workspace: Optional[torch.Tensor] = None,
+                          packed_weight: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Causal Conv3D of one chunk (see wvc_causal_conv3d_fwd in include/wvc.h).
+    ``weight`` gives the logical shape; when ``packed_weight`` (from
+    wvc_conv3d_pack_weights) is given the call reads that instead.
     Returns y (allocated if not given)."""
     lib = load()
     _need_cl(x, "x")
@@ -204,7 +239,10 @@ def wvc_causal_conv3d_fwd(x: torch.Tensor, weight: torch.Tensor, bias: Optional[
         _need_cl(t, name)
     _need_vec(bias, "bias", weight.shape[0])
     code = _dtype_code(x.dtype)
-    d = conv_desc(tuple(x.shape), tuple(weight.shape), code, stride, padding, dilation, groups)
+    layout = WVC_WEIGHT_STANDARD if packed_weight is None else WVC_WEIGHT_PACKED
+    d = conv_desc(tuple(x.shape), tuple(weight.shape), code, stride, padding, dilation, groups,
+                  layout)
+    wsrc = weight if packed_weight is None else packed_weight
     if y is None:
         ho, wo = conv_out_hw(x.shape[3], x.shape[4], weight.shape[2:], stride, padding, dilation)
         if ho < 1 or wo < 1:
@@ -218,7 +256,7 @@ def wvc_causal_conv3d_fwd(x: torch.Tensor, weight: torch.Tensor, bias: Optional[
     if workspace is not None:
         ws_bytes = workspace.numel() * workspace.element_size()
     _check(lib.wvc_causal_conv3d_fwd(ctypes.byref(d), _ptr(x), _ptr(cache_in), _ptr(cache_out),
-                                      _ptr(weight), _ptr(bias), _ptr(residual), _ptr(y),
+                                      _ptr(wsrc), _ptr(bias), _ptr(residual), _ptr(y),
                                       _ptr(workspace), ws_bytes, _stream(x)))
     return y
 
@@ -241,12 +279,14 @@ def wvc_rmsnorm_silu(x: torch.Tensor, gamma: torch.Tensor, beta: Optional[torch.
     return y
 
 
-def resblock_desc(x_shape, c_out: int, dtype: int, eps: float = 1e-12) -> ResblockDesc:
+def resblock_desc(x_shape, c_out: int, dtype: int, eps: float = 1e-12,
+                  weights_packed: bool = False) -> ResblockDesc:
     d = ResblockDesc()
     d.n, d.c_in, d.t, d.h, d.w = x_shape[0], x_shape[1], x_shape[2], x_shape[3], x_shape[4]
     d.c_out = c_out
     d.dtype = dtype
     d.eps = eps
+    d.weights_packed = int(bool(weights_packed))
     return d
 
 
@@ -259,19 +299,23 @@ def wvc_resblock_workspace_bytes(d: ResblockDesc) -> int:
 
 def wvc_resblock_fwd(x: torch.Tensor, params: dict, cache1_in=None, cache1_out=None,
                      cache2_in=None, cache2_out=None, y: Optional[torch.Tensor] = None,
-                     eps: float = 1e-12, workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+                     eps: float = 1e-12, workspace: Optional[torch.Tensor] = None,
+                     packed: Optional[dict] = None) -> torch.Tensor:
     """Wan residual block on one chunk (see wvc_resblock_fwd in include/wvc.h).
-    ``params``: gamma1, beta1, w1, b1, gamma2, beta2, w2, b2[, w_short, b_short]."""
+    ``params``: gamma1, beta1, w1, b1, gamma2, beta2, w2, b2[, w_short, b_short].
+    ``packed``: optional {w1, w2[, w_short]} from wvc_conv3d_pack_weights."""
     lib = load()
     _need_cl(x, "x")
     c_out = params["w1"].shape[0]
     for name in ("w1", "w2", "w_short"):
         _need_cl(params.get(name), name)
+    if packed is not None:
+        params = dict(params, **packed)
     for name, t in (("cache1_in", cache1_in), ("cache1_out", cache1_out),
                     ("cache2_in", cache2_in), ("cache2_out", cache2_out), ("y", y)):
         _need_cl(t, name)
     code = _dtype_code(x.dtype)
-    d = resblock_desc(tuple(x.shape), c_out, code, eps)
+    d = resblock_desc(tuple(x.shape), c_out, code, eps, weights_packed=packed is not None)
     if y is None:
         y = empty_cl((x.shape[0], c_out) + tuple(x.shape[2:]), x.dtype, x.device)
     need = wvc_resblock_workspace_bytes(d)

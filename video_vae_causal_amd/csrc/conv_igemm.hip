@@ -234,11 +234,6 @@ igemm_kernel(IgParams p) {
         const int r = q / p.TW, c = q - r * p.TW;
         boff[f] = lg * p.HP + r * p.HC + c;
     }
-    // A fragments: byte offset of (channel co, tap 0, input channel 8*lg).
-    uint32_t aoff[FCO];
-#pragma unroll
-    for (int f = 0; f < FCO; ++f)
-        aoff[f] = (uint32_t)(((co0 + f * M + lr) * TAPS * p.Cin + lg * 8) * 2);
     const __amdgpu_buffer_rsrc_t wr = rsrc(p.w, p.w_bytes);
     const size_t frame_elems = (size_t)p.frame_bytes / 2;
     const bool write_cache = KS == 3 && p.cache_out != nullptr && t == p.T - 1 && ct == 0;
@@ -255,22 +250,25 @@ igemm_kernel(IgParams p) {
     bf16x8 B[2][FPOS][KSTEPS];     // two tap sets: tap k reads B[k & 1]
     uint4 hv[NIT];
 
+    // Weights arrive packed in MFMA fragment order (see pack_weights_kernel):
+    // the fragment of M output channels x one K-step is 1 KiB, lane-contiguous.
+    const int nb = (p.Cin + 31) / 32;
     auto load_row = [&](auto set_tag, int rho) {
         constexpr int SET = decltype(set_tag)::value;
         const int u = u0 + rho / KS, kh = rho % KS;
-        const int kt = u % KS, cb = (u / KS) * 32;
+        const int kt = u % KS, cbi = u / KS;
 #pragma unroll
         for (int kw = 0; kw < KS; ++kw) {
             const int tap = (kt * KS + kh) * KS + kw;
 #pragma unroll
-            for (int ks = 0; ks < KSTEPS; ++ks) {
-                const int ch = cb + ks * GPL * 8;
-                const bool ok = ch + lg * 8 < p.Cin;
-                const uint32_t o = (uint32_t)(tap * p.Cin + ch) * 2;
+            for (int ks = 0; ks < KSTEPS; ++ks)
 #pragma unroll
-                for (int f = 0; f < FCO; ++f)
-                    A[SET][kw][f][ks] = as_bf16x8(bload(wr, ok ? aoff[f] + o : OOB));
-            }
+                for (int f = 0; f < FCO; ++f) {
+                    const int blk = co0 / M + f;
+                    const uint32_t o =
+                        (uint32_t)((((blk * TAPS + tap) * nb + cbi) * KSTEPS + ks) * 1024 + lane * 16);
+                    A[SET][kw][f][ks] = as_bf16x8(bload(wr, o));
+                }
         }
     };
     auto load_halo = [&](int u) {
@@ -461,6 +459,38 @@ igemm_kernel(IgParams p) {
     }
 }
 
+// Packs W[co][tap][ci] into MFMA fragment order for tile edge M:
+//   packed[co / M][tap][ci / 32][ks][lane][8 channels],  ks < M/16, lane < 64,
+//   row co = block*M + lane % M, channel = 32*cb + ks*(64/M)*8 + (lane / M)*8,
+// zero past C_in.  One fragment (one wave load) is then 1 KiB contiguous.
+template <int M>
+__global__ void __launch_bounds__(256) pack_weights_kernel(const uint16_t *__restrict__ w,
+                                                           uint4 *__restrict__ out, int cout,
+                                                           int cin, int taps) {
+    constexpr int KSTEPS = M / 16, GPL = 64 / M;
+    const int nb = (cin + 31) / 32;
+    const long chunks = (long)(cout / M) * taps * nb * KSTEPS * 64;
+    for (long i = (long)blockIdx.x * 256 + threadIdx.x; i < chunks; i += (long)gridDim.x * 256) {
+        long r = i;
+        const int lane = (int)(r % 64);
+        r /= 64;
+        const int ks = (int)(r % KSTEPS);
+        r /= KSTEPS;
+        const int cb = (int)(r % nb);
+        r /= nb;
+        const int tap = (int)(r % taps);
+        const int blk = (int)(r / taps);
+        const int co = blk * M + lane % M;
+        const int ch = cb * 32 + ks * GPL * 8 + (lane / M) * 8;
+        uint16_t v[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+            v[k] = ch + k < cin ? w[((size_t)co * taps + tap) * cin + ch + k] : (uint16_t)0;
+        out[i] = make_uint4(v[0] | ((uint32_t)v[1] << 16), v[2] | ((uint32_t)v[3] << 16),
+                            v[4] | ((uint32_t)v[5] << 16), v[6] | ((uint32_t)v[7] << 16));
+    }
+}
+
 struct Plan {
     int th, tw, hc, hp, tiles_h, tiles_w, co_t, co_tiles, S, U, co_major;
     long tiles;  // n * t * tiles_h * tiles_w * co_tiles
@@ -524,11 +554,9 @@ Plan make_plan(const ConvCall &c, ConvRoute r) {
     const long spatial = (long)c.n * c.t * pl.tiles_h * pl.tiles_w;
     const long slots = num_cus();  // one workgroup per CU
     // Small grid (fewer tiles than resident slots): order channel tiles
-    // slowest, and prefer 96-channel tiles when they split C_out into a
-    // multiple of 4 tiles -- with 8 XCDs, two XCDs then share each channel tile
-    // and hold 1/4 of the weights each in L2.
+    // slowest, so each XCD works on (about) one channel tile and keeps that
+    // slice of the weights in its L2.
     pl.co_major = spatial * (c.cout / pl.co_t) < slots;
-    if (pl.co_major && c.cout % 96 == 0 && (c.cout / 96) % 4 == 0) pl.co_t = 96;
     pl.co_tiles = c.cout / pl.co_t;
     pl.tiles = spatial * pl.co_tiles;
     // Split K when the tiles alone leave CUs idle: minimise
@@ -554,9 +582,21 @@ size_t part_bytes(const Plan &pl) {
     return (size_t)pl.tiles * pl.S * POS_T * pl.co_t * sizeof(float);
 }
 
-size_t ws_bytes_for(const Plan &pl) {
-    if (pl.S <= 1) return 0;
-    return CTR_BYTES + part_bytes(pl);
+int tile_m(int co_t) { return (co_t == 96 || co_t == 64) ? 16 : 32; }
+
+size_t packed_bytes(const ConvCall &c) {
+    const size_t nb = (size_t)(c.cin + 31) / 32;
+    return (size_t)c.cout * c.kt * c.kh * c.kw * nb * 32 * 2;
+}
+
+size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+// Workspace: [split-K counters, CTR_BYTES][partials][packed weights when the
+// call brings standard-layout weights].  The counter words always come first
+// so a workspace shared by calls of different plans keeps them zeroed.
+size_t ws_bytes_for(const Plan &pl, const ConvCall &c, bool need_pack) {
+    if (pl.S <= 1 && !need_pack) return 0;
+    return CTR_BYTES + align256(part_bytes(pl)) + (need_pack ? align256(packed_bytes(c)) : 0);
 }
 
 template <int KS, int CO_T, int M, int WAVES_CO>
@@ -572,26 +612,55 @@ hipError_t launch_variant(const IgParams &p, hipStream_t s) {
 
 size_t igemm_counter_bytes() { return CTR_BYTES; }
 
-size_t igemm_workspace_bytes(const ConvCall &c, ConvRoute r) {
+size_t igemm_workspace_bytes(const ConvCall &c, ConvRoute r, bool packed_given) {
     if (c.t <= 0) return 0;
-    return ws_bytes_for(make_plan(c, r));
+    return ws_bytes_for(make_plan(c, r), c, !packed_given);
+}
+
+size_t igemm_packed_weight_bytes(const ConvCall &c) { return packed_bytes(c); }
+
+hipError_t launch_pack_weights(const ConvCall &c, const void *w, void *packed, hipStream_t s) {
+    const int m = tile_m(co_tile_for(c.cout));
+    const int taps = c.kt * c.kh * c.kw;
+    const long chunks = (long)packed_bytes(c) / 16;
+    long blocks = (chunks + 255) / 256;
+    if (blocks > 8192) blocks = 8192;
+    if (blocks < 1) return hipSuccess;
+    if (m == 32)
+        hipLaunchKernelGGL(pack_weights_kernel<32>, dim3((unsigned)blocks), dim3(256), 0, s,
+                           static_cast<const uint16_t *>(w), static_cast<uint4 *>(packed), c.cout,
+                           c.cin, taps);
+    else
+        hipLaunchKernelGGL(pack_weights_kernel<16>, dim3((unsigned)blocks), dim3(256), 0, s,
+                           static_cast<const uint16_t *>(w), static_cast<uint4 *>(packed), c.cout,
+                           c.cin, taps);
+    return hipGetLastError();
 }
 
 bool igemm_supports(const ConvCall &c) {
-    // 32-bit buffer offsets: one frame and the weights must stay below 2 GiB.
+    // 32-bit buffer offsets: one frame and the packed weights must stay below 2 GiB.
     const size_t frame = (size_t)c.h * c.w * c.cin * 2;
-    const size_t wbytes = (size_t)c.cout * c.cin * c.kt * c.kh * c.kw * 2;
+    const size_t wbytes = packed_bytes(c);
     return frame < ((size_t)1 << 31) && wbytes < ((size_t)1 << 31) && c.cout % 32 == 0;
 }
 
-hipError_t launch_conv_igemm(const ConvCall &c, ConvRoute r, void *ws, size_t ws_bytes,
-                             void *cache_out, hipStream_t s) {
+hipError_t launch_conv_igemm(const ConvCall &c, ConvRoute r, bool packed_given, void *ws,
+                             size_t ws_bytes, void *cache_out, hipStream_t s) {
     const Plan pl = make_plan(c, r);
     if (pl.th == 0) return hipErrorInvalidValue;
+    if (ws_bytes < ws_bytes_for(pl, c, !packed_given) || (!ws && ws_bytes_for(pl, c, !packed_given)))
+        return hipErrorInvalidValue;
+    const void *wp = c.weight;
+    if (!packed_given) {
+        void *dst = static_cast<char *>(ws) + CTR_BYTES + align256(part_bytes(pl));
+        const hipError_t e = launch_pack_weights(c, c.weight, dst, s);
+        if (e != hipSuccess) return e;
+        wp = dst;
+    }
     IgParams p{};
     p.x = static_cast<const uint16_t *>(c.x);
     p.cache = static_cast<const uint16_t *>(c.cache_in);
-    p.w = static_cast<const uint16_t *>(c.weight);
+    p.w = static_cast<const uint16_t *>(wp);
     p.bias = static_cast<const uint16_t *>(c.bias);
     p.res = static_cast<const uint16_t *>(c.residual);
     p.y = static_cast<uint16_t *>(c.y);
@@ -613,9 +682,8 @@ hipError_t launch_conv_igemm(const ConvCall &c, ConvRoute r, void *ws, size_t ws
     p.U = pl.U;
     p.co_major = pl.co_major;
     p.frame_bytes = (uint32_t)((size_t)c.h * c.w * c.cin * 2);
-    p.w_bytes = (uint32_t)((size_t)c.cout * c.cin * c.kt * c.kh * c.kw * 2);
+    p.w_bytes = (uint32_t)packed_bytes(c);
     if (pl.S > 1) {
-        if (ws_bytes < ws_bytes_for(pl) || !ws) return hipErrorInvalidValue;
         p.ctr = static_cast<uint32_t *>(ws);
         p.part = reinterpret_cast<float *>(static_cast<char *>(ws) + CTR_BYTES);
     }

@@ -102,6 +102,8 @@ int plan_conv(const wvc_conv3d_desc *d, ConvPlan *pl, bool count = true) {
     if (d->n < 1 || d->c_in < 1 || d->c_out < 1 || d->t < 0 || d->h < 1 || d->w < 1)
         return fail(WVC_ERR_ARG, "bad shape n=%d c_in=%d c_out=%d t=%d h=%d w=%d", d->n, d->c_in,
                     d->c_out, d->t, d->h, d->w);
+    if (d->weight_layout != WVC_WEIGHT_STANDARD && d->weight_layout != WVC_WEIGHT_PACKED)
+        return fail(WVC_ERR_ARG, "weight_layout %d is neither standard nor packed", d->weight_layout);
     if (d->kt < 1 || d->kh < 1 || d->kw < 1 || d->stride_h < 1 || d->stride_w < 1 ||
         d->pad_h < 0 || d->pad_w < 0 || d->dil_t < 1 || d->dil_h < 1 || d->dil_w < 1)
         return fail(WVC_ERR_ARG, "bad kernel/stride/pad/dilation");
@@ -144,6 +146,13 @@ int plan_conv(const wvc_conv3d_desc *d, ConvPlan *pl, bool count = true) {
         pl->route = wvc::ConvRoute::Generic;
     if (pl->route != wvc::ConvRoute::Generic && !wvc::igemm_supports(c))
         pl->route = wvc::ConvRoute::Generic;
+    if (d->weight_layout == WVC_WEIGHT_PACKED) {
+        if (pl->route == wvc::ConvRoute::Generic) {
+            if (count) g_rejected++;
+            return fail(WVC_ERR_UNSUPPORTED, "packed weights exist only for the MFMA routes");
+        }
+        pl->w_bytes = wvc::igemm_packed_weight_bytes(c);
+    }
     return WVC_OK;
 }
 
@@ -168,12 +177,18 @@ int conv_fwd(const wvc_conv3d_desc *d, const void *x, const void *cache_in, void
     if (!ws && ws_bytes) return fail(WVC_ERR_ARG, "workspace is NULL but workspace_bytes > 0");
 
     // Fast routes read 16-byte vectors; anything not aligned takes the generic route.
+    const bool packed = d->weight_layout == WVC_WEIGHT_PACKED;
     if (pl.route != wvc::ConvRoute::Generic) {
         const bool al = aligned(x, 16) && aligned(cache_in, 16) && aligned(weight, 16) &&
                         aligned(y, 16) && aligned(residual, 16) && aligned(bias, 8);
-        if (!al) pl.route = wvc::ConvRoute::Generic;
+        if (!al) {
+            if (packed) return fail(WVC_ERR_ARG, "packed weights need 16-byte aligned tensors");
+            pl.route = wvc::ConvRoute::Generic;
+        }
     }
-    size_t need = pl.route == wvc::ConvRoute::Generic ? 0 : wvc::igemm_workspace_bytes(pl.call, pl.route);
+    size_t need = pl.route == wvc::ConvRoute::Generic
+                      ? 0
+                      : wvc::igemm_workspace_bytes(pl.call, pl.route, packed);
     if (ws_bytes < need)
         return fail(WVC_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", ws_bytes, need);
 
@@ -208,7 +223,7 @@ int conv_fwd(const wvc_conv3d_desc *d, const void *x, const void *cache_in, void
         if (pl.route == wvc::ConvRoute::Generic) {
             err = wvc::launch_conv_direct(c, s);
         } else {
-            err = wvc::launch_conv_igemm(c, pl.route, ws, ws_bytes, cache_out, s);
+            err = wvc::launch_conv_igemm(c, pl.route, packed, ws, ws_bytes, cache_out, s);
             cache_done = pl.route == wvc::ConvRoute::Fast3x3x3;  // written by the conv itself
         }
         if (err != hipSuccess) return hip_status(err, "conv launch");
@@ -263,6 +278,8 @@ int plan_block(const wvc_resblock_desc *d, BlockLayout *L) {
     if (d->n < 1 || d->c_in < 1 || d->c_out < 1 || d->t < 0 || d->h < 1 || d->w < 1)
         return fail(WVC_ERR_ARG, "bad resblock shape");
     if (!(d->eps > 0.f)) return fail(WVC_ERR_ARG, "eps must be > 0");
+    if (d->weights_packed != 0 && d->weights_packed != 1)
+        return fail(WVC_ERR_ARG, "weights_packed must be 0 or 1");
     const size_t pos = (size_t)d->n * d->t * d->h * d->w;
     // The convs' scratch comes first and always reserves the split-K counter
     // words at offset 0, whatever this chunk length needs: a later call with a
@@ -276,6 +293,7 @@ int plan_block(const wvc_resblock_desc *d, BlockLayout *L) {
     c.dil_t = c.dil_h = c.dil_w = 1;
     c.groups = 1;
     c.dtype = d->dtype;
+    c.weight_layout = d->weights_packed ? WVC_WEIGHT_PACKED : WVC_WEIGHT_STANDARD;
     size_t need = wvc::igemm_counter_bytes();
     for (int k = 0; k < 3; ++k) {
         if (k == 1) c.c_in = d->c_out;
@@ -287,7 +305,7 @@ int plan_block(const wvc_resblock_desc *d, BlockLayout *L) {
         }
         ConvPlan pl;
         if (plan_conv(&c, &pl, false) == WVC_OK && pl.route != wvc::ConvRoute::Generic) {
-            const size_t b = wvc::igemm_workspace_bytes(pl.call, pl.route);
+            const size_t b = wvc::igemm_workspace_bytes(pl.call, pl.route, d->weights_packed != 0);
             if (b > need) need = b;
         }
     }
@@ -317,7 +335,37 @@ size_t wvc_causal_conv3d_workspace_bytes(const wvc_conv3d_desc *d) {
     ConvPlan pl;
     if (plan_conv(d, &pl, /*count=*/false)) return (size_t)-1;  // a size query is not a call
     if (pl.route == wvc::ConvRoute::Generic) return 0;
-    return wvc::igemm_workspace_bytes(pl.call, pl.route);
+    return wvc::igemm_workspace_bytes(pl.call, pl.route, d->weight_layout == WVC_WEIGHT_PACKED);
+}
+
+size_t wvc_conv3d_packed_weight_bytes(const wvc_conv3d_desc *d) {
+    ConvPlan pl;
+    if (plan_conv(d, &pl, /*count=*/false)) return (size_t)-1;
+    if (pl.route == wvc::ConvRoute::Generic) {
+        fail(WVC_ERR_UNSUPPORTED, "packed weights exist only for the MFMA routes");
+        return (size_t)-1;
+    }
+    return wvc::igemm_packed_weight_bytes(pl.call);
+}
+
+int wvc_conv3d_pack_weights(const wvc_conv3d_desc *d, const void *weight, void *packed,
+                            void *stream) {
+    ConvPlan pl;
+    int rc = plan_conv(d, &pl, /*count=*/false);
+    if (rc) return rc;
+    if (pl.route == wvc::ConvRoute::Generic)
+        return fail(WVC_ERR_UNSUPPORTED, "packed weights exist only for the MFMA routes");
+    if (!weight || !packed) return fail(WVC_ERR_ARG, "weight or packed is NULL");
+    if (!aligned(weight, 2) || !aligned(packed, 16))
+        return fail(WVC_ERR_ARG, "packed weights need a 16-byte aligned buffer");
+    const size_t std_bytes = (size_t)d->c_out * d->c_in * d->kt * d->kh * d->kw * 2;
+    const Buf bufs[] = {{weight, std_bytes, false, "weight"},
+                        {packed, wvc::igemm_packed_weight_bytes(pl.call), true, "packed"}};
+    rc = check_aliasing(bufs, 2);
+    if (rc) return rc;
+    return hip_status(wvc::launch_pack_weights(pl.call, weight, packed,
+                                               static_cast<hipStream_t>(stream)),
+                      "weight packing launch");
 }
 
 int wvc_conv3d_cache_frames(const wvc_conv3d_desc *d) {
@@ -381,6 +429,7 @@ int wvc_resblock_fwd(const wvc_resblock_desc *d, const void *x, void *y,
     c1.dil_t = c1.dil_h = c1.dil_w = 1;
     c1.groups = 1;
     c1.dtype = d->dtype;
+    c1.weight_layout = d->weights_packed ? WVC_WEIGHT_PACKED : WVC_WEIGHT_STANDARD;
     wvc_conv3d_desc c2 = c1;
     c2.c_in = d->c_out;
 

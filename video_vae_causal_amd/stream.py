@@ -26,6 +26,15 @@ from . import _lib as L
 CACHE_T = 2
 
 
+def _try_pack(weight: torch.Tensor, padding) -> Optional[torch.Tensor]:
+    """Pack a layer's weights once for the MFMA routes; None when the layer
+    takes the direct route (no packed form exists)."""
+    try:
+        return L.wvc_conv3d_pack_weights(weight, padding)
+    except L.WvcError:
+        return None
+
+
 class _PingPong:
     def __init__(self, shape, dtype, device):
         self.buf = [L.empty_cl(shape, dtype, device), L.empty_cl(shape, dtype, device)]
@@ -58,6 +67,8 @@ class CausalConv3d:
         self.frames = L.wvc_conv3d_cache_frames(tuple(weight.shape))
         self.cache: Optional[_PingPong] = None
         self.ws: Optional[torch.Tensor] = None
+        self.padding = (1, 1) if weight.shape[3] == 3 else (0, 0)
+        self.packed = _try_pack(weight, self.padding)
 
     def start(self, n: int, h: int, w: int):
         c = self.weight.shape[1]
@@ -74,13 +85,15 @@ class CausalConv3d:
             self.start(x.shape[0], x.shape[3], x.shape[4])
         cin = self.cache.cin if self.frames else None
         cout = self.cache.cout if self.frames else None
+        layout = L.WVC_WEIGHT_PACKED if self.packed is not None else L.WVC_WEIGHT_STANDARD
         d = L.conv_desc(tuple(x.shape), tuple(self.weight.shape), L._dtype_code(x.dtype),
-                        padding=(1, 1) if self.weight.shape[3] == 3 else (0, 0))
+                        padding=self.padding, weight_layout=layout)
         need = L.wvc_causal_conv3d_workspace_bytes(d)
         if need and (self.ws is None or self.ws.numel() < need):
             self.ws = torch.zeros(need, dtype=torch.uint8, device=x.device)
         y = L.wvc_causal_conv3d_fwd(x, self.weight, self.bias, cin, cout, residual, y,
-                                    workspace=self.ws if need else None)
+                                    padding=self.padding, workspace=self.ws if need else None,
+                                    packed_weight=self.packed)
         if self.frames:
             self.cache.flip()
         return y
@@ -98,6 +111,10 @@ class ResBlock:
         self.c1: Optional[_PingPong] = None
         self.c2: Optional[_PingPong] = None
         self.ws: Optional[torch.Tensor] = None
+        packed = {"w1": _try_pack(params["w1"], (1, 1)), "w2": _try_pack(params["w2"], (1, 1))}
+        if params.get("w_short") is not None:
+            packed["w_short"] = _try_pack(params["w_short"], (0, 0))
+        self.packed = packed if all(v is not None for v in packed.values()) else None
 
     def start(self, n: int, h: int, w: int):
         cin = self.p["w1"].shape[1]
@@ -109,13 +126,14 @@ class ResBlock:
     def __call__(self, x: torch.Tensor, y: Optional[torch.Tensor] = None) -> torch.Tensor:
         if self.c1 is None:
             self.start(x.shape[0], x.shape[3], x.shape[4])
-        d = L.resblock_desc(tuple(x.shape), self.p["w1"].shape[0], L._dtype_code(x.dtype), self.eps)
+        d = L.resblock_desc(tuple(x.shape), self.p["w1"].shape[0], L._dtype_code(x.dtype), self.eps,
+                            weights_packed=self.packed is not None)
         need = L.wvc_resblock_workspace_bytes(d)
         if self.ws is None or self.ws.numel() < need:
             # zero-filled once: split-K counters start at zero, calls leave them so
             self.ws = torch.zeros(need, dtype=torch.uint8, device=x.device)
         y = L.wvc_resblock_fwd(x, self.p, self.c1.cin, self.c1.cout, self.c2.cin, self.c2.cout,
-                               y=y, eps=self.eps, workspace=self.ws)
+                               y=y, eps=self.eps, workspace=self.ws, packed=self.packed)
         self.c1.flip()
         self.c2.flip()
         return y
