@@ -55,6 +55,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "traffic.json"),
                     help="measured HBM bytes per launch (from rocprofv3 --pmc), if present")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run 5 plain device copies of MIB MiB (bf16) and exit: the known-size "
+                         "kernel that scales rocprofv3's FETCH_SIZE / WRITE_SIZE counters")
     return ap.parse_args()
 
 
@@ -217,7 +220,8 @@ def wl_layer96():
                 kernel=kernel, kernel_name="igemm_kernel<3, 96, 16, 2, false>",
                 kernel_units=acc.conv_flops(n, 4, h, w, c, c), kernel_bound="mfma",
                 kernel_bytes=acc.conv_launch_bytes(n, 4, h, w, c, c),
-                norm_kernel=norm_kernel, norm_bytes=acc.norm_bytes(n * c * t * h * w))
+                norm_kernel=norm_kernel, norm_kernel_name="rmsnorm_vec_kernel<true, 4>",
+                norm_bytes=acc.norm_bytes(n * c * t * h * w))
     return step, info
 
 
@@ -316,6 +320,46 @@ def cpu_baseline(workload: str):
             "sample": sample, "seconds": round(dt, 3), "flops": flops}
 
 
+def measured_traffic(path: str, key: str, kernel_name: str):
+    """HBM bytes per launch of ``kernel_name`` from rocprofv3 FETCH_SIZE and
+    WRITE_SIZE runs (scaled by the counters' reading for a copy of known size),
+    or None when there is no record or the kernel's source changed since."""
+    import hashlib
+    try:
+        entry = json.load(open(path)).get(key)
+    except (OSError, ValueError):
+        return None
+    if not entry or entry.get("kernel") != kernel_name:
+        return None
+    try:
+        src = open(os.path.join(ROOT, entry["source"]), "rb").read()
+    except (OSError, KeyError):
+        return None
+    if hashlib.sha256(src).hexdigest() != entry.get("source_sha256"):
+        return None
+    return entry.get("bytes_per_launch")
+
+
+def copy_calibration(mib: int):
+    """Five launches of torch's contiguous copy over ``mib`` MiB: each reads and
+    writes exactly that many bytes, so the counters' readings for it give the
+    scale of FETCH_SIZE and WRITE_SIZE."""
+    import torch
+    n = mib * (1 << 20) // 2
+    a = torch.ones(n, dtype=torch.bfloat16, device="cuda")
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(5):
+        b.copy_(a)
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / 5
+    print(json.dumps({"copy_bytes_read": 2 * n, "copy_bytes_written": 2 * n, "ms": round(ms, 4),
+                      "GBs_read_plus_write": round(4 * n / ms / 1e6, 1)}), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -323,6 +367,9 @@ def main():
               "(the path has no multi-GPU sharding in this build)", file=sys.stderr)
         sys.exit(2)
     import torch
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
     from video_vae_causal_amd import _lib as L
     L.load()
     torch.cuda.set_device(0)
@@ -334,15 +381,7 @@ def main():
     # dominant kernel, timed alone with events on the stream it is launched on
     k_ms, _ = time_region(info["kernel"], args.kernel_reps, 3)
     achieved = info["kernel_units"] / (k_ms * 1e-3) / 1e12
-    traffic = None
-    if os.path.exists(args.traffic_json):
-        try:
-            tj = json.load(open(args.traffic_json))
-            entry = tj.get(args.workload)
-            if entry and entry.get("kernel") == info["kernel_name"]:
-                traffic = entry.get("bytes_per_launch")
-        except (OSError, ValueError):
-            traffic = None
+    traffic = measured_traffic(args.traffic_json, args.workload, info["kernel_name"])
     roofline = {"bound": info["kernel_bound"], "achieved": round(achieved, 2),
                 "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": traffic,
@@ -367,7 +406,9 @@ def main():
         gbs = info["norm_bytes"] / (n_ms * 1e-3) / 1e9
         line["roofline_norm"] = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
                                  "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
-                                 "traffic": None, "kernel": "rmsnorm_vec_kernel",
+                                 "traffic": measured_traffic(args.traffic_json, args.workload + "/norm",
+                                                             info["norm_kernel_name"]),
+                                 "kernel": info["norm_kernel_name"],
                                  "kernel_ms": round(n_ms, 5), "bytes_per_launch": info["norm_bytes"]}
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(args.workload)
