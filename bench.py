@@ -74,13 +74,13 @@ def to_dev(a, dtype=None):
 
 
 def conv_workspace(x, w, padding=(1, 1), packed=False):
-    """Zero-filled conv workspace allocated once, outside any timed region."""
+    """Conv workspace allocated once, outside any timed region."""
     import torch
     from video_vae_causal_amd import _lib as L
     d = L.conv_desc(tuple(x.shape), tuple(w.shape), L.WVC_BF16, padding=padding,
                     weight_layout=L.WVC_WEIGHT_PACKED if packed else L.WVC_WEIGHT_STANDARD)
     need = L.wvc_causal_conv3d_workspace_bytes(d)
-    return torch.zeros(need, dtype=torch.uint8, device="cuda") if need else None
+    return torch.empty(need, dtype=torch.uint8, device="cuda") if need else None
 
 
 def time_region(fn, steps, warmup):
@@ -220,7 +220,7 @@ def wl_layer96():
                 kernel=kernel, kernel_name="igemm_kernel<3, 96, 16, 2, false>",
                 kernel_units=acc.conv_flops(n, 4, h, w, c, c), kernel_bound="mfma",
                 kernel_bytes=acc.conv_launch_bytes(n, 4, h, w, c, c),
-                norm_kernel=norm_kernel, norm_kernel_name="rmsnorm_vec_kernel<true, 4>",
+                norm_kernel=norm_kernel, norm_kernel_name="rmsnorm_flat_kernel<true, 2, true>",
                 norm_bytes=acc.norm_bytes(n * c * t * h * w))
     return step, info
 

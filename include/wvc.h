@@ -104,11 +104,10 @@ typedef struct wvc_counters {
  *   y         [N, C_out, t, h_out, w_out] written
  *   workspace / workspace_bytes: scratch of at least
  *             wvc_causal_conv3d_workspace_bytes(d) bytes (may be NULL if 0).
- *             It holds split-K partial sums and per-tile arrival counters:
- *             it must be zero-filled before its first use (wvc_cache_reset
- *             does that), and every successful call leaves it ready for the
- *             next one.  Calls that share a workspace must not overlap in
- *             time (use one stream, or one workspace per stream).
+ *             It holds split-K partial sums (and the packed weights when
+ *             standard-layout weights come in); its contents on entry do not
+ *             matter.  Calls that share a workspace must not overlap in time
+ *             (use one stream, or one workspace per stream).
  *
  * Routes: bf16 3x3x3 / stride 1 / pad 1 / dilation 1 with C_in % 8 == 0,
  * C_out % 32 == 0 and 16-byte aligned tensors takes the MFMA implicit-GEMM
@@ -200,8 +199,7 @@ typedef struct wvc_resblock_params {
  *   x [N, C_in, t, H, W] read; y [N, C_out, t, H, W] written.
  * Workspace: wvc_resblock_workspace_bytes(d) bytes (intermediates h1, a1, h2,
  * the shortcut output and the convs' scratch); it may not overlap any other
- * buffer, and like the conv workspace it must be zero-filled before its first
- * use and is left ready for the next call.
+ * buffer, and its contents on entry do not matter.
  */
 int wvc_resblock_fwd(const wvc_resblock_desc *d, const void *x, void *y,
                      const wvc_resblock_params *p, const void *cache1_in, void *cache1_out,

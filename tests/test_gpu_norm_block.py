@@ -39,6 +39,27 @@ def test_rmsnorm_silu_vs_oracle(c, dtype, beta, silu):
         check_f32(to_host(y), ref, f"norm c={c}")
 
 
+@pytest.mark.parametrize("c,h,w,dtype", [(16, 1031, 1019, "bf16"), (96, 420, 421, "bf16"),
+                                         (384, 211, 211, "bf16"), (1152, 121, 123, "bf16"),
+                                         (96, 297, 297, "f32")])
+def test_rmsnorm_silu_large_vs_oracle(c, h, w, dtype):
+    """Tensors of over two million 16-byte chunks (the launch for large
+    tensors: two chunks per thread, non-temporal accesses) whose position
+    count leaves a ragged last workgroup."""
+    shape = (1, c, 1, h, w)
+    x = inputs.quantize(inputs.normal(shape, c + 7, "x", std=1.5), dtype)
+    g = inputs.norm_gamma(c, c + 7, "g", dtype)
+    bt = inputs.norm_beta(c, c + 7, "b", dtype)
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    print(f"[case] norm large c={c} {h}x{w} {dtype}", flush=True)
+    y = L.wvc_rmsnorm_silu(to_dev(x, tdt), to_dev(g, tdt), to_dev(bt, tdt))
+    ref = oracle.silu(oracle.rms_norm(f64(x), f64(g), f64(bt)))
+    if dtype == "bf16":
+        check_bf16(to_host(y), ref, f"norm large c={c}")
+    else:
+        check_f32(to_host(y), ref, f"norm large c={c}")
+
+
 def test_rmsnorm_zero_vector_gives_beta():
     c = 96
     x = torch.zeros((1, c, 1, 2, 3), dtype=torch.bfloat16, device="cuda").contiguous(
@@ -115,9 +136,9 @@ def test_resblock_384_60x104_five_frames_one_at_a_time():
 def test_resblock_mixed_chunk_lengths_share_one_workspace():
     """Chunks of different lengths through one block (one workspace): at 384
     channels and 30x52 a 4-frame chunk runs unsplit while a 1-frame chunk
-    splits K, so the workspace's split-K counters must survive the longer
-    chunk's activations.  Regression test for a layout that placed them after
-    the chunk-length-dependent intermediates."""
+    splits K, so the split-K scratch and the chunk-length-dependent
+    intermediates share the workspace in different proportions from call to
+    call.  Regression test for a workspace layout that let them collide."""
     r = inputs.resblock_inputs(seed=31, shape=(1, 384, 8, 30, 52))
     xd = to_dev(r["x"])
     ref, _, _ = oracle.resblock(f64(r["x"]), block_params_f64(r["p"]), bf16=True)

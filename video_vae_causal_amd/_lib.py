@@ -251,8 +251,8 @@ def wvc_causal_conv3d_fwd(x: torch.Tensor, weight: torch.Tensor, bias: Optional[
     ws_bytes = 0
     if workspace is None:
         need = wvc_causal_conv3d_workspace_bytes(d)
-        if need:  # zero-filled: the split-K counters must start at zero
-            workspace = torch.zeros(need, dtype=torch.uint8, device=x.device)
+        if need:  # contents on entry do not matter
+            workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
     if workspace is not None:
         ws_bytes = workspace.numel() * workspace.element_size()
     _check(lib.wvc_causal_conv3d_fwd(ctypes.byref(d), _ptr(x), _ptr(cache_in), _ptr(cache_out),
@@ -319,8 +319,8 @@ def wvc_resblock_fwd(x: torch.Tensor, params: dict, cache1_in=None, cache1_out=N
     if y is None:
         y = empty_cl((x.shape[0], c_out) + tuple(x.shape[2:]), x.dtype, x.device)
     need = wvc_resblock_workspace_bytes(d)
-    if workspace is None and need:  # zero-filled: the split-K counters must start at zero
-        workspace = torch.zeros(need, dtype=torch.uint8, device=x.device)
+    if workspace is None and need:  # contents on entry do not matter
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     p = ResblockParams()
     for f, _ in ResblockParams._fields_:

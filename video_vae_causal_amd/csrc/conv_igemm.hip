@@ -15,35 +15,33 @@
 // halo tile held in LDS.
 //
 // Work decomposition
-//   workgroup : 256 threads (4 waves), CO_T output channels x 256 output
-//               positions of one output frame; the positions form a TH x TW
-//               spatial tile chosen by the host (TH*TW == 256).
+//   workgroup : 256 threads (4 waves), one per CU (up to 512 registers per
+//               lane), CO_T output channels x 256 output positions of one
+//               output frame; the positions form a TH x TW spatial tile chosen
+//               by the host (TH*TW == 256).
 //   K loop    : over work units (kt, 32-channel block).  A unit stages the
 //               halo of ONE input frame (t-2+kt: cache or chunk) for 32 input
 //               channels in LDS as [k-group(4)][(TH+2)(TW+2)][8 channels]
-//               (16 B entries, so the 16 lanes of one k-group read 16
-//               neighbouring positions as one contiguous run), then runs its
-//               9 spatial taps, each reading its B fragments from the same tile
-//               at a shifted offset.  The three temporal taps accumulate into
-//               the same registers: no per-slice batches exist.
+//               (16 B entries, so the lanes of one k-group read neighbouring
+//               positions as one contiguous run), then runs its 9 spatial
+//               taps, each reading its B fragments from the same tile at a
+//               shifted offset.  The three temporal taps accumulate into the
+//               same registers: no per-slice batches exist.
 //   waves     : 2 (channels) x 2 (positions); a wave owns CO_T/2 x 128 outputs
-//               as 16x16 MFMA tiles (v_mfma_f32_16x16x32_bf16).  Within a unit
-//               the A (weights, global) and B (LDS) fragments of tap k+1 are
-//               fetched while the MFMAs of tap k run (register ping-pong).
-//               Two workgroups share a CU, so one stages while the other
-//               computes.
+//               as M x M MFMA tiles (32x32x16 for 128 channels, 16x16x32 for
+//               96 and 64).  The pipeline is described at the kernel.
 //   loads     : buffer loads with the frame as the buffer range: positions
 //               outside the frame and channels past C_in read as zero in
 //               hardware, so staging has no branches.
 //   split-K   : small grids (one 60x104 or 30x52 frame) split the units of a
-//               tile over S workgroups.  Each writes fp32 partials in MFMA
-//               fragment order; the last to arrive (atomic counter) sums the S
-//               partials in split order -- deterministic, no float atomics --
-//               and runs the epilogue, then re-arms the counter for the next
-//               call.  Counters sit at a fixed offset (the workspace's first
-//               CTR_CAP words), partials after them.
+//               tile over S workgroups.  Each writes its fp32 partial sums in
+//               the output layout to the workspace (plain stores, no
+//               inter-workgroup synchronisation), and a second kernel adds the
+//               S partials in split order (deterministic), then bias and
+//               residual, and rounds once.
 //   epilogue  : + bias, + residual (fused block shortcut), one rounding to
-//               bf16, 8-byte stores of 4 consecutive channels.
+//               bf16, 8-byte stores of 4 consecutive channels.  Bias and
+//               residual are loaded before the first store.
 //   cache     : the workgroups of the chunk's last output frame (channel tile
 //               0) also write the interior of the halos they stage for frames
 //               T-2 and T-1 to cache_out: the rolling cache update costs no
@@ -64,11 +62,6 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int POS_T = 256;
-// Split-K arrival counters live at a fixed place -- the first CTR_CAP words of
-// the workspace -- so that a workspace reused by calls of different shapes
-// never finds partial sums where a later call expects a zeroed counter.
-constexpr int CTR_CAP = 4096;
-constexpr size_t CTR_BYTES = CTR_CAP * sizeof(uint32_t);
 constexpr uint32_t OOB = 0x80000000u;  // an offset past every buffer range used here
 constexpr int RSRC_WORD3 = 0x00020000;  // raw buffer, range-checked (CDNA data format)
 
@@ -80,8 +73,8 @@ struct IgParams {
     const uint16_t *res;
     uint16_t *y;
     uint16_t *cache_out;
-    float *part;
-    uint32_t *ctr;
+    float *part;  // split-K partial sums: [S][N][T][H][W][Cout] fp32
+    size_t part_stride;  // N*T*H*W*Cout: elements of one split's partials
     int T, H, W, Cin, Cout, F;
     int TH, TW, HC, HP;
     int tiles_w, tiles_h, co_tiles;
@@ -173,7 +166,6 @@ igemm_kernel(IgParams p) {
     static_assert(NIT <= 32, "staging mask");
 
     __shared__ uint4 halo[2][4 * HPM];
-    __shared__ int s_last;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
@@ -185,7 +177,6 @@ igemm_kernel(IgParams p) {
     int L = xcd_remap(blockIdx.x, p.total);
     const int s = SPLIT ? L % p.S : 0;
     if (SPLIT) L /= p.S;
-    const int tile_id = L;
     // Order of the logical tiles: channel tile fastest (large grids: the tiles
     // of one spatial block share its halo in L2) or slowest (small grids: each
     // XCD then works on one channel tile, so its weight slice stays in L2).
@@ -379,50 +370,59 @@ igemm_kernel(IgParams p) {
         }
     }
 
-    if (SPLIT) {
-        // Partials in MFMA fragment order: lane-contiguous 16-byte stores.
-        constexpr int TILE_F = POS_T * CO_T;
-        constexpr int WAVE_F = FCO * FPOS * 64 * ACC;
-        float *mine = p.part + ((size_t)tile_id * p.S + s) * TILE_F + (size_t)wave * WAVE_F;
-#pragma unroll
-        for (int i = 0; i < FCO; ++i)
-#pragma unroll
-            for (int j = 0; j < FPOS; ++j)
-#pragma unroll
-                for (int e = 0; e < ACC; e += 4)
-                    *reinterpret_cast<f32x4 *>(mine + ((i * FPOS + j) * 64 + lane) * ACC + e) =
-                        f32x4{acc[i][j][e], acc[i][j][e + 1], acc[i][j][e + 2], acc[i][j][e + 3]};
-        __threadfence();
-        __syncthreads();
-        if (tid == 0) s_last = (atomicAdd(p.ctr + tile_id, 1u) == (unsigned)(p.S - 1));
-        __syncthreads();
-        if (!s_last) return;
-        __threadfence();
-        const float *base = p.part + (size_t)tile_id * p.S * TILE_F + (size_t)wave * WAVE_F;
-#pragma unroll
-        for (int i = 0; i < FCO; ++i)
-#pragma unroll
-            for (int j = 0; j < FPOS; ++j)
-#pragma unroll
-                for (int e = 0; e < ACC; e += 4) {
-                    f32x4 sum = f32x4{0.f, 0.f, 0.f, 0.f};
-                    for (int ss = 0; ss < p.S; ++ss) {
-                        const f32x4 pv =
-                            ss == s ? f32x4{acc[i][j][e], acc[i][j][e + 1], acc[i][j][e + 2], acc[i][j][e + 3]}
-                                    : *reinterpret_cast<const f32x4 *>(
-                                          base + (size_t)ss * TILE_F + ((i * FPOS + j) * 64 + lane) * ACC + e);
-                        sum += pv;
-                    }
-                    acc[i][j][e] = sum[0];
-                    acc[i][j][e + 1] = sum[1];
-                    acc[i][j][e + 2] = sum[2];
-                    acc[i][j][e + 3] = sum[3];
-                }
-        if (tid == 0) p.ctr[tile_id] = 0u;  // re-armed for the next call
-    }
-
     // Epilogue.  Accumulator element e of tile (i, j) is output channel
     // co0 + i*M + (e/4)*8 + lg*4 + e%4 at position wpos*WPOS + j*M + lr.
+    if (SPLIT) {
+        // fp32 partial sums of this split, in the output layout; the reduce
+        // kernel adds bias and residual.
+        float *mine = p.part + (size_t)s * p.part_stride;
+#pragma unroll
+        for (int j = 0; j < FPOS; ++j) {
+            const int q = wpos * WPOS + j * M + lr;
+            const int r = q / p.TW, c = q - r * p.TW;
+            const int h = h0 + r, w = w0 + c;
+            if (h >= p.H || w >= p.W) continue;
+            const size_t obase = (((size_t)(n * p.T + t) * p.H + h) * p.W + w) * p.Cout;
+#pragma unroll
+            for (int i = 0; i < FCO; ++i)
+#pragma unroll
+                for (int e4 = 0; e4 < ACC / 4; ++e4) {
+                    const int co = co0 + i * M + e4 * 8 + lg * 4;
+                    *reinterpret_cast<f32x4 *>(mine + obase + co) =
+                        f32x4{acc[i][j][e4 * 4], acc[i][j][e4 * 4 + 1], acc[i][j][e4 * 4 + 2],
+                              acc[i][j][e4 * 4 + 3]};
+                }
+        }
+        return;
+    }
+    // Global loads and stores share one completion counter, so every bias
+    // and residual load is issued before the first store: a load issued after
+    // a store would wait for that store too.
+    uint2 bb[FCO][ACC / 4];
+    uint2 rr[FPOS][FCO][ACC / 4];
+#pragma unroll
+    for (int i = 0; i < FCO; ++i)
+#pragma unroll
+        for (int e4 = 0; e4 < ACC / 4; ++e4) {
+            const int co = co0 + i * M + e4 * 8 + lg * 4;
+            bb[i][e4] = p.bias ? *reinterpret_cast<const uint2 *>(p.bias + co) : make_uint2(0u, 0u);
+        }
+#pragma unroll
+    for (int j = 0; j < FPOS; ++j) {
+        const int q = wpos * WPOS + j * M + lr;
+        const int r = q / p.TW, c = q - r * p.TW;
+        const int h = h0 + r, w = w0 + c;
+        const bool inside = h < p.H && w < p.W;
+        const size_t obase = (((size_t)(n * p.T + t) * p.H + h) * p.W + w) * p.Cout;
+#pragma unroll
+        for (int i = 0; i < FCO; ++i)
+#pragma unroll
+            for (int e4 = 0; e4 < ACC / 4; ++e4) {
+                const int co = co0 + i * M + e4 * 8 + lg * 4;
+                rr[j][i][e4] = (p.res && inside) ? *reinterpret_cast<const uint2 *>(p.res + obase + co)
+                                                 : make_uint2(0u, 0u);
+            }
+    }
 #pragma unroll
     for (int j = 0; j < FPOS; ++j) {
         const int q = wpos * WPOS + j * M + lr;
@@ -437,19 +437,19 @@ igemm_kernel(IgParams p) {
                 const int co = co0 + i * M + e4 * 8 + lg * 4;
                 float v[4] = {acc[i][j][e4 * 4], acc[i][j][e4 * 4 + 1], acc[i][j][e4 * 4 + 2],
                               acc[i][j][e4 * 4 + 3]};
+                // the sum, then the bias, then the residual: the order the
+                // split-K reduce kernel uses too
                 if (p.bias) {
-                    const uint2 bb = *reinterpret_cast<const uint2 *>(p.bias + co);
-                    v[0] += bf16_to_f32(bb.x & 0xffffu);
-                    v[1] += bf16_to_f32(bb.x >> 16);
-                    v[2] += bf16_to_f32(bb.y & 0xffffu);
-                    v[3] += bf16_to_f32(bb.y >> 16);
+                    v[0] += bf16_to_f32(bb[i][e4].x & 0xffffu);
+                    v[1] += bf16_to_f32(bb[i][e4].x >> 16);
+                    v[2] += bf16_to_f32(bb[i][e4].y & 0xffffu);
+                    v[3] += bf16_to_f32(bb[i][e4].y >> 16);
                 }
                 if (p.res) {
-                    const uint2 rr = *reinterpret_cast<const uint2 *>(p.res + obase + co);
-                    v[0] += bf16_to_f32(rr.x & 0xffffu);
-                    v[1] += bf16_to_f32(rr.x >> 16);
-                    v[2] += bf16_to_f32(rr.y & 0xffffu);
-                    v[3] += bf16_to_f32(rr.y >> 16);
+                    v[0] += bf16_to_f32(rr[j][i][e4].x & 0xffffu);
+                    v[1] += bf16_to_f32(rr[j][i][e4].x >> 16);
+                    v[2] += bf16_to_f32(rr[j][i][e4].y & 0xffffu);
+                    v[3] += bf16_to_f32(rr[j][i][e4].y >> 16);
                 }
                 uint2 o;
                 o.x = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
@@ -457,6 +457,47 @@ igemm_kernel(IgParams p) {
                 *reinterpret_cast<uint2 *>(p.y + obase + co) = o;
             }
     }
+}
+
+// Split-K reduction: y = round(sum_s part[s] (in split order) + bias + residual),
+// 8 consecutive channels (one 16-byte output store) per thread.
+__global__ void __launch_bounds__(256) splitk_reduce_kernel(const float *__restrict__ part,
+                                                            size_t stride, int S,
+                                                            const uint16_t *__restrict__ bias,
+                                                            const uint16_t *__restrict__ res,
+                                                            uint16_t *__restrict__ y, long groups,
+                                                            int cout) {
+    const long gi = (long)blockIdx.x * 256 + threadIdx.x;
+    if (gi >= groups) return;
+    const size_t e0 = (size_t)gi * 8;
+    const int co = (int)(e0 % (size_t)cout);
+    const uint4 bv = bias ? *reinterpret_cast<const uint4 *>(bias + co) : make_uint4(0u, 0u, 0u, 0u);
+    const uint4 rv = res ? *reinterpret_cast<const uint4 *>(res + e0) : make_uint4(0u, 0u, 0u, 0u);
+    float v[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) v[k] = 0.f;
+    for (int sp = 0; sp < S; ++sp) {
+        const f32x4 a = *reinterpret_cast<const f32x4 *>(part + sp * stride + e0);
+        const f32x4 b = *reinterpret_cast<const f32x4 *>(part + sp * stride + e0 + 4);
+        v[0] += a[0]; v[1] += a[1]; v[2] += a[2]; v[3] += a[3];
+        v[4] += b[0]; v[5] += b[1]; v[6] += b[2]; v[7] += b[3];
+    }
+    const uint32_t bw[4] = {bv.x, bv.y, bv.z, bv.w}, rw[4] = {rv.x, rv.y, rv.z, rv.w};
+    uint32_t o[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        float lo = v[2 * k], hi = v[2 * k + 1];
+        if (bias) {
+            lo += bf16_to_f32(bw[k] & 0xffffu);
+            hi += bf16_to_f32(bw[k] >> 16);
+        }
+        if (res) {
+            lo += bf16_to_f32(rw[k] & 0xffffu);
+            hi += bf16_to_f32(rw[k] >> 16);
+        }
+        o[k] = (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+    }
+    *reinterpret_cast<uint4 *>(y + e0) = make_uint4(o[0], o[1], o[2], o[3]);
 }
 
 // Packs W[co][tap][ci] into MFMA fragment order for tile edge M:
@@ -563,7 +604,7 @@ Plan make_plan(const ConvCall &c, ConvRoute r) {
     // (rounds of resident workgroups) * (units per split + fixed cost).
     int best_s = 1;
     double best_cost = -1.0;
-    const int s_max = pl.tiles <= CTR_CAP ? pl.U : 1;
+    const int s_max = pl.U;
     for (int s = 1; s <= s_max && s <= 64; ++s) {
         const long wgs = pl.tiles * s;
         const double rounds = (double)((wgs + slots - 1) / slots);
@@ -577,9 +618,11 @@ Plan make_plan(const ConvCall &c, ConvRoute r) {
     return pl;
 }
 
-size_t part_bytes(const Plan &pl) {
+size_t out_elems(const ConvCall &c) { return (size_t)c.n * c.t * c.h * c.w * c.cout; }
+
+size_t part_bytes(const Plan &pl, const ConvCall &c) {
     if (pl.S <= 1) return 0;
-    return (size_t)pl.tiles * pl.S * POS_T * pl.co_t * sizeof(float);
+    return (size_t)pl.S * out_elems(c) * sizeof(float);
 }
 
 int tile_m(int co_t) { return (co_t == 96 || co_t == 64) ? 16 : 32; }
@@ -591,12 +634,10 @@ size_t packed_bytes(const ConvCall &c) {
 
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
-// Workspace: [split-K counters, CTR_BYTES][partials][packed weights when the
-// call brings standard-layout weights].  The counter words always come first
-// so a workspace shared by calls of different plans keeps them zeroed.
+// Workspace: [split-K partial sums][packed weights when the call brings
+// standard-layout weights].  Its contents on entry do not matter.
 size_t ws_bytes_for(const Plan &pl, const ConvCall &c, bool need_pack) {
-    if (pl.S <= 1 && !need_pack) return 0;
-    return CTR_BYTES + align256(part_bytes(pl)) + (need_pack ? align256(packed_bytes(c)) : 0);
+    return align256(part_bytes(pl, c)) + (need_pack ? align256(packed_bytes(c)) : 0);
 }
 
 template <int KS, int CO_T, int M, int WAVES_CO>
@@ -609,8 +650,6 @@ hipError_t launch_variant(const IgParams &p, hipStream_t s) {
 }
 
 }  // namespace
-
-size_t igemm_counter_bytes() { return CTR_BYTES; }
 
 size_t igemm_workspace_bytes(const ConvCall &c, ConvRoute r, bool packed_given) {
     if (c.t <= 0) return 0;
@@ -652,7 +691,7 @@ hipError_t launch_conv_igemm(const ConvCall &c, ConvRoute r, bool packed_given, 
         return hipErrorInvalidValue;
     const void *wp = c.weight;
     if (!packed_given) {
-        void *dst = static_cast<char *>(ws) + CTR_BYTES + align256(part_bytes(pl));
+        void *dst = static_cast<char *>(ws) + align256(part_bytes(pl, c));
         const hipError_t e = launch_pack_weights(c, c.weight, dst, s);
         if (e != hipSuccess) return e;
         wp = dst;
@@ -684,8 +723,8 @@ hipError_t launch_conv_igemm(const ConvCall &c, ConvRoute r, bool packed_given, 
     p.frame_bytes = (uint32_t)((size_t)c.h * c.w * c.cin * 2);
     p.w_bytes = (uint32_t)packed_bytes(c);
     if (pl.S > 1) {
-        p.ctr = static_cast<uint32_t *>(ws);
-        p.part = reinterpret_cast<float *>(static_cast<char *>(ws) + CTR_BYTES);
+        p.part = static_cast<float *>(ws);
+        p.part_stride = out_elems(c);
     }
     const long total = pl.tiles * pl.S;
     if (total <= 0) return hipSuccess;
@@ -695,12 +734,20 @@ hipError_t launch_conv_igemm(const ConvCall &c, ConvRoute r, bool packed_given, 
     // 128 channels: 32x32x16 MFMAs on 2 x 2 waves of 64 x 128.  96 and 64:
     // 16x16x32 MFMAs on 2 x 2 waves (48 or 32 channels x 128 positions).
     // 32: 32x32x16 on 1 x 4 waves of 32 x 64.
+    hipError_t e;
     switch (pl.co_t) {
-        case 128: return k3 ? launch_variant<3, 128, 32, 2>(p, s) : launch_variant<1, 128, 32, 2>(p, s);
-        case 96: return k3 ? launch_variant<3, 96, 16, 2>(p, s) : launch_variant<1, 96, 16, 2>(p, s);
-        case 64: return k3 ? launch_variant<3, 64, 16, 2>(p, s) : launch_variant<1, 64, 16, 2>(p, s);
-        default: return k3 ? launch_variant<3, 32, 32, 1>(p, s) : launch_variant<1, 32, 32, 1>(p, s);
+        case 128: e = k3 ? launch_variant<3, 128, 32, 2>(p, s) : launch_variant<1, 128, 32, 2>(p, s); break;
+        case 96: e = k3 ? launch_variant<3, 96, 16, 2>(p, s) : launch_variant<1, 96, 16, 2>(p, s); break;
+        case 64: e = k3 ? launch_variant<3, 64, 16, 2>(p, s) : launch_variant<1, 64, 16, 2>(p, s); break;
+        default: e = k3 ? launch_variant<3, 32, 32, 1>(p, s) : launch_variant<1, 32, 32, 1>(p, s); break;
     }
+    if (e != hipSuccess || pl.S <= 1) return e;
+    const long groups = (long)(out_elems(c) / 8);  // Cout % 32 == 0 on this route
+    const long blocks = (groups + 255) / 256;
+    if (blocks > 0x7fffffffL) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)blocks), dim3(256), 0, s, p.part,
+                       p.part_stride, pl.S, p.bias, p.res, p.y, groups, c.cout);
+    return hipGetLastError();
 }
 
 }  // namespace wvc

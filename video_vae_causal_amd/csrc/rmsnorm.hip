@@ -6,21 +6,18 @@
 // y_c = u_c * sigmoid(u_c).  fp32 inside, one rounding at the store.
 //
 // Bandwidth-bound: every element is read once and written once.  With the
-// channels-last layout one position's C channels are contiguous, so a group of
-// LPP lanes owns a position and the C/VEC 16-byte chunks are spread over the
-// group as chunk j + LPP*i (i < CH): for every i the group reads one
-// contiguous run, and consecutive groups read consecutive positions, so each
-// load instruction of a wave covers 64/LPP adjacent positions.  The sum of
-// squares is reduced across the group with lane shuffles (no LDS).  gamma and
-// beta are loaded once per thread: a lane sees the same channels at every
-// position it handles.
+// channels-last layout one position's C channels are contiguous, so a run of
+// whole positions is one contiguous block of memory; the kernel below streams
+// such blocks with fully coalesced 16-byte accesses and does the per-position
+// reduction in LDS.
 #include "wvc_internal.h"
 #include "wvc.h"
 
 namespace wvc {
 namespace {
 
-constexpr int MAX_CH = 8;
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 template <bool BF16>
 struct Vec;
@@ -35,11 +32,14 @@ struct Vec<true> {
             o[2 * k + 1] = bf16_to_f32(w[k] >> 16);
         }
     }
+    // gfx950's v_cvt_pk_bf16_f32: two floats to bf16, round to nearest even,
+    // in one instruction (the store-side rounding is most of this kernel's ALU
+    // work otherwise).
     __device__ static uint4 pack(const float *o) {
         uint32_t w[4];
 #pragma unroll
         for (int k = 0; k < 4; ++k)
-            w[k] = (uint32_t)f32_to_bf16(o[2 * k]) | ((uint32_t)f32_to_bf16(o[2 * k + 1]) << 16);
+            w[k] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{o[2 * k], o[2 * k + 1]}, bf16x2));
         return make_uint4(w[0], w[1], w[2], w[3]);
     }
 };
@@ -60,66 +60,112 @@ struct Vec<false> {
 
 template <bool BF16>
 __device__ __forceinline__ float silu(float u) {
-    // u * sigmoid(u) = u / (1 + e^-u); bf16 output tolerates the fast exp.
-    if (BF16) return u / (1.f + __expf(-u));
+    // u * sigmoid(u) = u / (1 + e^-u).  For a bf16 result the hardware exp2
+    // and reciprocal (about 1 ulp of fp32 each) are far inside the final
+    // rounding; the fp32 path keeps the accurate exp and division.
+    if (BF16) return u * __builtin_amdgcn_rcpf(1.f + __expf(-u));
     return u / (1.f + expf(-u));
 }
 
-template <bool BF16, int LPP>
-__global__ void __launch_bounds__(256) rmsnorm_vec_kernel(const uint4 *__restrict__ x,
-                                                          const uint4 *__restrict__ gamma,
-                                                          const uint4 *__restrict__ beta,
-                                                          uint4 *__restrict__ y, long positions,
-                                                          int chunks, int ch, float scale,
-                                                          float eps, int apply_silu) {
-    using V = Vec<BF16>;
-    const long gid = (long)blockIdx.x * 256 + threadIdx.x;
-    const long pos = gid / LPP;
-    const int j = (int)(gid % LPP);
-    // Every lane of a group takes part in the shuffles, so no early return
-    // before the reduction; lanes past the end load nothing.
-    const bool live = pos < positions;
+// Flat layout: a workgroup owns P whole positions, i.e. P*cpp consecutive
+// 16-byte chunks (cpp = chunks per position), and thread t takes chunks
+// t + 256k (k < K).  Every load and store instruction of a wave then covers
+// one contiguous 1 KiB run, whatever C is, so each cache line is read and
+// written whole by one instruction.  Per-position sums of squares go through
+// LDS: each chunk's partial sum is stored, R lanes per position add them up
+// (shuffles inside the R-lane group), and the reciprocal scale comes back
+// through LDS.  gamma and beta are staged in LDS once per workgroup.
+constexpr int FLAT_MAX_CPP = 256;
 
-    uint4 raw[MAX_CH];
-    float s = 0.f;
+// Non-temporal 16-byte accesses for tensors far larger than the caches: the
+// data is touched once, so it should not push other lines out of L2 / MALL.
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 ld_stream(const uint4 *p) {
+    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ void st_stream(uint4 *p, uint4 v) {
+    __builtin_nontemporal_store(u32x4{v.x, v.y, v.z, v.w}, reinterpret_cast<u32x4 *>(p));
+}
+
+template <bool BF16, int K, bool STREAM>
+__global__ void __launch_bounds__(256) rmsnorm_flat_kernel(const uint4 *__restrict__ x,
+                                                           const uint4 *__restrict__ gamma,
+                                                           const uint4 *__restrict__ beta,
+                                                           uint4 *__restrict__ y, long positions,
+                                                           int cpp, int P, int R, float scale,
+                                                           float eps, int apply_silu) {
+    using V = Vec<BF16>;
+    __shared__ float part[256 * K];
+    __shared__ float rinv[256 * K];
+    __shared__ uint4 g_s[FLAT_MAX_CPP];
+    __shared__ uint4 b_s[FLAT_MAX_CPP];
+    const int tid = threadIdx.x;
+    const long pos0 = (long)blockIdx.x * P;
+    const long left = positions - pos0;
+    const int np = left < P ? (int)left : P;
+    const int nchunks = np * cpp;
+    const uint4 *xb = x + pos0 * cpp;
+    uint4 *yb = y + pos0 * cpp;
+
+    uint4 raw[K];
 #pragma unroll
-    for (int i = 0; i < MAX_CH; ++i) {
-        if (i < ch && live) {
-            raw[i] = x[pos * chunks + j + LPP * i];
-            float f[V::N];
-            V::unpack(raw[i], f);
+    for (int k = 0; k < K; ++k) {
+        const int f = tid + 256 * k;
+        raw[k] = make_uint4(0u, 0u, 0u, 0u);
+        if (f < nchunks) raw[k] = STREAM ? ld_stream(xb + f) : xb[f];
+    }
+    for (int c = tid; c < cpp; c += 256) {
+        g_s[c] = gamma[c];
+        b_s[c] = beta ? beta[c] : make_uint4(0u, 0u, 0u, 0u);
+    }
+    float v[K][V::N];  // unpacked once, used by both passes
 #pragma unroll
-            for (int k = 0; k < V::N; ++k) s = fmaf(f[k], f[k], s);
+    for (int k = 0; k < K; ++k) {
+        const int f = tid + 256 * k;
+        V::unpack(raw[k], v[k]);
+        if (f < nchunks) {
+            float s = 0.f;
+#pragma unroll
+            for (int e = 0; e < V::N; ++e) s = fmaf(v[k][e], v[k][e], s);
+            part[f] = s;
         }
     }
+    __syncthreads();
+    // R lanes (a power of two dividing 64) per position; every lane of a group
+    // runs the same number of iterations, so the shuffles always pair live lanes.
+    for (int pp = tid / R; pp < np; pp += 256 / R) {
+        const int sub = tid % R;
+        float s = 0.f;
+        for (int c = sub; c < cpp; c += R) s += part[pp * cpp + c];
+        for (int off = R / 2; off > 0; off >>= 1) s += __shfl_xor(s, off, 64);
+        if (sub == 0) rinv[pp] = scale / fmaxf(sqrtf(s), eps);
+    }
+    __syncthreads();
 #pragma unroll
-    for (int off = LPP / 2; off > 0; off >>= 1) s += __shfl_xor(s, off, 64);
-    if (!live) return;
-    const float r = scale / fmaxf(sqrtf(s), eps);
+    for (int k = 0; k < K; ++k) {
+        const int f = tid + 256 * k;
+        if (f < nchunks) {
+            const int pp = f / cpp, c = f - pp * cpp;
+            const float r = rinv[pp];
+            float g[V::N], b[V::N], o[V::N];
+            V::unpack(g_s[c], g);
+            V::unpack(b_s[c], b);
 #pragma unroll
-    for (int i = 0; i < MAX_CH; ++i) {
-        if (i < ch) {
-            const int chunk = j + LPP * i;
-            float f[V::N], g[V::N], b[V::N];
-            V::unpack(raw[i], f);
-            V::unpack(gamma[chunk], g);
-            if (beta)
-                V::unpack(beta[chunk], b);
-            else
-#pragma unroll
-                for (int k = 0; k < V::N; ++k) b[k] = 0.f;
-#pragma unroll
-            for (int k = 0; k < V::N; ++k) {
-                const float u = f[k] * r * g[k] + b[k];
-                f[k] = apply_silu ? silu<BF16>(u) : u;
+            for (int e = 0; e < V::N; ++e) {
+                const float u = fmaf(v[k][e] * r, g[e], b[e]);
+                o[e] = apply_silu ? silu<BF16>(u) : u;
             }
-            y[pos * chunks + chunk] = V::pack(f);
+            if (STREAM)
+                st_stream(yb + f, V::pack(o));
+            else
+                yb[f] = V::pack(o);
         }
     }
 }
 
 // Any C: one thread per position, scalar loop (used when C is not a multiple
-// of the 16-byte vector or needs more than MAX_CH chunks per lane).
+// of the 16-byte vector, unaligned tensors, or more than FLAT_MAX_CPP chunks).
 template <bool BF16>
 __global__ void __launch_bounds__(256) rmsnorm_scalar_kernel(const void *xv, const void *gv,
                                                              const void *bv, void *yv,
@@ -147,16 +193,32 @@ __global__ void __launch_bounds__(256) rmsnorm_scalar_kernel(const void *xv, con
     }
 }
 
-template <bool BF16, int LPP>
-hipError_t launch_vec(const void *x, const void *g, const void *b, void *y, long positions,
-                      int chunks, int ch, float scale, float eps, int silu_on, hipStream_t s) {
-    const long threads = positions * LPP;
-    const long blocks = (threads + 255) / 256;
+int num_cus_norm() {
+    static int cached = 0;
+    if (!cached) {
+        int dev = 0, cus = 0;
+        if (hipGetDevice(&dev) == hipSuccess &&
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+            cus > 0)
+            cached = cus;
+        else
+            cached = 256;
+    }
+    return cached;
+}
+
+template <bool BF16, int K, bool STREAM>
+hipError_t launch_flat(const void *x, const void *g, const void *b, void *y, long positions,
+                       int cpp, float scale, float eps, int silu_on, hipStream_t s) {
+    const int P = 256 * K / cpp;  // whole positions per workgroup (cpp <= 256 * K)
+    int R = 1;                     // reducer lanes per position: power of two, <= 64
+    while (R < 64 && 2 * R * P <= 256 && 2 * R <= cpp) R *= 2;
+    const long blocks = (positions + P - 1) / P;
     if (blocks > 0x7fffffffL) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((rmsnorm_vec_kernel<BF16, LPP>), dim3((unsigned)blocks), dim3(256), 0, s,
+    hipLaunchKernelGGL((rmsnorm_flat_kernel<BF16, K, STREAM>), dim3((unsigned)blocks), dim3(256), 0, s,
                        static_cast<const uint4 *>(x), static_cast<const uint4 *>(g),
-                       static_cast<const uint4 *>(b), static_cast<uint4 *>(y), positions, chunks,
-                       ch, scale, eps, silu_on);
+                       static_cast<const uint4 *>(b), static_cast<uint4 *>(y), positions, cpp, P,
+                       R, scale, eps, silu_on);
     return hipGetLastError();
 }
 
@@ -167,20 +229,16 @@ hipError_t dispatch(const void *x, const void *g, const void *b, void *y, long p
     constexpr int VN = Vec<BF16>::N;
     const bool aligned = ((uintptr_t)x % 16 == 0) && ((uintptr_t)y % 16 == 0) &&
                          ((uintptr_t)g % 16 == 0) && ((uintptr_t)b % 16 == 0);
-    if (c % VN == 0 && aligned) {
-        const int chunks = c / VN;
-        int lpp = 1;
-        while (lpp < 16 && chunks % (lpp * 2) == 0) lpp *= 2;
-        const int ch = chunks / lpp;
-        if (ch <= MAX_CH) {
-            switch (lpp) {
-                case 1: return launch_vec<BF16, 1>(x, g, b, y, positions, chunks, ch, scale, eps, silu_on, s);
-                case 2: return launch_vec<BF16, 2>(x, g, b, y, positions, chunks, ch, scale, eps, silu_on, s);
-                case 4: return launch_vec<BF16, 4>(x, g, b, y, positions, chunks, ch, scale, eps, silu_on, s);
-                case 8: return launch_vec<BF16, 8>(x, g, b, y, positions, chunks, ch, scale, eps, silu_on, s);
-                default: return launch_vec<BF16, 16>(x, g, b, y, positions, chunks, ch, scale, eps, silu_on, s);
-            }
-        }
+    if (c % VN == 0 && aligned && c / VN <= FLAT_MAX_CPP) {
+        const int cpp = c / VN;
+        // Large tensors (far beyond L2): two chunks per thread, non-temporal
+        // accesses.  Small ones (one frame of a streamed block, read again by
+        // the next conv while it is still in L2): one chunk per thread, so the
+        // grid still covers every CU several times, and ordinary stores.
+        const long chunks = positions * cpp;
+        if (chunks >= 8L * 1024 * num_cus_norm())
+            return launch_flat<BF16, 2, true>(x, g, b, y, positions, cpp, scale, eps, silu_on, s);
+        return launch_flat<BF16, 1, false>(x, g, b, y, positions, cpp, scale, eps, silu_on, s);
     }
     const long blocks = (positions + 255) / 256;
     if (blocks > 0x7fffffffL) return hipErrorInvalidValue;

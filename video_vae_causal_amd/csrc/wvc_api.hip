@@ -281,10 +281,8 @@ int plan_block(const wvc_resblock_desc *d, BlockLayout *L) {
     if (d->weights_packed != 0 && d->weights_packed != 1)
         return fail(WVC_ERR_ARG, "weights_packed must be 0 or 1");
     const size_t pos = (size_t)d->n * d->t * d->h * d->w;
-    // The convs' scratch comes first and always reserves the split-K counter
-    // words at offset 0, whatever this chunk length needs: a later call with a
-    // different chunk length (and split) then still finds its counters zeroed
-    // instead of an earlier call's activations.
+    // The convs' scratch (split-K partials, packed weights) comes first, sized
+    // for the largest of the block's convs; the intermediates follow.
     wvc_conv3d_desc c{};
     c.n = d->n; c.c_in = d->c_in; c.c_out = d->c_out; c.t = d->t; c.h = d->h; c.w = d->w;
     c.kt = c.kh = c.kw = 3;
@@ -294,7 +292,7 @@ int plan_block(const wvc_resblock_desc *d, BlockLayout *L) {
     c.groups = 1;
     c.dtype = d->dtype;
     c.weight_layout = d->weights_packed ? WVC_WEIGHT_PACKED : WVC_WEIGHT_STANDARD;
-    size_t need = wvc::igemm_counter_bytes();
+    size_t need = 0;
     for (int k = 0; k < 3; ++k) {
         if (k == 1) c.c_in = d->c_out;
         if (k == 2) {  // the 1x1x1 shortcut, when there is one

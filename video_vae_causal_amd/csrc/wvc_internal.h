@@ -46,12 +46,9 @@ enum class ConvRoute { Fast3x3x3, Fast1x1x1, Generic };
 // MFMA implicit-GEMM route (bf16 only).  Weights are read in the packed
 // fragment order written by launch_pack_weights; a call that brings
 // standard-layout weights packs them into its workspace first.  The workspace
-// starts with the split-K arrival counters (igemm_counter_bytes() bytes),
-// which must be zero before the first call and are left zero by every call;
-// partial sums and packed weights follow.  The 3x3x3 route also writes
-// cache_out (may be nullptr) when t > 0.
+// holds split-K partial sums and packed weights; its contents on entry do not
+// matter.  The 3x3x3 route also writes cache_out (may be nullptr) when t > 0.
 size_t igemm_workspace_bytes(const ConvCall &c, ConvRoute r, bool packed_given);
-size_t igemm_counter_bytes();
 size_t igemm_packed_weight_bytes(const ConvCall &c);
 bool igemm_supports(const ConvCall &c);
 hipError_t launch_pack_weights(const ConvCall &c, const void *w, void *packed, hipStream_t s);

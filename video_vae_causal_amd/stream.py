@@ -90,7 +90,7 @@ class CausalConv3d:
                         padding=self.padding, weight_layout=layout)
         need = L.wvc_causal_conv3d_workspace_bytes(d)
         if need and (self.ws is None or self.ws.numel() < need):
-            self.ws = torch.zeros(need, dtype=torch.uint8, device=x.device)
+            self.ws = torch.empty(need, dtype=torch.uint8, device=x.device)
         y = L.wvc_causal_conv3d_fwd(x, self.weight, self.bias, cin, cout, residual, y,
                                     padding=self.padding, workspace=self.ws if need else None,
                                     packed_weight=self.packed)
@@ -130,8 +130,7 @@ class ResBlock:
                             weights_packed=self.packed is not None)
         need = L.wvc_resblock_workspace_bytes(d)
         if self.ws is None or self.ws.numel() < need:
-            # zero-filled once: split-K counters start at zero, calls leave them so
-            self.ws = torch.zeros(need, dtype=torch.uint8, device=x.device)
+            self.ws = torch.empty(need, dtype=torch.uint8, device=x.device)
         y = L.wvc_resblock_fwd(x, self.p, self.c1.cin, self.c1.cout, self.c2.cin, self.c2.cout,
                                y=y, eps=self.eps, workspace=self.ws, packed=self.packed)
         self.c1.flip()
