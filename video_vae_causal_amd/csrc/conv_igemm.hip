@@ -76,7 +76,6 @@ struct IgParams {
     float *part;  // split-K partial sums: [S][N][T][H][W][Cout] fp32
     size_t part_stride;  // N*T*H*W*Cout: elements of one split's partials
     int T, H, W, Cin, Cout, F;
-    int TH, TW, HC, HP;
     int tiles_w, tiles_h, co_tiles;
     int S, U;
     int total;
@@ -101,6 +100,11 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *base, uint32_
 
 __device__ __forceinline__ uint4 bload(__amdgpu_buffer_rsrc_t r, uint32_t off) {
     const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+__device__ __forceinline__ uint4 bload_s(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t soff) {
+    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, (int)soff, 0);
     return make_uint4(v.x, v.y, v.z, v.w);
 }
 
@@ -131,8 +135,22 @@ struct Mfma<32> {
 template <int N>
 using Int = std::integral_constant<int, N>;
 
+// Compile-time geometry of a TH x TW position tile (TH * TW == 256) and its
+// halo: HC columns, HP entries per 8-channel group, padded to HPAD (a multiple
+// of 64) so that every staging thread writes all of its slots unconditionally.
+template <int KS, int TW>
+struct Geo {
+    static constexpr int TH = POS_T / TW;
+    static constexpr int HC = TW + KS - 1;
+    static constexpr int HP = (TH + KS - 1) * HC;
+    static constexpr int NIT = (HP + 63) / 64;  // staging slots per thread
+    static constexpr int HPAD = NIT * 64;
+};
+
 // One workgroup = 256 threads = 4 waves laid out WAVES_CO (channels) x
-// 4/WAVES_CO (positions).  M is the MFMA tile edge (16: 16x16x32, 32: 32x32x16).
+// 4/WAVES_CO (positions).  M is the MFMA tile edge (16: 16x16x32, 32: 32x32x16);
+// TW the tile width, a template parameter so that every LDS and weight
+// address inside the K loop is a per-lane base plus an immediate offset.
 //
 // Pipeline (one workgroup per CU, up to 512 registers per lane):
 //   * a stage is one work unit (kt, 32-channel block); its halo tile lives in
@@ -147,25 +165,29 @@ using Int = std::integral_constant<int, N>;
 //   Global loads complete in issue order, so the issue order (row batch, then
 //   the next halo) is chosen such that every wait covers only loads issued at
 //   least one full row earlier.
-template <int KS, int CO_T, int M, int WAVES_CO, bool SPLIT>
+template <int KS, int CO_T, int M, int WAVES_CO, bool SPLIT, int TW>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 igemm_kernel(IgParams p) {
     using MF = Mfma<M>;
+    using G = Geo<KS, TW>;
     using acc_t = typename MF::acc_t;
     constexpr int ACC = MF::ACC;
-    constexpr int TAPS = KS * KS * KS;
     constexpr int PAD = KS / 2;
-    constexpr int HPM = KS == 3 ? 340 : 256;
-    constexpr int NIT = (4 * HPM + 255) / 256;
+    constexpr int NIT = G::NIT, HPAD = G::HPAD, HC = G::HC, HP = G::HP;
     constexpr int WAVES_POS = 4 / WAVES_CO;
     constexpr int WCO = CO_T / WAVES_CO, WPOS = POS_T / WAVES_POS;
     constexpr int FCO = WCO / M, FPOS = WPOS / M;
+    constexpr int NBLK = CO_T / M;  // M-row weight blocks per channel tile
     constexpr int KSTEPS = M / 16;  // MFMA K-steps per 32-channel block
     constexpr int GPL = 64 / M;     // 8-channel groups spanned by one K-step
+    constexpr int FRAG = 1024;      // bytes of one packed A fragment
     static_assert(WCO % M == 0 && WPOS % M == 0, "wave tile must be whole MFMA tiles");
+    static_assert(TW % M == 0 || M % TW == 0, "MFMA columns must tile the tile rows");
+    static_assert(WPOS % TW == 0, "a wave's positions must start on a tile row");
     static_assert(NIT <= 32, "staging mask");
+    static_assert((FCO * KSTEPS - 1) * FRAG < 4096, "weight offsets must fit the immediate");
 
-    __shared__ uint4 halo[2][4 * HPM];
+    __shared__ uint4 halo[2][4 * HPAD];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
@@ -195,36 +217,37 @@ igemm_kernel(IgParams p) {
     L /= p.tiles_h;
     const int t = L % p.T;
     const int n = L / p.T;
-    const int h0 = th * p.TH, w0 = tw * p.TW;
+    const int h0 = th * G::TH, w0 = tw * TW;
     const int co0 = ct * CO_T + wco * WCO;
     const int u0 = SPLIT ? (s * p.U) / p.S : 0;
     const int u1 = SPLIT ? ((s + 1) * p.U) / p.S : p.U;
 
-    // Staging: item k of this thread is halo position (tid>>2) + 64k, group g;
-    // its LDS entry is lbase + 64k when (tid>>2) + 64k < HP.
+    // Staging: slot k of this thread is halo position (tid>>2) + 64k of
+    // group g, LDS entry lbase + 64k (slots past HP are padding).
     uint32_t soff[NIT];  // byte offset of the 16-byte chunk inside a frame, or OOB
-    uint32_t interior = 0, lvalid = 0;
-    const int lbase = g * p.HP + (tid >> 2);
+    uint32_t interior = 0;
+    const int lbase = g * HPAD + (tid >> 2);
 #pragma unroll
     for (int k = 0; k < NIT; ++k) {
         const int hp = (tid >> 2) + 64 * k;
-        const bool valid = hp < p.HP;
-        const int r = hp / p.HC, c = hp - r * p.HC;
+        const int r = hp / HC, c = hp - r * HC;
         const int hs = h0 + r - PAD, ws = w0 + c - PAD;
-        const bool inframe = valid && hs >= 0 && hs < p.H && ws >= 0 && ws < p.W;
+        const bool inframe = hp < HP && hs >= 0 && hs < p.H && ws >= 0 && ws < p.W;
         soff[k] = inframe ? (uint32_t)(((hs * p.W + ws) * p.Cin + g * 8) * 2) : OOB;
-        if (valid) lvalid |= 1u << k;
-        if (inframe && r >= PAD && r < PAD + p.TH && c >= PAD && c < PAD + p.TW) interior |= 1u << k;
+        if (inframe && r >= PAD && r < PAD + G::TH && c >= PAD && c < PAD + TW) interior |= 1u << k;
     }
-    // B fragments: LDS entry of this lane's position at spatial tap (0,0),
-    // K-step 0; K-step ks adds ks*GPL*HP.
-    int boff[FPOS];
-#pragma unroll
-    for (int f = 0; f < FPOS; ++f) {
-        const int q = wpos * WPOS + f * M + lr;
-        const int r = q / p.TW, c = q - r * p.TW;
-        boff[f] = lg * p.HP + r * p.HC + c;
-    }
+    // B fragments: LDS entry of this lane's position (first MFMA column tile,
+    // spatial tap (0,0), K-step 0).  Column tile j, K-step ks and tap (kh, kw)
+    // add compile-time offsets.
+    const int bbase = [&] {
+        const int q = wpos * WPOS + lr;
+        const int r = q / TW, c = q - r * TW;
+        return lg * HPAD + r * HC + c;
+    }();
+    // Weights: packed as [co tile][unit][kh][kw][M-row block][K-step][lane],
+    // one 1 KiB fragment per (block, K-step); this wave's blocks start at
+    // wco * FCO.  A row (unit, kh) is one contiguous run of KS fragment groups.
+    const uint32_t wlane = (uint32_t)((wco * FCO * KSTEPS) * FRAG + lane * 16);
     const __amdgpu_buffer_rsrc_t wr = rsrc(p.w, p.w_bytes);
     const size_t frame_elems = (size_t)p.frame_bytes / 2;
     const bool write_cache = KS == 3 && p.cache_out != nullptr && t == p.T - 1 && ct == 0;
@@ -241,26 +264,18 @@ igemm_kernel(IgParams p) {
     bf16x8 B[2][FPOS][KSTEPS];     // two tap sets: tap k reads B[k & 1]
     uint4 hv[NIT];
 
-    // Weights arrive packed in MFMA fragment order (see pack_weights_kernel):
-    // the fragment of M output channels x one K-step is 1 KiB, lane-contiguous.
-    const int nb = (p.Cin + 31) / 32;
     auto load_row = [&](auto set_tag, int rho) {
         constexpr int SET = decltype(set_tag)::value;
         const int u = u0 + rho / KS, kh = rho % KS;
-        const int kt = u % KS, cbi = u / KS;
+        const uint32_t row = (uint32_t)((((ct * p.U + u) * KS + kh) * KS) * NBLK * KSTEPS) * FRAG;
 #pragma unroll
-        for (int kw = 0; kw < KS; ++kw) {
-            const int tap = (kt * KS + kh) * KS + kw;
+        for (int kw = 0; kw < KS; ++kw)
 #pragma unroll
-            for (int ks = 0; ks < KSTEPS; ++ks)
+            for (int f = 0; f < FCO; ++f)
 #pragma unroll
-                for (int f = 0; f < FCO; ++f) {
-                    const int blk = co0 / M + f;
-                    const uint32_t o =
-                        (uint32_t)((((blk * TAPS + tap) * nb + cbi) * KSTEPS + ks) * 1024 + lane * 16);
-                    A[SET][kw][f][ks] = as_bf16x8(bload(wr, o));
-                }
-        }
+                for (int ks = 0; ks < KSTEPS; ++ks)
+                    A[SET][kw][f][ks] = as_bf16x8(bload_s(wr, wlane + (f * KSTEPS + ks) * FRAG,
+                                                          row + kw * NBLK * KSTEPS * FRAG));
     };
     auto load_halo = [&](int u) {
         const int kt = u % KS, cb = (u / KS) * 32;
@@ -279,8 +294,7 @@ igemm_kernel(IgParams p) {
     };
     auto store_halo = [&](int u, int buf) {
 #pragma unroll
-        for (int k = 0; k < NIT; ++k)
-            if (lvalid & (1u << k)) halo[buf][lbase + 64 * k] = hv[k];
+        for (int k = 0; k < NIT; ++k) halo[buf][lbase + 64 * k] = hv[k];
         const int kt = u % KS, cb = (u / KS) * 32;
         if (write_cache && kt >= 1 && cb + g * 8 < p.Cin) {
             uint16_t *dst = p.cache_out + (size_t)(n * 2 + kt - 1) * frame_elems + cb;
@@ -290,12 +304,13 @@ igemm_kernel(IgParams p) {
                     *reinterpret_cast<uint4 *>(reinterpret_cast<char *>(dst) + soff[k]) = hv[k];
         }
     };
-    auto load_b = [&](auto set_tag, int buf, int j, int kh, int kw) {
+    // LDS entry offset of MFMA column tile j relative to column tile 0.
+    auto offj = [](int j) { return ((j * M) / TW) * HC + (j * M) % TW; };
+    auto load_b = [&](auto set_tag, const uint4 *hb, int j, int kh, int kw) {
         constexpr int BS = decltype(set_tag)::value;
-        const int toff = kh * p.HC + kw;
 #pragma unroll
         for (int ks = 0; ks < KSTEPS; ++ks)
-            B[BS][j][ks] = as_bf16x8(halo[buf][boff[j] + ks * GPL * p.HP + toff]);
+            B[BS][j][ks] = as_bf16x8(hb[offj(j) + ks * GPL * HPAD + kh * HC + kw]);
     };
 
     const int R = (u1 - u0) * KS;  // rows this workgroup runs
@@ -308,6 +323,7 @@ igemm_kernel(IgParams p) {
         constexpr int kh = SET % KS;  // rows are visited in groups of 3 == KS (or KS == 1)
         const int u = u0 + rho / KS;
         const int buf = (u - u0) & 1;
+        const uint4 *hb = &halo[buf][bbase];
         const bool last_stage = u + 1 >= u1;
         load_row(Int<(SET + 2) % 3>{}, rho + 2 < R ? rho + 2 : R - 1);
         if (kh == 0) load_halo(last_stage ? u : u + 1);
@@ -328,7 +344,7 @@ igemm_kernel(IgParams p) {
 #pragma unroll
                     for (int i = 0; i < FCO; ++i)
                         acc[i][j] = MF::run(A[SET][kw][i][ks], B[cur][j][ks], acc[i][j]);
-                    if (ks == 0 && next_in_stage) load_b(Int<cur ^ 1>{}, buf, j, nkh, nkw);
+                    if (ks == 0 && next_in_stage) load_b(Int<cur ^ 1>{}, hb, j, nkh, nkw);
                     __builtin_amdgcn_sched_barrier(0);
                 }
             }
@@ -341,8 +357,9 @@ igemm_kernel(IgParams p) {
         if (kh == KS - 1 && !last_stage) {
             store_halo(u + 1, buf ^ 1);
             __syncthreads();
+            const uint4 *hn = &halo[buf ^ 1][bbase];
 #pragma unroll
-            for (int j = 0; j < FPOS; ++j) load_b(Int<0>{}, buf ^ 1, j, 0, 0);
+            for (int j = 0; j < FPOS; ++j) load_b(Int<0>{}, hn, j, 0, 0);
         }
     };
 
@@ -352,8 +369,9 @@ igemm_kernel(IgParams p) {
         load_row(Int<1>{}, R > 1 ? 1 : 0);
         store_halo(u0, 0);
         __syncthreads();
+        const uint4 *h0p = &halo[0][bbase];
 #pragma unroll
-        for (int j = 0; j < FPOS; ++j) load_b(Int<0>{}, 0, j, 0, 0);
+        for (int j = 0; j < FPOS; ++j) load_b(Int<0>{}, h0p, j, 0, 0);
         if (KS == 3) {
             // R is a multiple of 3: one stage per iteration, no row guards.
             for (int rho = 0; rho < R; rho += 3) {
@@ -379,7 +397,7 @@ igemm_kernel(IgParams p) {
 #pragma unroll
         for (int j = 0; j < FPOS; ++j) {
             const int q = wpos * WPOS + j * M + lr;
-            const int r = q / p.TW, c = q - r * p.TW;
+            const int r = q / TW, c = q - r * TW;
             const int h = h0 + r, w = w0 + c;
             if (h >= p.H || w >= p.W) continue;
             const size_t obase = (((size_t)(n * p.T + t) * p.H + h) * p.W + w) * p.Cout;
@@ -410,7 +428,7 @@ igemm_kernel(IgParams p) {
 #pragma unroll
     for (int j = 0; j < FPOS; ++j) {
         const int q = wpos * WPOS + j * M + lr;
-        const int r = q / p.TW, c = q - r * p.TW;
+        const int r = q / TW, c = q - r * TW;
         const int h = h0 + r, w = w0 + c;
         const bool inside = h < p.H && w < p.W;
         const size_t obase = (((size_t)(n * p.T + t) * p.H + h) * p.W + w) * p.Cout;
@@ -426,7 +444,7 @@ igemm_kernel(IgParams p) {
 #pragma unroll
     for (int j = 0; j < FPOS; ++j) {
         const int q = wpos * WPOS + j * M + lr;
-        const int r = q / p.TW, c = q - r * p.TW;
+        const int r = q / TW, c = q - r * TW;
         const int h = h0 + r, w = w0 + c;
         if (h >= p.H || w >= p.W) continue;
         const size_t obase = (((size_t)(n * p.T + t) * p.H + h) * p.W + w) * p.Cout;
@@ -500,28 +518,39 @@ __global__ void __launch_bounds__(256) splitk_reduce_kernel(const float *__restr
     *reinterpret_cast<uint4 *>(y + e0) = make_uint4(o[0], o[1], o[2], o[3]);
 }
 
-// Packs W[co][tap][ci] into MFMA fragment order for tile edge M:
-//   packed[co / M][tap][ci / 32][ks][lane][8 channels],  ks < M/16, lane < 64,
-//   row co = block*M + lane % M, channel = 32*cb + ks*(64/M)*8 + (lane / M)*8,
-// zero past C_in.  One fragment (one wave load) is then 1 KiB contiguous.
+// Packs W[co][tap][ci] into the order the kernel reads, for channel tile CO_T
+// and MFMA tile edge M:
+//   packed[co tile][unit][kh][kw][block][ks][lane][8 channels]
+// with unit = (32-channel block cb) * KS + kt, block < CO_T/M, ks < M/16,
+// lane < 64; row co = tile*CO_T + block*M + lane % M, channel
+// 32*cb + ks*(64/M)*8 + (lane / M)*8; zero past C_in.  One fragment (one wave
+// load) is 1 KiB contiguous, and one kernel row (unit, kh) of a channel tile
+// is one contiguous run.
 template <int M>
 __global__ void __launch_bounds__(256) pack_weights_kernel(const uint16_t *__restrict__ w,
                                                            uint4 *__restrict__ out, int cout,
-                                                           int cin, int taps) {
+                                                           int cin, int ks_, int co_t) {
     constexpr int KSTEPS = M / 16, GPL = 64 / M;
     const int nb = (cin + 31) / 32;
-    const long chunks = (long)(cout / M) * taps * nb * KSTEPS * 64;
+    const int nblk = co_t / M, units = ks_ * nb, taps = ks_ * ks_ * ks_;
+    const long chunks = (long)(cout / co_t) * units * ks_ * ks_ * nblk * KSTEPS * 64;
     for (long i = (long)blockIdx.x * 256 + threadIdx.x; i < chunks; i += (long)gridDim.x * 256) {
         long r = i;
         const int lane = (int)(r % 64);
         r /= 64;
         const int ks = (int)(r % KSTEPS);
         r /= KSTEPS;
-        const int cb = (int)(r % nb);
-        r /= nb;
-        const int tap = (int)(r % taps);
-        const int blk = (int)(r / taps);
-        const int co = blk * M + lane % M;
+        const int blk = (int)(r % nblk);
+        r /= nblk;
+        const int kw = (int)(r % ks_);
+        r /= ks_;
+        const int kh = (int)(r % ks_);
+        r /= ks_;
+        const int u = (int)(r % units);
+        const int ct = (int)(r / units);
+        const int kt = u % ks_, cb = u / ks_;
+        const int tap = (kt * ks_ + kh) * ks_ + kw;
+        const int co = ct * co_t + blk * M + lane % M;
         const int ch = cb * 32 + ks * GPL * 8 + (lane / M) * 8;
         uint16_t v[8];
 #pragma unroll
@@ -533,7 +562,7 @@ __global__ void __launch_bounds__(256) pack_weights_kernel(const uint16_t *__res
 }
 
 struct Plan {
-    int th, tw, hc, hp, tiles_h, tiles_w, co_t, co_tiles, S, U, co_major;
+    int th, tw, tiles_h, tiles_w, co_t, co_tiles, S, U, co_major;
     long tiles;  // n * t * tiles_h * tiles_w * co_tiles
 };
 
@@ -551,14 +580,14 @@ int num_cus() {
     return cached;
 }
 
-// Pick a TH x TW tile (TH*TW == 256) that wastes the fewest positions on
-// ragged edges; ties go to the wider tile (longer contiguous runs).
-void choose_tile(int h, int w, int ks, int hp_max, int *th_out, int *tw_out) {
+// Pick a TH x TW tile (TH*TW == 256, TW one of the compiled widths 8, 16, 32)
+// that wastes the fewest positions on ragged edges; ties go to the wider tile
+// (longer contiguous runs).
+void choose_tile(int h, int w, int *th_out, int *tw_out) {
     int bth = 0, btw = 0;
     long best = -1;
-    for (int tw = 1; tw <= POS_T; tw *= 2) {
+    for (int tw = 8; tw <= 32; tw *= 2) {
         const int th = POS_T / tw;
-        if ((th + ks - 1) * (tw + ks - 1) > hp_max) continue;
         // tiles narrower than 16 columns split a 16-lane LDS read over rows
         // 2*(tw+2) bytes * 8 apart, which collide in the LDS banks: count them
         // as 25% more expensive
@@ -584,10 +613,7 @@ int co_tile_for(int cout) {
 Plan make_plan(const ConvCall &c, ConvRoute r) {
     Plan pl{};
     const int ks = r == ConvRoute::Fast3x3x3 ? 3 : 1;
-    const int hp_max = ks == 3 ? 340 : 256;
-    choose_tile(c.h, c.w, ks, hp_max, &pl.th, &pl.tw);
-    pl.hc = pl.tw + ks - 1;
-    pl.hp = (pl.th + ks - 1) * pl.hc;
+    choose_tile(c.h, c.w, &pl.th, &pl.tw);
     pl.tiles_h = (c.h + pl.th - 1) / pl.th;
     pl.tiles_w = (c.w + pl.tw - 1) / pl.tw;
     pl.co_t = co_tile_for(c.cout);
@@ -640,13 +666,25 @@ size_t ws_bytes_for(const Plan &pl, const ConvCall &c, bool need_pack) {
     return align256(part_bytes(pl, c)) + (need_pack ? align256(packed_bytes(c)) : 0);
 }
 
-template <int KS, int CO_T, int M, int WAVES_CO>
-hipError_t launch_variant(const IgParams &p, hipStream_t s) {
+template <int KS, int CO_T, int M, int WAVES_CO, int TW>
+hipError_t launch_tw(const IgParams &p, hipStream_t s) {
     if (p.S > 1)
-        hipLaunchKernelGGL((igemm_kernel<KS, CO_T, M, WAVES_CO, true>), dim3(p.total), dim3(256), 0, s, p);
+        hipLaunchKernelGGL((igemm_kernel<KS, CO_T, M, WAVES_CO, true, TW>), dim3(p.total), dim3(256), 0,
+                           s, p);
     else
-        hipLaunchKernelGGL((igemm_kernel<KS, CO_T, M, WAVES_CO, false>), dim3(p.total), dim3(256), 0, s, p);
+        hipLaunchKernelGGL((igemm_kernel<KS, CO_T, M, WAVES_CO, false, TW>), dim3(p.total), dim3(256),
+                           0, s, p);
     return hipGetLastError();
+}
+
+template <int KS, int CO_T, int M, int WAVES_CO>
+hipError_t launch_variant(const IgParams &p, int tw, hipStream_t s) {
+    switch (tw) {
+        case 8: return launch_tw<KS, CO_T, M, WAVES_CO, 8>(p, s);
+        case 16: return launch_tw<KS, CO_T, M, WAVES_CO, 16>(p, s);
+        case 32: return launch_tw<KS, CO_T, M, WAVES_CO, 32>(p, s);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 }  // namespace
@@ -659,8 +697,8 @@ size_t igemm_workspace_bytes(const ConvCall &c, ConvRoute r, bool packed_given) 
 size_t igemm_packed_weight_bytes(const ConvCall &c) { return packed_bytes(c); }
 
 hipError_t launch_pack_weights(const ConvCall &c, const void *w, void *packed, hipStream_t s) {
-    const int m = tile_m(co_tile_for(c.cout));
-    const int taps = c.kt * c.kh * c.kw;
+    const int co_t = co_tile_for(c.cout);
+    const int m = tile_m(co_t);
     const long chunks = (long)packed_bytes(c) / 16;
     long blocks = (chunks + 255) / 256;
     if (blocks > 8192) blocks = 8192;
@@ -668,11 +706,11 @@ hipError_t launch_pack_weights(const ConvCall &c, const void *w, void *packed, h
     if (m == 32)
         hipLaunchKernelGGL(pack_weights_kernel<32>, dim3((unsigned)blocks), dim3(256), 0, s,
                            static_cast<const uint16_t *>(w), static_cast<uint4 *>(packed), c.cout,
-                           c.cin, taps);
+                           c.cin, c.kt, co_t);
     else
         hipLaunchKernelGGL(pack_weights_kernel<16>, dim3((unsigned)blocks), dim3(256), 0, s,
                            static_cast<const uint16_t *>(w), static_cast<uint4 *>(packed), c.cout,
-                           c.cin, taps);
+                           c.cin, c.kt, co_t);
     return hipGetLastError();
 }
 
@@ -710,10 +748,6 @@ hipError_t launch_conv_igemm(const ConvCall &c, ConvRoute r, bool packed_given, 
     p.Cin = c.cin;
     p.Cout = c.cout;
     p.F = c.frames;
-    p.TH = pl.th;
-    p.TW = pl.tw;
-    p.HC = pl.hc;
-    p.HP = pl.hp;
     p.tiles_w = pl.tiles_w;
     p.tiles_h = pl.tiles_h;
     p.co_tiles = pl.co_tiles;
@@ -736,10 +770,10 @@ hipError_t launch_conv_igemm(const ConvCall &c, ConvRoute r, bool packed_given, 
     // 32: 32x32x16 on 1 x 4 waves of 32 x 64.
     hipError_t e;
     switch (pl.co_t) {
-        case 128: e = k3 ? launch_variant<3, 128, 32, 2>(p, s) : launch_variant<1, 128, 32, 2>(p, s); break;
-        case 96: e = k3 ? launch_variant<3, 96, 16, 2>(p, s) : launch_variant<1, 96, 16, 2>(p, s); break;
-        case 64: e = k3 ? launch_variant<3, 64, 16, 2>(p, s) : launch_variant<1, 64, 16, 2>(p, s); break;
-        default: e = k3 ? launch_variant<3, 32, 32, 1>(p, s) : launch_variant<1, 32, 32, 1>(p, s); break;
+        case 128: e = k3 ? launch_variant<3, 128, 32, 2>(p, pl.tw, s) : launch_variant<1, 128, 32, 2>(p, pl.tw, s); break;
+        case 96: e = k3 ? launch_variant<3, 96, 16, 2>(p, pl.tw, s) : launch_variant<1, 96, 16, 2>(p, pl.tw, s); break;
+        case 64: e = k3 ? launch_variant<3, 64, 16, 2>(p, pl.tw, s) : launch_variant<1, 64, 16, 2>(p, pl.tw, s); break;
+        default: e = k3 ? launch_variant<3, 32, 32, 1>(p, pl.tw, s) : launch_variant<1, 32, 32, 1>(p, pl.tw, s); break;
     }
     if (e != hipSuccess || pl.S <= 1) return e;
     const long groups = (long)(out_elems(c) / 8);  // Cout % 32 == 0 on this route
