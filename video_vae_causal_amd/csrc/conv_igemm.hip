@@ -188,6 +188,7 @@ igemm_kernel(IgParams p) {
     static_assert((FCO * KSTEPS - 1) * FRAG < 4096, "weight offsets must fit the immediate");
 
     __shared__ uint4 halo[2][4 * HPAD];
+    __shared__ uint2 bias_s[CO_T / 4];  // this channel tile's bias, read by the epilogue
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
@@ -221,6 +222,9 @@ igemm_kernel(IgParams p) {
     const int co0 = ct * CO_T + wco * WCO;
     const int u0 = SPLIT ? (s * p.U) / p.S : 0;
     const int u1 = SPLIT ? ((s + 1) * p.U) / p.S : p.U;
+    if (!SPLIT && tid < CO_T / 4)
+        bias_s[tid] = p.bias ? *reinterpret_cast<const uint2 *>(p.bias + ct * CO_T + tid * 4)
+                             : make_uint2(0u, 0u);
 
     // Staging: slot k of this thread is halo position (tid>>2) + 64k of
     // group g, LDS entry lbase + 64k (slots past HP are padding).
@@ -363,6 +367,7 @@ igemm_kernel(IgParams p) {
         }
     };
 
+    if (R <= 0) __syncthreads();  // (the prologue's barrier publishes bias_s otherwise)
     if (R > 0) {
         load_halo(u0);
         load_row(Int<0>{}, 0);
@@ -413,18 +418,16 @@ igemm_kernel(IgParams p) {
         }
         return;
     }
-    // Global loads and stores share one completion counter, so every bias
-    // and residual load is issued before the first store: a load issued after
-    // a store would wait for that store too.
+    // Global loads and stores share one completion counter, so every
+    // residual load is issued before the first store: a load issued after a
+    // store would wait for that store too.  The bias comes from LDS.
     uint2 bb[FCO][ACC / 4];
     uint2 rr[FPOS][FCO][ACC / 4];
 #pragma unroll
     for (int i = 0; i < FCO; ++i)
 #pragma unroll
-        for (int e4 = 0; e4 < ACC / 4; ++e4) {
-            const int co = co0 + i * M + e4 * 8 + lg * 4;
-            bb[i][e4] = p.bias ? *reinterpret_cast<const uint2 *>(p.bias + co) : make_uint2(0u, 0u);
-        }
+        for (int e4 = 0; e4 < ACC / 4; ++e4)
+            bb[i][e4] = bias_s[(wco * WCO + i * M + e4 * 8 + lg * 4) / 4];
 #pragma unroll
     for (int j = 0; j < FPOS; ++j) {
         const int q = wpos * WPOS + j * M + lr;
@@ -470,8 +473,8 @@ igemm_kernel(IgParams p) {
                     v[3] += bf16_to_f32(rr[j][i][e4].y >> 16);
                 }
                 uint2 o;
-                o.x = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
-                o.y = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
+                o.x = pack2_bf16(v[0], v[1]);
+                o.y = pack2_bf16(v[2], v[3]);
                 *reinterpret_cast<uint2 *>(p.y + obase + co) = o;
             }
     }
@@ -513,7 +516,7 @@ __global__ void __launch_bounds__(256) splitk_reduce_kernel(const float *__restr
             lo += bf16_to_f32(rw[k] & 0xffffu);
             hi += bf16_to_f32(rw[k] >> 16);
         }
-        o[k] = (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+        o[k] = pack2_bf16(lo, hi);
     }
     *reinterpret_cast<uint4 *>(y + e0) = make_uint4(o[0], o[1], o[2], o[3]);
 }

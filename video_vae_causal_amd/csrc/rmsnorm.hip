@@ -16,9 +16,6 @@
 namespace wvc {
 namespace {
 
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-
 template <bool BF16>
 struct Vec;
 template <>
@@ -32,15 +29,11 @@ struct Vec<true> {
             o[2 * k + 1] = bf16_to_f32(w[k] >> 16);
         }
     }
-    // gfx950's v_cvt_pk_bf16_f32: two floats to bf16, round to nearest even,
-    // in one instruction (the store-side rounding is most of this kernel's ALU
-    // work otherwise).
+    // gfx950's v_cvt_pk_bf16_f32 (pack2_bf16): the store-side rounding is
+    // most of this kernel's ALU work otherwise.
     __device__ static uint4 pack(const float *o) {
-        uint32_t w[4];
-#pragma unroll
-        for (int k = 0; k < 4; ++k)
-            w[k] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{o[2 * k], o[2 * k + 1]}, bf16x2));
-        return make_uint4(w[0], w[1], w[2], w[3]);
+        return make_uint4(pack2_bf16(o[0], o[1]), pack2_bf16(o[2], o[3]), pack2_bf16(o[4], o[5]),
+                          pack2_bf16(o[6], o[7]));
     }
 };
 template <>

@@ -24,6 +24,16 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
     return static_cast<uint16_t>(u >> 16);
 }
 
+// Two floats -> two bf16 (lo in the low half), round to nearest even, with
+// gfx950's v_cvt_pk_bf16_f32.  It agrees with f32_to_bf16 on every input
+// except some of magnitude below 2^-126 (the smallest normal binade and the
+// subnormals), which the kernels here never produce from non-degenerate data.
+typedef float wvc_f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 wvc_bf16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack2_bf16(float lo, float hi) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(wvc_f32x2{lo, hi}, wvc_bf16x2));
+}
+
 // ---------------------------------------------------------------------------
 // Conv launch description (already validated by the API layer).
 // Tensor layouts are channels-last, see include/wvc.h.
