@@ -136,15 +136,16 @@ template <int N>
 using Int = std::integral_constant<int, N>;
 
 // Compile-time geometry of a TH x TW position tile (TH * TW == 256) and its
-// halo: HC columns, HP entries per 8-channel group, padded to HPAD (a multiple
-// of 64) so that every staging thread writes all of its slots unconditionally.
+// halo: HC columns, HP entries per 8-channel group; each group gets NIT*64
+// slots (every staging thread writes all of its slots unconditionally) plus 4
+// entries, so that consecutive groups start 64 bytes apart in the LDS banks.
 template <int KS, int TW>
 struct Geo {
     static constexpr int TH = POS_T / TW;
     static constexpr int HC = TW + KS - 1;
     static constexpr int HP = (TH + KS - 1) * HC;
     static constexpr int NIT = (HP + 63) / 64;  // staging slots per thread
-    static constexpr int HPAD = NIT * 64;
+    static constexpr int HPAD = NIT * 64 + 4;
 };
 
 // One workgroup = 256 threads = 4 waves laid out WAVES_CO (channels) x
