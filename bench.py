@@ -141,7 +141,7 @@ def wl_resblock():
                 config={"workload": "resblock_384_60x104", "channels": c, "frames": t,
                         "height": h, "width": w, "chunk_frames": 1, "cache_frames": 2,
                         "batch": n},
-                kernel=kernel, kernel_name="igemm_kernel<3, 128, 32, 2, true>",
+                kernel=kernel, kernel_name="igemm_kernel<3, 128, 32, 2, true, 16> + splitk_reduce_kernel",
                 kernel_units=acc.conv_flops(n, 1, h, w, c, c), kernel_bound="mfma",
                 kernel_bytes=acc.conv_launch_bytes(n, 1, h, w, c, c))
     return step, info
@@ -176,7 +176,7 @@ def wl_layer384():
                 config={"workload": "layer_384_240x416", "channels": c, "frames": t,
                         "height": h, "width": w, "chunk_frames": t, "projection_out": int(wp.shape[0]),
                         "batch": n},
-                kernel=kernel, kernel_name="igemm_kernel<3, 128, 32, 2, false>", kernel_units=f3,
+                kernel=kernel, kernel_name="igemm_kernel<3, 128, 32, 2, false, 32>", kernel_units=f3,
                 kernel_bound="mfma", kernel_bytes=acc.conv_launch_bytes(n, t, h, w, c, c, cache_frames=0))
     return step, info
 
@@ -217,7 +217,7 @@ def wl_layer96():
     info = dict(workload="layer_96_480x832", conv_flops=conv_flops, latent_frames=t,
                 config={"workload": "layer_96_480x832", "channels": c, "frames": t,
                         "height": h, "width": w, "chunks": sizes, "batch": n},
-                kernel=kernel, kernel_name="igemm_kernel<3, 96, 16, 2, false>",
+                kernel=kernel, kernel_name="igemm_kernel<3, 96, 16, 2, false, 32>",
                 kernel_units=acc.conv_flops(n, 4, h, w, c, c), kernel_bound="mfma",
                 kernel_bytes=acc.conv_launch_bytes(n, 4, h, w, c, c),
                 norm_kernel=norm_kernel, norm_kernel_name="rmsnorm_flat_kernel<true, 2, true>",
@@ -262,7 +262,7 @@ def wl_decoder():
     info = dict(workload="decoder_stack_48_30x52", conv_flops=per_frame * t, latent_frames=t,
                 config={"workload": "decoder_stack_48_30x52", "latent_channels": cl_, "channels": width,
                         "frames": t, "height": h, "width": w, "chunk_frames": 1, "batch": n},
-                kernel=kernel, kernel_name="igemm_kernel<3, 128, 32, 2, true>",
+                kernel=kernel, kernel_name="igemm_kernel<3, 128, 32, 2, true, 16> + splitk_reduce_kernel",
                 kernel_units=acc.conv_flops(n, 1, 2 * h, 2 * w, width, width), kernel_bound="mfma",
                 kernel_bytes=acc.conv_launch_bytes(n, 1, 2 * h, 2 * w, width, width))
     return step, info
