@@ -156,6 +156,30 @@ def test_resblock_packed_and_standard_weights_agree_bitwise():
     assert torch.equal(y_std, y_pk)
 
 
+@pytest.mark.parametrize("c,t,h,w", [(384, 1, 60, 104), (384, 1, 30, 52), (96, 2, 9, 17),
+                                     (384, 3, 60, 104)])
+def test_resblock_equals_its_abi_composition_bitwise(c, t, h, w):
+    """wvc_resblock_fwd against the same block spelled out as single ABI calls
+    (norm, conv with cache, norm, conv with residual).  On split-K frames the
+    block fuses conv1's partial-sum reduction into norm2; that must give the
+    very bits the separate reduce + norm give."""
+    r = inputs.resblock_inputs(seed=c + h + t, shape=(1, c, t, h, w))
+    xd, pd = to_dev(r["x"]), block_params_dev(r["p"])
+    n = 1
+    caches = [L.empty_cl((n, c, 2, h, w)) for _ in range(4)]
+    for cc in caches:
+        L.wvc_cache_reset(cc)
+    print(f"[case] resblock composition c={c} t={t} {h}x{w}", flush=True)
+    y_blk = L.wvc_resblock_fwd(xd, pd, caches[0], caches[1], caches[2], caches[3])
+    h1 = L.wvc_rmsnorm_silu(xd, pd["gamma1"])
+    c1o, c2o = L.empty_cl((n, c, 2, h, w)), L.empty_cl((n, c, 2, h, w))
+    a1 = L.wvc_causal_conv3d_fwd(h1, pd["w1"], pd["b1"], caches[0], c1o)
+    h2 = L.wvc_rmsnorm_silu(a1, pd["gamma2"])
+    y_sep = L.wvc_causal_conv3d_fwd(h2, pd["w2"], pd["b2"], caches[2], c2o, residual=xd)
+    assert torch.equal(y_blk, y_sep)
+    assert torch.equal(caches[1], c1o) and torch.equal(caches[3], c2o)
+
+
 def test_resblock_checkpoint_resume_bitwise():
     r = inputs.resblock_inputs(seed=9, shape=(1, 64, 4, 8, 12))
     xd, pd = to_dev(r["x"]), block_params_dev(r["p"])

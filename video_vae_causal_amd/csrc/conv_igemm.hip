@@ -42,10 +42,10 @@
 //   epilogue  : + bias, + residual (fused block shortcut), one rounding to
 //               bf16, 8-byte stores of 4 consecutive channels.  Bias and
 //               residual are loaded before the first store.
-//   cache     : the workgroups of the chunk's last output frame (channel tile
-//               0) also write the interior of the halos they stage for frames
-//               T-2 and T-1 to cache_out: the rolling cache update costs no
-//               extra pass over the frames.
+//   cache     : the workgroups of the chunk's last output frame also write
+//               the interior of the halos they stage for frames T-2 and T-1 to
+//               cache_out (the channel tiles share out the channel blocks):
+//               the rolling cache update costs no extra pass over the frames.
 //   mapping   : workgroup ids are remapped so each XCD (own L2) receives a
 //               contiguous run of tiles: splits and channel tiles of one
 //               spatial tile, then its neighbours, share that XCD's L2.
@@ -255,7 +255,10 @@ igemm_kernel(IgParams p) {
     const uint32_t wlane = (uint32_t)((wco * FCO * KSTEPS) * FRAG + lane * 16);
     const __amdgpu_buffer_rsrc_t wr = rsrc(p.w, p.w_bytes);
     const size_t frame_elems = (size_t)p.frame_bytes / 2;
-    const bool write_cache = KS == 3 && p.cache_out != nullptr && t == p.T - 1 && ct == 0;
+    // Cache update: the workgroups of the chunk's last output frame write the
+    // halo interiors they stage for frames T-2 and T-1, each channel tile the
+    // 32-channel blocks cb with cb % co_tiles == its tile (balanced work).
+    const bool write_cache = KS == 3 && p.cache_out != nullptr && t == p.T - 1;
 
     acc_t acc[FCO][FPOS];
 #pragma unroll
@@ -301,7 +304,7 @@ igemm_kernel(IgParams p) {
 #pragma unroll
         for (int k = 0; k < NIT; ++k) halo[buf][lbase + 64 * k] = hv[k];
         const int kt = u % KS, cb = (u / KS) * 32;
-        if (write_cache && kt >= 1 && cb + g * 8 < p.Cin) {
+        if (write_cache && kt >= 1 && (u / KS) % p.co_tiles == ct && cb + g * 8 < p.Cin) {
             uint16_t *dst = p.cache_out + (size_t)(n * 2 + kt - 1) * frame_elems + cb;
 #pragma unroll
             for (int k = 0; k < NIT; ++k)
@@ -726,7 +729,8 @@ bool igemm_supports(const ConvCall &c) {
 }
 
 hipError_t launch_conv_igemm(const ConvCall &c, ConvRoute r, bool packed_given, void *ws,
-                             size_t ws_bytes, void *cache_out, hipStream_t s) {
+                             size_t ws_bytes, void *cache_out, hipStream_t s, ConvPartials *defer) {
+    if (defer) *defer = ConvPartials{};
     const Plan pl = make_plan(c, r);
     if (pl.th == 0) return hipErrorInvalidValue;
     if (ws_bytes < ws_bytes_for(pl, c, !packed_given) || (!ws && ws_bytes_for(pl, c, !packed_given)))
@@ -780,6 +784,12 @@ hipError_t launch_conv_igemm(const ConvCall &c, ConvRoute r, bool packed_given, 
         default: e = k3 ? launch_variant<3, 32, 32, 1>(p, pl.tw, s) : launch_variant<1, 32, 32, 1>(p, pl.tw, s); break;
     }
     if (e != hipSuccess || pl.S <= 1) return e;
+    if (defer) {
+        defer->part = p.part;
+        defer->stride = p.part_stride;
+        defer->S = pl.S;
+        return hipSuccess;
+    }
     const long groups = (long)(out_elems(c) / 8);  // Cout % 32 == 0 on this route
     const long blocks = (groups + 255) / 256;
     if (blocks > 0x7fffffffL) return hipErrorInvalidValue;

@@ -81,36 +81,78 @@ __device__ __forceinline__ void st_stream(uint4 *p, uint4 v) {
     __builtin_nontemporal_store(u32x4{v.x, v.y, v.z, v.w}, reinterpret_cast<u32x4 *>(p));
 }
 
-template <bool BF16, int K, bool STREAM>
+// Source of a conv's split-K partial sums for the fused variant.
+struct Partials {
+    const float *part;  // [S][positions * C] fp32
+    size_t stride;      // elements of one split
+    int S;
+    const uint4 *bias;  // [C] bf16, or nullptr
+};
+
+// FROM_PARTS: the input chunk is not read from x but built from partial sums,
+// x = round_bf16(sum over splits in order + bias), bit for bit what the
+// split-K reduce kernel stores (bf16 only).
+template <bool BF16, int K, bool STREAM, bool FROM_PARTS = false>
 __global__ void __launch_bounds__(256) rmsnorm_flat_kernel(const uint4 *__restrict__ x,
                                                            const uint4 *__restrict__ gamma,
                                                            const uint4 *__restrict__ beta,
                                                            uint4 *__restrict__ y, long positions,
                                                            int cpp, int P, int R, float scale,
-                                                           float eps, int apply_silu) {
+                                                           float eps, int apply_silu,
+                                                           Partials pp = Partials{}) {
     using V = Vec<BF16>;
     __shared__ float part[256 * K];
     __shared__ float rinv[256 * K];
     __shared__ uint4 g_s[FLAT_MAX_CPP];
     __shared__ uint4 b_s[FLAT_MAX_CPP];
+    __shared__ uint4 cb_s[FROM_PARTS ? FLAT_MAX_CPP : 1];  // the conv's bias
     const int tid = threadIdx.x;
     const long pos0 = (long)blockIdx.x * P;
     const long left = positions - pos0;
     const int np = left < P ? (int)left : P;
     const int nchunks = np * cpp;
-    const uint4 *xb = x + pos0 * cpp;
+    const uint4 *xb = FROM_PARTS ? nullptr : x + pos0 * cpp;
     uint4 *yb = y + pos0 * cpp;
 
-    uint4 raw[K];
-#pragma unroll
-    for (int k = 0; k < K; ++k) {
-        const int f = tid + 256 * k;
-        raw[k] = make_uint4(0u, 0u, 0u, 0u);
-        if (f < nchunks) raw[k] = STREAM ? ld_stream(xb + f) : xb[f];
-    }
     for (int c = tid; c < cpp; c += 256) {
         g_s[c] = gamma[c];
         b_s[c] = beta ? beta[c] : make_uint4(0u, 0u, 0u, 0u);
+        if constexpr (FROM_PARTS) cb_s[c] = pp.bias ? pp.bias[c] : make_uint4(0u, 0u, 0u, 0u);
+    }
+    uint4 raw[K];
+    if constexpr (FROM_PARTS) {
+        __syncthreads();  // cb_s
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            const int f = tid + 256 * k;
+            raw[k] = make_uint4(0u, 0u, 0u, 0u);
+            if (f < nchunks) {
+                const size_t e0 = (size_t)(pos0 * cpp + f) * 8;
+                float v[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) v[e] = 0.f;
+                for (int sp = 0; sp < pp.S; ++sp) {
+                    const float4 a = *reinterpret_cast<const float4 *>(pp.part + sp * pp.stride + e0);
+                    const float4 b = *reinterpret_cast<const float4 *>(pp.part + sp * pp.stride + e0 + 4);
+                    v[0] += a.x; v[1] += a.y; v[2] += a.z; v[3] += a.w;
+                    v[4] += b.x; v[5] += b.y; v[6] += b.z; v[7] += b.w;
+                }
+                if (pp.bias) {
+                    float bb[8];
+                    V::unpack(cb_s[f % cpp], bb);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) v[e] += bb[e];
+                }
+                raw[k] = V::pack(v);
+            }
+        }
+    } else {
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            const int f = tid + 256 * k;
+            raw[k] = make_uint4(0u, 0u, 0u, 0u);
+            if (f < nchunks) raw[k] = STREAM ? ld_stream(xb + f) : xb[f];
+        }
     }
     float v[K][V::N];  // unpacked once, used by both passes
 #pragma unroll
@@ -241,6 +283,26 @@ hipError_t dispatch(const void *x, const void *g, const void *b, void *y, long p
 }
 
 }  // namespace
+
+hipError_t launch_rmsnorm_silu_from_partials(const ConvPartials &pp, const void *bias,
+                                             const void *gamma, const void *beta, void *y,
+                                             long positions, int c, float eps, int apply_silu,
+                                             hipStream_t s) {
+    if (positions <= 0) return hipSuccess;
+    const int cpp = c / 8;
+    if (c % 8 != 0 || cpp > FLAT_MAX_CPP || pp.S < 1) return hipErrorInvalidValue;
+    const int P = 256 / cpp;
+    int R = 1;
+    while (R < 64 && 2 * R * P <= 256 && 2 * R <= cpp) R *= 2;
+    const long blocks = (positions + P - 1) / P;
+    if (blocks > 0x7fffffffL) return hipErrorInvalidValue;
+    const Partials q{pp.part, pp.stride, pp.S, static_cast<const uint4 *>(bias)};
+    hipLaunchKernelGGL((rmsnorm_flat_kernel<true, 1, false, true>), dim3((unsigned)blocks), dim3(256),
+                       0, s, nullptr, static_cast<const uint4 *>(gamma),
+                       static_cast<const uint4 *>(beta), static_cast<uint4 *>(y), positions, cpp, P,
+                       R, sqrtf((float)c), eps, apply_silu, q);
+    return hipGetLastError();
+}
 
 hipError_t launch_rmsnorm_silu(const void *x, const void *gamma, const void *beta, void *y,
                                long positions, int c, int dtype, float eps, int apply_silu,

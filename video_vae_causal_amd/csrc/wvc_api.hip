@@ -162,9 +162,13 @@ int hip_status(hipError_t err, const char *what) {
 }
 
 // Validated conv call shared by wvc_causal_conv3d_fwd and wvc_resblock_fwd.
+// With `defer` given, a split-K MFMA conv leaves its partial sums for the
+// caller instead of reducing them into y (defer->S > 1 then; see
+// launch_conv_igemm).
 int conv_fwd(const wvc_conv3d_desc *d, const void *x, const void *cache_in, void *cache_out,
              const void *weight, const void *bias, const void *residual, void *y, void *ws,
-             size_t ws_bytes, hipStream_t s) {
+             size_t ws_bytes, hipStream_t s, wvc::ConvPartials *defer = nullptr) {
+    if (defer) *defer = wvc::ConvPartials{};
     ConvPlan pl;
     int rc = plan_conv(d, &pl);
     if (rc) return rc;
@@ -223,7 +227,7 @@ int conv_fwd(const wvc_conv3d_desc *d, const void *x, const void *cache_in, void
         if (pl.route == wvc::ConvRoute::Generic) {
             err = wvc::launch_conv_direct(c, s);
         } else {
-            err = wvc::launch_conv_igemm(c, pl.route, packed, ws, ws_bytes, cache_out, s);
+            err = wvc::launch_conv_igemm(c, pl.route, packed, ws, ws_bytes, cache_out, s, defer);
             cache_done = pl.route == wvc::ConvRoute::Fast3x3x3;  // written by the conv itself
         }
         if (err != hipSuccess) return hip_status(err, "conv launch");
@@ -444,12 +448,25 @@ int wvc_resblock_fwd(const wvc_resblock_desc *d, const void *x, void *y,
                        d->eps, 1, s)))
         return rc;
     void *cws = ws + L.conv;
+    // On a split-K plan conv1's reduce is fused into norm2: the norm kernel
+    // adds the partial sums and the bias and rounds to bf16 itself (the value
+    // a1 would hold), so a1 is never written.
+    // (Only where the vector norm applies: bf16, 16-byte aligned parameters.)
+    const bool fuse = d->dtype == WVC_BF16 && d->c_out % 8 == 0 && d->c_out <= 2048 &&
+                      aligned(p->gamma2, 16) &&
+                      aligned(p->beta2, 16) && aligned(p->b1, 16) && aligned(h2, 16);
+    wvc::ConvPartials parts;
     if ((rc = conv_fwd(&c1, h1, cache1_in, cache1_out, p->w1, p->b1, nullptr, a1, cws, L.conv_bytes,
-                       s)))
+                       s, fuse ? &parts : nullptr)))
         return rc;
-    if ((rc = norm_fwd(a1, p->gamma2, p->beta2, h2, d->n, d->c_out, d->t, d->h, d->w, d->dtype,
-                       d->eps, 1, s)))
+    if (parts.S > 1) {
+        const hipError_t err = wvc::launch_rmsnorm_silu_from_partials(
+            parts, p->b1, p->gamma2, p->beta2, h2, (long)pos, d->c_out, d->eps, 1, s);
+        if (err != hipSuccess) return hip_status(err, "norm launch");
+    } else if ((rc = norm_fwd(a1, p->gamma2, p->beta2, h2, d->n, d->c_out, d->t, d->h, d->w,
+                              d->dtype, d->eps, 1, s))) {
         return rc;
+    }
     const void *shortcut = x;
     if (proj) {
         wvc_conv3d_desc cs = c1;

@@ -62,8 +62,19 @@ size_t igemm_workspace_bytes(const ConvCall &c, ConvRoute r, bool packed_given);
 size_t igemm_packed_weight_bytes(const ConvCall &c);
 bool igemm_supports(const ConvCall &c);
 hipError_t launch_pack_weights(const ConvCall &c, const void *w, void *packed, hipStream_t s);
+// Split-K partial sums left for a consumer (see launch_conv_igemm).
+struct ConvPartials {
+    const float *part = nullptr;  // [S][N][T][H][W][Cout] fp32
+    size_t stride = 0;            // elements of one split
+    int S = 0;                    // 0: the conv wrote y itself
+};
+// With `defer` given and a split-K plan, the reduce kernel is not launched:
+// *defer describes the partials (the caller's consumer adds them in split
+// order, then the bias, and rounds once).  Otherwise defer->S is 0 and y holds
+// the output.
 hipError_t launch_conv_igemm(const ConvCall &c, ConvRoute r, bool packed_given, void *ws,
-                             size_t ws_bytes, void *cache_out, hipStream_t s);
+                             size_t ws_bytes, void *cache_out, hipStream_t s,
+                             ConvPartials *defer = nullptr);
 // Direct-convolution route (any stride/pad/dilation, fp32 or bf16).
 hipError_t launch_conv_direct(const ConvCall &c, hipStream_t s);
 
@@ -75,6 +86,13 @@ hipError_t launch_cache_update(const void *x, const void *cache_in, void *cache_
 hipError_t launch_rmsnorm_silu(const void *x, const void *gamma, const void *beta, void *y,
                                long positions, int c, int dtype, float eps, int apply_silu,
                                hipStream_t s);
+// RMS norm + SiLU whose bf16 input is itself produced on the fly from split-K
+// partial sums: x = round_bf16(sum_s part[s] + bias), exactly what the reduce
+// kernel would store, then the norm of launch_rmsnorm_silu.  bf16 only.
+hipError_t launch_rmsnorm_silu_from_partials(const ConvPartials &pp, const void *bias,
+                                             const void *gamma, const void *beta, void *y,
+                                             long positions, int c, float eps, int apply_silu,
+                                             hipStream_t s);
 
 hipError_t launch_upsample2x(const void *x, void *y, long planes, int h, int w, int c,
                              int elem_bytes, hipStream_t s);

@@ -42,8 +42,9 @@ class _PingPong:
         self.reset()
 
     def reset(self):
-        for b in self.buf:
-            L.wvc_cache_reset(b)
+        # Only the buffer the next chunk reads must be zero (zero causal
+        # padding); the other one is entirely rewritten as that chunk's cache_out.
+        L.wvc_cache_reset(self.buf[0])
         self.cur = 0
 
     @property
