@@ -152,6 +152,28 @@ def test_direct_route_stride_pad_dilation(k, stride, pad, dil, dtype):
     (check_bf16 if dtype == "bf16" else check_f32)(to_host(y), ref, f"direct {k} {stride} {pad} {dil}")
 
 
+@pytest.mark.parametrize("cin,cout,t,h,w", [(64, 64, 2, 11, 19),      # one launch, no split
+                                             (384, 384, 1, 30, 52),   # split-K + reduce
+                                             (96, 96, 3, 5, 9)])
+def test_conv3x3x3_batch2_with_cache_out(cin, cout, t, h, w):
+    """N = 2: both batch items through the MFMA route in one call, each with
+    its own cache frames in and out."""
+    n = 2
+    x = inputs.quantize(inputs.normal((n, cin, t, h, w), 77, "x"), "bf16")
+    wt = inputs.conv_weight(cout, cin, (3, 3, 3), 77, "w", "bf16")
+    b = inputs.conv_bias(cout, 77, "b", "bf16")
+    cache = inputs.quantize(inputs.normal((n, cin, 2, h, w), 77, "cache"), "bf16")
+    print(f"[case] conv3 batch2 {cin}->{cout} t={t} {h}x{w}", flush=True)
+    L.wvc_reset_counters()
+    cout_t = L.empty_cl((n, cin, 2, h, w))
+    y = L.wvc_causal_conv3d_fwd(to_dev(x), to_dev(wt), to_dev(b), cache_in=to_dev(cache),
+                                cache_out=cout_t)
+    ref = oracle.causal_conv3d(f64(x), f64(wt), f64(b), cache=f64(cache))
+    check_bf16(to_host(y), ref, f"conv3 batch2 {cin}->{cout}")
+    np.testing.assert_array_equal(to_host(cout_t), oracle.next_cache(f64(cache), f64(x)))
+    assert L.wvc_get_counters()["fast_3x3x3"] == 1
+
+
 @pytest.mark.parametrize("cin,cout,h,w", [(64, 32, 9, 13), (384, 192, 12, 40), (48, 96, 5, 7)])
 def test_conv1x1x1_projection(cin, cout, h, w):
     x = inputs.quantize(inputs.normal((1, cin, 2, h, w), 9, "x"), "bf16")
