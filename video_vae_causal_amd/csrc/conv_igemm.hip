@@ -135,6 +135,15 @@ struct Mfma<32> {
 template <int N>
 using Int = std::integral_constant<int, N>;
 
+// Compile-time loop: f(Int<0>{}), ..., f(Int<N-1>{}).
+template <int N, int I = 0, typename F>
+__device__ __forceinline__ void static_for(F &&f) {
+    if constexpr (I < N) {
+        f(Int<I>{});
+        static_for<N, I + 1>(f);
+    }
+}
+
 // Compile-time geometry of a TH x TW position tile (TH * TW == 256) and its
 // halo: HC columns, HP entries per 8-channel group; each group gets NIT*64
 // slots (every staging thread writes all of its slots unconditionally) plus 4
@@ -159,13 +168,14 @@ struct Geo {
 //     into registers while the current stage computes and is written to the
 //     other half at the end of the stage, followed by one barrier.
 //   * a row is one kernel row kh of a stage: KS taps.  The weights (A
-//     fragments) of a whole row are fetched as one batch two rows ahead into
-//     one of three register sets (row r uses set r % 3).
+//     fragments) of a row are fetched two rows ahead into one of three
+//     register sets (row r uses set r % 3), one load per MFMA group.
 //   * the input patches (B fragments) of tap k+1 are read from LDS right after
 //     the last MFMA of tap k that used the same registers.
-//   Global loads complete in issue order, so the issue order (row batch, then
-//   the next halo) is chosen such that every wait covers only loads issued at
-//   least one full row earlier.
+//   Global loads complete in issue order: the weights a row uses were issued
+//   during the row two rows back, and the halo written at the end of a stage
+//   during that stage's first row, so every wait covers loads at least a row
+//   old.
 template <int KS, int CO_T, int M, int WAVES_CO, bool SPLIT, int TW>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 igemm_kernel(IgParams p) {
@@ -285,6 +295,36 @@ igemm_kernel(IgParams p) {
                     A[SET][kw][f][ks] = as_bf16x8(bload_s(wr, wlane + (f * KSTEPS + ks) * FRAG,
                                                           row + kw * NBLK * KSTEPS * FRAG));
     };
+    // One A fragment of row rho (IDX = (kw*FCO + f)*KSTEPS + ks) into set SET.
+    auto load_a_one = [&](auto set_tag, auto idx_tag, int rho) {
+        constexpr int SET = decltype(set_tag)::value;
+        constexpr int IDX = decltype(idx_tag)::value;
+        constexpr int kw = IDX / (FCO * KSTEPS), f = (IDX / KSTEPS) % FCO, ks = IDX % KSTEPS;
+        const int u = u0 + rho / KS, kh = rho % KS;
+        const uint32_t row = (uint32_t)((((ct * p.U + u) * KS + kh) * KS) * NBLK * KSTEPS) * FRAG;
+        A[SET][kw][f][ks] = as_bf16x8(bload_s(wr, wlane + (f * KSTEPS + ks) * FRAG,
+                                              row + kw * NBLK * KSTEPS * FRAG));
+    };
+    // The next stage's halo, one staging slot at a time (halo_setup first).
+    __amdgpu_buffer_rsrc_t hfr = rsrc(p.x, 0u);
+    uint32_t hcb2 = 0;
+    bool hgok = false;
+    auto halo_setup = [&](int u) {
+        const int kt = u % KS, cb = (u / KS) * 32;
+        const int ts = t - (KS - 1) + kt;
+        if (ts >= 0)
+            hfr = rsrc(p.x + (size_t)(n * p.T + ts) * frame_elems, p.frame_bytes);
+        else if (p.cache)
+            hfr = rsrc(p.cache + (size_t)(n * p.F + p.F + ts) * frame_elems, p.frame_bytes);
+        else
+            hfr = rsrc(p.x, 0u);  // zero causal padding: every load reads zero
+        hcb2 = (uint32_t)cb * 2;
+        hgok = cb + g * 8 < p.Cin;
+    };
+    auto halo_one = [&](auto k_tag) {
+        constexpr int k = decltype(k_tag)::value;
+        hv[k] = bload(hfr, (hgok && soff[k] != OOB) ? soff[k] + hcb2 : OOB);
+    };
     auto load_halo = [&](int u) {
         const int kt = u % KS, cb = (u / KS) * 32;
         const int ts = t - (KS - 1) + kt;
@@ -333,29 +373,46 @@ igemm_kernel(IgParams p) {
         const int buf = (u - u0) & 1;
         const uint4 *hb = &halo[buf][bbase];
         const bool last_stage = u + 1 >= u1;
-        load_row(Int<(SET + 2) % 3>{}, rho + 2 < R ? rho + 2 : R - 1);
-        if (kh == 0) load_halo(last_stage ? u : u + 1);
-        __builtin_amdgcn_sched_barrier(0);
+        const int rnext = rho + 2 < R ? rho + 2 : R - 1;
+        if (kh == 0) halo_setup(last_stage ? u : u + 1);
         // Tap tp = kh*KS + kw of the stage reads B[tp & 1]; the next tap's set is
         // filled while this tap's MFMAs run, so no LDS read ever overwrites
-        // registers an in-flight MFMA is still reading.
+        // registers an in-flight MFMA is still reading.  The global loads (the
+        // weights of row rho+2, and in a stage's first row the next halo) are
+        // spread one at a time over the row's MFMA groups: the wave issues in
+        // order, and a block of loads between two MFMAs would leave the matrix
+        // pipe idle while it is issued.
         auto tap = [&](auto kw_tag) {
             constexpr int kw = decltype(kw_tag)::value;
             constexpr int tp = kh * KS + kw;
             constexpr int cur = tp & 1;
             constexpr bool next_in_stage = tp + 1 < KS * KS;
             constexpr int nkh = (tp + 1) / KS, nkw = (tp + 1) % KS;
-#pragma unroll
-            for (int ks = 0; ks < KSTEPS; ++ks) {
-#pragma unroll
-                for (int j = 0; j < FPOS; ++j) {
+            static_for<KSTEPS>([&](auto ks_tag) {
+                constexpr int ks = decltype(ks_tag)::value;
+                static_for<FPOS>([&](auto j_tag) {
+                    constexpr int j = decltype(j_tag)::value;
 #pragma unroll
                     for (int i = 0; i < FCO; ++i)
                         acc[i][j] = MF::run(A[SET][kw][i][ks], B[cur][j][ks], acc[i][j]);
                     if (ks == 0 && next_in_stage) load_b(Int<cur ^ 1>{}, hb, j, nkh, nkw);
+                    // group index within the row, and the loads that fall on it
+                    constexpr int NG = KS * KSTEPS * FPOS, NL = KS * FCO * KSTEPS;
+                    constexpr int grp = (kw * KSTEPS + ks) * FPOS + j;
+                    static_for<NL>([&](auto li) {
+                        constexpr int L_ = decltype(li)::value;
+                        if constexpr ((L_ * NG) / NL == grp)
+                            load_a_one(Int<(SET + 2) % 3>{}, Int<L_>{}, rnext);
+                    });
+                    if constexpr (kh == 0) {
+                        static_for<NIT>([&](auto hk) {
+                            constexpr int K_ = decltype(hk)::value;
+                            if constexpr ((K_ * NG + NG / 2) / NIT == grp) halo_one(Int<K_>{});
+                        });
+                    }
                     __builtin_amdgcn_sched_barrier(0);
-                }
-            }
+                });
+            });
         };
         tap(Int<0>{});
         if constexpr (KS > 1) {
