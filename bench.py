@@ -220,7 +220,7 @@ def wl_layer96():
                 kernel=kernel, kernel_name="igemm_kernel<3, 96, 16, 2, false, 32>",
                 kernel_units=acc.conv_flops(n, 4, h, w, c, c), kernel_bound="mfma",
                 kernel_bytes=acc.conv_launch_bytes(n, 4, h, w, c, c),
-                norm_kernel=norm_kernel, norm_kernel_name="rmsnorm_flat_kernel<true, 2, true>",
+                norm_kernel=norm_kernel, norm_kernel_name="rmsnorm_flat_kernel<true, 2, true, false>",
                 norm_bytes=acc.norm_bytes(n * c * t * h * w))
     return step, info
 
