@@ -186,6 +186,26 @@ def test_conv1x1x1_projection(cin, cout, h, w):
     assert L.wvc_get_counters()["fast_1x1x1"] == 1
 
 
+@pytest.mark.parametrize("n,cin,cout,t,h,w", [(2, 40, 64, 2, 3, 7),     # C_in not a multiple of 32
+                                               (1, 384, 192, 1, 30, 52),  # 1560 positions: ragged last tile
+                                               (1, 256, 256, 3, 5, 5),
+                                               (2, 96, 32, 1, 1, 63)])
+def test_conv1x1x1_projection_edges_with_residual(n, cin, cout, t, h, w):
+    """The 1x1x1 route (one 64-position tile per workgroup, all output
+    channels): zero-padded channel blocks, a ragged last tile, two batch items
+    and a fused residual."""
+    x = inputs.quantize(inputs.normal((n, cin, t, h, w), 19, "x"), "bf16")
+    wt = inputs.conv_weight(cout, cin, (1, 1, 1), 19, "w", "bf16")
+    b = inputs.conv_bias(cout, 19, "b", "bf16")
+    res = inputs.quantize(inputs.normal((n, cout, t, h, w), 19, "r"), "bf16")
+    print(f"[case] conv1x1 n={n} {cin}->{cout} t={t} {h}x{w}", flush=True)
+    L.wvc_reset_counters()
+    y = L.wvc_causal_conv3d_fwd(to_dev(x), to_dev(wt), to_dev(b), residual=to_dev(res), padding=(0, 0))
+    ref = oracle.causal_conv3d(f64(x), f64(wt), f64(b), pad=(0, 0)) + f64(res)
+    check_bf16(to_host(y), ref, f"conv1x1 {cin}->{cout} + residual")
+    assert L.wvc_get_counters()["fast_1x1x1"] == 1
+
+
 @pytest.mark.parametrize("sizes", [[1, 1, 1, 1, 1], [2, 3], [4, 1], [1, 4]])
 def test_chunked_equals_whole(sizes):
     """Chunks with the rolling cache give the whole-sequence result.  Launches

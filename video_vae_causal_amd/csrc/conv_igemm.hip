@@ -704,7 +704,7 @@ Plan make_plan(const ConvCall &c, ConvRoute r) {
             best_s = s;
         }
     }
-    pl.S = best_s;
+    pl.S = proj_supports(c) ? 1 : best_s;  // the projection kernel never splits K
     return pl;
 }
 
@@ -716,6 +716,18 @@ size_t part_bytes(const Plan &pl, const ConvCall &c) {
 }
 
 int tile_m(int co_t) { return (co_t == 96 || co_t == 64) ? 16 : 32; }
+
+// Channel tile and MFMA edge the packed weights are ordered for: one tile of
+// all C_out channels in 16-row blocks for the 1x1x1 projection kernel,
+// otherwise the implicit-GEMM kernel's tile.
+struct PackGeom {
+    int co_t, m;
+};
+PackGeom pack_geom(const ConvCall &c) {
+    if (proj_supports(c)) return PackGeom{c.cout, 16};
+    const int ct = co_tile_for(c.cout);
+    return PackGeom{ct, tile_m(ct)};
+}
 
 size_t packed_bytes(const ConvCall &c) {
     const size_t nb = (size_t)(c.cin + 31) / 32;
@@ -761,8 +773,8 @@ size_t igemm_workspace_bytes(const ConvCall &c, ConvRoute r, bool packed_given) 
 size_t igemm_packed_weight_bytes(const ConvCall &c) { return packed_bytes(c); }
 
 hipError_t launch_pack_weights(const ConvCall &c, const void *w, void *packed, hipStream_t s) {
-    const int co_t = co_tile_for(c.cout);
-    const int m = tile_m(co_t);
+    const PackGeom pg = pack_geom(c);
+    const int co_t = pg.co_t, m = pg.m;
     const long chunks = (long)packed_bytes(c) / 16;
     long blocks = (chunks + 255) / 256;
     if (blocks > 8192) blocks = 8192;
@@ -799,6 +811,8 @@ hipError_t launch_conv_igemm(const ConvCall &c, ConvRoute r, bool packed_given, 
         if (e != hipSuccess) return e;
         wp = dst;
     }
+    if (r == ConvRoute::Fast1x1x1 && proj_supports(c))
+        return launch_conv_proj(c, wp, packed_bytes(c), s);
     IgParams p{};
     p.x = static_cast<const uint16_t *>(c.x);
     p.cache = static_cast<const uint16_t *>(c.cache_in);

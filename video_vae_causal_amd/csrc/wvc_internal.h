@@ -75,6 +75,12 @@ struct ConvPartials {
 hipError_t launch_conv_igemm(const ConvCall &c, ConvRoute r, bool packed_given, void *ws,
                              size_t ws_bytes, void *cache_out, hipStream_t s,
                              ConvPartials *defer = nullptr);
+// 1x1x1 projection kernel (conv_proj.hip), used by launch_conv_igemm for the
+// 1x1x1 route when proj_supports(c): C_out <= 256, C_in <= 480.  `packed` holds
+// the weights in the 16-row fragment order for a single channel tile.
+bool proj_supports(const ConvCall &c);
+hipError_t launch_conv_proj(const ConvCall &c, const void *packed, size_t packed_bytes,
+                            hipStream_t s);
 // Direct-convolution route (any stride/pad/dilation, fp32 or bf16).
 hipError_t launch_conv_direct(const ConvCall &c, hipStream_t s);
 
