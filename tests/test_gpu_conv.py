@@ -206,6 +206,29 @@ def test_conv1x1x1_projection_edges_with_residual(n, cin, cout, t, h, w):
     assert L.wvc_get_counters()["fast_1x1x1"] == 1
 
 
+@pytest.mark.parametrize("cin,cout,with_bias", [(384, 192, True), (96, 64, False), (256, 128, True),
+                                                (320, 176, True)])
+def test_conv1x1x1_projection_persistent_vs_oracle(cin, cout, with_bias):
+    """Enough 64-position tiles (66049 positions, a 1-position last tile) for
+    the persistent variant that keeps the weights in registers and loops over
+    tiles: one to three 16-channel blocks per wave, fewer than 12 K-steps and
+    an unused block (176 channels), no bias; every output against the oracle,
+    with a fused residual."""
+    shape = (1, cin, 1, 257, 257)
+    x = inputs.quantize(inputs.normal(shape, 23, "x"), "bf16")
+    wt = inputs.conv_weight(cout, cin, (1, 1, 1), 23, "w", "bf16")
+    b = inputs.conv_bias(cout, 23, "b", "bf16") if with_bias else None
+    res = inputs.quantize(inputs.normal((1, cout, 1, 257, 257), 23, "r"), "bf16")
+    print(f"[case] conv1x1 persistent {cin}->{cout} 257x257 bias={with_bias}", flush=True)
+    y = L.wvc_causal_conv3d_fwd(to_dev(x), to_dev(wt), to_dev(b) if with_bias else None,
+                                residual=to_dev(res), padding=(0, 0))
+    ref = oracle.causal_conv3d(f64(x), f64(wt), f64(b) if with_bias else None, pad=(0, 0)) + f64(res)
+    check_bf16(to_host(y), ref, f"conv1x1 persistent {cin}->{cout}")
+    y2 = L.wvc_causal_conv3d_fwd(to_dev(x), to_dev(wt), to_dev(b) if with_bias else None,
+                                 residual=to_dev(res), padding=(0, 0))
+    assert torch.equal(y, y2), "persistent projection is not run-to-run deterministic"
+
+
 @pytest.mark.parametrize("sizes", [[1, 1, 1, 1, 1], [2, 3], [4, 1], [1, 4]])
 def test_chunked_equals_whole(sizes):
     """Chunks with the rolling cache give the whole-sequence result.  Launches

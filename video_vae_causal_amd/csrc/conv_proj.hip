@@ -7,8 +7,17 @@
 // With a single tap there is no halo and the positions of a chunk are one
 // contiguous channels-last run, so the conv is a plain GEMM
 // [P x C_in] x [C_in x C_out] with arithmetic intensity ~C_out/3 FLOP/B: at
-// C_out = 192 it is bound by HBM, not by the matrix cores.  The kernel is laid
-// out for that:
+// C_out = 192 it is bound by HBM, not by the matrix cores.  Two kernels:
+//
+// proj_persist_kernel (C_in % 32 == 0, C_in <= 384, C_out <= 192, and at
+// least four tiles per CU): one 8-wave workgroup per CU keeps its slice of
+// the weights in registers for the whole launch and loops over 64-position
+// tiles, staging each through one of two LDS buffers while the next tile's
+// loads are in flight; a wave owns a quarter of the output channels for half
+// of the tile's positions, so the LDS reads per tile are twice the tile, not
+// one tile per wave.
+//
+// proj_kernel (every other shape) is laid out as follows:
 //   * a workgroup owns 64 consecutive positions and every output channel, so
 //     each input byte is read from HBM exactly once;
 //   * its input tile (64 x C_in bf16) is staged in LDS with fully coalesced
@@ -31,7 +40,8 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int PT = 64;  // positions per workgroup
+constexpr int PT = 64;    // positions per workgroup
+constexpr int MAXQ = 16;  // staging chunks per thread: PT * 4 * nb / 256 = nb <= 16
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
 
@@ -61,13 +71,24 @@ __global__ void __launch_bounds__(256) proj_kernel(const uint16_t *__restrict__ 
     // Stage the input tile: chunk q of the contiguous run (8 channels each)
     // goes to row q / (cin/8), entry q % (cin/8); the padding channels up to
     // nb*32 and the rows past np are zero.
+    // All of a thread's loads are issued before its first LDS store, so the
+    // tile costs one HBM round trip, not one per chunk.
     const int c8 = cin / 8;
     const uint4 *xg = reinterpret_cast<const uint4 *>(x + p0 * cin);
-    for (int q = tid; q < PT * nb * 4; q += 256) {
+    const int nq = PT * nb * 4;  // <= 256 * MAXQ (proj_supports bounds nb)
+    uint4 v[MAXQ];
+#pragma unroll
+    for (int k = 0; k < MAXQ; ++k) {
+        const int q = tid + 256 * k;
         const int r = q / (nb * 4), e = q - r * (nb * 4);
-        uint4 v = make_uint4(0u, 0u, 0u, 0u);
-        if (r < np && e < c8) v = xg[(long)r * c8 + e];
-        xs[r * pitch16 + e] = v;
+        v[k] = make_uint4(0u, 0u, 0u, 0u);
+        if (q < nq && r < np && e < c8) v[k] = xg[(long)r * c8 + e];
+    }
+#pragma unroll
+    for (int k = 0; k < MAXQ; ++k) {
+        const int q = tid + 256 * k;
+        const int r = q / (nb * 4), e = q - r * (nb * 4);
+        if (q < nq) xs[r * pitch16 + e] = v[k];
     }
 
     // Weights: packed [K-step][16-row block][lane] 1 KiB fragments.
@@ -151,11 +172,161 @@ __global__ void __launch_bounds__(256) proj_kernel(const uint16_t *__restrict__ 
     }
 }
 
+// Persistent variant, one workgroup of 8 waves per CU, for C_in % 32 == 0,
+// C_in <= 384 and C_out <= 192.  Wave w owns the output blocks (w & 3) + 4f
+// for the half (w >> 2) of the 64 positions, so each wave reads only its half
+// of the LDS tile.  Its weight fragments (NB K-steps x FCO blocks) are loaded
+// into registers once; the workgroup then loops over tiles g, g + grid, ...
+// Per tile: the tile's staged chunks go to one of two LDS buffers, one
+// barrier, the next tile's loads are issued, then the MFMAs and stores of
+// this tile run while those loads are in flight.  The bias is kept as fp32 in
+// LDS so that no global load in the epilogue waits behind the prefetch.
+template <int FCO, int MAXNB>
+__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+proj_persist_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict__ wp,
+                    const uint16_t *__restrict__ bias, const uint16_t *__restrict__ res,
+                    uint16_t *__restrict__ y, long P, int cin, int cout, uint32_t w_bytes) {
+    constexpr int MAXC = MAXNB / 2;  // 16-byte chunks per thread: 64 * nb * 4 / 512
+    extern __shared__ uint4 xs[];    // [2][PT][pitch16], then C_out fp32 bias
+    const int nb = cin / 32;
+    const int c8 = cin / 8;
+    const int pitch16 = c8 + 1;
+    const int buf16 = PT * pitch16;
+    const int nblk = cout / 16;
+    const int nq = PT * c8;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int cg = wave & 3, ph = wave >> 2;
+    const int lr = lane & 15, lg = lane >> 4;
+    const long ntiles = (P + PT - 1) / PT;
+
+    const __amdgpu_buffer_rsrc_t wr =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(wp), (short)0, (int)w_bytes, 0x00020000);
+    bf16x8 A[MAXNB][FCO];
+#pragma unroll
+    for (int ks = 0; ks < MAXNB; ++ks)
+#pragma unroll
+        for (int f = 0; f < FCO; ++f) {
+            const int blk = cg + 4 * f;
+            const int bc = blk < nblk ? blk : 0;  // surplus blocks read block 0, never stored
+            const int kc = ks < nb ? ks : 0;
+            A[ks][f] = as_bf16x8(wload(wr, (uint32_t)((kc * nblk + bc) * 1024 + lane * 16)));
+        }
+    float *bias_s = reinterpret_cast<float *>(xs + 2 * buf16);
+    for (int i = tid; i < cout; i += 512) bias_s[i] = bias ? bf16_to_f32(bias[i]) : 0.f;
+
+    // A tile is one contiguous run of np * c8 chunks; chunk q goes to LDS
+    // entry q + q / c8 (one pad entry per row).  Buffer loads bounded to the
+    // tile's bytes return zero for the rows past the last position.
+    const float inv_c8 = 1.0f / (float)c8;  // q / c8 exactly: q < 2^12, c8 <= 48
+    uint4 v[MAXC];
+    auto load_tile = [&](long tile) {
+        const long p0 = tile * PT;
+        const long left = P - p0;
+        const int np = tile < ntiles ? (int)(left < PT ? left : PT) : 0;
+        const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint16_t *>(x + (tile < ntiles ? p0 : 0) * cin), (short)0, np * cin * 2,
+            0x00020000);
+#pragma unroll
+        for (int k = 0; k < MAXC; ++k) {
+            const u32x4 t4 = __builtin_amdgcn_raw_buffer_load_b128(xr, tid * 16, k * 8192, 0);
+            v[k] = make_uint4(t4.x, t4.y, t4.z, t4.w);
+        }
+    };
+    auto store_tile = [&](int b) {
+#pragma unroll
+        for (int k = 0; k < MAXC; ++k) {
+            const int q = tid + 512 * k;
+            const int r = (int)(((float)q + 0.5f) * inv_c8);
+            if (q < nq) xs[b * buf16 + q + r] = v[k];
+        }
+    };
+    auto compute = [&](long tile, int b) {
+        const long p0 = tile * PT;
+        const int np = (int)(P - p0 < PT ? P - p0 : PT);
+        f32x4 acc[FCO][2];
+#pragma unroll
+        for (int f = 0; f < FCO; ++f)
+#pragma unroll
+            for (int j = 0; j < 2; ++j) acc[f][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        // B fragment j: row ph*32 + j*16 + lr, channels ks*32 + lg*8 .. +7.
+        const uint4 *xb = xs + b * buf16 + (ph * 32 + lr) * pitch16 + lg;
+#pragma unroll
+        for (int ks = 0; ks < MAXNB; ++ks) {
+            if (ks < nb) {
+                bf16x8 B[2];
+#pragma unroll
+                for (int j = 0; j < 2; ++j) B[j] = as_bf16x8(xb[j * 16 * pitch16 + ks * 4]);
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+#pragma unroll
+                    for (int f = 0; f < FCO; ++f)
+                        acc[f][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[ks][f], B[j], acc[f][j], 0, 0, 0);
+            }
+        }
+        // Element e of tile (f, j): channel blk*16 + lg*4 + e, position
+        // ph*32 + j*16 + lr; + bias, + residual, one rounding.
+#pragma unroll
+        for (int f = 0; f < FCO; ++f) {
+            const int blk = cg + 4 * f;
+            if (blk >= nblk) continue;
+            const int co = blk * 16 + lg * 4;
+            const float4 bq = *reinterpret_cast<const float4 *>(bias_s + co);
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const int r = ph * 32 + j * 16 + lr;
+                if (r >= np) continue;
+                const size_t o = (size_t)(p0 + r) * cout + co;
+                float vv[4] = {acc[f][j][0] + bq.x, acc[f][j][1] + bq.y, acc[f][j][2] + bq.z,
+                               acc[f][j][3] + bq.w};
+                if (res) {
+                    const uint2 rr = *reinterpret_cast<const uint2 *>(res + o);
+                    vv[0] += bf16_to_f32(rr.x & 0xffffu);
+                    vv[1] += bf16_to_f32(rr.x >> 16);
+                    vv[2] += bf16_to_f32(rr.y & 0xffffu);
+                    vv[3] += bf16_to_f32(rr.y >> 16);
+                }
+                *reinterpret_cast<uint2 *>(y + o) =
+                    make_uint2(pack2_bf16(vv[0], vv[1]), pack2_bf16(vv[2], vv[3]));
+            }
+        }
+    };
+
+    // Buffer b is written only after the barrier that follows the last reads
+    // of it (the compute two tiles back), so one barrier per tile suffices.
+    const long G = gridDim.x;
+    int b = 0;
+    long tile = blockIdx.x;
+    load_tile(tile);
+    for (; tile < ntiles; tile += G) {
+        store_tile(b);
+        __syncthreads();
+        load_tile(tile + G);
+        compute(tile, b);
+        b ^= 1;
+    }
+}
+
+int num_cus_proj() {
+    static int cached = 0;
+    if (!cached) {
+        int dev = 0, cus = 0;
+        if (hipGetDevice(&dev) == hipSuccess &&
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+            cus > 0)
+            cached = cus;
+        else
+            cached = 256;
+    }
+    return cached;
+}
+
 }  // namespace
 
 bool proj_supports(const ConvCall &c) {
     return c.kt == 1 && c.kh == 1 && c.kw == 1 && c.cout % 16 == 0 && c.cout <= 256 &&
-           c.cin % 8 == 0 && ((size_t)PT * ((c.cin + 31) / 32 * 4 + 1) * 16) <= 64 * 1024;
+           c.cin % 8 == 0 && (c.cin + 31) / 32 <= MAXQ &&
+           ((size_t)PT * ((c.cin + 31) / 32 * 4 + 1) * 16) <= 64 * 1024;
 }
 
 hipError_t launch_conv_proj(const ConvCall &c, const void *packed, size_t packed_bytes,
@@ -173,6 +344,19 @@ hipError_t launch_conv_proj(const ConvCall &c, const void *packed, size_t packed
     const auto *r = static_cast<const uint16_t *>(c.residual);
     auto *y = static_cast<uint16_t *>(c.y);
     const uint32_t wb = (uint32_t)packed_bytes;
+    // Persistent variant: C_in a multiple of 32 with at most 12 K-steps (the
+    // waves' weight fragments fit in registers), C_out <= 192, and several
+    // tiles per CU.
+    if (c.cin % 32 == 0 && nb <= 12 && fco <= 3 && blocks >= 4L * num_cus_proj()) {
+        const unsigned grid = (unsigned)num_cus_proj();
+        const size_t lds2 = 2 * lds + (size_t)c.cout * 4;
+        switch (fco) {
+            case 1: hipLaunchKernelGGL((proj_persist_kernel<1, 12>), dim3(grid), dim3(512), lds2, s, x, w, b, r, y, P, c.cin, c.cout, wb); break;
+            case 2: hipLaunchKernelGGL((proj_persist_kernel<2, 12>), dim3(grid), dim3(512), lds2, s, x, w, b, r, y, P, c.cin, c.cout, wb); break;
+            default: hipLaunchKernelGGL((proj_persist_kernel<3, 12>), dim3(grid), dim3(512), lds2, s, x, w, b, r, y, P, c.cin, c.cout, wb); break;
+        }
+        return hipGetLastError();
+    }
     switch (fco) {
         case 1: hipLaunchKernelGGL(proj_kernel<1>, dim3((unsigned)blocks), dim3(256), lds, s, x, w, b, r, y, P, c.cin, c.cout, wb); break;
         case 2: hipLaunchKernelGGL(proj_kernel<2>, dim3((unsigned)blocks), dim3(256), lds, s, x, w, b, r, y, P, c.cin, c.cout, wb); break;
