@@ -13,7 +13,9 @@
  * Conventions shared by every entry point
  * ---------------------------------------
  * Pointers.  Every tensor pointer is a DEVICE pointer owned by the caller.
- *   The library never allocates, frees or keeps a pointer past the call.
+ *   The library never allocates device memory, frees it, or keeps a pointer
+ *   past the call (a captured graph keeps the pointers it recorded; see the
+ *   graph calls at the end).
  * Streams.  `stream` is a hipStream_t passed as void* (NULL = the null
  *   stream).  Every call only enqueues work on that stream and returns; the
  *   library never synchronises.  Results are ready when the stream is.
@@ -240,6 +242,40 @@ const char *wvc_last_error(void);
 
 /* Library version string. */
 const char *wvc_version(void);
+
+/*
+ * Graphs.  A streamed decode enqueues a few dozen short launches per latent
+ * frame; [P1] section 8.5 counts the launches of its exported decoder per
+ * iteration and section 8.7 lists graph capture as the remedy for their
+ * overhead.  These calls record what the other entry points enqueue on one
+ * stream into a HIP graph and replay it with one call.
+ *
+ * wvc_graph_capture_begin(stream): starts a capture (thread-local mode) on
+ *   `stream`, which must be a created stream: the null stream cannot be
+ *   captured (WVC_ERR_ARG).  Until the matching end, library calls that
+ *   enqueue on `stream` from this thread are recorded instead of run.  They
+ *   must not need a workspace allocation or a host synchronisation in
+ *   between; the library's own calls never make either.
+ * wvc_graph_capture_end(stream, graph): ends the capture and instantiates
+ *   it.  *graph receives an opaque handle owned by the caller; it is NULL
+ *   after a failure (WVC_ERR_HIP, e.g. when a recorded launch was invalid).
+ * wvc_graph_launch(graph, stream): enqueues one replay on any stream (NULL
+ *   included).  A replay reads and writes exactly the buffers the recorded
+ *   calls named, at the sizes and values of their scalar arguments at capture
+ *   time: the caller keeps those buffers allocated, at the same addresses,
+ *   for the life of the graph.  Replays on one stream run in order, like the
+ *   calls they record; the route counters count the recorded calls once.
+ * wvc_graph_destroy(graph): releases the handle (NULL is a no-op).  Call it
+ *   once every replay has completed (synchronise the replay streams first).
+ *
+ * The graph handle and the HIP runtime's instantiated graph are the only
+ * things the library allocates; none of it is tensor memory.
+ */
+typedef struct wvc_graph wvc_graph;
+int wvc_graph_capture_begin(void *stream);
+int wvc_graph_capture_end(void *stream, wvc_graph **graph);
+int wvc_graph_launch(const wvc_graph *graph, void *stream);
+int wvc_graph_destroy(wvc_graph *graph);
 
 #ifdef __cplusplus
 }

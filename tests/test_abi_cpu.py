@@ -203,3 +203,15 @@ def test_binding_refuses_host_tensors(lib):
     w = torch.zeros((16, 16, 3, 3, 3), dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         L.wvc_causal_conv3d_fwd(x, w)
+
+
+def test_graph_calls_reject_bad_arguments_without_touching_the_gpu(lib):
+    # the null stream cannot be captured; NULL handles are argument errors
+    assert lib.wvc_graph_capture_begin(None) == L.WVC_ERR_ARG
+    assert "null stream" in L.wvc_last_error()
+    h = ctypes.c_void_p(0x1234)
+    assert lib.wvc_graph_capture_end(None, ctypes.byref(h)) == L.WVC_ERR_ARG
+    assert h.value is None                      # *graph is cleared on failure
+    assert lib.wvc_graph_capture_end(ctypes.c_void_p(0x1000), None) == L.WVC_ERR_ARG
+    assert lib.wvc_graph_launch(None, None) == L.WVC_ERR_ARG
+    assert lib.wvc_graph_destroy(None) == L.WVC_OK

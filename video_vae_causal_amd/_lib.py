@@ -33,7 +33,8 @@ EXPORTED = (
     "wvc_conv3d_packed_weight_bytes", "wvc_conv3d_pack_weights",
     "wvc_rmsnorm_silu", "wvc_resblock_fwd", "wvc_resblock_workspace_bytes", "wvc_cache_reset",
     "wvc_upsample_nearest2x", "wvc_set_strict", "wvc_get_strict", "wvc_get_counters",
-    "wvc_reset_counters", "wvc_last_error", "wvc_version",
+    "wvc_reset_counters", "wvc_last_error", "wvc_version", "wvc_graph_capture_begin",
+    "wvc_graph_capture_end", "wvc_graph_launch", "wvc_graph_destroy",
 )
 
 
@@ -111,6 +112,14 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.wvc_last_error.restype = ctypes.c_char_p
     lib.wvc_version.argtypes = []
     lib.wvc_version.restype = ctypes.c_char_p
+    lib.wvc_graph_capture_begin.argtypes = [vp]
+    lib.wvc_graph_capture_begin.restype = i
+    lib.wvc_graph_capture_end.argtypes = [vp, ctypes.POINTER(vp)]
+    lib.wvc_graph_capture_end.restype = i
+    lib.wvc_graph_launch.argtypes = [vp, vp]
+    lib.wvc_graph_launch.restype = i
+    lib.wvc_graph_destroy.argtypes = [vp]
+    lib.wvc_graph_destroy.restype = i
     _lib = lib
     return lib
 
@@ -375,3 +384,61 @@ def wvc_last_error() -> str:
 
 def wvc_version() -> str:
     return load().wvc_version().decode()
+
+
+# ---------------------------------------------------------------------------
+# Graphs (wvc_graph_* in include/wvc.h)
+# ---------------------------------------------------------------------------
+
+class Graph:
+    """Handle of a captured HIP graph.  ``launch()`` enqueues one replay on
+    the current stream; the handle is released by ``close()`` (or when it is
+    garbage-collected), after the device has finished every replay."""
+
+    def __init__(self, handle: ctypes.c_void_p, device: torch.device):
+        self._h = handle
+        self.device = device
+
+    def launch(self, stream: Optional[torch.cuda.Stream] = None):
+        wvc_graph_launch(self, stream)
+
+    def close(self):
+        if self._h is not None and self._h.value:
+            torch.cuda.synchronize(self.device)
+            _check(load().wvc_graph_destroy(self._h))
+        self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def _stream_handle(stream: Optional[torch.cuda.Stream], device=None) -> ctypes.c_void_p:
+    s = stream if stream is not None else torch.cuda.current_stream(device)
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def wvc_graph_capture_begin(stream: torch.cuda.Stream):
+    """Start recording the library calls enqueued on ``stream`` (a created
+    stream, not the null stream) from this thread."""
+    _check(load().wvc_graph_capture_begin(_stream_handle(stream)))
+
+
+def wvc_graph_capture_end(stream: torch.cuda.Stream) -> Graph:
+    """End the recording on ``stream`` and instantiate it."""
+    h = ctypes.c_void_p()
+    _check(load().wvc_graph_capture_end(_stream_handle(stream), ctypes.byref(h)))
+    return Graph(h, stream.device)
+
+
+def wvc_graph_launch(graph: Graph, stream: Optional[torch.cuda.Stream] = None):
+    """Enqueue one replay of ``graph`` on ``stream`` (default: current)."""
+    if graph._h is None:
+        raise ValueError("graph was destroyed")
+    _check(load().wvc_graph_launch(graph._h, _stream_handle(stream, graph.device)))
+
+
+def wvc_graph_destroy(graph: Graph):
+    graph.close()

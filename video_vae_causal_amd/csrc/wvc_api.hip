@@ -8,6 +8,8 @@
 #include <cstdlib>
 #include <cstring>
 
+#include <new>
+
 #include "wvc.h"
 #include "wvc_internal.h"
 
@@ -503,6 +505,59 @@ int wvc_upsample_nearest2x(const void *x, void *y, int n, int c, int t, int h, i
     return hip_status(
         wvc::launch_upsample2x(x, y, planes, h, w, c, e, static_cast<hipStream_t>(stream)),
         "upsample launch");
+}
+
+struct wvc_graph {
+    hipGraph_t graph;
+    hipGraphExec_t exec;
+};
+
+int wvc_graph_capture_begin(void *stream) {
+    if (!stream) return fail(WVC_ERR_ARG, "the null stream cannot be captured; pass a created stream");
+    return hip_status(hipStreamBeginCapture(static_cast<hipStream_t>(stream),
+                                            hipStreamCaptureModeThreadLocal),
+                      "begin capture");
+}
+
+int wvc_graph_capture_end(void *stream, wvc_graph **graph) {
+    if (!graph) return fail(WVC_ERR_ARG, "graph is NULL");
+    *graph = nullptr;
+    if (!stream) return fail(WVC_ERR_ARG, "stream is NULL");
+    hipGraph_t g = nullptr;
+    hipError_t err = hipStreamEndCapture(static_cast<hipStream_t>(stream), &g);
+    if (err != hipSuccess) {
+        if (g) (void)hipGraphDestroy(g);
+        return hip_status(err, "end capture");
+    }
+    if (!g) return fail(WVC_ERR_HIP, "end capture returned no graph");
+    hipGraphExec_t exec = nullptr;
+    err = hipGraphInstantiate(&exec, g, nullptr, nullptr, 0);
+    if (err != hipSuccess) {
+        (void)hipGraphDestroy(g);
+        return hip_status(err, "graph instantiate");
+    }
+    wvc_graph *h = new (std::nothrow) wvc_graph{g, exec};
+    if (!h) {
+        (void)hipGraphExecDestroy(exec);
+        (void)hipGraphDestroy(g);
+        return fail(WVC_ERR_HIP, "out of host memory for the graph handle");
+    }
+    *graph = h;
+    return WVC_OK;
+}
+
+int wvc_graph_launch(const wvc_graph *graph, void *stream) {
+    if (!graph) return fail(WVC_ERR_ARG, "graph is NULL");
+    return hip_status(hipGraphLaunch(graph->exec, static_cast<hipStream_t>(stream)), "graph launch");
+}
+
+int wvc_graph_destroy(wvc_graph *graph) {
+    if (!graph) return WVC_OK;
+    const hipError_t e1 = hipGraphExecDestroy(graph->exec);
+    const hipError_t e2 = hipGraphDestroy(graph->graph);
+    delete graph;
+    if (e1 != hipSuccess) return hip_status(e1, "graph exec destroy");
+    return hip_status(e2, "graph destroy");
 }
 
 void wvc_set_strict(int on) { g_strict.store(on ? 1 : 0); }

@@ -13,11 +13,16 @@ stream zero-fills the caches, which is exactly zero causal padding before
 frame 0.  The caches are the whole resumable state of a stream:
 ``state()``/``load_state()`` copy them out and back (checkpoint/resume).
 
+A chunk of a stack is a few dozen short launches.  ``capture`` records them
+into a HIP graph (the launch-overhead remedy of the Cosmos3 page's section
+8.7); ``FrameGraph`` replays one chunk per call with the stack's ping-pong
+state kept in step.
+
 Host orchestration only; every tensor operation is a libwvc call.
 """
 from __future__ import annotations
 
-from typing import Dict, List, Optional, Sequence
+from typing import Callable, Dict, List, Optional, Sequence
 
 import torch
 
@@ -102,6 +107,14 @@ class CausalConv3d:
     def caches(self) -> List[torch.Tensor]:
         return [self.cache.cin] if self.cache is not None else []
 
+    def reset(self):
+        """Zero the caches in place (a new sequence), keeping their buffers."""
+        if self.cache is not None:
+            self.cache.reset()
+
+    def pingpongs(self) -> List[_PingPong]:
+        return [self.cache] if self.cache is not None else []
+
 
 class ResBlock:
     """Wan residual block with the two caches of its 3x3x3 convs."""
@@ -121,8 +134,22 @@ class ResBlock:
         cin = self.p["w1"].shape[1]
         cout = self.p["w1"].shape[0]
         dt, dev = self.p["w1"].dtype, self.p["w1"].device
-        self.c1 = _PingPong((n, cin, CACHE_T, h, w), dt, dev)
-        self.c2 = _PingPong((n, cout, CACHE_T, h, w), dt, dev)
+        s1, s2 = (n, cin, CACHE_T, h, w), (n, cout, CACHE_T, h, w)
+        if self.c1 is not None and tuple(self.c1.buf[0].shape) == s1 and \
+                tuple(self.c2.buf[0].shape) == s2:
+            self.reset()
+            return
+        self.c1 = _PingPong(s1, dt, dev)
+        self.c2 = _PingPong(s2, dt, dev)
+
+    def reset(self):
+        """Zero the caches in place (a new sequence), keeping their buffers."""
+        if self.c1 is not None:
+            self.c1.reset()
+            self.c2.reset()
+
+    def pingpongs(self) -> List[_PingPong]:
+        return [self.c1, self.c2] if self.c1 is not None else []
 
     def __call__(self, x: torch.Tensor, y: Optional[torch.Tensor] = None) -> torch.Tensor:
         if self.c1 is None:
@@ -161,6 +188,14 @@ class Stream:
             for c in l.caches():
                 c.copy_(next(it))
 
+    def reset(self):
+        """Zero every cache in place (a new sequence)."""
+        for l in self._cache_layers():
+            l.reset()
+
+    def pingpongs(self) -> List[_PingPong]:
+        return [pp for l in self._cache_layers() for pp in l.pingpongs()]
+
 
 class DecoderStack(Stream):
     """Decoder-shaped stack: conv_in (C_lat -> C) -> 2 resblocks -> nearest 2x
@@ -181,14 +216,27 @@ class DecoderStack(Stream):
         for rb in self.rbs[2:]:
             rb.start(n, 2 * h, 2 * w)
 
+    def _buf(self, name: str, shape, like: torch.Tensor) -> torch.Tensor:
+        """Intermediate activation buffer, reused from chunk to chunk (so a
+        recorded graph names the same memory every time)."""
+        bufs = self.__dict__.setdefault("_bufs", {})
+        b = bufs.get(name)
+        if b is None or tuple(b.shape) != tuple(shape) or b.dtype != like.dtype:
+            b = L.empty_cl(shape, like.dtype, like.device)
+            bufs[name] = b
+        return b
+
     def chunk(self, x: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
-        h = self.conv_in(x)
-        h = self.rbs[0](h)
-        h = self.rbs[1](h)
-        h = L.wvc_upsample_nearest2x(h)
-        h = self.conv_up(h)
-        h = self.rbs[2](h)
-        return self.rbs[3](h, y=out)
+        n, _, t, h, w = x.shape
+        c = self.conv_in.weight.shape[0]
+        lo, hi = (n, c, t, h, w), (n, c, t, 2 * h, 2 * w)
+        a = self.conv_in(x, y=self._buf("in", lo, x))
+        a = self.rbs[0](a, y=self._buf("rb0", lo, x))
+        a = self.rbs[1](a, y=self._buf("rb1", lo, x))
+        a = L.wvc_upsample_nearest2x(a, y=self._buf("up", hi, x))
+        a = self.conv_up(a, y=self._buf("conv_up", hi, x))
+        a = self.rbs[2](a, y=self._buf("rb2", hi, x))
+        return self.rbs[3](a, y=out)
 
     def run(self, latent: torch.Tensor, chunk_frames: int = 1) -> torch.Tensor:
         n, c, t, h, w = latent.shape
@@ -218,3 +266,71 @@ def run_chunked(layer, x: torch.Tensor, sizes: Sequence[int]) -> torch.Tensor:
         outs.append(layer(chunk))
         t0 += s
     return torch.cat(outs, dim=2).contiguous(memory_format=torch.channels_last_3d)
+
+
+def capture(fn: Callable[[], object], device=None) -> L.Graph:
+    """Record the library calls that ``fn()`` enqueues into a HIP graph.
+
+    ``fn`` runs once on a side stream under capture: its calls are recorded,
+    not run, so it must only make library calls on buffers that already exist
+    (run it eagerly once first, so that every workspace and intermediate is
+    allocated).  Python state that ``fn`` changes (e.g. the cache parity) is
+    changed as if it had run."""
+    dev = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
+    side = torch.cuda.Stream(dev)
+    side.wait_stream(torch.cuda.current_stream(dev))
+    with torch.cuda.stream(side):
+        L.wvc_graph_capture_begin(side)
+        try:
+            fn()
+        except BaseException:
+            try:
+                L.wvc_graph_capture_end(side).close()
+            except Exception:
+                pass
+            raise
+        graph = L.wvc_graph_capture_end(side)
+    torch.cuda.current_stream(dev).wait_stream(side)
+    return graph
+
+
+class FrameGraph:
+    """One chunk of a streamed stack (``DecoderStack``, ``ResBlock`` or
+    ``CausalConv3d``) replayed as a HIP graph.
+
+    Chunk i reads the caches chunk i-1 wrote, so even and odd chunks name the
+    two buffers of every ping-pong the other way round: two graphs are
+    recorded, one per parity.  ``x`` and ``y`` are the static input and output
+    chunk buffers they read and write: fill ``x``, call, read ``y`` before the
+    next call.  ``reset()`` starts a new sequence."""
+
+    def __init__(self, stack, x_shape: Sequence[int], dtype=torch.bfloat16, device="cuda"):
+        n, c, t, h, w = x_shape
+        self.stack = stack
+        self._run = stack.chunk if hasattr(stack, "chunk") else \
+            (lambda x, out=None: stack(x, y=out))
+        self.x = L.empty_cl(tuple(x_shape), dtype, device)
+        L.wvc_cache_reset(self.x)
+        stack.start(n, h, w)
+        y = self._run(self.x)          # eager pass: sizes every workspace and buffer
+        self.y = L.empty_cl(tuple(y.shape), dtype, device)
+        self._pps = stack.pingpongs()
+        stack.reset()
+        self.graphs = [capture(lambda: self._run(self.x, out=self.y), device) for _ in range(2)]
+        # each recording flipped every cache once, so the parity is back to 0
+        self.parity = 0
+
+    def reset(self):
+        self.stack.reset()
+        self.parity = 0
+
+    def __call__(self) -> torch.Tensor:
+        self.graphs[self.parity].launch()
+        for pp in self._pps:        # the stack's ping-pong state follows the replay
+            pp.flip()
+        self.parity ^= 1
+        return self.y
+
+    def close(self):
+        for g in self.graphs:
+            g.close()
