@@ -52,7 +52,15 @@ def parse():
                              "decoder_stack_48_30x52"])
     ap.add_argument("--kernel-reps", type=int, default=50,
                     help="launches of the dominant kernel timed for the roofline")
+    ap.add_argument("--warmup-seconds", type=float, default=0.5,
+                    help="keep warming up (untimed) until this much wall time has passed "
+                         "after the --warmup steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--pipeline", choices=("auto", "on", "off"), default="auto",
+                    help="streamed workloads: split each frame's layers over two streams so that "
+                         "the second part of frame i runs next to the first part of frame i+1 "
+                         "(auto: on for the decoder stack, where it is faster; off for the single "
+                         "residual block, where it is not)")
     ap.add_argument("--graph", choices=("on", "off"), default="off",
                     help="replay the whole step as one recorded HIP graph (after the eager "
                          "warm-up) instead of enqueuing its launches one by one")
@@ -62,6 +70,11 @@ def parse():
                     help="only run 5 plain device copies of MIB MiB (bf16) and exit: the known-size "
                          "kernel that scales rocprofv3's FETCH_SIZE / WRITE_SIZE counters")
     return ap.parse_args()
+
+
+PIPELINE = False  # set from --pipeline in main()
+PIPELINED = ("resblock_384_60x104", "decoder_stack_48_30x52")  # workloads that honour it
+PIPELINE_AUTO = ("decoder_stack_48_30x52",)  # where it measured faster
 
 
 def cl(t):
@@ -86,12 +99,22 @@ def conv_workspace(x, w, padding=(1, 1), packed=False):
     return torch.empty(need, dtype=torch.uint8, device="cuda") if need else None
 
 
-def time_region(fn, steps, warmup):
-    """Warm up, then time exactly ``steps`` calls between two events on the
-    current stream, synchronised on both sides.  Returns (ms per call, wall s)."""
+def time_region(fn, steps, warmup, warmup_s=0.0):
+    """Warm up (``warmup`` calls, and more until ``warmup_s`` seconds have
+    passed: the GPU clock takes ~0.1 s of load to reach its steady state), then
+    time exactly ``steps`` calls between two events on the current stream,
+    synchronised on both sides.  Returns (ms per call, wall s)."""
     import torch
     for _ in range(warmup):
         fn()
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    k = 0
+    while time.perf_counter() - w0 < warmup_s:
+        fn()
+        k += 1
+        if k % 8 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     w0 = time.perf_counter()
@@ -122,11 +145,15 @@ def wl_resblock():
     rb = stream.ResBlock(p)
     rb.start(n, h, w)
 
+    pipe = stream.Pipeline(rb) if PIPELINE else None
+
     def step():
-        rb.c1.reset()
-        rb.c2.reset()
-        for i in range(t):
-            rb(frames[i], y=outs[i])
+        rb.reset()
+        if pipe is not None:
+            pipe.run(frames, outs)
+        else:
+            for i in range(t):
+                rb(frames[i], y=outs[i])
 
     conv_flops = 2 * t * acc.conv_flops(n, 1, h, w, c, c)
     # dominant kernel alone: the 3x3x3 conv of one 60x104 frame (no cache update)
@@ -243,10 +270,15 @@ def wl_decoder():
     out = L.empty_cl((n, width, t, 2 * h, 2 * w))
     outs = [out[:, :, i:i + 1] for i in range(t)]
 
+    pipe = stream.Pipeline(stack) if PIPELINE else None
+
     def step():
-        stack.start(n, h, w)
-        for i in range(t):
-            stack.chunk(frames[i], out=outs[i])
+        stack.reset()
+        if pipe is not None:
+            pipe.run(frames, outs)
+        else:
+            for i in range(t):
+                stack.chunk(frames[i], out=outs[i])
 
     per_frame = (acc.conv_flops(n, 1, h, w, cl_, width) + 4 * acc.conv_flops(n, 1, h, w, width, width)
                  + 5 * acc.conv_flops(n, 1, 2 * h, 2 * w, width, width))
@@ -369,6 +401,12 @@ def main():
         print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported "
               "(the path has no multi-GPU sharding in this build)", file=sys.stderr)
         sys.exit(2)
+    if args.pipeline == "auto":
+        args.pipeline = "on" if args.workload in PIPELINE_AUTO and args.graph == "off" else "off"
+    if args.pipeline == "on" and args.graph == "on":
+        print("--pipeline on runs two streams, which are not recorded into a graph; "
+              "use one of the two", file=sys.stderr)
+        sys.exit(2)
     import torch
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
@@ -377,6 +415,8 @@ def main():
     L.load()
     torch.cuda.set_device(0)
 
+    global PIPELINE
+    PIPELINE = args.pipeline == "on"
     step, info = WORKLOADS[args.workload]()
     timed = step
     if args.graph == "on":
@@ -389,11 +429,11 @@ def main():
         torch.cuda.synchronize()
         graph = stream.capture(step)
         timed = graph.launch
-    ms_step, wall = time_region(timed, args.steps, args.warmup)
+    ms_step, wall = time_region(timed, args.steps, args.warmup, args.warmup_seconds)
     value = info["conv_flops"] / (ms_step * 1e-3) / 1e12
 
     # dominant kernel, timed alone with events on the stream it is launched on
-    k_ms, _ = time_region(info["kernel"], args.kernel_reps, 3)
+    k_ms, _ = time_region(info["kernel"], args.kernel_reps, 3, min(args.warmup_seconds, 0.2))
     achieved = info["kernel_units"] / (k_ms * 1e-3) / 1e12
     traffic = measured_traffic(args.traffic_json, args.workload, info["kernel_name"])
     roofline = {"bound": info["kernel_bound"], "achieved": round(achieved, 2),
@@ -405,10 +445,12 @@ def main():
 
     line = {
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "steps": args.steps, "warmup": args.warmup, "warmup_s": args.warmup_seconds,
+        "ms_per_step": round(ms_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic (seeded Philox normals, random-init weights)",
-        "config": dict(info["config"], hip_graph=args.graph == "on"),
+        "config": dict(info["config"], hip_graph=args.graph == "on",
+                       two_stream_pipeline=PIPELINE and args.workload in PIPELINED),
         "pct_mfma_peak": round(100 * value / MFMA_BF16_PEAK_TFLOPS, 2),
         "ms_per_latent_frame": round(ms_step / info["latent_frames"], 4),
         "conv_flops_per_step": info["conv_flops"],
@@ -416,7 +458,7 @@ def main():
         "roofline": roofline,
     }
     if "norm_kernel" in info:
-        n_ms, _ = time_region(info["norm_kernel"], 20, 3)
+        n_ms, _ = time_region(info["norm_kernel"], 20, 3, min(args.warmup_seconds, 0.2))
         gbs = info["norm_bytes"] / (n_ms * 1e-3) / 1e9
         line["roofline_norm"] = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
                                  "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),

@@ -211,6 +211,28 @@ int wvc_resblock_fwd(const wvc_resblock_desc *d, const void *x, void *y,
 size_t wvc_resblock_workspace_bytes(const wvc_resblock_desc *d);
 
 /*
+ * The same block in two halves ([P1] 10.4 read as front = the path up to
+ * conv2's input, back = conv2 and the residual):
+ *   wvc_resblock_front:  h2 = SiLU(norm2(conv1(SiLU(norm1(x)) | cache1)))
+ *   wvc_resblock_back:   y  = conv2(h2 | cache2) + shortcut(x)
+ * wvc_resblock_fwd is front then back.  The back half of chunk i and the
+ * front half of chunk i+1 touch disjoint state (cache2 vs cache1), so a
+ * caller may run them concurrently on two streams; each half then needs its
+ * own workspace (wvc_resblock_workspace_bytes(d) bytes each, contents on
+ * entry do not matter) and each chunk its own h2 until its back half is done.
+ * h2 is [N, C_out, t, H, W] in the call's dtype, caller-owned, and may not
+ * overlap any other buffer of the call.  Arguments and errors otherwise as
+ * for wvc_resblock_fwd; the front half needs gamma1, w1, gamma2, the back
+ * half w2 (and w_short when C_in != C_out).
+ */
+int wvc_resblock_front(const wvc_resblock_desc *d, const void *x, void *h2,
+                       const wvc_resblock_params *p, const void *cache1_in, void *cache1_out,
+                       void *workspace, size_t workspace_bytes, void *stream);
+int wvc_resblock_back(const wvc_resblock_desc *d, const void *h2, const void *x, void *y,
+                      const wvc_resblock_params *p, const void *cache2_in, void *cache2_out,
+                      void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * Zero-fills `bytes` bytes of a cache (a fill kernel, never a memset node, so
  * it can be recorded in a graph).  A zeroed cache is exactly the zero causal
  * padding before frame 0, so this restarts a stream.  bytes % 4 == 0.

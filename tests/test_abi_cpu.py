@@ -183,6 +183,38 @@ def test_resblock_validation(lib):
     assert rcall(d, params=q) == L.WVC_ERR_ARG
 
 
+def test_resblock_halves_validation(lib):
+    d = rb_desc()
+    need = L.wvc_resblock_workspace_bytes(d)
+    p = L.ResblockParams()
+    p.gamma1, p.w1, p.gamma2, p.w2 = 0x50000000, 0x51000000, 0x52000000, 0x53000000
+    H2 = 0x60000000
+
+    def front(d=d, x=X, h2=H2, params=p, ws=WS, wsb=need, c1i=None, c1o=None):
+        return lib.wvc_resblock_front(ctypes.byref(d), x, h2, ctypes.byref(params) if params else None,
+                                      c1i, c1o, ws, wsb, None)
+
+    def back(d=d, h2=H2, x=X, y=Y, params=p, ws=WS, wsb=need, c2i=None, c2o=None):
+        return lib.wvc_resblock_back(ctypes.byref(d), h2, x, y, ctypes.byref(params) if params else None,
+                                     c2i, c2o, ws, wsb, None)
+
+    assert front(params=None) == L.WVC_ERR_ARG and back(params=None) == L.WVC_ERR_ARG
+    assert front(wsb=need - 1) == L.WVC_ERR_WORKSPACE and back(wsb=need - 1) == L.WVC_ERR_WORKSPACE
+    assert front(h2=None) == L.WVC_ERR_ARG and back(h2=None) == L.WVC_ERR_ARG
+    assert front(h2=X) == L.WVC_ERR_ALIAS           # h2 is written: may not overlap x
+    assert back(y=H2) == L.WVC_ERR_ALIAS            # y may not overlap h2
+    assert back(ws=H2) == L.WVC_ERR_ALIAS
+    assert front(c1i=CIN, c1o=CIN) == L.WVC_ERR_ALIAS
+    assert back(c2i=CIN, c2o=CIN) == L.WVC_ERR_ALIAS
+    assert back(d=rb_desc(c_out=32)) == L.WVC_ERR_ARG   # the shortcut conv is the back half's
+    q = L.ResblockParams()
+    q.w2 = 0x53000000
+    assert front(params=q) == L.WVC_ERR_ARG         # the front half needs gamma1, w1, gamma2
+    r = L.ResblockParams()
+    r.gamma1, r.w1, r.gamma2 = 0x50000000, 0x51000000, 0x52000000
+    assert back(params=r) == L.WVC_ERR_ARG          # the back half needs w2
+
+
 def test_norm_and_upsample_validation(lib):
     assert lib.wvc_rmsnorm_silu(X, B, None, Y, 1, 0, 1, 4, 4, L.WVC_BF16, 1e-12, 1, None) == L.WVC_ERR_ARG
     assert lib.wvc_rmsnorm_silu(X, B, None, Y, 1, 8, 1, 4, 4, L.WVC_BF16, 0.0, 1, None) == L.WVC_ERR_ARG

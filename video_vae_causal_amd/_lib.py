@@ -31,7 +31,8 @@ ERROR_NAMES = {0: "WVC_OK", 1: "WVC_ERR_ARG", 2: "WVC_ERR_UNSUPPORTED", 3: "WVC_
 EXPORTED = (
     "wvc_causal_conv3d_fwd", "wvc_causal_conv3d_workspace_bytes", "wvc_conv3d_cache_frames",
     "wvc_conv3d_packed_weight_bytes", "wvc_conv3d_pack_weights",
-    "wvc_rmsnorm_silu", "wvc_resblock_fwd", "wvc_resblock_workspace_bytes", "wvc_cache_reset",
+    "wvc_rmsnorm_silu", "wvc_resblock_fwd", "wvc_resblock_workspace_bytes",
+    "wvc_resblock_front", "wvc_resblock_back", "wvc_cache_reset",
     "wvc_upsample_nearest2x", "wvc_set_strict", "wvc_get_strict", "wvc_get_counters",
     "wvc_reset_counters", "wvc_last_error", "wvc_version", "wvc_graph_capture_begin",
     "wvc_graph_capture_end", "wvc_graph_launch", "wvc_graph_destroy",
@@ -94,6 +95,12 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.wvc_resblock_fwd.argtypes = [ctypes.POINTER(ResblockDesc), vp, vp,
                                      ctypes.POINTER(ResblockParams), vp, vp, vp, vp, vp, sz, vp]
     lib.wvc_resblock_fwd.restype = i
+    lib.wvc_resblock_front.argtypes = [ctypes.POINTER(ResblockDesc), vp, vp,
+                                       ctypes.POINTER(ResblockParams), vp, vp, vp, sz, vp]
+    lib.wvc_resblock_front.restype = i
+    lib.wvc_resblock_back.argtypes = [ctypes.POINTER(ResblockDesc), vp, vp, vp,
+                                      ctypes.POINTER(ResblockParams), vp, vp, vp, sz, vp]
+    lib.wvc_resblock_back.restype = i
     lib.wvc_resblock_workspace_bytes.argtypes = [ctypes.POINTER(ResblockDesc)]
     lib.wvc_resblock_workspace_bytes.restype = sz
     lib.wvc_cache_reset.argtypes = [vp, sz, vp]
@@ -338,6 +345,64 @@ def wvc_resblock_fwd(x: torch.Tensor, params: dict, cache1_in=None, cache1_out=N
     _check(lib.wvc_resblock_fwd(ctypes.byref(d), _ptr(x), _ptr(y), ctypes.byref(p),
                                 _ptr(cache1_in), _ptr(cache1_out), _ptr(cache2_in),
                                 _ptr(cache2_out), _ptr(workspace), ws_bytes, _stream(x)))
+    return y
+
+
+def _block_call(x, params, packed, eps, workspace, outs):
+    """Shared marshalling of the block halves: descriptor, params struct,
+    workspace (allocated when not given) and its size."""
+    _need_cl(x, "x")
+    c_out = params["w1"].shape[0]
+    for name in ("w1", "w2", "w_short"):
+        _need_cl(params.get(name), name)
+    if packed is not None:
+        params = dict(params, **packed)
+    for name, t in outs:
+        _need_cl(t, name)
+    d = resblock_desc(tuple(x.shape), c_out, _dtype_code(x.dtype), eps,
+                      weights_packed=packed is not None)
+    need = wvc_resblock_workspace_bytes(d)
+    if workspace is None and need:  # contents on entry do not matter
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    p = ResblockParams()
+    for f, _ in ResblockParams._fields_:
+        t = params.get(f)
+        setattr(p, f, None if t is None else t.data_ptr())
+    return d, p, c_out, workspace, ws_bytes
+
+
+def wvc_resblock_front(x: torch.Tensor, params: dict, cache1_in=None, cache1_out=None,
+                       h2: Optional[torch.Tensor] = None, eps: float = 1e-12,
+                       workspace: Optional[torch.Tensor] = None,
+                       packed: Optional[dict] = None) -> torch.Tensor:
+    """First half of the block, h2 = SiLU(norm2(conv1(SiLU(norm1(x)))))
+    (see wvc_resblock_front in include/wvc.h)."""
+    d, p, c_out, workspace, ws_bytes = _block_call(
+        x, params, packed, eps, workspace,
+        (("cache1_in", cache1_in), ("cache1_out", cache1_out), ("h2", h2)))
+    if h2 is None:
+        h2 = empty_cl((x.shape[0], c_out) + tuple(x.shape[2:]), x.dtype, x.device)
+    _check(load().wvc_resblock_front(ctypes.byref(d), _ptr(x), _ptr(h2), ctypes.byref(p),
+                                     _ptr(cache1_in), _ptr(cache1_out), _ptr(workspace),
+                                     ws_bytes, _stream(x)))
+    return h2
+
+
+def wvc_resblock_back(h2: torch.Tensor, x: torch.Tensor, params: dict, cache2_in=None,
+                      cache2_out=None, y: Optional[torch.Tensor] = None, eps: float = 1e-12,
+                      workspace: Optional[torch.Tensor] = None,
+                      packed: Optional[dict] = None) -> torch.Tensor:
+    """Second half of the block, y = conv2(h2) + shortcut(x) (see
+    wvc_resblock_back in include/wvc.h)."""
+    d, p, c_out, workspace, ws_bytes = _block_call(
+        x, params, packed, eps, workspace,
+        (("h2", h2), ("cache2_in", cache2_in), ("cache2_out", cache2_out), ("y", y)))
+    if y is None:
+        y = empty_cl((x.shape[0], c_out) + tuple(x.shape[2:]), x.dtype, x.device)
+    _check(load().wvc_resblock_back(ctypes.byref(d), _ptr(h2), _ptr(x), _ptr(y), ctypes.byref(p),
+                                    _ptr(cache2_in), _ptr(cache2_out), _ptr(workspace), ws_bytes,
+                                    _stream(x)))
     return y
 
 

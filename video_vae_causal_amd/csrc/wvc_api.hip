@@ -389,63 +389,55 @@ size_t wvc_resblock_workspace_bytes(const wvc_resblock_desc *d) {
     return L.total;
 }
 
-int wvc_resblock_fwd(const wvc_resblock_desc *d, const void *x, void *y,
-                     const wvc_resblock_params *p, const void *cache1_in, void *cache1_out,
-                     const void *cache2_in, void *cache2_out, void *workspace,
-                     size_t workspace_bytes, void *stream) {
-    BlockLayout L;
-    int rc = plan_block(d, &L);
+namespace {
+
+// Checks shared by the block entry points: the descriptor, the parameters the
+// given half uses, the workspace size; fills the two conv descriptors.
+int check_block(const wvc_resblock_desc *d, const wvc_resblock_params *p, bool front, bool back,
+                size_t workspace_bytes, const void *workspace, BlockLayout *L,
+                wvc_conv3d_desc *c1, wvc_conv3d_desc *c2) {
+    int rc = plan_block(d, L);
     if (rc) return rc;
     if (!p) return fail(WVC_ERR_ARG, "params is NULL");
-    if (!p->gamma1 || !p->w1 || !p->gamma2 || !p->w2)
-        return fail(WVC_ERR_ARG, "gamma1, w1, gamma2 and w2 are required");
+    if (front && (!p->gamma1 || !p->w1 || !p->gamma2))
+        return fail(WVC_ERR_ARG, "gamma1, w1 and gamma2 are required");
+    if (back && !p->w2) return fail(WVC_ERR_ARG, "w2 is required");
     const bool proj = d->c_in != d->c_out;
-    if (proj && !p->w_short) return fail(WVC_ERR_ARG, "C_in != C_out needs w_short");
-    if (!proj && p->w_short) return fail(WVC_ERR_ARG, "w_short given but C_in == C_out");
-    if (d->t > 0 && (!x || !y)) return fail(WVC_ERR_ARG, "x or y is NULL");
-    if (workspace_bytes < L.total || (!workspace && L.total))
+    if (back && proj && !p->w_short) return fail(WVC_ERR_ARG, "C_in != C_out needs w_short");
+    if (back && !proj && p->w_short) return fail(WVC_ERR_ARG, "w_short given but C_in == C_out");
+    if (workspace_bytes < L->total || (!workspace && L->total))
         return fail(WVC_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes,
-                    L.total);
-    const int e = elem_bytes(d->dtype);
-    const size_t pos = (size_t)d->n * d->t * d->h * d->w;
-    const size_t plane_in = (size_t)d->n * 2 * d->h * d->w;
-    const Buf bufs[] = {
-        {x, pos * d->c_in * e, false, "x"},
-        {y, pos * d->c_out * e, true, "y"},
-        {cache1_in, plane_in * d->c_in * e, false, "cache1_in"},
-        {cache1_out, plane_in * d->c_in * e, true, "cache1_out"},
-        {cache2_in, plane_in * d->c_out * e, false, "cache2_in"},
-        {cache2_out, plane_in * d->c_out * e, true, "cache2_out"},
-        {workspace, workspace_bytes, true, "workspace"},
-    };
-    rc = check_aliasing(bufs, 7);
-    if (rc) return rc;
-
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    char *ws = static_cast<char *>(workspace);
-    void *h1 = ws + L.h1, *a1 = ws + L.a1, *h2 = ws + L.h2, *sc = ws + L.sc;
-
-    wvc_conv3d_desc c1{};
-    c1.n = d->n; c1.c_in = d->c_in; c1.c_out = d->c_out; c1.t = d->t; c1.h = d->h; c1.w = d->w;
-    c1.kt = c1.kh = c1.kw = 3;
-    c1.stride_t = c1.stride_h = c1.stride_w = 1;
-    c1.pad_h = c1.pad_w = 1;
-    c1.dil_t = c1.dil_h = c1.dil_w = 1;
-    c1.groups = 1;
-    c1.dtype = d->dtype;
-    c1.weight_layout = d->weights_packed ? WVC_WEIGHT_PACKED : WVC_WEIGHT_STANDARD;
-    wvc_conv3d_desc c2 = c1;
-    c2.c_in = d->c_out;
-
-    // Validate both convs (and strict mode) before enqueueing anything.
+                    L->total);
+    *c1 = wvc_conv3d_desc{};
+    c1->n = d->n; c1->c_in = d->c_in; c1->c_out = d->c_out; c1->t = d->t; c1->h = d->h; c1->w = d->w;
+    c1->kt = c1->kh = c1->kw = 3;
+    c1->stride_t = c1->stride_h = c1->stride_w = 1;
+    c1->pad_h = c1->pad_w = 1;
+    c1->dil_t = c1->dil_h = c1->dil_w = 1;
+    c1->groups = 1;
+    c1->dtype = d->dtype;
+    c1->weight_layout = d->weights_packed ? WVC_WEIGHT_PACKED : WVC_WEIGHT_STANDARD;
+    *c2 = *c1;
+    c2->c_in = d->c_out;
+    // Validate the convs (and strict mode) before enqueueing anything.
     ConvPlan pl1, pl2;
-    if ((rc = plan_conv(&c1, &pl1)) || (rc = plan_conv(&c2, &pl2))) return rc;
-    if (strict_on() &&
-        (pl1.route == wvc::ConvRoute::Generic || pl2.route == wvc::ConvRoute::Generic)) {
+    if (front && (rc = plan_conv(c1, &pl1))) return rc;
+    if (back && (rc = plan_conv(c2, &pl2))) return rc;
+    if (strict_on() && ((front && pl1.route == wvc::ConvRoute::Generic) ||
+                        (back && pl2.route == wvc::ConvRoute::Generic))) {
         g_rejected++;
         return fail(WVC_ERR_STRICT, "strict mode: a block conv would take the generic route");
     }
+    return WVC_OK;
+}
 
+// h2 = SiLU(norm2(conv1(SiLU(norm1(x)) | cache1))).
+int block_front(const wvc_resblock_desc *d, const wvc_conv3d_desc &c1, const BlockLayout &L,
+                const void *x, void *h2, const wvc_resblock_params *p, const void *cache1_in,
+                void *cache1_out, char *ws, hipStream_t s) {
+    const size_t pos = (size_t)d->n * d->t * d->h * d->w;
+    void *h1 = ws + L.h1, *a1 = ws + L.a1;
+    int rc;
     if ((rc = norm_fwd(x, p->gamma1, p->beta1, h1, d->n, d->c_in, d->t, d->h, d->w, d->dtype,
                        d->eps, 1, s)))
         return rc;
@@ -465,21 +457,108 @@ int wvc_resblock_fwd(const wvc_resblock_desc *d, const void *x, void *y,
         const hipError_t err = wvc::launch_rmsnorm_silu_from_partials(
             parts, p->b1, p->gamma2, p->beta2, h2, (long)pos, d->c_out, d->eps, 1, s);
         if (err != hipSuccess) return hip_status(err, "norm launch");
-    } else if ((rc = norm_fwd(a1, p->gamma2, p->beta2, h2, d->n, d->c_out, d->t, d->h, d->w,
-                              d->dtype, d->eps, 1, s))) {
-        return rc;
+        return WVC_OK;
     }
+    return norm_fwd(a1, p->gamma2, p->beta2, h2, d->n, d->c_out, d->t, d->h, d->w, d->dtype, d->eps,
+                    1, s);
+}
+
+// y = conv2(h2 | cache2) + shortcut(x).
+int block_back(const wvc_resblock_desc *d, const wvc_conv3d_desc &c1, const wvc_conv3d_desc &c2,
+               const BlockLayout &L, const void *h2, const void *x, void *y,
+               const wvc_resblock_params *p, const void *cache2_in, void *cache2_out, char *ws,
+               hipStream_t s) {
+    void *cws = ws + L.conv;
     const void *shortcut = x;
-    if (proj) {
+    if (d->c_in != d->c_out) {
         wvc_conv3d_desc cs = c1;
         cs.kt = cs.kh = cs.kw = 1;
         cs.pad_h = cs.pad_w = 0;
-        if ((rc = conv_fwd(&cs, x, nullptr, nullptr, p->w_short, p->b_short, nullptr, sc, cws,
-                           L.conv_bytes, s)))
-            return rc;
+        void *sc = ws + L.sc;
+        const int rc = conv_fwd(&cs, x, nullptr, nullptr, p->w_short, p->b_short, nullptr, sc, cws,
+                                L.conv_bytes, s);
+        if (rc) return rc;
         shortcut = sc;
     }
     return conv_fwd(&c2, h2, cache2_in, cache2_out, p->w2, p->b2, shortcut, y, cws, L.conv_bytes, s);
+}
+
+}  // namespace
+
+int wvc_resblock_fwd(const wvc_resblock_desc *d, const void *x, void *y,
+                     const wvc_resblock_params *p, const void *cache1_in, void *cache1_out,
+                     const void *cache2_in, void *cache2_out, void *workspace,
+                     size_t workspace_bytes, void *stream) {
+    BlockLayout L;
+    wvc_conv3d_desc c1, c2;
+    int rc = check_block(d, p, true, true, workspace_bytes, workspace, &L, &c1, &c2);
+    if (rc) return rc;
+    if (d->t > 0 && (!x || !y)) return fail(WVC_ERR_ARG, "x or y is NULL");
+    const int e = elem_bytes(d->dtype);
+    const size_t pos = (size_t)d->n * d->t * d->h * d->w;
+    const size_t plane_in = (size_t)d->n * 2 * d->h * d->w;
+    const Buf bufs[] = {
+        {x, pos * d->c_in * e, false, "x"},
+        {y, pos * d->c_out * e, true, "y"},
+        {cache1_in, plane_in * d->c_in * e, false, "cache1_in"},
+        {cache1_out, plane_in * d->c_in * e, true, "cache1_out"},
+        {cache2_in, plane_in * d->c_out * e, false, "cache2_in"},
+        {cache2_out, plane_in * d->c_out * e, true, "cache2_out"},
+        {workspace, workspace_bytes, true, "workspace"},
+    };
+    if ((rc = check_aliasing(bufs, 7))) return rc;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    char *ws = static_cast<char *>(workspace);
+    void *h2 = ws + L.h2;
+    if ((rc = block_front(d, c1, L, x, h2, p, cache1_in, cache1_out, ws, s))) return rc;
+    return block_back(d, c1, c2, L, h2, x, y, p, cache2_in, cache2_out, ws, s);
+}
+
+int wvc_resblock_front(const wvc_resblock_desc *d, const void *x, void *h2,
+                       const wvc_resblock_params *p, const void *cache1_in, void *cache1_out,
+                       void *workspace, size_t workspace_bytes, void *stream) {
+    BlockLayout L;
+    wvc_conv3d_desc c1, c2;
+    int rc = check_block(d, p, true, false, workspace_bytes, workspace, &L, &c1, &c2);
+    if (rc) return rc;
+    if (d->t > 0 && (!x || !h2)) return fail(WVC_ERR_ARG, "x or h2 is NULL");
+    const int e = elem_bytes(d->dtype);
+    const size_t pos = (size_t)d->n * d->t * d->h * d->w;
+    const size_t plane_in = (size_t)d->n * 2 * d->h * d->w;
+    const Buf bufs[] = {
+        {x, pos * d->c_in * e, false, "x"},
+        {h2, pos * d->c_out * e, true, "h2"},
+        {cache1_in, plane_in * d->c_in * e, false, "cache1_in"},
+        {cache1_out, plane_in * d->c_in * e, true, "cache1_out"},
+        {workspace, workspace_bytes, true, "workspace"},
+    };
+    if ((rc = check_aliasing(bufs, 5))) return rc;
+    return block_front(d, c1, L, x, h2, p, cache1_in, cache1_out, static_cast<char *>(workspace),
+                       static_cast<hipStream_t>(stream));
+}
+
+int wvc_resblock_back(const wvc_resblock_desc *d, const void *h2, const void *x, void *y,
+                      const wvc_resblock_params *p, const void *cache2_in, void *cache2_out,
+                      void *workspace, size_t workspace_bytes, void *stream) {
+    BlockLayout L;
+    wvc_conv3d_desc c1, c2;
+    int rc = check_block(d, p, false, true, workspace_bytes, workspace, &L, &c1, &c2);
+    if (rc) return rc;
+    if (d->t > 0 && (!x || !h2 || !y)) return fail(WVC_ERR_ARG, "h2, x or y is NULL");
+    const int e = elem_bytes(d->dtype);
+    const size_t pos = (size_t)d->n * d->t * d->h * d->w;
+    const size_t plane_out = (size_t)d->n * 2 * d->h * d->w;
+    const Buf bufs[] = {
+        {h2, pos * d->c_out * e, false, "h2"},
+        {x, pos * d->c_in * e, false, "x"},
+        {y, pos * d->c_out * e, true, "y"},
+        {cache2_in, plane_out * d->c_out * e, false, "cache2_in"},
+        {cache2_out, plane_out * d->c_out * e, true, "cache2_out"},
+        {workspace, workspace_bytes, true, "workspace"},
+    };
+    if ((rc = check_aliasing(bufs, 6))) return rc;
+    return block_back(d, c1, c2, L, h2, x, y, p, cache2_in, cache2_out,
+                      static_cast<char *>(workspace), static_cast<hipStream_t>(stream));
 }
 
 int wvc_cache_reset(void *cache, size_t bytes, void *stream) {
@@ -531,10 +610,12 @@ int wvc_graph_capture_end(void *stream, wvc_graph **graph) {
     }
     if (!g) return fail(WVC_ERR_HIP, "end capture returned no graph");
     hipGraphExec_t exec = nullptr;
-    err = hipGraphInstantiate(&exec, g, nullptr, nullptr, 0);
+    hipGraphNode_t err_node = nullptr;
+    char log[256] = "";
+    err = hipGraphInstantiate(&exec, g, &err_node, log, sizeof(log));
     if (err != hipSuccess) {
         (void)hipGraphDestroy(g);
-        return hip_status(err, "graph instantiate");
+        return fail(WVC_ERR_HIP, "graph instantiate: %s %s", hipGetErrorString(err), log);
     }
     wvc_graph *h = new (std::nothrow) wvc_graph{g, exec};
     if (!h) {

@@ -40,6 +40,14 @@ def _try_pack(weight: torch.Tensor, padding) -> Optional[torch.Tensor]:
         return None
 
 
+def _cached_buf(bufs: Dict[str, torch.Tensor], name: str, shape, like: torch.Tensor) -> torch.Tensor:
+    b = bufs.get(name)
+    if b is None or tuple(b.shape) != tuple(shape) or b.dtype != like.dtype:
+        b = L.empty_cl(shape, like.dtype, like.device)
+        bufs[name] = b
+    return b
+
+
 class _PingPong:
     def __init__(self, shape, dtype, device):
         self.buf = [L.empty_cl(shape, dtype, device), L.empty_cl(shape, dtype, device)]
@@ -115,6 +123,9 @@ class CausalConv3d:
     def pingpongs(self) -> List[_PingPong]:
         return [self.cache] if self.cache is not None else []
 
+    def stages(self, x: torch.Tensor, y: torch.Tensor, buf) -> List[Callable[[], object]]:
+        return [lambda: self(x, y=y)]
+
 
 class ResBlock:
     """Wan residual block with the two caches of its 3x3x3 convs."""
@@ -168,6 +179,39 @@ class ResBlock:
     def caches(self) -> List[torch.Tensor]:
         return [self.c1.cin, self.c2.cin] if self.c1 is not None else []
 
+    def _half_ws(self, name: str, x: torch.Tensor) -> torch.Tensor:
+        d = L.resblock_desc(tuple(x.shape), self.p["w1"].shape[0], L._dtype_code(x.dtype), self.eps,
+                            weights_packed=self.packed is not None)
+        need = L.wvc_resblock_workspace_bytes(d)
+        ws = self.__dict__.get(name)
+        if ws is None or ws.numel() < need:
+            ws = torch.empty(need, dtype=torch.uint8, device=x.device)
+            setattr(self, name, ws)
+        return ws
+
+    def front(self, x: torch.Tensor, h2: torch.Tensor) -> torch.Tensor:
+        """First half (norm1, conv1, norm2) into h2; advances cache1."""
+        if self.c1 is None:
+            self.start(x.shape[0], x.shape[3], x.shape[4])
+        L.wvc_resblock_front(x, self.p, self.c1.cin, self.c1.cout, h2=h2, eps=self.eps,
+                             workspace=self._half_ws("ws_front", x), packed=self.packed)
+        self.c1.flip()
+        return h2
+
+    def back(self, h2: torch.Tensor, x: torch.Tensor, y: torch.Tensor) -> torch.Tensor:
+        """Second half (conv2 + shortcut) into y; advances cache2."""
+        L.wvc_resblock_back(h2, x, self.p, self.c2.cin, self.c2.cout, y=y, eps=self.eps,
+                            workspace=self._half_ws("ws_back", x), packed=self.packed)
+        self.c2.flip()
+        return y
+
+    def stages(self, x: torch.Tensor, y: torch.Tensor, buf) -> List[Callable[[], object]]:
+        """The chunk as two stages (front, back); ``buf(name, shape, like)``
+        supplies the intermediate h2."""
+        shape = (x.shape[0], self.p["w1"].shape[0]) + tuple(x.shape[2:])
+        h2 = buf("h2", shape, x)
+        return [lambda: self.front(x, h2), lambda: self.back(h2, x, y)]
+
 
 class Stream:
     """Runs a sequence of layers over a latent sequence chunk by chunk."""
@@ -202,6 +246,12 @@ class DecoderStack(Stream):
     upsample -> conv_up (C -> C) -> 2 resblocks, streamed chunk by chunk with one
     2-frame cache per 3x3x3 conv (10 caches for 4 resblocks)."""
 
+    # Pipeline cut: conv_in, both low-resolution blocks and the upsample on
+    # one stream; conv_up and the two full-resolution blocks on the other.
+    # The low-resolution convs fill fewer workgroups than there are CUs, and
+    # the other stream's convs use the rest.
+    PIPELINE_SPLIT = 6
+
     def __init__(self, p: Dict, eps: float = 1e-12):
         self.conv_in = CausalConv3d(p["w_in"], p.get("b_in"))
         self.rbs = [ResBlock(p[f"rb{k}"], eps) for k in range(4)]
@@ -219,24 +269,36 @@ class DecoderStack(Stream):
     def _buf(self, name: str, shape, like: torch.Tensor) -> torch.Tensor:
         """Intermediate activation buffer, reused from chunk to chunk (so a
         recorded graph names the same memory every time)."""
-        bufs = self.__dict__.setdefault("_bufs", {})
-        b = bufs.get(name)
-        if b is None or tuple(b.shape) != tuple(shape) or b.dtype != like.dtype:
-            b = L.empty_cl(shape, like.dtype, like.device)
-            bufs[name] = b
-        return b
+        return _cached_buf(self.__dict__.setdefault("_bufs", {}), name, shape, like)
 
-    def chunk(self, x: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    def stages(self, x: torch.Tensor, out: torch.Tensor, buf) -> List[Callable[[], object]]:
+        """The chunk as a list of stages (each a few library calls); the
+        intermediates come from ``buf(name, shape, like)``."""
         n, _, t, h, w = x.shape
         c = self.conv_in.weight.shape[0]
         lo, hi = (n, c, t, h, w), (n, c, t, 2 * h, 2 * w)
-        a = self.conv_in(x, y=self._buf("in", lo, x))
-        a = self.rbs[0](a, y=self._buf("rb0", lo, x))
-        a = self.rbs[1](a, y=self._buf("rb1", lo, x))
-        a = L.wvc_upsample_nearest2x(a, y=self._buf("up", hi, x))
-        a = self.conv_up(a, y=self._buf("conv_up", hi, x))
-        a = self.rbs[2](a, y=self._buf("rb2", hi, x))
-        return self.rbs[3](a, y=out)
+        a_in, a0, a1 = buf("in", lo, x), buf("rb0", lo, x), buf("rb1", lo, x)
+        up, a_up, a2 = buf("up", hi, x), buf("conv_up", hi, x), buf("rb2", hi, x)
+
+        def sub(k):
+            return lambda name, shape, like: buf(f"rb{k}.{name}", shape, like)
+
+        st = self.conv_in.stages(x, a_in, buf)
+        st += self.rbs[0].stages(a_in, a0, sub(0))
+        st += self.rbs[1].stages(a0, a1, sub(1))
+        st.append(lambda: L.wvc_upsample_nearest2x(a1, y=up))
+        st += self.conv_up.stages(up, a_up, buf)
+        st += self.rbs[2].stages(a_up, a2, sub(2))
+        st += self.rbs[3].stages(a2, out, sub(3))
+        return st
+
+    def chunk(self, x: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+        if out is None:
+            n, _, t, h, w = x.shape
+            out = L.empty_cl((n, self.conv_up.weight.shape[0], t, 2 * h, 2 * w), x.dtype, x.device)
+        for stage in self.stages(x, out, self._buf):
+            stage()
+        return out
 
     def run(self, latent: torch.Tensor, chunk_frames: int = 1) -> torch.Tensor:
         n, c, t, h, w = latent.shape
@@ -334,3 +396,81 @@ class FrameGraph:
     def close(self):
         for g in self.graphs:
             g.close()
+
+
+
+class Pipeline:
+    """Streams a stack over a sequence of chunks on two HIP streams.
+
+    A chunk is a list of stages (``stack.stages``).  Stages [0, split) of every
+    chunk run in order on stream A, stages [split, n) on stream B; B starts a
+    chunk once A has finished that chunk's first part (one event per chunk).
+    A stage touches the caches and workspace of its own layer only, and a
+    layer's stages all sit on one side of the split (a residual block may be
+    cut between its halves: they use different caches and workspaces), so
+    each stream runs its layers in chunk order exactly as the sequential loop
+    does, and the second part of chunk i runs next to the first part of chunk
+    i+1 (for a residual block: conv2 of frame i next to conv1 of frame i+1).
+    The intermediates live in ``slots`` buffer sets used round robin; A waits
+    before reusing a set until B is done with the chunk that used it last.
+    Every call is the one ``stack.chunk`` makes, so the outputs are bitwise
+    equal to the sequential loop.
+    """
+
+    def __init__(self, stack, split: Optional[int] = None, slots: int = 3, device=None):
+        self.stack = stack
+        self.split = split if split is not None else getattr(stack, "PIPELINE_SPLIT", 1)
+        self.slots = slots
+        dev = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
+        self.device = dev
+        self.streams = [torch.cuda.Stream(dev), torch.cuda.Stream(dev)]
+        self._bufs = [{} for _ in range(slots)]
+        self._ev_a = [torch.cuda.Event() for _ in range(slots)]
+        self._ev_b = [torch.cuda.Event() for _ in range(slots)]
+
+    def _buf(self, slot: int):
+        bufs = self._bufs[slot]
+
+        def get(name, shape, like):
+            b = bufs.get(name)
+            if b is None or tuple(b.shape) != tuple(shape) or b.dtype != like.dtype:
+                b = _cached_buf(bufs, name, shape, like)
+                for s in self.streams:
+                    b.record_stream(s)
+            return b
+        return get
+
+    def run(self, chunks: Sequence[torch.Tensor], outs: Sequence[torch.Tensor]):
+        """Run every chunk in order (chunks[i] -> outs[i]) from the stack's
+        current cache state.  The work goes to the two streams; the current
+        stream waits for all of it before this returns."""
+        if torch.cuda.is_current_stream_capturing():
+            # Recording a two-stream fork/join into a graph crashed the HIP
+            # runtime inside end-capture; graphs record single-stream work.
+            raise RuntimeError("Pipeline.run cannot be recorded into a graph; record the "
+                               "sequential chunk loop (or FrameGraph) instead")
+        main = torch.cuda.current_stream(self.device)
+        sa, sb = self.streams
+        sa.wait_stream(main)
+        sb.wait_stream(main)
+        for i, (x, y) in enumerate(zip(chunks, outs)):
+            slot = i % self.slots
+            stages = self.stack.stages(x, y, self._buf(slot))
+            if not 0 < self.split < len(stages):
+                raise ValueError(f"split {self.split} must cut the {len(stages)} stages in two")
+            with torch.cuda.stream(sa):
+                if i >= self.slots:
+                    sa.wait_event(self._ev_b[slot])   # B is done with this buffer set
+                for stage in stages[:self.split]:
+                    stage()
+                self._ev_a[slot].record(sa)
+            with torch.cuda.stream(sb):
+                sb.wait_event(self._ev_a[slot])
+                for stage in stages[self.split:]:
+                    stage()
+                self._ev_b[slot].record(sb)
+            x.record_stream(sa)
+            x.record_stream(sb)
+            y.record_stream(sb)
+        main.wait_stream(sa)
+        main.wait_stream(sb)
