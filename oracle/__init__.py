@@ -71,6 +71,13 @@ def _load():
     lib.oracle_round_bf16.argtypes = [dp, ctypes.c_long, dp]
     lib.oracle_conv_out_size.restype = ctypes.c_int
     lib.oracle_conv_out_size.argtypes = [i, i, i, i, i]
+    lib.oracle_strided_out_frames.restype = ctypes.c_int
+    lib.oracle_strided_out_frames.argtypes = [i, i, i]
+    lib.oracle_strided_out_size.restype = ctypes.c_int
+    lib.oracle_strided_out_size.argtypes = [i, i, i, i, i, i]
+    lib.oracle_causal_conv3d_strided.restype = ctypes.c_int
+    lib.oracle_causal_conv3d_strided.argtypes = [dp, i, i, i, i, i, dp, i, dp, i, i, i, i, dp,
+                                                 i, i, i, i, i, i, i, i, i, i, i, dp]
     _lib = lib
     return lib
 
@@ -151,6 +158,66 @@ def causal_conv3d_points(x, w, flat_idx, bias=None, cache=None, stride=(1, 1), p
     if rc != 0:
         raise ValueError("oracle_causal_conv3d_points rejected its arguments")
     return out
+
+
+def strided_out_frames(t: int, stride_t: int, t_phase: int = 0) -> int:
+    """Output frames of a t-frame chunk under temporal stride ``stride_t``
+    when ``t_phase`` sequence frames (mod stride_t) came before it."""
+    return int(_load().oracle_strided_out_frames(t, stride_t, t_phase))
+
+
+def causal_conv3d_strided(x, w, bias=None, cache=None, stride=(1, 1, 1), pad=(1, 1),
+                          pad_extra=(0, 0), dil=(1, 1, 1), t_phase: int = 0) -> np.ndarray:
+    """Causal Conv3D with temporal stride and trailing spatial zero padding,
+    fp64 ("Cosmos3 Wan VAE ...", section 10.5, the downsample path; see
+    oracle_causal_conv3d_strided in oracle.c for the definition).
+
+    ``stride`` = (st, sh, sw); ``pad`` = symmetric (ph, pw); ``pad_extra`` =
+    extra zero rows below / columns right of the frame; ``t_phase`` = number
+    of sequence frames before this chunk, modulo st.  ``cache`` as for
+    :func:`causal_conv3d`.
+    """
+    st, sh, sw = stride
+    x, w, b, c, (N, C, T, H, W), (Cout, kT, kH, kW), (_, _, ph, pw, dt, dh, dw), past = \
+        _conv_args(x, w, bias, cache, (sh, sw), pad, dil)
+    eh, ew = pad_extra
+    lib = _load()
+    To = lib.oracle_strided_out_frames(T, st, t_phase)
+    Ho = lib.oracle_strided_out_size(H, kH, sh, ph, eh, dh)
+    Wo = lib.oracle_strided_out_size(W, kW, sw, pw, ew, dw)
+    if To < 0:
+        raise ValueError("bad temporal stride or phase")
+    y = np.empty((N, Cout, To, Ho, Wo), dtype=np.float64)
+    if N * To == 0:
+        return y
+    rc = lib.oracle_causal_conv3d_strided(_ptr(x), N, C, T, H, W, _ptr(c),
+                                          past if c is not None else 0, _ptr(w), Cout, kT, kH, kW,
+                                          _ptr(b), st, t_phase, sh, sw, ph, pw, eh, ew, dt, dh, dw,
+                                          _ptr(y))
+    if rc != 0:
+        raise ValueError("oracle_causal_conv3d_strided rejected its arguments")
+    return y
+
+
+def downsample3d(x, p: dict, cache=None, t_phase: int = 0, temporal: bool = True,
+                 pad=(0, 0), pad_extra=(1, 1), bf16: bool = False):
+    """The downsample path of "Cosmos3 Wan VAE ...", section 10.5, on one
+    chunk: per frame a zero pad and a 3x3 stride-2 conv (``p["w_s"]``,
+    [C, C, 1, 3, 3], bias ``p["b_s"]``) halve H and W; then, when
+    ``temporal``, the causal 3x1x1 conv with temporal stride 2 (``p["w_t"]``,
+    [C, C, 3, 1, 1], bias ``p["b_t"]``) halves T, reading ``cache`` (the
+    last 2 frames of its input before this chunk) and anchoring at phase
+    ``t_phase``.  The zero pad is ``pad`` on every side plus ``pad_extra``
+    below and to the right.  With ``bf16`` the intermediate is rounded to
+    bf16, as it is stored.  Returns (y, next_cache)."""
+    s = causal_conv3d_strided(x, p["w_s"], p.get("b_s"), stride=(1, 2, 2), pad=pad,
+                              pad_extra=pad_extra)
+    s = _maybe_round(s, bf16)
+    if not temporal:
+        return s, None
+    y = causal_conv3d_strided(s, p["w_t"], p.get("b_t"), cache=cache, stride=(2, 1, 1),
+                              pad=(0, 0), t_phase=t_phase)
+    return _maybe_round(y, bf16), next_cache(cache, s)
 
 
 def rms_norm(x, gamma, beta=None, eps: float = DEFAULT_EPS) -> np.ndarray:

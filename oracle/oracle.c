@@ -214,6 +214,113 @@ int oracle_causal_conv3d_points(const double *x, int N, int Cin, int T, int H, i
 }
 
 /* ------------------------------------------------------------------------ */
+/* Strided causal convolution (the encoder's downsampling convs)            */
+/* ------------------------------------------------------------------------ */
+/*
+ * "Cosmos3 Wan VAE ...", section 10.5 (the downsample path): per frame a zero
+ * pad and a stride-2 Conv2d halve H and W; then a CausalConv3d with temporal
+ * stride 2 may halve T.  This is the same causal sum as oracle_causal_conv3d
+ * with two generalisations:
+ *
+ *   - temporal stride st >= 1.  Output frame j of a chunk is anchored at input
+ *     frame a_j = first + j*st of the chunk, and reads frames
+ *     a_j - (kT-1-kt)*dil_t (past-only padding, so output j never sees a
+ *     frame after a_j).  first = (st - t_phase % st) % st, where t_phase is
+ *     the number of sequence frames before this chunk, modulo st: the anchors
+ *     of a whole sequence are frames 0, st, 2st, ..., and a chunk that starts
+ *     at sequence frame g anchors at the first of those that is >= g.  So a
+ *     T-frame sequence gives ceil(T/st) output frames, and frame 0 alone
+ *     produces output 0 ("diffusion inference workload anatomy", token
+ *     ledger: the causal video VAE encodes the first frame on its own and
+ *     compresses the rest 4x in time, 81 frames -> 21 latents).
+ *   - trailing spatial zero padding: ext_h extra zero rows below the frame and
+ *     ext_w extra zero columns right of it, on top of the symmetric pad.
+ *     Ho = (H + 2 pad_h + ext_h - dil_h (kH-1) - 1)/stride_h + 1.
+ *
+ *   y[n,co,j,ho,wo] = sum over ci, kt, kh, kw (in that order) of
+ *       W[co,ci,kt,kh,kw] * X'[n, ci, a_j - (kT-1-kt)*dil_t,
+ *                             ho*stride_h - pad_h + kh*dil_h,
+ *                             wo*stride_w - pad_w + kw*dil_w]
+ *     + b[co]
+ *
+ * X' as above: frames < 0 of the chunk come from the cache (frame f of the
+ * cache stands for chunk frame f - cache_frames) or are zero; positions
+ * outside [0,H) x [0,W) are zero.
+ * y: [N, C_out, T_out, Ho, Wo] with T_out = the number of anchors in [0, T).
+ * Each output element is one plain sum, evaluated on its own.
+ * Returns 0, or -1 on an inconsistent argument.
+ */
+int oracle_strided_out_frames(int T, int stride_t, int t_phase) {
+    if (stride_t <= 0 || t_phase < 0 || T < 0) return -1;
+    const int first = (stride_t - t_phase % stride_t) % stride_t;
+    return first < T ? (T - 1 - first) / stride_t + 1 : 0;
+}
+
+int oracle_strided_out_size(int in_size, int k, int stride, int pad, int ext, int dil) {
+    const int span = dil * (k - 1) + 1;
+    if (in_size + 2 * pad + ext < span) return 0;
+    return (in_size + 2 * pad + ext - span) / stride + 1;
+}
+
+int oracle_causal_conv3d_strided(const double *x, int N, int Cin, int T, int H, int W,
+                                 const double *cache, int cache_frames,
+                                 const double *wt, int Cout, int kT, int kH, int kW,
+                                 const double *bias, int stride_t, int t_phase,
+                                 int stride_h, int stride_w, int pad_h, int pad_w,
+                                 int ext_h, int ext_w, int dil_t, int dil_h, int dil_w,
+                                 double *y) {
+    if (N < 0 || Cin <= 0 || Cout <= 0 || T < 0 || H <= 0 || W <= 0) return -1;
+    if (kT <= 0 || kH <= 0 || kW <= 0 || stride_h <= 0 || stride_w <= 0) return -1;
+    if (stride_t <= 0 || t_phase < 0 || t_phase >= stride_t) return -1;
+    if (dil_t <= 0 || dil_h <= 0 || dil_w <= 0 || pad_h < 0 || pad_w < 0) return -1;
+    if (ext_h < 0 || ext_w < 0) return -1;
+    const int past = dil_t * (kT - 1);
+    if (cache && cache_frames != past) return -1;
+    const int To = oracle_strided_out_frames(T, stride_t, t_phase);
+    const int Ho = oracle_strided_out_size(H, kH, stride_h, pad_h, ext_h, dil_h);
+    const int Wo = oracle_strided_out_size(W, kW, stride_w, pad_w, ext_w, dil_w);
+    if (Ho <= 0 || Wo <= 0) return -1;
+    const int first = (stride_t - t_phase % stride_t) % stride_t;
+    const long total = (long)N * Cout * To * Ho * Wo;
+
+#pragma omp parallel for schedule(static)
+    for (long idx = 0; idx < total; ++idx) {
+        long r = idx;
+        const int wo = (int)(r % Wo); r /= Wo;
+        const int ho = (int)(r % Ho); r /= Ho;
+        const int j = (int)(r % To); r /= To;
+        const int co = (int)(r % Cout); r /= Cout;
+        const int n = (int)r;
+        const int anchor = first + j * stride_t;
+        double acc = 0.0;
+        for (int ci = 0; ci < Cin; ++ci)
+            for (int kt = 0; kt < kT; ++kt) {
+                const int ts = anchor - (kT - 1 - kt) * dil_t;
+                const double *frame;
+                if (ts >= 0)
+                    frame = x + (((size_t)n * Cin + ci) * T + ts) * (size_t)H * W;
+                else if (cache && cache_frames + ts >= 0)
+                    frame = cache + (((size_t)n * Cin + ci) * cache_frames +
+                                     (size_t)(cache_frames + ts)) * (size_t)H * W;
+                else
+                    continue;
+                for (int kh = 0; kh < kH; ++kh) {
+                    const int hs = ho * stride_h - pad_h + kh * dil_h;
+                    if (hs < 0 || hs >= H) continue;
+                    for (int kw = 0; kw < kW; ++kw) {
+                        const int ws = wo * stride_w - pad_w + kw * dil_w;
+                        if (ws < 0 || ws >= W) continue;
+                        acc += wt[((((size_t)co * Cin + ci) * kT + kt) * kH + kh) * kW + kw] *
+                               frame[(size_t)hs * W + ws];
+                    }
+                }
+            }
+        y[idx] = bias ? acc + bias[co] : acc;
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
 /* RMS norm over channels                                                   */
 /* ------------------------------------------------------------------------ */
 /*
