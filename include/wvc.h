@@ -65,13 +65,18 @@ enum { WVC_WEIGHT_STANDARD = 0, WVC_WEIGHT_PACKED = 1 };
 typedef struct wvc_conv3d_desc {
     int n, c_in, c_out, t, h, w; /* batch, channels, frames in this chunk, spatial  */
     int kt, kh, kw;              /* kernel extent                                   */
-    int stride_t;                /* must be 1                                       */
+    int stride_t;                /* >= 1; see t_phase                               */
     int stride_h, stride_w;
     int pad_h, pad_w;            /* symmetric zero padding; temporal pad is causal  */
     int dil_t, dil_h, dil_w;
     int groups;                  /* must be 1                                       */
     int dtype;                   /* WVC_F32 or WVC_BF16                             */
     int weight_layout;           /* WVC_WEIGHT_STANDARD or WVC_WEIGHT_PACKED        */
+    int pad_h_extra, pad_w_extra;/* extra zero rows below / columns right of the
+                                    frame (the downsample's one-sided zero pad,
+                                    [P1] 10.5); 0 for the symmetric case        */
+    int t_phase;                 /* sequence frames before this chunk, modulo
+                                    stride_t (0 when stride_t == 1)             */
 } wvc_conv3d_desc;
 
 /* Route counters ([P3]: counters show which route every call took). */
@@ -80,6 +85,7 @@ typedef struct wvc_counters {
     uint64_t fast_1x1x1; /* MFMA 1x1x1 channel-projection route  */
     uint64_t generic;    /* direct-convolution route             */
     uint64_t rejected;   /* calls refused with WVC_ERR_UNSUPPORTED or WVC_ERR_STRICT */
+    uint64_t fast_strided; /* MFMA routes of the downsampling convs ([P1] 10.5) */
 } wvc_counters;
 
 /*
@@ -90,8 +96,17 @@ typedef struct wvc_counters {
  * kernel slice kt = kT-1 multiplies the current frame and slice kt multiplies
  * frame t - (kT-1-kt)*dil_t.  The bias is added once after the sum over all
  * slices, and stride, padding and dilation are honoured as given ([P3]).
- * The output has t frames and h_out = (h + 2 pad_h - dil_h (kh-1) - 1)/stride_h + 1
- * rows (w_out likewise).
+ * The output has h_out = (h + 2 pad_h + pad_h_extra - dil_h (kh-1) - 1)/stride_h + 1
+ * rows (w_out likewise) and t_out frames.  With stride_t == 1, t_out = t.
+ * With stride_t = s > 1 (the encoder's temporal downsample, [P1] 10.5) output
+ * frame j is anchored at chunk frame a_j = first + j*s, first =
+ * (s - t_phase) % s, and reads frames a_j - (kT-1-kt)*dil_t: the anchors of a
+ * whole sequence are its frames 0, s, 2s, ..., so T frames give ceil(T/s)
+ * outputs and the first frame alone gives the first ("diffusion inference
+ * workload anatomy", two-compressions paragraph: 81 frames -> 21 latents
+ * over two such stages).  t_out = the number of anchors in [0, t).  A caller
+ * streaming chunks passes t_phase = (frames already fed) % s; the cache
+ * carries the last F input frames as for stride 1.
  *
  *   x         [N, C_in, t, H, W]          read
  *   cache_in  [N, C_in, F, H, W] or NULL  read; NULL = zero causal padding
@@ -101,9 +116,9 @@ typedef struct wvc_counters {
  *   weight    [C_out, C_in, kT, kH, kW]   read (or its packed form when
  *                                          d->weight_layout is WVC_WEIGHT_PACKED)
  *   bias      [C_out] or NULL             read
- *   residual  [N, C_out, t, h_out, w_out] or NULL; added after the bias
+ *   residual  [N, C_out, t_out, h_out, w_out] or NULL; added after the bias
  *                                          (fused residual of the block)
- *   y         [N, C_out, t, h_out, w_out] written
+ *   y         [N, C_out, t_out, h_out, w_out] written
  *   workspace / workspace_bytes: scratch of at least
  *             wvc_causal_conv3d_workspace_bytes(d) bytes (may be NULL if 0).
  *             It holds split-K partial sums (and the packed weights when
@@ -115,11 +130,15 @@ typedef struct wvc_counters {
  * C_out % 32 == 0 and 16-byte aligned tensors takes the MFMA implicit-GEMM
  * kernel (which also writes cache_out, in the same pass); bf16 1x1x1 /
  * stride 1 / pad 0 with the same channel rules takes the MFMA projection
- * kernel; every
+ * kernel; the downsampling convs of [P1] 10.5 (bf16, same channel rules,
+ * dilation 1) take MFMA routes of their own, counted as fast_strided: the
+ * per-frame 1x3x3 stride (1,2,2) conv, and the 3x1x1 stride (2,1,1) conv
+ * without spatial padding; every
  * other legal call takes the direct-convolution route (counted as generic,
- * refused with WVC_ERR_STRICT in strict mode).  stride_t != 1 or groups != 1
- * is WVC_ERR_UNSUPPORTED ([P3]: the fast path covers 5-D tensors, unit
- * temporal stride and one group).
+ * refused with WVC_ERR_STRICT in strict mode).  groups != 1 is
+ * WVC_ERR_UNSUPPORTED ([P3]: its fast path covers 5-D tensors, unit temporal
+ * stride and one group; this library adds the strided routes the encoder
+ * needs, which [P3] leaves to the stock conv).
  * Aliasing: y, cache_out and workspace may not overlap any other buffer of the
  * call (WVC_ERR_ALIAS); read-only buffers may overlap each other (residual ==
  * x is legal).  cache_in and cache_out must therefore be distinct buffers.

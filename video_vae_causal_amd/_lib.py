@@ -43,7 +43,7 @@ class ConvDesc(ctypes.Structure):
     _fields_ = [(f, ctypes.c_int) for f in (
         "n", "c_in", "c_out", "t", "h", "w", "kt", "kh", "kw", "stride_t", "stride_h",
         "stride_w", "pad_h", "pad_w", "dil_t", "dil_h", "dil_w", "groups", "dtype",
-        "weight_layout")]
+        "weight_layout", "pad_h_extra", "pad_w_extra", "t_phase")]
 
 
 class ResblockDesc(ctypes.Structure):
@@ -57,7 +57,8 @@ class ResblockParams(ctypes.Structure):
 
 
 class Counters(ctypes.Structure):
-    _fields_ = [(f, ctypes.c_uint64) for f in ("fast_3x3x3", "fast_1x1x1", "generic", "rejected")]
+    _fields_ = [(f, ctypes.c_uint64) for f in ("fast_3x3x3", "fast_1x1x1", "generic", "rejected",
+                                               "fast_strided")]
 
 
 class WvcError(RuntimeError):
@@ -179,7 +180,8 @@ def empty_cl(shape: Sequence[int], dtype=torch.bfloat16, device="cuda") -> torch
 
 def conv_desc(x_shape, w_shape, dtype: int, stride=(1, 1, 1), padding=(1, 1),
               dilation=(1, 1, 1), groups: int = 1,
-              weight_layout: int = WVC_WEIGHT_STANDARD) -> ConvDesc:
+              weight_layout: int = WVC_WEIGHT_STANDARD, pad_extra=(0, 0),
+              t_phase: int = 0) -> ConvDesc:
     n, c, t, h, w = x_shape
     co, ci, kt, kh, kw = w_shape
     d = ConvDesc()
@@ -191,13 +193,21 @@ def conv_desc(x_shape, w_shape, dtype: int, stride=(1, 1, 1), padding=(1, 1),
     d.groups = groups
     d.dtype = dtype
     d.weight_layout = weight_layout
+    d.pad_h_extra, d.pad_w_extra = pad_extra
+    d.t_phase = t_phase
     return d
 
 
-def conv_out_hw(h, w, k, stride, padding, dilation):
-    ho = (h + 2 * padding[0] - dilation[1] * (k[1] - 1) - 1) // stride[1] + 1
-    wo = (w + 2 * padding[1] - dilation[2] * (k[2] - 1) - 1) // stride[2] + 1
+def conv_out_hw(h, w, k, stride, padding, dilation, pad_extra=(0, 0)):
+    ho = (h + 2 * padding[0] + pad_extra[0] - dilation[1] * (k[1] - 1) - 1) // stride[1] + 1
+    wo = (w + 2 * padding[1] + pad_extra[1] - dilation[2] * (k[2] - 1) - 1) // stride[2] + 1
     return ho, wo
+
+
+def conv_out_frames(t: int, stride_t: int = 1, t_phase: int = 0) -> int:
+    """Output frames of a t-frame chunk (see t_phase in include/wvc.h)."""
+    first = (stride_t - t_phase) % stride_t
+    return (t - 1 - first) // stride_t + 1 if first < t else 0
 
 
 def wvc_conv3d_cache_frames(weight_shape, dilation=(1, 1, 1)) -> int:
@@ -242,11 +252,14 @@ def wvc_causal_conv3d_fwd(x: torch.Tensor, weight: torch.Tensor, bias: Optional[
                           y: Optional[torch.Tensor] = None, stride=(1, 1, 1), padding=(1, 1),
                           dilation=(1, 1, 1), groups: int = 1,
                           workspace: Optional[torch.Tensor] = None,
-                          packed_weight: Optional[torch.Tensor] = None) -> torch.Tensor:
+                          packed_weight: Optional[torch.Tensor] = None, pad_extra=(0, 0),
+                          t_phase: int = 0) -> torch.Tensor:
     """Causal Conv3D of one chunk (see wvc_causal_conv3d_fwd in include/wvc.h).
     ``weight`` gives the logical shape; when ``packed_weight`` (from
     wvc_conv3d_pack_weights) is given the call reads that instead.
-    Returns y (allocated if not given)."""
+    ``stride`` is (temporal, h, w); ``pad_extra`` adds zero rows below / columns
+    right of the frame; ``t_phase`` is the number of sequence frames before this
+    chunk modulo the temporal stride.  Returns y (allocated if not given)."""
     lib = load()
     _need_cl(x, "x")
     _need_cl(weight, "weight")
@@ -257,13 +270,17 @@ def wvc_causal_conv3d_fwd(x: torch.Tensor, weight: torch.Tensor, bias: Optional[
     code = _dtype_code(x.dtype)
     layout = WVC_WEIGHT_STANDARD if packed_weight is None else WVC_WEIGHT_PACKED
     d = conv_desc(tuple(x.shape), tuple(weight.shape), code, stride, padding, dilation, groups,
-                  layout)
+                  layout, pad_extra, t_phase)
     wsrc = weight if packed_weight is None else packed_weight
     if y is None:
-        ho, wo = conv_out_hw(x.shape[3], x.shape[4], weight.shape[2:], stride, padding, dilation)
+        ho, wo = conv_out_hw(x.shape[3], x.shape[4], weight.shape[2:], stride, padding, dilation,
+                             pad_extra)
         if ho < 1 or wo < 1:
             raise WvcError(WVC_ERR_ARG, "kernel larger than the padded frame")
-        y = empty_cl((x.shape[0], weight.shape[0], x.shape[2], ho, wo), x.dtype, x.device)
+        if stride[0] < 1 or not 0 <= t_phase < stride[0]:
+            raise WvcError(WVC_ERR_ARG, "bad temporal stride or t_phase")
+        to = conv_out_frames(x.shape[2], stride[0], t_phase)
+        y = empty_cl((x.shape[0], weight.shape[0], to, ho, wo), x.dtype, x.device)
     ws_bytes = 0
     if workspace is None:
         need = wvc_causal_conv3d_workspace_bytes(d)

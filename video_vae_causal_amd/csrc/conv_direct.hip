@@ -5,7 +5,9 @@
 // Definition ("Cosmos3 Wan VAE -- engine size vs runtime context memory",
 // section 10.3): y[n,t,ho,wo,co] = sum over kt, kh, kw, ci of
 // W[co,kt,kh,kw,ci] * X'[n, t-(kT-1-kt)*dil_t, ho*s_h-p_h+kh*dil_h,
-// wo*s_w-p_w+kw*dil_w, ci], then + bias once ("cache-aware video decoder
+// wo*s_w-p_w+kw*dil_w, ci] (t the chunk frame output t is anchored at: t
+// itself for temporal stride 1, t0 + j*s_t under a temporal stride, [P1]
+// 10.5), then + bias once ("cache-aware video decoder
 // lowering": stride, padding and dilation honoured, bias after the sum).
 // Frames before the chunk come from the cache (or are zero); positions outside
 // the frame are zero.  One thread per output element, channel fastest so that
@@ -32,7 +34,7 @@ __device__ __forceinline__ void st<uint16_t>(uint16_t *p, float v) { *p = f32_to
 
 template <typename T>
 __global__ void __launch_bounds__(256) direct_kernel(ConvCall c) {
-    const long total = (long)c.n * c.t * c.ho * c.wo * c.cout;
+    const long total = (long)c.n * c.to * c.ho * c.wo * c.cout;
     const long idx = (long)blockIdx.x * 256 + threadIdx.x;
     if (idx >= total) return;
     long r = idx;
@@ -42,8 +44,9 @@ __global__ void __launch_bounds__(256) direct_kernel(ConvCall c) {
     r /= c.wo;
     const int ho = (int)(r % c.ho);
     r /= c.ho;
-    const int t = (int)(r % c.t);
-    const int n = (int)(r / c.t);
+    const int j = (int)(r % c.to);
+    const int n = (int)(r / c.to);
+    const int t = c.t0 + j * c.st;  // the chunk frame output j is anchored at
 
     const T *x = static_cast<const T *>(c.x);
     const T *cache = static_cast<const T *>(c.cache_in);
@@ -80,7 +83,7 @@ __global__ void __launch_bounds__(256) direct_kernel(ConvCall c) {
 }  // namespace
 
 hipError_t launch_conv_direct(const ConvCall &c, hipStream_t s) {
-    const long total = (long)c.n * c.t * c.ho * c.wo * c.cout;
+    const long total = (long)c.n * c.to * c.ho * c.wo * c.cout;
     if (total <= 0) return hipSuccess;
     const long blocks = (total + 255) / 256;
     if (blocks > 0x7fffffffL) return hipErrorInvalidValue;

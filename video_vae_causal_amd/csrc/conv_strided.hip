@@ -1,0 +1,395 @@
+// conv_strided.hip -- MFMA routes of the encoder's downsampling convs
+// ("Cosmos3 Wan VAE -- engine size vs runtime context memory", section 10.5:
+// per frame a zero pad and a stride-2 Conv2d halve H and W, then a causal
+// conv with temporal stride 2 halves T).
+//
+// Both are one GEMM per output frame, y[p, co] = b[co] + sum_k W[co, k] X[k, p]
+// with K = kT*kH*kW*C_in in the standard weight order (kt, kh, kw, ci), so
+// K-step ks of 32 channels is tap ks / (C_in/32), channel block ks % (C_in/32).
+//
+//   * temporal (MODE 0): 3x1x1, temporal stride s, no spatial padding.  Output
+//     frame j is anchored at chunk frame a = t0 + j*s and tap kt reads frame
+//     a - 2 + kt (the cache's frames before the chunk, zeros at a sequence
+//     start).  A position's K vector is its 3 tapped frames' channel vectors.
+//   * spatial (MODE 1): 1x3x3, spatial stride 2, zero pad ph/pw before and
+//     ph+eh/pw+ew after the frame.  Output (ho, wo) reads input rows
+//     2ho - ph + kh and columns 2wo - pw + kw.
+//
+// A workgroup owns PT consecutive output positions (a run of a frame in MODE
+// 0, a run of one output row in MODE 1) and every output channel, so the
+// activation bytes cross HBM once.  It stages what those positions read in
+// LDS with coalesced 16-byte loads:
+//   MODE 0: [position][K/8 chunks + 1 pad];
+//   MODE 1: [kh][column slot][C_in/8 chunks + 1 pad] for the 2*PT+1 input
+//     columns of the 3 input rows, even columns in slots 0..PT and odd ones in
+//     PT+1..2PT, so that the 16 lanes of a B-fragment read (16 consecutive
+//     output columns, input columns 2 apart) hit consecutive slots.
+// The rows are padded to an odd number of 16-byte entries, so those reads
+// land in distinct LDS banks.  The weights stream from L2 as 16x16x32 MFMA A
+// fragments, two K-steps ahead.  Waves split output channels x positions:
+// WCO groups of FCO 16-channel blocks times 4/WCO groups of FPOS 16-position
+// blocks.
+#include <type_traits>
+
+#include "wvc_internal.h"
+#include "wvc.h"
+
+namespace wvc {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int BATCH = 16;              // staging loads in flight per thread
+constexpr size_t LDS_MAX = 80 * 1024;  // two workgroups per CU
+
+struct SParams {
+    const uint16_t *x, *cache, *wp, *bias, *res;
+    uint16_t *y;
+    int n, t, h, w, ho, wo, cin, cout;
+    int F, st, t0, to;  // cache frames, temporal stride, first anchor, output frames
+    int ph, pw;
+    int tiles;          // position tiles per output frame (MODE 0) or row (MODE 1)
+    int nb;             // K-steps of 32
+    int pitch;          // LDS row pitch in 16-byte entries
+    uint32_t w_bytes;
+};
+
+__device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+__device__ __forceinline__ uint4 wload(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+template <int MODE, int PT, int FCO, int FPOS, int WCO>
+__global__ void __launch_bounds__(256) strided_kernel(SParams p) {
+    static_assert(FPOS * 16 * (4 / WCO) == PT, "position groups must tile the run");
+    extern __shared__ uint4 xs[];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wc = wave % WCO, wq = wave / WCO;  // channel group, position group
+    const int lr = lane & 15, lg = lane >> 4;
+    const int nblk = p.cout / 16;
+    const int c8 = p.cin / 8, cbs = p.cin / 32;
+
+    // Workgroup -> (n, output frame j, row / tile); MODE 1 adds the output row.
+    long L = blockIdx.x;
+    const int tile = (int)(L % p.tiles);
+    L /= p.tiles;
+    int oh = 0;
+    if (MODE == 1) {
+        oh = (int)(L % p.ho);
+        L /= p.ho;
+    }
+    const int j = (int)(L % p.to);
+    const int n = (int)(L / p.to);
+    const int q0 = tile * PT;  // first output position (MODE 0) / column (MODE 1)
+    const int npos = MODE == 0 ? p.ho * p.wo : p.wo;
+    const int np = npos - q0 < PT ? npos - q0 : PT;
+    const size_t frame = (size_t)p.h * p.w * p.cin;
+
+    // ---- staging
+    if (MODE == 0) {
+        // Three tapped frames of the anchor: chunk frames a-2..a, or cache.
+        const int a = p.t0 + j * p.st;
+        const uint16_t *src[3];
+#pragma unroll
+        for (int kt = 0; kt < 3; ++kt) {
+            const int f = a - 2 + kt;
+            src[kt] = f >= 0 ? p.x + ((size_t)n * p.t + f) * frame
+                             : (p.cache ? p.cache + ((size_t)n * p.F + p.F + f) * frame : nullptr);
+        }
+        const int ke = p.nb * 4;  // 16-byte chunks per position
+        const int total = PT * ke;
+        for (int base = 0; base < total; base += 256 * BATCH) {
+            uint4 v[BATCH];
+#pragma unroll
+            for (int k = 0; k < BATCH; ++k) {
+                const int q = base + tid + 256 * k;
+                const int r = q / ke, e = q - r * ke;
+                const int kt = e / c8, ch = e - kt * c8;
+                v[k] = make_uint4(0u, 0u, 0u, 0u);
+                if (q < total && r < np && src[kt])
+                    v[k] = *reinterpret_cast<const uint4 *>(src[kt] + (size_t)(q0 + r) * p.cin + ch * 8);
+            }
+#pragma unroll
+            for (int k = 0; k < BATCH; ++k) {
+                const int q = base + tid + 256 * k;
+                const int r = q / ke, e = q - r * ke;
+                if (q < total) xs[r * p.pitch + e] = v[k];
+            }
+        }
+    } else {
+        const uint16_t *fp = p.x + ((size_t)n * p.t + j) * frame;  // spatial: t_out == t
+        constexpr int NC = 2 * PT + 1;                              // input columns
+        const int total = 3 * NC * c8;
+        const int col0 = 2 * q0 - p.pw;
+        for (int base = 0; base < total; base += 256 * BATCH) {
+            uint4 v[BATCH];
+#pragma unroll
+            for (int k = 0; k < BATCH; ++k) {
+                const int q = base + tid + 256 * k;
+                const int ch = q % c8, rest = q / c8;
+                const int cc = rest % NC, kh = rest / NC;
+                const int hs = 2 * oh - p.ph + kh, ws = col0 + cc;
+                v[k] = make_uint4(0u, 0u, 0u, 0u);
+                if (q < total && hs >= 0 && hs < p.h && ws >= 0 && ws < p.w)
+                    v[k] = *reinterpret_cast<const uint4 *>(fp + ((size_t)hs * p.w + ws) * p.cin + ch * 8);
+            }
+#pragma unroll
+            for (int k = 0; k < BATCH; ++k) {
+                const int q = base + tid + 256 * k;
+                const int ch = q % c8, rest = q / c8;
+                const int cc = rest % NC, kh = rest / NC;
+                const int slot = (cc & 1) ? PT + 1 + (cc >> 1) : (cc >> 1);
+                if (q < total) xs[(kh * NC + slot) * p.pitch + ch] = v[k];
+            }
+        }
+    }
+
+    // ---- weights: packed [K-step][16-row block][lane] 1 KiB fragments
+    const __amdgpu_buffer_rsrc_t wr =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(p.wp), (short)0, (int)p.w_bytes, 0x00020000);
+    bf16x8 A[3][FCO];
+    auto load_a = [&](int set, int ks) {
+#pragma unroll
+        for (int f = 0; f < FCO; ++f) {
+            const int blk = wc * FCO + f;
+            const int bc = blk < nblk ? blk : 0;  // surplus blocks read block 0, never stored
+            const uint32_t off = (uint32_t)((ks * nblk + bc) * 1024 + lane * 16);
+            if (set == 0) A[0][f] = as_bf16x8(wload(wr, off));
+            else if (set == 1) A[1][f] = as_bf16x8(wload(wr, off));
+            else A[2][f] = as_bf16x8(wload(wr, off));
+        }
+    };
+    load_a(0, 0);
+    load_a(1, p.nb > 1 ? 1 : 0);
+
+    f32x4 acc[FCO][FPOS];
+#pragma unroll
+    for (int f = 0; f < FCO; ++f)
+#pragma unroll
+        for (int b = 0; b < FPOS; ++b) acc[f][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+    __syncthreads();
+
+    // LDS entry of the B fragment of position block b at K-step ks: the 16
+    // lanes lr are 16 consecutive output positions, lg the 8-channel group.
+    const int pos0 = wq * FPOS * 16 + lr;
+    auto b_entry = [&](int ks, int b) -> int {
+        if (MODE == 0) return (pos0 + b * 16) * p.pitch + ks * 4 + lg;
+        const int tap = ks / cbs, cb = ks - tap * cbs;
+        const int kh = tap / 3, kw = tap - kh * 3;
+        const int pp = pos0 + b * 16;
+        const int slot = kw == 1 ? PT + 1 + pp : pp + (kw >> 1);
+        return (kh * (2 * PT + 1) + slot) * p.pitch + cb * 4 + lg;
+    };
+    auto kstep = [&](auto set_tag, int ks) {
+        constexpr int SET = decltype(set_tag)::value;
+        load_a((SET + 2) % 3, ks + 2 < p.nb ? ks + 2 : p.nb - 1);
+        bf16x8 B[FPOS];
+#pragma unroll
+        for (int b = 0; b < FPOS; ++b) B[b] = as_bf16x8(xs[b_entry(ks, b)]);
+#pragma unroll
+        for (int b = 0; b < FPOS; ++b)
+#pragma unroll
+            for (int f = 0; f < FCO; ++f)
+                acc[f][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[SET][f], B[b], acc[f][b], 0, 0, 0);
+    };
+    for (int ks = 0; ks < p.nb; ks += 3) {
+        kstep(std::integral_constant<int, 0>{}, ks);
+        if (ks + 1 < p.nb) kstep(std::integral_constant<int, 1>{}, ks + 1);
+        if (ks + 2 < p.nb) kstep(std::integral_constant<int, 2>{}, ks + 2);
+    }
+
+    // ---- epilogue: element e of tile (f, b) is channel blk*16 + lg*4 + e at
+    // position pos0 + b*16; + bias, + residual, one rounding.
+    const size_t obase = MODE == 0 ? ((size_t)n * p.to + j) * (size_t)npos + q0
+                                   : (((size_t)n * p.to + j) * p.ho + oh) * (size_t)p.wo + q0;
+#pragma unroll
+    for (int f = 0; f < FCO; ++f) {
+        const int blk = wc * FCO + f;
+        if (blk >= nblk) continue;
+        const int co = blk * 16 + lg * 4;
+        float bv[4] = {0.f, 0.f, 0.f, 0.f};
+        if (p.bias) {
+            const uint2 bb = *reinterpret_cast<const uint2 *>(p.bias + co);
+            bv[0] = bf16_to_f32(bb.x & 0xffffu);
+            bv[1] = bf16_to_f32(bb.x >> 16);
+            bv[2] = bf16_to_f32(bb.y & 0xffffu);
+            bv[3] = bf16_to_f32(bb.y >> 16);
+        }
+#pragma unroll
+        for (int b = 0; b < FPOS; ++b) {
+            const int r = pos0 + b * 16;
+            if (r >= np) continue;
+            const size_t o = (obase + r) * p.cout + co;
+            float v[4] = {acc[f][b][0] + bv[0], acc[f][b][1] + bv[1], acc[f][b][2] + bv[2],
+                          acc[f][b][3] + bv[3]};
+            if (p.res) {
+                const uint2 rr = *reinterpret_cast<const uint2 *>(p.res + o);
+                v[0] += bf16_to_f32(rr.x & 0xffffu);
+                v[1] += bf16_to_f32(rr.x >> 16);
+                v[2] += bf16_to_f32(rr.y & 0xffffu);
+                v[3] += bf16_to_f32(rr.y >> 16);
+            }
+            *reinterpret_cast<uint2 *>(p.y + o) = make_uint2(pack2_bf16(v[0], v[1]), pack2_bf16(v[2], v[3]));
+        }
+    }
+}
+
+// Standard [C_out][K] bf16 weights -> [K-step][16-row block][lane] fragments:
+// lane (lr, lg) of block b at K-step ks holds row b*16 + lr, columns
+// ks*32 + lg*8 .. +7.
+__global__ void __launch_bounds__(256) strided_pack_kernel(const uint16_t *__restrict__ w,
+                                                           uint4 *__restrict__ out, int cout, int K) {
+    const int nblk = cout / 16, nb = K / 32;
+    const long total = (long)nb * nblk * 64;
+    for (long i = (long)blockIdx.x * 256 + threadIdx.x; i < total; i += (long)gridDim.x * 256) {
+        const int lane = (int)(i % 64);
+        const long rest = i / 64;
+        const int b = (int)(rest % nblk), ks = (int)(rest / nblk);
+        const int row = b * 16 + (lane & 15), col = ks * 32 + (lane >> 4) * 8;
+        out[i] = *reinterpret_cast<const uint4 *>(w + (size_t)row * K + col);
+    }
+}
+
+int k_total(const ConvCall &c) { return c.kt * c.kh * c.kw * c.cin; }
+
+bool is_temporal(const ConvCall &c) {
+    return c.kt == 3 && c.kh == 1 && c.kw == 1 && c.dt == 1 && c.st >= 2 && c.sh == 1 &&
+           c.sw == 1 && c.ph == 0 && c.pw == 0 && c.eh == 0 && c.ew == 0;
+}
+
+bool is_spatial2(const ConvCall &c) {
+    return c.kt == 1 && c.kh == 3 && c.kw == 3 && c.dh == 1 && c.dw == 1 && c.st == 1 &&
+           c.sh == 2 && c.sw == 2 && c.ph <= 1 && c.pw <= 1 && c.eh <= 1 && c.ew <= 1;
+}
+
+// Positions per workgroup and its LDS bytes.
+int run_length(const ConvCall &c) {
+    if (is_temporal(c)) return 64;
+    return (size_t)3 * 129 * (c.cin / 8 + 1) * 16 <= LDS_MAX ? 64 : 32;
+}
+
+size_t lds_bytes(const ConvCall &c) {
+    const int pt = run_length(c);
+    if (is_temporal(c)) return (size_t)pt * (k_total(c) / 8 + 1) * 16;
+    return (size_t)3 * (2 * pt + 1) * (c.cin / 8 + 1) * 16;
+}
+
+// Wave layout: channel groups x 16-channel blocks per group.
+struct Layout {
+    int wco, fco;
+};
+Layout layout_for(int cout) {
+    const int nblk = cout / 16;
+    if (nblk % 4 == 0) return {4, nblk / 4};
+    if (nblk % 2 == 0) return {2, nblk / 2};
+    return {1, nblk};
+}
+
+template <int MODE, int PT, int FCO, int WCO>
+hipError_t launch_one(const SParams &p, long blocks, size_t lds, hipStream_t s) {
+    constexpr int FPOS = PT / 16 / (4 / WCO);
+    if constexpr (FPOS >= 1 && FPOS * 16 * (4 / WCO) == PT) {
+        hipLaunchKernelGGL((strided_kernel<MODE, PT, FCO, FPOS, WCO>), dim3((unsigned)blocks), dim3(256),
+                           lds, s, p);
+        return hipGetLastError();
+    } else {
+        return hipErrorInvalidValue;
+    }
+}
+
+template <int MODE, int PT>
+hipError_t launch_mode(const SParams &p, Layout l, long blocks, size_t lds, hipStream_t s) {
+    switch (l.wco * 10 + l.fco) {
+        case 41: return launch_one<MODE, PT, 1, 4>(p, blocks, lds, s);
+        case 42: return launch_one<MODE, PT, 2, 4>(p, blocks, lds, s);
+        case 43: return launch_one<MODE, PT, 3, 4>(p, blocks, lds, s);
+        case 44: return launch_one<MODE, PT, 4, 4>(p, blocks, lds, s);
+        case 21: return launch_one<MODE, PT, 1, 2>(p, blocks, lds, s);
+        case 23: return launch_one<MODE, PT, 3, 2>(p, blocks, lds, s);
+        case 11: return launch_one<MODE, PT, 1, 1>(p, blocks, lds, s);
+        case 13: return launch_one<MODE, PT, 3, 1>(p, blocks, lds, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+bool layout_instantiated(Layout l) {
+    switch (l.wco * 10 + l.fco) {
+        case 41: case 42: case 43: case 44: case 21: case 23: case 11: case 13: return true;
+        default: return false;
+    }
+}
+
+}  // namespace
+
+bool strided_supports(const ConvCall &c) {
+    if (!(is_temporal(c) || is_spatial2(c))) return false;
+    if (c.cin % 32 != 0 || c.cout % 16 != 0 || c.cout > 256) return false;
+    if (!layout_instantiated(layout_for(c.cout))) return false;
+    if (k_total(c) / 32 > 255) return false;
+    if (is_spatial2(c) && (size_t)3 * 65 * (c.cin / 8 + 1) * 16 > LDS_MAX) return false;
+    // 32-position runs need at least two channel groups (16 positions per group)
+    if (is_spatial2(c) && run_length(c) == 32 && layout_for(c.cout).wco == 1) return false;
+    if (is_temporal(c) && lds_bytes(c) > LDS_MAX) return false;
+    // 32-bit fragment offsets
+    return (size_t)c.cout * k_total(c) * 2 < ((size_t)1 << 31);
+}
+
+size_t strided_packed_weight_bytes(const ConvCall &c) { return (size_t)c.cout * k_total(c) * 2; }
+
+size_t strided_workspace_bytes(const ConvCall &c, bool packed_given) {
+    return packed_given ? 0 : (strided_packed_weight_bytes(c) + 255) & ~(size_t)255;
+}
+
+hipError_t launch_strided_pack(const ConvCall &c, const void *w, void *packed, hipStream_t s) {
+    const long chunks = (long)strided_packed_weight_bytes(c) / 16;
+    long blocks = (chunks + 255) / 256;
+    if (blocks > 4096) blocks = 4096;
+    if (blocks < 1) return hipSuccess;
+    hipLaunchKernelGGL(strided_pack_kernel, dim3((unsigned)blocks), dim3(256), 0, s,
+                       static_cast<const uint16_t *>(w), static_cast<uint4 *>(packed), c.cout, k_total(c));
+    return hipGetLastError();
+}
+
+hipError_t launch_conv_strided(const ConvCall &c, ConvRoute r, bool packed_given, void *ws,
+                               size_t ws_bytes, hipStream_t s) {
+    if (!strided_supports(c)) return hipErrorInvalidValue;
+    const void *wp = c.weight;
+    if (!packed_given) {
+        if (ws_bytes < strided_workspace_bytes(c, false) || !ws) return hipErrorInvalidValue;
+        const hipError_t e = launch_strided_pack(c, c.weight, ws, s);
+        if (e != hipSuccess) return e;
+        wp = ws;
+    }
+    const bool temporal = r == ConvRoute::FastTemporal;
+    if (temporal != is_temporal(c)) return hipErrorInvalidValue;
+    SParams p{};
+    p.x = static_cast<const uint16_t *>(c.x);
+    p.cache = static_cast<const uint16_t *>(c.cache_in);
+    p.wp = static_cast<const uint16_t *>(wp);
+    p.bias = static_cast<const uint16_t *>(c.bias);
+    p.res = static_cast<const uint16_t *>(c.residual);
+    p.y = static_cast<uint16_t *>(c.y);
+    p.n = c.n; p.t = c.t; p.h = c.h; p.w = c.w; p.ho = c.ho; p.wo = c.wo;
+    p.cin = c.cin; p.cout = c.cout;
+    p.F = c.frames; p.st = c.st; p.t0 = c.t0; p.to = c.to;
+    p.ph = c.ph; p.pw = c.pw;
+    p.nb = k_total(c) / 32;
+    p.w_bytes = (uint32_t)strided_packed_weight_bytes(c);
+    const int pt = run_length(c);
+    p.pitch = temporal ? k_total(c) / 8 + 1 : c.cin / 8 + 1;
+    p.tiles = temporal ? (c.ho * c.wo + pt - 1) / pt : (c.wo + pt - 1) / pt;
+    const long blocks = temporal ? (long)c.n * c.to * p.tiles : (long)c.n * c.to * c.ho * p.tiles;
+    if (blocks <= 0) return hipSuccess;
+    if (blocks > 0x7fffffffL) return hipErrorInvalidValue;
+    const size_t lds = lds_bytes(c);
+    const Layout l = layout_for(c.cout);
+    if (temporal) return launch_mode<0, 64>(p, l, blocks, lds, s);
+    return pt == 64 ? launch_mode<1, 64>(p, l, blocks, lds, s) : launch_mode<1, 32>(p, l, blocks, lds, s);
+}
+
+}  // namespace wvc

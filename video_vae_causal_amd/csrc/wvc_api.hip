@@ -17,7 +17,7 @@ namespace {
 
 thread_local char g_err[512] = "";
 std::atomic<int> g_strict{-1};
-std::atomic<uint64_t> g_fast3{0}, g_fast1{0}, g_generic{0}, g_rejected{0};
+std::atomic<uint64_t> g_fast3{0}, g_fast1{0}, g_generic{0}, g_rejected{0}, g_strided{0};
 
 int fail(int code, const char *fmt, ...) {
     va_list ap;
@@ -84,14 +84,24 @@ struct ConvPlan {
     size_t x_bytes, cache_bytes, w_bytes, b_bytes, y_bytes;
 };
 
+bool strided_route(wvc::ConvRoute r) {
+    return r == wvc::ConvRoute::FastTemporal || r == wvc::ConvRoute::FastSpatial2;
+}
+
+size_t route_ws_bytes(const ConvPlan &pl, bool packed) {
+    if (pl.route == wvc::ConvRoute::Generic) return 0;
+    if (strided_route(pl.route)) return wvc::strided_workspace_bytes(pl.call, packed);
+    return wvc::igemm_workspace_bytes(pl.call, pl.route, packed);
+}
+
+size_t route_packed_bytes(const ConvPlan &pl) {
+    return strided_route(pl.route) ? wvc::strided_packed_weight_bytes(pl.call)
+                                   : wvc::igemm_packed_weight_bytes(pl.call);
+}
+
 // Validates the descriptor (not the pointers) and fills the sizes.
 int plan_conv(const wvc_conv3d_desc *d, ConvPlan *pl, bool count = true) {
     if (!d) return fail(WVC_ERR_ARG, "conv descriptor is NULL");
-    if (d->stride_t != 1) {
-        if (count) g_rejected++;
-        return fail(WVC_ERR_UNSUPPORTED, "temporal stride %d: only temporal stride 1 is supported",
-                    d->stride_t);
-    }
     if (d->groups != 1) {
         if (count) g_rejected++;
         return fail(WVC_ERR_UNSUPPORTED, "groups=%d: only one group is supported", d->groups);
@@ -107,11 +117,19 @@ int plan_conv(const wvc_conv3d_desc *d, ConvPlan *pl, bool count = true) {
     if (d->weight_layout != WVC_WEIGHT_STANDARD && d->weight_layout != WVC_WEIGHT_PACKED)
         return fail(WVC_ERR_ARG, "weight_layout %d is neither standard nor packed", d->weight_layout);
     if (d->kt < 1 || d->kh < 1 || d->kw < 1 || d->stride_h < 1 || d->stride_w < 1 ||
-        d->pad_h < 0 || d->pad_w < 0 || d->dil_t < 1 || d->dil_h < 1 || d->dil_w < 1)
+        d->pad_h < 0 || d->pad_w < 0 || d->dil_t < 1 || d->dil_h < 1 || d->dil_w < 1 ||
+        d->stride_t < 1 || d->stride_t > 64 || d->pad_h_extra < 0 || d->pad_w_extra < 0 ||
+        d->pad_h_extra > 64 || d->pad_w_extra > 64)
         return fail(WVC_ERR_ARG, "bad kernel/stride/pad/dilation");
-    const int ho = out_size(d->h, d->kh, d->stride_h, d->pad_h, d->dil_h);
-    const int wo = out_size(d->w, d->kw, d->stride_w, d->pad_w, d->dil_w);
+    if (d->t_phase < 0 || d->t_phase >= d->stride_t)
+        return fail(WVC_ERR_ARG, "t_phase %d must lie in [0, stride_t = %d)", d->t_phase, d->stride_t);
+    // One-sided padding extends the padded frame at its far end only.
+    const int ho = out_size(d->h + d->pad_h_extra, d->kh, d->stride_h, d->pad_h, d->dil_h);
+    const int wo = out_size(d->w + d->pad_w_extra, d->kw, d->stride_w, d->pad_w, d->dil_w);
     if (ho < 1 || wo < 1) return fail(WVC_ERR_ARG, "kernel larger than the padded frame");
+    // Output frames: anchors first, first + stride_t, ... inside the chunk.
+    const int first = (d->stride_t - d->t_phase) % d->stride_t;
+    const int to = first < d->t ? (d->t - 1 - first) / d->stride_t + 1 : 0;
     const long frames = (long)d->dil_t * (d->kt - 1);
     if (frames > 1024) return fail(WVC_ERR_ARG, "temporal receptive field too large");
 
@@ -124,6 +142,11 @@ int plan_conv(const wvc_conv3d_desc *d, ConvPlan *pl, bool count = true) {
     c.dt = d->dil_t; c.dh = d->dil_h; c.dw = d->dil_w;
     c.frames = (int)frames;
     c.dtype = d->dtype;
+    c.st = d->stride_t;
+    c.t0 = first;
+    c.to = to;
+    c.eh = d->pad_h_extra;
+    c.ew = d->pad_w_extra;
 
     size_t plane_in, plane_out, v;
     bool ok = mul_ok((size_t)d->h, (size_t)d->w, &plane_in) && mul_ok(plane_in, d->c_in, &plane_in);
@@ -132,28 +155,33 @@ int plan_conv(const wvc_conv3d_desc *d, ConvPlan *pl, bool count = true) {
     ok = ok && mul_ok(plane_in, (size_t)d->n * frames, &v) && mul_ok(v, e, &pl->cache_bytes);
     ok = ok && mul_ok((size_t)d->c_out * d->c_in, (size_t)d->kt * d->kh * d->kw, &v) &&
          mul_ok(v, e, &pl->w_bytes);
-    ok = ok && mul_ok(plane_out, (size_t)d->n * d->t, &v) && mul_ok(v, e, &pl->y_bytes);
+    ok = ok && mul_ok(plane_out, (size_t)d->n * to, &v) && mul_ok(v, e, &pl->y_bytes);
     if (!ok) return fail(WVC_ERR_ARG, "tensor size overflows");
     pl->b_bytes = (size_t)d->c_out * e;
 
     const bool chan_ok = d->c_in % 8 == 0 && d->c_out % 32 == 0;
-    const bool unit = d->stride_h == 1 && d->stride_w == 1;
+    const bool unit = d->stride_h == 1 && d->stride_w == 1 && d->stride_t == 1 &&
+                      d->pad_h_extra == 0 && d->pad_w_extra == 0;
+    const bool dil1 = d->dil_t == 1 && d->dil_h == 1 && d->dil_w == 1;
     if (d->dtype == WVC_BF16 && chan_ok && unit && d->kt == 3 && d->kh == 3 && d->kw == 3 &&
-        d->pad_h == 1 && d->pad_w == 1 && d->dil_t == 1 && d->dil_h == 1 && d->dil_w == 1)
+        d->pad_h == 1 && d->pad_w == 1 && dil1)
         pl->route = wvc::ConvRoute::Fast3x3x3;
     else if (d->dtype == WVC_BF16 && chan_ok && unit && d->kt == 1 && d->kh == 1 && d->kw == 1 &&
              d->pad_h == 0 && d->pad_w == 0)
         pl->route = wvc::ConvRoute::Fast1x1x1;
+    else if (d->dtype == WVC_BF16 && wvc::strided_supports(c))
+        pl->route = d->kt > 1 ? wvc::ConvRoute::FastTemporal : wvc::ConvRoute::FastSpatial2;
     else
         pl->route = wvc::ConvRoute::Generic;
-    if (pl->route != wvc::ConvRoute::Generic && !wvc::igemm_supports(c))
+    if ((pl->route == wvc::ConvRoute::Fast3x3x3 || pl->route == wvc::ConvRoute::Fast1x1x1) &&
+        !wvc::igemm_supports(c))
         pl->route = wvc::ConvRoute::Generic;
     if (d->weight_layout == WVC_WEIGHT_PACKED) {
         if (pl->route == wvc::ConvRoute::Generic) {
             if (count) g_rejected++;
             return fail(WVC_ERR_UNSUPPORTED, "packed weights exist only for the MFMA routes");
         }
-        pl->w_bytes = wvc::igemm_packed_weight_bytes(c);
+        pl->w_bytes = route_packed_bytes(*pl);
     }
     return WVC_OK;
 }
@@ -175,7 +203,9 @@ int conv_fwd(const wvc_conv3d_desc *d, const void *x, const void *cache_in, void
     int rc = plan_conv(d, &pl);
     if (rc) return rc;
     if (!weight) return fail(WVC_ERR_ARG, "weight is NULL");
-    if (d->t > 0 && (!x || !y)) return fail(WVC_ERR_ARG, "x or y is NULL");
+    // y is needed only when the chunk has output frames (a strided chunk may
+    // have none: its frames only feed the cache).
+    if (d->t > 0 && (!x || (pl.call.to > 0 && !y))) return fail(WVC_ERR_ARG, "x or y is NULL");
     if (pl.call.frames == 0) {
         cache_in = nullptr;
         cache_out = nullptr;
@@ -192,9 +222,7 @@ int conv_fwd(const wvc_conv3d_desc *d, const void *x, const void *cache_in, void
             pl.route = wvc::ConvRoute::Generic;
         }
     }
-    size_t need = pl.route == wvc::ConvRoute::Generic
-                      ? 0
-                      : wvc::igemm_workspace_bytes(pl.call, pl.route, packed);
+    size_t need = route_ws_bytes(pl, packed);
     if (ws_bytes < need)
         return fail(WVC_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", ws_bytes, need);
 
@@ -228,6 +256,8 @@ int conv_fwd(const wvc_conv3d_desc *d, const void *x, const void *cache_in, void
     if (d->t > 0) {
         if (pl.route == wvc::ConvRoute::Generic) {
             err = wvc::launch_conv_direct(c, s);
+        } else if (strided_route(pl.route)) {
+            err = wvc::launch_conv_strided(c, pl.route, packed, ws, ws_bytes, s);
         } else {
             err = wvc::launch_conv_igemm(c, pl.route, packed, ws, ws_bytes, cache_out, s, defer);
             cache_done = pl.route == wvc::ConvRoute::Fast3x3x3;  // written by the conv itself
@@ -244,6 +274,8 @@ int conv_fwd(const wvc_conv3d_desc *d, const void *x, const void *cache_in, void
         g_fast3++;
     else if (pl.route == wvc::ConvRoute::Fast1x1x1)
         g_fast1++;
+    else if (strided_route(pl.route))
+        g_strided++;
     else
         g_generic++;
     return WVC_OK;
@@ -338,8 +370,7 @@ int wvc_causal_conv3d_fwd(const wvc_conv3d_desc *d, const void *x, const void *c
 size_t wvc_causal_conv3d_workspace_bytes(const wvc_conv3d_desc *d) {
     ConvPlan pl;
     if (plan_conv(d, &pl, /*count=*/false)) return (size_t)-1;  // a size query is not a call
-    if (pl.route == wvc::ConvRoute::Generic) return 0;
-    return wvc::igemm_workspace_bytes(pl.call, pl.route, d->weight_layout == WVC_WEIGHT_PACKED);
+    return route_ws_bytes(pl, d->weight_layout == WVC_WEIGHT_PACKED);
 }
 
 size_t wvc_conv3d_packed_weight_bytes(const wvc_conv3d_desc *d) {
@@ -349,7 +380,7 @@ size_t wvc_conv3d_packed_weight_bytes(const wvc_conv3d_desc *d) {
         fail(WVC_ERR_UNSUPPORTED, "packed weights exist only for the MFMA routes");
         return (size_t)-1;
     }
-    return wvc::igemm_packed_weight_bytes(pl.call);
+    return route_packed_bytes(pl);
 }
 
 int wvc_conv3d_pack_weights(const wvc_conv3d_desc *d, const void *weight, void *packed,
@@ -364,11 +395,12 @@ int wvc_conv3d_pack_weights(const wvc_conv3d_desc *d, const void *weight, void *
         return fail(WVC_ERR_ARG, "packed weights need a 16-byte aligned buffer");
     const size_t std_bytes = (size_t)d->c_out * d->c_in * d->kt * d->kh * d->kw * 2;
     const Buf bufs[] = {{weight, std_bytes, false, "weight"},
-                        {packed, wvc::igemm_packed_weight_bytes(pl.call), true, "packed"}};
+                        {packed, route_packed_bytes(pl), true, "packed"}};
     rc = check_aliasing(bufs, 2);
     if (rc) return rc;
-    return hip_status(wvc::launch_pack_weights(pl.call, weight, packed,
-                                               static_cast<hipStream_t>(stream)),
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    return hip_status(strided_route(pl.route) ? wvc::launch_strided_pack(pl.call, weight, packed, s)
+                                              : wvc::launch_pack_weights(pl.call, weight, packed, s),
                       "weight packing launch");
 }
 
@@ -650,6 +682,7 @@ void wvc_get_counters(wvc_counters *out) {
     out->fast_1x1x1 = g_fast1.load();
     out->generic = g_generic.load();
     out->rejected = g_rejected.load();
+    out->fast_strided = g_strided.load();
 }
 
 void wvc_reset_counters(void) {
@@ -657,6 +690,7 @@ void wvc_reset_counters(void) {
     g_fast1 = 0;
     g_generic = 0;
     g_rejected = 0;
+    g_strided = 0;
 }
 
 const char *wvc_last_error(void) { return g_err; }

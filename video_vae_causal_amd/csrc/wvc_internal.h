@@ -49,9 +49,23 @@ struct ConvCall {
     int kt, kh, kw, sh, sw, ph, pw, dt, dh, dw;
     int frames;            // F = dt*(kt-1)
     int dtype;             // WVC_F32 / WVC_BF16
+    int st, t0, to;        // temporal stride, first anchor frame, output frames
+    int eh, ew;            // extra zero rows below / columns right of the frame
 };
 
-enum class ConvRoute { Fast3x3x3, Fast1x1x1, Generic };
+enum class ConvRoute { Fast3x3x3, Fast1x1x1, FastTemporal, FastSpatial2, Generic };
+
+// MFMA routes of the encoder's downsampling convs ("Cosmos3 Wan VAE", section
+// 10.5), conv_strided.hip: FastTemporal (3x1x1, temporal stride 2, no spatial
+// padding) and FastSpatial2 (1x3x3, spatial stride 2).  Their packed weights
+// are the conv as one [C_out x K] GEMM operand, K = kT*kH*kW*C_in in the
+// standard weight order, in 16x16x32 MFMA A-fragment order.
+bool strided_supports(const ConvCall &c);
+size_t strided_workspace_bytes(const ConvCall &c, bool packed_given);
+size_t strided_packed_weight_bytes(const ConvCall &c);
+hipError_t launch_strided_pack(const ConvCall &c, const void *w, void *packed, hipStream_t s);
+hipError_t launch_conv_strided(const ConvCall &c, ConvRoute r, bool packed_given, void *ws,
+                               size_t ws_bytes, hipStream_t s);
 
 // MFMA implicit-GEMM route (bf16 only).  Weights are read in the packed
 // fragment order written by launch_pack_weights; a call that brings

@@ -180,6 +180,23 @@ def decoder_inputs(seed: int = 5, shape=(1, 48, 21, 30, 52), width: int = 384,
     return {"latent": quantize(normal(shape, seed, "latent"), dtype), "p": p}
 
 
+def downsample_inputs(seed: int = 6, shape=(1, 96, 17, 480, 832), dtype: str = "bf16",
+                      with_x: bool = True) -> Dict:
+    """The encoder's downsample path at the pages' L0 feature-map size: the
+    96-channel 17x480x832 map, a 1x3x3 stride-2 conv (spatial), a 3x1x1
+    temporal-stride-2 conv, and the RMS-norm gammas before and after."""
+    c = shape[1]
+    d = {"gamma1": norm_gamma(c, seed, "gamma1", dtype),
+         "w_s": conv_weight(c, c, (1, 3, 3), seed, "w_s", dtype),
+         "b_s": conv_bias(c, seed, "b_s", dtype),
+         "w_t": conv_weight(c, c, (3, 1, 1), seed, "w_t", dtype),
+         "b_t": conv_bias(c, seed, "b_t", dtype),
+         "gamma2": norm_gamma(c, seed, "gamma2", dtype)}
+    if with_x:
+        d["x"] = quantize(normal(shape, seed, "x"), dtype)
+    return d
+
+
 def sample_indices(shape: Tuple[int, ...], count: int, seed: int,
                    include_frames: Optional[List[int]] = None) -> np.ndarray:
     """Flat NCTHW indices for point-sampled checks: ``count`` uniformly random
