@@ -48,8 +48,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="resblock_384_60x104",
-                    choices=["resblock_384_60x104", "layer_384_240x416", "layer_96_480x832",
-                             "decoder_stack_48_30x52"])
+                    choices=sorted(["resblock_384_60x104", "layer_384_240x416", "layer_96_480x832",
+                                    "decoder_stack_48_30x52", "downsample_96_480x832"]))
     ap.add_argument("--kernel-reps", type=int, default=50,
                     help="launches of the dominant kernel timed for the roofline")
     ap.add_argument("--warmup-seconds", type=float, default=0.5,
@@ -303,8 +303,66 @@ def wl_decoder():
     return step, info
 
 
+def wl_downsample():
+    """The encoder's downsample path ("Cosmos3 Wan VAE", section 10.5) on the
+    pages' L0 map: RMS norm + SiLU, the 1x3x3 stride-2 conv (480x832 ->
+    240x416, one trailing zero row and column), the 3x1x1 temporal-stride-2
+    conv (17 -> 9 frames, its cache and phase carried across chunks), RMS norm
+    + SiLU; chunks of 1+4+4+4+4 frames."""
+    import torch
+    from video_vae_causal_amd import _lib as L, accounting as acc, inputs
+    d = inputs.downsample_inputs()
+    n, c, t, h, w = d["x"].shape
+    x = to_dev(d["x"])
+    p = {k: to_dev(v) for k, v in d.items() if k != "x"}
+    ho, wo = h // 2, w // 2
+    sizes = [1, 4, 4, 4, 4]
+    starts = [int(v) for v in np.cumsum([0] + sizes[:-1])]
+    phases = [g % 2 for g in starts]
+    touts = [L.conv_out_frames(k, 2, ph) for k, ph in zip(sizes, phases)]
+    ostarts = [int(v) for v in np.cumsum([0] + touts[:-1])]
+    h1 = L.empty_cl(x.shape)
+    sbuf = L.empty_cl((n, c, t, ho, wo))
+    y = L.empty_cl((n, c, sum(touts), ho, wo))
+    out = L.empty_cl(y.shape)
+    caches = [L.empty_cl((n, c, 2, ho, wo)) for _ in range(2)]
+    hs = [cl(h1[:, :, s:s + k]) for s, k in zip(starts, sizes)]
+    ss = [cl(sbuf[:, :, s:s + k]) for s, k in zip(starts, sizes)]
+    ys = [y[:, :, s:s + k] for s, k in zip(ostarts, touts)]
+    sp_kw = dict(stride=(1, 2, 2), padding=(0, 0), pad_extra=(1, 1))
+    tm_kw = dict(stride=(2, 1, 1), padding=(0, 0))
+    wsp = L.wvc_conv3d_pack_weights(p["w_s"], **sp_kw)
+    wtp = L.wvc_conv3d_pack_weights(p["w_t"], **tm_kw)
+
+    def step():
+        L.wvc_rmsnorm_silu(x, p["gamma1"], y=h1)
+        L.wvc_cache_reset(caches[0])
+        for i in range(len(sizes)):
+            L.wvc_causal_conv3d_fwd(hs[i], p["w_s"], p["b_s"], y=ss[i], packed_weight=wsp, **sp_kw)
+            L.wvc_causal_conv3d_fwd(ss[i], p["w_t"], p["b_t"], caches[i % 2], caches[(i + 1) % 2],
+                                    y=ys[i], packed_weight=wtp, t_phase=phases[i], **tm_kw)
+        L.wvc_rmsnorm_silu(y, p["gamma2"], y=out)
+
+    f_sp = 2 * 9 * c * c * t * ho * wo
+    f_tm = 2 * 3 * c * c * sum(touts) * ho * wo
+
+    def kernel():
+        L.wvc_causal_conv3d_fwd(hs[1], p["w_s"], p["b_s"], y=ss[1], packed_weight=wsp, **sp_kw)
+
+    k_bytes = 2 * c * (4 * h * w + 4 * ho * wo) + 2 * 9 * c * c
+    info = dict(workload="downsample_96_480x832", conv_flops=f_sp + f_tm, latent_frames=t,
+                config={"workload": "downsample_96_480x832", "channels": c, "frames": t,
+                        "height": h, "width": w, "out_frames": sum(touts), "out_height": ho,
+                        "out_width": wo, "chunks": sizes, "batch": n},
+                kernel=kernel, kernel_name="strided_kernel<1, 64, 3, 2, 2>",
+                kernel_units=k_bytes, kernel_bound="hbm", kernel_bytes=k_bytes,
+                kernel_flops=2 * 9 * c * c * 4 * ho * wo)
+    return step, info
+
+
 WORKLOADS = {"resblock_384_60x104": wl_resblock, "layer_384_240x416": wl_layer384,
-             "layer_96_480x832": wl_layer96, "decoder_stack_48_30x52": wl_decoder}
+             "layer_96_480x832": wl_layer96, "decoder_stack_48_30x52": wl_decoder,
+             "downsample_96_480x832": wl_downsample}
 
 
 # ---------------------------------------------------------------------------
@@ -339,6 +397,16 @@ def cpu_baseline(workload: str):
         oracle.resblock(x, p, past, past, bf16=True)
         dt = time.perf_counter() - t0
         sample = "1 of 5 latent frames (frame 2, non-zero caches) through the block"
+    elif workload == "downsample_96_480x832":
+        d = inputs.downsample_inputs()
+        xs = d["x"][:, :, :4].astype(np.float64)   # frames 0..3 (one 4-frame chunk)
+        n, c, f, h, w = xs.shape
+        flops = 2 * 9 * c * c * f * (h // 2) * (w // 2)
+        t0 = time.perf_counter()
+        oracle.causal_conv3d_strided(xs, d["w_s"].astype(np.float64), d["b_s"].astype(np.float64),
+                                     stride=(1, 2, 2), pad=(0, 0), pad_extra=(1, 1))
+        dt = time.perf_counter() - t0
+        sample = "frames 0-3 (one 4-frame chunk) of the stride-2 spatial conv"
     else:
         d = inputs.layer384_inputs() if workload == "layer_384_240x416" else inputs.layer96_inputs()
         x = d["x"][:, :, :3]
@@ -434,13 +502,21 @@ def main():
 
     # dominant kernel, timed alone with events on the stream it is launched on
     k_ms, _ = time_region(info["kernel"], args.kernel_reps, 3, min(args.warmup_seconds, 0.2))
-    achieved = info["kernel_units"] / (k_ms * 1e-3) / 1e12
     traffic = measured_traffic(args.traffic_json, args.workload, info["kernel_name"])
+    if info["kernel_bound"] == "hbm":
+        achieved = info["kernel_bytes"] / (k_ms * 1e-3) / 1e9
+        peak, unit = HBM_PEAK_GBS, "GB/s"
+        flops = info["kernel_flops"]
+    else:
+        achieved = info["kernel_units"] / (k_ms * 1e-3) / 1e12
+        peak, unit = MFMA_BF16_PEAK_TFLOPS, "TFLOP/s"
+        flops = info["kernel_units"]
     roofline = {"bound": info["kernel_bound"], "achieved": round(achieved, 2),
-                "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": traffic,
+                "peak": peak, "unit": unit,
+                "frac": round(achieved / peak, 4), "traffic": traffic,
                 "kernel": info["kernel_name"], "kernel_ms": round(k_ms, 5),
-                "flops_per_launch": info["kernel_units"],
+                "flops_per_launch": flops,
+                "mfma_frac": round(flops / (k_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
                 "algorithmic_bytes_per_launch": info["kernel_bytes"]}
 
     line = {

@@ -222,23 +222,30 @@ def wvc_causal_conv3d_workspace_bytes(d: ConvDesc) -> int:
     return v
 
 
-def wvc_conv3d_packed_weight_bytes(w_shape, dtype=torch.bfloat16, padding=(1, 1)) -> int:
-    d = conv_desc((1, w_shape[1], 1, 1, 1), tuple(w_shape), _dtype_code(dtype), padding=padding)
+def wvc_conv3d_packed_weight_bytes(w_shape, dtype=torch.bfloat16, padding=(1, 1), stride=(1, 1, 1),
+                                   pad_extra=(0, 0)) -> int:
+    # the packed order depends on the channels and the kernel only; the
+    # descriptor needs some frame the kernel fits in
+    d = conv_desc((1, w_shape[1], 1, 16, 16), tuple(w_shape), _dtype_code(dtype), stride=stride,
+                  padding=padding, pad_extra=pad_extra)
     v = load().wvc_conv3d_packed_weight_bytes(ctypes.byref(d))
     if v == ctypes.c_size_t(-1).value:
         raise WvcError(WVC_ERR_UNSUPPORTED, load().wvc_last_error().decode())
     return v
 
 
-def wvc_conv3d_pack_weights(weight: torch.Tensor, padding=(1, 1)) -> torch.Tensor:
+def wvc_conv3d_pack_weights(weight: torch.Tensor, padding=(1, 1), stride=(1, 1, 1),
+                            pad_extra=(0, 0)) -> torch.Tensor:
     """Weights [C_out, C_in, kT, kH, kW] (channels_last_3d) -> their packed MFMA
     fragment order (a flat uint8 device tensor), for calls with
     weight_layout=WVC_WEIGHT_PACKED (see wvc_conv3d_pack_weights in
     include/wvc.h)."""
     _need_cl(weight, "weight")
     shape = tuple(weight.shape)
-    d = conv_desc((1, shape[1], 1, 1, 1), shape, _dtype_code(weight.dtype), padding=padding)
-    packed = torch.empty(wvc_conv3d_packed_weight_bytes(shape, weight.dtype, padding),
+    d = conv_desc((1, shape[1], 1, 16, 16), shape, _dtype_code(weight.dtype), stride=stride,
+                  padding=padding, pad_extra=pad_extra)
+    packed = torch.empty(wvc_conv3d_packed_weight_bytes(shape, weight.dtype, padding, stride,
+                                                        pad_extra),
                          dtype=torch.uint8, device=weight.device)
     _check(load().wvc_conv3d_pack_weights(ctypes.byref(d), _ptr(weight), _ptr(packed),
                                           _stream(weight)))

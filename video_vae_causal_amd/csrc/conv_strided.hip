@@ -26,7 +26,8 @@
 //     output columns, input columns 2 apart) hit consecutive slots.
 // The rows are padded to an odd number of 16-byte entries, so those reads
 // land in distinct LDS banks.  The weights stream from L2 as 16x16x32 MFMA A
-// fragments, two K-steps ahead.  Waves split output channels x positions:
+// fragments, several K-steps ahead: a K-step is only FCO x FPOS MFMAs, far
+// shorter than an L2 round trip.  Waves split output channels x positions:
 // WCO groups of FCO 16-channel blocks times 4/WCO groups of FPOS 16-position
 // blocks.
 #include <type_traits>
@@ -41,8 +42,26 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int BATCH = 16;              // staging loads in flight per thread
+constexpr int BATCH = 20;              // staging loads in flight per thread (one batch at C_in = 96)
 constexpr size_t LDS_MAX = 80 * 1024;  // two workgroups per CU
+
+template <int I>
+using Int = std::integral_constant<int, I>;
+
+template <int N, int I = 0, typename F>
+__device__ __forceinline__ void static_for(F &&f) {
+    if constexpr (I < N) {
+        f(Int<I>{});
+        static_for<N, I + 1>(f);
+    }
+}
+
+// q / d for 0 <= q < 2^15 and d >= 1, exactly: q + 0.5 is exact in fp32 and
+// the rounded product is within (q + 0.5)/d * 2^-23 < 2^-8/d of (q + 0.5)/d,
+// which lies at least 0.5/d away from every integer.
+__device__ __forceinline__ int div_small(int q, float inv_d) {
+    return (int)(((float)q + 0.5f) * inv_d);
+}
 
 struct SParams {
     const uint16_t *x, *cache, *wp, *bias, *res;
@@ -66,6 +85,12 @@ __device__ __forceinline__ uint4 wload(__amdgpu_buffer_rsrc_t r, uint32_t off) {
 template <int MODE, int PT, int FCO, int FPOS, int WCO>
 __global__ void __launch_bounds__(256) strided_kernel(SParams p) {
     static_assert(FPOS * 16 * (4 / WCO) == PT, "position groups must tile the run");
+    // A-fragment register sets = K-steps in flight.  The K-step count is
+    // taps x C_in/32, a multiple of the tap count, so NS = taps divides it:
+    // the K loop body then has no bounds checks, and the compiler's wait
+    // counts stay exact across iterations instead of draining every load at
+    // the loop head.
+    constexpr int NS = MODE == 0 ? 3 : 9;
     extern __shared__ uint4 xs[];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -103,69 +128,70 @@ __global__ void __launch_bounds__(256) strided_kernel(SParams p) {
         }
         const int ke = p.nb * 4;  // 16-byte chunks per position
         const int total = PT * ke;
+        const float inv_ke = 1.0f / (float)ke, inv_c8 = 1.0f / (float)c8;
         for (int base = 0; base < total; base += 256 * BATCH) {
             uint4 v[BATCH];
+            int dst[BATCH];
 #pragma unroll
             for (int k = 0; k < BATCH; ++k) {
                 const int q = base + tid + 256 * k;
-                const int r = q / ke, e = q - r * ke;
-                const int kt = e / c8, ch = e - kt * c8;
+                const int r = div_small(q, inv_ke), e = q - r * ke;
+                const int kt = div_small(e, inv_c8), ch = e - kt * c8;
+                const uint16_t *sp = kt == 0 ? src[0] : (kt == 1 ? src[1] : src[2]);
                 v[k] = make_uint4(0u, 0u, 0u, 0u);
-                if (q < total && r < np && src[kt])
-                    v[k] = *reinterpret_cast<const uint4 *>(src[kt] + (size_t)(q0 + r) * p.cin + ch * 8);
+                dst[k] = q < total ? r * p.pitch + e : -1;
+                if (q < total && r < np && sp)
+                    v[k] = *reinterpret_cast<const uint4 *>(sp + (size_t)(q0 + r) * p.cin + ch * 8);
             }
 #pragma unroll
-            for (int k = 0; k < BATCH; ++k) {
-                const int q = base + tid + 256 * k;
-                const int r = q / ke, e = q - r * ke;
-                if (q < total) xs[r * p.pitch + e] = v[k];
-            }
+            for (int k = 0; k < BATCH; ++k)
+                if (dst[k] >= 0) xs[dst[k]] = v[k];
         }
     } else {
         const uint16_t *fp = p.x + ((size_t)n * p.t + j) * frame;  // spatial: t_out == t
         constexpr int NC = 2 * PT + 1;                              // input columns
         const int total = 3 * NC * c8;
         const int col0 = 2 * q0 - p.pw;
+        const float inv_c8 = 1.0f / (float)c8, inv_nc = 1.0f / (float)NC;
         for (int base = 0; base < total; base += 256 * BATCH) {
             uint4 v[BATCH];
+            int dst[BATCH];
 #pragma unroll
             for (int k = 0; k < BATCH; ++k) {
                 const int q = base + tid + 256 * k;
-                const int ch = q % c8, rest = q / c8;
-                const int cc = rest % NC, kh = rest / NC;
+                const int rest = div_small(q, inv_c8), ch = q - rest * c8;
+                const int kh = div_small(rest, inv_nc), cc = rest - kh * NC;
                 const int hs = 2 * oh - p.ph + kh, ws = col0 + cc;
+                const int slot = (cc & 1) ? PT + 1 + (cc >> 1) : (cc >> 1);
                 v[k] = make_uint4(0u, 0u, 0u, 0u);
+                dst[k] = q < total ? (kh * NC + slot) * p.pitch + ch : -1;
                 if (q < total && hs >= 0 && hs < p.h && ws >= 0 && ws < p.w)
                     v[k] = *reinterpret_cast<const uint4 *>(fp + ((size_t)hs * p.w + ws) * p.cin + ch * 8);
             }
 #pragma unroll
-            for (int k = 0; k < BATCH; ++k) {
-                const int q = base + tid + 256 * k;
-                const int ch = q % c8, rest = q / c8;
-                const int cc = rest % NC, kh = rest / NC;
-                const int slot = (cc & 1) ? PT + 1 + (cc >> 1) : (cc >> 1);
-                if (q < total) xs[(kh * NC + slot) * p.pitch + ch] = v[k];
-            }
+            for (int k = 0; k < BATCH; ++k)
+                if (dst[k] >= 0) xs[dst[k]] = v[k];
         }
     }
 
     // ---- weights: packed [K-step][16-row block][lane] 1 KiB fragments
     const __amdgpu_buffer_rsrc_t wr =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(p.wp), (short)0, (int)p.w_bytes, 0x00020000);
-    bf16x8 A[3][FCO];
-    auto load_a = [&](int set, int ks) {
+    bf16x8 A[NS][FCO];
+    auto load_a = [&](auto set_tag, int ks) {
+        constexpr int SET = decltype(set_tag)::value;
 #pragma unroll
         for (int f = 0; f < FCO; ++f) {
             const int blk = wc * FCO + f;
             const int bc = blk < nblk ? blk : 0;  // surplus blocks read block 0, never stored
-            const uint32_t off = (uint32_t)((ks * nblk + bc) * 1024 + lane * 16);
-            if (set == 0) A[0][f] = as_bf16x8(wload(wr, off));
-            else if (set == 1) A[1][f] = as_bf16x8(wload(wr, off));
-            else A[2][f] = as_bf16x8(wload(wr, off));
+            A[SET][f] = as_bf16x8(wload(wr, (uint32_t)((ks * nblk + bc) * 1024 + lane * 16)));
         }
     };
-    load_a(0, 0);
-    load_a(1, p.nb > 1 ? 1 : 0);
+    // K-steps 0 .. NS-2 in flight before the first MFMA.
+    static_for<NS - 1>([&](auto i) {
+        constexpr int I = decltype(i)::value;
+        load_a(i, I < p.nb ? I : p.nb - 1);
+    });
 
     f32x4 acc[FCO][FPOS];
 #pragma unroll
@@ -185,22 +211,31 @@ __global__ void __launch_bounds__(256) strided_kernel(SParams p) {
         const int slot = kw == 1 ? PT + 1 + pp : pp + (kw >> 1);
         return (kh * (2 * PT + 1) + slot) * p.pitch + cb * 4 + lg;
     };
-    auto kstep = [&](auto set_tag, int ks) {
-        constexpr int SET = decltype(set_tag)::value;
-        load_a((SET + 2) % 3, ks + 2 < p.nb ? ks + 2 : p.nb - 1);
-        bf16x8 B[FPOS];
+    // K-step ks uses set ks % NS and first refills the set of K-step ks-1
+    // (whose MFMAs are issued) with K-step ks + NS - 1 (clamped at the end:
+    // the surplus loads are never used).
+    // The B fragments of K-step ks+1 are read from LDS (into one of three
+    // sets) before the MFMAs of ks, so the LDS latency hides behind them.
+    bf16x8 B[3][FPOS];
 #pragma unroll
-        for (int b = 0; b < FPOS; ++b) B[b] = as_bf16x8(xs[b_entry(ks, b)]);
+    for (int b = 0; b < FPOS; ++b) B[0][b] = as_bf16x8(xs[b_entry(0, b)]);
+    for (int ks0 = 0; ks0 < p.nb; ks0 += NS) {
+        static_for<NS>([&](auto i) {
+            constexpr int SET = decltype(i)::value;
+            constexpr int BS = SET % 3, BN = (SET + 1) % 3;
+            const int ks = ks0 + SET;
+            const int nxt = ks + NS - 1 < p.nb ? ks + NS - 1 : p.nb - 1;
+            load_a(Int<(SET + NS - 1) % NS>{}, nxt);
+            const int kb = ks + 1 < p.nb ? ks + 1 : ks;
 #pragma unroll
-        for (int b = 0; b < FPOS; ++b)
+            for (int b = 0; b < FPOS; ++b) B[BN][b] = as_bf16x8(xs[b_entry(kb, b)]);
 #pragma unroll
-            for (int f = 0; f < FCO; ++f)
-                acc[f][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[SET][f], B[b], acc[f][b], 0, 0, 0);
-    };
-    for (int ks = 0; ks < p.nb; ks += 3) {
-        kstep(std::integral_constant<int, 0>{}, ks);
-        if (ks + 1 < p.nb) kstep(std::integral_constant<int, 1>{}, ks + 1);
-        if (ks + 2 < p.nb) kstep(std::integral_constant<int, 2>{}, ks + 2);
+            for (int b = 0; b < FPOS; ++b)
+#pragma unroll
+                for (int f = 0; f < FCO; ++f)
+                    acc[f][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[SET][f], B[BS][b], acc[f][b], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+        });
     }
 
     // ---- epilogue: element e of tile (f, b) is channel blk*16 + lg*4 + e at
