@@ -333,6 +333,86 @@ def decoder_stack(latent, p: dict, bf16: bool = False, eps=DEFAULT_EPS):
     return h
 
 
+def tile_origins(size: int, tile: int, stride: int) -> list:
+    """Start offsets of overlapping tiles along one axis ("VSR Hover
+    Comparison", the decoder-tiling paragraph: tile_size (60, 104) with
+    tile_stride (30, 52) on the latent).  Reading (the page gives size and
+    stride only): tiles start at 0, stride, 2*stride, ... while they fit, and
+    one more tile is aligned to the far edge if the last one stops short of
+    it; a frame no larger than the tile is one tile."""
+    if size <= tile:
+        return [0]
+    starts = list(range(0, size - tile + 1, stride))
+    if starts[-1] + tile < size:
+        starts.append(size - tile)
+    return starts
+
+
+def ramp_weights(length: int, ramp_lo: int, ramp_hi: int) -> np.ndarray:
+    """Per-pixel blend weight along one axis of a tile of ``length`` output
+    pixels ("VSR Hover Comparison": tiles are fused with complementary linear
+    ramp weights).  Over the ``ramp_lo`` pixels it shares with the previous
+    tile the weight rises as (i + 1/2) / ramp_lo; over the ``ramp_hi`` pixels it
+    shares with the next tile it falls as (length - i - 1/2) / ramp_hi;
+    elsewhere it is 1.  Across one overlap the two tiles' weights sum to 1."""
+    i = np.arange(length, dtype=np.float64)
+    w = np.ones(length)
+    if ramp_lo > 0:
+        w = np.where(i < ramp_lo, (i + 0.5) / ramp_lo, w)
+    if ramp_hi > 0:
+        w = np.where(i >= length - ramp_hi, w * (length - i - 0.5) / ramp_hi, w)
+    return w
+
+
+def blend_tiles(tiles, origins, out_hw, scale: int = 1) -> np.ndarray:
+    """Blend overlapping output tiles into one frame: each tile [N, C, T, h, w]
+    at latent origin (y0, x0) covers output rows scale*y0 ... of ``out_hw``;
+    its weight is the product of the row and column ramps over the overlaps
+    with its neighbours (overlap lengths taken from the other origins); the
+    result is sum(weight * tile) / sum(weight) per output pixel."""
+    H, W = out_hw
+    ys = sorted({o[0] for o in origins})
+    xs = sorted({o[1] for o in origins})
+    first = np.asarray(tiles[0])
+    N, C, T = first.shape[:3]
+    acc = np.zeros((N, C, T, H, W))
+    wsum = np.zeros((H, W))
+    for tile, (y0, x0) in zip(tiles, origins):
+        tile = np.asarray(tile, dtype=np.float64)
+        h, w = tile.shape[3:]
+        oy, ox = scale * y0, scale * x0
+        iy, ix = ys.index(y0), xs.index(x0)
+        # overlaps (output pixels) with the neighbouring tiles on each side
+        top = (scale * ys[iy - 1] + h) - oy if iy > 0 else 0
+        bottom = (oy + h) - scale * ys[iy + 1] if iy + 1 < len(ys) else 0
+        left = (scale * xs[ix - 1] + w) - ox if ix > 0 else 0
+        right = (ox + w) - scale * xs[ix + 1] if ix + 1 < len(xs) else 0
+        if min(top, bottom, left, right) < 0:
+            raise ValueError("tiles leave a gap: the stride must not exceed the tile")
+        wgt = np.outer(ramp_weights(h, top, bottom), ramp_weights(w, left, right))
+        acc[:, :, :, oy:oy + h, ox:ox + w] += wgt * tile
+        wsum[oy:oy + h, ox:ox + w] += wgt
+    return acc / wsum
+
+
+def tiled_decoder_stack(latent, p: dict, tile=(60, 104), stride=(30, 52), bf16: bool = False,
+                        eps=DEFAULT_EPS):
+    """Decode ``latent`` tile by tile ("VSR Hover Comparison": spatial tiles of
+    the latent, each decoded on its own, fused with ramp weights): every tile
+    goes through :func:`decoder_stack` over all frames from zero caches, and
+    the 2x-upsampled outputs are blended with :func:`blend_tiles`.  With
+    ``bf16`` each tile's output is rounded as stored and the blend result is
+    rounded once."""
+    latent = _f64(latent)
+    N, C, T, H, W = latent.shape
+    th, tw = min(tile[0], H), min(tile[1], W)
+    origins = [(y, x) for y in tile_origins(H, th, stride[0]) for x in tile_origins(W, tw, stride[1])]
+    outs = [decoder_stack(latent[:, :, :, y:y + th, x:x + tw], p, bf16=bf16, eps=eps)
+            for y, x in origins]
+    y = blend_tiles(outs, origins, (2 * H, 2 * W), scale=2)
+    return _maybe_round(y, bf16)
+
+
 def rel_l2(y, ref) -> float:
     """||y - ref||_2 / ||ref||_2 in fp64."""
     y = np.asarray(y, dtype=np.float64)
