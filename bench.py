@@ -49,7 +49,11 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="resblock_384_60x104",
                     choices=sorted(["resblock_384_60x104", "layer_384_240x416", "layer_96_480x832",
-                                    "decoder_stack_48_30x52", "downsample_96_480x832"]))
+                                    "decoder_stack_48_30x52", "downsample_96_480x832",
+                                    "decoder_tiled_192x336"]))
+    ap.add_argument("--tiling", choices=sorted(TILINGS), default="page",
+                    help="decoder_tiled_192x336: the page's (60,104)/(30,52) tiles, a reduced "
+                         "overlap (stride (52,96)), or no tiling")
     ap.add_argument("--kernel-reps", type=int, default=50,
                     help="launches of the dominant kernel timed for the roofline")
     ap.add_argument("--warmup-seconds", type=float, default=0.5,
@@ -360,9 +364,69 @@ def wl_downsample():
     return step, info
 
 
+TILINGS = {"page": ((60, 104), (30, 52)), "reduced": ((60, 104), (52, 96)), "untiled": (None, None)}
+TILING = "page"  # set from --tiling in main()
+
+
+def wl_tiled():
+    """Tiled decode ("VSR Hover Comparison", decoder tiling): the decoder-shaped
+    stack on a 192x336 latent (a 2688x1536 video's latent at 8x), 3 frames,
+    in (60, 104) latent tiles at the page's stride (30, 52) -- 50 % overlap --
+    or a reduced stride, or untiled; tiles blended with linear ramps."""
+    import torch
+    from video_vae_causal_amd import _lib as L, accounting as acc, inputs, stream
+    d = inputs.decoder_inputs(seed=8, shape=(1, 48, 3, 192, 336))
+    n, cl_, t, h, w = d["latent"].shape
+    width = d["p"]["w_in"].shape[0]
+    lat = to_dev(d["latent"])
+    p = {k: ({kk: to_dev(vv) for kk, vv in v.items()} if isinstance(v, dict) else to_dev(v))
+         for k, v in d["p"].items()}
+    stack = stream.DecoderStack(p)
+    tile, stride = TILINGS[TILING]
+    if tile is None:
+        def step():
+            stack.run(lat, chunk_frames=1)
+        tiles, th, tw = 1, h, w
+    else:
+        td = stream.TiledDecode(stack, tile=tile, stride=stride)
+        th, tw, ys, xs = td.origins(h, w)
+        tiles = len(ys) * len(xs)
+
+        def step():
+            td.run(lat, chunk_frames=1)
+
+    def per_frame(hh, ww):
+        return (acc.conv_flops(n, 1, hh, ww, cl_, width) + 4 * acc.conv_flops(n, 1, hh, ww, width, width)
+                + 5 * acc.conv_flops(n, 1, 2 * hh, 2 * ww, width, width))
+
+    # the dominant kernel: the 3x3x3 conv on one decoded tile frame at 2x
+    kx = cl(torch.randn((n, width, 1, 2 * th, 2 * tw), device="cuda").to(torch.bfloat16))
+    ky = L.empty_cl(kx.shape)
+    cache = L.empty_cl((n, width, 2, 2 * th, 2 * tw))
+    L.wvc_cache_reset(cache)
+    kws = conv_workspace(kx, p["w_up"], packed=True)
+    wup = L.wvc_conv3d_pack_weights(p["w_up"])
+
+    def kernel():
+        L.wvc_causal_conv3d_fwd(kx, p["w_up"], p["b_up"], cache, None, None, ky, workspace=kws,
+                                packed_weight=wup)
+
+    info = dict(workload="decoder_tiled_192x336", conv_flops=tiles * t * per_frame(th, tw),
+                latent_frames=t,
+                config={"workload": "decoder_tiled_192x336", "latent_channels": cl_, "channels": width,
+                        "frames": t, "height": h, "width": w, "tiling": TILING,
+                        "tile": list(tile) if tile else None, "stride": list(stride) if stride else None,
+                        "tiles": tiles, "decoded_latent_px_per_px": round(tiles * th * tw / (h * w), 3),
+                        "chunk_frames": 1, "batch": n},
+                kernel=kernel, kernel_name="igemm_kernel<3, 128, 32, 2, *, *> (conv at 2x tile)",
+                kernel_units=acc.conv_flops(n, 1, 2 * th, 2 * tw, width, width), kernel_bound="mfma",
+                kernel_bytes=acc.conv_launch_bytes(n, 1, 2 * th, 2 * tw, width, width))
+    return step, info
+
+
 WORKLOADS = {"resblock_384_60x104": wl_resblock, "layer_384_240x416": wl_layer384,
              "layer_96_480x832": wl_layer96, "decoder_stack_48_30x52": wl_decoder,
-             "downsample_96_480x832": wl_downsample}
+             "downsample_96_480x832": wl_downsample, "decoder_tiled_192x336": wl_tiled}
 
 
 # ---------------------------------------------------------------------------
@@ -397,6 +461,19 @@ def cpu_baseline(workload: str):
         oracle.resblock(x, p, past, past, bf16=True)
         dt = time.perf_counter() - t0
         sample = "1 of 5 latent frames (frame 2, non-zero caches) through the block"
+    elif workload == "decoder_tiled_192x336":
+        d = inputs.decoder_inputs(seed=8, shape=(1, 48, 3, 192, 336), with_latent_window=(30, 52))
+        lat = d["latent"][:, :, :1].astype(np.float64)
+        p = {k: ({kk: vv.astype(np.float64) for kk, vv in v.items()} if isinstance(v, dict)
+                 else v.astype(np.float64)) for k, v in d["p"].items()}
+        n, cl_, t, h, w = lat.shape
+        width = p["w_in"].shape[0]
+        flops = (acc.conv_flops(n, 1, h, w, cl_, width) + 4 * acc.conv_flops(n, 1, h, w, width, width)
+                 + 5 * acc.conv_flops(n, 1, 2 * h, 2 * w, width, width))
+        t0 = time.perf_counter()
+        oracle.decoder_stack(lat, p, bf16=True)
+        dt = time.perf_counter() - t0
+        sample = "latent frame 0, the 30x52 top-left window, through the whole stack"
     elif workload == "downsample_96_480x832":
         d = inputs.downsample_inputs()
         xs = d["x"][:, :, :4].astype(np.float64)   # frames 0..3 (one 4-frame chunk)
@@ -483,8 +560,9 @@ def main():
     L.load()
     torch.cuda.set_device(0)
 
-    global PIPELINE
+    global PIPELINE, TILING
     PIPELINE = args.pipeline == "on"
+    TILING = args.tiling
     step, info = WORKLOADS[args.workload]()
     timed = step
     if args.graph == "on":

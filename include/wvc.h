@@ -9,6 +9,8 @@
  *        (devpress.csdn.net), sections 8.5, 10.1-10.4.
  *   [P3] "cache-aware video decoder lowering" (rit.work), section on turning
  *        Conv3D into batched Conv2D.
+ *   [P5] "VSR Hover Comparison" (vsr-hover-compare.pages.dev), the
+ *        decoder-tiling paragraph.
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -266,6 +268,41 @@ int wvc_cache_reset(void *cache, size_t bytes, void *stream);
  */
 int wvc_upsample_nearest2x(const void *x, void *y, int n, int c, int t, int h, int w, int dtype,
                            void *stream);
+
+/*
+ * Spatial tiling with overlap blending ([P5] "VSR Hover Comparison", the
+ * decoder-tiling paragraph: the latent is decoded in overlapping spatial
+ * tiles, (60, 104) at stride (30, 52) there, and the decoded tiles are fused
+ * with complementary linear-ramp weights).  A caller extracts each latent tile,
+ * decodes it through the stack (its own caches, all frames), blends the
+ * decoded tile into an fp32 accumulator, and finishes once all tiles are in.
+ *
+ * wvc_tile_extract: tile[n, c, t, i, j] = x[n, c, t, y0 + i, x0 + j] for
+ *   i < th, j < tw.  x [N, C, T, H, W], tile [N, C, T, th, tw]; the window must
+ *   lie inside the frame.
+ * wvc_tile_blend: for i < th, j < tw, with w = wy(i) * wx(j):
+ *   acc[n, c, t, y0 + i, x0 + j] += w * tile[n, c, t, i, j] and
+ *   wsum[y0 + i, x0 + j] += w.  Along an axis of length L the weight is
+ *   (i + 1/2)/lo over the lo = ramp_top (ramp_left) pixels shared with the
+ *   previous tile, times (L - i - 1/2)/hi over the hi = ramp_bottom
+ *   (ramp_right) pixels shared with the next tile, else 1 (a tile's two ramps
+ *   may meet).  tile [N, C, T, th, tw] in the call's dtype; acc fp32
+ *   [N, C, T, H, W] channels-last; wsum fp32 [H, W]; both zeroed by the
+ *   caller (wvc_cache_reset) before the first tile.  C % 4 == 0; ramps in
+ *   [0, th] / [0, tw]; the tile must lie inside [H, W].
+ * wvc_tile_blend_finish: y = acc / wsum per position, rounded once to the
+ *   dtype; every position must have been covered (wsum > 0).
+ * All three only enqueue work; tiles blended into one accumulator must be
+ * enqueued in order on one stream.  Written buffers may not overlap the
+ * others (WVC_ERR_ALIAS).
+ */
+int wvc_tile_extract(const void *x, void *tile, int n, int c, int t, int h, int w, int y0, int x0,
+                     int th, int tw, int dtype, void *stream);
+int wvc_tile_blend(const void *tile, float *acc, float *wsum, int n, int c, int t, int th, int tw,
+                   int h, int w, int y0, int x0, int ramp_top, int ramp_bottom, int ramp_left,
+                   int ramp_right, int dtype, void *stream);
+int wvc_tile_blend_finish(const float *acc, const float *wsum, void *y, int n, int c, int t, int h,
+                          int w, int dtype, void *stream);
 
 /* Strict mode ([P3]: a strict mode stops on an unexpected fallback): when on,
  * a call that would take the generic route fails with WVC_ERR_STRICT.

@@ -272,3 +272,24 @@ def test_graph_calls_reject_bad_arguments_without_touching_the_gpu(lib):
     assert lib.wvc_graph_capture_end(ctypes.c_void_p(0x1000), None) == L.WVC_ERR_ARG
     assert lib.wvc_graph_launch(None, None) == L.WVC_ERR_ARG
     assert lib.wvc_graph_destroy(None) == L.WVC_OK
+
+
+def test_tiling_validation(lib):
+    A, WS_, T = 0x70000000, 0x78000000, 0x7c000000
+    # window outside the frame, bad dtype, aliasing
+    assert lib.wvc_tile_extract(X, Y, 1, 8, 1, 16, 16, 10, 0, 8, 8, L.WVC_BF16, None) == L.WVC_ERR_ARG
+    assert lib.wvc_tile_extract(X, Y, 1, 8, 1, 16, 16, 0, 0, 8, 8, 9, None) == L.WVC_ERR_UNSUPPORTED
+    assert lib.wvc_tile_extract(X, X, 1, 8, 1, 16, 16, 0, 0, 8, 8, L.WVC_BF16, None) == L.WVC_ERR_ALIAS
+    # blend: C % 4, ramps beyond the tile, tile outside the output, aliasing acc/wsum
+    assert lib.wvc_tile_blend(T, A, WS_, 1, 6, 1, 8, 8, 16, 16, 0, 0, 0, 0, 0, 0, L.WVC_BF16, None) == L.WVC_ERR_ARG
+    assert lib.wvc_tile_blend(T, A, WS_, 1, 8, 1, 8, 8, 16, 16, 0, 0, 9, 0, 0, 0, L.WVC_BF16, None) == L.WVC_ERR_ARG
+    assert lib.wvc_tile_blend(T, A, WS_, 1, 8, 1, 8, 8, 16, 16, 12, 0, 0, 0, 0, 0, L.WVC_BF16, None) == L.WVC_ERR_ARG
+    assert lib.wvc_tile_blend(T, A, A + 64, 1, 8, 1, 8, 8, 16, 16, 0, 0, 0, 0, 0, 0, L.WVC_BF16, None) == L.WVC_ERR_ALIAS
+    assert lib.wvc_tile_blend_finish(A, WS_, A, 1, 8, 1, 16, 16, L.WVC_BF16, None) == L.WVC_ERR_ALIAS
+    assert lib.wvc_tile_blend_finish(A, WS_, Y, 1, 6, 1, 16, 16, L.WVC_BF16, None) == L.WVC_ERR_ARG
+    assert stream_origins() == [[0, 30, 60], [0, 52, 104], [0]]
+
+
+def stream_origins():
+    from video_vae_causal_amd import stream
+    return [stream.tile_origins(120, 60, 30), stream.tile_origins(208, 104, 52), stream.tile_origins(40, 60, 30)]

@@ -36,6 +36,7 @@ EXPORTED = (
     "wvc_upsample_nearest2x", "wvc_set_strict", "wvc_get_strict", "wvc_get_counters",
     "wvc_reset_counters", "wvc_last_error", "wvc_version", "wvc_graph_capture_begin",
     "wvc_graph_capture_end", "wvc_graph_launch", "wvc_graph_destroy",
+    "wvc_tile_extract", "wvc_tile_blend", "wvc_tile_blend_finish",
 )
 
 
@@ -120,6 +121,12 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.wvc_last_error.restype = ctypes.c_char_p
     lib.wvc_version.argtypes = []
     lib.wvc_version.restype = ctypes.c_char_p
+    lib.wvc_tile_extract.argtypes = [vp, vp] + [i] * 10 + [vp]
+    lib.wvc_tile_extract.restype = i
+    lib.wvc_tile_blend.argtypes = [vp, vp, vp] + [i] * 14 + [vp]
+    lib.wvc_tile_blend.restype = i
+    lib.wvc_tile_blend_finish.argtypes = [vp, vp, vp] + [i] * 6 + [vp]
+    lib.wvc_tile_blend_finish.restype = i
     lib.wvc_graph_capture_begin.argtypes = [vp]
     lib.wvc_graph_capture_begin.restype = i
     lib.wvc_graph_capture_end.argtypes = [vp, ctypes.POINTER(vp)]
@@ -531,3 +538,56 @@ def wvc_graph_launch(graph: Graph, stream: Optional[torch.cuda.Stream] = None):
 
 def wvc_graph_destroy(graph: Graph):
     graph.close()
+
+
+# ---------------------------------------------------------------------------
+# Spatial tiling with overlap blending (wvc_tile_* in include/wvc.h)
+# ---------------------------------------------------------------------------
+
+def wvc_tile_extract(x: torch.Tensor, y0: int, x0: int, th: int, tw: int,
+                     tile: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """tile = x[:, :, :, y0:y0+th, x0:x0+tw] as a channels-last tensor."""
+    _need_cl(x, "x")
+    n, c, t, h, w = x.shape
+    if tile is None:
+        tile = empty_cl((n, c, t, th, tw), x.dtype, x.device)
+    _need_cl(tile, "tile")
+    _check(load().wvc_tile_extract(_ptr(x), _ptr(tile), n, c, t, h, w, y0, x0, th, tw,
+                                   _dtype_code(x.dtype), _stream(x)))
+    return tile
+
+
+def blend_accumulators(like: torch.Tensor, h: int, w: int):
+    """Zeroed fp32 accumulator [N, C, T, h, w] (channels-last) and weight sum [h, w]."""
+    n, c, t = like.shape[:3]
+    acc = empty_cl((n, c, t, h, w), torch.float32, like.device)
+    wsum = torch.empty((h, w), dtype=torch.float32, device=like.device)
+    wvc_cache_reset(acc)
+    _check(load().wvc_cache_reset(_ptr(wsum), wsum.numel() * 4, _stream(like)))
+    return acc, wsum
+
+
+def wvc_tile_blend(tile: torch.Tensor, acc: torch.Tensor, wsum: torch.Tensor, y0: int, x0: int,
+                   ramps=(0, 0, 0, 0)):
+    """acc += w * tile at (y0, x0), wsum += w; ramps = (top, bottom, left, right)."""
+    _need_cl(tile, "tile")
+    _need_cl(acc, "acc")
+    n, c, t, th, tw = tile.shape
+    h, w = acc.shape[3:]
+    if acc.dtype != torch.float32 or wsum.dtype != torch.float32 or tuple(wsum.shape) != (h, w):
+        raise ValueError("acc and wsum must be fp32, wsum [H, W]")
+    _check(load().wvc_tile_blend(_ptr(tile), _ptr(acc), _ptr(wsum), n, c, t, th, tw, h, w, y0, x0,
+                                 *ramps, _dtype_code(tile.dtype), _stream(tile)))
+
+
+def wvc_tile_blend_finish(acc: torch.Tensor, wsum: torch.Tensor, dtype=torch.bfloat16,
+                          y: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """y = acc / wsum, rounded once to ``dtype``."""
+    _need_cl(acc, "acc")
+    n, c, t, h, w = acc.shape
+    if y is None:
+        y = empty_cl((n, c, t, h, w), dtype, acc.device)
+    _need_cl(y, "y")
+    _check(load().wvc_tile_blend_finish(_ptr(acc), _ptr(wsum), _ptr(y), n, c, t, h, w,
+                                        _dtype_code(y.dtype), _stream(acc)))
+    return y

@@ -618,6 +618,70 @@ int wvc_upsample_nearest2x(const void *x, void *y, int n, int c, int t, int h, i
         "upsample launch");
 }
 
+int wvc_tile_extract(const void *x, void *tile, int n, int c, int t, int h, int w, int y0, int x0,
+                     int th, int tw, int dtype, void *stream) {
+    const int e = elem_bytes(dtype);
+    if (!e) return fail(WVC_ERR_UNSUPPORTED, "dtype %d is neither WVC_F32 nor WVC_BF16", dtype);
+    if (n < 1 || c < 1 || t < 0 || h < 1 || w < 1 || th < 1 || tw < 1 || y0 < 0 || x0 < 0 ||
+        y0 + th > h || x0 + tw > w)
+        return fail(WVC_ERR_ARG, "tile window %dx%d at (%d, %d) outside the %dx%d frame", th, tw, y0,
+                    x0, h, w);
+    const long planes = (long)n * t;
+    if (planes > 0 && (!x || !tile)) return fail(WVC_ERR_ARG, "x or tile is NULL");
+    const Buf bufs[] = {{x, (size_t)planes * h * w * c * e, false, "x"},
+                        {tile, (size_t)planes * th * tw * c * e, true, "tile"}};
+    int rc = check_aliasing(bufs, 2);
+    if (rc) return rc;
+    return hip_status(wvc::launch_tile_extract(x, tile, planes, h, w, y0, x0, th, tw, c, e,
+                                               static_cast<hipStream_t>(stream)),
+                      "tile extract launch");
+}
+
+int wvc_tile_blend(const void *tile, float *acc, float *wsum, int n, int c, int t, int th, int tw,
+                   int h, int w, int y0, int x0, int ramp_top, int ramp_bottom, int ramp_left,
+                   int ramp_right, int dtype, void *stream) {
+    const int e = elem_bytes(dtype);
+    if (!e) return fail(WVC_ERR_UNSUPPORTED, "dtype %d is neither WVC_F32 nor WVC_BF16", dtype);
+    if (n < 1 || c < 1 || c % 4 != 0 || t < 0 || h < 1 || w < 1 || th < 1 || tw < 1 || y0 < 0 ||
+        x0 < 0 || y0 + th > h || x0 + tw > w)
+        return fail(WVC_ERR_ARG, "bad tile blend shape (C %% 4 == 0, tile inside the frame)");
+    if (ramp_top < 0 || ramp_bottom < 0 || ramp_left < 0 || ramp_right < 0 || ramp_top > th ||
+        ramp_bottom > th || ramp_left > tw || ramp_right > tw)
+        return fail(WVC_ERR_ARG, "ramps must lie in [0, tile size]");
+    const long planes = (long)n * t;
+    if (planes > 0 && (!tile || !acc || !wsum)) return fail(WVC_ERR_ARG, "tile, acc or wsum is NULL");
+    if (!aligned(tile, 8) || !aligned(acc, 16) || !aligned(wsum, 4))
+        return fail(WVC_ERR_ARG, "tile blend needs 8-byte aligned tile, 16-byte aligned acc");
+    const Buf bufs[] = {{tile, (size_t)planes * th * tw * c * e, false, "tile"},
+                        {acc, (size_t)planes * h * w * c * 4, true, "acc"},
+                        {wsum, (size_t)h * w * 4, true, "wsum"}};
+    int rc = check_aliasing(bufs, 3);
+    if (rc) return rc;
+    return hip_status(wvc::launch_tile_blend(tile, acc, wsum, planes, c, th, tw, h, w, y0, x0, ramp_top,
+                                             ramp_bottom, ramp_left, ramp_right, dtype == WVC_BF16,
+                                             static_cast<hipStream_t>(stream)),
+                      "tile blend launch");
+}
+
+int wvc_tile_blend_finish(const float *acc, const float *wsum, void *y, int n, int c, int t, int h,
+                          int w, int dtype, void *stream) {
+    const int e = elem_bytes(dtype);
+    if (!e) return fail(WVC_ERR_UNSUPPORTED, "dtype %d is neither WVC_F32 nor WVC_BF16", dtype);
+    if (n < 1 || c < 1 || c % 4 != 0 || t < 0 || h < 1 || w < 1)
+        return fail(WVC_ERR_ARG, "bad tile finish shape (C %% 4 == 0)");
+    const long planes = (long)n * t;
+    if (planes > 0 && (!acc || !wsum || !y)) return fail(WVC_ERR_ARG, "acc, wsum or y is NULL");
+    if (!aligned(acc, 16) || !aligned(y, 8)) return fail(WVC_ERR_ARG, "misaligned acc or y");
+    const Buf bufs[] = {{acc, (size_t)planes * h * w * c * 4, false, "acc"},
+                        {wsum, (size_t)h * w * 4, false, "wsum"},
+                        {y, (size_t)planes * h * w * c * e, true, "y"}};
+    int rc = check_aliasing(bufs, 3);
+    if (rc) return rc;
+    return hip_status(wvc::launch_tile_finish(acc, wsum, y, planes, c, (long)h * w, dtype == WVC_BF16,
+                                              static_cast<hipStream_t>(stream)),
+                      "tile finish launch");
+}
+
 struct wvc_graph {
     hipGraph_t graph;
     hipGraphExec_t exec;

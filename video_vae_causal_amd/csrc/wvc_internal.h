@@ -119,4 +119,13 @@ hipError_t launch_upsample2x(const void *x, void *y, long planes, int h, int w, 
 
 hipError_t launch_fill_zero(void *p, size_t bytes, hipStream_t s);
 
+// Spatial tiling with overlap blending (tiling.hip).
+hipError_t launch_tile_extract(const void *x, void *y, long planes, int h, int w, int y0, int x0,
+                               int th, int tw, int c, int elem, hipStream_t s);
+hipError_t launch_tile_blend(const void *tile, float *acc, float *wsum, long planes, int c, int th,
+                             int tw, int h, int w, int y0, int x0, int rt, int rb, int rl, int rr,
+                             bool bf16, hipStream_t s);
+hipError_t launch_tile_finish(const float *acc, const float *wsum, void *y, long planes, int c,
+                              long hw, bool bf16, hipStream_t s);
+
 }  // namespace wvc

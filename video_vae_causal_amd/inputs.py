@@ -169,7 +169,10 @@ def layer384_inputs(seed: int = 4, shape=(1, 384, 17, 240, 416), cproj: int = 19
 
 
 def decoder_inputs(seed: int = 5, shape=(1, 48, 21, 30, 52), width: int = 384,
-                   dtype: str = "bf16") -> Dict:
+                   dtype: str = "bf16", with_latent_window=None) -> Dict:
+    """Decoder-stack weights and a latent of ``shape``; with
+    ``with_latent_window`` = (h, w) only the top-left h x w window of that
+    latent is returned (the same values, without generating the rest)."""
     cl = shape[1]
     p = {"w_in": conv_weight(width, cl, (3, 3, 3), seed, "w_in", dtype),
          "b_in": conv_bias(width, seed, "b_in", dtype),
@@ -177,7 +180,10 @@ def decoder_inputs(seed: int = 5, shape=(1, 48, 21, 30, 52), width: int = 384,
          "b_up": conv_bias(width, seed, "b_up", dtype)}
     for k in range(4):
         p[f"rb{k}"] = resblock_params(width, seed, f"rb{k}", dtype)
-    return {"latent": quantize(normal(shape, seed, "latent"), dtype), "p": p}
+    lat = quantize(normal(shape, seed, "latent"), dtype)
+    if with_latent_window is not None:
+        lat = np.ascontiguousarray(lat[:, :, :, :with_latent_window[0], :with_latent_window[1]])
+    return {"latent": lat, "p": p}
 
 
 def downsample_inputs(seed: int = 6, shape=(1, 96, 17, 480, 832), dtype: str = "bf16",

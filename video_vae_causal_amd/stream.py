@@ -474,3 +474,60 @@ class Pipeline:
             y.record_stream(sb)
         main.wait_stream(sa)
         main.wait_stream(sb)
+
+
+def tile_origins(size: int, tile: int, stride: int) -> List[int]:
+    """Tile starts along one axis: 0, stride, 2*stride, ... while the tile
+    fits, plus one tile aligned to the far edge if the last stops short; a
+    frame no larger than the tile is one tile."""
+    if size <= tile:
+        return [0]
+    if not 0 < stride <= tile:
+        raise ValueError("the stride must lie in (0, tile]: larger strides leave gaps")
+    starts = list(range(0, size - tile + 1, stride))
+    if starts[-1] + tile < size:
+        starts.append(size - tile)
+    return starts
+
+
+class TiledDecode:
+    """Decode a latent in overlapping spatial tiles and blend them ("VSR
+    Hover Comparison", decoder tiling: (60, 104) tiles at stride (30, 52) of
+    the latent, fused with complementary linear ramps).
+
+    Each tile is cut out of the latent (wvc_tile_extract), decoded through
+    ``stack`` over all frames from zero caches, and blended into an fp32
+    accumulator (wvc_tile_blend) with ramps over its overlaps with its
+    neighbours; wvc_tile_blend_finish divides by the weight sum and rounds
+    once.  ``scale`` is the stack's spatial upsampling factor (2 for the
+    decoder stack).  Smaller overlaps decode fewer latent pixels; the page
+    measures that trade."""
+
+    def __init__(self, stack, tile=(60, 104), stride=(30, 52), scale: int = 2):
+        self.stack = stack
+        self.tile = tuple(tile)
+        self.stride = tuple(stride)
+        self.scale = scale
+
+    def origins(self, h: int, w: int):
+        th, tw = min(self.tile[0], h), min(self.tile[1], w)
+        return th, tw, tile_origins(h, th, self.stride[0]), tile_origins(w, tw, self.stride[1])
+
+    def run(self, latent: torch.Tensor, chunk_frames: int = 1) -> torch.Tensor:
+        n, c, t, h, w = latent.shape
+        th, tw, ys, xs = self.origins(h, w)
+        s = self.scale
+        acc = wsum = None
+        for iy, y0 in enumerate(ys):
+            for ix, x0 in enumerate(xs):
+                tile = L.wvc_tile_extract(latent, y0, x0, th, tw)
+                out = self.stack.run(tile, chunk_frames=chunk_frames)
+                if acc is None:
+                    acc, wsum = L.blend_accumulators(out, s * h, s * w)
+                oh, ow = out.shape[3:]
+                top = s * (ys[iy - 1] + th - y0) if iy > 0 else 0
+                bottom = s * (y0 + th - ys[iy + 1]) if iy + 1 < len(ys) else 0
+                left = s * (xs[ix - 1] + tw - x0) if ix > 0 else 0
+                right = s * (x0 + tw - xs[ix + 1]) if ix + 1 < len(xs) else 0
+                L.wvc_tile_blend(out, acc, wsum, s * y0, s * x0, (top, bottom, left, right))
+        return L.wvc_tile_blend_finish(acc, wsum, latent.dtype)
