@@ -358,7 +358,7 @@ def wl_downsample():
                 config={"workload": "downsample_96_480x832", "channels": c, "frames": t,
                         "height": h, "width": w, "out_frames": sum(touts), "out_height": ho,
                         "out_width": wo, "chunks": sizes, "batch": n},
-                kernel=kernel, kernel_name="strided_kernel<1, 64, 3, 2, 2>",
+                kernel=kernel, kernel_name="strided_kernel<1, 64, 3, 2, 2, 12>",
                 kernel_units=k_bytes, kernel_bound="hbm", kernel_bytes=k_bytes,
                 kernel_flops=2 * 9 * c * c * 4 * ho * wo)
     return step, info

@@ -82,7 +82,22 @@ __device__ __forceinline__ uint4 wload(__amdgpu_buffer_rsrc_t r, uint32_t off) {
     return make_uint4(v.x, v.y, v.z, v.w);
 }
 
-template <int MODE, int PT, int FCO, int FPOS, int WCO>
+// Workgroup ids are dispatched round-robin over the 8 XCDs, each with its own
+// L2.  Hand XCD k the k-th contiguous slice of the logical order instead, so
+// that neighbouring runs (which share input rows: an input row feeds two
+// output rows at stride 2) are staged through the same L2.  A bijection on
+// [0, total).
+__device__ __forceinline__ long xcd_slice(long bid, long total) {
+    const long xcd = bid & 7, local = bid >> 3;
+    const long per = total >> 3, rem = total & 7;
+    const long start = xcd < rem ? xcd * (per + 1) : rem * (per + 1) + (xcd - rem) * per;
+    return start + local;
+}
+
+// C8T: C_in / 8 when known at compile time (0: read from p).  With it every
+// division of the staging and K-step index arithmetic is by a constant, and
+// the K loop's trip counts are constants; the 96-channel path uses it.
+template <int MODE, int PT, int FCO, int FPOS, int WCO, int C8T = 0>
 __global__ void __launch_bounds__(256) strided_kernel(SParams p) {
     static_assert(FPOS * 16 * (4 / WCO) == PT, "position groups must tile the run");
     // A-fragment register sets = K-steps in flight.  The K-step count is
@@ -97,10 +112,11 @@ __global__ void __launch_bounds__(256) strided_kernel(SParams p) {
     const int wc = wave % WCO, wq = wave / WCO;  // channel group, position group
     const int lr = lane & 15, lg = lane >> 4;
     const int nblk = p.cout / 16;
-    const int c8 = p.cin / 8, cbs = p.cin / 32;
+    const int c8 = C8T ? C8T : p.cin / 8, cbs = c8 / 4;
+    const int nb = C8T ? (MODE == 0 ? 3 : 9) * (C8T / 4) : p.nb;  // K-steps
 
     // Workgroup -> (n, output frame j, row / tile); MODE 1 adds the output row.
-    long L = blockIdx.x;
+    long L = xcd_slice(blockIdx.x, gridDim.x);
     const int tile = (int)(L % p.tiles);
     L /= p.tiles;
     int oh = 0;
@@ -116,7 +132,7 @@ __global__ void __launch_bounds__(256) strided_kernel(SParams p) {
     const size_t frame = (size_t)p.h * p.w * p.cin;
 
     // ---- staging
-    if (MODE == 0) {
+    if constexpr (MODE == 0) {
         // Three tapped frames of the anchor: chunk frames a-2..a, or cache.
         const int a = p.t0 + j * p.st;
         const uint16_t *src[3];
@@ -126,7 +142,7 @@ __global__ void __launch_bounds__(256) strided_kernel(SParams p) {
             src[kt] = f >= 0 ? p.x + ((size_t)n * p.t + f) * frame
                              : (p.cache ? p.cache + ((size_t)n * p.F + p.F + f) * frame : nullptr);
         }
-        const int ke = p.nb * 4;  // 16-byte chunks per position
+        const int ke = nb * 4;  // 16-byte chunks per position
         const int total = PT * ke;
         const float inv_ke = 1.0f / (float)ke, inv_c8 = 1.0f / (float)c8;
         for (int base = 0; base < total; base += 256 * BATCH) {
@@ -135,8 +151,8 @@ __global__ void __launch_bounds__(256) strided_kernel(SParams p) {
 #pragma unroll
             for (int k = 0; k < BATCH; ++k) {
                 const int q = base + tid + 256 * k;
-                const int r = div_small(q, inv_ke), e = q - r * ke;
-                const int kt = div_small(e, inv_c8), ch = e - kt * c8;
+                const int r = C8T ? q / ke : div_small(q, inv_ke), e = q - r * ke;
+                const int kt = C8T ? e / c8 : div_small(e, inv_c8), ch = e - kt * c8;
                 const uint16_t *sp = kt == 0 ? src[0] : (kt == 1 ? src[1] : src[2]);
                 v[k] = make_uint4(0u, 0u, 0u, 0u);
                 dst[k] = q < total ? r * p.pitch + e : -1;
@@ -147,6 +163,41 @@ __global__ void __launch_bounds__(256) strided_kernel(SParams p) {
             for (int k = 0; k < BATCH; ++k)
                 if (dst[k] >= 0) xs[dst[k]] = v[k];
         }
+    } else if constexpr (C8T != 0) {
+        // Constant channel count: one buffer resource per input row (bounded
+        // to the row, so columns outside the frame -- negative offsets wrap
+        // to huge ones -- and rows outside it read zero in hardware) and all
+        // 3 rows' loads in flight before the first LDS store.
+        const uint16_t *fp = p.x + ((size_t)n * p.t + j) * frame;
+        constexpr int NC = 2 * PT + 1, PER_ROW = NC * C8T, KPR = (PER_ROW + 255) / 256;
+        const int row_bytes = p.w * p.cin * 2;
+        const int col0 = 2 * q0 - p.pw;
+        uint4 v[3][KPR];
+#pragma unroll
+        for (int kh = 0; kh < 3; ++kh) {
+            const int hs = 2 * oh - p.ph + kh;
+            const bool ok = hs >= 0 && hs < p.h;
+            const __amdgpu_buffer_rsrc_t rr = __builtin_amdgcn_make_buffer_rsrc(
+                const_cast<uint16_t *>(fp + (size_t)(ok ? hs : 0) * p.w * p.cin), (short)0,
+                ok ? row_bytes : 0, 0x00020000);
+#pragma unroll
+            for (int k = 0; k < KPR; ++k) {
+                const int q = tid + 256 * k;
+                const int cc = q / C8T, ch = q - cc * C8T;
+                const int off = q < PER_ROW ? (col0 + cc) * p.cin * 2 + ch * 16 : -1;
+                const u32x4 t4 = __builtin_amdgcn_raw_buffer_load_b128(rr, off, 0, 0);
+                v[kh][k] = make_uint4(t4.x, t4.y, t4.z, t4.w);
+            }
+        }
+#pragma unroll
+        for (int kh = 0; kh < 3; ++kh)
+#pragma unroll
+            for (int k = 0; k < KPR; ++k) {
+                const int q = tid + 256 * k;
+                const int cc = q / C8T, ch = q - cc * C8T;
+                const int slot = (cc & 1) ? PT + 1 + (cc >> 1) : (cc >> 1);
+                if (q < PER_ROW) xs[(kh * NC + slot) * (C8T + 1) + ch] = v[kh][k];
+            }
     } else {
         const uint16_t *fp = p.x + ((size_t)n * p.t + j) * frame;  // spatial: t_out == t
         constexpr int NC = 2 * PT + 1;                              // input columns
@@ -159,8 +210,8 @@ __global__ void __launch_bounds__(256) strided_kernel(SParams p) {
 #pragma unroll
             for (int k = 0; k < BATCH; ++k) {
                 const int q = base + tid + 256 * k;
-                const int rest = div_small(q, inv_c8), ch = q - rest * c8;
-                const int kh = div_small(rest, inv_nc), cc = rest - kh * NC;
+                const int rest = C8T ? q / c8 : div_small(q, inv_c8), ch = q - rest * c8;
+                const int kh = C8T ? rest / NC : div_small(rest, inv_nc), cc = rest - kh * NC;
                 const int hs = 2 * oh - p.ph + kh, ws = col0 + cc;
                 const int slot = (cc & 1) ? PT + 1 + (cc >> 1) : (cc >> 1);
                 v[k] = make_uint4(0u, 0u, 0u, 0u);
@@ -190,7 +241,7 @@ __global__ void __launch_bounds__(256) strided_kernel(SParams p) {
     // K-steps 0 .. NS-2 in flight before the first MFMA.
     static_for<NS - 1>([&](auto i) {
         constexpr int I = decltype(i)::value;
-        load_a(i, I < p.nb ? I : p.nb - 1);
+        load_a(i, I < nb ? I : nb - 1);
     });
 
     f32x4 acc[FCO][FPOS];
@@ -219,14 +270,14 @@ __global__ void __launch_bounds__(256) strided_kernel(SParams p) {
     bf16x8 B[3][FPOS];
 #pragma unroll
     for (int b = 0; b < FPOS; ++b) B[0][b] = as_bf16x8(xs[b_entry(0, b)]);
-    for (int ks0 = 0; ks0 < p.nb; ks0 += NS) {
+    for (int ks0 = 0; ks0 < nb; ks0 += NS) {
         static_for<NS>([&](auto i) {
             constexpr int SET = decltype(i)::value;
             constexpr int BS = SET % 3, BN = (SET + 1) % 3;
             const int ks = ks0 + SET;
-            const int nxt = ks + NS - 1 < p.nb ? ks + NS - 1 : p.nb - 1;
+            const int nxt = ks + NS - 1 < nb ? ks + NS - 1 : nb - 1;
             load_a(Int<(SET + NS - 1) % NS>{}, nxt);
-            const int kb = ks + 1 < p.nb ? ks + 1 : ks;
+            const int kb = ks + 1 < nb ? ks + 1 : ks;
 #pragma unroll
             for (int b = 0; b < FPOS; ++b) B[BN][b] = as_bf16x8(xs[b_entry(kb, b)]);
 #pragma unroll
@@ -329,6 +380,13 @@ template <int MODE, int PT, int FCO, int WCO>
 hipError_t launch_one(const SParams &p, long blocks, size_t lds, hipStream_t s) {
     constexpr int FPOS = PT / 16 / (4 / WCO);
     if constexpr (FPOS >= 1 && FPOS * 16 * (4 / WCO) == PT) {
+        if constexpr (FCO == 3 && WCO == 2 && PT == 64) {
+            if (p.cin == 96) {  // the 96-channel encoder level: constant index arithmetic
+                hipLaunchKernelGGL((strided_kernel<MODE, PT, FCO, FPOS, WCO, 12>), dim3((unsigned)blocks),
+                                   dim3(256), lds, s, p);
+                return hipGetLastError();
+            }
+        }
         hipLaunchKernelGGL((strided_kernel<MODE, PT, FCO, FPOS, WCO>), dim3((unsigned)blocks), dim3(256),
                            lds, s, p);
         return hipGetLastError();
