@@ -558,11 +558,21 @@ __global__ void __launch_bounds__(256) splitk_reduce_kernel(const float *__restr
     float v[8];
 #pragma unroll
     for (int k = 0; k < 8; ++k) v[k] = 0.f;
-    for (int sp = 0; sp < S; ++sp) {
-        const f32x4 a = *reinterpret_cast<const f32x4 *>(part + sp * stride + e0);
-        const f32x4 b = *reinterpret_cast<const f32x4 *>(part + sp * stride + e0 + 4);
-        v[0] += a[0]; v[1] += a[1]; v[2] += a[2]; v[3] += a[3];
-        v[4] += b[0]; v[5] += b[1]; v[6] += b[2]; v[7] += b[3];
+    // Splits in order, four splits' loads in flight before their adds.
+    for (int sp0 = 0; sp0 < S; sp0 += 4) {
+        f32x4 a[4], b[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+            if (sp0 + u < S) {
+                a[u] = *reinterpret_cast<const f32x4 *>(part + (sp0 + u) * stride + e0);
+                b[u] = *reinterpret_cast<const f32x4 *>(part + (sp0 + u) * stride + e0 + 4);
+            }
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+            if (sp0 + u < S) {
+                v[0] += a[u][0]; v[1] += a[u][1]; v[2] += a[u][2]; v[3] += a[u][3];
+                v[4] += b[u][0]; v[5] += b[u][1]; v[6] += b[u][2]; v[7] += b[u][3];
+            }
     }
     const uint32_t bw[4] = {bv.x, bv.y, bv.z, bv.w}, rw[4] = {rv.x, rv.y, rv.z, rv.w};
     uint32_t o[4];

@@ -131,11 +131,21 @@ __global__ void __launch_bounds__(256) rmsnorm_flat_kernel(const uint4 *__restri
                 float v[8];
 #pragma unroll
                 for (int e = 0; e < 8; ++e) v[e] = 0.f;
-                for (int sp = 0; sp < pp.S; ++sp) {
-                    const float4 a = *reinterpret_cast<const float4 *>(pp.part + sp * pp.stride + e0);
-                    const float4 b = *reinterpret_cast<const float4 *>(pp.part + sp * pp.stride + e0 + 4);
-                    v[0] += a.x; v[1] += a.y; v[2] += a.z; v[3] += a.w;
-                    v[4] += b.x; v[5] += b.y; v[6] += b.z; v[7] += b.w;
+                // splits in order, four splits' loads in flight before their adds
+                for (int sp0 = 0; sp0 < pp.S; sp0 += 4) {
+                    float4 a[4], b[4];
+#pragma unroll
+                    for (int u = 0; u < 4; ++u)
+                        if (sp0 + u < pp.S) {
+                            a[u] = *reinterpret_cast<const float4 *>(pp.part + (sp0 + u) * pp.stride + e0);
+                            b[u] = *reinterpret_cast<const float4 *>(pp.part + (sp0 + u) * pp.stride + e0 + 4);
+                        }
+#pragma unroll
+                    for (int u = 0; u < 4; ++u)
+                        if (sp0 + u < pp.S) {
+                            v[0] += a[u].x; v[1] += a[u].y; v[2] += a[u].z; v[3] += a[u].w;
+                            v[4] += b[u].x; v[5] += b[u].y; v[6] += b[u].z; v[7] += b[u].w;
+                        }
                 }
                 if (pp.bias) {
                     float bb[8];

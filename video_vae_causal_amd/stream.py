@@ -49,20 +49,31 @@ def _cached_buf(bufs: Dict[str, torch.Tensor], name: str, shape, like: torch.Ten
 
 
 class _PingPong:
+    """A layer's cache pair.  After ``reset()`` the cache is *fresh*: the next
+    chunk passes ``cache_in = NULL``, which the library reads as zero causal
+    padding, so a new sequence costs no fill.  ``materialize()`` writes those
+    zeros into the buffer for callers that need the buffer itself (a graph
+    that records buffer addresses, a checkpoint)."""
+
     def __init__(self, shape, dtype, device):
         self.buf = [L.empty_cl(shape, dtype, device), L.empty_cl(shape, dtype, device)]
         self.cur = 0
         self.reset()
 
     def reset(self):
-        # Only the buffer the next chunk reads must be zero (zero causal
-        # padding); the other one is entirely rewritten as that chunk's cache_out.
-        L.wvc_cache_reset(self.buf[0])
         self.cur = 0
+        self.fresh = True
+
+    def materialize(self):
+        if self.fresh:
+            # Only the buffer the next chunk reads must be zero; the other is
+            # entirely rewritten as that chunk's cache_out.
+            L.wvc_cache_reset(self.buf[self.cur])
+            self.fresh = False
 
     @property
     def cin(self):
-        return self.buf[self.cur]
+        return None if self.fresh else self.buf[self.cur]
 
     @property
     def cout(self):
@@ -70,6 +81,7 @@ class _PingPong:
 
     def flip(self):
         self.cur ^= 1
+        self.fresh = False
 
 
 class CausalConv3d:
@@ -113,7 +125,10 @@ class CausalConv3d:
         return y
 
     def caches(self) -> List[torch.Tensor]:
-        return [self.cache.cin] if self.cache is not None else []
+        if self.cache is None:
+            return []
+        self.cache.materialize()
+        return [self.cache.cin]
 
     def reset(self):
         """Zero the caches in place (a new sequence), keeping their buffers."""
@@ -177,7 +192,11 @@ class ResBlock:
         return y
 
     def caches(self) -> List[torch.Tensor]:
-        return [self.c1.cin, self.c2.cin] if self.c1 is not None else []
+        if self.c1 is None:
+            return []
+        self.c1.materialize()
+        self.c2.materialize()
+        return [self.c1.cin, self.c2.cin]
 
     def _half_ws(self, name: str, x: torch.Tensor) -> torch.Tensor:
         d = L.resblock_desc(tuple(x.shape), self.p["w1"].shape[0], L._dtype_code(x.dtype), self.eps,
@@ -377,13 +396,15 @@ class FrameGraph:
         y = self._run(self.x)          # eager pass: sizes every workspace and buffer
         self.y = L.empty_cl(tuple(y.shape), dtype, device)
         self._pps = stack.pingpongs()
-        stack.reset()
+        self.reset()   # the recorded calls must name the cache buffers, not NULL
         self.graphs = [capture(lambda: self._run(self.x, out=self.y), device) for _ in range(2)]
         # each recording flipped every cache once, so the parity is back to 0
         self.parity = 0
 
     def reset(self):
         self.stack.reset()
+        for pp in self._pps:
+            pp.materialize()
         self.parity = 0
 
     def __call__(self) -> torch.Tensor:
