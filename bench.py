@@ -418,7 +418,9 @@ def wl_tiled():
                         "tile": list(tile) if tile else None, "stride": list(stride) if stride else None,
                         "tiles": tiles, "decoded_latent_px_per_px": round(tiles * th * tw / (h * w), 3),
                         "chunk_frames": 1, "batch": n},
-                kernel=kernel, kernel_name="igemm_kernel<3, 128, 32, 2, *, *> (conv at 2x tile)",
+                kernel=kernel,
+                kernel_name=("igemm_kernel<3, 128, 32, 2, true, 16> + splitk_reduce_kernel" if tile
+                             else "igemm_kernel<3, 128, 32, 2, *, *> (whole 384x672 frame)"),
                 kernel_units=acc.conv_flops(n, 1, 2 * th, 2 * tw, width, width), kernel_bound="mfma",
                 kernel_bytes=acc.conv_launch_bytes(n, 1, 2 * th, 2 * tw, width, width))
     return step, info
