@@ -75,6 +75,11 @@ def _load():
     lib.oracle_strided_out_frames.argtypes = [i, i, i]
     lib.oracle_strided_out_size.restype = ctypes.c_int
     lib.oracle_strided_out_size.argtypes = [i, i, i, i, i, i]
+    u8p = ctypes.POINTER(ctypes.c_uint8)
+    lib.oracle_e4m3_decode.restype = None
+    lib.oracle_e4m3_decode.argtypes = [u8p, ctypes.c_long, dp]
+    lib.oracle_e4m3_encode.restype = None
+    lib.oracle_e4m3_encode.argtypes = [dp, ctypes.c_long, u8p]
     lib.oracle_causal_conv3d_strided.restype = ctypes.c_int
     lib.oracle_causal_conv3d_strided.argtypes = [dp, i, i, i, i, i, dp, i, dp, i, i, i, i, dp,
                                                  i, i, i, i, i, i, i, i, i, i, i, dp]
@@ -411,6 +416,87 @@ def tiled_decoder_stack(latent, p: dict, tile=(60, 104), stride=(30, 52), bf16: 
             for y, x in origins]
     y = blend_tiles(outs, origins, (2 * H, 2 * W), scale=2)
     return _maybe_round(y, bf16)
+
+
+# ---------------------------------------------------------------------------
+# 8-bit (E4M3) quantised conv: "Cosmos3 Wan VAE ...", sections 7 and 9 (8-bit
+# weights and activations as the byte reduction of the 16-bit engine), in the
+# OCP OFP8 E4M3 format (codec in oracle.c).
+# ---------------------------------------------------------------------------
+E4M3_MAX = 448.0
+
+
+def e4m3_decode(codes) -> np.ndarray:
+    """E4M3 codes (uint8) -> their real values (fp64; NaN for the NaN codes)."""
+    c = np.ascontiguousarray(np.asarray(codes, dtype=np.uint8))
+    y = np.empty(c.shape, dtype=np.float64)
+    _load().oracle_e4m3_decode(c.ctypes.data_as(ctypes.POINTER(ctypes.c_uint8)), c.size, _ptr(y))
+    return y
+
+
+def e4m3_encode(x) -> np.ndarray:
+    """Nearest E4M3 code, ties to even, saturating at +-448 (uint8)."""
+    x = _f64(x)
+    c = np.empty(x.shape, dtype=np.uint8)
+    _load().oracle_e4m3_encode(_ptr(x), x.size, c.ctypes.data_as(ctypes.POINTER(ctypes.c_uint8)))
+    return c
+
+
+def e4m3_scaled_input(x, scale) -> np.ndarray:
+    """The value a quantiser rounds: x times the reciprocal of the scale, both
+    the reciprocal and the product in fp32 (the pages fix no arithmetic for
+    the quantiser; this reading makes the rounding decision reproducible)."""
+    x32 = np.asarray(x, dtype=np.float32)
+    r = np.float32(1.0) / np.asarray(scale, dtype=np.float32)
+    return (x32 * r).astype(np.float64)
+
+
+def quantize_e4m3(x, scale: float) -> np.ndarray:
+    """Per-tensor quantisation: codes = E4M3(fl32(x * fl32(1/scale)))."""
+    return e4m3_encode(e4m3_scaled_input(x, np.float32(scale)))
+
+
+def quantize_rows_e4m3(w2d):
+    """Per-row (per output channel) absmax quantisation of a [rows, cols]
+    matrix: scale_r = fl32(amax_r / 448) (1 when the row is all zero), codes
+    = E4M3(fl32(w * fl32(1/scale_r))).  Returns (codes uint8, scales fp32)."""
+    w32 = np.asarray(w2d, dtype=np.float32)
+    amax = np.max(np.abs(w32), axis=1)
+    scale = (amax / np.float32(E4M3_MAX)).astype(np.float32)
+    scale[amax == 0] = np.float32(1.0)
+    return e4m3_encode(e4m3_scaled_input(w32, scale[:, None])), scale
+
+
+def quantize_conv_weights_e4m3(w):
+    """[C_out, C_in, kT, kH, kW] weights -> (codes of the same shape, scales
+    [C_out]) with one scale per output channel over its C_in*kT*kH*kW taps."""
+    w = np.asarray(w)
+    codes, scale = quantize_rows_e4m3(w.reshape(w.shape[0], -1))
+    return codes.reshape(w.shape), scale
+
+
+def causal_conv3d_e4m3(xq, x_scale, wq, w_scale, bias=None, cache_q=None, residual=None):
+    """Causal 3x3x3 conv of E4M3 operands: the codes are decoded exactly, the
+    activations (chunk and cache) times the one per-tensor scale, the weights
+    times the scale of their output channel; then the conv of section 10.3
+    (``causal_conv3d``) in fp64, the bias once, and the residual after it."""
+    x = e4m3_decode(xq) * float(x_scale)
+    w = e4m3_decode(wq) * np.asarray(w_scale, dtype=np.float64)[:, None, None, None, None]
+    cache = None if cache_q is None else e4m3_decode(cache_q) * float(x_scale)
+    y = causal_conv3d(x, w, bias, cache)
+    if residual is not None:
+        y = y + _f64(residual)
+    return y
+
+
+def norm_silu_e4m3(x, gamma, beta=None, scale: float = 1.0, eps=DEFAULT_EPS):
+    """RMS norm + SiLU quantised to E4M3 with a per-tensor scale.  Returns
+    (v, codes): v = norm_silu(x) / scale in fp64, the value the quantiser
+    rounds, and its codes.  The GPU computes v in fp32, so a code may differ
+    where v lies within fp32 error of a rounding boundary; the tests compare
+    against v for that reason."""
+    v = norm_silu(x, gamma, beta, eps) / float(scale)
+    return v, e4m3_encode(v)
 
 
 def rel_l2(y, ref) -> float:

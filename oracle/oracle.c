@@ -419,3 +419,71 @@ void oracle_round_bf16(const double *x, long count, double *y) {
         y[i] = r;
     }
 }
+
+/* ------------------------------------------------------------------------ */
+/* 8-bit floating point, E4M3                                               */
+/* ------------------------------------------------------------------------ */
+/*
+ * The quantised Conv3D of "Cosmos3 Wan VAE -- engine size vs runtime context
+ * memory" (sections 7 and 9: 8-bit weights and activations halve the bytes
+ * of the 16-bit engine) is taken here in the 8-bit float format the MI355X
+ * matrix cores read: E4M3 as defined by the OCP 8-bit Floating Point
+ * specification (OFP8).  A code is s.eeee.mmm with exponent bias 7:
+ *   e == 0          : (-1)^s * m * 2^-9            (zero and subnormals)
+ *   1 <= e <= 15    : (-1)^s * (1 + m/8) * 2^(e-7)  (normals)
+ *   e == 15, m == 7 : NaN (the format has no infinities)
+ * so the largest finite magnitude is 1.75 * 2^8 = 448.
+ */
+double oracle_e4m3_decode_one(unsigned code) {
+    const int s = (code >> 7) & 1, e = (code >> 3) & 15, m = code & 7;
+    double v;
+    if (e == 15 && m == 7) return NAN;
+    if (e == 0)
+        v = ldexp((double)m, -9);
+    else
+        v = ldexp(1.0 + m / 8.0, e - 7);
+    return s ? -v : v;
+}
+
+void oracle_e4m3_decode(const uint8_t *codes, long count, double *y) {
+    for (long i = 0; i < count; ++i) y[i] = oracle_e4m3_decode_one(codes[i]);
+}
+
+/*
+ * Encoding of a real value: round to the nearest E4M3 value, ties to the even
+ * code (the OFP8 round-to-nearest-even mode), and saturate: magnitudes beyond
+ * 448 become 448 with the value's sign (OFP8's saturating conversion).  NaN
+ * becomes the NaN code 0x7F.  A value v with 2^E <= |v| < 2^(E+1) sits on a
+ * grid of spacing 2^(E-3); below 2^-6 the spacing stays 2^-9.  rint() rounds
+ * half to even in the default rounding mode.
+ */
+void oracle_e4m3_encode(const double *x, long count, uint8_t *codes) {
+    for (long i = 0; i < count; ++i) {
+        const double v = x[i];
+        if (isnan(v)) {
+            codes[i] = 0x7F;
+            continue;
+        }
+        const unsigned sign = signbit(v) ? 0x80u : 0u;
+        const double a = fabs(v);
+        unsigned mag;
+        if (a >= 448.0) {
+            mag = 0x7E;
+        } else if (a < ldexp(1.0, -6)) {
+            /* subnormal grid: m * 2^-9, m in 0..8 (8 is the smallest normal) */
+            mag = (unsigned)rint(ldexp(a, 9));
+        } else {
+            int e2;
+            frexp(a, &e2); /* a = f * 2^e2, 0.5 <= f < 1: E = e2 - 1 */
+            int E = e2 - 1;
+            unsigned m = (unsigned)rint(ldexp(a, 3 - E)) - 8u; /* 8..16 -> 0..8 */
+            if (m == 8) {
+                m = 0;
+                E += 1;
+            }
+            mag = (unsigned)(E + 7) << 3 | m;
+            if (mag > 0x7E) mag = 0x7E;
+        }
+        codes[i] = (uint8_t)(sign | mag);
+    }
+}
