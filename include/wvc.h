@@ -57,7 +57,7 @@ enum {
     WVC_ERR_HIP = 6          /* the HIP runtime reported an error at launch    */
 };
 
-enum { WVC_F32 = 0, WVC_BF16 = 1 };
+enum { WVC_F32 = 0, WVC_BF16 = 1, WVC_E4M3 = 2 /* OCP 8-bit float, see the E4M3 calls */ };
 
 /* Weight layouts: the standard [C_out][kT][kH][kW][C_in] one, or the packed
  * MFMA fragment order written by wvc_conv3d_pack_weights (fast routes only). */
@@ -72,7 +72,7 @@ typedef struct wvc_conv3d_desc {
     int pad_h, pad_w;            /* symmetric zero padding; temporal pad is causal  */
     int dil_t, dil_h, dil_w;
     int groups;                  /* must be 1                                       */
-    int dtype;                   /* WVC_F32 or WVC_BF16                             */
+    int dtype;                   /* WVC_F32, WVC_BF16, or WVC_E4M3 (8-bit calls)    */
     int weight_layout;           /* WVC_WEIGHT_STANDARD or WVC_WEIGHT_PACKED        */
     int pad_h_extra, pad_w_extra;/* extra zero rows below / columns right of the
                                     frame (the downsample's one-sided zero pad,
@@ -307,6 +307,61 @@ int wvc_tile_blend_finish(const float *acc, const float *wsum, void *y, int n, i
 /* Strict mode ([P3]: a strict mode stops on an unexpected fallback): when on,
  * a call that would take the generic route fails with WVC_ERR_STRICT.
  * Initialised from the environment variable WVC_STRICT (=1 turns it on). */
+/*
+ * 8-bit (E4M3) path.  [P1] sections 7 and 9 name 8-bit weights and
+ * activations for the Conv3D as the way to cut the bytes of the 16-bit
+ * engine; on MI355X the 8-bit float the matrix cores read is OCP E4M3
+ * (OFP8: exponent bias 7, no infinities, largest finite 448, codes 0x7F and
+ * 0xFF are NaN), which also runs the MFMA at twice the bf16 rate.  Codes are
+ * carried as bytes.  Every quantiser rounds to the nearest code, ties to the
+ * even code, and saturates at +-448; the code of a NaN input is unspecified.
+ * Quantisation multiplies by the reciprocal of the scale, both rounded to
+ * fp32: q = E4M3(fl32(x * fl32(1 / scale))); the real value of code q is
+ * decode(q) * scale.
+ *
+ * wvc_quantize_e4m3: count elements of x (WVC_BF16 or WVC_F32, any layout)
+ *   with one per-tensor scale (finite, > 0, host value) -> q (count bytes,
+ *   written, may not overlap x).
+ * wvc_quantize_rows_e4m3: x viewed as [rows][cols] (row-major) -> q, with one
+ *   scale per row written to scale[rows] (fp32, device): scale_r =
+ *   fl32(amax_r / 448), 1 for an all-zero row.  For conv weights in the
+ *   standard layout a row is one output channel: the per-channel weight scales
+ *   of the 8-bit conv.
+ * wvc_rmsnorm_silu_e4m3: wvc_rmsnorm_silu of a bf16 x whose result is stored
+ *   as codes (q [N, C, T, H, W] channels-last bytes, may not overlap x) with
+ *   the per-tensor activation scale `scale` (finite, > 0): the norm writes the
+ *   8-bit conv's input directly, 1 byte per element instead of 2.
+ *
+ * wvc_causal_conv3d_e4m3_fwd: the causal 3x3x3 conv of wvc_causal_conv3d_fwd
+ *   on codes.  d->dtype must be WVC_E4M3; only 3x3x3, stride 1, pad 1,
+ *   dilation 1 with C_in % 16 == 0 and C_out % 32 == 0 and 16-byte aligned
+ *   tensors is supported (WVC_ERR_UNSUPPORTED / WVC_ERR_ARG otherwise; there
+ *   is no generic 8-bit route).
+ *     x, cache_in, cache_out  E4M3 codes, shapes and layouts as for the bf16
+ *                             conv; the cache holds codes of the same scale
+ *     weight                  E4M3 codes [C_out][3][3][3][C_in], or packed
+ *                             by wvc_conv3d_pack_weights with an E4M3
+ *                             descriptor (d->weight_layout)
+ *     x_scale                 per-tensor activation scale (host, finite > 0)
+ *     w_scale                 [C_out] fp32 per-output-channel weight scales
+ *                             (device, 16-byte aligned)
+ *     bias, residual, y       bf16, as for the bf16 conv
+ *   y = round_bf16(x_scale * w_scale[co] * S + b[co] + residual), S the sum of
+ *   decode(x code) * decode(w code) over the same taps as the bf16 conv
+ *   (products exact, accumulated in fp32).  Workspace: as for the bf16 conv,
+ *   wvc_causal_conv3d_workspace_bytes(d) with the E4M3 descriptor.
+ *   wvc_causal_conv3d_fwd refuses E4M3 descriptors (WVC_ERR_UNSUPPORTED).
+ */
+int wvc_quantize_e4m3(const void *x, int dtype, int64_t count, float scale, void *q, void *stream);
+int wvc_quantize_rows_e4m3(const void *x, int dtype, int64_t rows, int64_t cols, void *q,
+                           float *scale, void *stream);
+int wvc_rmsnorm_silu_e4m3(const void *x, const void *gamma, const void *beta, void *q, int n, int c,
+                          int t, int h, int w, float eps, int apply_silu, float scale, void *stream);
+int wvc_causal_conv3d_e4m3_fwd(const wvc_conv3d_desc *d, const void *x, float x_scale,
+                               const void *cache_in, void *cache_out, const void *weight,
+                               const float *w_scale, const void *bias, const void *residual,
+                               void *y, void *workspace, size_t workspace_bytes, void *stream);
+
 void wvc_set_strict(int on);
 int wvc_get_strict(void);
 

@@ -489,6 +489,19 @@ def causal_conv3d_e4m3(xq, x_scale, wq, w_scale, bias=None, cache_q=None, residu
     return y
 
 
+def causal_conv3d_e4m3_points(xq, x_scale, wq, w_scale, flat_idx, bias=None, cache_q=None,
+                              residual=None):
+    """:func:`causal_conv3d_e4m3` evaluated only at the given flat indices of
+    the NCTHW output."""
+    x = e4m3_decode(xq) * float(x_scale)
+    w = e4m3_decode(wq) * np.asarray(w_scale, dtype=np.float64)[:, None, None, None, None]
+    cache = None if cache_q is None else e4m3_decode(cache_q) * float(x_scale)
+    y = causal_conv3d_points(x, w, flat_idx, bias, cache)
+    if residual is not None:
+        y = y + _f64(residual).ravel()[np.asarray(flat_idx, dtype=np.int64).ravel()]
+    return y
+
+
 def norm_silu_e4m3(x, gamma, beta=None, scale: float = 1.0, eps=DEFAULT_EPS):
     """RMS norm + SiLU quantised to E4M3 with a per-tensor scale.  Returns
     (v, codes): v = norm_silu(x) / scale in fp64, the value the quantiser

@@ -293,3 +293,68 @@ def test_tiling_validation(lib):
 def stream_origins():
     from video_vae_causal_amd import stream
     return [stream.tile_origins(120, 60, 30), stream.tile_origins(208, 104, 52), stream.tile_origins(40, 60, 30)]
+
+
+def e4m3_call(lib, d, x=X, xs=1.0, cin=CIN, cout=COUT, w=W, ws_scale=WS + 0x100000, b=B, res=None,
+              y=Y, ws=None, wsb=0):
+    return lib.wvc_causal_conv3d_e4m3_fwd(ctypes.byref(d) if d is not None else None, x, xs, cin,
+                                          cout, w, ws_scale, b, res, y, ws, wsb, None)
+
+
+def test_e4m3_conv_validation(lib):
+    ok = desc(x_shape=(1, 32, 2, 8, 8), w_shape=(32, 32, 3, 3, 3), dtype=L.WVC_E4M3)
+    need = lib.wvc_causal_conv3d_workspace_bytes(ctypes.byref(ok))
+    assert need != ctypes.c_size_t(-1).value and need > 0  # packs the weights
+    # packed sizes: one 64-byte slice per (output channel, tap, 64-channel unit)
+    assert lib.wvc_conv3d_packed_weight_bytes(ctypes.byref(ok)) == 32 * 27 * 64
+    wide = desc(x_shape=(1, 96, 2, 8, 8), w_shape=(128, 96, 3, 3, 3), dtype=L.WVC_E4M3)
+    assert lib.wvc_conv3d_packed_weight_bytes(ctypes.byref(wide)) == 128 * 27 * 2 * 64
+    # the bf16 entry point refuses 8-bit descriptors
+    assert call(lib, ok) == L.WVC_ERR_UNSUPPORTED
+    assert "e4m3" in L.wvc_last_error()
+    # the 8-bit entry point needs an 8-bit descriptor
+    assert e4m3_call(lib, desc()) == L.WVC_ERR_ARG
+    assert e4m3_call(lib, None) == L.WVC_ERR_ARG
+    # 3x3x3 / stride 1 / pad 1 / C_in % 16 / C_out % 32 only: no generic 8-bit route
+    for bad in (desc(x_shape=(1, 32, 2, 8, 8), w_shape=(32, 32, 1, 1, 1), padding=(0, 0), dtype=L.WVC_E4M3),
+                desc(x_shape=(1, 24, 2, 8, 8), w_shape=(32, 24, 3, 3, 3), dtype=L.WVC_E4M3),
+                desc(x_shape=(1, 32, 2, 8, 8), w_shape=(48, 32, 3, 3, 3), dtype=L.WVC_E4M3),
+                desc(x_shape=(1, 32, 2, 8, 8), w_shape=(32, 32, 3, 3, 3), dilation=(1, 2, 2),
+                     dtype=L.WVC_E4M3),
+                desc(x_shape=(1, 32, 2, 8, 8), w_shape=(32, 32, 3, 3, 3), stride=(1, 2, 2),
+                     dtype=L.WVC_E4M3)):
+        assert e4m3_call(lib, bad) == L.WVC_ERR_UNSUPPORTED
+    # scales
+    assert e4m3_call(lib, ok, ws_scale=None, ws=WS, wsb=need) == L.WVC_ERR_ARG
+    assert e4m3_call(lib, ok, ws_scale=WS + 4, ws=WS, wsb=need) == L.WVC_ERR_ARG  # unaligned
+    for xs in (0.0, -1.0, float("inf"), float("nan")):
+        assert e4m3_call(lib, ok, xs=xs, ws=WS, wsb=need) == L.WVC_ERR_ARG
+    # workspace too small, unaligned tensors, aliasing of y with the scales
+    assert e4m3_call(lib, ok, ws=WS, wsb=need - 1) == L.WVC_ERR_WORKSPACE
+    assert e4m3_call(lib, ok, x=X + 8, ws=WS, wsb=need) == L.WVC_ERR_ARG
+    assert e4m3_call(lib, ok, ws_scale=Y, ws=WS, wsb=need) == L.WVC_ERR_ALIAS
+    # the block entry points stay 16/32-bit
+    rd = L.resblock_desc((1, 32, 2, 8, 8), 32, L.WVC_E4M3)
+    assert lib.wvc_resblock_workspace_bytes(ctypes.byref(rd)) == ctypes.c_size_t(-1).value
+
+
+def test_e4m3_quantiser_and_norm_validation(lib):
+    assert lib.wvc_quantize_e4m3(X, L.WVC_E4M3, 16, 1.0, Y, None) == L.WVC_ERR_UNSUPPORTED
+    assert lib.wvc_quantize_e4m3(X, L.WVC_BF16, -1, 1.0, Y, None) == L.WVC_ERR_ARG
+    for sc in (0.0, -2.0, float("inf"), float("nan")):
+        assert lib.wvc_quantize_e4m3(X, L.WVC_BF16, 16, sc, Y, None) == L.WVC_ERR_ARG
+    assert lib.wvc_quantize_e4m3(X, L.WVC_BF16, 16, 1.0, None, None) == L.WVC_ERR_ARG
+    assert lib.wvc_quantize_e4m3(X, L.WVC_BF16, 64, 1.0, X + 64, None) == L.WVC_ERR_ALIAS
+    assert lib.wvc_quantize_e4m3(None, L.WVC_BF16, 0, 1.0, None, None) == L.WVC_OK  # empty
+    assert lib.wvc_quantize_rows_e4m3(X, L.WVC_F32, 4, 0, Y, W, None) == L.WVC_ERR_ARG
+    assert lib.wvc_quantize_rows_e4m3(X, L.WVC_F32, 4, 8, Y, None, None) == L.WVC_ERR_ARG
+    assert lib.wvc_quantize_rows_e4m3(X, L.WVC_F32, 4, 8, Y, Y + 8, None) == L.WVC_ERR_ALIAS
+    assert lib.wvc_quantize_rows_e4m3(X, 7, 4, 8, Y, W, None) == L.WVC_ERR_UNSUPPORTED
+    args = dict(n=1, c=16, t=1, h=4, w=4)
+    norm = lambda **kw: lib.wvc_rmsnorm_silu_e4m3(
+        kw.get("x", X), kw.get("g", W), None, kw.get("q", Y), args["n"], args["c"], args["t"],
+        args["h"], args["w"], kw.get("eps", 1e-12), 1, kw.get("scale", 1.0), None)
+    assert norm(eps=0.0) == L.WVC_ERR_ARG
+    assert norm(scale=0.0) == L.WVC_ERR_ARG
+    assert norm(g=None) == L.WVC_ERR_ARG
+    assert norm(q=X + 16) == L.WVC_ERR_ALIAS

@@ -1,0 +1,253 @@
+"""GPU parity of the 8-bit (OCP E4M3) path: quantisers, the norm that writes
+codes, and the causal 3x3x3 conv on codes ("Cosmos3 Wan VAE -- engine size vs
+runtime context memory", sections 7 and 9: 8-bit weights and activations).
+
+Bars:
+  * quantisers: bit-exact codes (and per-row scales) against the oracle, whose
+    rounding decision is taken on the same fp32 value the kernel rounds;
+  * norm -> codes: the kernel's fp32 norm differs from the fp64 oracle by
+    rounding, so a code must equal the oracle's nearest code, or, where the
+    oracle's value lies within 3e-5 (relative) of the midpoint between two
+    codes, either of them;
+  * conv: the bf16 tolerance of every conv here (relative L2 <= 1e-2, max abs
+    <= 2e-2 max|ref|), and relative L2 <= 3e-3, against the fp64 conv of the
+    decoded operands: products of codes are exact and the fp32 sum adds far
+    less than the final bf16 rounding (2^-9 relative).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from video_vae_causal_amd import _lib as L
+from video_vae_causal_amd import inputs as I
+from _gpu_util import check_bf16, dev, f64, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+E4M3_REL_L2 = 3e-3
+NORM_TIE_BAND = 3e-5
+
+
+def codes_dev(a: np.ndarray) -> torch.Tensor:
+    t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.uint8)).to(dev())
+    if t.dim() == 5:
+        t = t.contiguous(memory_format=torch.channels_last_3d)
+    return t
+
+
+def codes_host(t: torch.Tensor) -> np.ndarray:
+    return t.cpu().numpy()
+
+
+def same_codes(a, b):
+    """Codes equal, except that +0 and -0 (0x00, 0x80) count as one value: the
+    sign of a zero result is not specified."""
+    a, b = np.asarray(a), np.asarray(b)
+    return (a == b) | (((a & 0x7F) == 0) & ((b & 0x7F) == 0))
+
+
+def check_e4m3_conv(y, ref, what):
+    check_bf16(y, ref, what)
+    rel = oracle.rel_l2(y, ref)
+    assert rel <= E4M3_REL_L2, f"{what}: rel L2 {rel} > {E4M3_REL_L2}"
+
+
+# ---------------------------------------------------------------------------
+# quantisers
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("scale", [1.0, 0.37, 2.0 ** -5])
+def test_quantize_every_bf16_value(scale):
+    bits = (np.arange(1 << 16, dtype=np.uint32) << 16).view(np.float32)
+    v = bits[np.isfinite(bits)]
+    print(f"[case] quantize all {v.size} finite bf16 values, scale={scale}", flush=True)
+    x = torch.from_numpy(v.copy()).to(dev()).to(torch.bfloat16)
+    q = codes_host(L.wvc_quantize_e4m3(x, scale))
+    ref = oracle.quantize_e4m3(v, scale)
+    print(f"[parity] sign-of-zero differences: {int(np.sum(q != ref))}", flush=True)
+    bad = np.flatnonzero(~same_codes(q, ref))
+    assert bad.size == 0, f"{bad.size} codes differ, first: x={v[bad[:5]]} gpu={q[bad[:5]]} ref={ref[bad[:5]]}"
+
+
+def test_quantize_fp32_vector_and_ragged_tails():
+    v = I.normal((100003,), 11, "q32", std=3.0) * np.exp(I.normal((100003,), 11, "e", std=2.0))
+    v = v.astype(np.float32)
+    x = torch.from_numpy(v).to(dev())
+    for lo, hi in ((0, v.size), (1, v.size), (3, 1000), (0, 7)):  # unaligned starts, short tails
+        print(f"[case] quantize fp32 [{lo}:{hi}]", flush=True)
+        q = codes_host(L.wvc_quantize_e4m3(x[lo:hi].clone() if lo == 0 else x[lo:hi], 0.5))
+        assert same_codes(q, oracle.quantize_e4m3(v[lo:hi], 0.5)).all()
+
+
+@pytest.mark.parametrize("cout,cin,dtype", [(40, 96, torch.bfloat16), (7, 16, torch.float32),
+                                            (384, 384, torch.bfloat16)])
+def test_quantize_rows_matches_oracle_bitwise(cout, cin, dtype):
+    print(f"[case] row quantiser cout={cout} cin={cin} {dtype}", flush=True)
+    w = I.normal((cout, cin, 3, 3, 3), 12, "wq") * np.exp(I.normal((cout, 1, 1, 1, 1), 12, "rs", std=2.0))
+    w[cout // 2] = 0.0  # an all-zero row takes scale 1
+    w = I.quantize(w.astype(np.float32), "bf16" if dtype == torch.bfloat16 else "f32")
+    wd = to_dev(w, dtype)
+    q, sc = L.wvc_quantize_rows_e4m3(wd)
+    # rows in the device's memory order: [C_out][kT][kH][kW][C_in]
+    rows = np.ascontiguousarray(w.transpose(0, 2, 3, 4, 1)).reshape(cout, -1)
+    ref_q, ref_s = oracle.quantize_rows_e4m3(rows)
+    assert np.array_equal(sc.cpu().numpy(), ref_s)
+    got = codes_host(q.permute(0, 2, 3, 4, 1).contiguous()).reshape(cout, -1)
+    assert same_codes(got, ref_q).all()
+
+
+# ---------------------------------------------------------------------------
+# norm + SiLU -> codes
+# ---------------------------------------------------------------------------
+def nearest_code_ok(q, v):
+    """q: device codes; v: the oracle's fp64 value to be rounded (same shape)."""
+    ref = oracle.e4m3_encode(v)
+    ok = same_codes(q, ref)
+    if ok.all():
+        return 0
+    bad = np.flatnonzero(~ok.ravel())
+    vv = v.ravel()[bad]
+    dq, dr = oracle.e4m3_decode(q.ravel()[bad]), oracle.e4m3_decode(ref.ravel()[bad])
+    mid = 0.5 * (dq + dr)
+    near = np.abs(vv - mid) <= NORM_TIE_BAND * np.abs(vv) + 1e-30
+    # the two codes must be neighbours on the grid, straddling v
+    adjacent = np.abs(q.ravel()[bad].astype(int) - ref.ravel()[bad].astype(int)) == 1
+    assert np.all(near & adjacent), (
+        f"{int((~(near & adjacent)).sum())} codes off the nearest: v={vv[~near][:5]} "
+        f"gpu={dq[~near][:5]} ref={dr[~near][:5]}")
+    return bad.size
+
+
+@pytest.mark.parametrize("shape,scale", [((1, 96, 3, 20, 36), 4.0 / 448),
+                                         ((1, 384, 2, 12, 20), 1.0 / 448),
+                                         ((2, 24, 2, 7, 9), 6.0 / 448),
+                                         ((1, 20, 2, 5, 6), 3.0 / 448)])  # C % 8 != 0: scalar kernel
+def test_norm_silu_e4m3_nearest_code(shape, scale):
+    n, c, t, h, w = shape
+    print(f"[case] norm->e4m3 shape={shape} scale={scale:.5f}", flush=True)
+    x = I.quantize(I.normal(shape, 13, "nx", std=2.0), "bf16")
+    g = I.norm_gamma(c, 13, "ng", "bf16")
+    b = I.quantize(I.normal((c,), 13, "nb", std=0.2), "bf16")
+    q = L.wvc_rmsnorm_silu_e4m3(to_dev(x), to_dev(g), scale, beta=to_dev(b))
+    v, _ = oracle.norm_silu_e4m3(f64(x), f64(g), f64(b), scale=scale)
+    flips = nearest_code_ok(codes_host(q), v)
+    print(f"[parity] norm->e4m3 {shape}: {flips} of {v.size} codes at a rounding midpoint", flush=True)
+    assert flips <= max(4, v.size // 10000)
+
+
+def test_norm_silu_e4m3_large_streaming_path():
+    # large enough for the two-chunks-per-thread, non-temporal variant
+    shape = (1, 96, 2, 240, 416)
+    print(f"[case] norm->e4m3 streaming shape={shape}", flush=True)
+    x = I.quantize(I.normal(shape, 14, "nx"), "bf16")
+    g = I.norm_gamma(96, 14, "ng", "bf16")
+    q = codes_host(L.wvc_rmsnorm_silu_e4m3(to_dev(x), to_dev(g), 5.0 / 448))
+    v, _ = oracle.norm_silu_e4m3(f64(x), f64(g), None, scale=5.0 / 448)
+    flips = nearest_code_ok(q, v)
+    assert flips <= v.size // 10000
+
+
+# ---------------------------------------------------------------------------
+# conv on codes
+# ---------------------------------------------------------------------------
+def run_conv(d, packed=False, residual=True, cache=True):
+    x, w = codes_dev(d["x"]), codes_dev(d["w"])
+    ws = torch.from_numpy(d["w_scale"]).to(dev())
+    pw = L.wvc_conv3d_pack_weights(w) if packed else None
+    y = L.wvc_causal_conv3d_e4m3_fwd(
+        x, d["x_scale"], w, ws, bias=to_dev(d["b"]),
+        cache_in=codes_dev(d["cache"]) if cache else None,
+        residual=to_dev(d["res"]) if residual and "res" in d else None, packed_weight=pw)
+    return y
+
+
+@pytest.mark.parametrize("cin,cout,t,h,w", [
+    (32, 32, 3, 20, 20),     # 32-channel tiles, split-K
+    (64, 128, 2, 24, 40),    # 128-channel tiles, ragged tile columns
+    (96, 128, 2, 17, 33),    # a half-filled 64-channel unit, ragged rows and columns
+    (128, 256, 1, 9, 70),    # two channel tiles, one frame
+    (16, 64, 3, 11, 13),     # C_in below one unit; C_out on 32-channel tiles
+])
+def test_conv_e4m3_vs_oracle(cin, cout, t, h, w):
+    print(f"[case] e4m3 conv cin={cin} cout={cout} t={t} h={h} w={w}", flush=True)
+    d = I.e4m3_conv_inputs(seed=15, shape=(1, cin, t, h, w), cout=cout, with_residual=True)
+    y = to_host(run_conv(d))
+    ref = oracle.causal_conv3d_e4m3(d["x"], d["x_scale"], d["w"], d["w_scale"], f64(d["b"]),
+                                    d["cache"], f64(d["res"]))
+    check_e4m3_conv(y, ref, f"e4m3 conv {cin}->{cout} {t}x{h}x{w}")
+
+
+def test_conv_e4m3_no_cache_is_zero_past_and_cache_out_exact():
+    d = I.e4m3_conv_inputs(seed=16, shape=(1, 64, 3, 10, 12), cout=64)
+    x, w = codes_dev(d["x"]), codes_dev(d["w"])
+    ws = torch.from_numpy(d["w_scale"]).to(dev())
+    cache_out = L.empty_cl((1, 64, 2, 10, 12), torch.uint8)
+    cache_out.fill_(0xAA)
+    print("[case] e4m3 conv without cache, with cache_out", flush=True)
+    y = to_host(L.wvc_causal_conv3d_e4m3_fwd(x, d["x_scale"], w, ws, bias=to_dev(d["b"]),
+                                              cache_out=cache_out))
+    ref = oracle.causal_conv3d_e4m3(d["x"], d["x_scale"], d["w"], d["w_scale"], f64(d["b"]))
+    check_e4m3_conv(y, ref, "e4m3 conv zero past")
+    assert np.array_equal(codes_host(cache_out), d["x"][:, :, 1:])
+
+
+def test_conv_e4m3_packed_equals_standard_bitwise():
+    d = I.e4m3_conv_inputs(seed=17, shape=(1, 96, 2, 16, 24), cout=128, with_residual=True)
+    print("[case] e4m3 conv packed vs standard weights", flush=True)
+    a = run_conv(d, packed=False)
+    b = run_conv(d, packed=True)
+    assert torch.equal(a, b)
+
+
+def test_conv_e4m3_chunked_stream_equals_oracle_whole():
+    d = I.e4m3_conv_inputs(seed=18, shape=(1, 64, 5, 14, 18), cout=64, with_cache=False)
+    x, w = codes_dev(d["x"]), codes_dev(d["w"])
+    ws = torch.from_numpy(d["w_scale"]).to(dev())
+    b = to_dev(d["b"])
+    ref = oracle.causal_conv3d_e4m3(d["x"], d["x_scale"], d["w"], d["w_scale"], f64(d["b"]))
+    caches = [L.empty_cl((1, 64, 2, 14, 18), torch.uint8) for _ in range(2)]
+    outs, cin, k = [], None, 0
+    print("[case] e4m3 conv streamed in chunks 1+2+2", flush=True)
+    for lo, hi in ((0, 1), (1, 3), (3, 5)):
+        xc = x[:, :, lo:hi].contiguous(memory_format=torch.channels_last_3d)
+        outs.append(to_host(L.wvc_causal_conv3d_e4m3_fwd(xc, d["x_scale"], w, ws, bias=b,
+                                                          cache_in=cin, cache_out=caches[k])))
+        cin, k = caches[k], 1 - k
+    check_e4m3_conv(np.concatenate(outs, axis=2), ref, "e4m3 conv chunked")
+
+
+def test_norm_then_conv_e4m3_block_half():
+    # norm + SiLU writing codes, then the 8-bit conv reading them: one half of
+    # a residual block on the 8-bit path, against the oracle's own codes
+    shape, cout, scale = (1, 128, 3, 12, 20), 128, 3.0 / 448
+    print(f"[case] norm->e4m3->conv {shape}", flush=True)
+    x = I.quantize(I.normal(shape, 19, "bx"), "bf16")
+    g = I.norm_gamma(128, 19, "bg", "bf16")
+    wf = I.conv_weight(cout, 128, (3, 3, 3), 19, "bw", "bf16")
+    b = I.conv_bias(cout, 19, "bb", "bf16")
+    wq_dev, ws_dev = L.wvc_quantize_rows_e4m3(to_dev(wf))
+    q = L.wvc_rmsnorm_silu_e4m3(to_dev(x), to_dev(g), scale)
+    y = to_host(L.wvc_causal_conv3d_e4m3_fwd(q, scale, wq_dev, ws_dev, bias=to_dev(b)))
+    _, xq = oracle.norm_silu_e4m3(f64(x), f64(g), None, scale=scale)
+    wq, ws = oracle.quantize_conv_weights_e4m3(wf)
+    ref = oracle.causal_conv3d_e4m3(xq, scale, wq, ws, f64(b))
+    check_e4m3_conv(y, ref, "norm->e4m3->conv")
+    # and the 8-bit half stays close to the bf16 reference of the same layer
+    ref_bf = oracle.causal_conv3d(oracle.norm_silu(f64(x), f64(g)), f64(wf), f64(b))
+    rel = oracle.rel_l2(y, ref_bf)
+    print(f"[parity] 8-bit vs unquantised layer rel_l2={rel:.3e}", flush=True)
+    assert rel < 0.1
+
+
+def test_conv_e4m3_full_size_sampled():
+    # the 384-channel layer at 240x416, 17 frames, as the bench times it
+    shape = (1, 384, 17, 240, 416)
+    d = I.e4m3_conv_inputs(seed=7, shape=shape, cout=384, with_cache=False)
+    print(f"[case] e4m3 conv full size {shape}", flush=True)
+    y = run_conv(d, packed=True, residual=False, cache=False)
+    idx = I.sample_indices((1, 384, 17, 240, 416), 3000, 20, include_frames=[0, 16])
+    coords = [torch.from_numpy(a).to(dev()) for a in np.unravel_index(idx, shape)]
+    got = y[tuple(coords)].float().cpu().numpy().astype(np.float64)
+    ref = oracle.causal_conv3d_e4m3_points(d["x"], d["x_scale"], d["w"], d["w_scale"], idx,
+                                           f64(d["b"]))
+    check_e4m3_conv(got, ref, "e4m3 conv 384 full size (sampled)")

@@ -22,7 +22,7 @@ LIB_PATH = os.path.join(_HERE, "libwvc.so")
 
 WVC_OK, WVC_ERR_ARG, WVC_ERR_UNSUPPORTED, WVC_ERR_ALIAS, WVC_ERR_WORKSPACE, WVC_ERR_STRICT, \
     WVC_ERR_HIP = range(7)
-WVC_F32, WVC_BF16 = 0, 1
+WVC_F32, WVC_BF16, WVC_E4M3 = 0, 1, 2
 WVC_WEIGHT_STANDARD, WVC_WEIGHT_PACKED = 0, 1
 ERROR_NAMES = {0: "WVC_OK", 1: "WVC_ERR_ARG", 2: "WVC_ERR_UNSUPPORTED", 3: "WVC_ERR_ALIAS",
                4: "WVC_ERR_WORKSPACE", 5: "WVC_ERR_STRICT", 6: "WVC_ERR_HIP"}
@@ -37,6 +37,8 @@ EXPORTED = (
     "wvc_reset_counters", "wvc_last_error", "wvc_version", "wvc_graph_capture_begin",
     "wvc_graph_capture_end", "wvc_graph_launch", "wvc_graph_destroy",
     "wvc_tile_extract", "wvc_tile_blend", "wvc_tile_blend_finish",
+    "wvc_causal_conv3d_e4m3_fwd", "wvc_quantize_e4m3", "wvc_quantize_rows_e4m3",
+    "wvc_rmsnorm_silu_e4m3",
 )
 
 
@@ -135,6 +137,15 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.wvc_graph_launch.restype = i
     lib.wvc_graph_destroy.argtypes = [vp]
     lib.wvc_graph_destroy.restype = i
+    lib.wvc_causal_conv3d_e4m3_fwd.argtypes = [dptr, vp, f, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.wvc_causal_conv3d_e4m3_fwd.restype = i
+    i64 = ctypes.c_int64
+    lib.wvc_quantize_e4m3.argtypes = [vp, i, i64, f, vp, vp]
+    lib.wvc_quantize_e4m3.restype = i
+    lib.wvc_quantize_rows_e4m3.argtypes = [vp, i, i64, i64, vp, vp, vp]
+    lib.wvc_quantize_rows_e4m3.restype = i
+    lib.wvc_rmsnorm_silu_e4m3.argtypes = [vp, vp, vp, vp, i, i, i, i, i, f, i, f, vp]
+    lib.wvc_rmsnorm_silu_e4m3.restype = i
     _lib = lib
     return lib
 
@@ -158,7 +169,9 @@ def _dtype_code(dt: torch.dtype) -> int:
         return WVC_BF16
     if dt == torch.float32:
         return WVC_F32
-    raise TypeError(f"unsupported dtype {dt}: bfloat16 or float32")
+    if dt == torch.uint8:  # E4M3 codes
+        return WVC_E4M3
+    raise TypeError(f"unsupported dtype {dt}: bfloat16, float32 or uint8 (E4M3 codes)")
 
 
 def _need_cl(t: Optional[torch.Tensor], name: str, ndim: int = 5):
@@ -306,6 +319,99 @@ def wvc_causal_conv3d_fwd(x: torch.Tensor, weight: torch.Tensor, bias: Optional[
                                       _ptr(wsrc), _ptr(bias), _ptr(residual), _ptr(y),
                                       _ptr(workspace), ws_bytes, _stream(x)))
     return y
+
+
+def wvc_causal_conv3d_e4m3_fwd(x: torch.Tensor, x_scale: float, weight: torch.Tensor,
+                               w_scale: torch.Tensor, bias: Optional[torch.Tensor] = None,
+                               cache_in: Optional[torch.Tensor] = None,
+                               cache_out: Optional[torch.Tensor] = None,
+                               residual: Optional[torch.Tensor] = None,
+                               y: Optional[torch.Tensor] = None,
+                               workspace: Optional[torch.Tensor] = None,
+                               packed_weight: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Causal 3x3x3 conv of E4M3 operands (see wvc_causal_conv3d_e4m3_fwd in
+    include/wvc.h).  x, caches and weight are uint8 tensors of E4M3 codes in
+    channels_last_3d; w_scale is a float32 vector [C_out]; bias, residual and
+    y are bfloat16.  Returns y (allocated if not given)."""
+    lib = load()
+    _need_cl(x, "x")
+    _need_cl(weight, "weight")
+    for name, t in (("cache_in", cache_in), ("cache_out", cache_out), ("residual", residual),
+                    ("y", y)):
+        _need_cl(t, name)
+    _need_vec(bias, "bias", weight.shape[0])
+    _need_vec(w_scale, "w_scale", weight.shape[0])
+    if x.dtype != torch.uint8 or weight.dtype != torch.uint8 or w_scale.dtype != torch.float32:
+        raise TypeError("x and weight must be uint8 (E4M3 codes), w_scale float32")
+    layout = WVC_WEIGHT_STANDARD if packed_weight is None else WVC_WEIGHT_PACKED
+    d = conv_desc(tuple(x.shape), tuple(weight.shape), WVC_E4M3, weight_layout=layout)
+    wsrc = weight if packed_weight is None else packed_weight
+    if y is None:
+        y = empty_cl((x.shape[0], weight.shape[0], x.shape[2], x.shape[3], x.shape[4]),
+                     torch.bfloat16, x.device)
+    ws_bytes = 0
+    if workspace is None:
+        need = wvc_causal_conv3d_workspace_bytes(d)
+        if need:
+            workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    if workspace is not None:
+        ws_bytes = workspace.numel() * workspace.element_size()
+    _check(lib.wvc_causal_conv3d_e4m3_fwd(ctypes.byref(d), _ptr(x), float(x_scale), _ptr(cache_in),
+                                           _ptr(cache_out), _ptr(wsrc), _ptr(w_scale), _ptr(bias),
+                                           _ptr(residual), _ptr(y), _ptr(workspace), ws_bytes,
+                                           _stream(x)))
+    return y
+
+
+def wvc_quantize_e4m3(x: torch.Tensor, scale: float, q: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """E4M3 codes of fl32(x * fl32(1/scale)), same shape and strides as x (uint8)."""
+    if not x.is_cuda or not x.is_contiguous(memory_format=torch.channels_last_3d if x.dim() == 5
+                                            else torch.contiguous_format):
+        raise ValueError("x must be a dense device tensor")
+    if q is None:
+        q = torch.empty_like(x, dtype=torch.uint8)
+    _check(load().wvc_quantize_e4m3(_ptr(x), _dtype_code(x.dtype), x.numel(), float(scale), _ptr(q),
+                                    _stream(x)))
+    return q
+
+
+def wvc_quantize_rows_e4m3(x: torch.Tensor, q: Optional[torch.Tensor] = None,
+                           scale: Optional[torch.Tensor] = None):
+    """Per-row absmax quantisation of a tensor viewed as [shape[0], rest] in its
+    memory order (conv weights in channels_last_3d: one row per output
+    channel).  Returns (codes uint8 like x, scales float32 [shape[0]])."""
+    if not x.is_cuda:
+        raise ValueError("x must be a device tensor")
+    mf = torch.channels_last_3d if x.dim() == 5 else torch.contiguous_format
+    if not x.is_contiguous(memory_format=mf):
+        raise ValueError("x must be dense (channels_last_3d for 5-d tensors)")
+    rows = x.shape[0]
+    if q is None:
+        q = torch.empty_like(x, dtype=torch.uint8)
+    if scale is None:
+        scale = torch.empty(rows, dtype=torch.float32, device=x.device)
+    _check(load().wvc_quantize_rows_e4m3(_ptr(x), _dtype_code(x.dtype), rows, x.numel() // max(rows, 1),
+                                         _ptr(q), _ptr(scale), _stream(x)))
+    return q, scale
+
+
+def wvc_rmsnorm_silu_e4m3(x: torch.Tensor, gamma: torch.Tensor, scale: float,
+                          beta: Optional[torch.Tensor] = None, q: Optional[torch.Tensor] = None,
+                          eps: float = 1e-12, apply_silu: bool = True) -> torch.Tensor:
+    """RMS norm (+ SiLU) of a bf16 tensor, stored as E4M3 codes of
+    fl32(y * fl32(1/scale)) (see wvc_rmsnorm_silu_e4m3 in include/wvc.h)."""
+    _need_cl(x, "x")
+    _need_cl(q, "q")
+    n, c, t, h, w = x.shape
+    _need_vec(gamma, "gamma", c)
+    _need_vec(beta, "beta", c)
+    if x.dtype != torch.bfloat16:
+        raise TypeError("x must be bfloat16")
+    if q is None:
+        q = empty_cl(x.shape, torch.uint8, x.device)
+    _check(load().wvc_rmsnorm_silu_e4m3(_ptr(x), _ptr(gamma), _ptr(beta), _ptr(q), n, c, t, h, w,
+                                        float(eps), int(bool(apply_silu)), float(scale), _stream(x)))
+    return q
 
 
 def wvc_rmsnorm_silu(x: torch.Tensor, gamma: torch.Tensor, beta: Optional[torch.Tensor] = None,

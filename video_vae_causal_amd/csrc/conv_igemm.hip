@@ -49,6 +49,17 @@
 //   mapping   : workgroup ids are remapped so each XCD (own L2) receives a
 //               contiguous run of tiles: splits and channel tiles of one
 //               spatial tile, then its neighbours, share that XCD's L2.
+//
+// 8-bit variant (FP8): activations, cache and weights are OCP E4M3 codes (the
+// quantised Conv3D of "Cosmos3 Wan VAE", sections 7 and 9, in the format
+// gfx950's matrix cores read).  A work unit is then 64 input channels: its
+// halo slice is the same 64 bytes per position as a 32-channel bf16 unit, so
+// staging, LDS layout and weight fragments are unchanged byte for byte, and
+// the two 16-byte fragments a lane holds for the two bf16 K-steps form the
+// 32-byte operand of one v_mfma_f32_32x32x64_f8f6f4 (64 channels per MFMA,
+// twice the bf16 rate).  The sum is exact products accumulated in fp32; the
+// epilogue (or the split-K reduce) multiplies it by x_scale * w_scale[co]
+// before the bias.
 #include <type_traits>
 
 #include "wvc_internal.h"
@@ -60,19 +71,23 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
 
 constexpr int POS_T = 256;
 constexpr uint32_t OOB = 0x80000000u;  // an offset past every buffer range used here
 constexpr int RSRC_WORD3 = 0x00020000;  // raw buffer, range-checked (CDNA data format)
 
 struct IgParams {
-    const uint16_t *x;
-    const uint16_t *cache;
+    const void *x;      // bf16 or E4M3 codes
+    const void *cache;  // same type as x
     const uint16_t *w;
     const uint16_t *bias;
     const uint16_t *res;
     uint16_t *y;
-    uint16_t *cache_out;
+    void *cache_out;    // same type as x
+    const float *wscale;  // E4M3: per-output-channel weight scale [Cout]
+    float xscale;         // E4M3: activation scale
     float *part;  // split-K partial sums: [S][N][T][H][W][Cout] fp32
     size_t part_stride;  // N*T*H*W*Cout: elements of one split's partials
     int T, H, W, Cin, Cout, F;
@@ -132,6 +147,12 @@ struct Mfma<32> {
     }
 };
 
+// 32x32x64 MFMA of E4M3 operands (format 0 for A and B, no block scales):
+// lane l holds 32 codes of A row / B column l % 32.
+__device__ __forceinline__ f32x16 mfma_e4m3(i32x8 a, i32x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
 template <int N>
 using Int = std::integral_constant<int, N>;
 
@@ -176,9 +197,10 @@ struct Geo {
 //   during the row two rows back, and the halo written at the end of a stage
 //   during that stage's first row, so every wait covers loads at least a row
 //   old.
-template <int KS, int CO_T, int M, int WAVES_CO, bool SPLIT, int TW>
+template <int KS, int CO_T, int M, int WAVES_CO, bool SPLIT, int TW, bool FP8 = false>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 igemm_kernel(IgParams p) {
+    static_assert(!FP8 || M == 32, "the 8-bit path uses 32x32x64 MFMAs");
     using MF = Mfma<M>;
     using G = Geo<KS, TW>;
     using acc_t = typename MF::acc_t;
@@ -192,6 +214,11 @@ igemm_kernel(IgParams p) {
     constexpr int KSTEPS = M / 16;  // MFMA K-steps per 32-channel block
     constexpr int GPL = 64 / M;     // 8-channel groups spanned by one K-step
     constexpr int FRAG = 1024;      // bytes of one packed A fragment
+    constexpr int ESZ = FP8 ? 1 : 2;       // bytes per activation element
+    constexpr int CPE = 16 / ESZ;          // channels per 16-byte LDS entry
+    constexpr int CB = 4 * CPE;            // channels per work unit
+    constexpr int KA = FP8 ? 1 : KSTEPS;   // MFMAs per (tap, block, column tile)
+    using frag_t = std::conditional_t<FP8, i32x8, bf16x8>;
     static_assert(WCO % M == 0 && WPOS % M == 0, "wave tile must be whole MFMA tiles");
     static_assert(TW % M == 0 || M % TW == 0, "MFMA columns must tile the tile rows");
     static_assert(WPOS % TW == 0, "a wave's positions must start on a tile row");
@@ -200,6 +227,7 @@ igemm_kernel(IgParams p) {
 
     __shared__ uint4 halo[2][4 * HPAD];
     __shared__ uint2 bias_s[CO_T / 4];  // this channel tile's bias, read by the epilogue
+    __shared__ float4 scale_s[FP8 ? CO_T / 4 : 1];  // x_scale * w_scale[co] (8-bit path)
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
@@ -233,9 +261,15 @@ igemm_kernel(IgParams p) {
     const int co0 = ct * CO_T + wco * WCO;
     const int u0 = SPLIT ? (s * p.U) / p.S : 0;
     const int u1 = SPLIT ? ((s + 1) * p.U) / p.S : p.U;
-    if (!SPLIT && tid < CO_T / 4)
+    if (!SPLIT && tid < CO_T / 4) {
         bias_s[tid] = p.bias ? *reinterpret_cast<const uint2 *>(p.bias + ct * CO_T + tid * 4)
                              : make_uint2(0u, 0u);
+        if constexpr (FP8) {
+            const float4 ws = *reinterpret_cast<const float4 *>(p.wscale + ct * CO_T + tid * 4);
+            scale_s[tid] = make_float4(p.xscale * ws.x, p.xscale * ws.y, p.xscale * ws.z,
+                                       p.xscale * ws.w);
+        }
+    }
 
     // Staging: slot k of this thread is halo position (tid>>2) + 64k of
     // group g, LDS entry lbase + 64k (slots past HP are padding).
@@ -248,7 +282,7 @@ igemm_kernel(IgParams p) {
         const int r = hp / HC, c = hp - r * HC;
         const int hs = h0 + r - PAD, ws = w0 + c - PAD;
         const bool inframe = hp < HP && hs >= 0 && hs < p.H && ws >= 0 && ws < p.W;
-        soff[k] = inframe ? (uint32_t)(((hs * p.W + ws) * p.Cin + g * 8) * 2) : OOB;
+        soff[k] = inframe ? (uint32_t)((hs * p.W + ws) * p.Cin * ESZ + g * 16) : OOB;
         if (inframe && r >= PAD && r < PAD + G::TH && c >= PAD && c < PAD + TW) interior |= 1u << k;
     }
     // B fragments: LDS entry of this lane's position (first MFMA column tile,
@@ -264,7 +298,8 @@ igemm_kernel(IgParams p) {
     // wco * FCO.  A row (unit, kh) is one contiguous run of KS fragment groups.
     const uint32_t wlane = (uint32_t)((wco * FCO * KSTEPS) * FRAG + lane * 16);
     const __amdgpu_buffer_rsrc_t wr = rsrc(p.w, p.w_bytes);
-    const size_t frame_elems = (size_t)p.frame_bytes / 2;
+    const char *xb = static_cast<const char *>(p.x);
+    const char *cb_base = static_cast<const char *>(p.cache);
     // Cache update: the workgroups of the chunk's last output frame write the
     // halo interiors they stage for frames T-2 and T-1, each channel tile the
     // 32-channel blocks cb with cb % co_tiles == its tile (balanced work).
@@ -278,9 +313,21 @@ igemm_kernel(IgParams p) {
 #pragma unroll
             for (int e = 0; e < ACC; ++e) acc[i][j][e] = 0.f;
 
-    bf16x8 A[3][KS][FCO][KSTEPS];  // three row sets: [set][kw][co tile][K-step]
-    bf16x8 B[2][FPOS][KSTEPS];     // two tap sets: tap k reads B[k & 1]
+    // bf16: one fragment per K-step.  8-bit: one 32-byte operand whose halves
+    // are the 16-byte fragments of K-steps 0 and 1.
+    frag_t A[3][KS][FCO][KA];  // three row sets: [set][kw][co tile][K-step]
+    frag_t B[2][FPOS][KA];     // two tap sets: tap k reads B[k & 1]
     uint4 hv[NIT];
+    auto put = [](frag_t &dst, int ks, uint4 v) {
+        if constexpr (FP8) {
+            if (ks == 0)
+                dst.lo = __builtin_bit_cast(i32x4, v);
+            else
+                dst.hi = __builtin_bit_cast(i32x4, v);
+        } else {
+            dst = as_bf16x8(v);
+        }
+    };
 
     auto load_row = [&](auto set_tag, int rho) {
         constexpr int SET = decltype(set_tag)::value;
@@ -292,8 +339,8 @@ igemm_kernel(IgParams p) {
             for (int f = 0; f < FCO; ++f)
 #pragma unroll
                 for (int ks = 0; ks < KSTEPS; ++ks)
-                    A[SET][kw][f][ks] = as_bf16x8(bload_s(wr, wlane + (f * KSTEPS + ks) * FRAG,
-                                                          row + kw * NBLK * KSTEPS * FRAG));
+                    put(A[SET][kw][f][FP8 ? 0 : ks], ks,
+                        bload_s(wr, wlane + (f * KSTEPS + ks) * FRAG, row + kw * NBLK * KSTEPS * FRAG));
     };
     // One A fragment of row rho (IDX = (kw*FCO + f)*KSTEPS + ks) into set SET.
     auto load_a_one = [&](auto set_tag, auto idx_tag, int rho) {
@@ -302,54 +349,54 @@ igemm_kernel(IgParams p) {
         constexpr int kw = IDX / (FCO * KSTEPS), f = (IDX / KSTEPS) % FCO, ks = IDX % KSTEPS;
         const int u = u0 + rho / KS, kh = rho % KS;
         const uint32_t row = (uint32_t)((((ct * p.U + u) * KS + kh) * KS) * NBLK * KSTEPS) * FRAG;
-        A[SET][kw][f][ks] = as_bf16x8(bload_s(wr, wlane + (f * KSTEPS + ks) * FRAG,
-                                              row + kw * NBLK * KSTEPS * FRAG));
+        put(A[SET][kw][f][FP8 ? 0 : ks], ks,
+            bload_s(wr, wlane + (f * KSTEPS + ks) * FRAG, row + kw * NBLK * KSTEPS * FRAG));
     };
     // The next stage's halo, one staging slot at a time (halo_setup first).
     __amdgpu_buffer_rsrc_t hfr = rsrc(p.x, 0u);
     uint32_t hcb2 = 0;
     bool hgok = false;
     auto halo_setup = [&](int u) {
-        const int kt = u % KS, cb = (u / KS) * 32;
+        const int kt = u % KS, cb = (u / KS) * CB;
         const int ts = t - (KS - 1) + kt;
         if (ts >= 0)
-            hfr = rsrc(p.x + (size_t)(n * p.T + ts) * frame_elems, p.frame_bytes);
+            hfr = rsrc(xb + (size_t)(n * p.T + ts) * p.frame_bytes, p.frame_bytes);
         else if (p.cache)
-            hfr = rsrc(p.cache + (size_t)(n * p.F + p.F + ts) * frame_elems, p.frame_bytes);
+            hfr = rsrc(cb_base + (size_t)(n * p.F + p.F + ts) * p.frame_bytes, p.frame_bytes);
         else
             hfr = rsrc(p.x, 0u);  // zero causal padding: every load reads zero
-        hcb2 = (uint32_t)cb * 2;
-        hgok = cb + g * 8 < p.Cin;
+        hcb2 = (uint32_t)cb * ESZ;
+        hgok = cb + g * CPE < p.Cin;
     };
     auto halo_one = [&](auto k_tag) {
         constexpr int k = decltype(k_tag)::value;
         hv[k] = bload(hfr, (hgok && soff[k] != OOB) ? soff[k] + hcb2 : OOB);
     };
     auto load_halo = [&](int u) {
-        const int kt = u % KS, cb = (u / KS) * 32;
+        const int kt = u % KS, cb = (u / KS) * CB;
         const int ts = t - (KS - 1) + kt;
         __amdgpu_buffer_rsrc_t fr;
         if (ts >= 0)
-            fr = rsrc(p.x + (size_t)(n * p.T + ts) * frame_elems, p.frame_bytes);
+            fr = rsrc(xb + (size_t)(n * p.T + ts) * p.frame_bytes, p.frame_bytes);
         else if (p.cache)
-            fr = rsrc(p.cache + (size_t)(n * p.F + p.F + ts) * frame_elems, p.frame_bytes);
+            fr = rsrc(cb_base + (size_t)(n * p.F + p.F + ts) * p.frame_bytes, p.frame_bytes);
         else
             fr = rsrc(p.x, 0u);  // zero causal padding: every load reads zero
-        const bool gok = cb + g * 8 < p.Cin;
+        const bool gok = cb + g * CPE < p.Cin;
 #pragma unroll
         for (int k = 0; k < NIT; ++k)
-            hv[k] = bload(fr, (gok && soff[k] != OOB) ? soff[k] + (uint32_t)cb * 2 : OOB);
+            hv[k] = bload(fr, (gok && soff[k] != OOB) ? soff[k] + (uint32_t)cb * ESZ : OOB);
     };
     auto store_halo = [&](int u, int buf) {
 #pragma unroll
         for (int k = 0; k < NIT; ++k) halo[buf][lbase + 64 * k] = hv[k];
-        const int kt = u % KS, cb = (u / KS) * 32;
-        if (write_cache && kt >= 1 && (u / KS) % p.co_tiles == ct && cb + g * 8 < p.Cin) {
-            uint16_t *dst = p.cache_out + (size_t)(n * 2 + kt - 1) * frame_elems + cb;
+        const int kt = u % KS, cb = (u / KS) * CB;
+        if (write_cache && kt >= 1 && (u / KS) % p.co_tiles == ct && cb + g * CPE < p.Cin) {
+            char *dst = static_cast<char *>(p.cache_out) + (size_t)(n * 2 + kt - 1) * p.frame_bytes +
+                        (size_t)cb * ESZ;
 #pragma unroll
             for (int k = 0; k < NIT; ++k)
-                if (interior & (1u << k))
-                    *reinterpret_cast<uint4 *>(reinterpret_cast<char *>(dst) + soff[k]) = hv[k];
+                if (interior & (1u << k)) *reinterpret_cast<uint4 *>(dst + soff[k]) = hv[k];
         }
     };
     // LDS entry offset of MFMA column tile j relative to column tile 0.
@@ -358,7 +405,7 @@ igemm_kernel(IgParams p) {
         constexpr int BS = decltype(set_tag)::value;
 #pragma unroll
         for (int ks = 0; ks < KSTEPS; ++ks)
-            B[BS][j][ks] = as_bf16x8(hb[offj(j) + ks * GPL * HPAD + kh * HC + kw]);
+            put(B[BS][j][FP8 ? 0 : ks], ks, hb[offj(j) + ks * GPL * HPAD + kh * HC + kw]);
     };
 
     const int R = (u1 - u0) * KS;  // rows this workgroup runs
@@ -388,17 +435,21 @@ igemm_kernel(IgParams p) {
             constexpr int cur = tp & 1;
             constexpr bool next_in_stage = tp + 1 < KS * KS;
             constexpr int nkh = (tp + 1) / KS, nkw = (tp + 1) % KS;
-            static_for<KSTEPS>([&](auto ks_tag) {
+            static_for<KA>([&](auto ks_tag) {
                 constexpr int ks = decltype(ks_tag)::value;
                 static_for<FPOS>([&](auto j_tag) {
                     constexpr int j = decltype(j_tag)::value;
 #pragma unroll
-                    for (int i = 0; i < FCO; ++i)
-                        acc[i][j] = MF::run(A[SET][kw][i][ks], B[cur][j][ks], acc[i][j]);
+                    for (int i = 0; i < FCO; ++i) {
+                        if constexpr (FP8)
+                            acc[i][j] = mfma_e4m3(A[SET][kw][i][0], B[cur][j][0], acc[i][j]);
+                        else
+                            acc[i][j] = MF::run(A[SET][kw][i][ks], B[cur][j][ks], acc[i][j]);
+                    }
                     if (ks == 0 && next_in_stage) load_b(Int<cur ^ 1>{}, hb, j, nkh, nkw);
                     // group index within the row, and the loads that fall on it
-                    constexpr int NG = KS * KSTEPS * FPOS, NL = KS * FCO * KSTEPS;
-                    constexpr int grp = (kw * KSTEPS + ks) * FPOS + j;
+                    constexpr int NG = KS * KA * FPOS, NL = KS * FCO * KSTEPS;
+                    constexpr int grp = (kw * KA + ks) * FPOS + j;
                     static_for<NL>([&](auto li) {
                         constexpr int L_ = decltype(li)::value;
                         if constexpr ((L_ * NG) / NL == grp)
@@ -519,8 +570,15 @@ igemm_kernel(IgParams p) {
                 const int co = co0 + i * M + e4 * 8 + lg * 4;
                 float v[4] = {acc[i][j][e4 * 4], acc[i][j][e4 * 4 + 1], acc[i][j][e4 * 4 + 2],
                               acc[i][j][e4 * 4 + 3]};
-                // the sum, then the bias, then the residual: the order the
-                // split-K reduce kernel uses too
+                // the sum (times the scales on the 8-bit path), then the bias,
+                // then the residual: the order the split-K reduce kernel uses too
+                if constexpr (FP8) {
+                    const float4 sc = scale_s[(wco * WCO + i * M + e4 * 8 + lg * 4) / 4];
+                    v[0] *= sc.x;
+                    v[1] *= sc.y;
+                    v[2] *= sc.z;
+                    v[3] *= sc.w;
+                }
                 if (p.bias) {
                     v[0] += bf16_to_f32(bb[i][e4].x & 0xffffu);
                     v[1] += bf16_to_f32(bb[i][e4].x >> 16);
@@ -542,13 +600,16 @@ igemm_kernel(IgParams p) {
 }
 
 // Split-K reduction: y = round(sum_s part[s] (in split order) + bias + residual),
-// 8 consecutive channels (one 16-byte output store) per thread.
+// 8 consecutive channels (one 16-byte output store) per thread.  On the 8-bit
+// path (wscale given) the sum is multiplied by xscale * wscale[co] first.
 __global__ void __launch_bounds__(256) splitk_reduce_kernel(const float *__restrict__ part,
                                                             size_t stride, int S,
                                                             const uint16_t *__restrict__ bias,
                                                             const uint16_t *__restrict__ res,
                                                             uint16_t *__restrict__ y, long groups,
-                                                            int cout) {
+                                                            int cout,
+                                                            const float *__restrict__ wscale = nullptr,
+                                                            float xscale = 1.f) {
     const long gi = (long)blockIdx.x * 256 + threadIdx.x;
     if (gi >= groups) return;
     const size_t e0 = (size_t)gi * 8;
@@ -574,6 +635,13 @@ __global__ void __launch_bounds__(256) splitk_reduce_kernel(const float *__restr
                 v[4] += b[u][0]; v[5] += b[u][1]; v[6] += b[u][2]; v[7] += b[u][3];
             }
     }
+    if (wscale) {
+        const float4 s0 = *reinterpret_cast<const float4 *>(wscale + co);
+        const float4 s1 = *reinterpret_cast<const float4 *>(wscale + co + 4);
+        const float sc[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+#pragma unroll
+        for (int k = 0; k < 8; ++k) v[k] *= xscale * sc[k];
+    }
     const uint32_t bw[4] = {bv.x, bv.y, bv.z, bv.w}, rw[4] = {rv.x, rv.y, rv.z, rv.w};
     uint32_t o[4];
 #pragma unroll
@@ -594,18 +662,19 @@ __global__ void __launch_bounds__(256) splitk_reduce_kernel(const float *__restr
 
 // Packs W[co][tap][ci] into the order the kernel reads, for channel tile CO_T
 // and MFMA tile edge M:
-//   packed[co tile][unit][kh][kw][block][ks][lane][8 channels]
-// with unit = (32-channel block cb) * KS + kt, block < CO_T/M, ks < M/16,
-// lane < 64; row co = tile*CO_T + block*M + lane % M, channel
-// 32*cb + ks*(64/M)*8 + (lane / M)*8; zero past C_in.  One fragment (one wave
-// load) is 1 KiB contiguous, and one kernel row (unit, kh) of a channel tile
-// is one contiguous run.
-template <int M>
-__global__ void __launch_bounds__(256) pack_weights_kernel(const uint16_t *__restrict__ w,
+//   packed[co tile][unit][kh][kw][block][ks][lane][16 bytes]
+// with unit = (channel block cb) * KS + kt, block < CO_T/M, ks < M/16,
+// lane < 64; row co = tile*CO_T + block*M + lane % M.  A 16-byte entry holds
+// E = 8 bf16 or 16 E4M3 channels: channel 4E*cb + ks*(64/M)*E + (lane / M)*E
+// onwards; zero past C_in.  One fragment (one wave load) is 1 KiB contiguous,
+// and one kernel row (unit, kh) of a channel tile is one contiguous run.
+template <int M, bool FP8 = false>
+__global__ void __launch_bounds__(256) pack_weights_kernel(const void *__restrict__ wv,
                                                            uint4 *__restrict__ out, int cout,
                                                            int cin, int ks_, int co_t) {
     constexpr int KSTEPS = M / 16, GPL = 64 / M;
-    const int nb = (cin + 31) / 32;
+    constexpr int E = FP8 ? 16 : 8;
+    const int nb = (cin + 4 * E - 1) / (4 * E);
     const int nblk = co_t / M, units = ks_ * nb, taps = ks_ * ks_ * ks_;
     const long chunks = (long)(cout / co_t) * units * ks_ * ks_ * nblk * KSTEPS * 64;
     for (long i = (long)blockIdx.x * 256 + threadIdx.x; i < chunks; i += (long)gridDim.x * 256) {
@@ -625,13 +694,20 @@ __global__ void __launch_bounds__(256) pack_weights_kernel(const uint16_t *__res
         const int kt = u % ks_, cb = u / ks_;
         const int tap = (kt * ks_ + kh) * ks_ + kw;
         const int co = ct * co_t + blk * M + lane % M;
-        const int ch = cb * 32 + ks * GPL * 8 + (lane / M) * 8;
-        uint16_t v[8];
+        const int ch = cb * 4 * E + ks * GPL * E + (lane / M) * E;
+        uint32_t wd[4] = {0u, 0u, 0u, 0u};
+        if constexpr (FP8) {
+            const uint8_t *w = static_cast<const uint8_t *>(wv);
 #pragma unroll
-        for (int k = 0; k < 8; ++k)
-            v[k] = ch + k < cin ? w[((size_t)co * taps + tap) * cin + ch + k] : (uint16_t)0;
-        out[i] = make_uint4(v[0] | ((uint32_t)v[1] << 16), v[2] | ((uint32_t)v[3] << 16),
-                            v[4] | ((uint32_t)v[5] << 16), v[6] | ((uint32_t)v[7] << 16));
+            for (int k = 0; k < 16; ++k)
+                if (ch + k < cin) wd[k / 4] |= (uint32_t)w[((size_t)co * taps + tap) * cin + ch + k] << (8 * (k % 4));
+        } else {
+            const uint16_t *w = static_cast<const uint16_t *>(wv);
+#pragma unroll
+            for (int k = 0; k < 8; ++k)
+                if (ch + k < cin) wd[k / 2] |= (uint32_t)w[((size_t)co * taps + tap) * cin + ch + k] << (16 * (k % 2));
+        }
+        out[i] = make_uint4(wd[0], wd[1], wd[2], wd[3]);
     }
 }
 
@@ -677,8 +753,14 @@ void choose_tile(int h, int w, int *th_out, int *tw_out) {
     *tw_out = btw;
 }
 
-int co_tile_for(int cout) {
+bool is_e4m3(const ConvCall &c) { return c.dtype == WVC_E4M3; }
+// Input channels per work unit: one 64-byte slice of a position's channels.
+int unit_channels(const ConvCall &c) { return is_e4m3(c) ? 64 : 32; }
+int act_bytes(const ConvCall &c) { return is_e4m3(c) ? 1 : 2; }
+
+int co_tile_for(int cout, bool e4m3 = false) {
     if (cout % 128 == 0) return 128;
+    if (e4m3) return 32;  // the 8-bit path has 32x32 MFMA tiles only
     if (cout % 96 == 0) return 96;
     if (cout % 64 == 0) return 64;
     return 32;  // the route requires cout % 32 == 0
@@ -690,8 +772,8 @@ Plan make_plan(const ConvCall &c, ConvRoute r) {
     choose_tile(c.h, c.w, &pl.th, &pl.tw);
     pl.tiles_h = (c.h + pl.th - 1) / pl.th;
     pl.tiles_w = (c.w + pl.tw - 1) / pl.tw;
-    pl.co_t = co_tile_for(c.cout);
-    pl.U = ks * ((c.cin + 31) / 32);
+    pl.co_t = co_tile_for(c.cout, is_e4m3(c));
+    pl.U = ks * ((c.cin + unit_channels(c) - 1) / unit_channels(c));
     const long spatial = (long)c.n * c.t * pl.tiles_h * pl.tiles_w;
     const long slots = num_cus();  // one workgroup per CU
     // Small grid (fewer tiles than resident slots): order channel tiles
@@ -735,13 +817,14 @@ struct PackGeom {
 };
 PackGeom pack_geom(const ConvCall &c) {
     if (proj_supports(c)) return PackGeom{c.cout, 16};
-    const int ct = co_tile_for(c.cout);
-    return PackGeom{ct, tile_m(ct)};
+    const int ct = co_tile_for(c.cout, is_e4m3(c));
+    return PackGeom{ct, is_e4m3(c) ? 32 : tile_m(ct)};
 }
 
 size_t packed_bytes(const ConvCall &c) {
-    const size_t nb = (size_t)(c.cin + 31) / 32;
-    return (size_t)c.cout * c.kt * c.kh * c.kw * nb * 32 * 2;
+    // one 64-byte slice per (output channel, tap, unit)
+    const size_t nb = (size_t)(c.cin + unit_channels(c) - 1) / unit_channels(c);
+    return (size_t)c.cout * c.kt * c.kh * c.kw * nb * 64;
 }
 
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
@@ -752,23 +835,23 @@ size_t ws_bytes_for(const Plan &pl, const ConvCall &c, bool need_pack) {
     return align256(part_bytes(pl, c)) + (need_pack ? align256(packed_bytes(c)) : 0);
 }
 
-template <int KS, int CO_T, int M, int WAVES_CO, int TW>
+template <int KS, int CO_T, int M, int WAVES_CO, int TW, bool FP8>
 hipError_t launch_tw(const IgParams &p, hipStream_t s) {
     if (p.S > 1)
-        hipLaunchKernelGGL((igemm_kernel<KS, CO_T, M, WAVES_CO, true, TW>), dim3(p.total), dim3(256), 0,
-                           s, p);
+        hipLaunchKernelGGL((igemm_kernel<KS, CO_T, M, WAVES_CO, true, TW, FP8>), dim3(p.total),
+                           dim3(256), 0, s, p);
     else
-        hipLaunchKernelGGL((igemm_kernel<KS, CO_T, M, WAVES_CO, false, TW>), dim3(p.total), dim3(256),
-                           0, s, p);
+        hipLaunchKernelGGL((igemm_kernel<KS, CO_T, M, WAVES_CO, false, TW, FP8>), dim3(p.total),
+                           dim3(256), 0, s, p);
     return hipGetLastError();
 }
 
-template <int KS, int CO_T, int M, int WAVES_CO>
+template <int KS, int CO_T, int M, int WAVES_CO, bool FP8 = false>
 hipError_t launch_variant(const IgParams &p, int tw, hipStream_t s) {
     switch (tw) {
-        case 8: return launch_tw<KS, CO_T, M, WAVES_CO, 8>(p, s);
-        case 16: return launch_tw<KS, CO_T, M, WAVES_CO, 16>(p, s);
-        case 32: return launch_tw<KS, CO_T, M, WAVES_CO, 32>(p, s);
+        case 8: return launch_tw<KS, CO_T, M, WAVES_CO, 8, FP8>(p, s);
+        case 16: return launch_tw<KS, CO_T, M, WAVES_CO, 16, FP8>(p, s);
+        case 32: return launch_tw<KS, CO_T, M, WAVES_CO, 32, FP8>(p, s);
         default: return hipErrorInvalidValue;
     }
 }
@@ -789,27 +872,31 @@ hipError_t launch_pack_weights(const ConvCall &c, const void *w, void *packed, h
     long blocks = (chunks + 255) / 256;
     if (blocks > 8192) blocks = 8192;
     if (blocks < 1) return hipSuccess;
-    if (m == 32)
-        hipLaunchKernelGGL(pack_weights_kernel<32>, dim3((unsigned)blocks), dim3(256), 0, s,
-                           static_cast<const uint16_t *>(w), static_cast<uint4 *>(packed), c.cout,
-                           c.cin, c.kt, co_t);
+    if (is_e4m3(c))
+        hipLaunchKernelGGL((pack_weights_kernel<32, true>), dim3((unsigned)blocks), dim3(256), 0, s,
+                           w, static_cast<uint4 *>(packed), c.cout, c.cin, c.kt, co_t);
+    else if (m == 32)
+        hipLaunchKernelGGL(pack_weights_kernel<32>, dim3((unsigned)blocks), dim3(256), 0, s, w,
+                           static_cast<uint4 *>(packed), c.cout, c.cin, c.kt, co_t);
     else
-        hipLaunchKernelGGL(pack_weights_kernel<16>, dim3((unsigned)blocks), dim3(256), 0, s,
-                           static_cast<const uint16_t *>(w), static_cast<uint4 *>(packed), c.cout,
-                           c.cin, c.kt, co_t);
+        hipLaunchKernelGGL(pack_weights_kernel<16>, dim3((unsigned)blocks), dim3(256), 0, s, w,
+                           static_cast<uint4 *>(packed), c.cout, c.cin, c.kt, co_t);
     return hipGetLastError();
 }
 
 bool igemm_supports(const ConvCall &c) {
     // 32-bit buffer offsets: one frame and the packed weights must stay below 2 GiB.
-    const size_t frame = (size_t)c.h * c.w * c.cin * 2;
+    const size_t frame = (size_t)c.h * c.w * c.cin * act_bytes(c);
     const size_t wbytes = packed_bytes(c);
+    if (is_e4m3(c) && (c.cin % 16 != 0 || c.kt != 3)) return false;
     return frame < ((size_t)1 << 31) && wbytes < ((size_t)1 << 31) && c.cout % 32 == 0;
 }
 
 hipError_t launch_conv_igemm(const ConvCall &c, ConvRoute r, bool packed_given, void *ws,
                              size_t ws_bytes, void *cache_out, hipStream_t s, ConvPartials *defer) {
     if (defer) *defer = ConvPartials{};
+    if (is_e4m3(c)) defer = nullptr;  // the fused consumers read bf16 sums without scales
+    if (is_e4m3(c) && r != ConvRoute::Fast3x3x3) return hipErrorInvalidValue;
     const Plan pl = make_plan(c, r);
     if (pl.th == 0) return hipErrorInvalidValue;
     if (ws_bytes < ws_bytes_for(pl, c, !packed_given) || (!ws && ws_bytes_for(pl, c, !packed_given)))
@@ -824,13 +911,15 @@ hipError_t launch_conv_igemm(const ConvCall &c, ConvRoute r, bool packed_given, 
     if (r == ConvRoute::Fast1x1x1 && proj_supports(c))
         return launch_conv_proj(c, wp, packed_bytes(c), s);
     IgParams p{};
-    p.x = static_cast<const uint16_t *>(c.x);
-    p.cache = static_cast<const uint16_t *>(c.cache_in);
+    p.x = c.x;
+    p.cache = c.cache_in;
     p.w = static_cast<const uint16_t *>(wp);
     p.bias = static_cast<const uint16_t *>(c.bias);
     p.res = static_cast<const uint16_t *>(c.residual);
     p.y = static_cast<uint16_t *>(c.y);
-    p.cache_out = r == ConvRoute::Fast3x3x3 ? static_cast<uint16_t *>(cache_out) : nullptr;
+    p.cache_out = r == ConvRoute::Fast3x3x3 ? cache_out : nullptr;
+    p.wscale = c.wscale;
+    p.xscale = c.xscale;
     p.T = c.t;
     p.H = c.h;
     p.W = c.w;
@@ -843,7 +932,7 @@ hipError_t launch_conv_igemm(const ConvCall &c, ConvRoute r, bool packed_given, 
     p.S = pl.S;
     p.U = pl.U;
     p.co_major = pl.co_major;
-    p.frame_bytes = (uint32_t)((size_t)c.h * c.w * c.cin * 2);
+    p.frame_bytes = (uint32_t)((size_t)c.h * c.w * c.cin * act_bytes(c));
     p.w_bytes = (uint32_t)packed_bytes(c);
     if (pl.S > 1) {
         p.part = static_cast<float *>(ws);
@@ -858,7 +947,10 @@ hipError_t launch_conv_igemm(const ConvCall &c, ConvRoute r, bool packed_given, 
     // 16x16x32 MFMAs on 2 x 2 waves (48 or 32 channels x 128 positions).
     // 32: 32x32x16 on 1 x 4 waves of 32 x 64.
     hipError_t e;
-    switch (pl.co_t) {
+    if (is_e4m3(c))
+        e = pl.co_t == 128 ? launch_variant<3, 128, 32, 2, true>(p, pl.tw, s)
+                           : launch_variant<3, 32, 32, 1, true>(p, pl.tw, s);
+    else switch (pl.co_t) {
         case 128: e = k3 ? launch_variant<3, 128, 32, 2>(p, pl.tw, s) : launch_variant<1, 128, 32, 2>(p, pl.tw, s); break;
         case 96: e = k3 ? launch_variant<3, 96, 16, 2>(p, pl.tw, s) : launch_variant<1, 96, 16, 2>(p, pl.tw, s); break;
         case 64: e = k3 ? launch_variant<3, 64, 16, 2>(p, pl.tw, s) : launch_variant<1, 64, 16, 2>(p, pl.tw, s); break;
@@ -875,7 +967,8 @@ hipError_t launch_conv_igemm(const ConvCall &c, ConvRoute r, bool packed_given, 
     const long blocks = (groups + 255) / 256;
     if (blocks > 0x7fffffffL) return hipErrorInvalidValue;
     hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)blocks), dim3(256), 0, s, p.part,
-                       p.part_stride, pl.S, p.bias, p.res, p.y, groups, c.cout);
+                       p.part_stride, pl.S, p.bias, p.res, p.y, groups, c.cout,
+                       is_e4m3(c) ? c.wscale : nullptr, c.xscale);
     return hipGetLastError();
 }
 

@@ -324,7 +324,7 @@ int num_cus_proj() {
 }  // namespace
 
 bool proj_supports(const ConvCall &c) {
-    return c.kt == 1 && c.kh == 1 && c.kw == 1 && c.cout % 16 == 0 && c.cout <= 256 &&
+    return c.dtype != WVC_E4M3 && c.kt == 1 && c.kh == 1 && c.kw == 1 && c.cout % 16 == 0 && c.cout <= 256 &&
            c.cin % 8 == 0 && (c.cin + 31) / 32 <= MAXQ &&
            ((size_t)PT * ((c.cin + 31) / 32 * 4 + 1) * 16) <= 64 * 1024;
 }

@@ -92,14 +92,18 @@ struct Partials {
 // FROM_PARTS: the input chunk is not read from x but built from partial sums,
 // x = round_bf16(sum over splits in order + bias), bit for bit what the
 // split-K reduce kernel stores (bf16 only).
-template <bool BF16, int K, bool STREAM, bool FROM_PARTS = false>
+// OUT8: the result is stored as E4M3 codes of fl32(y * qr), 8 bytes per chunk
+// of 8 channels (bf16 input only): the quantised conv's input written by the
+// norm itself, half the bytes of a bf16 store.
+template <bool BF16, int K, bool STREAM, bool FROM_PARTS = false, bool OUT8 = false>
 __global__ void __launch_bounds__(256) rmsnorm_flat_kernel(const uint4 *__restrict__ x,
                                                            const uint4 *__restrict__ gamma,
                                                            const uint4 *__restrict__ beta,
                                                            uint4 *__restrict__ y, long positions,
                                                            int cpp, int P, int R, float scale,
                                                            float eps, int apply_silu,
-                                                           Partials pp = Partials{}) {
+                                                           Partials pp = Partials{}, float qr = 1.f) {
+    static_assert(!OUT8 || BF16, "E4M3 output from bf16 input only");
     using V = Vec<BF16>;
     __shared__ float part[256 * K];
     __shared__ float rinv[256 * K];
@@ -201,21 +205,31 @@ __global__ void __launch_bounds__(256) rmsnorm_flat_kernel(const uint4 *__restri
                 const float u = fmaf(v[k][e] * r, g[e], b[e]);
                 o[e] = apply_silu ? silu<BF16>(u) : u;
             }
-            if (STREAM)
+            if constexpr (OUT8) {
+                const uint2 c8 = make_uint2(pack4_e4m3(o[0] * qr, o[1] * qr, o[2] * qr, o[3] * qr),
+                                            pack4_e4m3(o[4] * qr, o[5] * qr, o[6] * qr, o[7] * qr));
+                uint2 *q8 = reinterpret_cast<uint2 *>(y) + pos0 * cpp + f;
+                if (STREAM)
+                    __builtin_nontemporal_store(c8.x, &q8->x), __builtin_nontemporal_store(c8.y, &q8->y);
+                else
+                    *q8 = c8;
+            } else if (STREAM) {
                 st_stream(yb + f, V::pack(o));
-            else
+            } else {
                 yb[f] = V::pack(o);
+            }
         }
     }
 }
 
 // Any C: one thread per position, scalar loop (used when C is not a multiple
 // of the 16-byte vector, unaligned tensors, or more than FLAT_MAX_CPP chunks).
-template <bool BF16>
+template <bool BF16, bool OUT8 = false>
 __global__ void __launch_bounds__(256) rmsnorm_scalar_kernel(const void *xv, const void *gv,
                                                              const void *bv, void *yv,
                                                              long positions, int c, float scale,
-                                                             float eps, int apply_silu) {
+                                                             float eps, int apply_silu,
+                                                             float qr = 1.f) {
     const long pos = (long)blockIdx.x * 256 + threadIdx.x;
     if (pos >= positions) return;
     auto load = [](const void *p, long i) -> float {
@@ -231,7 +245,9 @@ __global__ void __launch_bounds__(256) rmsnorm_scalar_kernel(const void *xv, con
     for (int k = 0; k < c; ++k) {
         float u = load(xv, pos * c + k) * r * load(gv, k) + (bv ? load(bv, k) : 0.f);
         if (apply_silu) u = silu<BF16>(u);
-        if (BF16)
+        if (OUT8)
+            static_cast<uint8_t *>(yv)[pos * c + k] = to_e4m3(u * qr);
+        else if (BF16)
             static_cast<uint16_t *>(yv)[pos * c + k] = f32_to_bf16(u);
         else
             static_cast<float *>(yv)[pos * c + k] = u;
@@ -311,6 +327,44 @@ hipError_t launch_rmsnorm_silu_from_partials(const ConvPartials &pp, const void 
                        0, s, nullptr, static_cast<const uint4 *>(gamma),
                        static_cast<const uint4 *>(beta), static_cast<uint4 *>(y), positions, cpp, P,
                        R, sqrtf((float)c), eps, apply_silu, q);
+    return hipGetLastError();
+}
+
+hipError_t launch_rmsnorm_silu_e4m3(const void *x, const void *gamma, const void *beta, void *q,
+                                    long positions, int c, float eps, int apply_silu, float qr,
+                                    hipStream_t s) {
+    if (positions <= 0) return hipSuccess;
+    const float scale = sqrtf((float)c);
+    const bool aligned = ((uintptr_t)x % 16 == 0) && ((uintptr_t)q % 8 == 0) &&
+                         ((uintptr_t)gamma % 16 == 0) && ((uintptr_t)beta % 16 == 0);
+    if (c % 8 == 0 && aligned && c / 8 <= FLAT_MAX_CPP) {
+        const int cpp = c / 8;
+        const long chunks = positions * cpp;
+        const bool big = chunks >= 8L * 1024 * num_cus_norm();
+        const int K = big ? 2 : 1;
+        const int P = 256 * K / cpp;
+        int R = 1;
+        while (R < 64 && 2 * R * P <= 256 && 2 * R <= cpp) R *= 2;
+        const long blocks = (positions + P - 1) / P;
+        if (blocks > 0x7fffffffL) return hipErrorInvalidValue;
+        if (big)
+            hipLaunchKernelGGL((rmsnorm_flat_kernel<true, 2, true, false, true>), dim3((unsigned)blocks),
+                               dim3(256), 0, s, static_cast<const uint4 *>(x),
+                               static_cast<const uint4 *>(gamma), static_cast<const uint4 *>(beta),
+                               static_cast<uint4 *>(q), positions, cpp, P, R, scale, eps, apply_silu,
+                               Partials{}, qr);
+        else
+            hipLaunchKernelGGL((rmsnorm_flat_kernel<true, 1, false, false, true>), dim3((unsigned)blocks),
+                               dim3(256), 0, s, static_cast<const uint4 *>(x),
+                               static_cast<const uint4 *>(gamma), static_cast<const uint4 *>(beta),
+                               static_cast<uint4 *>(q), positions, cpp, P, R, scale, eps, apply_silu,
+                               Partials{}, qr);
+        return hipGetLastError();
+    }
+    const long blocks = (positions + 255) / 256;
+    if (blocks > 0x7fffffffL) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((rmsnorm_scalar_kernel<true, true>), dim3((unsigned)blocks), dim3(256), 0, s, x,
+                       gamma, beta, q, positions, c, scale, eps, apply_silu, qr);
     return hipGetLastError();
 }
 

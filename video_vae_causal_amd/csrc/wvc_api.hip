@@ -3,6 +3,7 @@
 // and per-thread error text.  Every argument error is reported before any
 // work is enqueued.
 #include <atomic>
+#include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
@@ -106,10 +107,13 @@ int plan_conv(const wvc_conv3d_desc *d, ConvPlan *pl, bool count = true) {
         if (count) g_rejected++;
         return fail(WVC_ERR_UNSUPPORTED, "groups=%d: only one group is supported", d->groups);
     }
-    const int e = elem_bytes(d->dtype);
+    // E4M3 calls: 1-byte codes in x, cache and weight; bf16 bias, residual, y.
+    const bool e4m3 = d->dtype == WVC_E4M3;
+    const int e = e4m3 ? 1 : elem_bytes(d->dtype);
+    const int eo = e4m3 ? 2 : e;
     if (!e) {
         if (count) g_rejected++;
-        return fail(WVC_ERR_UNSUPPORTED, "dtype %d is neither WVC_F32 nor WVC_BF16", d->dtype);
+        return fail(WVC_ERR_UNSUPPORTED, "dtype %d is not WVC_F32, WVC_BF16 or WVC_E4M3", d->dtype);
     }
     if (d->n < 1 || d->c_in < 1 || d->c_out < 1 || d->t < 0 || d->h < 1 || d->w < 1)
         return fail(WVC_ERR_ARG, "bad shape n=%d c_in=%d c_out=%d t=%d h=%d w=%d", d->n, d->c_in,
@@ -155,9 +159,9 @@ int plan_conv(const wvc_conv3d_desc *d, ConvPlan *pl, bool count = true) {
     ok = ok && mul_ok(plane_in, (size_t)d->n * frames, &v) && mul_ok(v, e, &pl->cache_bytes);
     ok = ok && mul_ok((size_t)d->c_out * d->c_in, (size_t)d->kt * d->kh * d->kw, &v) &&
          mul_ok(v, e, &pl->w_bytes);
-    ok = ok && mul_ok(plane_out, (size_t)d->n * to, &v) && mul_ok(v, e, &pl->y_bytes);
+    ok = ok && mul_ok(plane_out, (size_t)d->n * to, &v) && mul_ok(v, eo, &pl->y_bytes);
     if (!ok) return fail(WVC_ERR_ARG, "tensor size overflows");
-    pl->b_bytes = (size_t)d->c_out * e;
+    pl->b_bytes = (size_t)d->c_out * eo;
 
     const bool chan_ok = d->c_in % 8 == 0 && d->c_out % 32 == 0;
     const bool unit = d->stride_h == 1 && d->stride_w == 1 && d->stride_t == 1 &&
@@ -176,6 +180,19 @@ int plan_conv(const wvc_conv3d_desc *d, ConvPlan *pl, bool count = true) {
     if ((pl->route == wvc::ConvRoute::Fast3x3x3 || pl->route == wvc::ConvRoute::Fast1x1x1) &&
         !wvc::igemm_supports(c))
         pl->route = wvc::ConvRoute::Generic;
+    if (e4m3) {
+        // The 8-bit conv exists on the MFMA 3x3x3 route only.
+        const bool fits = d->c_in % 16 == 0 && d->c_out % 32 == 0 && unit && d->kt == 3 &&
+                          d->kh == 3 && d->kw == 3 && d->pad_h == 1 && d->pad_w == 1 && dil1 &&
+                          wvc::igemm_supports(c);
+        if (!fits) {
+            if (count) g_rejected++;
+            return fail(WVC_ERR_UNSUPPORTED,
+                        "E4M3 convs must be 3x3x3, stride 1, pad 1, dilation 1, C_in %% 16 == 0, "
+                        "C_out %% 32 == 0");
+        }
+        pl->route = wvc::ConvRoute::Fast3x3x3;
+    }
     if (d->weight_layout == WVC_WEIGHT_PACKED) {
         if (pl->route == wvc::ConvRoute::Generic) {
             if (count) g_rejected++;
@@ -197,12 +214,20 @@ int hip_status(hipError_t err, const char *what) {
 // launch_conv_igemm).
 int conv_fwd(const wvc_conv3d_desc *d, const void *x, const void *cache_in, void *cache_out,
              const void *weight, const void *bias, const void *residual, void *y, void *ws,
-             size_t ws_bytes, hipStream_t s, wvc::ConvPartials *defer = nullptr) {
+             size_t ws_bytes, hipStream_t s, wvc::ConvPartials *defer = nullptr,
+             float x_scale = 1.f, const float *w_scale = nullptr) {
     if (defer) *defer = wvc::ConvPartials{};
     ConvPlan pl;
     int rc = plan_conv(d, &pl);
     if (rc) return rc;
+    const bool e4m3 = d->dtype == WVC_E4M3;
     if (!weight) return fail(WVC_ERR_ARG, "weight is NULL");
+    if (e4m3) {
+        if (!w_scale || !aligned(w_scale, 16))
+            return fail(WVC_ERR_ARG, "w_scale must be a 16-byte aligned device array of C_out floats");
+        if (!(x_scale > 0.f) || !(x_scale < INFINITY))
+            return fail(WVC_ERR_ARG, "x_scale must be finite and > 0");
+    }
     // y is needed only when the chunk has output frames (a strided chunk may
     // have none: its frames only feed the cache).
     if (d->t > 0 && (!x || (pl.call.to > 0 && !y))) return fail(WVC_ERR_ARG, "x or y is NULL");
@@ -218,7 +243,9 @@ int conv_fwd(const wvc_conv3d_desc *d, const void *x, const void *cache_in, void
         const bool al = aligned(x, 16) && aligned(cache_in, 16) && aligned(weight, 16) &&
                         aligned(y, 16) && aligned(residual, 16) && aligned(bias, 8);
         if (!al) {
-            if (packed) return fail(WVC_ERR_ARG, "packed weights need 16-byte aligned tensors");
+            if (packed || e4m3)
+                return fail(WVC_ERR_ARG, "%s need 16-byte aligned tensors",
+                            e4m3 ? "E4M3 convs" : "packed weights");
             pl.route = wvc::ConvRoute::Generic;
         }
     }
@@ -235,8 +262,9 @@ int conv_fwd(const wvc_conv3d_desc *d, const void *x, const void *cache_in, void
         {residual, pl.y_bytes, false, "residual"},
         {y, pl.y_bytes, true, "y"},
         {ws, ws_bytes, true, "workspace"},
+        {w_scale, e4m3 ? (size_t)d->c_out * 4 : 0, false, "w_scale"},
     };
-    rc = check_aliasing(bufs, 8);
+    rc = check_aliasing(bufs, 9);
     if (rc) return rc;
 
     if (pl.route == wvc::ConvRoute::Generic && strict_on()) {
@@ -251,6 +279,8 @@ int conv_fwd(const wvc_conv3d_desc *d, const void *x, const void *cache_in, void
     c.bias = bias;
     c.residual = residual;
     c.y = y;
+    c.xscale = x_scale;
+    c.wscale = e4m3 ? w_scale : nullptr;
     hipError_t err = hipSuccess;
     bool cache_done = false;
     if (d->t > 0) {
@@ -267,7 +297,7 @@ int conv_fwd(const wvc_conv3d_desc *d, const void *x, const void *cache_in, void
     if (cache_out && !cache_done) {
         const size_t frame_elems = (size_t)d->h * d->w * d->c_in;
         err = wvc::launch_cache_update(x, cache_in, cache_out, d->n, d->t, c.frames, frame_elems,
-                                       elem_bytes(d->dtype), s);
+                                       e4m3 ? 1 : elem_bytes(d->dtype), s);
         if (err != hipSuccess) return hip_status(err, "cache update launch");
     }
     if (pl.route == wvc::ConvRoute::Fast3x3x3)
@@ -363,8 +393,23 @@ int wvc_causal_conv3d_fwd(const wvc_conv3d_desc *d, const void *x, const void *c
                           void *cache_out, const void *weight, const void *bias,
                           const void *residual, void *y, void *workspace, size_t workspace_bytes,
                           void *stream) {
+    if (d && d->dtype == WVC_E4M3) {
+        g_rejected++;
+        return fail(WVC_ERR_UNSUPPORTED, "E4M3 convs take wvc_causal_conv3d_e4m3_fwd (they need scales)");
+    }
     return conv_fwd(d, x, cache_in, cache_out, weight, bias, residual, y, workspace,
                     workspace_bytes, static_cast<hipStream_t>(stream));
+}
+
+int wvc_causal_conv3d_e4m3_fwd(const wvc_conv3d_desc *d, const void *x, float x_scale,
+                               const void *cache_in, void *cache_out, const void *weight,
+                               const float *w_scale, const void *bias, const void *residual,
+                               void *y, void *workspace, size_t workspace_bytes, void *stream) {
+    if (!d) return fail(WVC_ERR_ARG, "conv descriptor is NULL");
+    if (d->dtype != WVC_E4M3)
+        return fail(WVC_ERR_ARG, "wvc_causal_conv3d_e4m3_fwd needs d->dtype == WVC_E4M3");
+    return conv_fwd(d, x, cache_in, cache_out, weight, bias, residual, y, workspace,
+                    workspace_bytes, static_cast<hipStream_t>(stream), nullptr, x_scale, w_scale);
 }
 
 size_t wvc_causal_conv3d_workspace_bytes(const wvc_conv3d_desc *d) {
@@ -393,7 +438,8 @@ int wvc_conv3d_pack_weights(const wvc_conv3d_desc *d, const void *weight, void *
     if (!weight || !packed) return fail(WVC_ERR_ARG, "weight or packed is NULL");
     if (!aligned(weight, 2) || !aligned(packed, 16))
         return fail(WVC_ERR_ARG, "packed weights need a 16-byte aligned buffer");
-    const size_t std_bytes = (size_t)d->c_out * d->c_in * d->kt * d->kh * d->kw * 2;
+    const size_t std_bytes =
+        (size_t)d->c_out * d->c_in * d->kt * d->kh * d->kw * (d->dtype == WVC_E4M3 ? 1 : 2);
     const Buf bufs[] = {{weight, std_bytes, false, "weight"},
                         {packed, route_packed_bytes(pl), true, "packed"}};
     rc = check_aliasing(bufs, 2);
@@ -402,6 +448,60 @@ int wvc_conv3d_pack_weights(const wvc_conv3d_desc *d, const void *weight, void *
     return hip_status(strided_route(pl.route) ? wvc::launch_strided_pack(pl.call, weight, packed, s)
                                               : wvc::launch_pack_weights(pl.call, weight, packed, s),
                       "weight packing launch");
+}
+
+int wvc_quantize_e4m3(const void *x, int dtype, int64_t count, float scale, void *q, void *stream) {
+    if (dtype != WVC_BF16 && dtype != WVC_F32)
+        return fail(WVC_ERR_UNSUPPORTED, "the quantiser reads WVC_BF16 or WVC_F32, not dtype %d", dtype);
+    if (count < 0) return fail(WVC_ERR_ARG, "count < 0");
+    if (!(scale > 0.f) || !(scale < INFINITY)) return fail(WVC_ERR_ARG, "scale must be finite and > 0");
+    if (count > 0 && (!x || !q)) return fail(WVC_ERR_ARG, "x or q is NULL");
+    const Buf bufs[] = {{x, (size_t)count * elem_bytes(dtype), false, "x"}, {q, (size_t)count, true, "q"}};
+    int rc = check_aliasing(bufs, 2);
+    if (rc) return rc;
+    const float qr = 1.f / scale;  // fp32, IEEE
+    return hip_status(wvc::launch_quantize_e4m3(x, dtype == WVC_BF16, (long)count, qr, q,
+                                                static_cast<hipStream_t>(stream)),
+                      "quantiser launch");
+}
+
+int wvc_quantize_rows_e4m3(const void *x, int dtype, int64_t rows, int64_t cols, void *q,
+                           float *scale, void *stream) {
+    if (dtype != WVC_BF16 && dtype != WVC_F32)
+        return fail(WVC_ERR_UNSUPPORTED, "the quantiser reads WVC_BF16 or WVC_F32, not dtype %d", dtype);
+    if (rows < 0 || cols < 1 || rows > 0x7fffffff) return fail(WVC_ERR_ARG, "bad rows/cols");
+    size_t count;
+    if (!mul_ok((size_t)rows, (size_t)cols, &count)) return fail(WVC_ERR_ARG, "tensor size overflows");
+    if (rows > 0 && (!x || !q || !scale)) return fail(WVC_ERR_ARG, "x, q or scale is NULL");
+    const Buf bufs[] = {{x, count * elem_bytes(dtype), false, "x"},
+                        {q, count, true, "q"},
+                        {scale, (size_t)rows * 4, true, "scale"}};
+    int rc = check_aliasing(bufs, 3);
+    if (rc) return rc;
+    return hip_status(wvc::launch_quantize_rows_e4m3(x, dtype == WVC_BF16, (long)rows, (long)cols, q,
+                                                     scale, static_cast<hipStream_t>(stream)),
+                      "row quantiser launch");
+}
+
+int wvc_rmsnorm_silu_e4m3(const void *x, const void *gamma, const void *beta, void *q, int n, int c,
+                          int t, int h, int w, float eps, int apply_silu, float scale, void *stream) {
+    if (n < 1 || c < 1 || t < 0 || h < 1 || w < 1)
+        return fail(WVC_ERR_ARG, "bad shape n=%d c=%d t=%d h=%d w=%d", n, c, t, h, w);
+    if (!(eps > 0.f)) return fail(WVC_ERR_ARG, "eps must be > 0");
+    if (!(scale > 0.f) || !(scale < INFINITY)) return fail(WVC_ERR_ARG, "scale must be finite and > 0");
+    if (!gamma) return fail(WVC_ERR_ARG, "gamma is NULL");
+    const long positions = (long)n * t * h * w;
+    if (positions > 0 && (!x || !q)) return fail(WVC_ERR_ARG, "x or q is NULL");
+    const size_t elems = (size_t)positions * c;
+    const Buf bufs[] = {{x, elems * 2, false, "x"},
+                        {q, elems, true, "q"},
+                        {gamma, (size_t)c * 2, false, "gamma"},
+                        {beta, (size_t)c * 2, false, "beta"}};
+    int rc = check_aliasing(bufs, 4);
+    if (rc) return rc;
+    return hip_status(wvc::launch_rmsnorm_silu_e4m3(x, gamma, beta, q, positions, c, eps, apply_silu,
+                                                    1.f / scale, static_cast<hipStream_t>(stream)),
+                      "rmsnorm e4m3 launch");
 }
 
 int wvc_conv3d_cache_frames(const wvc_conv3d_desc *d) {

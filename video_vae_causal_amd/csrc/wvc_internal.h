@@ -35,6 +35,26 @@ __device__ __forceinline__ uint32_t pack2_bf16(float lo, float hi) {
 }
 
 // ---------------------------------------------------------------------------
+// OCP E4M3 (8-bit float: bias 7, no infinities, largest finite 448) codes.
+// v_cvt_pk_fp8_f32 rounds to nearest even; the inputs are clamped to +-448
+// first so that out-of-range values saturate.  Codes for NaN inputs are
+// unspecified.
+// ---------------------------------------------------------------------------
+constexpr float E4M3_MAX = 448.f;
+__device__ __forceinline__ float e4m3_clamp(float v) {
+    return __builtin_amdgcn_fmed3f(v, -E4M3_MAX, E4M3_MAX);
+}
+// 4 floats -> 4 codes in one word (v[0] in the low byte).
+__device__ __forceinline__ uint32_t pack4_e4m3(float a, float b, float c, float d) {
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(e4m3_clamp(a), e4m3_clamp(b), 0, false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(e4m3_clamp(c), e4m3_clamp(d), w, true);
+    return (uint32_t)w;
+}
+__device__ __forceinline__ uint8_t to_e4m3(float a) {
+    return (uint8_t)(__builtin_amdgcn_cvt_pk_fp8_f32(e4m3_clamp(a), 0.f, 0, false) & 0xff);
+}
+
+// ---------------------------------------------------------------------------
 // Conv launch description (already validated by the API layer).
 // Tensor layouts are channels-last, see include/wvc.h.
 // ---------------------------------------------------------------------------
@@ -48,9 +68,13 @@ struct ConvCall {
     int n, cin, cout, t, h, w, ho, wo;
     int kt, kh, kw, sh, sw, ph, pw, dt, dh, dw;
     int frames;            // F = dt*(kt-1)
-    int dtype;             // WVC_F32 / WVC_BF16
+    int dtype;             // WVC_F32 / WVC_BF16 / WVC_E4M3
     int st, t0, to;        // temporal stride, first anchor frame, output frames
     int eh, ew;            // extra zero rows below / columns right of the frame
+    // WVC_E4M3 calls: x, cache and weight hold E4M3 codes; bias, residual and
+    // y are bf16; the sum is multiplied by xscale * wscale[co].
+    float xscale;
+    const float *wscale;   // [Cout], 16-byte aligned
 };
 
 enum class ConvRoute { Fast3x3x3, Fast1x1x1, FastTemporal, FastSpatial2, Generic };
@@ -67,7 +91,7 @@ hipError_t launch_strided_pack(const ConvCall &c, const void *w, void *packed, h
 hipError_t launch_conv_strided(const ConvCall &c, ConvRoute r, bool packed_given, void *ws,
                                size_t ws_bytes, hipStream_t s);
 
-// MFMA implicit-GEMM route (bf16 only).  Weights are read in the packed
+// MFMA implicit-GEMM route (bf16; the 3x3x3 conv also in E4M3).  Weights are read in the packed
 // fragment order written by launch_pack_weights; a call that brings
 // standard-layout weights packs them into its workspace first.  The workspace
 // holds split-K partial sums and packed weights; its contents on entry do not
@@ -113,6 +137,19 @@ hipError_t launch_rmsnorm_silu_from_partials(const ConvPartials &pp, const void 
                                              const void *gamma, const void *beta, void *y,
                                              long positions, int c, float eps, int apply_silu,
                                              hipStream_t s);
+
+// RMS norm + SiLU of a bf16 tensor, stored as E4M3 codes of fl32(u * qr)
+// (qr: the reciprocal of the activation scale).
+hipError_t launch_rmsnorm_silu_e4m3(const void *x, const void *gamma, const void *beta, void *q,
+                                    long positions, int c, float eps, int apply_silu, float qr,
+                                    hipStream_t s);
+// E4M3 quantisers (quant.hip).  Per tensor: q = E4M3(fl32(x * qr)).  Per row
+// of a [rows, cols] matrix: scale_r = fl32(amax_r / 448) (1 for an all-zero
+// row), q = E4M3(fl32(x * fl32(1 / scale_r))).  x is bf16 or fp32.
+hipError_t launch_quantize_e4m3(const void *x, bool bf16, long count, float qr, void *q,
+                                hipStream_t s);
+hipError_t launch_quantize_rows_e4m3(const void *x, bool bf16, long rows, long cols, void *q,
+                                     float *scale, hipStream_t s);
 
 hipError_t launch_upsample2x(const void *x, void *y, long planes, int h, int w, int c,
                              int elem_bytes, hipStream_t s);

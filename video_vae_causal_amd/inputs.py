@@ -203,6 +203,39 @@ def downsample_inputs(seed: int = 6, shape=(1, 96, 17, 480, 832), dtype: str = "
     return d
 
 
+def e4m3_codes(shape, seed: int, name: str, exp_lo: int = 1, exp_hi: int = 14) -> np.ndarray:
+    """Random 8-bit E4M3 codes (uint8): uniform sign and 3-bit mantissa, the
+    4-bit exponent field uniform in [exp_lo, exp_hi] (exp_hi <= 14 never
+    draws the NaN codes).  No arithmetic: the bits are drawn directly."""
+    g = _gen(seed, name)
+    sign = g.integers(0, 2, size=tuple(shape), dtype=np.uint8) << np.uint8(7)
+    expo = g.integers(exp_lo, exp_hi + 1, size=tuple(shape), dtype=np.uint8) << np.uint8(3)
+    mant = g.integers(0, 8, size=tuple(shape), dtype=np.uint8)
+    return (sign | expo | mant).astype(np.uint8)
+
+
+def e4m3_conv_inputs(seed: int = 7, shape=(1, 384, 17, 240, 416), cout: int = 384,
+                     with_cache: bool = True, with_residual: bool = False) -> Dict:
+    """Operands of an 8-bit causal 3x3x3 conv: activation and cache codes, weight
+    codes [C_out, C_in, 3, 3, 3], a per-tensor activation scale, per-output-
+    channel weight scales (float32, uniform in [0.5, 1.5] * 2^-4 / sqrt(27 C_in)
+    so that the outputs stay O(1)), bias N(0, 0.1) and residual N(0, 1) in bf16."""
+    n, c, t, h, w = shape
+    g = _gen(seed, "scales")
+    d = {
+        "x": e4m3_codes(shape, seed, "x", 1, 12),
+        "w": e4m3_codes((cout, c, 3, 3, 3), seed, "w", 1, 14),
+        "x_scale": float(np.float32(2.0 ** -6)),
+        "w_scale": (g.uniform(0.5, 1.5, cout) * 2.0 ** -4 / np.sqrt(27 * c)).astype(np.float32),
+        "b": quantize(normal((cout,), seed, "b", std=0.1), "bf16"),
+    }
+    if with_cache:
+        d["cache"] = e4m3_codes((n, c, 2, h, w), seed, "cache", 1, 12)
+    if with_residual:
+        d["res"] = quantize(normal((n, cout, t, h, w), seed, "res"), "bf16")
+    return d
+
+
 def sample_indices(shape: Tuple[int, ...], count: int, seed: int,
                    include_frames: Optional[List[int]] = None) -> np.ndarray:
     """Flat NCTHW indices for point-sampled checks: ``count`` uniformly random
