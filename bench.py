@@ -11,6 +11,9 @@ A step is one pass of the whole hot path over one batch of synthetic input:
       updates.
   layer_384_240x416: causal conv 3x3x3 384->384 over x[1,384,17,240,416]
       (whole sequence), then the 1x1x1 384->192 projection.
+  layer_384_240x416_e4m3: the same layer with the 3x3x3 conv on 8-bit E4M3
+      codes (activations with one scale, weights with one scale per output
+      channel; fp32 accumulation, bf16 output), the projection in bf16.
   layer_96_480x832: RMSNorm+SiLU then causal conv 3x3x3 96->96 over
       x[1,96,17,480,832] in chunks 1+4+4+4+4 with the cache.
   decoder_stack_48_30x52: latent[1,48,21,30,52] -> conv_in -> 2 resblocks ->
@@ -38,6 +41,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+MFMA_FP8_PEAK_TFLOPS = 5000.0    # MI355X dense fp8 MFMA
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
 METRIC = "causal Conv3D bf16 TFLOP/s (% MFMA peak) + ms per decoded latent frame"
 
@@ -49,6 +53,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="resblock_384_60x104",
                     choices=sorted(["resblock_384_60x104", "layer_384_240x416", "layer_96_480x832",
+                                    "layer_384_240x416_e4m3",
                                     "decoder_stack_48_30x52", "downsample_96_480x832",
                                     "decoder_tiled_192x336"]))
     ap.add_argument("--tiling", choices=sorted(TILINGS), default="page",
@@ -212,6 +217,61 @@ def wl_layer384():
                         "batch": n},
                 kernel=kernel, kernel_name="igemm_kernel<3, 128, 32, 2, false, 32>", kernel_units=f3,
                 kernel_bound="mfma", kernel_bytes=acc.conv_launch_bytes(n, t, h, w, c, c, cache_frames=0))
+    return step, info
+
+
+def wl_layer384_e4m3():
+    import torch
+    from video_vae_causal_amd import _lib as L, accounting as acc, inputs
+    shape = (1, 384, 17, 240, 416)
+    n, c, t, h, w = shape
+    d = inputs.e4m3_conv_inputs(seed=7, shape=shape, cout=c, with_cache=False)
+    x = cl(torch.from_numpy(d["x"]).to("cuda"))
+    wq = cl(torch.from_numpy(d["w"]).to("cuda"))
+    ws = torch.from_numpy(d["w_scale"]).to("cuda")
+    b = to_dev(d["b"])
+    wp = to_dev(inputs.conv_weight(192, c, (1, 1, 1), 7, "wp", "bf16"))
+    bp = to_dev(inputs.conv_bias(192, 7, "bp", "bf16"))
+    y = L.empty_cl((n, c, t, h, w))
+    proj = L.empty_cl((n, 192, t, h, w))
+    d8 = L.conv_desc(shape, tuple(wq.shape), L.WVC_E4M3, weight_layout=L.WVC_WEIGHT_PACKED)
+    need = L.wvc_causal_conv3d_workspace_bytes(d8)
+    ws3 = torch.empty(need, dtype=torch.uint8, device="cuda") if need else None
+    ws1 = conv_workspace(y, wp, padding=(0, 0), packed=True)
+    wqp = L.wvc_conv3d_pack_weights(wq)
+    wpp = L.wvc_conv3d_pack_weights(wp, padding=(0, 0))
+    # the norm that writes these codes in a block, timed on a bf16 activation
+    # of the same shape
+    xn = to_dev(inputs.quantize(inputs.normal(shape, 7, "xn"), "bf16"))
+    gn = to_dev(inputs.norm_gamma(c, 7, "gn", "bf16"))
+    qn = L.empty_cl(shape, torch.uint8)
+    del d
+
+    def conv():
+        L.wvc_causal_conv3d_e4m3_fwd(x, 2.0 ** -6, wq, ws, b, y=y, workspace=ws3, packed_weight=wqp)
+
+    def step():
+        conv()
+        L.wvc_causal_conv3d_fwd(y, wp, bp, y=proj, padding=(0, 0), workspace=ws1, packed_weight=wpp)
+
+    def norm_kernel():
+        L.wvc_rmsnorm_silu_e4m3(xn, gn, 4.0 / 448, q=qn)
+
+    f3 = acc.conv_flops(n, t, h, w, c, c)
+    f1 = acc.conv_flops(n, t, h, w, c, 192, (1, 1, 1))
+    elems = n * c * t * h * w
+    # compulsory bytes: input codes and weight codes (1 byte), bias and the
+    # per-channel scales, the bf16 output
+    k_bytes = elems * 1 + c * c * 27 * 1 + c * 2 + c * 4 + elems * 2
+    info = dict(workload="layer_384_240x416_e4m3", conv_flops=f3 + f1, latent_frames=t,
+                config={"workload": "layer_384_240x416_e4m3", "channels": c, "frames": t,
+                        "height": h, "width": w, "chunk_frames": t, "projection_out": 192,
+                        "batch": n, "conv_operands": "e4m3", "projection": "bf16"},
+                kernel=conv, kernel_name="igemm_kernel<3, 128, 32, 2, false, 32, true>",
+                kernel_units=f3, kernel_bound="mfma", kernel_peak=MFMA_FP8_PEAK_TFLOPS,
+                kernel_bytes=k_bytes, dtype="e4m3 x e4m3 -> f32 (conv), bf16 (projection)",
+                norm_kernel=norm_kernel, norm_kernel_name="rmsnorm_flat_kernel<true, 2, true, false, true>",
+                norm_bytes=elems * 3)
     return step, info
 
 
@@ -427,6 +487,7 @@ def wl_tiled():
 
 
 WORKLOADS = {"resblock_384_60x104": wl_resblock, "layer_384_240x416": wl_layer384,
+             "layer_384_240x416_e4m3": wl_layer384_e4m3,
              "layer_96_480x832": wl_layer96, "decoder_stack_48_30x52": wl_decoder,
              "downsample_96_480x832": wl_downsample, "decoder_tiled_192x336": wl_tiled}
 
@@ -435,71 +496,81 @@ WORKLOADS = {"resblock_384_60x104": wl_resblock, "layer_384_240x416": wl_layer38
 # CPU baseline: the fp64 oracle on a bounded sample of the same workload.
 # ---------------------------------------------------------------------------
 
+def cpu_time_loop(run, min_s: float = 10.0):
+    """Run the sample once, then again until ``min_s`` seconds of CPU work
+    have passed; returns (seconds, runs)."""
+    t0 = time.perf_counter()
+    runs = 0
+    while True:
+        run()
+        runs += 1
+        dt = time.perf_counter() - t0
+        if dt >= min_s:
+            return dt, runs
+
+
 def cpu_baseline(workload: str):
     import oracle
     from video_vae_causal_amd import accounting as acc, inputs
     threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
-    if workload == "decoder_stack_48_30x52":
-        d = inputs.decoder_inputs(seed=5)
-        lat = d["latent"][:, :, :1].astype(np.float64)
-        p = {k: ({kk: vv.astype(np.float64) for kk, vv in v.items()} if isinstance(v, dict)
-                 else v.astype(np.float64)) for k, v in d["p"].items()}
+
+    def f64_params(p):
+        return {k: ({kk: vv.astype(np.float64) for kk, vv in v.items()} if isinstance(v, dict)
+                    else v.astype(np.float64)) for k, v in p.items()}
+
+    if workload in ("decoder_stack_48_30x52", "decoder_tiled_192x336"):
+        if workload == "decoder_stack_48_30x52":
+            d = inputs.decoder_inputs(seed=5)
+            sample = "latent frames 0-1 of 21 through the whole stack (bf16-boundary oracle)"
+        else:
+            d = inputs.decoder_inputs(seed=8, shape=(1, 48, 3, 192, 336), with_latent_window=(30, 52))
+            sample = "latent frames 0-1, the 30x52 top-left window, through the whole stack"
+        lat = d["latent"][:, :, :2].astype(np.float64)
+        p = f64_params(d["p"])
         n, cl_, t, h, w = lat.shape
         width = p["w_in"].shape[0]
-        flops = (acc.conv_flops(n, 1, h, w, cl_, width) + 4 * acc.conv_flops(n, 1, h, w, width, width)
-                 + 5 * acc.conv_flops(n, 1, 2 * h, 2 * w, width, width))
-        t0 = time.perf_counter()
-        oracle.decoder_stack(lat, p, bf16=True)
-        dt = time.perf_counter() - t0
-        sample = "latent frame 0 of 21 through the whole stack (bf16-boundary oracle)"
+        flops = (acc.conv_flops(n, t, h, w, cl_, width) + 4 * acc.conv_flops(n, t, h, w, width, width)
+                 + 5 * acc.conv_flops(n, t, 2 * h, 2 * w, width, width))
+        run = lambda: oracle.decoder_stack(lat, p, bf16=True)
     elif workload == "resblock_384_60x104":
         r = inputs.resblock_inputs(seed=2)
-        x = r["x"][:, :, 2:3].astype(np.float64)
-        p = {k: v.astype(np.float64) for k, v in r["p"].items()}
-        n, c, _, h, w = x.shape
-        past = r["x"][:, :, 0:2].astype(np.float64)   # non-zero caches: every tap is computed
-        flops = 2 * acc.conv_flops(n, 1, h, w, c, c)
-        t0 = time.perf_counter()
-        oracle.resblock(x, p, past, past, bf16=True)
-        dt = time.perf_counter() - t0
-        sample = "1 of 5 latent frames (frame 2, non-zero caches) through the block"
-    elif workload == "decoder_tiled_192x336":
-        d = inputs.decoder_inputs(seed=8, shape=(1, 48, 3, 192, 336), with_latent_window=(30, 52))
-        lat = d["latent"][:, :, :1].astype(np.float64)
-        p = {k: ({kk: vv.astype(np.float64) for kk, vv in v.items()} if isinstance(v, dict)
-                 else v.astype(np.float64)) for k, v in d["p"].items()}
-        n, cl_, t, h, w = lat.shape
-        width = p["w_in"].shape[0]
-        flops = (acc.conv_flops(n, 1, h, w, cl_, width) + 4 * acc.conv_flops(n, 1, h, w, width, width)
-                 + 5 * acc.conv_flops(n, 1, 2 * h, 2 * w, width, width))
-        t0 = time.perf_counter()
-        oracle.decoder_stack(lat, p, bf16=True)
-        dt = time.perf_counter() - t0
-        sample = "latent frame 0, the 30x52 top-left window, through the whole stack"
+        x = r["x"].astype(np.float64)
+        p = f64_params(r["p"])
+        n, c, t, h, w = x.shape
+        flops = 2 * acc.conv_flops(n, t, h, w, c, c)
+        run = lambda: oracle.resblock(x, p, bf16=True)
+        sample = "the whole 5-frame step through the block (bf16-boundary oracle)"
     elif workload == "downsample_96_480x832":
         d = inputs.downsample_inputs()
         xs = d["x"][:, :, :4].astype(np.float64)   # frames 0..3 (one 4-frame chunk)
         n, c, f, h, w = xs.shape
         flops = 2 * 9 * c * c * f * (h // 2) * (w // 2)
-        t0 = time.perf_counter()
-        oracle.causal_conv3d_strided(xs, d["w_s"].astype(np.float64), d["b_s"].astype(np.float64),
-                                     stride=(1, 2, 2), pad=(0, 0), pad_extra=(1, 1))
-        dt = time.perf_counter() - t0
+        ws_, bs_ = d["w_s"].astype(np.float64), d["b_s"].astype(np.float64)
+        run = lambda: oracle.causal_conv3d_strided(xs, ws_, bs_, stride=(1, 2, 2), pad=(0, 0),
+                                                   pad_extra=(1, 1))
         sample = "frames 0-3 (one 4-frame chunk) of the stride-2 spatial conv"
+    elif workload == "layer_384_240x416_e4m3":
+        rows = 120
+        d = inputs.e4m3_conv_inputs(seed=7, shape=(1, 384, 3, rows, 416), cout=384, with_cache=False)
+        n, c, f, h, w = d["x"].shape
+        flops = acc.conv_flops(n, f, h, w, c, c)
+        b64 = d["b"].astype(np.float64)
+        run = lambda: oracle.causal_conv3d_e4m3(d["x"], d["x_scale"], d["w"], d["w_scale"], b64)
+        sample = f"3 frames x {rows} rows x 416 of the 8-bit 3x3x3 conv (decode + fp64 conv)"
     else:
         d = inputs.layer384_inputs() if workload == "layer_384_240x416" else inputs.layer96_inputs()
-        x = d["x"][:, :, :3]
-        n, c, _, h, w = x.shape
-        rows = 24 if c == 384 else 48
-        xs = x[:, :, :, :rows].astype(np.float64)    # frames 0..2, first rows of the frame
+        c = d["x"].shape[1]
+        frames, rows = (3, 120) if c == 384 else (4, 480)
+        xs = d["x"][:, :, :frames, :rows].astype(np.float64)
+        n, c, _, h, w = xs.shape
         past = np.zeros((n, c, 2, rows, w))
-        flops = acc.conv_flops(n, 3, rows, w, c, c)
-        t0 = time.perf_counter()
-        oracle.causal_conv3d(xs, d["w"].astype(np.float64), d["b"].astype(np.float64), cache=past)
-        dt = time.perf_counter() - t0
-        sample = f"frames 0-2, rows 0-{rows - 1} of the 3x3x3 conv"
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": sample, "seconds": round(dt, 3), "flops": flops}
+        flops = acc.conv_flops(n, frames, rows, w, c, c)
+        w64, b64 = d["w"].astype(np.float64), d["b"].astype(np.float64)
+        run = lambda: oracle.causal_conv3d(xs, w64, b64, cache=past)
+        sample = f"frames 0-{frames - 1}, rows 0-{rows - 1} of the 3x3x3 conv"
+    dt, runs = cpu_time_loop(run)
+    return {"value": flops * runs / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": sample + f", run {runs}x", "seconds": round(dt, 3), "flops": flops * runs}
 
 
 def measured_traffic(path: str, key: str, kernel_name: str):
@@ -589,25 +660,26 @@ def main():
         flops = info["kernel_flops"]
     else:
         achieved = info["kernel_units"] / (k_ms * 1e-3) / 1e12
-        peak, unit = MFMA_BF16_PEAK_TFLOPS, "TFLOP/s"
+        peak, unit = info.get("kernel_peak", MFMA_BF16_PEAK_TFLOPS), "TFLOP/s"
         flops = info["kernel_units"]
     roofline = {"bound": info["kernel_bound"], "achieved": round(achieved, 2),
                 "peak": peak, "unit": unit,
                 "frac": round(achieved / peak, 4), "traffic": traffic,
                 "kernel": info["kernel_name"], "kernel_ms": round(k_ms, 5),
                 "flops_per_launch": flops,
-                "mfma_frac": round(flops / (k_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+                "mfma_frac": round(flops / (k_ms * 1e-3) / 1e12 / info.get("kernel_peak", MFMA_BF16_PEAK_TFLOPS), 4),
                 "algorithmic_bytes_per_launch": info["kernel_bytes"]}
 
     line = {
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "warmup_s": args.warmup_seconds,
         "ms_per_step": round(ms_step, 4),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": info.get("dtype", "bf16"),
         "data": "synthetic (seeded Philox normals, random-init weights)",
         "config": dict(info["config"], hip_graph=args.graph == "on",
                        two_stream_pipeline=PIPELINE and args.workload in PIPELINED),
-        "pct_mfma_peak": round(100 * value / MFMA_BF16_PEAK_TFLOPS, 2),
+        "pct_mfma_peak": round(100 * value / info.get("kernel_peak", MFMA_BF16_PEAK_TFLOPS), 2),
         "ms_per_latent_frame": round(ms_step / info["latent_frames"], 4),
         "conv_flops_per_step": info["conv_flops"],
         "wall_s_timed": round(wall, 3),
