@@ -11,6 +11,9 @@ A step is one pass of the whole hot path over one batch of synthetic input:
       updates.
   layer_384_240x416: causal conv 3x3x3 384->384 over x[1,384,17,240,416]
       (whole sequence), then the 1x1x1 384->192 projection.
+  resblock_384_60x104_e4m3: the default workload on the 8-bit path: the
+      norms store E4M3 codes, both convs run on codes (weights with one scale
+      per output channel), outputs and residual bf16.
   layer_384_240x416_e4m3: the same layer with the 3x3x3 conv on 8-bit E4M3
       codes (activations with one scale, weights with one scale per output
       channel; fp32 accumulation, bf16 output), the projection in bf16.
@@ -53,7 +56,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="resblock_384_60x104",
                     choices=sorted(["resblock_384_60x104", "layer_384_240x416", "layer_96_480x832",
-                                    "layer_384_240x416_e4m3",
+                                    "layer_384_240x416_e4m3", "resblock_384_60x104_e4m3",
                                     "decoder_stack_48_30x52", "downsample_96_480x832",
                                     "decoder_tiled_192x336"]))
     ap.add_argument("--tiling", choices=sorted(TILINGS), default="page",
@@ -186,6 +189,54 @@ def wl_resblock():
     return step, info
 
 
+def wl_resblock_e4m3():
+    import torch
+    from video_vae_causal_amd import _lib as L, accounting as acc, inputs, stream
+    r = inputs.resblock_inputs(seed=2)
+    n, c, t, h, w = r["x"].shape
+    x = to_dev(r["x"])
+    p = {k: to_dev(v) for k, v in r["p"].items()}
+    frames = [cl(x[:, :, i:i + 1]) for i in range(t)]
+    out = L.empty_cl(x.shape)
+    outs = [out[:, :, i:i + 1] for i in range(t)]
+    # activation scales: a fixed calibration for these synthetic activations
+    # (SiLU of unit-RMS values stays below 5)
+    rb = stream.ResBlockE4M3(p, 5.0 / 448, 5.0 / 448)
+    rb.start(n, h, w)
+
+    def step():
+        rb.reset()
+        for i in range(t):
+            rb(frames[i], y=outs[i])
+
+    conv_flops = 2 * t * acc.conv_flops(n, 1, h, w, c, c)
+    qx = L.empty_cl((n, c, 1, h, w), torch.uint8)
+    L.wvc_quantize_e4m3(frames[0], 5.0 / 448, q=qx)
+    cache = L.empty_cl((n, c, 2, h, w), torch.uint8)
+    L.wvc_cache_reset(cache)
+    ky = L.empty_cl((n, c, 1, h, w))
+    wq, wsc, wqp = rb.w["w1"]
+    d8 = L.conv_desc(tuple(qx.shape), tuple(wq.shape), L.WVC_E4M3, weight_layout=L.WVC_WEIGHT_PACKED)
+    need = L.wvc_causal_conv3d_workspace_bytes(d8)
+    kws = torch.empty(need, dtype=torch.uint8, device="cuda") if need else None
+
+    def kernel():
+        L.wvc_causal_conv3d_e4m3_fwd(qx, 5.0 / 448, wq, wsc, p["b1"], cache, None, None, ky,
+                                     workspace=kws, packed_weight=wqp)
+
+    info = dict(workload="resblock_384_60x104_e4m3", conv_flops=conv_flops, latent_frames=t,
+                config={"workload": "resblock_384_60x104_e4m3", "channels": c, "frames": t,
+                        "height": h, "width": w, "chunk_frames": 1, "cache_frames": 2,
+                        "batch": n, "conv_operands": "e4m3", "activation_scales": [5.0 / 448] * 2},
+                kernel=kernel,
+                kernel_name="igemm_kernel<3, 128, 32, 2, true, 16, true> + splitk_reduce_kernel",
+                kernel_units=acc.conv_flops(n, 1, h, w, c, c), kernel_bound="mfma",
+                kernel_peak=MFMA_FP8_PEAK_TFLOPS,
+                kernel_bytes=n * h * w * c * 3 + c * c * 27 + c * 6 + n * h * w * c * 2,
+                dtype="e4m3 x e4m3 -> f32 (convs); norms, residual and outputs bf16")
+    return step, info
+
+
 def wl_layer384():
     import torch
     from video_vae_causal_amd import _lib as L, accounting as acc, inputs
@@ -270,7 +321,7 @@ def wl_layer384_e4m3():
                 kernel=conv, kernel_name="igemm_kernel<3, 128, 32, 2, false, 32, true>",
                 kernel_units=f3, kernel_bound="mfma", kernel_peak=MFMA_FP8_PEAK_TFLOPS,
                 kernel_bytes=k_bytes, dtype="e4m3 x e4m3 -> f32 (conv), bf16 (projection)",
-                norm_kernel=norm_kernel, norm_kernel_name="rmsnorm_flat_kernel<true, 2, true, false, true>",
+                norm_kernel=norm_kernel, norm_kernel_name="rmsnorm_flat_kernel<true, 4, true, false, true>",
                 norm_bytes=elems * 3)
     return step, info
 
@@ -487,7 +538,7 @@ def wl_tiled():
 
 
 WORKLOADS = {"resblock_384_60x104": wl_resblock, "layer_384_240x416": wl_layer384,
-             "layer_384_240x416_e4m3": wl_layer384_e4m3,
+             "layer_384_240x416_e4m3": wl_layer384_e4m3, "resblock_384_60x104_e4m3": wl_resblock_e4m3,
              "layer_96_480x832": wl_layer96, "decoder_stack_48_30x52": wl_decoder,
              "downsample_96_480x832": wl_downsample, "decoder_tiled_192x336": wl_tiled}
 
@@ -549,6 +600,14 @@ def cpu_baseline(workload: str):
         run = lambda: oracle.causal_conv3d_strided(xs, ws_, bs_, stride=(1, 2, 2), pad=(0, 0),
                                                    pad_extra=(1, 1))
         sample = "frames 0-3 (one 4-frame chunk) of the stride-2 spatial conv"
+    elif workload == "resblock_384_60x104_e4m3":
+        r = inputs.resblock_inputs(seed=2)
+        x = r["x"].astype(np.float64)
+        p = f64_params(r["p"])
+        n, c, t, h, w = x.shape
+        flops = 2 * acc.conv_flops(n, t, h, w, c, c)
+        run = lambda: oracle.resblock_e4m3(x, p, 5.0 / 448, 5.0 / 448)
+        sample = "the whole 5-frame step through the 8-bit block"
     elif workload == "layer_384_240x416_e4m3":
         rows = 120
         d = inputs.e4m3_conv_inputs(seed=7, shape=(1, 384, 3, rows, 416), cout=384, with_cache=False)

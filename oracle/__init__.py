@@ -512,6 +512,21 @@ def norm_silu_e4m3(x, gamma, beta=None, scale: float = 1.0, eps=DEFAULT_EPS):
     return v, e4m3_encode(v)
 
 
+def resblock_e4m3(x, p: dict, s1: float, s2: float, eps=DEFAULT_EPS):
+    """The residual block of section 10.4 on the 8-bit path, over a whole
+    sequence from a fresh cache (identity shortcut): norm1 + SiLU quantised at
+    activation scale s1, the E4M3 conv1 with per-output-channel weight scales,
+    rounded to bf16 where it is stored; norm2 + SiLU quantised at s2, the E4M3
+    conv2, plus the block input, rounded to bf16."""
+    x = _f64(x)
+    w1q, w1s = quantize_conv_weights_e4m3(p["w1"])
+    w2q, w2s = quantize_conv_weights_e4m3(p["w2"])
+    _, q1 = norm_silu_e4m3(x, p["gamma1"], p.get("beta1"), s1, eps)
+    h = round_bf16(causal_conv3d_e4m3(q1, s1, w1q, w1s, p.get("b1")))
+    _, q2 = norm_silu_e4m3(h, p["gamma2"], p.get("beta2"), s2, eps)
+    return round_bf16(causal_conv3d_e4m3(q2, s2, w2q, w2s, p.get("b2"), None, x))
+
+
 def rel_l2(y, ref) -> float:
     """||y - ref||_2 / ||ref||_2 in fp64."""
     y = np.asarray(y, dtype=np.float64)

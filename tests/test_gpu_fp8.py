@@ -251,3 +251,26 @@ def test_conv_e4m3_full_size_sampled():
     ref = oracle.causal_conv3d_e4m3_points(d["x"], d["x_scale"], d["w"], d["w_scale"], idx,
                                            f64(d["b"]))
     check_e4m3_conv(got, ref, "e4m3 conv 384 full size (sampled)")
+
+
+@pytest.mark.parametrize("c,t,h,w", [(128, 3, 20, 36), (384, 5, 60, 104)])
+def test_resblock_e4m3_streamed_vs_oracle(c, t, h, w):
+    # the 8-bit residual block fed one frame at a time through its code caches,
+    # against the oracle's whole-sequence 8-bit block (with its own codes)
+    from video_vae_causal_amd import stream
+    print(f"[case] 8-bit resblock c={c} t={t} {h}x{w}, streamed per frame", flush=True)
+    p = I.resblock_params(c, 21, "blk", "bf16")
+    x = I.quantize(I.normal((1, c, t, h, w), 21, "x"), "bf16")
+    s1, s2 = 5.0 / 448, 5.0 / 448
+    pd = {k: to_dev(v) for k, v in p.items()}
+    blk = stream.ResBlockE4M3(pd, s1, s2)
+    xd = to_dev(x)
+    outs = []
+    for f in range(t):
+        xf = xd[:, :, f:f + 1].contiguous(memory_format=torch.channels_last_3d)
+        outs.append(to_host(blk(xf)))
+    y = np.concatenate(outs, axis=2)
+    ref = oracle.resblock_e4m3(f64(x), {k: f64(v) for k, v in p.items()}, s1, s2)
+    check_bf16(y, ref, f"8-bit resblock {c}ch")
+    rel = oracle.rel_l2(y, ref)
+    assert rel <= 5e-3, rel

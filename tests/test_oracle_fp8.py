@@ -159,3 +159,41 @@ def test_norm_silu_e4m3_is_scaled_norm_silu():
     ref = F.silu(torch.from_numpy(F.normalize(torch.from_numpy(x), dim=1).numpy() * 4.0 * g[None, :, None, None, None])).numpy()
     assert np.allclose(v * 0.03125, ref, rtol=1e-12, atol=1e-14)
     assert np.array_equal(codes, oracle.e4m3_encode(v))
+
+
+def test_resblock_e4m3_equals_torch_recomposition():
+    # the 8-bit block rebuilt from torch ops: F.normalize-based norm, torch's
+    # float8_e4m3fn cast (after explicit saturation), torch conv3d, bf16 casts
+    rng = np.random.default_rng(9)
+    c, shape = 16, (1, 16, 3, 5, 6)
+    x = torch.from_numpy(rng.standard_normal(shape)).to(torch.bfloat16).double()
+    p = {"gamma1": 1 + 0.05 * rng.standard_normal(c), "gamma2": 1 + 0.05 * rng.standard_normal(c),
+         "w1": rng.standard_normal((c, c, 3, 3, 3)) / np.sqrt(27 * c),
+         "w2": rng.standard_normal((c, c, 3, 3, 3)) / np.sqrt(27 * c),
+         "b1": 0.1 * rng.standard_normal(c), "b2": 0.1 * rng.standard_normal(c)}
+    p = {k: torch.from_numpy(v).to(torch.bfloat16).double().numpy() for k, v in p.items()}
+    s1, s2 = 5.0 / 448, 3.0 / 448
+    y = oracle.resblock_e4m3(x.numpy(), p, s1, s2)
+
+    def q(v, s):  # codes of v / s, decoded back to multiples of s
+        t = torch.clamp(v / s, -448.0, 448.0).to(torch.float8_e4m3fn)
+        return t.double() * s
+
+    def wq(w):
+        w = torch.from_numpy(w)
+        sc = (w.abs().amax(dim=(1, 2, 3, 4)).float() / 448.0).double()
+        codes = (w.float() * (1.0 / sc.float())[:, None, None, None, None]).to(torch.float8_e4m3fn)
+        return codes.double() * sc[:, None, None, None, None]
+
+    def norm_silu(v, g):
+        u = F.normalize(v, dim=1, eps=1e-12) * np.sqrt(c) * torch.from_numpy(g)[None, :, None, None, None]
+        return F.silu(u)
+
+    def conv(v, w, b):
+        v = F.pad(v, (1, 1, 1, 1, 2, 0))
+        return F.conv3d(v, w, torch.from_numpy(b))
+
+    h = conv(q(norm_silu(x, p["gamma1"]), s1), wq(p["w1"]), p["b1"]).to(torch.bfloat16).double()
+    ref = (conv(q(norm_silu(h, p["gamma2"]), s2), wq(p["w2"]), p["b2"]) + x).to(torch.bfloat16).double()
+    assert np.allclose(y, ref.numpy(), rtol=1e-2, atol=1e-2)
+    assert oracle.rel_l2(y, ref.numpy()) < 1e-3

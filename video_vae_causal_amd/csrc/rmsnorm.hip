@@ -73,6 +73,7 @@ constexpr int FLAT_MAX_CPP = 256;
 // Non-temporal 16-byte accesses for tensors far larger than the caches: the
 // data is touched once, so it should not push other lines out of L2 / MALL.
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint4 ld_stream(const uint4 *p) {
     const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
     return make_uint4(v.x, v.y, v.z, v.w);
@@ -210,7 +211,7 @@ __global__ void __launch_bounds__(256) rmsnorm_flat_kernel(const uint4 *__restri
                                             pack4_e4m3(o[4] * qr, o[5] * qr, o[6] * qr, o[7] * qr));
                 uint2 *q8 = reinterpret_cast<uint2 *>(y) + pos0 * cpp + f;
                 if (STREAM)
-                    __builtin_nontemporal_store(c8.x, &q8->x), __builtin_nontemporal_store(c8.y, &q8->y);
+                    __builtin_nontemporal_store(u32x2{c8.x, c8.y}, reinterpret_cast<u32x2 *>(q8));
                 else
                     *q8 = c8;
             } else if (STREAM) {
@@ -340,15 +341,18 @@ hipError_t launch_rmsnorm_silu_e4m3(const void *x, const void *gamma, const void
     if (c % 8 == 0 && aligned && c / 8 <= FLAT_MAX_CPP) {
         const int cpp = c / 8;
         const long chunks = positions * cpp;
+        // Large tensors: four chunks per thread (more reads in flight per
+        // thread; with half the write bytes of the bf16 store the read stream
+        // sets the pace), non-temporal accesses.
         const bool big = chunks >= 8L * 1024 * num_cus_norm();
-        const int K = big ? 2 : 1;
+        const int K = big ? 4 : 1;
         const int P = 256 * K / cpp;
         int R = 1;
         while (R < 64 && 2 * R * P <= 256 && 2 * R <= cpp) R *= 2;
         const long blocks = (positions + P - 1) / P;
         if (blocks > 0x7fffffffL) return hipErrorInvalidValue;
         if (big)
-            hipLaunchKernelGGL((rmsnorm_flat_kernel<true, 2, true, false, true>), dim3((unsigned)blocks),
+            hipLaunchKernelGGL((rmsnorm_flat_kernel<true, 4, true, false, true>), dim3((unsigned)blocks),
                                dim3(256), 0, s, static_cast<const uint4 *>(x),
                                static_cast<const uint4 *>(gamma), static_cast<const uint4 *>(beta),
                                static_cast<uint4 *>(q), positions, cpp, P, R, scale, eps, apply_silu,

@@ -232,6 +232,78 @@ class ResBlock:
         return [lambda: self.front(x, h2), lambda: self.back(h2, x, y)]
 
 
+class ResBlockE4M3:
+    """The residual block on the 8-bit path (identity shortcut, C_in == C_out):
+    norm1 + SiLU stored as E4M3 codes at activation scale s1, the 8-bit conv1
+    (bf16 out), norm2 + SiLU as codes at s2, the 8-bit conv2 with the block
+    input added as its residual.  The weights are quantised once, one scale per
+    output channel, and packed; the caches hold codes.  The activation scales
+    are the caller's calibration constants."""
+
+    def __init__(self, params: Dict[str, torch.Tensor], s1: float, s2: float, eps: float = 1e-12):
+        if params["w1"].shape[0] != params["w1"].shape[1] or params.get("w_short") is not None:
+            raise ValueError("ResBlockE4M3 covers the identity-shortcut block (C_in == C_out)")
+        self.p, self.s1, self.s2, self.eps = params, float(s1), float(s2), eps
+        self.w = {}
+        for k in ("w1", "w2"):
+            q, sc = L.wvc_quantize_rows_e4m3(params[k])
+            self.w[k] = (q, sc, L.wvc_conv3d_pack_weights(q))
+        self.c1: Optional[_PingPong] = None
+        self.c2: Optional[_PingPong] = None
+        self.bufs: Dict[str, torch.Tensor] = {}
+        self.ws: Dict[str, torch.Tensor] = {}
+
+    def start(self, n: int, h: int, w: int):
+        c = self.p["w1"].shape[0]
+        shape = (n, c, CACHE_T, h, w)
+        if self.c1 is not None and tuple(self.c1.buf[0].shape) == shape:
+            self.reset()
+            return
+        dev = self.p["w1"].device
+        self.c1 = _PingPong(shape, torch.uint8, dev)
+        self.c2 = _PingPong(shape, torch.uint8, dev)
+
+    def reset(self):
+        if self.c1 is not None:
+            self.c1.reset()
+            self.c2.reset()
+
+    def pingpongs(self) -> List[_PingPong]:
+        return [self.c1, self.c2] if self.c1 is not None else []
+
+    def caches(self) -> List[torch.Tensor]:
+        if self.c1 is None:
+            return []
+        self.c1.materialize()
+        self.c2.materialize()
+        return [self.c1.cin, self.c2.cin]
+
+    def _conv(self, name: str, q: torch.Tensor, scale: float, cache: _PingPong, y: torch.Tensor,
+              residual: Optional[torch.Tensor]):
+        wq, wsc, packed = self.w[name]
+        d = L.conv_desc(tuple(q.shape), tuple(wq.shape), L.WVC_E4M3, weight_layout=L.WVC_WEIGHT_PACKED)
+        need = L.wvc_causal_conv3d_workspace_bytes(d)
+        ws = self.ws.get(name)
+        if need and (ws is None or ws.numel() < need):
+            ws = self.ws[name] = torch.empty(need, dtype=torch.uint8, device=q.device)
+        L.wvc_causal_conv3d_e4m3_fwd(q, scale, wq, wsc, self.p["b" + name[1]], cache.cin, cache.cout,
+                                     residual, y, workspace=ws if need else None, packed_weight=packed)
+        cache.flip()
+
+    def __call__(self, x: torch.Tensor, y: Optional[torch.Tensor] = None) -> torch.Tensor:
+        if self.c1 is None:
+            self.start(x.shape[0], x.shape[3], x.shape[4])
+        q = _cached_buf(self.bufs, "q", x.shape, x.new_empty(0, dtype=torch.uint8))
+        h = _cached_buf(self.bufs, "h", x.shape, x)
+        if y is None:
+            y = L.empty_cl(x.shape, x.dtype, x.device)
+        L.wvc_rmsnorm_silu_e4m3(x, self.p["gamma1"], self.s1, beta=self.p.get("beta1"), q=q, eps=self.eps)
+        self._conv("w1", q, self.s1, self.c1, h, None)
+        L.wvc_rmsnorm_silu_e4m3(h, self.p["gamma2"], self.s2, beta=self.p.get("beta2"), q=q, eps=self.eps)
+        self._conv("w2", q, self.s2, self.c2, y, x)
+        return y
+
+
 class Stream:
     """Runs a sequence of layers over a latent sequence chunk by chunk."""
 
