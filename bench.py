@@ -62,6 +62,9 @@ def parse():
     ap.add_argument("--tiling", choices=sorted(TILINGS), default="page",
                     help="decoder_tiled_192x336: the page's (60,104)/(30,52) tiles, a reduced "
                          "overlap (stride (52,96)), or no tiling")
+    ap.add_argument("--fuse-norm", choices=("on", "off"), default="on",
+                    help="downsample_96_480x832: compute the first RMS norm + SiLU inside the "
+                         "stride-2 conv (on) or as its own kernel (off)")
     ap.add_argument("--kernel-reps", type=int, default=50,
                     help="launches of the dominant kernel timed for the roofline")
     ap.add_argument("--warmup-seconds", type=float, default=0.5,
@@ -446,7 +449,8 @@ def wl_downsample():
     pages' L0 map: RMS norm + SiLU, the 1x3x3 stride-2 conv (480x832 ->
     240x416, one trailing zero row and column), the 3x1x1 temporal-stride-2
     conv (17 -> 9 frames, its cache and phase carried across chunks), RMS norm
-    + SiLU; chunks of 1+4+4+4+4 frames."""
+    + SiLU; chunks of 1+4+4+4+4 frames.  With --fuse-norm on (the default) the
+    first norm runs inside the stride-2 conv's staging."""
     import torch
     from video_vae_causal_amd import _lib as L, accounting as acc, inputs
     d = inputs.downsample_inputs()
@@ -465,6 +469,7 @@ def wl_downsample():
     out = L.empty_cl(y.shape)
     caches = [L.empty_cl((n, c, 2, ho, wo)) for _ in range(2)]
     hs = [cl(h1[:, :, s:s + k]) for s, k in zip(starts, sizes)]
+    xs = [cl(x[:, :, s:s + k]) for s, k in zip(starts, sizes)]
     ss = [cl(sbuf[:, :, s:s + k]) for s, k in zip(starts, sizes)]
     ys = [y[:, :, s:s + k] for s, k in zip(ostarts, touts)]
     sp_kw = dict(stride=(1, 2, 2), padding=(0, 0), pad_extra=(1, 1))
@@ -472,11 +477,19 @@ def wl_downsample():
     wsp = L.wvc_conv3d_pack_weights(p["w_s"], **sp_kw)
     wtp = L.wvc_conv3d_pack_weights(p["w_t"], **tm_kw)
 
+    def spatial(i):
+        if FUSE_NORM:
+            L.wvc_rmsnorm_silu_conv3d_fwd(xs[i], p["gamma1"], p["w_s"], p["b_s"], y=ss[i],
+                                          packed_weight=wsp)
+        else:
+            L.wvc_causal_conv3d_fwd(hs[i], p["w_s"], p["b_s"], y=ss[i], packed_weight=wsp, **sp_kw)
+
     def step():
-        L.wvc_rmsnorm_silu(x, p["gamma1"], y=h1)
+        if not FUSE_NORM:
+            L.wvc_rmsnorm_silu(x, p["gamma1"], y=h1)
         L.wvc_cache_reset(caches[0])
         for i in range(len(sizes)):
-            L.wvc_causal_conv3d_fwd(hs[i], p["w_s"], p["b_s"], y=ss[i], packed_weight=wsp, **sp_kw)
+            spatial(i)
             L.wvc_causal_conv3d_fwd(ss[i], p["w_t"], p["b_t"], caches[i % 2], caches[(i + 1) % 2],
                                     y=ys[i], packed_weight=wtp, t_phase=phases[i], **tm_kw)
         L.wvc_rmsnorm_silu(y, p["gamma2"], y=out)
@@ -485,19 +498,22 @@ def wl_downsample():
     f_tm = 2 * 3 * c * c * sum(touts) * ho * wo
 
     def kernel():
-        L.wvc_causal_conv3d_fwd(hs[1], p["w_s"], p["b_s"], y=ss[1], packed_weight=wsp, **sp_kw)
+        spatial(1)
 
     k_bytes = 2 * c * (4 * h * w + 4 * ho * wo) + 2 * 9 * c * c
     info = dict(workload="downsample_96_480x832", conv_flops=f_sp + f_tm, latent_frames=t,
                 config={"workload": "downsample_96_480x832", "channels": c, "frames": t,
                         "height": h, "width": w, "out_frames": sum(touts), "out_height": ho,
-                        "out_width": wo, "chunks": sizes, "batch": n},
-                kernel=kernel, kernel_name="strided_kernel<1, 64, 3, 2, 2, 12>",
+                        "out_width": wo, "chunks": sizes, "batch": n, "fused_norm": FUSE_NORM},
+                kernel=kernel,
+                kernel_name=("strided_kernel<1, 64, 3, 2, 2, 12, true>" if FUSE_NORM
+                             else "strided_kernel<1, 64, 3, 2, 2, 12, false>"),
                 kernel_units=k_bytes, kernel_bound="hbm", kernel_bytes=k_bytes,
                 kernel_flops=2 * 9 * c * c * 4 * ho * wo)
     return step, info
 
 
+FUSE_NORM = True  # set from --fuse-norm in main()
 TILINGS = {"page": ((60, 104), (30, 52)), "reduced": ((60, 104), (52, 96)), "untiled": (None, None)}
 TILING = "page"  # set from --tiling in main()
 
@@ -619,10 +635,10 @@ def cpu_baseline(workload: str):
         xs = d["x"][:, :, :4].astype(np.float64)   # frames 0..3 (one 4-frame chunk)
         n, c, f, h, w = xs.shape
         flops = 2 * 9 * c * c * f * (h // 2) * (w // 2)
-        ws_, bs_ = d["w_s"].astype(np.float64), d["b_s"].astype(np.float64)
-        run = lambda: oracle.causal_conv3d_strided(xs, ws_, bs_, stride=(1, 2, 2), pad=(0, 0),
-                                                   pad_extra=(1, 1))
-        sample = "frames 0-3 (one 4-frame chunk) of the stride-2 spatial conv"
+        ws_, bs_, g_ = d["w_s"].astype(np.float64), d["b_s"].astype(np.float64), d["gamma1"].astype(np.float64)
+        run = lambda: oracle.causal_conv3d_strided(oracle.norm_silu(xs, g_, bf16=True), ws_, bs_,
+                                                   stride=(1, 2, 2), pad=(0, 0), pad_extra=(1, 1))
+        sample = "frames 0-3 (one 4-frame chunk): norm + SiLU, then the stride-2 spatial conv"
     elif workload == "resblock_384_60x104_e4m3":
         r = inputs.resblock_inputs(seed=2)
         x = r["x"].astype(np.float64)
@@ -715,8 +731,9 @@ def main():
     L.load()
     torch.cuda.set_device(0)
 
-    global PIPELINE, TILING
+    global PIPELINE, TILING, FUSE_NORM
     PIPELINE = args.pipeline == "on"
+    FUSE_NORM = args.fuse_norm == "on"
     TILING = args.tiling
     step, info = WORKLOADS[args.workload]()
     timed = step

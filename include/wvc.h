@@ -308,6 +308,26 @@ int wvc_tile_blend_finish(const float *acc, const float *wsum, void *y, int n, i
  * a call that would take the generic route fails with WVC_ERR_STRICT.
  * Initialised from the environment variable WVC_STRICT (=1 turns it on). */
 /*
+ * Fused RMS norm + SiLU and the encoder's stride-2 spatial conv ([P1] 10.5:
+ * the norm + SiLU before the per-frame zero pad and 3x3 stride-2 conv; 10.2
+ * and 10.4 for the norm and SiLU):
+ *   y = conv_d( round_bf16( silu( rmsnorm(x; gamma, beta, eps) ) ) ) + residual
+ * with the norm of wvc_rmsnorm_silu over C_in and the conv of
+ * wvc_causal_conv3d_fwd for descriptor d; the zero padding of the conv pads
+ * the normalised tensor.  The normalised tensor is computed inside the conv's
+ * staging and never stored: one pass over x instead of three.  d must take
+ * the MFMA 1x3x3 stride (1,2,2) route (bf16, C_in % 32 == 0, C_out % 16 == 0,
+ * C_out <= 256; WVC_ERR_UNSUPPORTED otherwise); all tensors 16-byte aligned.
+ * gamma [C_in], beta [C_in] or NULL, bf16; eps > 0.  The norm's fp32 sum of
+ * squares may be ordered differently from wvc_rmsnorm_silu's, so results can
+ * differ from the unfused pair in the last bit of a few normalised values.
+ */
+int wvc_rmsnorm_silu_conv3d_fwd(const wvc_conv3d_desc *d, const void *x, const void *gamma,
+                                const void *beta, float eps, const void *weight, const void *bias,
+                                const void *residual, void *y, void *workspace,
+                                size_t workspace_bytes, void *stream);
+
+/*
  * 8-bit (E4M3) path.  [P1] sections 7 and 9 name 8-bit weights and
  * activations for the Conv3D as the way to cut the bytes of the 16-bit
  * engine; on MI355X the 8-bit float the matrix cores read is OCP E4M3

@@ -358,3 +358,22 @@ def test_e4m3_quantiser_and_norm_validation(lib):
     assert norm(scale=0.0) == L.WVC_ERR_ARG
     assert norm(g=None) == L.WVC_ERR_ARG
     assert norm(q=X + 16) == L.WVC_ERR_ALIAS
+
+
+def test_fused_norm_conv_validation(lib):
+    sp = L.conv_desc((1, 96, 2, 16, 16), (96, 96, 1, 3, 3), L.WVC_BF16, stride=(1, 2, 2),
+                     padding=(0, 0), pad_extra=(1, 1))
+    need = lib.wvc_causal_conv3d_workspace_bytes(ctypes.byref(sp))
+    G, BE = W + 0x200000, W + 0x300000
+    f = lambda d, **kw: lib.wvc_rmsnorm_silu_conv3d_fwd(
+        ctypes.byref(d), kw.get("x", X), kw.get("g", G), kw.get("be", BE), kw.get("eps", 1e-12), W, B,
+        None, kw.get("y", Y), WS, need, None)
+    # only the stride-2 spatial route has a fused form
+    assert f(desc()) == L.WVC_ERR_UNSUPPORTED
+    assert f(sp, g=None) == L.WVC_ERR_ARG
+    assert f(sp, eps=0.0) == L.WVC_ERR_ARG
+    assert f(sp, g=G + 8) == L.WVC_ERR_ARG        # unaligned gamma
+    assert f(sp, y=G) == L.WVC_ERR_ALIAS          # y over gamma
+    assert need > 0  # standard-layout weights are packed into the workspace
+    assert lib.wvc_rmsnorm_silu_conv3d_fwd(ctypes.byref(sp), X, G, None, 1e-12, W, B, None, Y, WS,
+                                           need - 1, None) == L.WVC_ERR_WORKSPACE

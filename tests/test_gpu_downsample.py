@@ -171,3 +171,37 @@ def test_downsample_full_size_sampled():
         ref.append(oracle.causal_conv3d_strided(win, wt_, bt, stride=(1, 1, 1), pad=(0, 0))[0, :, 2, 0, 0])
         got.append(yd[0, :, j, h, w])
     check_bf16(np.stack(got, 1), np.stack(ref, 1), "temporal stride 2, full size (sampled)")
+
+
+@pytest.mark.parametrize("cin,cout,t,h,w,beta", [
+    (96, 96, 2, 13, 150, False),   # the 96-channel path: ragged 64-column runs, odd rows
+    (96, 96, 1, 8, 16, True),      # with beta: the zero padding must stay zero, not SiLU(beta)
+    (64, 128, 2, 9, 70, True),     # the general channel count path
+    (128, 64, 1, 6, 10, False),
+])
+def test_fused_norm_spatial_conv_vs_oracle(cin, cout, t, h, w, beta):
+    # RMS norm + SiLU computed in the stride-2 conv's staging, against the
+    # oracle's norm (rounded to bf16, where the unfused path stores it) then conv
+    x = bf((1, cin, t, h, w), 61, "x") * 2.0
+    g = inputs.norm_gamma(cin, 61, "g", "bf16")
+    be = inputs.quantize(inputs.normal((cin,), 61, "be", std=0.3), "bf16") if beta else None
+    wt = inputs.conv_weight(cout, cin, (1, 3, 3), 61, "w", "bf16")
+    b = inputs.conv_bias(cout, 61, "b", "bf16")
+    print(f"[case] fused norm + spatial s2 {cin}->{cout} t={t} {h}x{w} beta={beta}", flush=True)
+    L.wvc_reset_counters()
+    y = L.wvc_rmsnorm_silu_conv3d_fwd(to_dev(x), to_dev(g), to_dev(wt), to_dev(b),
+                                      beta=to_dev(be) if beta else None)
+    strided_route_taken(True)
+    hn = oracle.norm_silu(f64(x), f64(g), f64(be) if beta else None, bf16=True)
+    ref = oracle.causal_conv3d_strided(hn, f64(wt), f64(b), stride=(1, 2, 2), pad=(0, 0),
+                                       pad_extra=(1, 1))
+    assert tuple(y.shape) == ref.shape
+    check_bf16(to_host(y), ref, f"fused norm + spatial conv {cin}->{cout}")
+    # and it matches the unfused pair of kernels to within the last bit of
+    # a few normalised inputs
+    hd = L.wvc_rmsnorm_silu(to_dev(x), to_dev(g), to_dev(be) if beta else None)
+    y2 = L.wvc_causal_conv3d_fwd(hd, to_dev(wt), to_dev(b), stride=(1, 2, 2), padding=(0, 0),
+                                 pad_extra=(1, 1))
+    rel = oracle.rel_l2(to_host(y), to_host(y2))
+    print(f"[parity] fused vs unfused rel_l2={rel:.2e}", flush=True)
+    assert rel < 2e-3

@@ -38,7 +38,7 @@ EXPORTED = (
     "wvc_graph_capture_end", "wvc_graph_launch", "wvc_graph_destroy",
     "wvc_tile_extract", "wvc_tile_blend", "wvc_tile_blend_finish",
     "wvc_causal_conv3d_e4m3_fwd", "wvc_quantize_e4m3", "wvc_quantize_rows_e4m3",
-    "wvc_rmsnorm_silu_e4m3",
+    "wvc_rmsnorm_silu_e4m3", "wvc_rmsnorm_silu_conv3d_fwd",
 )
 
 
@@ -137,6 +137,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.wvc_graph_launch.restype = i
     lib.wvc_graph_destroy.argtypes = [vp]
     lib.wvc_graph_destroy.restype = i
+    lib.wvc_rmsnorm_silu_conv3d_fwd.argtypes = [dptr, vp, vp, vp, f, vp, vp, vp, vp, vp, sz, vp]
+    lib.wvc_rmsnorm_silu_conv3d_fwd.restype = i
     lib.wvc_causal_conv3d_e4m3_fwd.argtypes = [dptr, vp, f, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.wvc_causal_conv3d_e4m3_fwd.restype = i
     i64 = ctypes.c_int64
@@ -318,6 +320,45 @@ def wvc_causal_conv3d_fwd(x: torch.Tensor, weight: torch.Tensor, bias: Optional[
     _check(lib.wvc_causal_conv3d_fwd(ctypes.byref(d), _ptr(x), _ptr(cache_in), _ptr(cache_out),
                                       _ptr(wsrc), _ptr(bias), _ptr(residual), _ptr(y),
                                       _ptr(workspace), ws_bytes, _stream(x)))
+    return y
+
+
+def wvc_rmsnorm_silu_conv3d_fwd(x: torch.Tensor, gamma: torch.Tensor, weight: torch.Tensor,
+                                bias: Optional[torch.Tensor] = None,
+                                beta: Optional[torch.Tensor] = None, eps: float = 1e-12,
+                                residual: Optional[torch.Tensor] = None,
+                                y: Optional[torch.Tensor] = None, stride=(1, 2, 2),
+                                padding=(0, 0), pad_extra=(1, 1),
+                                workspace: Optional[torch.Tensor] = None,
+                                packed_weight: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """RMS norm + SiLU fused into the stride-2 spatial conv (see
+    wvc_rmsnorm_silu_conv3d_fwd in include/wvc.h).  Returns y."""
+    lib = load()
+    _need_cl(x, "x")
+    _need_cl(weight, "weight")
+    _need_cl(residual, "residual")
+    _need_cl(y, "y")
+    _need_vec(bias, "bias", weight.shape[0])
+    _need_vec(gamma, "gamma", x.shape[1])
+    _need_vec(beta, "beta", x.shape[1])
+    layout = WVC_WEIGHT_STANDARD if packed_weight is None else WVC_WEIGHT_PACKED
+    d = conv_desc(tuple(x.shape), tuple(weight.shape), _dtype_code(x.dtype), stride, padding,
+                  weight_layout=layout, pad_extra=pad_extra)
+    if y is None:
+        ho, wo = conv_out_hw(x.shape[3], x.shape[4], weight.shape[2:], stride, padding, (1, 1, 1),
+                             pad_extra)
+        y = empty_cl((x.shape[0], weight.shape[0], x.shape[2], ho, wo), x.dtype, x.device)
+    ws_bytes = 0
+    if workspace is None:
+        need = wvc_causal_conv3d_workspace_bytes(d)
+        if need:
+            workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    if workspace is not None:
+        ws_bytes = workspace.numel() * workspace.element_size()
+    wsrc = weight if packed_weight is None else packed_weight
+    _check(lib.wvc_rmsnorm_silu_conv3d_fwd(ctypes.byref(d), _ptr(x), _ptr(gamma), _ptr(beta),
+                                            float(eps), _ptr(wsrc), _ptr(bias), _ptr(residual),
+                                            _ptr(y), _ptr(workspace), ws_bytes, _stream(x)))
     return y
 
 

@@ -30,6 +30,14 @@
 // shorter than an L2 round trip.  Waves split output channels x positions:
 // WCO groups of FCO 16-channel blocks times 4/WCO groups of FPOS 16-position
 // blocks.
+//
+// Fused norm (NORM, spatial route): the conv's input is the RMS norm + SiLU
+// of x (section 10.2 and 10.4 of the same page; the downsample path puts it
+// right before the stride-2 conv).  Each staged input position holds all
+// C_in channels, so after staging one thread per position computes its
+// channel norm in LDS, applies gamma, beta and SiLU, rounds to bf16 (the value
+// the norm kernel would have stored) and writes it back; positions in the
+// zero padding stay zero.  The normalised tensor never goes through HBM.
 #include <type_traits>
 
 #include "wvc_internal.h"
@@ -66,6 +74,8 @@ __device__ __forceinline__ int div_small(int q, float inv_d) {
 struct SParams {
     const uint16_t *x, *cache, *wp, *bias, *res;
     uint16_t *y;
+    const uint16_t *gamma, *beta;  // fused norm (NORM): gamma [C_in], beta [C_in] or null
+    float eps, norm_scale;         // norm clamp and sqrt(C_in)
     int n, t, h, w, ho, wo, cin, cout;
     int F, st, t0, to;  // cache frames, temporal stride, first anchor, output frames
     int ph, pw;
@@ -97,9 +107,10 @@ __device__ __forceinline__ long xcd_slice(long bid, long total) {
 // C8T: C_in / 8 when known at compile time (0: read from p).  With it every
 // division of the staging and K-step index arithmetic is by a constant, and
 // the K loop's trip counts are constants; the 96-channel path uses it.
-template <int MODE, int PT, int FCO, int FPOS, int WCO, int C8T = 0>
+template <int MODE, int PT, int FCO, int FPOS, int WCO, int C8T = 0, bool NORM = false>
 __global__ void __launch_bounds__(256) strided_kernel(SParams p) {
     static_assert(FPOS * 16 * (4 / WCO) == PT, "position groups must tile the run");
+    static_assert(!NORM || MODE == 1, "the fused norm is on the spatial route");
     // A-fragment register sets = K-steps in flight.  The K-step count is
     // taps x C_in/32, a multiple of the tap count, so NS = taps divides it:
     // the K loop body then has no bounds checks, and the compiler's wait
@@ -222,6 +233,53 @@ __global__ void __launch_bounds__(256) strided_kernel(SParams p) {
 #pragma unroll
             for (int k = 0; k < BATCH; ++k)
                 if (dst[k] >= 0) xs[dst[k]] = v[k];
+        }
+    }
+
+    // ---- fused norm + SiLU of the staged positions (spatial route)
+    if constexpr (NORM) {
+        __syncthreads();  // every staged chunk is in LDS
+        constexpr int NC = 2 * PT + 1;
+        const int col0 = 2 * q0 - p.pw;
+        const uint4 *gq = reinterpret_cast<const uint4 *>(p.gamma);
+        const uint4 *bq = reinterpret_cast<const uint4 *>(p.beta);
+        auto unpack = [](uint4 u, float *o) {
+            const uint32_t wd[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                o[2 * k] = bf16_to_f32(wd[k] & 0xffffu);
+                o[2 * k + 1] = bf16_to_f32(wd[k] >> 16);
+            }
+        };
+        for (int pos = tid; pos < 3 * NC; pos += 256) {
+            const int kh = pos / NC, slot = pos - kh * NC;
+            const int cc = slot <= PT ? 2 * slot : 2 * (slot - PT - 1) + 1;
+            const int hs = 2 * oh - p.ph + kh, ws = col0 + cc;
+            const bool in = hs >= 0 && hs < p.h && ws >= 0 && ws < p.w;
+            uint4 *e = xs + (size_t)pos * (C8T ? C8T + 1 : p.pitch);
+            float ss = 0.f;
+            for (int k = 0; k < c8; ++k) {
+                float v[8];
+                unpack(e[k], v);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) ss = fmaf(v[i], v[i], ss);
+            }
+            const float r = p.norm_scale / fmaxf(sqrtf(ss), p.eps);
+            for (int k = 0; k < c8; ++k) {
+                float v[8], g[8], b[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+                unpack(e[k], v);
+                unpack(gq[k], g);
+                if (bq) unpack(bq[k], b);
+                uint32_t o[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float u0 = fmaf(v[2 * i] * r, g[2 * i], b[2 * i]);
+                    const float u1 = fmaf(v[2 * i + 1] * r, g[2 * i + 1], b[2 * i + 1]);
+                    o[i] = pack2_bf16(u0 * __builtin_amdgcn_rcpf(1.f + __expf(-u0)),
+                                      u1 * __builtin_amdgcn_rcpf(1.f + __expf(-u1)));
+                }
+                e[k] = in ? make_uint4(o[0], o[1], o[2], o[3]) : make_uint4(0u, 0u, 0u, 0u);
+            }
         }
     }
 
@@ -376,23 +434,29 @@ Layout layout_for(int cout) {
     return {1, nblk};
 }
 
-template <int MODE, int PT, int FCO, int WCO>
-hipError_t launch_one(const SParams &p, long blocks, size_t lds, hipStream_t s) {
+template <int MODE, int PT, int FCO, int WCO, bool NORM>
+hipError_t launch_norm(const SParams &p, long blocks, size_t lds, hipStream_t s) {
     constexpr int FPOS = PT / 16 / (4 / WCO);
-    if constexpr (FPOS >= 1 && FPOS * 16 * (4 / WCO) == PT) {
+    if constexpr (FPOS >= 1 && FPOS * 16 * (4 / WCO) == PT && (!NORM || MODE == 1)) {
         if constexpr (FCO == 3 && WCO == 2 && PT == 64) {
             if (p.cin == 96) {  // the 96-channel encoder level: constant index arithmetic
-                hipLaunchKernelGGL((strided_kernel<MODE, PT, FCO, FPOS, WCO, 12>), dim3((unsigned)blocks),
-                                   dim3(256), lds, s, p);
+                hipLaunchKernelGGL((strided_kernel<MODE, PT, FCO, FPOS, WCO, 12, NORM>),
+                                   dim3((unsigned)blocks), dim3(256), lds, s, p);
                 return hipGetLastError();
             }
         }
-        hipLaunchKernelGGL((strided_kernel<MODE, PT, FCO, FPOS, WCO>), dim3((unsigned)blocks), dim3(256),
-                           lds, s, p);
+        hipLaunchKernelGGL((strided_kernel<MODE, PT, FCO, FPOS, WCO, 0, NORM>), dim3((unsigned)blocks),
+                           dim3(256), lds, s, p);
         return hipGetLastError();
     } else {
         return hipErrorInvalidValue;
     }
+}
+
+template <int MODE, int PT, int FCO, int WCO>
+hipError_t launch_one(const SParams &p, long blocks, size_t lds, hipStream_t s) {
+    if (p.gamma) return launch_norm<MODE, PT, FCO, WCO, true>(p, blocks, lds, s);
+    return launch_norm<MODE, PT, FCO, WCO, false>(p, blocks, lds, s);
 }
 
 template <int MODE, int PT>
@@ -467,6 +531,13 @@ hipError_t launch_conv_strided(const ConvCall &c, ConvRoute r, bool packed_given
     p.bias = static_cast<const uint16_t *>(c.bias);
     p.res = static_cast<const uint16_t *>(c.residual);
     p.y = static_cast<uint16_t *>(c.y);
+    if (c.norm_gamma) {
+        if (temporal) return hipErrorInvalidValue;  // the fused norm is on the spatial route
+        p.gamma = static_cast<const uint16_t *>(c.norm_gamma);
+        p.beta = static_cast<const uint16_t *>(c.norm_beta);
+        p.eps = c.norm_eps;
+        p.norm_scale = sqrtf((float)c.cin);
+    }
     p.n = c.n; p.t = c.t; p.h = c.h; p.w = c.w; p.ho = c.ho; p.wo = c.wo;
     p.cin = c.cin; p.cout = c.cout;
     p.F = c.frames; p.st = c.st; p.t0 = c.t0; p.to = c.to;

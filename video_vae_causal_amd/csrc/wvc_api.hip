@@ -203,6 +203,8 @@ int plan_conv(const wvc_conv3d_desc *d, ConvPlan *pl, bool count = true) {
     return WVC_OK;
 }
 
+bool ws_ok(const void *ws, size_t bytes) { return ws || bytes == 0; }
+
 int hip_status(hipError_t err, const char *what) {
     if (err == hipSuccess) return WVC_OK;
     return fail(WVC_ERR_HIP, "%s: %s", what, hipGetErrorString(err));
@@ -399,6 +401,60 @@ int wvc_causal_conv3d_fwd(const wvc_conv3d_desc *d, const void *x, const void *c
     }
     return conv_fwd(d, x, cache_in, cache_out, weight, bias, residual, y, workspace,
                     workspace_bytes, static_cast<hipStream_t>(stream));
+}
+
+int wvc_rmsnorm_silu_conv3d_fwd(const wvc_conv3d_desc *d, const void *x, const void *gamma,
+                                const void *beta, float eps, const void *weight, const void *bias,
+                                const void *residual, void *y, void *workspace,
+                                size_t workspace_bytes, void *stream) {
+    ConvPlan pl;
+    int rc = plan_conv(d, &pl);
+    if (rc) return rc;
+    if (pl.route != wvc::ConvRoute::FastSpatial2) {
+        g_rejected++;
+        return fail(WVC_ERR_UNSUPPORTED,
+                    "the fused norm + conv exists for the bf16 1x3x3 stride-(1,2,2) route only");
+    }
+    if (!weight) return fail(WVC_ERR_ARG, "weight is NULL");
+    if (!gamma) return fail(WVC_ERR_ARG, "gamma is NULL");
+    if (!(eps > 0.f)) return fail(WVC_ERR_ARG, "eps must be > 0");
+    if (d->t > 0 && (!x || !y)) return fail(WVC_ERR_ARG, "x or y is NULL");
+    if (!ws_ok(workspace, workspace_bytes)) return fail(WVC_ERR_ARG, "workspace is NULL but workspace_bytes > 0");
+    const bool packed = d->weight_layout == WVC_WEIGHT_PACKED;
+    if (!(aligned(x, 16) && aligned(weight, 16) && aligned(y, 16) && aligned(residual, 16) &&
+          aligned(bias, 8) && aligned(gamma, 16) && aligned(beta, 16)))
+        return fail(WVC_ERR_ARG, "the fused norm + conv needs 16-byte aligned tensors");
+    const size_t need = route_ws_bytes(pl, packed);
+    if (workspace_bytes < need)
+        return fail(WVC_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, need);
+    const Buf bufs[] = {
+        {x, pl.x_bytes, false, "x"},
+        {weight, pl.w_bytes, false, "weight"},
+        {bias, pl.b_bytes, false, "bias"},
+        {residual, pl.y_bytes, false, "residual"},
+        {gamma, (size_t)d->c_in * 2, false, "gamma"},
+        {beta, (size_t)d->c_in * 2, false, "beta"},
+        {y, pl.y_bytes, true, "y"},
+        {workspace, workspace_bytes, true, "workspace"},
+    };
+    rc = check_aliasing(bufs, 8);
+    if (rc) return rc;
+    wvc::ConvCall &c = pl.call;
+    c.x = x;
+    c.weight = weight;
+    c.bias = bias;
+    c.residual = residual;
+    c.y = y;
+    c.norm_gamma = gamma;
+    c.norm_beta = beta;
+    c.norm_eps = eps;
+    if (d->t > 0 && pl.call.to > 0) {
+        const hipError_t err = wvc::launch_conv_strided(c, pl.route, packed, workspace, workspace_bytes,
+                                                        static_cast<hipStream_t>(stream));
+        if (err != hipSuccess) return hip_status(err, "fused norm + conv launch");
+    }
+    g_strided++;
+    return WVC_OK;
 }
 
 int wvc_causal_conv3d_e4m3_fwd(const wvc_conv3d_desc *d, const void *x, float x_scale,

@@ -75,6 +75,12 @@ struct ConvCall {
     // y are bf16; the sum is multiplied by xscale * wscale[co].
     float xscale;
     const float *wscale;   // [Cout], 16-byte aligned
+    // Spatial stride-2 route only: the conv's input is RMS norm + SiLU of x
+    // with these gamma [Cin] (bf16) / beta [Cin] or nullptr, computed in the
+    // conv's staging (nullptr gamma: x is the input itself).
+    const void *norm_gamma;
+    const void *norm_beta;
+    float norm_eps;
 };
 
 enum class ConvRoute { Fast3x3x3, Fast1x1x1, FastTemporal, FastSpatial2, Generic };
