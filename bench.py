@@ -65,6 +65,9 @@ def parse():
     ap.add_argument("--fuse-norm", choices=("on", "off"), default="on",
                     help="downsample_96_480x832: compute the first RMS norm + SiLU inside the "
                          "stride-2 conv (on) or as its own kernel (off)")
+    ap.add_argument("--kernel-timing", choices=("graph", "eager"), default="graph",
+                    help="time the dominant kernel from a replayed HIP graph of its launches, or "
+                         "from eager launches (for profiler runs that collect counters)")
     ap.add_argument("--kernel-reps", type=int, default=50,
                     help="launches of the dominant kernel timed for the roofline")
     ap.add_argument("--warmup-seconds", type=float, default=0.5,
@@ -142,7 +145,7 @@ def time_region(fn, steps, warmup, warmup_s=0.0):
     return start.elapsed_time(end) / steps, wall
 
 
-def kernel_ms(fn, reps, warmup_s):
+def kernel_ms(fn, reps, warmup_s, use_graph=True):
     """Average duration of one launch of ``fn``'s kernels, with HIP events on
     the current stream around replays of a HIP graph that records ``reps``
     calls of ``fn`` back to back: replays carry no host launch overhead, which
@@ -150,6 +153,9 @@ def kernel_ms(fn, reps, warmup_s):
     Falls back to timing eager calls if the calls cannot be recorded."""
     import torch
     from video_vae_causal_amd import stream
+    if not use_graph:
+        ms, _ = time_region(fn, reps, 3, warmup_s)
+        return ms, "eager launches"
     try:
         fn()
         torch.cuda.synchronize()
@@ -209,7 +215,7 @@ def wl_resblock():
                 config={"workload": "resblock_384_60x104", "channels": c, "frames": t,
                         "height": h, "width": w, "chunk_frames": 1, "cache_frames": 2,
                         "batch": n},
-                kernel=kernel, kernel_name="igemm_kernel<3, 128, 32, 2, true, 16> + splitk_reduce_kernel",
+                kernel=kernel, kernel_name="igemm_kernel<3, 128, 32, 2, true, 16, false> + splitk_reduce_kernel",
                 kernel_units=acc.conv_flops(n, 1, h, w, c, c), kernel_bound="mfma",
                 kernel_bytes=acc.conv_launch_bytes(n, 1, h, w, c, c))
     return step, info
@@ -292,7 +298,7 @@ def wl_layer384():
                 config={"workload": "layer_384_240x416", "channels": c, "frames": t,
                         "height": h, "width": w, "chunk_frames": t, "projection_out": int(wp.shape[0]),
                         "batch": n},
-                kernel=kernel, kernel_name="igemm_kernel<3, 128, 32, 2, false, 32>", kernel_units=f3,
+                kernel=kernel, kernel_name="igemm_kernel<3, 128, 32, 2, false, 32, false>", kernel_units=f3,
                 kernel_bound="mfma", kernel_bytes=acc.conv_launch_bytes(n, t, h, w, c, c, cache_frames=0))
     return step, info
 
@@ -388,10 +394,10 @@ def wl_layer96():
     info = dict(workload="layer_96_480x832", conv_flops=conv_flops, latent_frames=t,
                 config={"workload": "layer_96_480x832", "channels": c, "frames": t,
                         "height": h, "width": w, "chunks": sizes, "batch": n},
-                kernel=kernel, kernel_name="igemm_kernel<3, 96, 16, 2, false, 32>",
+                kernel=kernel, kernel_name="igemm_kernel<3, 96, 16, 2, false, 32, false>",
                 kernel_units=acc.conv_flops(n, 4, h, w, c, c), kernel_bound="mfma",
                 kernel_bytes=acc.conv_launch_bytes(n, 4, h, w, c, c),
-                norm_kernel=norm_kernel, norm_kernel_name="rmsnorm_flat_kernel<true, 2, true, false>",
+                norm_kernel=norm_kernel, norm_kernel_name="rmsnorm_flat_kernel<true, 2, true, false, false>",
                 norm_bytes=acc.norm_bytes(n * c * t * h * w))
     return step, info
 
@@ -438,7 +444,7 @@ def wl_decoder():
     info = dict(workload="decoder_stack_48_30x52", conv_flops=per_frame * t, latent_frames=t,
                 config={"workload": "decoder_stack_48_30x52", "latent_channels": cl_, "channels": width,
                         "frames": t, "height": h, "width": w, "chunk_frames": 1, "batch": n},
-                kernel=kernel, kernel_name="igemm_kernel<3, 128, 32, 2, true, 16> + splitk_reduce_kernel",
+                kernel=kernel, kernel_name="igemm_kernel<3, 128, 32, 2, true, 16, false> + splitk_reduce_kernel",
                 kernel_units=acc.conv_flops(n, 1, 2 * h, 2 * w, width, width), kernel_bound="mfma",
                 kernel_bytes=acc.conv_launch_bytes(n, 1, 2 * h, 2 * w, width, width))
     return step, info
@@ -569,8 +575,8 @@ def wl_tiled():
                         "tiles": tiles, "decoded_latent_px_per_px": round(tiles * th * tw / (h * w), 3),
                         "chunk_frames": 1, "batch": n},
                 kernel=kernel,
-                kernel_name=("igemm_kernel<3, 128, 32, 2, true, 16> + splitk_reduce_kernel" if tile
-                             else "igemm_kernel<3, 128, 32, 2, *, *> (whole 384x672 frame)"),
+                kernel_name=("igemm_kernel<3, 128, 32, 2, true, 16, false> + splitk_reduce_kernel" if tile
+                             else "igemm_kernel<3, 128, 32, 2, *, *, false> (whole 384x672 frame)"),
                 kernel_units=acc.conv_flops(n, 1, 2 * th, 2 * tw, width, width), kernel_bound="mfma",
                 kernel_bytes=acc.conv_launch_bytes(n, 1, 2 * th, 2 * tw, width, width))
     return step, info
@@ -751,7 +757,8 @@ def main():
     value = info["conv_flops"] / (ms_step * 1e-3) / 1e12
 
     # dominant kernel, timed alone with events on the stream it is launched on
-    k_ms, k_timing = kernel_ms(info["kernel"], args.kernel_reps, min(args.warmup_seconds, 0.2))
+    k_ms, k_timing = kernel_ms(info["kernel"], args.kernel_reps, min(args.warmup_seconds, 0.2),
+                               args.kernel_timing == "graph")
     traffic = measured_traffic(args.traffic_json, args.workload, info["kernel_name"])
     if info["kernel_bound"] == "hbm":
         achieved = info["kernel_bytes"] / (k_ms * 1e-3) / 1e9
@@ -785,7 +792,8 @@ def main():
         "roofline": roofline,
     }
     if "norm_kernel" in info:
-        n_ms, n_timing = kernel_ms(info["norm_kernel"], 20, min(args.warmup_seconds, 0.2))
+        n_ms, n_timing = kernel_ms(info["norm_kernel"], 20, min(args.warmup_seconds, 0.2),
+                                   args.kernel_timing == "graph")
         gbs = info["norm_bytes"] / (n_ms * 1e-3) / 1e9
         line["roofline_norm"] = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
                                  "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
