@@ -205,3 +205,25 @@ def test_fused_norm_spatial_conv_vs_oracle(cin, cout, t, h, w, beta):
     rel = oracle.rel_l2(to_host(y), to_host(y2))
     print(f"[parity] fused vs unfused rel_l2={rel:.2e}", flush=True)
     assert rel < 2e-3
+
+
+@pytest.mark.parametrize("fused", [False, True])
+def test_spatial_stride2_larger_grid(fused):
+    # a few thousand 64-column runs over 4 frames, ragged in both directions
+    cin, cout, t, h, w = 96, 96, 4, 162, 258
+    x = bf((1, cin, t, h, w), 71, "x")
+    wt = inputs.conv_weight(cout, cin, (1, 3, 3), 71, "w", "bf16")
+    b = inputs.conv_bias(cout, 71, "b", "bf16")
+    g = inputs.norm_gamma(cin, 71, "g", "bf16")
+    be = inputs.quantize(inputs.normal((cin,), 71, "be", std=0.3), "bf16")
+    print(f"[case] spatial s2 larger grid {t}x{h}x{w} fused={fused}", flush=True)
+    if fused:
+        y = L.wvc_rmsnorm_silu_conv3d_fwd(to_dev(x), to_dev(g), to_dev(wt), to_dev(b), beta=to_dev(be))
+        xin = oracle.norm_silu(f64(x), f64(g), f64(be), bf16=True)
+    else:
+        y = L.wvc_causal_conv3d_fwd(to_dev(x), to_dev(wt), to_dev(b), stride=(1, 2, 2), padding=(0, 0),
+                                    pad_extra=(1, 1))
+        xin = f64(x)
+    ref = oracle.causal_conv3d_strided(xin, f64(wt), f64(b), stride=(1, 2, 2), pad=(0, 0), pad_extra=(1, 1))
+    assert tuple(y.shape) == ref.shape
+    check_bf16(to_host(y), ref, f"spatial s2 larger grid fused={fused}")
