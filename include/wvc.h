@@ -382,6 +382,43 @@ int wvc_causal_conv3d_e4m3_fwd(const wvc_conv3d_desc *d, const void *x, float x_
                                const float *w_scale, const void *bias, const void *residual,
                                void *y, void *workspace, size_t workspace_bytes, void *stream);
 
+/*
+ * The residual block of wvc_resblock_fwd on the 8-bit path (identity
+ * shortcut, C_in == C_out): norm1 + SiLU stored as codes at activation scale
+ * s1, the 8-bit conv1 (bf16 result), norm2 + SiLU as codes at s2, the 8-bit
+ * conv2 plus x:
+ *   q1 = E4M3(silu(norm1(x)) / s1)          (quantiser rule above)
+ *   h  = round_bf16(s1 * w1_scale[co] * conv(q1 | cache1) + b1)
+ *   q2 = E4M3(silu(norm2(h)) / s2)
+ *   y  = round_bf16(s2 * w2_scale[co] * conv(q2 | cache2) + b2 + x)
+ * d->dtype must be WVC_BF16 (x, y, gamma, beta, biases); w1 and w2 are E4M3
+ * codes in the standard layout or packed by wvc_conv3d_pack_weights with an
+ * E4M3 descriptor (d->weights_packed); w1_scale/w2_scale [C] fp32, 16-byte
+ * aligned.  The caches hold codes: cache1 of q1, cache2 of q2, each
+ * [N, C, 2, H, W] bytes (in NULL = zero causal padding; out NULL = skip).
+ * The C_in/C_out, alignment and channel rules of the 8-bit conv apply.  On a
+ * split-K plan conv1's partial sums are added, scaled and rounded inside the
+ * norm2 kernel, bit for bit the h above, so h is never stored.  Workspace:
+ * wvc_resblock_e4m3_workspace_bytes(d) bytes, contents on entry irrelevant.
+ * Aliasing, errors and streams as for wvc_resblock_fwd.
+ */
+typedef struct wvc_resblock_e4m3_params {
+    const void *gamma1, *beta1;  /* norm1 over C (bf16); beta1 may be NULL */
+    const void *w1;              /* conv1 codes                            */
+    const float *w1_scale;       /* [C] fp32                               */
+    const void *b1;              /* [C] bf16 or NULL                       */
+    const void *gamma2, *beta2;  /* norm2; beta2 may be NULL               */
+    const void *w2;
+    const float *w2_scale;
+    const void *b2;
+    float s1, s2;                /* activation scales of q1, q2 (> 0)      */
+} wvc_resblock_e4m3_params;
+int wvc_resblock_e4m3_fwd(const wvc_resblock_desc *d, const void *x, void *y,
+                          const wvc_resblock_e4m3_params *p, const void *cache1_in,
+                          void *cache1_out, const void *cache2_in, void *cache2_out,
+                          void *workspace, size_t workspace_bytes, void *stream);
+size_t wvc_resblock_e4m3_workspace_bytes(const wvc_resblock_desc *d);
+
 void wvc_set_strict(int on);
 int wvc_get_strict(void);
 

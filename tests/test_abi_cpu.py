@@ -377,3 +377,35 @@ def test_fused_norm_conv_validation(lib):
     assert need > 0  # standard-layout weights are packed into the workspace
     assert lib.wvc_rmsnorm_silu_conv3d_fwd(ctypes.byref(sp), X, G, None, 1e-12, W, B, None, Y, WS,
                                            need - 1, None) == L.WVC_ERR_WORKSPACE
+
+
+def test_resblock_e4m3_validation(lib):
+    rd = L.resblock_desc((1, 32, 2, 8, 8), 32, L.WVC_BF16)
+    need = lib.wvc_resblock_e4m3_workspace_bytes(ctypes.byref(rd))
+    assert need != ctypes.c_size_t(-1).value and need > 0
+    bad = L.resblock_desc((1, 32, 2, 8, 8), 64, L.WVC_BF16)   # projection shortcut
+    assert lib.wvc_resblock_e4m3_workspace_bytes(ctypes.byref(bad)) == ctypes.c_size_t(-1).value
+    f32 = L.resblock_desc((1, 32, 2, 8, 8), 32, L.WVC_F32)
+    assert lib.wvc_resblock_e4m3_workspace_bytes(ctypes.byref(f32)) == ctypes.c_size_t(-1).value
+    odd = L.resblock_desc((1, 24, 2, 8, 8), 24, L.WVC_BF16)   # C % 16 != 0: no 8-bit conv
+    assert lib.wvc_resblock_e4m3_workspace_bytes(ctypes.byref(odd)) == ctypes.c_size_t(-1).value
+
+    def params(**kw):
+        pr = L.ResblockE4M3Params()
+        base = dict(gamma1=W + 0x100000, gamma2=W + 0x110000, w1=W, w2=W + 0x200000,
+                    w1_scale=W + 0x300000, w2_scale=W + 0x310000, s1=0.01, s2=0.01)
+        base.update(kw)
+        for k, v in base.items():
+            setattr(pr, k, v)
+        return pr
+
+    call = lambda pr, wsb=need, y=Y: lib.wvc_resblock_e4m3_fwd(
+        ctypes.byref(rd), X, y, ctypes.byref(pr), None, None, None, None, WS, wsb, None)
+    assert call(params(w1_scale=None)) == L.WVC_ERR_ARG
+    assert call(params(gamma2=None)) == L.WVC_ERR_ARG
+    assert call(params(s1=0.0)) == L.WVC_ERR_ARG
+    assert call(params(s2=float("inf"))) == L.WVC_ERR_ARG
+    assert call(params(), wsb=need - 1) == L.WVC_ERR_WORKSPACE
+    assert call(params(), y=X) == L.WVC_ERR_ALIAS
+    assert lib.wvc_resblock_e4m3_fwd(ctypes.byref(rd), X, Y, None, None, None, None, None, WS, need,
+                                     None) == L.WVC_ERR_ARG

@@ -227,3 +227,12 @@ def test_spatial_stride2_larger_grid(fused):
     ref = oracle.causal_conv3d_strided(xin, f64(wt), f64(b), stride=(1, 2, 2), pad=(0, 0), pad_extra=(1, 1))
     assert tuple(y.shape) == ref.shape
     check_bf16(to_host(y), ref, f"spatial s2 larger grid fused={fused}")
+
+
+def test_fused_norm_spatial_conv_empty_chunk():
+    x = L.empty_cl((1, 96, 0, 8, 16))
+    g = torch.ones(96, device="cuda", dtype=torch.bfloat16)
+    wt = to_dev(inputs.conv_weight(96, 96, (1, 3, 3), 72, "w", "bf16"))
+    print("[case] fused norm + spatial conv, empty chunk", flush=True)
+    y = L.wvc_rmsnorm_silu_conv3d_fwd(x, g, wt)
+    assert tuple(y.shape) == (1, 96, 0, 4, 8)

@@ -274,3 +274,74 @@ def test_resblock_e4m3_streamed_vs_oracle(c, t, h, w):
     check_bf16(y, ref, f"8-bit resblock {c}ch")
     rel = oracle.rel_l2(y, ref)
     assert rel <= 5e-3, rel
+
+
+def test_conv_e4m3_empty_chunk_only_rolls_the_cache():
+    # a chunk of zero frames computes nothing and passes the cache through
+    c, h, w = 32, 6, 10
+    d = I.e4m3_conv_inputs(seed=23, shape=(1, c, 1, h, w), cout=c)
+    x0 = L.empty_cl((1, c, 0, h, w), torch.uint8)
+    wq = codes_dev(d["w"])
+    ws = torch.from_numpy(d["w_scale"]).to(dev())
+    cin = codes_dev(d["cache"])
+    cout = L.empty_cl((1, c, 2, h, w), torch.uint8)
+    cout.fill_(0x55)
+    print("[case] e4m3 conv, empty chunk", flush=True)
+    y = L.wvc_causal_conv3d_e4m3_fwd(x0, d["x_scale"], wq, ws, cache_in=cin, cache_out=cout)
+    assert y.shape[2] == 0
+    assert np.array_equal(codes_host(cout), d["cache"])
+
+
+def test_quantisers_and_norm_on_empty_tensors():
+    print("[case] empty quantiser / norm inputs", flush=True)
+    x = torch.empty(0, device=dev(), dtype=torch.bfloat16)
+    assert L.wvc_quantize_e4m3(x, 1.0).numel() == 0
+    xn = L.empty_cl((1, 16, 0, 4, 4))
+    g = torch.ones(16, device=dev(), dtype=torch.bfloat16)
+    assert L.wvc_rmsnorm_silu_e4m3(xn, g, 1.0).numel() == 0
+
+
+@pytest.mark.parametrize("c,h,w", [(384, 60, 104), (128, 40, 72)])
+def test_resblock_e4m3_entry_equals_its_chain_bitwise(c, h, w):
+    # wvc_resblock_e4m3_fwd (conv1's partial sums fed into the norm2 kernel)
+    # against the same block built from the separate entry points: norm ->
+    # codes, 8-bit conv (reduce included), norm -> codes, 8-bit conv + x
+    from video_vae_causal_amd import stream
+    print(f"[case] 8-bit block entry vs chain, c={c} {h}x{w}", flush=True)
+    p = {k: to_dev(v) for k, v in I.resblock_params(c, 24, "blk", "bf16", with_beta=True).items()}
+    x = to_dev(I.quantize(I.normal((1, c, 2, h, w), 24, "x"), "bf16"))
+    s1, s2 = 5.0 / 448, 4.0 / 448
+    blk = stream.ResBlockE4M3(p, s1, s2)
+    y_entry = torch.cat([blk(x[:, :, f:f + 1].contiguous(memory_format=torch.channels_last_3d))
+                         for f in range(2)], dim=2)
+    (w1q, w1s, _), (w2q, w2s, _) = blk.w["w1"], blk.w["w2"]
+    pair1 = [L.empty_cl((1, c, 2, h, w), torch.uint8) for _ in range(2)]
+    pair2 = [L.empty_cl((1, c, 2, h, w), torch.uint8) for _ in range(2)]
+    outs = []
+    for f in range(2):  # frame 0 from zero past, frame 1 reading the caches frame 0 wrote
+        xf = x[:, :, f:f + 1].contiguous(memory_format=torch.channels_last_3d)
+        c1_in, c1_out = (None, pair1[0]) if f == 0 else (pair1[0], pair1[1])
+        c2_in, c2_out = (None, pair2[0]) if f == 0 else (pair2[0], pair2[1])
+        q1 = L.wvc_rmsnorm_silu_e4m3(xf, p["gamma1"], s1, beta=p["beta1"])
+        hb = L.wvc_causal_conv3d_e4m3_fwd(q1, s1, w1q, w1s, p["b1"], c1_in, c1_out)
+        q2 = L.wvc_rmsnorm_silu_e4m3(hb, p["gamma2"], s2, beta=p["beta2"])
+        outs.append(L.wvc_causal_conv3d_e4m3_fwd(q2, s2, w2q, w2s, p["b2"], c2_in, c2_out,
+                                                 residual=xf))
+    y_chain = torch.cat(outs, dim=2)
+    assert torch.equal(y_entry, y_chain)
+
+
+def test_resblock_e4m3_empty_chunk_passes_caches():
+    from video_vae_causal_amd import _lib
+    c, h, w = 64, 6, 8
+    print("[case] 8-bit block, empty chunk", flush=True)
+    p = {k: to_dev(v) for k, v in I.resblock_params(c, 25, "blk", "bf16").items()}
+    q = {"gamma1": p["gamma1"], "gamma2": p["gamma2"], "b1": p["b1"], "b2": p["b2"]}
+    for k in ("w1", "w2"):
+        q[k], q[k + "_scale"] = L.wvc_quantize_rows_e4m3(p[k])
+    cin = [codes_dev(I.e4m3_codes((1, c, 2, h, w), 25, n)) for n in ("c1", "c2")]
+    cout = [L.empty_cl((1, c, 2, h, w), torch.uint8) for _ in range(2)]
+    x0 = L.empty_cl((1, c, 0, h, w))
+    y = L.wvc_resblock_e4m3_fwd(x0, q, 0.01, 0.01, cin[0], cout[0], cin[1], cout[1])
+    assert y.shape[2] == 0
+    assert torch.equal(cout[0], cin[0]) and torch.equal(cout[1], cin[1])

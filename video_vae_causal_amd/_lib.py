@@ -38,7 +38,8 @@ EXPORTED = (
     "wvc_graph_capture_end", "wvc_graph_launch", "wvc_graph_destroy",
     "wvc_tile_extract", "wvc_tile_blend", "wvc_tile_blend_finish",
     "wvc_causal_conv3d_e4m3_fwd", "wvc_quantize_e4m3", "wvc_quantize_rows_e4m3",
-    "wvc_rmsnorm_silu_e4m3", "wvc_rmsnorm_silu_conv3d_fwd",
+    "wvc_rmsnorm_silu_e4m3", "wvc_rmsnorm_silu_conv3d_fwd", "wvc_resblock_e4m3_fwd",
+    "wvc_resblock_e4m3_workspace_bytes",
 )
 
 
@@ -57,6 +58,13 @@ class ResblockDesc(ctypes.Structure):
 class ResblockParams(ctypes.Structure):
     _fields_ = [(f, ctypes.c_void_p) for f in (
         "gamma1", "beta1", "w1", "b1", "gamma2", "beta2", "w2", "b2", "w_short", "b_short")]
+
+
+class ResblockE4M3Params(ctypes.Structure):
+    _fields_ = [("gamma1", ctypes.c_void_p), ("beta1", ctypes.c_void_p), ("w1", ctypes.c_void_p),
+                ("w1_scale", ctypes.c_void_p), ("b1", ctypes.c_void_p), ("gamma2", ctypes.c_void_p),
+                ("beta2", ctypes.c_void_p), ("w2", ctypes.c_void_p), ("w2_scale", ctypes.c_void_p),
+                ("b2", ctypes.c_void_p), ("s1", ctypes.c_float), ("s2", ctypes.c_float)]
 
 
 class Counters(ctypes.Structure):
@@ -137,6 +145,11 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.wvc_graph_launch.restype = i
     lib.wvc_graph_destroy.argtypes = [vp]
     lib.wvc_graph_destroy.restype = i
+    lib.wvc_resblock_e4m3_fwd.argtypes = [ctypes.POINTER(ResblockDesc), vp, vp,
+                                          ctypes.POINTER(ResblockE4M3Params), vp, vp, vp, vp, vp, sz, vp]
+    lib.wvc_resblock_e4m3_fwd.restype = i
+    lib.wvc_resblock_e4m3_workspace_bytes.argtypes = [ctypes.POINTER(ResblockDesc)]
+    lib.wvc_resblock_e4m3_workspace_bytes.restype = sz
     lib.wvc_rmsnorm_silu_conv3d_fwd.argtypes = [dptr, vp, vp, vp, f, vp, vp, vp, vp, vp, sz, vp]
     lib.wvc_rmsnorm_silu_conv3d_fwd.restype = i
     lib.wvc_causal_conv3d_e4m3_fwd.argtypes = [dptr, vp, f, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
@@ -320,6 +333,48 @@ def wvc_causal_conv3d_fwd(x: torch.Tensor, weight: torch.Tensor, bias: Optional[
     _check(lib.wvc_causal_conv3d_fwd(ctypes.byref(d), _ptr(x), _ptr(cache_in), _ptr(cache_out),
                                       _ptr(wsrc), _ptr(bias), _ptr(residual), _ptr(y),
                                       _ptr(workspace), ws_bytes, _stream(x)))
+    return y
+
+
+def wvc_resblock_e4m3_workspace_bytes(d: ResblockDesc) -> int:
+    v = load().wvc_resblock_e4m3_workspace_bytes(ctypes.byref(d))
+    if v == ctypes.c_size_t(-1).value:
+        raise WvcError(WVC_ERR_ARG, load().wvc_last_error().decode())
+    return v
+
+
+def wvc_resblock_e4m3_fwd(x: torch.Tensor, params: dict, s1: float, s2: float, cache1_in=None,
+                          cache1_out=None, cache2_in=None, cache2_out=None,
+                          y: Optional[torch.Tensor] = None, eps: float = 1e-12,
+                          workspace: Optional[torch.Tensor] = None, packed: bool = False) -> torch.Tensor:
+    """The residual block on the 8-bit path (see wvc_resblock_e4m3_fwd in
+    include/wvc.h).  ``params`` holds gamma1, beta1, gamma2, beta2, b1, b2
+    (bf16 vectors), w1, w2 (uint8 E4M3 codes, packed when ``packed``) and
+    w1_scale, w2_scale (float32 [C]).  Caches are uint8 codes."""
+    lib = load()
+    _need_cl(x, "x")
+    _need_cl(y, "y")
+    for name, t in (("cache1_in", cache1_in), ("cache1_out", cache1_out), ("cache2_in", cache2_in),
+                    ("cache2_out", cache2_out)):
+        _need_cl(t, name)
+    c = x.shape[1]
+    for k in ("gamma1", "gamma2", "beta1", "beta2", "b1", "b2", "w1_scale", "w2_scale"):
+        _need_vec(params.get(k), k, c)
+    d = resblock_desc(tuple(x.shape), c, WVC_BF16, eps, weights_packed=packed)
+    if y is None:
+        y = empty_cl(x.shape, x.dtype, x.device)
+    if workspace is None:
+        workspace = torch.empty(max(1, wvc_resblock_e4m3_workspace_bytes(d)), dtype=torch.uint8,
+                                device=x.device)
+    pr = ResblockE4M3Params()
+    for k in ("gamma1", "beta1", "w1", "w1_scale", "b1", "gamma2", "beta2", "w2", "w2_scale", "b2"):
+        t = params.get(k)
+        setattr(pr, k, None if t is None else t.data_ptr())
+    pr.s1, pr.s2 = float(s1), float(s2)
+    _check(lib.wvc_resblock_e4m3_fwd(ctypes.byref(d), _ptr(x), _ptr(y), ctypes.byref(pr),
+                                      _ptr(cache1_in), _ptr(cache1_out), _ptr(cache2_in),
+                                      _ptr(cache2_out), _ptr(workspace),
+                                      workspace.numel() * workspace.element_size(), _stream(x)))
     return y
 
 

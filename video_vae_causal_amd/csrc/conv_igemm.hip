@@ -895,7 +895,7 @@ bool igemm_supports(const ConvCall &c) {
 hipError_t launch_conv_igemm(const ConvCall &c, ConvRoute r, bool packed_given, void *ws,
                              size_t ws_bytes, void *cache_out, hipStream_t s, ConvPartials *defer) {
     if (defer) *defer = ConvPartials{};
-    if (is_e4m3(c)) defer = nullptr;  // the fused consumers read bf16 sums without scales
+    // (8-bit conv: deferred partials are raw sums; the consumer applies the scales)
     if (is_e4m3(c) && r != ConvRoute::Fast3x3x3) return hipErrorInvalidValue;
     const Plan pl = make_plan(c, r);
     if (pl.th == 0) return hipErrorInvalidValue;

@@ -88,6 +88,8 @@ struct Partials {
     size_t stride;      // elements of one split
     int S;
     const uint4 *bias;  // [C] bf16, or nullptr
+    const float4 *wscale = nullptr;  // 8-bit conv: [C] weight scales (sum *= xscale * wscale)
+    float xscale = 1.f;
 };
 
 // FROM_PARTS: the input chunk is not read from x but built from partial sums,
@@ -111,6 +113,7 @@ __global__ void __launch_bounds__(256) rmsnorm_flat_kernel(const uint4 *__restri
     __shared__ uint4 g_s[FLAT_MAX_CPP];
     __shared__ uint4 b_s[FLAT_MAX_CPP];
     __shared__ uint4 cb_s[FROM_PARTS ? FLAT_MAX_CPP : 1];  // the conv's bias
+    __shared__ float4 sc_s[FROM_PARTS ? 2 * FLAT_MAX_CPP : 1];  // x_scale * w_scale (8-bit conv)
     const int tid = threadIdx.x;
     const long pos0 = (long)blockIdx.x * P;
     const long left = positions - pos0;
@@ -122,7 +125,14 @@ __global__ void __launch_bounds__(256) rmsnorm_flat_kernel(const uint4 *__restri
     for (int c = tid; c < cpp; c += 256) {
         g_s[c] = gamma[c];
         b_s[c] = beta ? beta[c] : make_uint4(0u, 0u, 0u, 0u);
-        if constexpr (FROM_PARTS) cb_s[c] = pp.bias ? pp.bias[c] : make_uint4(0u, 0u, 0u, 0u);
+        if constexpr (FROM_PARTS) {
+            cb_s[c] = pp.bias ? pp.bias[c] : make_uint4(0u, 0u, 0u, 0u);
+            if (pp.wscale) {
+                const float4 a = pp.wscale[2 * c], b = pp.wscale[2 * c + 1];
+                sc_s[2 * c] = make_float4(pp.xscale * a.x, pp.xscale * a.y, pp.xscale * a.z, pp.xscale * a.w);
+                sc_s[2 * c + 1] = make_float4(pp.xscale * b.x, pp.xscale * b.y, pp.xscale * b.z, pp.xscale * b.w);
+            }
+        }
     }
     uint4 raw[K];
     if constexpr (FROM_PARTS) {
@@ -151,6 +161,11 @@ __global__ void __launch_bounds__(256) rmsnorm_flat_kernel(const uint4 *__restri
                             v[0] += a[u].x; v[1] += a[u].y; v[2] += a[u].z; v[3] += a[u].w;
                             v[4] += b[u].x; v[5] += b[u].y; v[6] += b[u].z; v[7] += b[u].w;
                         }
+                }
+                if (pp.wscale) {  // the split-K reduce's order: the sum, times the scales
+                    const float4 a = sc_s[2 * (f % cpp)], b = sc_s[2 * (f % cpp) + 1];
+                    v[0] *= a.x; v[1] *= a.y; v[2] *= a.z; v[3] *= a.w;
+                    v[4] *= b.x; v[5] *= b.y; v[6] *= b.z; v[7] *= b.w;
                 }
                 if (pp.bias) {
                     float bb[8];
@@ -314,7 +329,8 @@ hipError_t dispatch(const void *x, const void *g, const void *b, void *y, long p
 hipError_t launch_rmsnorm_silu_from_partials(const ConvPartials &pp, const void *bias,
                                              const void *gamma, const void *beta, void *y,
                                              long positions, int c, float eps, int apply_silu,
-                                             hipStream_t s) {
+                                             hipStream_t s, const float *wscale, float xscale,
+                                             float out_qr) {
     if (positions <= 0) return hipSuccess;
     const int cpp = c / 8;
     if (c % 8 != 0 || cpp > FLAT_MAX_CPP || pp.S < 1) return hipErrorInvalidValue;
@@ -323,11 +339,18 @@ hipError_t launch_rmsnorm_silu_from_partials(const ConvPartials &pp, const void 
     while (R < 64 && 2 * R * P <= 256 && 2 * R <= cpp) R *= 2;
     const long blocks = (positions + P - 1) / P;
     if (blocks > 0x7fffffffL) return hipErrorInvalidValue;
-    const Partials q{pp.part, pp.stride, pp.S, static_cast<const uint4 *>(bias)};
-    hipLaunchKernelGGL((rmsnorm_flat_kernel<true, 1, false, true>), dim3((unsigned)blocks), dim3(256),
-                       0, s, nullptr, static_cast<const uint4 *>(gamma),
-                       static_cast<const uint4 *>(beta), static_cast<uint4 *>(y), positions, cpp, P,
-                       R, sqrtf((float)c), eps, apply_silu, q);
+    const Partials q{pp.part, pp.stride, pp.S, static_cast<const uint4 *>(bias),
+                     reinterpret_cast<const float4 *>(wscale), xscale};
+    if (out_qr > 0.f)  // 8-bit output: codes of fl32(y * out_qr)
+        hipLaunchKernelGGL((rmsnorm_flat_kernel<true, 1, false, true, true>), dim3((unsigned)blocks),
+                           dim3(256), 0, s, nullptr, static_cast<const uint4 *>(gamma),
+                           static_cast<const uint4 *>(beta), static_cast<uint4 *>(y), positions, cpp, P,
+                           R, sqrtf((float)c), eps, apply_silu, q, out_qr);
+    else
+        hipLaunchKernelGGL((rmsnorm_flat_kernel<true, 1, false, true>), dim3((unsigned)blocks), dim3(256),
+                           0, s, nullptr, static_cast<const uint4 *>(gamma),
+                           static_cast<const uint4 *>(beta), static_cast<uint4 *>(y), positions, cpp, P,
+                           R, sqrtf((float)c), eps, apply_silu, q);
     return hipGetLastError();
 }
 

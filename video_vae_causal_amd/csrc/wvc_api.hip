@@ -671,7 +671,115 @@ int block_back(const wvc_resblock_desc *d, const wvc_conv3d_desc &c1, const wvc_
     return conv_fwd(&c2, h2, cache2_in, cache2_out, p->w2, p->b2, shortcut, y, cws, L.conv_bytes, s);
 }
 
+// ---- the 8-bit residual block
+struct Block8Layout {
+    size_t conv_bytes, q, h, total;
+};
+
+int plan_block8(const wvc_resblock_desc *d, Block8Layout *L, wvc_conv3d_desc *c, ConvPlan *pl,
+                bool count) {
+    if (!d) return fail(WVC_ERR_ARG, "resblock descriptor is NULL");
+    if (d->dtype != WVC_BF16)
+        return fail(WVC_ERR_UNSUPPORTED, "the 8-bit block reads and writes bf16 (dtype WVC_BF16)");
+    if (d->n < 1 || d->c_in < 1 || d->c_out < 1 || d->t < 0 || d->h < 1 || d->w < 1)
+        return fail(WVC_ERR_ARG, "bad resblock shape");
+    if (d->c_in != d->c_out)
+        return fail(WVC_ERR_UNSUPPORTED, "the 8-bit block has the identity shortcut (C_in == C_out)");
+    if (!(d->eps > 0.f)) return fail(WVC_ERR_ARG, "eps must be > 0");
+    if (d->weights_packed != 0 && d->weights_packed != 1)
+        return fail(WVC_ERR_ARG, "weights_packed must be 0 or 1");
+    *c = wvc_conv3d_desc{};
+    c->n = d->n; c->c_in = d->c_in; c->c_out = d->c_out; c->t = d->t; c->h = d->h; c->w = d->w;
+    c->kt = c->kh = c->kw = 3;
+    c->stride_t = c->stride_h = c->stride_w = 1;
+    c->pad_h = c->pad_w = 1;
+    c->dil_t = c->dil_h = c->dil_w = 1;
+    c->groups = 1;
+    c->dtype = WVC_E4M3;
+    c->weight_layout = d->weights_packed ? WVC_WEIGHT_PACKED : WVC_WEIGHT_STANDARD;
+    const int rc = plan_conv(c, pl, count);
+    if (rc) return rc;
+    const size_t pos = (size_t)d->n * d->t * d->h * d->w;
+    L->conv_bytes = align256(route_ws_bytes(*pl, d->weights_packed != 0));
+    L->q = L->conv_bytes;                                  // codes of a norm output
+    L->h = L->q + align256(pos * d->c_in);                 // conv1 output, when not fused
+    L->total = L->h + align256(pos * d->c_out * 2);
+    return WVC_OK;
+}
+
 }  // namespace
+
+size_t wvc_resblock_e4m3_workspace_bytes(const wvc_resblock_desc *d) {
+    Block8Layout L;
+    wvc_conv3d_desc c;
+    ConvPlan pl;
+    if (plan_block8(d, &L, &c, &pl, false)) return (size_t)-1;
+    return L.total;
+}
+
+int wvc_resblock_e4m3_fwd(const wvc_resblock_desc *d, const void *x, void *y,
+                          const wvc_resblock_e4m3_params *p, const void *cache1_in,
+                          void *cache1_out, const void *cache2_in, void *cache2_out,
+                          void *workspace, size_t workspace_bytes, void *stream) {
+    Block8Layout L;
+    wvc_conv3d_desc c;
+    ConvPlan pl;
+    int rc = plan_block8(d, &L, &c, &pl, true);
+    if (rc) return rc;
+    if (!p) return fail(WVC_ERR_ARG, "params is NULL");
+    if (!p->gamma1 || !p->gamma2 || !p->w1 || !p->w2 || !p->w1_scale || !p->w2_scale)
+        return fail(WVC_ERR_ARG, "gamma1, gamma2, w1, w2, w1_scale and w2_scale are required");
+    if (!(p->s1 > 0.f) || !(p->s1 < INFINITY) || !(p->s2 > 0.f) || !(p->s2 < INFINITY))
+        return fail(WVC_ERR_ARG, "activation scales must be finite and > 0");
+    if (d->t > 0 && (!x || !y)) return fail(WVC_ERR_ARG, "x or y is NULL");
+    if (workspace_bytes < L.total || (!workspace && L.total))
+        return fail(WVC_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, L.total);
+    const size_t pos = (size_t)d->n * d->t * d->h * d->w;
+    const size_t plane = (size_t)d->n * 2 * d->h * d->w * d->c_in;
+    const Buf bufs[] = {
+        {x, pos * d->c_in * 2, false, "x"},
+        {y, pos * d->c_out * 2, true, "y"},
+        {cache1_in, plane, false, "cache1_in"},
+        {cache1_out, plane, true, "cache1_out"},
+        {cache2_in, plane, false, "cache2_in"},
+        {cache2_out, plane, true, "cache2_out"},
+        {workspace, workspace_bytes, true, "workspace"},
+    };
+    if ((rc = check_aliasing(bufs, 7))) return rc;
+    if (d->t == 0) {  // no frames: the caches pass through
+        wvc::ConvPartials none;
+        if ((rc = conv_fwd(&c, x, cache1_in, cache1_out, p->w1, p->b1, nullptr, nullptr, workspace,
+                           L.conv_bytes, static_cast<hipStream_t>(stream), &none, p->s1, p->w1_scale)))
+            return rc;
+        return conv_fwd(&c, x, cache2_in, cache2_out, p->w2, p->b2, nullptr, nullptr, workspace,
+                        L.conv_bytes, static_cast<hipStream_t>(stream), &none, p->s2, p->w2_scale);
+    }
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    char *ws = static_cast<char *>(workspace);
+    void *q = ws + L.q, *h = ws + L.h;
+    hipError_t err = wvc::launch_rmsnorm_silu_e4m3(x, p->gamma1, p->beta1, q, (long)pos, d->c_in,
+                                                   d->eps, 1, 1.f / p->s1, s);
+    if (err != hipSuccess) return hip_status(err, "norm launch");
+    // conv1's split-K partial sums go straight into norm2 (scales, bias, one
+    // bf16 rounding, the norm, the codes), where the vector norm applies
+    const bool fuse = d->c_out % 8 == 0 && d->c_out <= 2048 && aligned(p->gamma2, 16) &&
+                      aligned(p->beta2, 16) && aligned(p->b1, 16) && aligned(p->w1_scale, 16) &&
+                      aligned(q, 16);
+    wvc::ConvPartials parts;
+    if ((rc = conv_fwd(&c, q, cache1_in, cache1_out, p->w1, p->b1, nullptr, h, ws, L.conv_bytes, s,
+                       fuse ? &parts : nullptr, p->s1, p->w1_scale)))
+        return rc;
+    if (parts.S > 1)
+        err = wvc::launch_rmsnorm_silu_from_partials(parts, p->b1, p->gamma2, p->beta2, q, (long)pos,
+                                                     d->c_out, d->eps, 1, s, p->w1_scale, p->s1,
+                                                     1.f / p->s2);
+    else
+        err = wvc::launch_rmsnorm_silu_e4m3(h, p->gamma2, p->beta2, q, (long)pos, d->c_out, d->eps, 1,
+                                            1.f / p->s2, s);
+    if (err != hipSuccess) return hip_status(err, "norm launch");
+    return conv_fwd(&c, q, cache2_in, cache2_out, p->w2, p->b2, x, y, ws, L.conv_bytes, s, nullptr,
+                    p->s2, p->w2_scale);
+}
 
 int wvc_resblock_fwd(const wvc_resblock_desc *d, const void *x, void *y,
                      const wvc_resblock_params *p, const void *cache1_in, void *cache1_out,

@@ -137,12 +137,15 @@ hipError_t launch_rmsnorm_silu(const void *x, const void *gamma, const void *bet
                                long positions, int c, int dtype, float eps, int apply_silu,
                                hipStream_t s);
 // RMS norm + SiLU whose bf16 input is itself produced on the fly from split-K
-// partial sums: x = round_bf16(sum_s part[s] + bias), exactly what the reduce
-// kernel would store, then the norm of launch_rmsnorm_silu.  bf16 only.
+// partial sums: x = round_bf16(sum_s part[s] (* xscale * wscale[c] for an
+// 8-bit conv) + bias), exactly what the reduce kernel would store, then the
+// norm of launch_rmsnorm_silu, stored as bf16 or, with out_qr > 0, as E4M3
+// codes of fl32(y * out_qr).  bf16 only.
 hipError_t launch_rmsnorm_silu_from_partials(const ConvPartials &pp, const void *bias,
                                              const void *gamma, const void *beta, void *y,
                                              long positions, int c, float eps, int apply_silu,
-                                             hipStream_t s);
+                                             hipStream_t s, const float *wscale = nullptr,
+                                             float xscale = 1.f, float out_qr = 0.f);
 
 // RMS norm + SiLU of a bf16 tensor, stored as E4M3 codes of fl32(u * qr)
 // (qr: the reciprocal of the activation scale).

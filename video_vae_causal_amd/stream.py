@@ -233,10 +233,11 @@ class ResBlock:
 
 
 class ResBlockE4M3:
-    """The residual block on the 8-bit path (identity shortcut, C_in == C_out):
-    norm1 + SiLU stored as E4M3 codes at activation scale s1, the 8-bit conv1
-    (bf16 out), norm2 + SiLU as codes at s2, the 8-bit conv2 with the block
-    input added as its residual.  The weights are quantised once, one scale per
+    """The residual block on the 8-bit path (identity shortcut, C_in == C_out),
+    one ``wvc_resblock_e4m3_fwd`` call per chunk: norm1 + SiLU stored as E4M3
+    codes at activation scale s1, the 8-bit conv1, norm2 + SiLU as codes at s2
+    (fed straight from conv1's split-K partial sums), the 8-bit conv2 plus the
+    block input.  The weights are quantised once on the GPU, one scale per
     output channel, and packed; the caches hold codes.  The activation scales
     are the caller's calibration constants."""
 
@@ -248,10 +249,14 @@ class ResBlockE4M3:
         for k in ("w1", "w2"):
             q, sc = L.wvc_quantize_rows_e4m3(params[k])
             self.w[k] = (q, sc, L.wvc_conv3d_pack_weights(q))
+        self.q8 = {"gamma1": params["gamma1"], "beta1": params.get("beta1"),
+                   "gamma2": params["gamma2"], "beta2": params.get("beta2"),
+                   "b1": params.get("b1"), "b2": params.get("b2"),
+                   "w1": self.w["w1"][2], "w1_scale": self.w["w1"][1],
+                   "w2": self.w["w2"][2], "w2_scale": self.w["w2"][1]}
         self.c1: Optional[_PingPong] = None
         self.c2: Optional[_PingPong] = None
-        self.bufs: Dict[str, torch.Tensor] = {}
-        self.ws: Dict[str, torch.Tensor] = {}
+        self.ws: Optional[torch.Tensor] = None
 
     def start(self, n: int, h: int, w: int):
         c = self.p["w1"].shape[0]
@@ -278,29 +283,18 @@ class ResBlockE4M3:
         self.c2.materialize()
         return [self.c1.cin, self.c2.cin]
 
-    def _conv(self, name: str, q: torch.Tensor, scale: float, cache: _PingPong, y: torch.Tensor,
-              residual: Optional[torch.Tensor]):
-        wq, wsc, packed = self.w[name]
-        d = L.conv_desc(tuple(q.shape), tuple(wq.shape), L.WVC_E4M3, weight_layout=L.WVC_WEIGHT_PACKED)
-        need = L.wvc_causal_conv3d_workspace_bytes(d)
-        ws = self.ws.get(name)
-        if need and (ws is None or ws.numel() < need):
-            ws = self.ws[name] = torch.empty(need, dtype=torch.uint8, device=q.device)
-        L.wvc_causal_conv3d_e4m3_fwd(q, scale, wq, wsc, self.p["b" + name[1]], cache.cin, cache.cout,
-                                     residual, y, workspace=ws if need else None, packed_weight=packed)
-        cache.flip()
-
     def __call__(self, x: torch.Tensor, y: Optional[torch.Tensor] = None) -> torch.Tensor:
         if self.c1 is None:
             self.start(x.shape[0], x.shape[3], x.shape[4])
-        q = _cached_buf(self.bufs, "q", x.shape, x.new_empty(0, dtype=torch.uint8))
-        h = _cached_buf(self.bufs, "h", x.shape, x)
-        if y is None:
-            y = L.empty_cl(x.shape, x.dtype, x.device)
-        L.wvc_rmsnorm_silu_e4m3(x, self.p["gamma1"], self.s1, beta=self.p.get("beta1"), q=q, eps=self.eps)
-        self._conv("w1", q, self.s1, self.c1, h, None)
-        L.wvc_rmsnorm_silu_e4m3(h, self.p["gamma2"], self.s2, beta=self.p.get("beta2"), q=q, eps=self.eps)
-        self._conv("w2", q, self.s2, self.c2, y, x)
+        d = L.resblock_desc(tuple(x.shape), x.shape[1], L.WVC_BF16, self.eps, weights_packed=True)
+        need = L.wvc_resblock_e4m3_workspace_bytes(d)
+        if self.ws is None or self.ws.numel() < need:
+            self.ws = torch.empty(max(1, need), dtype=torch.uint8, device=x.device)
+        y = L.wvc_resblock_e4m3_fwd(x, self.q8, self.s1, self.s2, self.c1.cin, self.c1.cout,
+                                    self.c2.cin, self.c2.cout, y=y, eps=self.eps, workspace=self.ws,
+                                    packed=True)
+        self.c1.flip()
+        self.c2.flip()
         return y
 
 
