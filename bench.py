@@ -57,6 +57,7 @@ def parse():
     ap.add_argument("--workload", default="resblock_384_60x104",
                     choices=sorted(["resblock_384_60x104", "layer_384_240x416", "layer_96_480x832",
                                     "layer_384_240x416_e4m3", "resblock_384_60x104_e4m3",
+                                    "decoder_stack_48_30x52_e4m3",
                                     "decoder_stack_48_30x52", "downsample_96_480x832",
                                     "decoder_tiled_192x336"]))
     ap.add_argument("--tiling", choices=sorted(TILINGS), default="page",
@@ -91,8 +92,8 @@ def parse():
 
 
 PIPELINE = False  # set from --pipeline in main()
-PIPELINED = ("resblock_384_60x104", "decoder_stack_48_30x52")  # workloads that honour it
-PIPELINE_AUTO = ("decoder_stack_48_30x52",)  # where it measured faster
+PIPELINED = ("resblock_384_60x104", "decoder_stack_48_30x52", "decoder_stack_48_30x52_e4m3")
+PIPELINE_AUTO = ("decoder_stack_48_30x52", "decoder_stack_48_30x52_e4m3")  # where it measured faster
 
 
 def cl(t):
@@ -431,7 +432,7 @@ def wl_decoder():
                  + 5 * acc.conv_flops(n, 1, 2 * h, 2 * w, width, width))
     cache = L.empty_cl((n, width, 2, 2 * h, 2 * w))
     L.wvc_cache_reset(cache)
-    kx = cl(torch.randn((n, width, 1, 2 * h, 2 * w), device="cuda").to(torch.bfloat16))
+    kx = to_dev(inputs.quantize(inputs.normal((n, width, 1, 2 * h, 2 * w), 5, "kernel_x"), "bf16"))
     ky = L.empty_cl((n, width, 1, 2 * h, 2 * w))
 
     kws = conv_workspace(kx, p["w_up"], packed=True)
@@ -447,6 +448,66 @@ def wl_decoder():
                 kernel=kernel, kernel_name="igemm_kernel<3, 128, 32, 2, true, 16, false> + splitk_reduce_kernel",
                 kernel_units=acc.conv_flops(n, 1, 2 * h, 2 * w, width, width), kernel_bound="mfma",
                 kernel_bytes=acc.conv_launch_bytes(n, 1, 2 * h, 2 * w, width, width))
+    return step, info
+
+
+def wl_decoder_e4m3():
+    """The decoder stack on the 8-bit path: conv_in and conv_up quantise their
+    inputs (activation scales 6/448 and 8/448), the residual blocks are the
+    8-bit block (norm outputs at 6/448); streamed a latent frame at a time,
+    two-stream pipeline as for the bf16 stack."""
+    import torch
+    from video_vae_causal_amd import _lib as L, accounting as acc, inputs, stream
+    d = inputs.decoder_inputs(seed=5)
+    n, cl_, t, h, w = d["latent"].shape
+    width = d["p"]["w_in"].shape[0]
+    lat = to_dev(d["latent"])
+    p = {k: ({kk: to_dev(vv) for kk, vv in v.items()} if isinstance(v, dict) else to_dev(v))
+         for k, v in d["p"].items()}
+    frames = [cl(lat[:, :, i:i + 1]) for i in range(t)]
+    scales = {"in": 6.0 / 448, "up": 8.0 / 448, "rb": [(6.0 / 448, 6.0 / 448)] * 4}
+    stack = stream.DecoderStackE4M3(p, scales)
+    stack.start(n, h, w)
+    out = L.empty_cl((n, width, t, 2 * h, 2 * w))
+    outs = [out[:, :, i:i + 1] for i in range(t)]
+    pipe = stream.Pipeline(stack) if PIPELINE else None
+
+    def step():
+        stack.reset()
+        if pipe is not None:
+            pipe.run(frames, outs)
+        else:
+            for i in range(t):
+                stack.chunk(frames[i], out=outs[i])
+
+    per_frame = (acc.conv_flops(n, 1, h, w, cl_, width) + 4 * acc.conv_flops(n, 1, h, w, width, width)
+                 + 5 * acc.conv_flops(n, 1, 2 * h, 2 * w, width, width))
+    kx = L.empty_cl((n, width, 1, 2 * h, 2 * w), torch.uint8)
+    L.wvc_quantize_e4m3(to_dev(inputs.quantize(inputs.normal((n, width, 1, 2 * h, 2 * w), 5, "kernel_x"),
+                                               "bf16")), 8.0 / 448, q=kx)
+    cache = L.empty_cl((n, width, 2, 2 * h, 2 * w), torch.uint8)
+    L.wvc_cache_reset(cache)
+    ky = L.empty_cl((n, width, 1, 2 * h, 2 * w))
+    cu = stack.conv_up
+    d8 = L.conv_desc(tuple(kx.shape), tuple(cu.wq.shape), L.WVC_E4M3, weight_layout=L.WVC_WEIGHT_PACKED)
+    need = L.wvc_causal_conv3d_workspace_bytes(d8)
+    kws = torch.empty(need, dtype=torch.uint8, device="cuda") if need else None
+
+    def kernel():
+        L.wvc_causal_conv3d_e4m3_fwd(kx, 8.0 / 448, cu.wq, cu.wsc, p["b_up"], cache, None, None, ky,
+                                     workspace=kws, packed_weight=cu.packed)
+
+    info = dict(workload="decoder_stack_48_30x52_e4m3", conv_flops=per_frame * t, latent_frames=t,
+                config={"workload": "decoder_stack_48_30x52_e4m3", "latent_channels": cl_,
+                        "channels": width, "frames": t, "height": h, "width": w, "chunk_frames": 1,
+                        "batch": n, "conv_operands": "e4m3", "activation_scales": scales},
+                kernel=kernel,
+                kernel_name="igemm_kernel<3, 128, 32, 2, true, 16, true> + splitk_reduce_kernel",
+                kernel_units=acc.conv_flops(n, 1, 2 * h, 2 * w, width, width), kernel_bound="mfma",
+                kernel_peak=MFMA_FP8_PEAK_TFLOPS,
+                kernel_bytes=n * 4 * h * w * width * 3 + width * width * 27 + width * 6
+                + n * 4 * h * w * width * 2,
+                dtype="e4m3 x e4m3 -> f32 (convs); norms, upsample and activations bf16")
     return step, info
 
 
@@ -584,6 +645,7 @@ def wl_tiled():
 
 WORKLOADS = {"resblock_384_60x104": wl_resblock, "layer_384_240x416": wl_layer384,
              "layer_384_240x416_e4m3": wl_layer384_e4m3, "resblock_384_60x104_e4m3": wl_resblock_e4m3,
+             "decoder_stack_48_30x52_e4m3": wl_decoder_e4m3,
              "layer_96_480x832": wl_layer96, "decoder_stack_48_30x52": wl_decoder,
              "downsample_96_480x832": wl_downsample, "decoder_tiled_192x336": wl_tiled}
 
@@ -645,6 +707,17 @@ def cpu_baseline(workload: str):
         run = lambda: oracle.causal_conv3d_strided(oracle.norm_silu(xs, g_, bf16=True), ws_, bs_,
                                                    stride=(1, 2, 2), pad=(0, 0), pad_extra=(1, 1))
         sample = "frames 0-3 (one 4-frame chunk): norm + SiLU, then the stride-2 spatial conv"
+    elif workload == "decoder_stack_48_30x52_e4m3":
+        d = inputs.decoder_inputs(seed=5)
+        lat = d["latent"][:, :, :2].astype(np.float64)
+        p = f64_params(d["p"])
+        n, cl_, t, h, w = lat.shape
+        width = p["w_in"].shape[0]
+        flops = (acc.conv_flops(n, t, h, w, cl_, width) + 4 * acc.conv_flops(n, t, h, w, width, width)
+                 + 5 * acc.conv_flops(n, t, 2 * h, 2 * w, width, width))
+        sc = {"in": 6.0 / 448, "up": 8.0 / 448, "rb": [(6.0 / 448, 6.0 / 448)] * 4}
+        run = lambda: oracle.decoder_stack_e4m3(lat, p, sc)
+        sample = "latent frames 0-1 of 21 through the whole 8-bit stack"
     elif workload == "resblock_384_60x104_e4m3":
         r = inputs.resblock_inputs(seed=2)
         x = r["x"].astype(np.float64)

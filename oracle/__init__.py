@@ -527,6 +527,26 @@ def resblock_e4m3(x, p: dict, s1: float, s2: float, eps=DEFAULT_EPS):
     return round_bf16(causal_conv3d_e4m3(q2, s2, w2q, w2s, p.get("b2"), None, x))
 
 
+def decoder_stack_e4m3(latent, p: dict, scales: dict, eps=DEFAULT_EPS):
+    """``decoder_stack`` on the 8-bit path, over the whole sequence: conv_in and
+    conv_up read their input quantised at ``scales["in"]`` / ``scales["up"]``
+    (``quantize_e4m3``) with per-output-channel weight scales, rounded to bf16
+    where stored; the residual blocks are ``resblock_e4m3`` with
+    ``scales["rb"][k]`` = (s1, s2)."""
+    def conv8(x, w, b, s):
+        wq, ws = quantize_conv_weights_e4m3(w)
+        return round_bf16(causal_conv3d_e4m3(quantize_e4m3(x, s), s, wq, ws, b))
+
+    h = conv8(_f64(latent), p["w_in"], p.get("b_in"), scales["in"])
+    for k in (0, 1):
+        h = resblock_e4m3(h, p[f"rb{k}"], *scales["rb"][k], eps=eps)
+    h = upsample_nearest2x(h)
+    h = conv8(h, p["w_up"], p.get("b_up"), scales["up"])
+    for k in (2, 3):
+        h = resblock_e4m3(h, p[f"rb{k}"], *scales["rb"][k], eps=eps)
+    return h
+
+
 def rel_l2(y, ref) -> float:
     """||y - ref||_2 / ||ref||_2 in fp64."""
     y = np.asarray(y, dtype=np.float64)

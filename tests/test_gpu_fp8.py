@@ -345,3 +345,57 @@ def test_resblock_e4m3_empty_chunk_passes_caches():
     y = L.wvc_resblock_e4m3_fwd(x0, q, 0.01, 0.01, cin[0], cout[0], cin[1], cout[1])
     assert y.shape[2] == 0
     assert torch.equal(cout[0], cin[0]) and torch.equal(cout[1], cin[1])
+
+
+DEC8_SCALES = {"in": 6.0 / 448, "up": 8.0 / 448, "rb": [(6.0 / 448, 6.0 / 448)] * 4}
+
+
+def _dec8_case(shape=(1, 48, 3, 10, 16), width=128, seed=26):
+    d = I.decoder_inputs(seed=seed, shape=shape, width=width)
+    pd = {k: ({kk: to_dev(vv) for kk, vv in v.items()} if isinstance(v, dict) else to_dev(v))
+          for k, v in d["p"].items()}
+    p64 = {k: ({kk: f64(vv) for kk, vv in v.items()} if isinstance(v, dict) else f64(v))
+           for k, v in d["p"].items()}
+    return d["latent"], pd, p64
+
+
+def test_decoder_stack_e4m3_streamed_vs_oracle():
+    # the 8-bit decoder stack fed one latent frame at a time, against the
+    # oracle's whole-sequence 8-bit stack
+    from video_vae_causal_amd import stream
+    lat, pd, p64 = _dec8_case()
+    print(f"[case] 8-bit decoder stack {lat.shape}, width 128, per frame", flush=True)
+    stack = stream.DecoderStackE4M3(pd, DEC8_SCALES)
+    y = to_host(stack.run(to_dev(lat), chunk_frames=1))
+    ref = oracle.decoder_stack_e4m3(f64(lat), p64, DEC8_SCALES)
+    # Six quantisers in series: wherever the GPU's fp32 and the oracle's fp64
+    # land on different sides of a bf16 rounding, the next quantiser may pick
+    # the neighbouring code, a whole 8-bit step, and such flips compound.  On
+    # this case the oracle itself moves by 5.1 % (relative L2) when 1 % of its
+    # latent values move by one bf16 ulp, and its 8-bit stack lies 7.5 % from
+    # its unquantised one; the bar sits between the two.  Single layers are
+    # held to 3e-3 by the tests above.
+    rel = oracle.rel_l2(y, ref)
+    print(f"[parity] 8-bit decoder stack rel_l2={rel:.3e} (bar 6e-2)", flush=True)
+    assert rel <= 6e-2
+    ref_bf = oracle.decoder_stack(f64(lat), p64, bf16=True)
+    rel_bf = oracle.rel_l2(y, ref_bf)
+    print(f"[parity] 8-bit decoder stack vs unquantised rel_l2={rel_bf:.3e}", flush=True)
+    assert rel_bf <= 0.12
+
+
+def test_decoder_stack_e4m3_pipeline_equals_sequential_bitwise():
+    from video_vae_causal_amd import stream
+    lat, pd, _ = _dec8_case(shape=(1, 48, 4, 10, 16), seed=27)
+    print("[case] 8-bit decoder stack, two-stream pipeline vs sequential", flush=True)
+    latd = to_dev(lat)
+    frames = [latd[:, :, i:i + 1].contiguous(memory_format=torch.channels_last_3d) for i in range(4)]
+    stack = stream.DecoderStackE4M3(pd, DEC8_SCALES)
+    stack.start(1, 10, 16)
+    seq = [stack.chunk(f).clone() for f in frames]
+    stack.reset()
+    outs = [L.empty_cl((1, 128, 1, 20, 32)) for _ in range(4)]
+    stream.Pipeline(stack).run(frames, outs)
+    torch.cuda.synchronize()
+    for a, b in zip(seq, outs):
+        assert torch.equal(a, b)

@@ -161,6 +161,74 @@ def test_norm_silu_e4m3_is_scaled_norm_silu():
     assert np.array_equal(codes, oracle.e4m3_encode(v))
 
 
+def _torch_q(v, s):
+    """codes of v / s (torch's float8 cast after explicit saturation), decoded
+    back to multiples of s"""
+    t = torch.clamp(v / s, -448.0, 448.0).to(torch.float8_e4m3fn)
+    return t.double() * s
+
+
+def _torch_wq(w):
+    w = torch.from_numpy(w) if isinstance(w, np.ndarray) else w
+    sc = (w.abs().amax(dim=(1, 2, 3, 4)).float() / 448.0).double()
+    codes = (w.float() * (1.0 / sc.float())[:, None, None, None, None]).to(torch.float8_e4m3fn)
+    return codes.double() * sc[:, None, None, None, None]
+
+
+def _torch_conv(v, w, b):
+    return F.conv3d(F.pad(v, (1, 1, 1, 1, 2, 0)), w, torch.from_numpy(b))
+
+
+def _torch_block8(x, p, s1, s2):
+    c = x.shape[1]
+
+    def norm_silu(v, g):
+        u = F.normalize(v, dim=1, eps=1e-12) * np.sqrt(c) * torch.from_numpy(g)[None, :, None, None, None]
+        return F.silu(u)
+
+    h = _torch_conv(_torch_q(norm_silu(x, p["gamma1"]), s1), _torch_wq(p["w1"]), p["b1"])
+    h = h.to(torch.bfloat16).double()
+    y = _torch_conv(_torch_q(norm_silu(h, p["gamma2"]), s2), _torch_wq(p["w2"]), p["b2"]) + x
+    return y.to(torch.bfloat16).double()
+
+
+def _rand_block(rng, c):
+    p = {"gamma1": 1 + 0.05 * rng.standard_normal(c), "gamma2": 1 + 0.05 * rng.standard_normal(c),
+         "w1": rng.standard_normal((c, c, 3, 3, 3)) / np.sqrt(27 * c),
+         "w2": rng.standard_normal((c, c, 3, 3, 3)) / np.sqrt(27 * c),
+         "b1": 0.1 * rng.standard_normal(c), "b2": 0.1 * rng.standard_normal(c)}
+    return {k: torch.from_numpy(v).to(torch.bfloat16).double().numpy() for k, v in p.items()}
+
+
+def test_decoder_stack_e4m3_equals_torch_recomposition():
+    rng = np.random.default_rng(10)
+    cl, c = 8, 16
+    lat = torch.from_numpy(rng.standard_normal((1, cl, 2, 3, 4))).to(torch.bfloat16).double()
+    bf = lambda a: torch.from_numpy(a).to(torch.bfloat16).double().numpy()
+    p = {"w_in": bf(rng.standard_normal((c, cl, 3, 3, 3)) / np.sqrt(27 * cl)), "b_in": bf(0.1 * rng.standard_normal(c)),
+         "w_up": bf(rng.standard_normal((c, c, 3, 3, 3)) / np.sqrt(27 * c)), "b_up": bf(0.1 * rng.standard_normal(c))}
+    for k in range(4):
+        p[f"rb{k}"] = _rand_block(rng, c)
+    scales = {"in": 6.0 / 448, "up": 8.0 / 448, "rb": [(6.0 / 448, 5.0 / 448)] * 4}
+    y = oracle.decoder_stack_e4m3(lat.numpy(), p, scales)
+
+    def conv8(v, w, b, s):
+        # the quantiser multiplies by fl32(1/s) in fp32 (exact for bf16 inputs)
+        v32 = (v.float() * (1.0 / torch.tensor(s, dtype=torch.float32))).double()
+        q = torch.clamp(v32, -448.0, 448.0).to(torch.float8_e4m3fn).double() * s
+        return _torch_conv(q, _torch_wq(w), b).to(torch.bfloat16).double()
+
+    h = conv8(lat, p["w_in"], p["b_in"], scales["in"])
+    for k in (0, 1):
+        h = _torch_block8(h, p[f"rb{k}"], *scales["rb"][k])
+    h = F.interpolate(h, scale_factor=(1, 2, 2), mode="nearest")
+    h = conv8(h, p["w_up"], p["b_up"], scales["up"])
+    for k in (2, 3):
+        h = _torch_block8(h, p[f"rb{k}"], *scales["rb"][k])
+    assert y.shape == tuple(h.shape)
+    assert oracle.rel_l2(y, h.numpy()) < 2e-3
+
+
 def test_resblock_e4m3_equals_torch_recomposition():
     # the 8-bit block rebuilt from torch ops: F.normalize-based norm, torch's
     # float8_e4m3fn cast (after explicit saturation), torch conv3d, bf16 casts

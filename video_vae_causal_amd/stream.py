@@ -232,6 +232,59 @@ class ResBlock:
         return [lambda: self.front(x, h2), lambda: self.back(h2, x, y)]
 
 
+class CausalConv3dE4M3:
+    """A causal 3x3x3 conv on the 8-bit path whose input is not a norm output
+    (the decoder's conv_in and conv_up): the bf16 chunk is quantised at the
+    activation scale ``scale`` (``wvc_quantize_e4m3``), then the 8-bit conv
+    runs on the codes with its code cache; the output is bf16."""
+
+    def __init__(self, weight: torch.Tensor, bias: Optional[torch.Tensor], scale: float):
+        self.weight, self.bias, self.scale = weight, bias, float(scale)
+        self.wq, self.wsc = L.wvc_quantize_rows_e4m3(weight)
+        self.packed = L.wvc_conv3d_pack_weights(self.wq)
+        self.cache: Optional[_PingPong] = None
+        self.bufs: Dict[str, torch.Tensor] = {}
+        self.ws: Optional[torch.Tensor] = None
+
+    def start(self, n: int, h: int, w: int):
+        shape = (n, self.weight.shape[1], CACHE_T, h, w)
+        if self.cache is None or tuple(self.cache.buf[0].shape) != shape:
+            self.cache = _PingPong(shape, torch.uint8, self.weight.device)
+        else:
+            self.cache.reset()
+
+    def reset(self):
+        if self.cache is not None:
+            self.cache.reset()
+
+    def pingpongs(self) -> List[_PingPong]:
+        return [self.cache] if self.cache is not None else []
+
+    def caches(self) -> List[torch.Tensor]:
+        if self.cache is None:
+            return []
+        self.cache.materialize()
+        return [self.cache.cin]
+
+    def __call__(self, x: torch.Tensor, y: Optional[torch.Tensor] = None) -> torch.Tensor:
+        if self.cache is None:
+            self.start(x.shape[0], x.shape[3], x.shape[4])
+        q = _cached_buf(self.bufs, "q", x.shape, x.new_empty(0, dtype=torch.uint8))
+        L.wvc_quantize_e4m3(x, self.scale, q=q)
+        d = L.conv_desc(tuple(q.shape), tuple(self.wq.shape), L.WVC_E4M3, weight_layout=L.WVC_WEIGHT_PACKED)
+        need = L.wvc_causal_conv3d_workspace_bytes(d)
+        if need and (self.ws is None or self.ws.numel() < need):
+            self.ws = torch.empty(need, dtype=torch.uint8, device=x.device)
+        y = L.wvc_causal_conv3d_e4m3_fwd(q, self.scale, self.wq, self.wsc, self.bias, self.cache.cin,
+                                         self.cache.cout, None, y, workspace=self.ws if need else None,
+                                         packed_weight=self.packed)
+        self.cache.flip()
+        return y
+
+    def stages(self, x: torch.Tensor, y: torch.Tensor, buf) -> List[Callable[[], object]]:
+        return [lambda: self(x, y=y)]
+
+
 class ResBlockE4M3:
     """The residual block on the 8-bit path (identity shortcut, C_in == C_out),
     one ``wvc_resblock_e4m3_fwd`` call per chunk: norm1 + SiLU stored as E4M3
@@ -296,6 +349,9 @@ class ResBlockE4M3:
         self.c1.flip()
         self.c2.flip()
         return y
+
+    def stages(self, x: torch.Tensor, y: torch.Tensor, buf) -> List[Callable[[], object]]:
+        return [lambda: self(x, y=y)]
 
 
 class Stream:
@@ -398,6 +454,22 @@ class DecoderStack(Stream):
             y = self.chunk(x)
             out[:, :, t0:t1].copy_(y)
         return out
+
+
+class DecoderStackE4M3(DecoderStack):
+    """The decoder-shaped stack on the 8-bit path: conv_in and conv_up quantise
+    their bf16 inputs at the activation scales ``scales["in"]`` and
+    ``scales["up"]``; each residual block k quantises its two norm outputs at
+    ``scales["rb"][k]`` = (s1, s2).  Activations between layers stay bf16."""
+
+    # conv_in, rb0, rb1 and the upsample on one stream; the rest on the other
+    PIPELINE_SPLIT = 4
+
+    def __init__(self, p: Dict, scales: Dict, eps: float = 1e-12):
+        self.conv_in = CausalConv3dE4M3(p["w_in"], p.get("b_in"), scales["in"])
+        self.rbs = [ResBlockE4M3(p[f"rb{k}"], *scales["rb"][k], eps) for k in range(4)]
+        self.conv_up = CausalConv3dE4M3(p["w_up"], p.get("b_up"), scales["up"])
+        Stream.__init__(self, [self.conv_in] + self.rbs[:2] + [self.conv_up] + self.rbs[2:])
 
 
 def run_chunked(layer, x: torch.Tensor, sizes: Sequence[int]) -> torch.Tensor:
