@@ -794,7 +794,7 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported "
-              "(the path has no multi-GPU sharding in this build)", file=sys.stderr)
+              "(the library runs on one GPU and has no multi-GPU sharding)", file=sys.stderr)
         sys.exit(2)
     if args.pipeline == "auto":
         args.pipeline = "on" if args.workload in PIPELINE_AUTO and args.graph == "off" else "off"
