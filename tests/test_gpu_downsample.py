@@ -133,8 +133,9 @@ def test_downsample3d_chain_vs_oracle():
 def test_downsample_full_size_sampled():
     """The L0 feature map of the pages (96 ch, 17x480x832): spatial stride-2
     conv to 17x240x416, then the temporal stride-2 conv to 9x240x416;
-    sampled outputs of each against the oracle, evaluated on the inputs each
-    sampled output reads."""
+    sampled outputs of each against the oracle, evaluated only on the input
+    values each sampled output reads (the oracle computes its own
+    intermediate, rounded to bf16 where the GPU stores it)."""
     d = inputs.downsample_inputs()
     print("[case] downsample 96ch 17x480x832: generated", flush=True)
     x = to_dev(d["x"])
@@ -148,14 +149,20 @@ def test_downsample_full_size_sampled():
                                                        g.integers(0, 416, 96))]
     pts += [(0, 0, 0), (16, 239, 415), (5, 239, 0), (9, 0, 415)]
     ws, bs = f64(d["w_s"]), f64(d["b_s"])
-    spd = to_host(sp)
-    got, ref = [], []
-    for t, h, w in pts:
+
+    def oracle_spatial(t, h, w):
+        """The oracle's stride-2 conv output at (t, h, w), all channels: the
+        3x3 window at (2h, 2w) with the trailing zero row and column."""
         win = np.zeros((1, 96, 1, 3, 3))
         rows = slice(2 * h, min(2 * h + 3, 480))
         cols = slice(2 * w, min(2 * w + 3, 832))
         win[:, :, 0, :rows.stop - rows.start, :cols.stop - cols.start] = d["x"][:, :, t, rows, cols]
-        ref.append(oracle.causal_conv3d_strided(win, ws, bs, stride=(1, 1, 1), pad=(0, 0))[0, :, 0, 0, 0])
+        return oracle.causal_conv3d_strided(win, ws, bs, stride=(1, 1, 1), pad=(0, 0))[0, :, 0, 0, 0]
+
+    spd = to_host(sp)
+    got, ref = [], []
+    for t, h, w in pts:
+        ref.append(oracle_spatial(t, h, w))
         got.append(spd[0, :, t, h, w])
     check_bf16(np.stack(got, 1), np.stack(ref, 1), "spatial stride 2, full size (sampled)")
     wt_, bt = f64(d["w_t"]), f64(d["b_t"])
@@ -163,14 +170,29 @@ def test_downsample_full_size_sampled():
     got, ref = [], []
     for t, h, w in pts:
         j = t % 9
-        win = np.zeros((1, 96, 3, 1, 1))  # frames 2j-2 .. 2j of the stored bf16 intermediate
+        win = np.zeros((1, 96, 3, 1, 1))  # frames 2j-2 .. 2j of the intermediate, bf16 as stored
         for kt in range(3):
             f = 2 * j - 2 + kt
             if f >= 0:
-                win[0, :, kt, 0, 0] = spd[0, :, f, h, w]
+                win[0, :, kt, 0, 0] = oracle.round_bf16(oracle_spatial(f, h, w))
         ref.append(oracle.causal_conv3d_strided(win, wt_, bt, stride=(1, 1, 1), pad=(0, 0))[0, :, 2, 0, 0])
         got.append(yd[0, :, j, h, w])
     check_bf16(np.stack(got, 1), np.stack(ref, 1), "temporal stride 2, full size (sampled)")
+
+    # the same spatial conv with the first RMS norm + SiLU fused into it (the
+    # bench's launch configuration), on the oracle's own bf16 norm output
+    g1 = f64(d["gamma1"])
+    spn = to_host(L.wvc_rmsnorm_silu_conv3d_fwd(x, to_dev(d["gamma1"]), to_dev(d["w_s"]), to_dev(d["b_s"])))
+    got, ref = [], []
+    for t, h, w in pts[:48] + pts[-4:]:
+        win = np.zeros((1, 96, 1, 3, 3))
+        rows = slice(2 * h, min(2 * h + 3, 480))
+        cols = slice(2 * w, min(2 * w + 3, 832))
+        xin = oracle.norm_silu(f64(d["x"][:, :, t:t + 1, rows, cols]), g1, bf16=True)
+        win[:, :, :, :rows.stop - rows.start, :cols.stop - cols.start] = xin
+        ref.append(oracle.causal_conv3d_strided(win, ws, bs, stride=(1, 1, 1), pad=(0, 0))[0, :, 0, 0, 0])
+        got.append(spn[0, :, t, h, w])
+    check_bf16(np.stack(got, 1), np.stack(ref, 1), "norm + spatial stride 2 fused, full size (sampled)")
 
 
 @pytest.mark.parametrize("cin,cout,t,h,w,beta", [

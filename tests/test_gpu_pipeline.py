@@ -46,7 +46,8 @@ def block_params(cin, cout, seed, beta):
 @pytest.mark.parametrize("cin,cout,t,h,w,beta", [(64, 64, 3, 9, 13, True), (48, 96, 2, 7, 11, False),
                                                   (384, 384, 1, 60, 104, False)])
 def test_front_then_back_equals_whole_block_bitwise(cin, cout, t, h, w, beta):
-    x = to_dev(inputs.quantize(inputs.normal((1, cin, t, h, w), 41, "x"), "bf16"))
+    xh = inputs.quantize(inputs.normal((1, cin, t, h, w), 41, "x"), "bf16")
+    x = to_dev(xh)
     p = block_params_dev(block_params(cin, cout, 41, beta))
     print(f"[case] block halves {cin}->{cout} t={t} {h}x{w}", flush=True)
     c1 = [L.empty_cl((1, cin, 2, h, w)) for _ in range(2)]
@@ -64,7 +65,7 @@ def test_front_then_back_equals_whole_block_bitwise(cin, cout, t, h, w, beta):
     assert torch.equal(c1[1], c1b[1]) and torch.equal(c2[1], c2b[1])
     if h * w < 1000:
         pf = block_params_f64(block_params(cin, cout, 41, beta))
-        ref, _, _ = oracle.resblock(f64(to_host(x)), pf, bf16=True)
+        ref, _, _ = oracle.resblock(f64(xh), pf, bf16=True)
         check_bf16(to_host(y_split), ref, f"block halves {cin}->{cout}")
 
 
