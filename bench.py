@@ -88,6 +88,10 @@ def parse():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run 5 plain device copies of MIB MiB (bf16) and exit: the known-size "
                          "kernel that scales rocprofv3's FETCH_SIZE / WRITE_SIZE counters")
+    ap.add_argument("--library-gemm", default="", metavar="M,N,K",
+                    help="only time the vendor library's dense GEMM of this shape (bf16 through "
+                         "torch.matmul in both operand orders, E4M3 through torch._scaled_mm) on "
+                         "operands already laid out as matrices, print one JSON line and exit")
     return ap.parse_args()
 
 
@@ -790,6 +794,45 @@ def copy_calibration(mib: int):
                       "GBs_read_plus_write": round(4 * n / ms / 1e6, 1)}), flush=True)
 
 
+def library_gemm(spec: str):
+    """The vendor library's GEMM (hipBLASLt under torch) on the conv's contraction
+    shape, M = C_out, K = 27 * C_in, N = output positions, with both operands
+    already materialised: a reference point for the implicit-GEMM conv, which
+    builds its B operand from the halo on the fly."""
+    import torch
+    m, n, k = (int(v) for v in spec.split(","))
+    a = torch.randn(m, k, device="cuda", dtype=torch.bfloat16)
+    b = torch.randn(k, n, device="cuda", dtype=torch.bfloat16)
+    bt = torch.randn(n, k, device="cuda", dtype=torch.bfloat16)
+    c = torch.empty(m, n, device="cuda", dtype=torch.bfloat16)
+    ct = torch.empty(n, m, device="cuda", dtype=torch.bfloat16)
+
+    def timed(fn, reps=20):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        start.record()
+        for _ in range(reps):
+            fn()
+        end.record()
+        torch.cuda.synchronize()
+        return start.elapsed_time(end) / reps
+
+    flops = 2.0 * m * n * k
+    out = {"library_gemm": [m, n, k], "flops": flops}
+    for key, fn in (("bf16_w_x", lambda: torch.matmul(a, b, out=c)),
+                    ("bf16_xt_wt", lambda: torch.matmul(bt, a.t(), out=ct))):
+        ms = timed(fn)
+        out[key] = {"ms": round(ms, 4), "tflops": round(flops / ms / 1e9, 1)}
+    a8, bt8 = a.to(torch.float8_e4m3fn), bt.to(torch.float8_e4m3fn)
+    one = torch.ones((), device="cuda")
+    ms = timed(lambda: torch._scaled_mm(bt8, a8.t(), scale_a=one, scale_b=one,
+                                        out_dtype=torch.bfloat16))
+    out["e4m3_xt_wt"] = {"ms": round(ms, 4), "tflops": round(flops / ms / 1e9, 1)}
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -805,6 +848,9 @@ def main():
     import torch
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
+        return
+    if args.library_gemm:
+        library_gemm(args.library_gemm)
         return
     from video_vae_causal_amd import _lib as L
     L.load()
