@@ -167,16 +167,41 @@ __device__ __forceinline__ void static_for(F &&f) {
 
 // Compile-time geometry of a TH x TW position tile (TH * TW == 256) and its
 // halo: HC columns, HP entries per 8-channel group; each group gets NIT*64
-// slots (every staging thread writes all of its slots unconditionally) plus 4
-// entries, so that consecutive groups start 64 bytes apart in the LDS banks.
+// slots (every staging thread writes all of its slots unconditionally).
+//
+// LDS banks: gfx950's LDS has 64 four-byte banks, so a 16-byte entry e sits on
+// the bank quad e % 16, and a ds_read_b128 / ds_write_b128 is served in cycles
+// of 16 lanes whose lane numbers are distinct mod 16.  An access is therefore
+// conflict-free whenever every lane's entry is congruent to its lane number
+// mod 16 (measured: a layout breaking this runs at about half the rate).  The
+// groups are a multiple of 16 entries apart, and the staging threads and the
+// B-fragment lanes are laid out to keep that congruence (see bcol below).
 template <int KS, int TW>
 struct Geo {
     static constexpr int TH = POS_T / TW;
     static constexpr int HC = TW + KS - 1;
     static constexpr int HP = (TH + KS - 1) * HC;
     static constexpr int NIT = (HP + 63) / 64;  // staging slots per thread
-    static constexpr int HPAD = NIT * 64 + 4;
+    static constexpr int HPAD = NIT * 64;
+    static_assert(HPAD % 16 == 0, "group starts must keep the bank congruence");
 };
+
+// Row offset (dr) and column (c), inside its MFMA column tile, of the output
+// position held by B column n.  Row-major order except for 32-column tiles of
+// a 16-wide tile: their second tile row starts HC entries after the first, so
+// its columns are rotated by HC mod 16 to put column n on entry == n (mod 16).
+// Tiles 8 wide keep row-major order: no rotation can reach the congruence
+// there, and the host charges them for it.
+template <int M, int TW, int HC>
+__device__ __forceinline__ void bcol(int n, int &dr, int &c) {
+    if constexpr (M == 32 && TW == 16) {
+        dr = n >> 4;
+        c = dr ? ((n - 16 - HC) & 15) : n;
+    } else {
+        dr = n / TW;
+        c = n % TW;
+    }
+}
 
 // One workgroup = 256 threads = 4 waves laid out WAVES_CO (channels) x
 // 4/WAVES_CO (positions).  M is the MFMA tile edge (16: 16x16x32, 32: 32x32x16);
@@ -234,7 +259,11 @@ igemm_kernel(IgParams p) {
     const int wco = wave % WAVES_CO, wpos = wave / WAVES_CO;
     const int lr = lane % M;  // A row / B column of this lane inside an MFMA tile
     const int lg = lane / M;  // 8-channel group of this lane inside a K-step
-    const int g = tid & 3;    // staging: 8-channel group
+    // staging: 8-channel group g and halo position (mod 64) sp of this thread;
+    // lane l stages entry g*HPAD + sp == l (mod 16), and each wave still
+    // covers 16 positions x all 4 groups (64 contiguous bytes per position)
+    const int g = (tid >> 4) & 3;
+    const int sp = (tid & 15) + 16 * (tid >> 6);
 
     int L = xcd_remap(blockIdx.x, p.total);
     const int s = SPLIT ? L % p.S : 0;
@@ -271,14 +300,14 @@ igemm_kernel(IgParams p) {
         }
     }
 
-    // Staging: slot k of this thread is halo position (tid>>2) + 64k of
-    // group g, LDS entry lbase + 64k (slots past HP are padding).
+    // Staging: slot k of this thread is halo position sp + 64k of group g,
+    // LDS entry lbase + 64k (slots past HP are padding).
     uint32_t soff[NIT];  // byte offset of the 16-byte chunk inside a frame, or OOB
     uint32_t interior = 0;
-    const int lbase = g * HPAD + (tid >> 2);
+    const int lbase = g * HPAD + sp;
 #pragma unroll
     for (int k = 0; k < NIT; ++k) {
-        const int hp = (tid >> 2) + 64 * k;
+        const int hp = sp + 64 * k;
         const int r = hp / HC, c = hp - r * HC;
         const int hs = h0 + r - PAD, ws = w0 + c - PAD;
         const bool inframe = hp < HP && hs >= 0 && hs < p.H && ws >= 0 && ws < p.W;
@@ -288,11 +317,9 @@ igemm_kernel(IgParams p) {
     // B fragments: LDS entry of this lane's position (first MFMA column tile,
     // spatial tap (0,0), K-step 0).  Column tile j, K-step ks and tap (kh, kw)
     // add compile-time offsets.
-    const int bbase = [&] {
-        const int q = wpos * WPOS + lr;
-        const int r = q / TW, c = q - r * TW;
-        return lg * HPAD + r * HC + c;
-    }();
+    int bdr, bc;  // this lane's B column: row offset and column in its tile
+    bcol<M, TW, HC>(lr, bdr, bc);
+    const int bbase = lg * HPAD + ((wpos * WPOS) / TW + bdr) * HC + bc;
     // Weights: packed as [co tile][unit][kh][kw][M-row block][K-step][lane],
     // one 1 KiB fragment per (block, K-step); this wave's blocks start at
     // wco * FCO.  A row (unit, kh) is one contiguous run of KS fragment groups.
@@ -506,15 +533,17 @@ igemm_kernel(IgParams p) {
     }
 
     // Epilogue.  Accumulator element e of tile (i, j) is output channel
-    // co0 + i*M + (e/4)*8 + lg*4 + e%4 at position wpos*WPOS + j*M + lr.
+    // co0 + i*M + (e/4)*8 + lg*4 + e%4 at the position of B column lr in
+    // column tile j: tile row (wpos*WPOS + j*M)/TW + bdr, column
+    // (wpos*WPOS + j*M)%TW + bc.
     if (SPLIT) {
         // fp32 partial sums of this split, in the output layout; the reduce
         // kernel adds bias and residual.
         float *mine = p.part + (size_t)s * p.part_stride;
 #pragma unroll
         for (int j = 0; j < FPOS; ++j) {
-            const int q = wpos * WPOS + j * M + lr;
-            const int r = q / TW, c = q - r * TW;
+            const int q0 = wpos * WPOS + j * M;
+            const int r = q0 / TW + bdr, c = q0 % TW + bc;
             const int h = h0 + r, w = w0 + c;
             if (h >= p.H || w >= p.W) continue;
             const size_t obase = (((size_t)(n * p.T + t) * p.H + h) * p.W + w) * p.Cout;
@@ -542,8 +571,8 @@ igemm_kernel(IgParams p) {
             bb[i][e4] = bias_s[(wco * WCO + i * M + e4 * 8 + lg * 4) / 4];
 #pragma unroll
     for (int j = 0; j < FPOS; ++j) {
-        const int q = wpos * WPOS + j * M + lr;
-        const int r = q / TW, c = q - r * TW;
+        const int q0 = wpos * WPOS + j * M;
+        const int r = q0 / TW + bdr, c = q0 % TW + bc;
         const int h = h0 + r, w = w0 + c;
         const bool inside = h < p.H && w < p.W;
         const size_t obase = (((size_t)(n * p.T + t) * p.H + h) * p.W + w) * p.Cout;
@@ -558,8 +587,8 @@ igemm_kernel(IgParams p) {
     }
 #pragma unroll
     for (int j = 0; j < FPOS; ++j) {
-        const int q = wpos * WPOS + j * M + lr;
-        const int r = q / TW, c = q - r * TW;
+        const int q0 = wpos * WPOS + j * M;
+        const int r = q0 / TW + bdr, c = q0 % TW + bc;
         const int h = h0 + r, w = w0 + c;
         if (h >= p.H || w >= p.W) continue;
         const size_t obase = (((size_t)(n * p.T + t) * p.H + h) * p.W + w) * p.Cout;
