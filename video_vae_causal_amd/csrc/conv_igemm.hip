@@ -167,23 +167,32 @@ __device__ __forceinline__ void static_for(F &&f) {
 
 // Compile-time geometry of a TH x TW position tile (TH * TW == 256) and its
 // halo: HC columns, HP entries per 8-channel group; each group gets NIT*64
-// slots (every staging thread writes all of its slots unconditionally).
+// slots (every staging thread writes all of its slots unconditionally), plus
+// GAP entries.
 //
 // LDS banks: gfx950's LDS has 64 four-byte banks, so a 16-byte entry e sits on
 // the bank quad e % 16, and a ds_read_b128 / ds_write_b128 is served in cycles
 // of 16 lanes whose lane numbers are distinct mod 16.  An access is therefore
 // conflict-free whenever every lane's entry is congruent to its lane number
-// mod 16 (measured: a layout breaking this runs at about half the rate).  The
-// groups are a multiple of 16 entries apart, and the staging threads and the
-// B-fragment lanes are laid out to keep that congruence (see bcol below).
-template <int KS, int TW>
+// mod 16, up to one offset shared by the wave (measured: a layout breaking
+// this runs at about half the rate).
+//   * 32x32 tiles: a B fragment's 64 lanes are two 32-lane halves, one per
+//     k-group, which never share a cycle, so the group gap only matters to the
+//     staging stores.  These keep the 4 groups of one position on 4
+//     neighbouring lanes (one contiguous 64-byte global load per lane quad),
+//     and with the groups 2 entries past a multiple of 16 apart (GAP = 2)
+//     their stores are conflict-free as well (measured: gaps of 4 mod 16 and
+//     of 0 mod 8 conflict).
+//   * 16x16 tiles: the 4 k-groups sit on lanes 16 apart, so the groups must
+//     start a multiple of 16 entries apart (GAP = 0), and the staging threads
+//     are laid out so that their stores keep the congruence too.
+template <int KS, int TW, bool CONG>
 struct Geo {
     static constexpr int TH = POS_T / TW;
     static constexpr int HC = TW + KS - 1;
     static constexpr int HP = (TH + KS - 1) * HC;
     static constexpr int NIT = (HP + 63) / 64;  // staging slots per thread
-    static constexpr int HPAD = NIT * 64;
-    static_assert(HPAD % 16 == 0, "group starts must keep the bank congruence");
+    static constexpr int HPAD = NIT * 64 + (CONG ? 0 : 2);
 };
 
 // Row offset (dr) and column (c), inside its MFMA column tile, of the output
@@ -227,7 +236,9 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
 igemm_kernel(IgParams p) {
     static_assert(!FP8 || M == 32, "the 8-bit path uses 32x32x64 MFMAs");
     using MF = Mfma<M>;
-    using G = Geo<KS, TW>;
+    // 16x16 tiles take the bank-congruent group pitch and staging map
+    constexpr bool CONG = M == 16;
+    using G = Geo<KS, TW, CONG>;
     using acc_t = typename MF::acc_t;
     constexpr int ACC = MF::ACC;
     constexpr int PAD = KS / 2;
@@ -259,11 +270,13 @@ igemm_kernel(IgParams p) {
     const int wco = wave % WAVES_CO, wpos = wave / WAVES_CO;
     const int lr = lane % M;  // A row / B column of this lane inside an MFMA tile
     const int lg = lane / M;  // 8-channel group of this lane inside a K-step
-    // staging: 8-channel group g and halo position (mod 64) sp of this thread;
-    // lane l stages entry g*HPAD + sp == l (mod 16), and each wave still
-    // covers 16 positions x all 4 groups (64 contiguous bytes per position)
-    const int g = (tid >> 4) & 3;
-    const int sp = (tid & 15) + 16 * (tid >> 6);
+    // staging: 8-channel group g and halo position (mod 64) sp of this
+    // thread.  Either map has each wave cover 16 positions x all 4 groups (64
+    // contiguous bytes per position).  The congruent map puts lane l on entry
+    // g*HPAD + sp == l (mod 16); the other keeps a position's 4 groups on 4
+    // neighbouring lanes, which halves the 384-channel conv's L2 misses.
+    const int g = CONG ? (tid >> 4) & 3 : tid & 3;
+    const int sp = CONG ? (tid & 15) + 16 * (tid >> 6) : tid >> 2;
 
     int L = xcd_remap(blockIdx.x, p.total);
     const int s = SPLIT ? L % p.S : 0;
