@@ -37,6 +37,12 @@ def conv_case(cin, cout, t, h, w, seed, k=(3, 3, 3), dtype="bf16"):
     (32, 128, 1, 8, 8),
     (32, 32, 2, 1, 70),      # one-row frames
     (384, 384, 1, 30, 52),   # decoder low-res frame
+    # the host's tile choice (fewest ragged positions, 8-wide tiles charged 25 %)
+    # gives each MFMA shape x tile width its own LDS maps:
+    (96, 96, 2, 14, 45),     # 16x16x32 MFMA on 16-wide tiles, ragged both ways
+    (64, 64, 2, 31, 17),     # 16x16x32 MFMA on 8-wide tiles
+    (128, 128, 2, 31, 17),   # 32x32x16 MFMA on 8-wide tiles
+    (128, 128, 2, 14, 45),   # 32x32x16 MFMA on 16-wide tiles (rotated second rows)
 ])
 def test_conv3x3x3_bf16_vs_oracle(cin, cout, t, h, w):
     x, wt, b, cache = conv_case(cin, cout, t, h, w, seed=cin + cout + h)

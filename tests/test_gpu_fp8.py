@@ -167,6 +167,7 @@ def run_conv(d, packed=False, residual=True, cache=True):
     (96, 128, 2, 17, 33),    # a half-filled 64-channel unit, ragged rows and columns
     (128, 256, 1, 9, 70),    # two channel tiles, one frame
     (16, 64, 3, 11, 13),     # C_in below one unit; C_out on 32-channel tiles
+    (64, 128, 2, 31, 17),    # 8-wide position tiles
 ])
 def test_conv_e4m3_vs_oracle(cin, cout, t, h, w):
     print(f"[case] e4m3 conv cin={cin} cout={cout} t={t} h={h} w={w}", flush=True)
