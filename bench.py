@@ -88,6 +88,11 @@ def parse():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run 5 plain device copies of MIB MiB (bf16) and exit: the known-size "
                          "kernel that scales rocprofv3's FETCH_SIZE / WRITE_SIZE counters")
+    ap.add_argument("--operands", choices=("random", "zero"), default="random",
+                    help="zero: layer_384_240x416 only, with all-zero input and weights -- a diagnostic "
+                         "that keeps every instruction, address and wait of the conv and removes the "
+                         "operands' bit toggling, to separate the chip's clock response from the "
+                         "schedule; its numbers are not the metric")
     ap.add_argument("--library-gemm", default="", metavar="M,N,K",
                     help="only time the vendor library's dense GEMM of this shape (bf16 through "
                          "torch.matmul in both operand orders, E4M3 through torch._scaled_mm) on "
@@ -96,6 +101,7 @@ def parse():
 
 
 PIPELINE = False  # set from --pipeline in main()
+OPERANDS = "random"  # set from --operands in main()
 PIPELINED = ("resblock_384_60x104", "decoder_stack_48_30x52", "decoder_stack_48_30x52_e4m3")
 PIPELINE_AUTO = ("decoder_stack_48_30x52", "decoder_stack_48_30x52_e4m3")  # where it measured faster
 
@@ -286,6 +292,9 @@ def wl_layer384():
 
     ws3 = conv_workspace(x, wt, packed=True)
     ws1 = conv_workspace(y, wp, padding=(0, 0), packed=True)
+    if OPERANDS == "zero":
+        for a in (x, wt, b, wp, bp):
+            a.zero_()
     wtp = L.wvc_conv3d_pack_weights(wt)
     wpp = L.wvc_conv3d_pack_weights(wp, padding=(0, 0))
 
@@ -302,7 +311,7 @@ def wl_layer384():
     info = dict(workload="layer_384_240x416", conv_flops=f3 + f1, latent_frames=t,
                 config={"workload": "layer_384_240x416", "channels": c, "frames": t,
                         "height": h, "width": w, "chunk_frames": t, "projection_out": int(wp.shape[0]),
-                        "batch": n},
+                        "batch": n, **({"operands": "zero (diagnostic)"} if OPERANDS == "zero" else {})},
                 kernel=kernel, kernel_name="igemm_kernel<3, 128, 32, 2, false, 32, false>", kernel_units=f3,
                 kernel_bound="mfma", kernel_bytes=acc.conv_launch_bytes(n, t, h, w, c, c, cache_frames=0))
     return step, info
@@ -839,6 +848,11 @@ def main():
         print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported "
               "(the library runs on one GPU and has no multi-GPU sharding)", file=sys.stderr)
         sys.exit(2)
+    if args.operands == "zero":
+        if args.workload != "layer_384_240x416":
+            print("--operands zero is a diagnostic of the layer_384_240x416 workload only", file=sys.stderr)
+            sys.exit(2)
+        args.no_cpu_baseline = True  # the oracle's sample is random data
     if args.pipeline == "auto":
         args.pipeline = "on" if args.workload in PIPELINE_AUTO and args.graph == "off" else "off"
     if args.pipeline == "on" and args.graph == "on":
@@ -856,7 +870,8 @@ def main():
     L.load()
     torch.cuda.set_device(0)
 
-    global PIPELINE, TILING, FUSE_NORM
+    global PIPELINE, TILING, FUSE_NORM, OPERANDS
+    OPERANDS = args.operands
     PIPELINE = args.pipeline == "on"
     FUSE_NORM = args.fuse_norm == "on"
     TILING = args.tiling
@@ -901,7 +916,8 @@ def main():
         "ms_per_step": round(ms_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": info.get("dtype", "bf16"),
-        "data": "synthetic (seeded Philox normals, random-init weights)",
+        "data": ("synthetic (seeded Philox normals, random-init weights)" if args.operands == "random"
+                 else "all-zero input and weights (diagnostic, not the metric)"),
         "config": dict(info["config"], hip_graph=args.graph == "on",
                        two_stream_pipeline=PIPELINE and args.workload in PIPELINED),
         "pct_mfma_peak": round(100 * value / info.get("kernel_peak", MFMA_BF16_PEAK_TFLOPS), 2),
