@@ -18,7 +18,7 @@ from __future__ import annotations
 import ctypes
 import os
 import subprocess
-from typing import Optional, Sequence
+from typing import Optional
 
 import numpy as np
 
