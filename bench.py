@@ -408,7 +408,7 @@ def wl_layer96():
     info = dict(workload="layer_96_480x832", conv_flops=conv_flops, latent_frames=t,
                 config={"workload": "layer_96_480x832", "channels": c, "frames": t,
                         "height": h, "width": w, "chunks": sizes, "batch": n},
-                kernel=kernel, kernel_name="igemm_kernel<3, 96, 16, 2, false, 32, false>",
+                kernel=kernel, kernel_name="igemm_persist_kernel<96, 16, 2, 32, false>",
                 kernel_units=acc.conv_flops(n, 4, h, w, c, c), kernel_bound="mfma",
                 kernel_bytes=acc.conv_launch_bytes(n, 4, h, w, c, c),
                 norm_kernel=norm_kernel, norm_kernel_name="rmsnorm_flat_kernel<true, 2, true, false, false>",

@@ -43,6 +43,10 @@ def conv_case(cin, cout, t, h, w, seed, k=(3, 3, 3), dtype="bf16"):
     (64, 64, 2, 31, 17),     # 16x16x32 MFMA on 8-wide tiles
     (128, 128, 2, 31, 17),   # 32x32x16 MFMA on 8-wide tiles
     (128, 128, 2, 14, 45),   # 32x32x16 MFMA on 16-wide tiles (rotated second rows)
+    # more tiles than CUs: 16x16 tiles run persistent workgroups (several tiles
+    # each, the next tile's halo fetched during the current one)
+    (96, 192, 3, 100, 150),  # two channel tiles, ragged rows and columns
+    (64, 64, 3, 128, 200),
 ])
 def test_conv3x3x3_bf16_vs_oracle(cin, cout, t, h, w):
     x, wt, b, cache = conv_case(cin, cout, t, h, w, seed=cin + cout + h)
@@ -160,7 +164,8 @@ def test_direct_route_stride_pad_dilation(k, stride, pad, dil, dtype):
 
 @pytest.mark.parametrize("cin,cout,t,h,w", [(64, 64, 2, 11, 19),      # one launch, no split
                                              (384, 384, 1, 30, 52),   # split-K + reduce
-                                             (96, 96, 3, 5, 9)])
+                                             (96, 96, 3, 5, 9),
+                                             (96, 96, 4, 120, 160)])  # persistent workgroups
 def test_conv3x3x3_batch2_with_cache_out(cin, cout, t, h, w):
     """N = 2: both batch items through the MFMA route in one call, each with
     its own cache frames in and out."""

@@ -231,10 +231,10 @@ __device__ __forceinline__ void bcol(int n, int &dr, int &c) {
 //   during the row two rows back, and the halo written at the end of a stage
 //   during that stage's first row, so every wait covers loads at least a row
 //   old.
-template <int KS, int CO_T, int M, int WAVES_CO, bool SPLIT, int TW, bool FP8 = false>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
-igemm_kernel(IgParams p) {
+template <int KS, int CO_T, int M, int WAVES_CO, bool SPLIT, int TW, bool FP8, bool PERSIST>
+__device__ __forceinline__ void igemm_body(const IgParams &p) {
     static_assert(!FP8 || M == 32, "the 8-bit path uses 32x32x64 MFMAs");
+    static_assert(!PERSIST || (!SPLIT && KS == 3), "persistent workgroups: whole-K 3x3x3 tiles");
     using MF = Mfma<M>;
     // 16x16 tiles take the bank-congruent group pitch and staging map
     constexpr bool CONG = M == 16;
@@ -278,55 +278,99 @@ igemm_kernel(IgParams p) {
     const int g = CONG ? (tid >> 4) & 3 : tid & 3;
     const int sp = CONG ? (tid & 15) + 16 * (tid >> 6) : tid >> 2;
 
-    int L = xcd_remap(blockIdx.x, p.total);
+    // PERSIST: one workgroup per CU runs a sequence of tiles.  XCD k's
+    // workgroups share its contiguous slice of the logical tile order (the
+    // slice xcd_remap hands it), each taking every (workgroups per XCD)-th
+    // tile, so the XCD's L2 sees neighbouring tiles at any moment.
+    int Lcur, Lend = 0, Lstep = 0;
+    if constexpr (PERSIST) {
+        const int xcd = blockIdx.x & 7;
+        const int per = p.total >> 3, rem = p.total & 7;
+        const int start = xcd < rem ? xcd * (per + 1) : rem * (per + 1) + (xcd - rem) * per;
+        Lcur = start + (int)(blockIdx.x >> 3);
+        Lend = start + per + (xcd < rem ? 1 : 0);
+        Lstep = (int)(gridDim.x >> 3);
+        if (Lcur >= Lend) return;  // uniform per workgroup, before any barrier
+    } else {
+        Lcur = xcd_remap(blockIdx.x, p.total);
+    }
+    int L = Lcur;
     const int s = SPLIT ? L % p.S : 0;
     if (SPLIT) L /= p.S;
     // Order of the logical tiles: channel tile fastest (large grids: the tiles
     // of one spatial block share its halo in L2) or slowest (small grids: each
     // XCD then works on one channel tile, so its weight slice stays in L2).
-    int ct;
-    if (p.co_major) {
-        const int per_ct = (int)(p.total / p.S) / p.co_tiles;
-        ct = L / per_ct;
-        L -= ct * per_ct;
-    } else {
-        ct = L % p.co_tiles;
-        L /= p.co_tiles;
-    }
-    const int tw = L % p.tiles_w;
-    L /= p.tiles_w;
-    const int th = L % p.tiles_h;
-    L /= p.tiles_h;
-    const int t = L % p.T;
-    const int n = L / p.T;
-    const int h0 = th * G::TH, w0 = tw * TW;
-    const int co0 = ct * CO_T + wco * WCO;
+    auto decode = [&](int l, int &ct_, int &t_, int &n_, int &h0_, int &w0_) {
+        if (p.co_major) {
+            const int per_ct = (int)(p.total / p.S) / p.co_tiles;
+            ct_ = l / per_ct;
+            l -= ct_ * per_ct;
+        } else {
+            ct_ = l % p.co_tiles;
+            l /= p.co_tiles;
+        }
+        const int tw_ = l % p.tiles_w;
+        l /= p.tiles_w;
+        const int th_ = l % p.tiles_h;
+        l /= p.tiles_h;
+        t_ = l % p.T;
+        n_ = l / p.T;
+        h0_ = th_ * G::TH;
+        w0_ = tw_ * TW;
+    };
+    int ct, t, n, h0, w0;
+    decode(L, ct, t, n, h0, w0);
+    int co0 = ct * CO_T + wco * WCO;
     const int u0 = SPLIT ? (s * p.U) / p.S : 0;
     const int u1 = SPLIT ? ((s + 1) * p.U) / p.S : p.U;
-    if (!SPLIT && tid < CO_T / 4) {
-        bias_s[tid] = p.bias ? *reinterpret_cast<const uint2 *>(p.bias + ct * CO_T + tid * 4)
-                             : make_uint2(0u, 0u);
-        if constexpr (FP8) {
-            const float4 ws = *reinterpret_cast<const float4 *>(p.wscale + ct * CO_T + tid * 4);
-            scale_s[tid] = make_float4(p.xscale * ws.x, p.xscale * ws.y, p.xscale * ws.z,
-                                       p.xscale * ws.w);
+    auto load_bias = [&](int ct_) {
+        if (!SPLIT && tid < CO_T / 4) {
+            bias_s[tid] = p.bias ? *reinterpret_cast<const uint2 *>(p.bias + ct_ * CO_T + tid * 4)
+                                 : make_uint2(0u, 0u);
+            if constexpr (FP8) {
+                const float4 ws = *reinterpret_cast<const float4 *>(p.wscale + ct_ * CO_T + tid * 4);
+                scale_s[tid] = make_float4(p.xscale * ws.x, p.xscale * ws.y, p.xscale * ws.z,
+                                           p.xscale * ws.w);
+            }
         }
-    }
+    };
+    load_bias(ct);
 
     // Staging: slot k of this thread is halo position sp + 64k of group g,
     // LDS entry lbase + 64k (slots past HP are padding).
     uint32_t soff[NIT];  // byte offset of the 16-byte chunk inside a frame, or OOB
     uint32_t interior = 0;
     const int lbase = g * HPAD + sp;
+    auto stage_offsets = [&](int h0_, int w0_, uint32_t (&so)[NIT], uint32_t &inner) {
+        inner = 0;
 #pragma unroll
-    for (int k = 0; k < NIT; ++k) {
-        const int hp = sp + 64 * k;
-        const int r = hp / HC, c = hp - r * HC;
-        const int hs = h0 + r - PAD, ws = w0 + c - PAD;
-        const bool inframe = hp < HP && hs >= 0 && hs < p.H && ws >= 0 && ws < p.W;
-        soff[k] = inframe ? (uint32_t)((hs * p.W + ws) * p.Cin * ESZ + g * 16) : OOB;
-        if (inframe && r >= PAD && r < PAD + G::TH && c >= PAD && c < PAD + TW) interior |= 1u << k;
-    }
+        for (int k = 0; k < NIT; ++k) {
+            const int hp = sp + 64 * k;
+            const int r = hp / HC, c = hp - r * HC;
+            const int hs = h0_ + r - PAD, ws = w0_ + c - PAD;
+            const bool inframe = hp < HP && hs >= 0 && hs < p.H && ws >= 0 && ws < p.W;
+            so[k] = inframe ? (uint32_t)((hs * p.W + ws) * p.Cin * ESZ + g * 16) : OOB;
+            if (inframe && r >= PAD && r < PAD + G::TH && c >= PAD && c < PAD + TW) inner |= 1u << k;
+        }
+    };
+    stage_offsets(h0, w0, soff, interior);
+    // PERSIST: the workgroup's next tile, whose first halo and first two
+    // weight rows the current tile's last stage prefetches in place of the
+    // surplus loads a single tile ends with.
+    bool has_next = false;
+    int ct_n = 0, t_n = 0, n_n = 0, h0_n = 0, w0_n = 0;
+    uint32_t soff_n[NIT];
+    uint32_t interior_n = 0;
+    auto plan_next = [&]() {
+        if constexpr (PERSIST) {
+            has_next = Lcur + Lstep < Lend;
+            if (has_next) {
+                decode(Lcur + Lstep, ct_n, t_n, n_n, h0_n, w0_n);
+                stage_offsets(h0_n, w0_n, soff_n, interior_n);
+            }
+        }
+    };
+    plan_next();
     // B fragments: LDS entry of this lane's position (first MFMA column tile,
     // spatial tap (0,0), K-step 0).  Column tile j, K-step ks and tap (kh, kw)
     // add compile-time offsets.
@@ -343,7 +387,7 @@ igemm_kernel(IgParams p) {
     // Cache update: the workgroups of the chunk's last output frame write the
     // halo interiors they stage for frames T-2 and T-1, each channel tile the
     // 32-channel blocks cb with cb % co_tiles == its tile (balanced work).
-    const bool write_cache = KS == 3 && p.cache_out != nullptr && t == p.T - 1;
+    bool write_cache = KS == 3 && p.cache_out != nullptr && t == p.T - 1;
 
     acc_t acc[FCO][FPOS];
 #pragma unroll
@@ -369,10 +413,10 @@ igemm_kernel(IgParams p) {
         }
     };
 
-    auto load_row = [&](auto set_tag, int rho) {
+    auto load_row = [&](auto set_tag, int rho, int ct_) {
         constexpr int SET = decltype(set_tag)::value;
         const int u = u0 + rho / KS, kh = rho % KS;
-        const uint32_t row = (uint32_t)((((ct * p.U + u) * KS + kh) * KS) * NBLK * KSTEPS) * FRAG;
+        const uint32_t row = (uint32_t)((((ct_ * p.U + u) * KS + kh) * KS) * NBLK * KSTEPS) * FRAG;
 #pragma unroll
         for (int kw = 0; kw < KS; ++kw)
 #pragma unroll
@@ -383,12 +427,12 @@ igemm_kernel(IgParams p) {
                         bload_s(wr, wlane + (f * KSTEPS + ks) * FRAG, row + kw * NBLK * KSTEPS * FRAG));
     };
     // One A fragment of row rho (IDX = (kw*FCO + f)*KSTEPS + ks) into set SET.
-    auto load_a_one = [&](auto set_tag, auto idx_tag, int rho) {
+    auto load_a_one = [&](auto set_tag, auto idx_tag, int rho, int ct_) {
         constexpr int SET = decltype(set_tag)::value;
         constexpr int IDX = decltype(idx_tag)::value;
         constexpr int kw = IDX / (FCO * KSTEPS), f = (IDX / KSTEPS) % FCO, ks = IDX % KSTEPS;
         const int u = u0 + rho / KS, kh = rho % KS;
-        const uint32_t row = (uint32_t)((((ct * p.U + u) * KS + kh) * KS) * NBLK * KSTEPS) * FRAG;
+        const uint32_t row = (uint32_t)((((ct_ * p.U + u) * KS + kh) * KS) * NBLK * KSTEPS) * FRAG;
         put(A[SET][kw][f][FP8 ? 0 : ks], ks,
             bload_s(wr, wlane + (f * KSTEPS + ks) * FRAG, row + kw * NBLK * KSTEPS * FRAG));
     };
@@ -396,21 +440,25 @@ igemm_kernel(IgParams p) {
     __amdgpu_buffer_rsrc_t hfr = rsrc(p.x, 0u);
     uint32_t hcb2 = 0;
     bool hgok = false;
-    auto halo_setup = [&](int u) {
+    bool hnext = false;  // PERSIST: the loads being set up are the next tile's
+    auto halo_setup = [&](int u, bool nxt) {
+        const int t_ = nxt ? t_n : t, n_ = nxt ? n_n : n;
         const int kt = u % KS, cb = (u / KS) * CB;
-        const int ts = t - (KS - 1) + kt;
+        const int ts = t_ - (KS - 1) + kt;
         if (ts >= 0)
-            hfr = rsrc(xb + (size_t)(n * p.T + ts) * p.frame_bytes, p.frame_bytes);
+            hfr = rsrc(xb + (size_t)(n_ * p.T + ts) * p.frame_bytes, p.frame_bytes);
         else if (p.cache)
-            hfr = rsrc(cb_base + (size_t)(n * p.F + p.F + ts) * p.frame_bytes, p.frame_bytes);
+            hfr = rsrc(cb_base + (size_t)(n_ * p.F + p.F + ts) * p.frame_bytes, p.frame_bytes);
         else
             hfr = rsrc(p.x, 0u);  // zero causal padding: every load reads zero
         hcb2 = (uint32_t)cb * ESZ;
         hgok = cb + g * CPE < p.Cin;
+        hnext = nxt;
     };
     auto halo_one = [&](auto k_tag) {
         constexpr int k = decltype(k_tag)::value;
-        hv[k] = bload(hfr, (hgok && soff[k] != OOB) ? soff[k] + hcb2 : OOB);
+        const uint32_t so = (PERSIST && hnext) ? soff_n[k] : soff[k];
+        hv[k] = bload(hfr, (hgok && so != OOB) ? so + hcb2 : OOB);
     };
     auto load_halo = [&](int u) {
         const int kt = u % KS, cb = (u / KS) * CB;
@@ -461,7 +509,10 @@ igemm_kernel(IgParams p) {
         const uint4 *hb = &halo[buf][bbase];
         const bool last_stage = u + 1 >= u1;
         const int rnext = rho + 2 < R ? rho + 2 : R - 1;
-        if (kh == 0) halo_setup(last_stage ? u : u + 1);
+        // PERSIST: the last stage fetches the next tile's first halo (the
+        // long-latency loads) instead of re-fetching its own last stage's
+        const bool setup_next = PERSIST && last_stage && has_next;
+        if (kh == 0) halo_setup(setup_next ? 0 : (last_stage ? u : u + 1), setup_next);
         // Tap tp = kh*KS + kw of the stage reads B[tp & 1]; the next tap's set is
         // filled while this tap's MFMAs run, so no LDS read ever overwrites
         // registers an in-flight MFMA is still reading.  The global loads (the
@@ -493,7 +544,7 @@ igemm_kernel(IgParams p) {
                     static_for<NL>([&](auto li) {
                         constexpr int L_ = decltype(li)::value;
                         if constexpr ((L_ * NG) / NL == grp)
-                            load_a_one(Int<(SET + 2) % 3>{}, Int<L_>{}, rnext);
+                            load_a_one(Int<(SET + 2) % 3>{}, Int<L_>{}, rnext, ct);
                     });
                     if constexpr (kh == 0) {
                         static_for<NIT>([&](auto hk) {
@@ -522,13 +573,16 @@ igemm_kernel(IgParams p) {
     if (R <= 0) __syncthreads();  // (the prologue's barrier publishes bias_s otherwise)
     if (R > 0) {
         load_halo(u0);
-        load_row(Int<0>{}, 0);
-        load_row(Int<1>{}, R > 1 ? 1 : 0);
+        load_row(Int<0>{}, 0, ct);
+        load_row(Int<1>{}, R > 1 ? 1 : 0, ct);
         store_halo(u0, 0);
         __syncthreads();
         const uint4 *h0p = &halo[0][bbase];
 #pragma unroll
         for (int j = 0; j < FPOS; ++j) load_b(Int<0>{}, h0p, j, 0, 0);
+    }
+    for (;;) {  // one pass per tile (PERSIST), else exactly one
+    if (R > 0) {
         if (KS == 3) {
             // R is a multiple of 3: one stage per iteration, no row guards.
             for (int rho = 0; rho < R; rho += 3) {
@@ -639,6 +693,57 @@ igemm_kernel(IgParams p) {
                 *reinterpret_cast<uint2 *>(p.y + obase + co) = o;
             }
     }
+    if constexpr (!PERSIST) {
+        break;
+    } else {
+        if (!has_next) break;
+        // Next tile.  Its first halo (hv) was fetched during this tile's last
+        // stage; its first two weight rows are issued now, after the stores,
+        // where the epilogue's registers are free again.  The barrier waits
+        // for every wave to finish with the halo buffers and bias_s.
+        load_row(Int<0>{}, 0, ct_n);
+        load_row(Int<1>{}, R > 1 ? 1 : 0, ct_n);
+        __syncthreads();
+        Lcur += Lstep;
+        ct = ct_n;
+        t = t_n;
+        n = n_n;
+        h0 = h0_n;
+        w0 = w0_n;
+        co0 = ct * CO_T + wco * WCO;
+#pragma unroll
+        for (int k = 0; k < NIT; ++k) soff[k] = soff_n[k];
+        interior = interior_n;
+        write_cache = KS == 3 && p.cache_out != nullptr && t == p.T - 1;
+        load_bias(ct);
+        store_halo(u0, 0);
+        __syncthreads();
+        const uint4 *h0p = &halo[0][bbase];
+#pragma unroll
+        for (int j = 0; j < FPOS; ++j) load_b(Int<0>{}, h0p, j, 0, 0);
+#pragma unroll
+        for (int i = 0; i < FCO; ++i)
+#pragma unroll
+            for (int j = 0; j < FPOS; ++j)
+#pragma unroll
+                for (int e = 0; e < ACC; ++e) acc[i][j][e] = 0.f;
+        plan_next();
+    }
+    }  // tiles
+}
+
+// One tile per workgroup (split-K partial sums when SPLIT).
+template <int KS, int CO_T, int M, int WAVES_CO, bool SPLIT, int TW, bool FP8 = false>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+igemm_kernel(IgParams p) {
+    igemm_body<KS, CO_T, M, WAVES_CO, SPLIT, TW, FP8, false>(p);
+}
+
+// Persistent workgroups: one per CU, each through a run of whole-K tiles.
+template <int CO_T, int M, int WAVES_CO, int TW, bool FP8 = false>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+igemm_persist_kernel(IgParams p) {
+    igemm_body<3, CO_T, M, WAVES_CO, false, TW, FP8, true>(p);
 }
 
 // Split-K reduction: y = round(sum_s part[s] (in split order) + bias + residual),
@@ -879,12 +984,25 @@ size_t ws_bytes_for(const Plan &pl, const ConvCall &c, bool need_pack) {
 
 template <int KS, int CO_T, int M, int WAVES_CO, int TW, bool FP8>
 hipError_t launch_tw(const IgParams &p, hipStream_t s) {
-    if (p.S > 1)
+    // Grids with more whole-K 3x3x3 tiles than CUs run persistent: one
+    // workgroup per CU, each through a run of tiles, so that a tile's first
+    // loads overlap the previous tile's epilogue.  The tile split over XCDs
+    // needs a CU count that is a multiple of 8.
+    const int cus = num_cus();
+    if (p.S > 1) {
         hipLaunchKernelGGL((igemm_kernel<KS, CO_T, M, WAVES_CO, true, TW, FP8>), dim3(p.total),
                            dim3(256), 0, s, p);
-    else
-        hipLaunchKernelGGL((igemm_kernel<KS, CO_T, M, WAVES_CO, false, TW, FP8>), dim3(p.total),
-                           dim3(256), 0, s, p);
+        return hipGetLastError();
+    }
+    if constexpr (KS == 3 && M == 16) {
+        if (cus % 8 == 0 && p.total > cus) {
+            hipLaunchKernelGGL((igemm_persist_kernel<CO_T, M, WAVES_CO, TW, FP8>), dim3(cus),
+                               dim3(256), 0, s, p);
+            return hipGetLastError();
+        }
+    }
+    hipLaunchKernelGGL((igemm_kernel<KS, CO_T, M, WAVES_CO, false, TW, FP8>), dim3(p.total),
+                       dim3(256), 0, s, p);
     return hipGetLastError();
 }
 
