@@ -4,13 +4,18 @@ python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-
 
 A step is one pass of the whole hot path over one batch of synthetic input:
 
-  resblock_384_60x104 (default): the Wan residual block, C=384, 60x104, 5
+  layer_384_240x416 (default): causal conv 3x3x3 384->384 over
+      x[1,384,17,240,416] (whole sequence, writing the 2-frame cache a next
+      chunk would read), then the 1x1x1 384->192 projection.  The default
+      line also carries, measured in the same run: the decoder-shaped stack
+      streamed one latent frame at a time (ms per decoded latent frame), and
+      the fused RMS norm + SiLU over the 96-channel 17x480x832 map (GB/s and
+      its fraction of HBM bandwidth).
+  resblock_384_60x104: the Wan residual block, C=384, 60x104, 5
       latent frames fed one frame at a time through the 2-frame caches (caches
       reset at the start of each step): per frame RMSNorm+SiLU -> causal conv
       3x3x3 -> RMSNorm+SiLU -> causal conv 3x3x3 + residual, plus the cache
       updates.
-  layer_384_240x416: causal conv 3x3x3 384->384 over x[1,384,17,240,416]
-      (whole sequence), then the 1x1x1 384->192 projection.
   resblock_384_60x104_e4m3: the default workload on the 8-bit path: the
       norms store E4M3 codes, both convs run on codes (weights with one scale
       per output channel), outputs and residual bf16.
@@ -27,7 +32,9 @@ Prints one JSON line.  ``value`` is the conv throughput of the whole step
 TFLOP/s; ``ms_per_latent_frame`` is the step time per latent frame.  The
 ``roofline`` object covers the dominant kernel (the 3x3x3 conv, or the norm
 where stated), timed live with HIP events on the stream it runs on; the
-``cpu_baseline`` object times the fp64 CPU oracle on a bounded sample.
+``cpu_baseline`` object times the fp64 CPU oracle on a bounded sample (with
+all host threads and with one), and compares the GPU's output of the timed
+step with the oracle's on that sample (``parity``).
 Inputs are seeded synthetic tensors already resident in HBM when timing starts.
 """
 from __future__ import annotations
@@ -54,7 +61,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="resblock_384_60x104",
+    ap.add_argument("--workload", default="layer_384_240x416",
                     choices=sorted(["resblock_384_60x104", "layer_384_240x416", "layer_96_480x832",
                                     "layer_384_240x416_e4m3", "resblock_384_60x104_e4m3",
                                     "decoder_stack_48_30x52_e4m3",
@@ -75,6 +82,9 @@ def parse():
                     help="keep warming up (untimed) until this much wall time has passed "
                          "after the --warmup steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="layer_384_240x416: leave out the decoder-stack and norm measurements "
+                         "the default line carries")
     ap.add_argument("--pipeline", choices=("auto", "on", "off"), default="auto",
                     help="streamed workloads: split each frame's layers over two streams so that "
                          "the second part of frame i runs next to the first part of frame i+1 "
@@ -126,6 +136,13 @@ def conv_workspace(x, w, padding=(1, 1), packed=False):
                     weight_layout=L.WVC_WEIGHT_PACKED if packed else L.WVC_WEIGHT_STANDARD)
     need = L.wvc_causal_conv3d_workspace_bytes(d)
     return torch.empty(need, dtype=torch.uint8, device="cuda") if need else None
+
+
+def conv_kernel_name(x, w, padding=(1, 1)):
+    """The kernel the library launches for a conv of x by w (packed weights)."""
+    from video_vae_causal_amd import _lib as L
+    return L.wvc_conv3d_kernel_name(L.conv_desc(tuple(x.shape), tuple(w.shape), L.WVC_BF16,
+                                                padding=padding, weight_layout=L.WVC_WEIGHT_PACKED))
 
 
 def time_region(fn, steps, warmup, warmup_s=0.0):
@@ -211,24 +228,26 @@ def wl_resblock():
                 rb(frames[i], y=outs[i])
 
     conv_flops = 2 * t * acc.conv_flops(n, 1, h, w, c, c)
-    # dominant kernel alone: the 3x3x3 conv of one 60x104 frame (no cache update)
+    # dominant kernel alone: the 3x3x3 conv of one 60x104 frame with its cache
+    # in and out, as the block's convs run
     cache = L.empty_cl((n, c, 2, h, w))
+    cache_o = L.empty_cl((n, c, 2, h, w))
     L.wvc_cache_reset(cache)
     ky = L.empty_cl((n, c, 1, h, w))
     kws = conv_workspace(frames[0], p["w1"], packed=True)
     w1p = L.wvc_conv3d_pack_weights(p["w1"])
 
     def kernel():
-        L.wvc_causal_conv3d_fwd(frames[0], p["w1"], p["b1"], cache, None, None, ky, workspace=kws,
+        L.wvc_causal_conv3d_fwd(frames[0], p["w1"], p["b1"], cache, cache_o, None, ky, workspace=kws,
                                 packed_weight=w1p)
 
     info = dict(workload="resblock_384_60x104", conv_flops=conv_flops, latent_frames=t,
                 config={"workload": "resblock_384_60x104", "channels": c, "frames": t,
                         "height": h, "width": w, "chunk_frames": 1, "cache_frames": 2,
                         "batch": n},
-                kernel=kernel, kernel_name="igemm_kernel<3, 128, 32, 2, true, 16, false> + splitk_reduce_kernel",
+                kernel=kernel, kernel_name=conv_kernel_name(frames[0], p["w1"]),
                 kernel_units=acc.conv_flops(n, 1, h, w, c, c), kernel_bound="mfma",
-                kernel_bytes=acc.conv_launch_bytes(n, 1, h, w, c, c))
+                kernel_bytes=acc.conv_launch_bytes(n, 1, h, w, c, c, cache_out_frames=2))
     return step, info
 
 
@@ -289,6 +308,9 @@ def wl_layer384():
     wp, bp = to_dev(d["wp"]), to_dev(d["bp"])
     y = L.empty_cl((n, c, t, h, w))
     proj = L.empty_cl((n, wp.shape[0], t, h, w))
+    # the cache a following chunk would read: the last 2 input frames, written
+    # by the conv's own staging pass
+    cache_out = L.empty_cl((n, c, 2, h, w))
 
     ws3 = conv_workspace(x, wt, packed=True)
     ws1 = conv_workspace(y, wp, padding=(0, 0), packed=True)
@@ -298,22 +320,31 @@ def wl_layer384():
     wtp = L.wvc_conv3d_pack_weights(wt)
     wpp = L.wvc_conv3d_pack_weights(wp, padding=(0, 0))
 
+    def kernel():
+        L.wvc_causal_conv3d_fwd(x, wt, b, cache_out=cache_out, y=y, workspace=ws3, packed_weight=wtp)
+
     def step():
-        L.wvc_causal_conv3d_fwd(x, wt, b, y=y, workspace=ws3, packed_weight=wtp)
+        kernel()
         L.wvc_causal_conv3d_fwd(y, wp, bp, y=proj, padding=(0, 0), workspace=ws1, packed_weight=wpp)
 
     f3 = acc.conv_flops(n, t, h, w, c, c)
     f1 = acc.conv_flops(n, t, h, w, c, wp.shape[0], (1, 1, 1))
+    kname = L.wvc_conv3d_kernel_name(L.conv_desc(tuple(x.shape), tuple(wt.shape), L.WVC_BF16,
+                                                 weight_layout=L.WVC_WEIGHT_PACKED))
 
-    def kernel():
-        L.wvc_causal_conv3d_fwd(x, wt, b, y=y, workspace=ws3, packed_weight=wtp)
+    def gpu_outputs():
+        """The timed step's outputs, for the oracle comparison of the CPU leg."""
+        return {"y": y, "proj": proj}
 
     info = dict(workload="layer_384_240x416", conv_flops=f3 + f1, latent_frames=t,
                 config={"workload": "layer_384_240x416", "channels": c, "frames": t,
                         "height": h, "width": w, "chunk_frames": t, "projection_out": int(wp.shape[0]),
-                        "batch": n, **({"operands": "zero (diagnostic)"} if OPERANDS == "zero" else {})},
-                kernel=kernel, kernel_name="igemm_kernel<3, 128, 32, 2, false, 32, false>", kernel_units=f3,
-                kernel_bound="mfma", kernel_bytes=acc.conv_launch_bytes(n, t, h, w, c, c, cache_frames=0))
+                        "batch": n, "cache_out": True,
+                        **({"operands": "zero (diagnostic)"} if OPERANDS == "zero" else {})},
+                kernel=kernel, kernel_name=kname, kernel_units=f3, kernel_reps=10,
+                kernel_bound="mfma",
+                kernel_bytes=acc.conv_launch_bytes(n, t, h, w, c, c, cache_frames=0, cache_out_frames=2),
+                host=d, gpu_outputs=gpu_outputs)
     return step, info
 
 
@@ -408,7 +439,7 @@ def wl_layer96():
     info = dict(workload="layer_96_480x832", conv_flops=conv_flops, latent_frames=t,
                 config={"workload": "layer_96_480x832", "channels": c, "frames": t,
                         "height": h, "width": w, "chunks": sizes, "batch": n},
-                kernel=kernel, kernel_name="igemm_persist_kernel<96, 16, 2, 32, false>",
+                kernel=kernel, kernel_name=conv_kernel_name(hs[1], wt),
                 kernel_units=acc.conv_flops(n, 4, h, w, c, c), kernel_bound="mfma",
                 kernel_bytes=acc.conv_launch_bytes(n, 4, h, w, c, c),
                 norm_kernel=norm_kernel, norm_kernel_name="rmsnorm_flat_kernel<true, 2, true, false, false>",
@@ -444,6 +475,7 @@ def wl_decoder():
     per_frame = (acc.conv_flops(n, 1, h, w, cl_, width) + 4 * acc.conv_flops(n, 1, h, w, width, width)
                  + 5 * acc.conv_flops(n, 1, 2 * h, 2 * w, width, width))
     cache = L.empty_cl((n, width, 2, 2 * h, 2 * w))
+    cache_o = L.empty_cl((n, width, 2, 2 * h, 2 * w))
     L.wvc_cache_reset(cache)
     kx = to_dev(inputs.quantize(inputs.normal((n, width, 1, 2 * h, 2 * w), 5, "kernel_x"), "bf16"))
     ky = L.empty_cl((n, width, 1, 2 * h, 2 * w))
@@ -452,15 +484,16 @@ def wl_decoder():
     wup = L.wvc_conv3d_pack_weights(p["w_up"])
 
     def kernel():
-        L.wvc_causal_conv3d_fwd(kx, p["w_up"], p["b_up"], cache, None, None, ky, workspace=kws,
+        L.wvc_causal_conv3d_fwd(kx, p["w_up"], p["b_up"], cache, cache_o, None, ky, workspace=kws,
                                 packed_weight=wup)
 
     info = dict(workload="decoder_stack_48_30x52", conv_flops=per_frame * t, latent_frames=t,
                 config={"workload": "decoder_stack_48_30x52", "latent_channels": cl_, "channels": width,
                         "frames": t, "height": h, "width": w, "chunk_frames": 1, "batch": n},
-                kernel=kernel, kernel_name="igemm_kernel<3, 128, 32, 2, true, 16, false> + splitk_reduce_kernel",
+                kernel=kernel, kernel_name=conv_kernel_name(kx, p["w_up"]),
                 kernel_units=acc.conv_flops(n, 1, 2 * h, 2 * w, width, width), kernel_bound="mfma",
-                kernel_bytes=acc.conv_launch_bytes(n, 1, 2 * h, 2 * w, width, width))
+                kernel_bytes=acc.conv_launch_bytes(n, 1, 2 * h, 2 * w, width, width, cache_out_frames=2),
+                host=d, stack=stack, frames_dev=frames, outs=outs)
     return step, info
 
 
@@ -649,8 +682,7 @@ def wl_tiled():
                         "tiles": tiles, "decoded_latent_px_per_px": round(tiles * th * tw / (h * w), 3),
                         "chunk_frames": 1, "batch": n},
                 kernel=kernel,
-                kernel_name=("igemm_kernel<3, 128, 32, 2, true, 16, false> + splitk_reduce_kernel" if tile
-                             else "igemm_kernel<3, 128, 32, 2, *, *, false> (whole 384x672 frame)"),
+                kernel_name=conv_kernel_name(kx, p["w_up"]),
                 kernel_units=acc.conv_flops(n, 1, 2 * th, 2 * tw, width, width), kernel_bound="mfma",
                 kernel_bytes=acc.conv_launch_bytes(n, 1, 2 * th, 2 * tw, width, width))
     return step, info
@@ -661,6 +693,74 @@ WORKLOADS = {"resblock_384_60x104": wl_resblock, "layer_384_240x416": wl_layer38
              "decoder_stack_48_30x52_e4m3": wl_decoder_e4m3,
              "layer_96_480x832": wl_layer96, "decoder_stack_48_30x52": wl_decoder,
              "downsample_96_480x832": wl_downsample, "decoder_tiled_192x336": wl_tiled}
+
+
+# ---------------------------------------------------------------------------
+# Measurements the default line carries besides its own workload.
+# ---------------------------------------------------------------------------
+
+def extra_decoder(args):
+    """ms per decoded latent frame: the decoder-shaped stack (48-ch latent
+    [1,48,21,30,52] -> 384 ch, 30x52 -> 60x104) streamed one latent frame at a
+    time through its ten 2-frame caches, two-stream pipeline on; plus a
+    sequential pass with events around every frame, for frame 0 (zero
+    caches) and the steady state of frames 2-20 (both cached frames real)."""
+    import torch
+    global PIPELINE
+    saved, PIPELINE = PIPELINE, True
+    try:
+        step, info = wl_decoder()
+    finally:
+        PIPELINE = saved
+    ms, _ = time_region(step, args.steps, args.warmup, args.warmup_seconds)
+    stack, frames_dev = info["stack"], info["frames_dev"]
+    n_fr = info["latent_frames"]
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(n_fr + 1)]
+    per = []
+    for _ in range(3):
+        stack.reset()
+        ev[0].record()
+        for i in range(n_fr):
+            stack.chunk(frames_dev[i], out=info["outs"][i])
+            ev[i + 1].record()
+        torch.cuda.synchronize()
+        per.append([ev[i].elapsed_time(ev[i + 1]) for i in range(n_fr)])
+    per = np.median(np.array(per), axis=0)
+    tflops = info["conv_flops"] / (ms * 1e-3) / 1e12
+    return {"ms_per_decoded_latent_frame": round(ms / n_fr, 4),
+            "decoder_stack": {"workload": "decoder_stack_48_30x52", "latent_frames": n_fr,
+                              "ms_per_step": round(ms, 4), "conv_tflops": round(tflops, 1),
+                              "pct_mfma_peak": round(100 * tflops / MFMA_BF16_PEAK_TFLOPS, 2),
+                              "two_stream_pipeline": True,
+                              "sequential_ms_frame0": round(float(per[0]), 4),
+                              "sequential_ms_per_frame_2_to_20": round(float(per[2:].mean()), 4),
+                              "sequential_ms_per_frame": round(float(per.sum()) / n_fr, 4),
+                              "dominant_kernel": info["kernel_name"]}}
+
+
+def extra_norm96(args):
+    """The fused RMS norm + SiLU over the 96-channel encoder map
+    x[1,96,17,480,832] (bf16 in and out): its HBM roofline."""
+    from video_vae_causal_amd import _lib as L, accounting as acc, inputs
+    shape = (1, 96, 17, 480, 832)
+    x = to_dev(inputs.quantize(inputs.normal(shape, 3, "x"), "bf16"))
+    g = to_dev(inputs.norm_gamma(96, 3, "gamma", "bf16"))
+    y = L.empty_cl(shape)
+
+    def norm_kernel():
+        L.wvc_rmsnorm_silu(x, g, y=y)
+
+    n_ms, n_timing = kernel_ms(norm_kernel, 20, min(args.warmup_seconds, 0.2),
+                               args.kernel_timing == "graph")
+    nbytes = acc.norm_bytes(int(np.prod(shape)))
+    gbs = nbytes / (n_ms * 1e-3) / 1e9
+    name = "rmsnorm_flat_kernel<true, 2, true, false, false>"
+    return {"roofline_norm": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                              "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                              "traffic": measured_traffic(args.traffic_json, "layer_96_480x832/norm", name),
+                              "kernel": name, "kernel_ms": round(n_ms, 5), "timing": n_timing,
+                              "bytes_per_launch": nbytes,
+                              "workload": "rmsnorm_silu_96_480x832 (x[1,96,17,480,832] bf16)"}}
 
 
 # ---------------------------------------------------------------------------
@@ -680,10 +780,89 @@ def cpu_time_loop(run, min_s: float = 10.0):
             return dt, runs
 
 
-def cpu_baseline(workload: str):
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def omp_threads(k: int):
+    """Set the OpenMP thread count of later parallel regions started from this
+    thread (the oracle's library is built with OpenMP)."""
+    import ctypes
+    ctypes.CDLL("libgomp.so.1").omp_set_num_threads(int(k))
+
+
+def layer384_baseline(info, threads):
+    """The 384-channel layer's leg: the oracle on output frames 2-4, rows
+    0-119 of the 3x3x3 conv (its cache = input frames 0-1, so every tap is a
+    real frame), timed on all host threads; the same conv on 2 rows of one
+    frame with one thread; then the GPU's output of the timed step compared
+    with the oracle's on that sample (rows 0-118, whose 3x3 window lies inside
+    the cropped rows) and the projection of frame 2 likewise."""
+    import oracle
+    from video_vae_causal_amd import accounting as acc
+    d = info["host"]
+    rows = 120
+    w64, b64 = d["w"].astype(np.float64), d["b"].astype(np.float64)
+    xs = d["x"][:, :, 2:5, :rows].astype(np.float64)
+    past = d["x"][:, :, 0:2, :rows].astype(np.float64)
+    n, c, f, h, w = xs.shape
+    flops = acc.conv_flops(n, f, h, w, c, c)
+    out = {}
+    run = lambda: out.__setitem__("y", oracle.causal_conv3d(xs, w64, b64, cache=past))
+    dt, runs = cpu_time_loop(run)
+    res = {"value": flops * runs / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+           "cpu_model": cpu_model(),
+           "sample": f"3x3x3 conv output frames 2-4 x rows 0-{rows - 1} x 416 x 384 channels "
+                     f"(cache = input frames 0-1), run {runs}x",
+           "seconds": round(dt, 3), "flops": flops * runs}
+    # one thread, a smaller sample of the same conv: frame 2, rows 0-1
+    x1, p1 = xs[:, :, 0:1, :2], past[:, :, :, :2]
+    f1 = acc.conv_flops(n, 1, 2, w, c, c)
+    omp_threads(1)
+    try:
+        dt1, runs1 = cpu_time_loop(lambda: oracle.causal_conv3d(x1, w64, b64, cache=p1), min_s=5.0)
+    finally:
+        omp_threads(threads)
+    res["single_thread"] = {"value": f1 * runs1 / dt1 / 1e12, "unit": "TFLOP/s", "cores": 1,
+                            "sample": f"conv output frame 2, rows 0-1 x 416 x 384 channels, run {runs1}x",
+                            "seconds": round(dt1, 3), "flops": f1 * runs1}
+    # parity of the benched run on the sample
+    g = info["gpu_outputs"]()
+    ref = out["y"][:, :, :, :rows - 1]
+    got = g["y"][:, :, 2:5, :rows - 1].float().cpu().numpy().astype(np.float64)
+    parity = {"conv": parity_entry(got, ref, "bf16 conv vs fp64 oracle, frames 2-4, rows 0-118, all "
+                                             "416 columns and 384 channels")}
+    conv_b = oracle.round_bf16(ref[:, :, 0:1])          # the conv output as stored (bf16)
+    pref = oracle.causal_conv3d(conv_b, d["wp"].astype(np.float64), d["bp"].astype(np.float64), pad=(0, 0))
+    pgot = g["proj"][:, :, 2:3, :rows - 1].float().cpu().numpy().astype(np.float64)
+    parity["projection"] = parity_entry(pgot, pref, "1x1x1 384->192 of the bf16 conv output, frame 2, "
+                                                    "rows 0-118 (oracle fed the oracle's rounded conv)")
+    res["parity"] = parity
+    return res
+
+
+def parity_entry(got, ref, what):
+    import oracle
+    rel = oracle.rel_l2(got, ref)
+    mx = oracle.max_abs(got, ref)
+    bound = 2e-2 * float(np.max(np.abs(ref)))
+    return {"compared": int(ref.size), "rel_l2": float(f"{rel:.4g}"), "max_abs": float(f"{mx:.4g}"),
+            "max_abs_bound": float(f"{bound:.4g}"), "rel_l2_bound": 1e-2,
+            "pass": bool(rel <= 1e-2 and mx <= bound), "what": what}
+
+
+def cpu_baseline(workload: str, info=None):
     import oracle
     from video_vae_causal_amd import accounting as acc, inputs
     threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    if workload == "layer_384_240x416" and info is not None and "host" in info:
+        return layer384_baseline(info, threads)
 
     def f64_params(p):
         return {k: ({kk: vv.astype(np.float64) for kk, vv in v.items()} if isinstance(v, dict)
@@ -760,6 +939,7 @@ def cpu_baseline(workload: str):
         sample = f"frames 0-{frames - 1}, rows 0-{rows - 1} of the 3x3x3 conv"
     dt, runs = cpu_time_loop(run)
     return {"value": flops * runs / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "cpu_model": cpu_model(),
             "sample": sample + f", run {runs}x", "seconds": round(dt, 3), "flops": flops * runs}
 
 
@@ -891,8 +1071,8 @@ def main():
     value = info["conv_flops"] / (ms_step * 1e-3) / 1e12
 
     # dominant kernel, timed alone with events on the stream it is launched on
-    k_ms, k_timing = kernel_ms(info["kernel"], args.kernel_reps, min(args.warmup_seconds, 0.2),
-                               args.kernel_timing == "graph")
+    k_ms, k_timing = kernel_ms(info["kernel"], info.get("kernel_reps", args.kernel_reps),
+                               min(args.warmup_seconds, 0.2), args.kernel_timing == "graph")
     traffic = measured_traffic(args.traffic_json, args.workload, info["kernel_name"])
     if info["kernel_bound"] == "hbm":
         achieved = info["kernel_bytes"] / (k_ms * 1e-3) / 1e9
@@ -937,8 +1117,15 @@ def main():
                                  "kernel": info["norm_kernel_name"],
                                  "kernel_ms": round(n_ms, 5), "timing": n_timing,
                                  "bytes_per_launch": info["norm_bytes"]}
+    if args.workload == "layer_384_240x416" and not args.no_extras and args.operands == "random":
+        line.update(extra_decoder(args))
+        line.update(extra_norm96(args))
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(args.workload)
+        cb = cpu_baseline(args.workload, info)
+        parity = cb.pop("parity", None)
+        line["cpu_baseline"] = cb
+        if parity is not None:
+            line["parity"] = parity
     print(json.dumps(line), flush=True)
 
 

@@ -50,7 +50,9 @@ extern "C" {
 enum {
     WVC_OK = 0,
     WVC_ERR_ARG = 1,         /* null / negative / inconsistent argument        */
-    WVC_ERR_UNSUPPORTED = 2, /* temporal stride != 1, groups != 1, bad dtype   */
+    WVC_ERR_UNSUPPORTED = 2, /* groups != 1, a dtype no route covers, an E4M3 or
+                                fused call outside its one route, packed weights
+                                for the direct route                          */
     WVC_ERR_ALIAS = 3,       /* a written buffer overlaps another buffer       */
     WVC_ERR_WORKSPACE = 4,   /* workspace missing or too small                 */
     WVC_ERR_STRICT = 5,      /* strict mode on and the call needs the generic route */
@@ -173,6 +175,15 @@ size_t wvc_conv3d_packed_weight_bytes(const wvc_conv3d_desc *d);
 int wvc_conv3d_pack_weights(const wvc_conv3d_desc *d, const void *weight, void *packed,
                             void *stream);
 
+/* Name of the kernel a wvc_causal_conv3d_fwd call with this descriptor
+ * launches on the current device (with its template arguments, as profilers
+ * print it; a split-K plan names its reduce kernel too), for profiling and
+ * tests ([P3]: the counters show which route a call took; this names the
+ * variant inside the route).  The aligned-tensor case is assumed.  "" for an
+ * invalid descriptor.  The text lives in a thread-local buffer, valid until
+ * the thread's next call of this function. */
+const char *wvc_conv3d_kernel_name(const wvc_conv3d_desc *d);
+
 /* Past frames F a causal conv keeps: dil_t * (kT - 1) ([P1] 10.3, the causal
  * pad tuple puts all temporal padding before frame 0).  -1 if d is invalid. */
 int wvc_conv3d_cache_frames(const wvc_conv3d_desc *d);
@@ -255,8 +266,11 @@ int wvc_resblock_back(const wvc_resblock_desc *d, const void *h2, const void *x,
 
 /*
  * Zero-fills `bytes` bytes of a cache (a fill kernel, never a memset node, so
- * it can be recorded in a graph).  A zeroed cache is exactly the zero causal
- * padding before frame 0, so this restarts a stream.  bytes % 4 == 0.
+ * it can be recorded in a graph).  [P1] 10.3 pads the temporal axis with zeros
+ * before frame 0 only (the causal pad tuple), and 8.5 concatenates the cached
+ * past frames in front of each chunk; a zeroed cache therefore reproduces
+ * that zero padding exactly, so this restarts a stream.  bytes % 4 == 0;
+ * WVC_ERR_ARG for a NULL cache with bytes > 0 or a misaligned pointer/size.
  */
 int wvc_cache_reset(void *cache, size_t bytes, void *stream);
 
@@ -304,9 +318,6 @@ int wvc_tile_blend(const void *tile, float *acc, float *wsum, int n, int c, int 
 int wvc_tile_blend_finish(const float *acc, const float *wsum, void *y, int n, int c, int t, int h,
                           int w, int dtype, void *stream);
 
-/* Strict mode ([P3]: a strict mode stops on an unexpected fallback): when on,
- * a call that would take the generic route fails with WVC_ERR_STRICT.
- * Initialised from the environment variable WVC_STRICT (=1 turns it on). */
 /*
  * Fused RMS norm + SiLU and the encoder's stride-2 spatial conv ([P1] 10.5:
  * the norm + SiLU before the per-frame zero pad and 3x3 stride-2 conv; 10.2
@@ -419,6 +430,9 @@ int wvc_resblock_e4m3_fwd(const wvc_resblock_desc *d, const void *x, void *y,
                           void *workspace, size_t workspace_bytes, void *stream);
 size_t wvc_resblock_e4m3_workspace_bytes(const wvc_resblock_desc *d);
 
+/* Strict mode ([P3]: a strict mode stops on an unexpected fallback): when on,
+ * a call that would take the generic route fails with WVC_ERR_STRICT.
+ * Initialised from the environment variable WVC_STRICT (=1 turns it on). */
 void wvc_set_strict(int on);
 int wvc_get_strict(void);
 

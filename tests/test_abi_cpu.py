@@ -409,3 +409,103 @@ def test_resblock_e4m3_validation(lib):
     assert call(params(), y=X) == L.WVC_ERR_ALIAS
     assert lib.wvc_resblock_e4m3_fwd(ctypes.byref(rd), X, Y, None, None, None, None, None, WS, need,
                                      None) == L.WVC_ERR_ARG
+
+
+# ---------------------------------------------------------------------------
+# Binding-side size checks.  The C ABI sizes every buffer from the descriptor
+# it builds from x and the weight, so a buffer of another size must be refused
+# by the binding before any launch.  Here the binding's device check points at
+# the CPU, so host tensors stand in for device ones; every call below must
+# raise before reaching the stream query (which would need a GPU).
+# ---------------------------------------------------------------------------
+
+@pytest.fixture
+def host_binding(lib, monkeypatch):
+    import torch
+    monkeypatch.setattr(L, "DEVICE_TYPE", "cpu")
+
+    def no_launch(*a, **k):
+        raise AssertionError("reached a launch: the mismatch was not caught by the binding")
+    monkeypatch.setattr(L, "_stream", no_launch)
+    return torch
+
+
+def cl_host(torch, shape, dtype=None):
+    return torch.zeros(shape, dtype=dtype or torch.bfloat16).contiguous(
+        memory_format=torch.channels_last_3d)
+
+
+def test_conv_binding_refuses_mismatched_buffers(host_binding):
+    torch = host_binding
+    x = cl_host(torch, (1, 16, 2, 8, 12))
+    w = cl_host(torch, (32, 16, 3, 3, 3))
+    b = torch.zeros(32, dtype=torch.bfloat16)
+    cache = cl_host(torch, (1, 16, 2, 8, 12))
+    y = cl_host(torch, (1, 32, 2, 8, 12))
+    bad = [
+        dict(cache_in=cl_host(torch, (1, 16, 2, 4, 12))),          # cache of another resolution
+        dict(cache_out=cl_host(torch, (1, 16, 1, 8, 12))),         # one cache frame
+        dict(cache_in=cl_host(torch, (1, 16, 2, 8, 12), torch.float32)),  # other dtype
+        dict(y=cl_host(torch, (1, 32, 1, 8, 12))),                 # fewer frames
+        dict(y=cl_host(torch, (1, 16, 2, 8, 12))),                 # C_in instead of C_out
+        dict(residual=cl_host(torch, (1, 32, 2, 8, 11))),
+        dict(bias=torch.zeros(16, dtype=torch.bfloat16)),
+        dict(packed_weight=torch.zeros(100, dtype=torch.uint8)),   # wrong packed size
+    ]
+    for kw in bad:
+        args = dict(bias=b, cache_in=cache, cache_out=cl_host(torch, (1, 16, 2, 8, 12)), y=y)
+        args.update(kw)
+        with pytest.raises((ValueError, TypeError)):
+            L.wvc_causal_conv3d_fwd(x, w, **args)
+    with pytest.raises((ValueError, TypeError)):   # weight C_in != x's channels
+        L.wvc_causal_conv3d_fwd(x, cl_host(torch, (32, 8, 3, 3, 3)), y=y)
+    # a well-formed call passes every check and stops at the (stubbed) launch
+    with pytest.raises(AssertionError, match="reached a launch"):
+        L.wvc_causal_conv3d_fwd(x, w, b, cache, cl_host(torch, (1, 16, 2, 8, 12)), y=y)
+
+
+def test_block_binding_refuses_mismatched_buffers(host_binding):
+    torch = host_binding
+    c = 32
+    x = cl_host(torch, (1, c, 1, 6, 10))
+    vec = lambda n: torch.zeros(n, dtype=torch.bfloat16)
+    p = {"gamma1": vec(c), "w1": cl_host(torch, (c, c, 3, 3, 3)), "b1": vec(c), "gamma2": vec(c),
+         "w2": cl_host(torch, (c, c, 3, 3, 3)), "b2": vec(c)}
+    good = lambda: cl_host(torch, (1, c, 2, 6, 10))
+    for kw in (dict(cache1_in=cl_host(torch, (1, c, 2, 3, 10))),
+               dict(cache2_out=cl_host(torch, (1, c, 2, 6, 5))),
+               dict(y=cl_host(torch, (1, c, 2, 6, 10)))):
+        args = dict(cache1_in=good(), cache1_out=good(), cache2_in=good(), cache2_out=good())
+        args.update(kw)
+        with pytest.raises((ValueError, TypeError)):
+            L.wvc_resblock_fwd(x, p, **args)
+    with pytest.raises((ValueError, TypeError)):
+        L.wvc_resblock_fwd(x, dict(p, gamma2=vec(c - 8)))
+    with pytest.raises((ValueError, TypeError)):
+        L.wvc_resblock_fwd(x, p, packed={"w1": torch.zeros(64, dtype=torch.uint8),
+                                         "w2": torch.zeros(64, dtype=torch.uint8)})
+    with pytest.raises((ValueError, TypeError)):
+        L.wvc_resblock_front(x, p, h2=cl_host(torch, (1, c, 1, 6, 9)))
+    with pytest.raises((ValueError, TypeError)):
+        L.wvc_resblock_back(x, x, p, cache2_in=cl_host(torch, (1, c, 2, 6, 9)))
+
+
+def test_norm_upsample_e4m3_bindings_refuse_mismatched_buffers(host_binding):
+    torch = host_binding
+    x = cl_host(torch, (1, 32, 2, 6, 10))
+    g = torch.zeros(32, dtype=torch.bfloat16)
+    with pytest.raises((ValueError, TypeError)):
+        L.wvc_rmsnorm_silu(x, g, y=cl_host(torch, (1, 32, 1, 6, 10)))
+    with pytest.raises((ValueError, TypeError)):
+        L.wvc_rmsnorm_silu(x, torch.zeros(16, dtype=torch.bfloat16))
+    with pytest.raises((ValueError, TypeError)):
+        L.wvc_rmsnorm_silu_e4m3(x, g, 0.1, q=cl_host(torch, (1, 32, 2, 6, 10)))  # bf16, not codes
+    with pytest.raises((ValueError, TypeError)):
+        L.wvc_upsample_nearest2x(x, y=cl_host(torch, (1, 32, 2, 12, 10)))
+    q = cl_host(torch, (1, 32, 2, 6, 10), torch.uint8)
+    wq = cl_host(torch, (32, 32, 3, 3, 3), torch.uint8)
+    ws = torch.ones(32)
+    with pytest.raises((ValueError, TypeError)):
+        L.wvc_causal_conv3d_e4m3_fwd(q, 0.1, wq, ws, cache_in=cl_host(torch, (1, 32, 2, 6, 5), torch.uint8))
+    with pytest.raises((ValueError, TypeError)):
+        L.wvc_causal_conv3d_e4m3_fwd(q, 0.1, wq, ws, y=cl_host(torch, (1, 32, 2, 6, 10), torch.uint8))

@@ -44,3 +44,17 @@ def test_workload_flops():
     assert acc.conv_flops(1, 17, 240, 416, 384, 384) == 13_514_802_462_720
     assert acc.conv_flops(1, 1, 60, 104, 384, 384) == 49_686_773_760
     assert acc.conv_flops(1, 17, 480, 832, 96, 96) == 3_378_700_615_680
+
+
+def test_conv_launch_bytes():
+    # 384-channel 60x104 frame with its 2 cached frames: 3 input frames, the
+    # 384x384x27 weights and bias, 1 output frame, 2 cache-out frames
+    plane = 60 * 104 * 384 * 2
+    wb = 384 * 384 * 27 * 2 + 384 * 2
+    assert acc.conv_launch_bytes(1, 1, 60, 104, 384, 384) == 3 * plane + wb + plane
+    assert acc.conv_launch_bytes(1, 1, 60, 104, 384, 384, cache_out_frames=2) == 5 * plane + wb + plane
+    assert acc.conv_launch_bytes(1, 1, 60, 104, 384, 384, residual=True) == 3 * plane + wb + 2 * plane
+    # the whole 17-frame sequence from zero padding: no cache read
+    p4 = 240 * 416 * 384 * 2
+    assert acc.conv_launch_bytes(1, 17, 240, 416, 384, 384, cache_frames=0, cache_out_frames=2) == \
+        17 * p4 + wb + 17 * p4 + 2 * p4

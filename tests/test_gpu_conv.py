@@ -43,10 +43,6 @@ def conv_case(cin, cout, t, h, w, seed, k=(3, 3, 3), dtype="bf16"):
     (64, 64, 2, 31, 17),     # 16x16x32 MFMA on 8-wide tiles
     (128, 128, 2, 31, 17),   # 32x32x16 MFMA on 8-wide tiles
     (128, 128, 2, 14, 45),   # 32x32x16 MFMA on 16-wide tiles (rotated second rows)
-    # more tiles than CUs: 16x16 tiles run persistent workgroups (several tiles
-    # each, the next tile's halo fetched during the current one)
-    (96, 192, 3, 100, 150),  # two channel tiles, ragged rows and columns
-    (64, 64, 3, 128, 200),
 ])
 def test_conv3x3x3_bf16_vs_oracle(cin, cout, t, h, w):
     x, wt, b, cache = conv_case(cin, cout, t, h, w, seed=cin + cout + h)
@@ -56,6 +52,27 @@ def test_conv3x3x3_bf16_vs_oracle(cin, cout, t, h, w):
     ref = oracle.causal_conv3d(f64(x), f64(wt), f64(b), cache=f64(cache))
     check_bf16(to_host(y), ref, f"conv3 {cin}->{cout} {h}x{w}")
     assert L.wvc_get_counters()["fast_3x3x3"] == 1
+
+
+@pytest.mark.parametrize("cin,cout,t,h,w,tw", [
+    (96, 192, 3, 100, 150, 32),  # two channel tiles, ragged rows and columns
+    (64, 64, 4, 128, 200, 16),
+    (96, 96, 8, 2048, 8, 8),     # 8-wide tiles (one per row band), 512 tiles
+    (64, 64, 8, 2048, 8, 8),
+])
+def test_conv3x3x3_persistent_workgroups_vs_oracle(cin, cout, t, h, w, tw):
+    """Grids of 16x16 MFMA tiles with more tiles than CUs and no split of K run
+    persistent workgroups (several tiles each, the next tile's halo fetched
+    during the current one).  The library names the kernel it launches; the
+    case must reach the persistent kernel at the expected tile width."""
+    x, wt, b, cache = conv_case(cin, cout, t, h, w, seed=cin + cout + h + 1)
+    d = L.conv_desc(x.shape, wt.shape, L.WVC_BF16)
+    name = L.wvc_conv3d_kernel_name(d)
+    print(f"[case] conv3 persistent cin={cin} cout={cout} t={t} {h}x{w}: {name}", flush=True)
+    assert name.startswith("igemm_persist_kernel<") and name.endswith(f", 16, 2, {tw}, false>"), name
+    y = L.wvc_causal_conv3d_fwd(to_dev(x), to_dev(wt), to_dev(b), cache_in=to_dev(cache))
+    ref = oracle.causal_conv3d(f64(x), f64(wt), f64(b), cache=f64(cache))
+    check_bf16(to_host(y), ref, f"conv3 persistent {cin}->{cout} {h}x{w}")
 
 
 def test_split_k_workspace_reused_across_shapes():

@@ -39,7 +39,7 @@ EXPORTED = (
     "wvc_tile_extract", "wvc_tile_blend", "wvc_tile_blend_finish",
     "wvc_causal_conv3d_e4m3_fwd", "wvc_quantize_e4m3", "wvc_quantize_rows_e4m3",
     "wvc_rmsnorm_silu_e4m3", "wvc_rmsnorm_silu_conv3d_fwd", "wvc_resblock_e4m3_fwd",
-    "wvc_resblock_e4m3_workspace_bytes",
+    "wvc_resblock_e4m3_workspace_bytes", "wvc_conv3d_kernel_name",
 )
 
 
@@ -79,6 +79,13 @@ class WvcError(RuntimeError):
 
 
 _lib = None
+# Device type every tensor argument must live on (the library takes device
+# pointers only).
+DEVICE_TYPE = "cuda"
+
+
+def _on_device(t: torch.Tensor) -> bool:
+    return t.device.type == DEVICE_TYPE
 
 
 def load(path: str = LIB_PATH) -> ctypes.CDLL:
@@ -96,6 +103,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.wvc_causal_conv3d_fwd.restype = i
     lib.wvc_causal_conv3d_workspace_bytes.argtypes = [dptr]
     lib.wvc_causal_conv3d_workspace_bytes.restype = sz
+    lib.wvc_conv3d_kernel_name.argtypes = [dptr]
+    lib.wvc_conv3d_kernel_name.restype = ctypes.c_char_p
     lib.wvc_conv3d_cache_frames.argtypes = [dptr]
     lib.wvc_conv3d_cache_frames.restype = i
     lib.wvc_conv3d_packed_weight_bytes.argtypes = [dptr]
@@ -192,7 +201,7 @@ def _dtype_code(dt: torch.dtype) -> int:
 def _need_cl(t: Optional[torch.Tensor], name: str, ndim: int = 5):
     if t is None:
         return
-    if not t.is_cuda:
+    if not _on_device(t):
         raise ValueError(f"{name} must be a device tensor")
     if t.dim() != ndim:
         raise ValueError(f"{name} must have {ndim} dims, got {tuple(t.shape)}")
@@ -203,8 +212,38 @@ def _need_cl(t: Optional[torch.Tensor], name: str, ndim: int = 5):
 def _need_vec(t: Optional[torch.Tensor], name: str, c: int):
     if t is None:
         return
-    if not t.is_cuda or t.dim() != 1 or t.shape[0] != c or not t.is_contiguous():
+    if not _on_device(t) or t.dim() != 1 or t.shape[0] != c or not t.is_contiguous():
         raise ValueError(f"{name} must be a contiguous device vector of {c} elements")
+
+
+def _need_exact(t: Optional[torch.Tensor], name: str, shape, dtype: torch.dtype,
+                device: torch.device):
+    """A buffer the library reads or writes at a size derived from other
+    arguments: it must have exactly that shape, dtype and device (the C ABI
+    gets a bare pointer and trusts the size), channels-last when 5-d."""
+    if t is None:
+        return
+    shape = tuple(int(v) for v in shape)
+    if tuple(t.shape) != shape:
+        raise ValueError(f"{name} must have shape {shape}, got {tuple(t.shape)}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.device != device:
+        raise ValueError(f"{name} must be on {device}, got {t.device}")
+    _need_cl(t, name, len(shape))
+    if len(shape) == 1 and not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _need_bytes(t: Optional[torch.Tensor], name: str, nbytes: int, device: torch.device):
+    """A flat buffer (packed weights) of exactly ``nbytes`` bytes on ``device``."""
+    if t is None:
+        return
+    if not _on_device(t) or t.device != device or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous tensor on {device}")
+    got = t.numel() * t.element_size()
+    if got != nbytes:
+        raise ValueError(f"{name} holds {got} bytes, {nbytes} expected")
 
 
 def empty_cl(shape: Sequence[int], dtype=torch.bfloat16, device="cuda") -> torch.Tensor:
@@ -248,6 +287,11 @@ def conv_out_frames(t: int, stride_t: int = 1, t_phase: int = 0) -> int:
 def wvc_conv3d_cache_frames(weight_shape, dilation=(1, 1, 1)) -> int:
     d = conv_desc((1, weight_shape[1], 1, 1, 1), weight_shape, WVC_BF16, dilation=dilation)
     return load().wvc_conv3d_cache_frames(ctypes.byref(d))
+
+
+def wvc_conv3d_kernel_name(d: ConvDesc) -> str:
+    """The kernel a conv call with descriptor ``d`` launches on this device."""
+    return load().wvc_conv3d_kernel_name(ctypes.byref(d)).decode()
 
 
 def wvc_causal_conv3d_workspace_bytes(d: ConvDesc) -> int:
@@ -305,24 +349,33 @@ def wvc_causal_conv3d_fwd(x: torch.Tensor, weight: torch.Tensor, bias: Optional[
     lib = load()
     _need_cl(x, "x")
     _need_cl(weight, "weight")
-    for name, t in (("cache_in", cache_in), ("cache_out", cache_out), ("residual", residual),
-                    ("y", y)):
-        _need_cl(t, name)
-    _need_vec(bias, "bias", weight.shape[0])
     code = _dtype_code(x.dtype)
+    n, c, t, h, w = x.shape
+    _need_exact(weight, "weight", (weight.shape[0], c) + tuple(weight.shape[2:]), x.dtype, x.device)
+    _need_exact(bias, "bias", (weight.shape[0],), x.dtype, x.device)
+    ho, wo = conv_out_hw(h, w, weight.shape[2:], stride, padding, dilation, pad_extra)
+    if ho < 1 or wo < 1:
+        raise WvcError(WVC_ERR_ARG, "kernel larger than the padded frame")
+    if stride[0] < 1 or not 0 <= t_phase < stride[0]:
+        raise WvcError(WVC_ERR_ARG, "bad temporal stride or t_phase")
+    to = conv_out_frames(t, stride[0], t_phase)
+    out_shape = (n, weight.shape[0], to, ho, wo)
+    frames = dilation[0] * (weight.shape[2] - 1)
+    if frames > 0:  # (a conv with no temporal reach ignores the caches)
+        for name, cc in (("cache_in", cache_in), ("cache_out", cache_out)):
+            _need_exact(cc, name, (n, c, frames, h, w), x.dtype, x.device)
+    _need_exact(residual, "residual", out_shape, x.dtype, x.device)
+    _need_exact(y, "y", out_shape, x.dtype, x.device)
     layout = WVC_WEIGHT_STANDARD if packed_weight is None else WVC_WEIGHT_PACKED
     d = conv_desc(tuple(x.shape), tuple(weight.shape), code, stride, padding, dilation, groups,
                   layout, pad_extra, t_phase)
+    if packed_weight is not None:
+        _need_bytes(packed_weight, "packed_weight",
+                    wvc_conv3d_packed_weight_bytes(tuple(weight.shape), x.dtype, padding, stride,
+                                                   pad_extra), x.device)
     wsrc = weight if packed_weight is None else packed_weight
     if y is None:
-        ho, wo = conv_out_hw(x.shape[3], x.shape[4], weight.shape[2:], stride, padding, dilation,
-                             pad_extra)
-        if ho < 1 or wo < 1:
-            raise WvcError(WVC_ERR_ARG, "kernel larger than the padded frame")
-        if stride[0] < 1 or not 0 <= t_phase < stride[0]:
-            raise WvcError(WVC_ERR_ARG, "bad temporal stride or t_phase")
-        to = conv_out_frames(x.shape[2], stride[0], t_phase)
-        y = empty_cl((x.shape[0], weight.shape[0], to, ho, wo), x.dtype, x.device)
+        y = empty_cl(out_shape, x.dtype, x.device)
     ws_bytes = 0
     if workspace is None:
         need = wvc_causal_conv3d_workspace_bytes(d)
@@ -353,13 +406,22 @@ def wvc_resblock_e4m3_fwd(x: torch.Tensor, params: dict, s1: float, s2: float, c
     w1_scale, w2_scale (float32 [C]).  Caches are uint8 codes."""
     lib = load()
     _need_cl(x, "x")
-    _need_cl(y, "y")
-    for name, t in (("cache1_in", cache1_in), ("cache1_out", cache1_out), ("cache2_in", cache2_in),
-                    ("cache2_out", cache2_out)):
-        _need_cl(t, name)
-    c = x.shape[1]
-    for k in ("gamma1", "gamma2", "beta1", "beta2", "b1", "b2", "w1_scale", "w2_scale"):
-        _need_vec(params.get(k), k, c)
+    n, c, t, h, w = x.shape
+    if x.dtype != torch.bfloat16:
+        raise TypeError("x must be bfloat16")
+    _need_exact(y, "y", x.shape, torch.bfloat16, x.device)
+    for name, cc in (("cache1_in", cache1_in), ("cache1_out", cache1_out), ("cache2_in", cache2_in),
+                     ("cache2_out", cache2_out)):
+        _need_exact(cc, name, (n, c, 2, h, w), torch.uint8, x.device)
+    for k in ("gamma1", "gamma2", "beta1", "beta2", "b1", "b2"):
+        _need_exact(params.get(k), k, (c,), torch.bfloat16, x.device)
+    for k in ("w1_scale", "w2_scale"):
+        _need_exact(params.get(k), k, (c,), torch.float32, x.device)
+    wbytes = wvc_conv3d_packed_weight_bytes((c, c, 3, 3, 3), torch.uint8) if packed else c * c * 27
+    for k in ("w1", "w2"):
+        if params.get(k) is None or params[k].numel() * params[k].element_size() != wbytes \
+                or params[k].dtype != torch.uint8 or params[k].device != x.device:
+            raise ValueError(f"{k} must be {wbytes} bytes of E4M3 codes (uint8) on {x.device}")
     d = resblock_desc(tuple(x.shape), c, WVC_BF16, eps, weights_packed=packed)
     if y is None:
         y = empty_cl(x.shape, x.dtype, x.device)
@@ -391,18 +453,26 @@ def wvc_rmsnorm_silu_conv3d_fwd(x: torch.Tensor, gamma: torch.Tensor, weight: to
     lib = load()
     _need_cl(x, "x")
     _need_cl(weight, "weight")
-    _need_cl(residual, "residual")
-    _need_cl(y, "y")
-    _need_vec(bias, "bias", weight.shape[0])
-    _need_vec(gamma, "gamma", x.shape[1])
-    _need_vec(beta, "beta", x.shape[1])
+    n, c, t, h, w = x.shape
+    _need_exact(weight, "weight", (weight.shape[0], c) + tuple(weight.shape[2:]), x.dtype, x.device)
+    _need_exact(bias, "bias", (weight.shape[0],), x.dtype, x.device)
+    _need_exact(gamma, "gamma", (c,), x.dtype, x.device)
+    _need_exact(beta, "beta", (c,), x.dtype, x.device)
+    ho, wo = conv_out_hw(h, w, weight.shape[2:], stride, padding, (1, 1, 1), pad_extra)
+    if ho < 1 or wo < 1:
+        raise WvcError(WVC_ERR_ARG, "kernel larger than the padded frame")
+    out_shape = (n, weight.shape[0], t, ho, wo)
+    _need_exact(residual, "residual", out_shape, x.dtype, x.device)
+    _need_exact(y, "y", out_shape, x.dtype, x.device)
     layout = WVC_WEIGHT_STANDARD if packed_weight is None else WVC_WEIGHT_PACKED
     d = conv_desc(tuple(x.shape), tuple(weight.shape), _dtype_code(x.dtype), stride, padding,
                   weight_layout=layout, pad_extra=pad_extra)
+    if packed_weight is not None:
+        _need_bytes(packed_weight, "packed_weight",
+                    wvc_conv3d_packed_weight_bytes(tuple(weight.shape), x.dtype, padding, stride,
+                                                   pad_extra), x.device)
     if y is None:
-        ho, wo = conv_out_hw(x.shape[3], x.shape[4], weight.shape[2:], stride, padding, (1, 1, 1),
-                             pad_extra)
-        y = empty_cl((x.shape[0], weight.shape[0], x.shape[2], ho, wo), x.dtype, x.device)
+        y = empty_cl(out_shape, x.dtype, x.device)
     ws_bytes = 0
     if workspace is None:
         need = wvc_causal_conv3d_workspace_bytes(d)
@@ -432,19 +502,25 @@ def wvc_causal_conv3d_e4m3_fwd(x: torch.Tensor, x_scale: float, weight: torch.Te
     lib = load()
     _need_cl(x, "x")
     _need_cl(weight, "weight")
-    for name, t in (("cache_in", cache_in), ("cache_out", cache_out), ("residual", residual),
-                    ("y", y)):
-        _need_cl(t, name)
-    _need_vec(bias, "bias", weight.shape[0])
-    _need_vec(w_scale, "w_scale", weight.shape[0])
     if x.dtype != torch.uint8 or weight.dtype != torch.uint8 or w_scale.dtype != torch.float32:
         raise TypeError("x and weight must be uint8 (E4M3 codes), w_scale float32")
+    n, c, t, h, w = x.shape
+    co = weight.shape[0]
+    _need_exact(weight, "weight", (co, c) + tuple(weight.shape[2:]), torch.uint8, x.device)
+    _need_exact(bias, "bias", (co,), torch.bfloat16, x.device)
+    _need_exact(w_scale, "w_scale", (co,), torch.float32, x.device)
+    for name, cc in (("cache_in", cache_in), ("cache_out", cache_out)):
+        _need_exact(cc, name, (n, c, 2, h, w), torch.uint8, x.device)
+    for name, tt in (("residual", residual), ("y", y)):
+        _need_exact(tt, name, (n, co, t, h, w), torch.bfloat16, x.device)
     layout = WVC_WEIGHT_STANDARD if packed_weight is None else WVC_WEIGHT_PACKED
     d = conv_desc(tuple(x.shape), tuple(weight.shape), WVC_E4M3, weight_layout=layout)
+    if packed_weight is not None:
+        _need_bytes(packed_weight, "packed_weight",
+                    wvc_conv3d_packed_weight_bytes(tuple(weight.shape), torch.uint8), x.device)
     wsrc = weight if packed_weight is None else packed_weight
     if y is None:
-        y = empty_cl((x.shape[0], weight.shape[0], x.shape[2], x.shape[3], x.shape[4]),
-                     torch.bfloat16, x.device)
+        y = empty_cl((n, co, t, h, w), torch.bfloat16, x.device)
     ws_bytes = 0
     if workspace is None:
         need = wvc_causal_conv3d_workspace_bytes(d)
@@ -461,7 +537,7 @@ def wvc_causal_conv3d_e4m3_fwd(x: torch.Tensor, x_scale: float, weight: torch.Te
 
 def wvc_quantize_e4m3(x: torch.Tensor, scale: float, q: Optional[torch.Tensor] = None) -> torch.Tensor:
     """E4M3 codes of fl32(x * fl32(1/scale)), same shape and strides as x (uint8)."""
-    if not x.is_cuda or not x.is_contiguous(memory_format=torch.channels_last_3d if x.dim() == 5
+    if not _on_device(x) or not x.is_contiguous(memory_format=torch.channels_last_3d if x.dim() == 5
                                             else torch.contiguous_format):
         raise ValueError("x must be a dense device tensor")
     if q is None:
@@ -476,7 +552,7 @@ def wvc_quantize_rows_e4m3(x: torch.Tensor, q: Optional[torch.Tensor] = None,
     """Per-row absmax quantisation of a tensor viewed as [shape[0], rest] in its
     memory order (conv weights in channels_last_3d: one row per output
     channel).  Returns (codes uint8 like x, scales float32 [shape[0]])."""
-    if not x.is_cuda:
+    if not _on_device(x):
         raise ValueError("x must be a device tensor")
     mf = torch.channels_last_3d if x.dim() == 5 else torch.contiguous_format
     if not x.is_contiguous(memory_format=mf):
@@ -497,12 +573,12 @@ def wvc_rmsnorm_silu_e4m3(x: torch.Tensor, gamma: torch.Tensor, scale: float,
     """RMS norm (+ SiLU) of a bf16 tensor, stored as E4M3 codes of
     fl32(y * fl32(1/scale)) (see wvc_rmsnorm_silu_e4m3 in include/wvc.h)."""
     _need_cl(x, "x")
-    _need_cl(q, "q")
     n, c, t, h, w = x.shape
-    _need_vec(gamma, "gamma", c)
-    _need_vec(beta, "beta", c)
     if x.dtype != torch.bfloat16:
         raise TypeError("x must be bfloat16")
+    _need_exact(q, "q", x.shape, torch.uint8, x.device)
+    _need_exact(gamma, "gamma", (c,), torch.bfloat16, x.device)
+    _need_exact(beta, "beta", (c,), torch.bfloat16, x.device)
     if q is None:
         q = empty_cl(x.shape, torch.uint8, x.device)
     _check(load().wvc_rmsnorm_silu_e4m3(_ptr(x), _ptr(gamma), _ptr(beta), _ptr(q), n, c, t, h, w,
@@ -516,10 +592,10 @@ def wvc_rmsnorm_silu(x: torch.Tensor, gamma: torch.Tensor, beta: Optional[torch.
     """Channel RMS norm (+ SiLU) (see wvc_rmsnorm_silu in include/wvc.h)."""
     lib = load()
     _need_cl(x, "x")
-    _need_cl(y, "y")
     n, c, t, h, w = x.shape
-    _need_vec(gamma, "gamma", c)
-    _need_vec(beta, "beta", c)
+    _need_exact(y, "y", x.shape, x.dtype, x.device)
+    _need_exact(gamma, "gamma", (c,), x.dtype, x.device)
+    _need_exact(beta, "beta", (c,), x.dtype, x.device)
     if y is None:
         y = empty_cl(x.shape, x.dtype, x.device)
     _check(lib.wvc_rmsnorm_silu(_ptr(x), _ptr(gamma), _ptr(beta), _ptr(y), n, c, t, h, w,
@@ -546,6 +622,26 @@ def wvc_resblock_workspace_bytes(d: ResblockDesc) -> int:
     return v
 
 
+def _check_block_params(x: torch.Tensor, params: dict, packed: Optional[dict]):
+    """Shapes, dtypes and devices of a bf16/fp32 block's parameters (and of the
+    packed weights when given) against x and w1."""
+    _need_cl(x, "x")
+    ci = x.shape[1]
+    co = params["w1"].shape[0]
+    dt, dev = x.dtype, x.device
+    shapes = {"w1": (co, ci, 3, 3, 3), "w2": (co, co, 3, 3, 3), "gamma1": (ci,), "beta1": (ci,),
+              "b1": (co,), "gamma2": (co,), "beta2": (co,), "b2": (co,),
+              "w_short": (co, ci, 1, 1, 1), "b_short": (co,)}
+    for k, shp in shapes.items():
+        _need_exact(params.get(k), k, shp, dt, dev)
+    if packed is not None:
+        for k, pad in (("w1", (1, 1)), ("w2", (1, 1)), ("w_short", (0, 0))):
+            if packed.get(k) is not None:
+                _need_bytes(packed[k], f"packed {k}",
+                            wvc_conv3d_packed_weight_bytes(shapes[k], dt, pad), dev)
+    return co
+
+
 def wvc_resblock_fwd(x: torch.Tensor, params: dict, cache1_in=None, cache1_out=None,
                      cache2_in=None, cache2_out=None, y: Optional[torch.Tensor] = None,
                      eps: float = 1e-12, workspace: Optional[torch.Tensor] = None,
@@ -554,15 +650,14 @@ def wvc_resblock_fwd(x: torch.Tensor, params: dict, cache1_in=None, cache1_out=N
     ``params``: gamma1, beta1, w1, b1, gamma2, beta2, w2, b2[, w_short, b_short].
     ``packed``: optional {w1, w2[, w_short]} from wvc_conv3d_pack_weights."""
     lib = load()
-    _need_cl(x, "x")
-    c_out = params["w1"].shape[0]
-    for name in ("w1", "w2", "w_short"):
-        _need_cl(params.get(name), name)
+    c_out = _check_block_params(x, params, packed)
     if packed is not None:
         params = dict(params, **packed)
-    for name, t in (("cache1_in", cache1_in), ("cache1_out", cache1_out),
-                    ("cache2_in", cache2_in), ("cache2_out", cache2_out), ("y", y)):
-        _need_cl(t, name)
+    n, ci, t, h, w = x.shape
+    for name, cc, ch in (("cache1_in", cache1_in, ci), ("cache1_out", cache1_out, ci),
+                         ("cache2_in", cache2_in, c_out), ("cache2_out", cache2_out, c_out)):
+        _need_exact(cc, name, (n, ch, 2, h, w), x.dtype, x.device)
+    _need_exact(y, "y", (n, c_out, t, h, w), x.dtype, x.device)
     code = _dtype_code(x.dtype)
     d = resblock_desc(tuple(x.shape), c_out, code, eps, weights_packed=packed is not None)
     if y is None:
@@ -584,14 +679,15 @@ def wvc_resblock_fwd(x: torch.Tensor, params: dict, cache1_in=None, cache1_out=N
 def _block_call(x, params, packed, eps, workspace, outs):
     """Shared marshalling of the block halves: descriptor, params struct,
     workspace (allocated when not given) and its size."""
-    _need_cl(x, "x")
-    c_out = params["w1"].shape[0]
-    for name in ("w1", "w2", "w_short"):
-        _need_cl(params.get(name), name)
+    c_out = _check_block_params(x, params, packed)
     if packed is not None:
         params = dict(params, **packed)
-    for name, t in outs:
-        _need_cl(t, name)
+    n, ci, t, h, w = x.shape
+    want = {"cache1_in": (n, ci, 2, h, w), "cache1_out": (n, ci, 2, h, w),
+            "cache2_in": (n, c_out, 2, h, w), "cache2_out": (n, c_out, 2, h, w),
+            "h2": (n, c_out, t, h, w), "y": (n, c_out, t, h, w)}
+    for name, tt in outs:
+        _need_exact(tt, name, want[name], x.dtype, x.device)
     d = resblock_desc(tuple(x.shape), c_out, _dtype_code(x.dtype), eps,
                       weights_packed=packed is not None)
     need = wvc_resblock_workspace_bytes(d)
@@ -649,8 +745,8 @@ def wvc_cache_reset(cache: torch.Tensor):
 def wvc_upsample_nearest2x(x: torch.Tensor, y: Optional[torch.Tensor] = None) -> torch.Tensor:
     lib = load()
     _need_cl(x, "x")
-    _need_cl(y, "y")
     n, c, t, h, w = x.shape
+    _need_exact(y, "y", (n, c, t, 2 * h, 2 * w), x.dtype, x.device)
     if y is None:
         y = empty_cl((n, c, t, 2 * h, 2 * w), x.dtype, x.device)
     _check(lib.wvc_upsample_nearest2x(_ptr(x), _ptr(y), n, c, t, h, w, _dtype_code(x.dtype),
@@ -751,9 +847,9 @@ def wvc_tile_extract(x: torch.Tensor, y0: int, x0: int, th: int, tw: int,
     """tile = x[:, :, :, y0:y0+th, x0:x0+tw] as a channels-last tensor."""
     _need_cl(x, "x")
     n, c, t, h, w = x.shape
+    _need_exact(tile, "tile", (n, c, t, th, tw), x.dtype, x.device)
     if tile is None:
         tile = empty_cl((n, c, t, th, tw), x.dtype, x.device)
-    _need_cl(tile, "tile")
     _check(load().wvc_tile_extract(_ptr(x), _ptr(tile), n, c, t, h, w, y0, x0, th, tw,
                                    _dtype_code(x.dtype), _stream(x)))
     return tile
@@ -776,8 +872,10 @@ def wvc_tile_blend(tile: torch.Tensor, acc: torch.Tensor, wsum: torch.Tensor, y0
     _need_cl(acc, "acc")
     n, c, t, th, tw = tile.shape
     h, w = acc.shape[3:]
-    if acc.dtype != torch.float32 or wsum.dtype != torch.float32 or tuple(wsum.shape) != (h, w):
-        raise ValueError("acc and wsum must be fp32, wsum [H, W]")
+    _need_exact(acc, "acc", (n, c, t, h, w), torch.float32, tile.device)
+    _need_exact(wsum, "wsum", (h, w), torch.float32, tile.device)
+    if not wsum.is_contiguous():
+        raise ValueError("wsum must be contiguous")
     _check(load().wvc_tile_blend(_ptr(tile), _ptr(acc), _ptr(wsum), n, c, t, th, tw, h, w, y0, x0,
                                  *ramps, _dtype_code(tile.dtype), _stream(tile)))
 
@@ -787,9 +885,14 @@ def wvc_tile_blend_finish(acc: torch.Tensor, wsum: torch.Tensor, dtype=torch.bfl
     """y = acc / wsum, rounded once to ``dtype``."""
     _need_cl(acc, "acc")
     n, c, t, h, w = acc.shape
+    if acc.dtype != torch.float32:
+        raise TypeError("acc must be float32")
+    _need_exact(wsum, "wsum", (h, w), torch.float32, acc.device)
+    if not wsum.is_contiguous():
+        raise ValueError("wsum must be contiguous")
     if y is None:
         y = empty_cl((n, c, t, h, w), dtype, acc.device)
-    _need_cl(y, "y")
+    _need_exact(y, "y", (n, c, t, h, w), y.dtype, acc.device)
     _check(load().wvc_tile_blend_finish(_ptr(acc), _ptr(wsum), _ptr(y), n, c, t, h, w,
                                         _dtype_code(y.dtype), _stream(acc)))
     return y

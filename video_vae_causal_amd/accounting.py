@@ -35,10 +35,12 @@ def tensor_bytes(shape, dtype: str = "bf16") -> int:
 
 
 def conv_launch_bytes(n, t, h, w, c_in, c_out, k=(3, 3, 3), dtype="bf16",
-                      residual: bool = False, cache_frames: int = 2) -> int:
+                      residual: bool = False, cache_frames: int = 2,
+                      cache_out_frames: int = 0) -> int:
     """Compulsory bytes of one conv launch over a t-frame chunk: the chunk, the
     cache_frames past frames it reads, the weights and bias, the output chunk
-    (and the residual when fused)."""
+    (and the residual when fused), and the cache_out_frames frames of the
+    next cache it writes."""
     e = DTYPE_BYTES[dtype]
     plane_in = n * h * w * c_in
     plane_out = n * h * w * c_out
@@ -47,6 +49,7 @@ def conv_launch_bytes(n, t, h, w, c_in, c_out, k=(3, 3, 3), dtype="bf16",
     b += t * plane_out * e
     if residual:
         b += t * plane_out * e
+    b += cache_out_frames * plane_in * e
     return b
 
 

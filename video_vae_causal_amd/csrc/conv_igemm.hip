@@ -60,6 +60,7 @@
 // twice the bf16 rate).  The sum is exact products accumulated in fp32; the
 // epilogue (or the split-K reduce) multiplies it by x_scale * w_scale[co]
 // before the bias.
+#include <cstdio>
 #include <type_traits>
 
 #include "wvc_internal.h"
@@ -982,6 +983,14 @@ size_t ws_bytes_for(const Plan &pl, const ConvCall &c, bool need_pack) {
     return align256(part_bytes(pl, c)) + (need_pack ? align256(packed_bytes(c)) : 0);
 }
 
+// Whole-K 3x3x3 grids of 16x16 MFMA tiles with more tiles than CUs run
+// persistent workgroups (the tile split over XCDs needs a CU count that is a
+// multiple of 8).
+bool runs_persistent(int ks, int m, int S, long total) {
+    const int cus = num_cus();
+    return ks == 3 && m == 16 && S == 1 && cus % 8 == 0 && total > cus;
+}
+
 template <int KS, int CO_T, int M, int WAVES_CO, int TW, bool FP8>
 hipError_t launch_tw(const IgParams &p, hipStream_t s) {
     // Grids with more whole-K 3x3x3 tiles than CUs run persistent: one
@@ -995,7 +1004,7 @@ hipError_t launch_tw(const IgParams &p, hipStream_t s) {
         return hipGetLastError();
     }
     if constexpr (KS == 3 && M == 16) {
-        if (cus % 8 == 0 && p.total > cus) {
+        if (runs_persistent(KS, M, p.S, p.total)) {
             hipLaunchKernelGGL((igemm_persist_kernel<CO_T, M, WAVES_CO, TW, FP8>), dim3(cus),
                                dim3(256), 0, s, p);
             return hipGetLastError();
@@ -1050,6 +1059,25 @@ bool igemm_supports(const ConvCall &c) {
     const size_t wbytes = packed_bytes(c);
     if (is_e4m3(c) && (c.cin % 16 != 0 || c.kt != 3)) return false;
     return frame < ((size_t)1 << 31) && wbytes < ((size_t)1 << 31) && c.cout % 32 == 0;
+}
+
+int igemm_kernel_name(const ConvCall &c, ConvRoute r, char *buf, size_t n) {
+    if (r == ConvRoute::Fast1x1x1 && proj_supports(c))
+        return snprintf(buf, n, "%s", proj_kernel_name(c));
+    const Plan pl = make_plan(c, r);
+    const int ks = r == ConvRoute::Fast3x3x3 ? 3 : 1;
+    const bool fp8 = is_e4m3(c);
+    const int co_t = pl.co_t;
+    const int m = fp8 ? 32 : tile_m(co_t);
+    const int waves_co = co_t == 32 ? 1 : 2;
+    const char *f8 = fp8 ? "true" : "false";
+    if (pl.S > 1)
+        return snprintf(buf, n, "igemm_kernel<%d, %d, %d, %d, true, %d, %s> + splitk_reduce_kernel",
+                        ks, co_t, m, waves_co, pl.tw, f8);
+    if (runs_persistent(ks, m, pl.S, pl.tiles))
+        return snprintf(buf, n, "igemm_persist_kernel<%d, %d, %d, %d, %s>", co_t, m, waves_co, pl.tw, f8);
+    return snprintf(buf, n, "igemm_kernel<%d, %d, %d, %d, false, %d, %s>", ks, co_t, m, waves_co,
+                    pl.tw, f8);
 }
 
 hipError_t launch_conv_igemm(const ConvCall &c, ConvRoute r, bool packed_given, void *ws,

@@ -329,6 +329,20 @@ bool proj_supports(const ConvCall &c) {
            ((size_t)PT * ((c.cin + 31) / 32 * 4 + 1) * 16) <= 64 * 1024;
 }
 
+const char *proj_kernel_name(const ConvCall &c) {
+    const long P = (long)c.n * c.t * c.h * c.w;
+    const long blocks = (P + PT - 1) / PT;
+    const int nb = (c.cin + 31) / 32;
+    const int fco = (c.cout / 16 + 3) / 4;
+    if (c.cin % 32 == 0 && nb <= 12 && fco <= 3 && blocks >= 4L * num_cus_proj()) {
+        static const char *names[] = {"proj_persist_kernel<1, 12>", "proj_persist_kernel<2, 12>",
+                                      "proj_persist_kernel<3, 12>"};
+        return names[fco < 1 ? 0 : fco - 1];
+    }
+    static const char *names[] = {"proj_kernel<1>", "proj_kernel<2>", "proj_kernel<3>", "proj_kernel<4>"};
+    return names[fco < 1 ? 0 : (fco > 4 ? 3 : fco - 1)];
+}
+
 hipError_t launch_conv_proj(const ConvCall &c, const void *packed, size_t packed_bytes,
                             hipStream_t s) {
     const long P = (long)c.n * c.t * c.h * c.w;

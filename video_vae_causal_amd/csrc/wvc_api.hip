@@ -560,6 +560,20 @@ int wvc_rmsnorm_silu_e4m3(const void *x, const void *gamma, const void *beta, vo
                       "rmsnorm e4m3 launch");
 }
 
+const char *wvc_conv3d_kernel_name(const wvc_conv3d_desc *d) {
+    thread_local char name[160];
+    name[0] = 0;
+    ConvPlan pl;
+    if (plan_conv(d, &pl, /*count=*/false)) return name;  // a query is not a call
+    switch (pl.route) {
+        case wvc::ConvRoute::Generic: snprintf(name, sizeof(name), "direct_conv_kernel"); break;
+        case wvc::ConvRoute::FastTemporal:
+        case wvc::ConvRoute::FastSpatial2: snprintf(name, sizeof(name), "strided_kernel"); break;
+        default: wvc::igemm_kernel_name(pl.call, pl.route, name, sizeof(name)); break;
+    }
+    return name;
+}
+
 int wvc_conv3d_cache_frames(const wvc_conv3d_desc *d) {
     if (!d || d->kt < 1 || d->dil_t < 1) return -1;
     return d->dil_t * (d->kt - 1);

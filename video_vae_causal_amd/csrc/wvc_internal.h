@@ -123,6 +123,10 @@ hipError_t launch_conv_igemm(const ConvCall &c, ConvRoute r, bool packed_given, 
 // 1x1x1 route when proj_supports(c): C_out <= 256, C_in <= 480.  `packed` holds
 // the weights in the 16-row fragment order for a single channel tile.
 bool proj_supports(const ConvCall &c);
+const char *proj_kernel_name(const ConvCall &c);
+// Name of the kernel(s) launch_conv_igemm launches for this call on the
+// current device (snprintf semantics into buf).
+int igemm_kernel_name(const ConvCall &c, ConvRoute r, char *buf, size_t n);
 hipError_t launch_conv_proj(const ConvCall &c, const void *packed, size_t packed_bytes,
                             hipStream_t s);
 // Direct-convolution route (any stride/pad/dilation, fp32 or bf16).

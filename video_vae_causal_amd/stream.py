@@ -83,6 +83,17 @@ class _PingPong:
         self.cur ^= 1
         self.fresh = False
 
+    def fits(self, shape) -> bool:
+        return tuple(self.buf[0].shape) == tuple(shape)
+
+
+def _fits(pp: Optional[_PingPong], shape) -> bool:
+    """Whether a layer's cache pair serves a chunk of this batch and frame
+    size.  A chunk of another size cannot continue the stream: the layer
+    starts a new sequence (fresh caches of the new size) instead of letting
+    the library write full-size cache frames into a smaller buffer."""
+    return pp is not None and pp.fits(shape)
+
 
 class CausalConv3d:
     """A causal 3x3x3 conv layer with its rolling 2-frame cache."""
@@ -107,8 +118,9 @@ class CausalConv3d:
 
     def __call__(self, x: torch.Tensor, y: Optional[torch.Tensor] = None,
                  residual: Optional[torch.Tensor] = None) -> torch.Tensor:
-        if self.cache is None and self.frames:
-            self.start(x.shape[0], x.shape[3], x.shape[4])
+        n, c, _, h, w = x.shape
+        if self.frames and not _fits(self.cache, (n, c, self.frames, h, w)):
+            self.start(n, h, w)
         cin = self.cache.cin if self.frames else None
         cout = self.cache.cout if self.frames else None
         layout = L.WVC_WEIGHT_PACKED if self.packed is not None else L.WVC_WEIGHT_STANDARD
@@ -177,9 +189,13 @@ class ResBlock:
     def pingpongs(self) -> List[_PingPong]:
         return [self.c1, self.c2] if self.c1 is not None else []
 
+    def _ensure(self, x: torch.Tensor):
+        n, c, _, h, w = x.shape
+        if not _fits(self.c1, (n, c, CACHE_T, h, w)):
+            self.start(n, h, w)
+
     def __call__(self, x: torch.Tensor, y: Optional[torch.Tensor] = None) -> torch.Tensor:
-        if self.c1 is None:
-            self.start(x.shape[0], x.shape[3], x.shape[4])
+        self._ensure(x)
         d = L.resblock_desc(tuple(x.shape), self.p["w1"].shape[0], L._dtype_code(x.dtype), self.eps,
                             weights_packed=self.packed is not None)
         need = L.wvc_resblock_workspace_bytes(d)
@@ -210,8 +226,7 @@ class ResBlock:
 
     def front(self, x: torch.Tensor, h2: torch.Tensor) -> torch.Tensor:
         """First half (norm1, conv1, norm2) into h2; advances cache1."""
-        if self.c1 is None:
-            self.start(x.shape[0], x.shape[3], x.shape[4])
+        self._ensure(x)
         L.wvc_resblock_front(x, self.p, self.c1.cin, self.c1.cout, h2=h2, eps=self.eps,
                              workspace=self._half_ws("ws_front", x), packed=self.packed)
         self.c1.flip()
@@ -219,6 +234,9 @@ class ResBlock:
 
     def back(self, h2: torch.Tensor, x: torch.Tensor, y: torch.Tensor) -> torch.Tensor:
         """Second half (conv2 + shortcut) into y; advances cache2."""
+        n, _, _, h, w = x.shape
+        if not _fits(self.c2, (n, self.p["w1"].shape[0], CACHE_T, h, w)):
+            raise ValueError("back() of a chunk whose front() ran at another size")
         L.wvc_resblock_back(h2, x, self.p, self.c2.cin, self.c2.cout, y=y, eps=self.eps,
                             workspace=self._half_ws("ws_back", x), packed=self.packed)
         self.c2.flip()
@@ -267,8 +285,9 @@ class CausalConv3dE4M3:
         return [self.cache.cin]
 
     def __call__(self, x: torch.Tensor, y: Optional[torch.Tensor] = None) -> torch.Tensor:
-        if self.cache is None:
-            self.start(x.shape[0], x.shape[3], x.shape[4])
+        n, c, _, h, w = x.shape
+        if not _fits(self.cache, (n, c, CACHE_T, h, w)):
+            self.start(n, h, w)
         q = _cached_buf(self.bufs, "q", x.shape, x.new_empty(0, dtype=torch.uint8))
         L.wvc_quantize_e4m3(x, self.scale, q=q)
         d = L.conv_desc(tuple(q.shape), tuple(self.wq.shape), L.WVC_E4M3, weight_layout=L.WVC_WEIGHT_PACKED)
@@ -337,8 +356,9 @@ class ResBlockE4M3:
         return [self.c1.cin, self.c2.cin]
 
     def __call__(self, x: torch.Tensor, y: Optional[torch.Tensor] = None) -> torch.Tensor:
-        if self.c1 is None:
-            self.start(x.shape[0], x.shape[3], x.shape[4])
+        n, c, _, h, w = x.shape
+        if not _fits(self.c1, (n, c, CACHE_T, h, w)):
+            self.start(n, h, w)
         d = L.resblock_desc(tuple(x.shape), x.shape[1], L.WVC_BF16, self.eps, weights_packed=True)
         need = L.wvc_resblock_e4m3_workspace_bytes(d)
         if self.ws is None or self.ws.numel() < need:
