@@ -125,3 +125,60 @@ def test_pipelined_decoder_21_frames_equals_sequential():
         pipe.run(frames, outs)
         torch.cuda.synchronize()
         assert torch.equal(out, seq), f"pass {rep}: pipeline differs from the sequential frames"
+
+
+@pytest.mark.skip(reason="ending a HIP stream capture that recorded the two-stream fork/join "
+                         "crashed the host process (segmentation fault inside hipStreamEndCapture), "
+                         "also with fork and join events that outlive the capture; the cause is not "
+                         "known, so Pipeline.run raises under capture and this case stays off the GPU")
+def test_pipelined_decoder_recorded_into_a_graph_equals_sequential():
+    """The two-stream pipeline recorded into one HIP graph: its fork and join
+    use events that outlive the capture (no temporary events are destroyed
+    while they are recorded into it).  Every replay, with eager work and
+    synchronisations in between, equals the sequential chunk loop bitwise."""
+    d = inputs.decoder_inputs(seed=16, shape=(1, 16, 4, 6, 9), width=64)
+    pd, lat = stack_dev(d["p"]), to_dev(d["latent"])
+    t = lat.shape[2]
+    seq = stream.DecoderStack(pd).run(lat, chunk_frames=1)
+    stack = stream.DecoderStack(pd)
+    stack.start(1, 6, 9)
+    frames = [cl(lat[:, :, i:i + 1]) for i in range(t)]
+    out = L.empty_cl(seq.shape)
+    outs = [out[:, :, i:i + 1] for i in range(t)]
+    pipe = stream.Pipeline(stack)
+    pipe.run(frames, outs)              # eager pass: sizes every buffer set
+    torch.cuda.synchronize()
+    assert torch.equal(out, seq)
+    stack.reset()                       # the recording starts a fresh sequence
+    print("[case] pipeline recorded into a graph", flush=True)
+    graph = stream.capture(lambda: pipe.run(frames, outs))
+    try:
+        for rep in range(3):
+            out.fill_(float("nan"))
+            graph.launch()
+            torch.cuda.synchronize()
+            assert torch.equal(out, seq), f"replay {rep} differs from the sequential loop"
+            other = stream.DecoderStack(pd).run(lat, chunk_frames=2)   # eager work in between
+            torch.cuda.synchronize()
+            check_bf16(to_host(other), to_host(seq), "eager 2-frame chunks between replays")
+    finally:
+        torch.cuda.synchronize()
+        graph.close()
+
+
+def test_pipeline_refuses_to_be_recorded(monkeypatch):
+    """Until the capture crash above is understood, a pipelined pass refuses
+    to run on a capturing stream, before it enqueues anything (the capture
+    state is simulated here: no capture is started)."""
+    d = inputs.decoder_inputs(seed=16, shape=(1, 16, 2, 6, 9), width=64)
+    stack = stream.DecoderStack(stack_dev(d["p"]))
+    lat = to_dev(d["latent"])
+    stack.start(1, 6, 9)
+    out = L.empty_cl((1, 64, 2, 12, 18))
+    frames = [cl(lat[:, :, i:i + 1]) for i in range(2)]
+    outs = [out[:, :, i:i + 1] for i in range(2)]
+    pipe = stream.Pipeline(stack)
+    torch.cuda.synchronize()
+    monkeypatch.setattr(torch.cuda, "is_current_stream_capturing", lambda: True)
+    with pytest.raises(RuntimeError, match="cannot be recorded"):
+        pipe.run(frames, outs)

@@ -604,8 +604,12 @@ class Pipeline:
         self.device = dev
         self.streams = [torch.cuda.Stream(dev), torch.cuda.Stream(dev)]
         self._bufs = [{} for _ in range(slots)]
+        # Every event the pipeline records lives as long as the pipeline (the
+        # fork and join use these instead of wait_stream's temporary events).
         self._ev_a = [torch.cuda.Event() for _ in range(slots)]
         self._ev_b = [torch.cuda.Event() for _ in range(slots)]
+        self._ev_fork = torch.cuda.Event()
+        self._ev_join = [torch.cuda.Event(), torch.cuda.Event()]
 
     def _buf(self, slot: int):
         bufs = self._bufs[slot]
@@ -624,14 +628,17 @@ class Pipeline:
         current cache state.  The work goes to the two streams; the current
         stream waits for all of it before this returns."""
         if torch.cuda.is_current_stream_capturing():
-            # Recording a two-stream fork/join into a graph crashed the HIP
-            # runtime inside end-capture; graphs record single-stream work.
+            # Ending a capture that recorded this two-stream fork/join crashed
+            # the HIP runtime (a host segmentation fault inside end-capture),
+            # also with every event outliving the capture; graphs record
+            # single-stream work only.
             raise RuntimeError("Pipeline.run cannot be recorded into a graph; record the "
                                "sequential chunk loop (or FrameGraph) instead")
         main = torch.cuda.current_stream(self.device)
         sa, sb = self.streams
-        sa.wait_stream(main)
-        sb.wait_stream(main)
+        self._ev_fork.record(main)
+        sa.wait_event(self._ev_fork)
+        sb.wait_event(self._ev_fork)
         for i, (x, y) in enumerate(zip(chunks, outs)):
             slot = i % self.slots
             stages = self.stack.stages(x, y, self._buf(slot))
@@ -651,8 +658,9 @@ class Pipeline:
             x.record_stream(sa)
             x.record_stream(sb)
             y.record_stream(sb)
-        main.wait_stream(sa)
-        main.wait_stream(sb)
+        for ev, st in zip(self._ev_join, (sa, sb)):
+            ev.record(st)
+            main.wait_event(ev)
 
 
 def tile_origins(size: int, tile: int, stride: int) -> List[int]:
