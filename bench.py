@@ -818,7 +818,7 @@ def layer384_baseline(info, threads):
     dt, runs = cpu_time_loop(run)
     res = {"value": flops * runs / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
            "cpu_model": cpu_model(),
-           "sample": f"3x3x3 conv output frames 2-4 x rows 0-{rows - 1} x 416 x 384 channels "
+           "sample": f"3x3x3 conv output frames 2-4 x rows 0-{rows - 1} x {w} x {c} channels "
                      f"(cache = input frames 0-1), run {runs}x",
            "seconds": round(dt, 3), "flops": flops * runs}
     # one thread, a smaller sample of the same conv: frame 2, rows 0-1
@@ -830,7 +830,7 @@ def layer384_baseline(info, threads):
     finally:
         omp_threads(threads)
     res["single_thread"] = {"value": f1 * runs1 / dt1 / 1e12, "unit": "TFLOP/s", "cores": 1,
-                            "sample": f"conv output frame 2, rows 0-1 x 416 x 384 channels, run {runs1}x",
+                            "sample": f"conv output frame 2, rows 0-1 x {w} x {c} channels, run {runs1}x",
                             "seconds": round(dt1, 3), "flops": f1 * runs1}
     # parity of the benched run on the sample
     g = info["gpu_outputs"]()
