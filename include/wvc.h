@@ -152,6 +152,29 @@ int wvc_causal_conv3d_fwd(const wvc_conv3d_desc *d, const void *x, const void *c
                           const void *residual, void *y, void *workspace,
                           size_t workspace_bytes, void *stream);
 
+/*
+ * wvc_causal_conv3d_fwd for callers that cannot allocate device memory: code
+ * under HIP graph capture, serving loops and harnesses that forbid hipMalloc.
+ * The same kernels run; their scratch (split-K partial sums, and the packed
+ * weights when standard-layout weights come in) lives in a fixed device array
+ * inside the library, WVC_NOALLOC_SCRATCH_MIB MiB per GPU, held until the
+ * process ends, instead of a caller workspace.  The call allocates nothing;
+ * the caller still passes every input and output.
+ *   Arguments, routes, results and errors as for wvc_causal_conv3d_fwd; a
+ *   call whose wvc_causal_conv3d_workspace_bytes(d) exceeds the array fails
+ *   with WVC_ERR_WORKSPACE before anything is enqueued.  The stream must
+ *   belong to the current device.  The array's contents on entry do not
+ *   matter (nothing in it needs clearing).
+ *   Every call on one GPU shares that GPU's array, which keeps the last call's
+ *   contents: calls that overlap in time on one GPU (different streams or
+ *   threads) race on it and give wrong results.  Serialise them, e.g. on one
+ *   stream.
+ */
+#define WVC_NOALLOC_SCRATCH_MIB 48
+int wvc_causal_conv3d_fwd_noalloc(const wvc_conv3d_desc *d, const void *x, const void *cache_in,
+                                  void *cache_out, const void *weight, const void *bias,
+                                  const void *residual, void *y, void *stream);
+
 /* Bytes of workspace wvc_causal_conv3d_fwd needs for this descriptor
  * (0 when none; (size_t)-1 for an invalid descriptor).  A call with
  * standard-layout weights on a fast route needs room to pack them. */

@@ -509,3 +509,21 @@ def test_norm_upsample_e4m3_bindings_refuse_mismatched_buffers(host_binding):
         L.wvc_causal_conv3d_e4m3_fwd(q, 0.1, wq, ws, cache_in=cl_host(torch, (1, 32, 2, 6, 5), torch.uint8))
     with pytest.raises((ValueError, TypeError)):
         L.wvc_causal_conv3d_e4m3_fwd(q, 0.1, wq, ws, y=cl_host(torch, (1, 32, 2, 6, 10), torch.uint8))
+
+
+def test_noalloc_scratch_size_and_validation(lib):
+    """The allocation-free conv call: its scratch limit as the header states it,
+    and argument errors (including a need beyond the scratch) reported before
+    the scratch is even looked up (no GPU involved)."""
+    text = open(HEADER).read()
+    m = re.search(r"#define\s+WVC_NOALLOC_SCRATCH_MIB\s+(\d+)", text)
+    assert m and int(m.group(1)) == L.WVC_NOALLOC_SCRATCH_MIB
+    L.wvc_reset_counters()
+    f = lib.wvc_causal_conv3d_fwd_noalloc
+    assert f(None, X, CIN, COUT, W, B, None, Y, None) == L.WVC_ERR_ARG
+    assert f(ctypes.byref(desc(groups=2)), X, CIN, COUT, W, B, None, Y, None) == L.WVC_ERR_UNSUPPORTED
+    big = desc(x_shape=(1, 384, 2, 60, 104), w_shape=(384, 384, 3, 3, 3))
+    assert L.wvc_causal_conv3d_workspace_bytes(big) > L.WVC_NOALLOC_SCRATCH_MIB << 20
+    assert f(ctypes.byref(big), X, CIN, COUT, W, B, None, Y, None) == L.WVC_ERR_WORKSPACE
+    assert "scratch" in L.wvc_last_error()
+    assert L.wvc_get_counters()["fast_3x3x3"] == 0

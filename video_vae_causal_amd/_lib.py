@@ -24,6 +24,7 @@ WVC_OK, WVC_ERR_ARG, WVC_ERR_UNSUPPORTED, WVC_ERR_ALIAS, WVC_ERR_WORKSPACE, WVC_
     WVC_ERR_HIP = range(7)
 WVC_F32, WVC_BF16, WVC_E4M3 = 0, 1, 2
 WVC_WEIGHT_STANDARD, WVC_WEIGHT_PACKED = 0, 1
+WVC_NOALLOC_SCRATCH_MIB = 48  # include/wvc.h: scratch array of the allocation-free conv call
 ERROR_NAMES = {0: "WVC_OK", 1: "WVC_ERR_ARG", 2: "WVC_ERR_UNSUPPORTED", 3: "WVC_ERR_ALIAS",
                4: "WVC_ERR_WORKSPACE", 5: "WVC_ERR_STRICT", 6: "WVC_ERR_HIP"}
 
@@ -39,7 +40,7 @@ EXPORTED = (
     "wvc_tile_extract", "wvc_tile_blend", "wvc_tile_blend_finish",
     "wvc_causal_conv3d_e4m3_fwd", "wvc_quantize_e4m3", "wvc_quantize_rows_e4m3",
     "wvc_rmsnorm_silu_e4m3", "wvc_rmsnorm_silu_conv3d_fwd", "wvc_resblock_e4m3_fwd",
-    "wvc_resblock_e4m3_workspace_bytes", "wvc_conv3d_kernel_name",
+    "wvc_resblock_e4m3_workspace_bytes", "wvc_conv3d_kernel_name", "wvc_causal_conv3d_fwd_noalloc",
 )
 
 
@@ -101,6 +102,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     dptr = ctypes.POINTER(ConvDesc)
     lib.wvc_causal_conv3d_fwd.argtypes = [dptr, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.wvc_causal_conv3d_fwd.restype = i
+    lib.wvc_causal_conv3d_fwd_noalloc.argtypes = [dptr, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.wvc_causal_conv3d_fwd_noalloc.restype = i
     lib.wvc_causal_conv3d_workspace_bytes.argtypes = [dptr]
     lib.wvc_causal_conv3d_workspace_bytes.restype = sz
     lib.wvc_conv3d_kernel_name.argtypes = [dptr]
@@ -347,6 +350,48 @@ def wvc_causal_conv3d_fwd(x: torch.Tensor, weight: torch.Tensor, bias: Optional[
     right of the frame; ``t_phase`` is the number of sequence frames before this
     chunk modulo the temporal stride.  Returns y (allocated if not given)."""
     lib = load()
+    d, out_shape, wsrc = _conv_checks(x, weight, bias, cache_in, cache_out, residual, y, stride,
+                                      padding, dilation, groups, packed_weight, pad_extra, t_phase)
+    if y is None:
+        y = empty_cl(out_shape, x.dtype, x.device)
+    ws_bytes = 0
+    if workspace is None:
+        need = wvc_causal_conv3d_workspace_bytes(d)
+        if need:  # contents on entry do not matter
+            workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    if workspace is not None:
+        ws_bytes = workspace.numel() * workspace.element_size()
+    _check(lib.wvc_causal_conv3d_fwd(ctypes.byref(d), _ptr(x), _ptr(cache_in), _ptr(cache_out),
+                                      _ptr(wsrc), _ptr(bias), _ptr(residual), _ptr(y),
+                                      _ptr(workspace), ws_bytes, _stream(x)))
+    return y
+
+
+def wvc_causal_conv3d_fwd_noalloc(x: torch.Tensor, weight: torch.Tensor, y: torch.Tensor,
+                                  bias: Optional[torch.Tensor] = None,
+                                  cache_in: Optional[torch.Tensor] = None,
+                                  cache_out: Optional[torch.Tensor] = None,
+                                  residual: Optional[torch.Tensor] = None, stride=(1, 1, 1),
+                                  padding=(1, 1), dilation=(1, 1, 1), groups: int = 1,
+                                  packed_weight: Optional[torch.Tensor] = None, pad_extra=(0, 0),
+                                  t_phase: int = 0) -> torch.Tensor:
+    """wvc_causal_conv3d_fwd without a workspace: the library's fixed scratch
+    array serves the kernels (see wvc_causal_conv3d_fwd_noalloc in
+    include/wvc.h).  Allocates nothing, so ``y`` must be given."""
+    if y is None:
+        raise ValueError("y must be given: the allocation-free call allocates nothing")
+    d, _, wsrc = _conv_checks(x, weight, bias, cache_in, cache_out, residual, y, stride, padding,
+                              dilation, groups, packed_weight, pad_extra, t_phase)
+    _check(load().wvc_causal_conv3d_fwd_noalloc(ctypes.byref(d), _ptr(x), _ptr(cache_in),
+                                                _ptr(cache_out), _ptr(wsrc), _ptr(bias),
+                                                _ptr(residual), _ptr(y), _stream(x)))
+    return y
+
+
+def _conv_checks(x, weight, bias, cache_in, cache_out, residual, y, stride, padding, dilation,
+                 groups, packed_weight, pad_extra, t_phase):
+    """Checks of a conv call's tensors against the descriptor built from x and
+    the weight; returns (descriptor, output shape, weight pointer source)."""
     _need_cl(x, "x")
     _need_cl(weight, "weight")
     code = _dtype_code(x.dtype)
@@ -374,19 +419,7 @@ def wvc_causal_conv3d_fwd(x: torch.Tensor, weight: torch.Tensor, bias: Optional[
                     wvc_conv3d_packed_weight_bytes(tuple(weight.shape), x.dtype, padding, stride,
                                                    pad_extra), x.device)
     wsrc = weight if packed_weight is None else packed_weight
-    if y is None:
-        y = empty_cl(out_shape, x.dtype, x.device)
-    ws_bytes = 0
-    if workspace is None:
-        need = wvc_causal_conv3d_workspace_bytes(d)
-        if need:  # contents on entry do not matter
-            workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
-    if workspace is not None:
-        ws_bytes = workspace.numel() * workspace.element_size()
-    _check(lib.wvc_causal_conv3d_fwd(ctypes.byref(d), _ptr(x), _ptr(cache_in), _ptr(cache_out),
-                                      _ptr(wsrc), _ptr(bias), _ptr(residual), _ptr(y),
-                                      _ptr(workspace), ws_bytes, _stream(x)))
-    return y
+    return d, out_shape, wsrc
 
 
 def wvc_resblock_e4m3_workspace_bytes(d: ResblockDesc) -> int:

@@ -4,6 +4,7 @@
 // work is enqueued.
 #include <atomic>
 #include <cmath>
+#include <mutex>
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
@@ -387,9 +388,70 @@ int plan_block(const wvc_resblock_desc *d, BlockLayout *L) {
     return WVC_OK;
 }
 
+// ---- scratch of the allocation-free conv entry point
+//
+// One fixed device array per GPU, in place of a caller workspace.  In host
+// code `scratch` names a host-side stand-in, never the device memory: its
+// device address is looked up once per device (hipGetSymbolAddress, with that
+// device current) and only that address is handed to kernels.
+constexpr size_t NOALLOC_SCRATCH_BYTES = (size_t)WVC_NOALLOC_SCRATCH_MIB << 20;
+static __device__ __align__(256) unsigned char scratch[NOALLOC_SCRATCH_BYTES];
+
+constexpr int SCRATCH_DEVICES = 64;
+struct ScratchSlot {
+    std::once_flag once;
+    void *ptr = nullptr;
+    hipError_t err = hipSuccess;
+};
+ScratchSlot g_scratch[SCRATCH_DEVICES];
+
+// Device address of the current device's scratch array.
+int scratch_address(void **out) {
+    int dev = -1;
+    const hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_status(e, "hipGetDevice");
+    if (dev < 0 || dev >= SCRATCH_DEVICES)
+        return fail(WVC_ERR_ARG, "device %d: the scratch table covers devices 0-%d", dev,
+                    SCRATCH_DEVICES - 1);
+    ScratchSlot &slot = g_scratch[dev];
+    std::call_once(slot.once, [&slot] {
+        void *p = nullptr;
+        slot.err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (slot.err == hipSuccess && p == nullptr) slot.err = hipErrorInvalidSymbol;
+        slot.ptr = slot.err == hipSuccess ? p : nullptr;
+    });
+    if (slot.err != hipSuccess) return hip_status(slot.err, "scratch symbol address");
+    *out = slot.ptr;
+    return WVC_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+int wvc_causal_conv3d_fwd_noalloc(const wvc_conv3d_desc *d, const void *x, const void *cache_in,
+                                  void *cache_out, const void *weight, const void *bias,
+                                  const void *residual, void *y, void *stream) {
+    if (d && d->dtype == WVC_E4M3) {
+        g_rejected++;
+        return fail(WVC_ERR_UNSUPPORTED, "E4M3 convs take wvc_causal_conv3d_e4m3_fwd (they need scales)");
+    }
+    ConvPlan pl;
+    const int rc = plan_conv(d, &pl, /*count=*/false);  // conv_fwd counts the call
+    if (rc) return rc;
+    const size_t need = route_ws_bytes(pl, d->weight_layout == WVC_WEIGHT_PACKED);
+    if (need > NOALLOC_SCRATCH_BYTES)
+        return fail(WVC_ERR_WORKSPACE,
+                    "the call needs %zu bytes of scratch; the allocation-free entry point has %zu "
+                    "(take wvc_causal_conv3d_fwd with a workspace)", need, NOALLOC_SCRATCH_BYTES);
+    void *ws = nullptr;
+    if (need > 0) {
+        const int r2 = scratch_address(&ws);
+        if (r2) return r2;
+    }
+    return conv_fwd(d, x, cache_in, cache_out, weight, bias, residual, y, ws, need,
+                    static_cast<hipStream_t>(stream));
+}
 
 int wvc_causal_conv3d_fwd(const wvc_conv3d_desc *d, const void *x, const void *cache_in,
                           void *cache_out, const void *weight, const void *bias,
