@@ -251,6 +251,40 @@ def test_spatial_stride2_larger_grid(fused):
     check_bf16(to_host(y), ref, f"spatial s2 larger grid fused={fused}")
 
 
+@pytest.mark.parametrize("fused", [False, True])
+@pytest.mark.parametrize("n,t,h,w,pad,ext", [
+    (2, 3, 161, 200, (1, 1), (0, 0)),   # symmetric pads, odd rows: runs that cross strip ends
+    (1, 5, 96, 130, (0, 0), (1, 1)),    # 63-column strips, ragged last strip
+])
+def test_spatial_stride2_row_walk_96(n, t, h, w, pad, ext, fused):
+    """The 96-channel spatial route walks down output rows of 63-column strips,
+    several rows per workgroup with a 3-row ring in LDS: grids with more rows
+    than CUs, so workgroups continue across rows and cross from one strip or
+    frame to the next."""
+    cin = cout = 96
+    x = bf((n, cin, t, h, w), 81, "x")
+    wt = inputs.conv_weight(cout, cin, (1, 3, 3), 81, "w", "bf16")
+    b = inputs.conv_bias(cout, 81, "b", "bf16")
+    g = inputs.norm_gamma(cin, 81, "g", "bf16")
+    be = inputs.quantize(inputs.normal((cin,), 81, "be", std=0.3), "bf16")
+    res = bf((n, cout, t, (h + 2 * pad[0] + ext[0] - 3) // 2 + 1, (w + 2 * pad[1] + ext[1] - 3) // 2 + 1),
+             81, "res")
+    print(f"[case] row walk {n}x{t}x{h}x{w} pad={pad} ext={ext} fused={fused}", flush=True)
+    L.wvc_reset_counters()
+    if fused:
+        y = L.wvc_rmsnorm_silu_conv3d_fwd(to_dev(x), to_dev(g), to_dev(wt), to_dev(b), beta=to_dev(be),
+                                          residual=to_dev(res), padding=pad, pad_extra=ext)
+        xin = oracle.norm_silu(f64(x), f64(g), f64(be), bf16=True)
+    else:
+        y = L.wvc_causal_conv3d_fwd(to_dev(x), to_dev(wt), to_dev(b), residual=to_dev(res), stride=(1, 2, 2),
+                                    padding=pad, pad_extra=ext)
+        xin = f64(x)
+    strided_route_taken(True)
+    ref = oracle.causal_conv3d_strided(xin, f64(wt), f64(b), stride=(1, 2, 2), pad=pad, pad_extra=ext) + f64(res)
+    assert tuple(y.shape) == ref.shape
+    check_bf16(to_host(y), ref, f"row walk {n}x{t}x{h}x{w} fused={fused}")
+
+
 def test_fused_norm_spatial_conv_empty_chunk():
     x = L.empty_cl((1, 96, 0, 8, 16))
     g = torch.ones(96, device="cuda", dtype=torch.bfloat16)

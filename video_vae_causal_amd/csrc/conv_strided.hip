@@ -383,6 +383,346 @@ __global__ void __launch_bounds__(256) strided_kernel(SParams p) {
     }
 }
 
+// ---------------------------------------------------------------------------
+// Row-walking variant of the spatial route for C_in = C_out = 96 (the encoder
+// level the downsample path runs at): persistent workgroups, one per CU, each
+// walking down a run of output rows of one 63-column strip.
+//
+// An item is one output row of a strip: 64 output columns through the MFMAs,
+// 63 of them stored (127 input columns per input row).  Output row oh reads
+// input rows 2oh-ph .. 2oh-ph+2 and the next output row shares the last of
+// them, so a ring of 3 input rows lives in LDS and each item stages 2 new
+// rows: each input row is staged once instead of 1.5 times on average, and
+// with the fused norm each input position is normalised once.
+//
+// Waves: 8 (two per SIMD), wave (wc, wq) = output channels 48 wc .. 48 wc + 47
+// for the K quarter wq (K-steps 7 wq .. 7 wq + 6; the last quarter has 6 of
+// the 27).  Its A fragments (84 VGPRs) stay in registers for the whole run
+// instead of streaming 166 KB of weights from L2 per output row.  The K
+// quarters of a channel group meet in LDS: each wave stores its partial sums
+// of the three 16-column blocks other waves finish and finishes block wq
+// itself, adding the four quarters' sums in quarter order (a fixed order,
+// whichever wave adds them).
+//
+// Each wave finishes its block of an item one item late, between the next
+// item's K-steps, so that those stores and partial-sum reads overlap MFMAs.
+//
+// Staging: before an item's MFMAs, the loads of the next item's two input
+// rows are issued (each row a contiguous run of 127 positions x 192 bytes in
+// memory; thread t loads 16-byte chunks t, t + 512, ...: coalesced).  After
+// the K loop they go to the ring rows the current item was the last to read;
+// with the fused norm, the staged positions are then normalised in place,
+// two threads per position (sum of squares with v_dot2_f32_bf16,
+// gamma/beta, SiLU, one rounding to bf16).  A strip's first item stages all three rows before its K loop.
+//
+// LDS row layout: the even input columns of a row at entries 13 s (s = column
+// / 2), the odd ones from entry 840 on.  A B-fragment read (16 consecutive
+// output columns of one tap) touches 16 consecutive slots of one parity, 13
+// entries apart (distinct bank quads), and a position-per-lane access of
+// neighbouring columns (one even, one odd) lands 8 entries apart mod 16.
+constexpr int RW_C8 = 12;            // 16-byte chunks per position (96 channels)
+constexpr int RW_COLS = 127;         // input columns staged per row
+constexpr int RW_PT = 63;            // output columns stored per item
+constexpr int RW_PITCH = 13;         // entries per column slot (12 + 1)
+constexpr int RW_ODD = 840;          // first entry of the odd columns
+constexpr int RW_ROW = 1680;         // entries per ring row
+constexpr int RW_KS = 27;            // K-steps: 9 taps x 3 blocks of 32 channels
+constexpr int RW_KQ = 7;             // K-steps per quarter (the last has 6)
+constexpr int RW_ROWCH = RW_COLS * RW_C8;  // chunks per staged row (1524)
+constexpr int RW_THREADS = 512;
+constexpr int RW_PER = (2 * RW_ROWCH + RW_THREADS - 1) / RW_THREADS;  // chunks per thread, 2 rows (6)
+
+__device__ __forceinline__ int rw_entry(int col) {
+    return (col & 1) ? RW_ODD + (col >> 1) * RW_PITCH : (col >> 1) * RW_PITCH;
+}
+
+template <bool NORM>
+__global__ void __launch_bounds__(RW_THREADS) strided_rows_kernel(SParams p, int items) {
+    __shared__ uint4 ring[3 * RW_ROW];
+    // partial sums exchanged between the K quarters: red[block b][source
+    // quarter, skipping b][wc][f][lane]
+    __shared__ f32x4 red[4][3][2][3][64];
+    __shared__ float4 gam_s[RW_C8 * 2], bet_s[RW_C8 * 2];
+    __shared__ float4 bias_s[24];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wc = wave & 1, wq = wave >> 1;
+    const int lr = lane & 15, lg = lane >> 4;
+    const int i_begin = (int)((long)blockIdx.x * items / gridDim.x);
+    const int i_end = (int)((long)(blockIdx.x + 1) * items / gridDim.x);
+    if (i_begin >= i_end) return;  // uniform per workgroup, before any barrier
+
+    if (tid < 24) {
+        uint2 bb = make_uint2(0u, 0u);
+        if (p.bias) bb = reinterpret_cast<const uint2 *>(p.bias)[tid];
+        bias_s[tid] = make_float4(bf16_to_f32(bb.x & 0xffffu), bf16_to_f32(bb.x >> 16),
+                                  bf16_to_f32(bb.y & 0xffffu), bf16_to_f32(bb.y >> 16));
+    }
+    if (NORM && tid < RW_C8 * 2) {
+        const uint4 gq = reinterpret_cast<const uint4 *>(p.gamma)[tid >> 1];
+        const uint4 bq = p.beta ? reinterpret_cast<const uint4 *>(p.beta)[tid >> 1] : make_uint4(0, 0, 0, 0);
+        const uint32_t g0 = (tid & 1) ? gq.z : gq.x, g1 = (tid & 1) ? gq.w : gq.y;
+        const uint32_t b0 = (tid & 1) ? bq.z : bq.x, b1 = (tid & 1) ? bq.w : bq.y;
+        gam_s[tid] = make_float4(bf16_to_f32(g0 & 0xffffu), bf16_to_f32(g0 >> 16), bf16_to_f32(g1 & 0xffffu),
+                                 bf16_to_f32(g1 >> 16));
+        bet_s[tid] = make_float4(bf16_to_f32(b0 & 0xffffu), bf16_to_f32(b0 >> 16), bf16_to_f32(b1 & 0xffffu),
+                                 bf16_to_f32(b1 >> 16));
+    }
+
+    // ---- weights: this wave's A fragments, loaded once
+    const __amdgpu_buffer_rsrc_t wr =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(p.wp), (short)0, (int)p.w_bytes, 0x00020000);
+    const int ks0 = wq * RW_KQ;
+    bf16x8 A[RW_KQ][3];
+#pragma unroll
+    for (int m = 0; m < RW_KQ; ++m) {
+        const int ks = ks0 + m < RW_KS ? ks0 + m : RW_KS - 1;
+#pragma unroll
+        for (int f = 0; f < 3; ++f)
+            A[m][f] = as_bf16x8(wload(wr, (uint32_t)((ks * 6 + wc * 3 + f) * 1024 + lane * 16)));
+    }
+
+    const size_t frame = (size_t)p.h * p.w * 96;
+    const int frame_bytes = (int)(frame * 2);
+    const int tiles = p.tiles;
+
+    // Staging of `rows` input rows starting at input row hs0 of frame (n, j),
+    // columns col0 .. col0 + 126: chunk q (q = tid + 512 k) is chunk q % 12 of
+    // column (q / 12) % 127 of row q / 1524.  Loads into raw[], then stores to
+    // the ring.
+    uint4 raw[RW_PER];
+    int dst[RW_PER];  // ring entry of each staged chunk, -1 past the end
+    auto issue = [&](int n_, int j_, int hs0, int col0, int qbase, int qend) __attribute__((always_inline)) {
+        const __amdgpu_buffer_rsrc_t fr = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint16_t *>(p.x + ((size_t)n_ * p.t + j_) * frame), (short)0, frame_bytes, 0x00020000);
+#pragma unroll
+        for (int k = 0; k < RW_PER; ++k) {
+            int q = qbase + tid + RW_THREADS * k;
+            // recomputed per call: hoisted copies of these indices would stay
+            // live across the whole item loop
+            asm volatile("" : "+v"(q));
+            const int row = q / RW_ROWCH, rem = q - row * RW_ROWCH;
+            const int col = rem / RW_C8, ch = rem - col * RW_C8;
+            const int hs = hs0 + row, ws = col0 + col;
+            // out-of-frame positions (the zero padding) read zero in hardware;
+            // a frame is below 2^31 bytes, so 32-bit offsets do
+            const bool in = q < qend && (unsigned)hs < (unsigned)p.h && (unsigned)ws < (unsigned)p.w;
+            const uint32_t off = in ? (uint32_t)(hs * p.w + ws) * 192u + (uint32_t)ch * 16u : 0x80000000u;
+            const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(fr, (int)off, 0, 0);
+            raw[k] = make_uint4(v.x, v.y, v.z, v.w);
+            dst[k] = q < qend ? ((hs + 3) % 3) * RW_ROW + rw_entry(col) + ch : -1;
+        }
+    };
+    auto store = [&]() __attribute__((always_inline)) {
+#pragma unroll
+        for (int k = 0; k < RW_PER; ++k)
+            if (dst[k] >= 0) ring[dst[k]] = raw[k];
+    };
+    // Fused norm of the staged positions, rows hs0 .. hs0 + rows - 1, in place
+    // in the ring: two threads per position (6 chunks = 48 channels each),
+    // their sums of squares combined across the lane pair.
+    auto normalise = [&](int hs0, int rows, int col0) __attribute__((always_inline)) {
+        if constexpr (NORM) {
+            typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+            constexpr int H8 = RW_C8 / 2;
+            for (int t2 = tid; t2 < 2 * rows * RW_COLS; t2 += RW_THREADS) {
+                const int pos = t2 >> 1, half = t2 & 1;
+                const int row = pos / RW_COLS, col = pos - row * RW_COLS;
+                const int hs = hs0 + row, ws = col0 + col;
+                const bool in = (unsigned)hs < (unsigned)p.h && (unsigned)ws < (unsigned)p.w;
+                uint4 *e = ring + ((hs + 3) % 3) * RW_ROW + rw_entry(col) + half * H8;
+                uint4 v[H8];
+                float ss = 0.f;
+#pragma unroll
+                for (int k = 0; k < H8; ++k) {
+                    v[k] = e[k];
+                    ss = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, v[k].x),
+                                                         __builtin_bit_cast(bf16x2, v[k].x), ss, false);
+                    ss = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, v[k].y),
+                                                         __builtin_bit_cast(bf16x2, v[k].y), ss, false);
+                    ss = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, v[k].z),
+                                                         __builtin_bit_cast(bf16x2, v[k].z), ss, false);
+                    ss = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, v[k].w),
+                                                         __builtin_bit_cast(bf16x2, v[k].w), ss, false);
+                }
+                // lane pairs (2m, 2m+1) hold the two halves; both add in the
+                // same order (half 0 + half 1), so both get the same bits
+                const float other = __shfl_xor(ss, 1);
+                const float tot = half ? other + ss : ss + other;
+                const float r = p.norm_scale / fmaxf(sqrtf(tot), p.eps);
+#pragma unroll
+                for (int k = 0; k < H8; ++k) {
+                    const float4 g0 = gam_s[2 * (half * H8 + k)], g1 = gam_s[2 * (half * H8 + k) + 1];
+                    const float4 b0 = bet_s[2 * (half * H8 + k)], b1 = bet_s[2 * (half * H8 + k) + 1];
+                    const float gg[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+                    const float bb[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+                    const uint32_t wd[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
+                    uint32_t o[4];
+#pragma unroll
+                    for (int d = 0; d < 4; ++d) {
+                        const float u0 = fmaf(bf16_to_f32(wd[d] & 0xffffu) * r, gg[2 * d], bb[2 * d]);
+                        const float u1 = fmaf(__uint_as_float(wd[d] & 0xffff0000u) * r, gg[2 * d + 1], bb[2 * d + 1]);
+                        o[d] = pack2_bf16(u0 * __builtin_amdgcn_rcpf(1.f + __expf(-u0)),
+                                          u1 * __builtin_amdgcn_rcpf(1.f + __expf(-u1)));
+                    }
+                    e[k] = in ? make_uint4(o[0], o[1], o[2], o[3]) : make_uint4(0u, 0u, 0u, 0u);
+                    __builtin_amdgcn_sched_barrier(0);  // one chunk at a time: few live values
+                }
+            }
+        }
+    };
+
+    // Epilogue of an item, finished one item late, during the next item's
+    // MFMAs: block wq of the finished item, the four quarters' partial sums
+    // in quarter order (its own from registers), + bias, + residual (loaded
+    // at the top of the iteration, ahead of the staging loads that share the
+    // load counter), one rounding.  Piece f covers 16 output channels.
+    bool have_prev = false;
+    size_t prev_obase = 0;
+    bool prev_st = false;
+    f32x4 prev_mine[3];
+    uint2 prev_res[3];
+    const int pp_mine = wq * 16 + lr;
+    auto epi_piece = [&](int f) __attribute__((always_inline)) {
+        const int co = wc * 48 + f * 16 + lg * 4;
+        float v[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const f32x4 part = q == wq ? prev_mine[f] : red[wq][q < wq ? q : q - 1][wc][f][lane];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] += part[e];
+        }
+        const float4 bv4 = bias_s[co / 4];
+        v[0] += bv4.x;
+        v[1] += bv4.y;
+        v[2] += bv4.z;
+        v[3] += bv4.w;
+        if (p.res) {
+            v[0] += bf16_to_f32(prev_res[f].x & 0xffffu);
+            v[1] += bf16_to_f32(prev_res[f].x >> 16);
+            v[2] += bf16_to_f32(prev_res[f].y & 0xffffu);
+            v[3] += bf16_to_f32(prev_res[f].y >> 16);
+        }
+        if (prev_st)
+            *reinterpret_cast<uint2 *>(p.y + prev_obase + co) =
+                make_uint2(pack2_bf16(v[0], v[1]), pack2_bf16(v[2], v[3]));
+    };
+
+    bool fresh = true;
+    for (int i = i_begin; i < i_end; ++i) {
+        // item -> (n, j, ct, oh), oh fastest
+        const int oh = i % p.ho;
+        int r_ = i / p.ho;
+        const int ct = r_ % tiles;
+        r_ /= tiles;
+        const int j = r_ % p.to, n = r_ / p.to;
+        const int r0 = 2 * oh - p.ph;  // first input row of this item
+        const int col0 = 2 * (ct * RW_PT) - p.pw;
+        if (have_prev && p.res && prev_st) {
+#pragma unroll
+            for (int f = 0; f < 3; ++f)
+                prev_res[f] = *reinterpret_cast<const uint2 *>(p.res + prev_obase + wc * 48 + f * 16 + lg * 4);
+        }
+        if (fresh) {  // all three rows, in two batches of loads
+            for (int qb = 0; qb < 3 * RW_ROWCH; qb += RW_THREADS * RW_PER) {
+                issue(n, j, r0, col0, qb, 3 * RW_ROWCH);
+                store();
+            }
+            if (NORM) {
+                __syncthreads();
+                normalise(r0, 3, col0);
+            }
+            __syncthreads();
+        }
+        // next item continues this strip: its two new rows r0+3, r0+4
+        const bool next = i + 1 < i_end && oh + 1 < p.ho;
+        if (next) issue(n, j, r0 + 3, col0, 0, 2 * RW_ROWCH);
+
+        // ---- K loop over this wave's quarter.  Each quarter is its own
+        // compile-time instance, so every B-fragment address is one of three
+        // per-row bases plus an immediate offset.  The previous item's
+        // epilogue pieces go between its K-steps.
+        const uint4 *rowb[3];
+#pragma unroll
+        for (int kh = 0; kh < 3; ++kh) rowb[kh] = ring + ((r0 + kh + 3) % 3) * RW_ROW + lr * RW_PITCH + lg;
+        f32x4 acc[3][4];
+#pragma unroll
+        for (int f = 0; f < 3; ++f)
+#pragma unroll
+            for (int b = 0; b < 4; ++b) acc[f][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+        const bool epi = have_prev;
+        auto kloop = [&](auto wq_tag) __attribute__((always_inline)) {
+            constexpr int WQ = decltype(wq_tag)::value;
+            constexpr int K0 = WQ * RW_KQ;
+            constexpr int NK = WQ == 3 ? RW_KS - 3 * RW_KQ : RW_KQ;
+            // entry offset of K-step ks, column block b, relative to this lane's row base
+            auto off = [](int ks, int b) constexpr {
+                const int tap = ks / 3, cb = ks % 3, kw = tap % 3;
+                return (kw == 1 ? RW_ODD + b * 16 * RW_PITCH : (b * 16 + (kw >> 1)) * RW_PITCH) + cb * 4;
+            };
+            bf16x8 B[2][4];
+#pragma unroll
+            for (int b = 0; b < 4; ++b) B[0][b] = as_bf16x8(rowb[K0 / 9][off(K0, b)]);
+            static_for<NK>([&](auto mt) {
+                constexpr int m = decltype(mt)::value;
+                constexpr int cur = m & 1;
+                if constexpr (m + 1 < NK) {
+                    constexpr int ks = K0 + m + 1;
+#pragma unroll
+                    for (int b = 0; b < 4; ++b) B[cur ^ 1][b] = as_bf16x8(rowb[ks / 9][off(ks, b)]);
+                }
+#pragma unroll
+                for (int b = 0; b < 4; ++b)
+#pragma unroll
+                    for (int f = 0; f < 3; ++f)
+                        acc[f][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[m][f], B[cur][b], acc[f][b], 0, 0, 0);
+                if constexpr (m >= 1 && m <= 3) {
+                    if (epi) epi_piece(m - 1);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            });
+        };
+        switch (wq) {
+            case 0: kloop(Int<0>{}); break;
+            case 1: kloop(Int<1>{}); break;
+            case 2: kloop(Int<2>{}); break;
+            default: kloop(Int<3>{}); break;
+        }
+        __syncthreads();  // K loops and the previous epilogue done: red free, ring rows r0, r0+1 free
+        // partial sums of the blocks other waves finish
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+            if (b != wq) {
+#pragma unroll
+                for (int f = 0; f < 3; ++f) red[b][wq < b ? wq : wq - 1][wc][f][lane] = acc[f][b];
+            }
+#pragma unroll
+        for (int f = 0; f < 3; ++f)  // (selects keep acc in registers)
+            prev_mine[f] = wq == 0 ? acc[f][0] : wq == 1 ? acc[f][1] : wq == 2 ? acc[f][2] : acc[f][3];
+        prev_obase = ((((size_t)n * p.to + j) * p.ho + oh) * (size_t)p.wo + ct * RW_PT + pp_mine) * 96;
+        prev_st = pp_mine < RW_PT && ct * RW_PT + pp_mine < p.wo;
+        have_prev = true;
+        if (next) {
+            store();
+            if (NORM) {
+                __syncthreads();
+                normalise(r0 + 3, 2, col0);
+            }
+        }
+        __syncthreads();  // new rows and partial sums in
+        fresh = !next;
+    }
+    // the last item's epilogue
+    if (p.res && prev_st) {
+#pragma unroll
+        for (int f = 0; f < 3; ++f)
+            prev_res[f] = *reinterpret_cast<const uint2 *>(p.res + prev_obase + wc * 48 + f * 16 + lg * 4);
+    }
+#pragma unroll
+    for (int f = 0; f < 3; ++f) epi_piece(f);
+}
+
 // Standard [C_out][K] bf16 weights -> [K-step][16-row block][lane] fragments:
 // lane (lr, lg) of block b at K-step ks holds row b*16 + lr, columns
 // ks*32 + lg*8 .. +7.
@@ -474,6 +814,27 @@ hipError_t launch_mode(const SParams &p, Layout l, long blocks, size_t lds, hipS
     }
 }
 
+// The row-walking kernel: the spatial stride-2 conv at 96 -> 96 channels
+// (its weights are held in registers, which fixes both channel counts).
+bool rows_route(const ConvCall &c) {
+    return is_spatial2(c) && c.cin == 96 && c.cout == 96 &&
+           (size_t)c.h * c.w * c.cin * 2 < ((size_t)1 << 31);
+}
+
+int num_cus_strided() {
+    static int cached = 0;
+    if (!cached) {
+        int dev = 0, cus = 0;
+        if (hipGetDevice(&dev) == hipSuccess &&
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+            cus > 0)
+            cached = cus;
+        else
+            cached = 256;
+    }
+    return cached;
+}
+
 bool layout_instantiated(Layout l) {
     switch (l.wco * 10 + l.fco) {
         case 41: case 42: case 43: case 44: case 21: case 23: case 11: case 13: return true;
@@ -550,6 +911,18 @@ hipError_t launch_conv_strided(const ConvCall &c, ConvRoute r, bool packed_given
     const long blocks = temporal ? (long)c.n * c.to * p.tiles : (long)c.n * c.to * c.ho * p.tiles;
     if (blocks <= 0) return hipSuccess;
     if (blocks > 0x7fffffffL) return hipErrorInvalidValue;
+    if (rows_route(c)) {
+        // one persistent workgroup per CU over the output rows of 63-column strips
+        p.tiles = (c.wo + RW_PT - 1) / RW_PT;
+        const long items = (long)c.n * c.to * p.tiles * c.ho;
+        if (items > 0x7fffffffL) return hipErrorInvalidValue;
+        const unsigned grid = (unsigned)(items < num_cus_strided() ? items : num_cus_strided());
+        if (p.gamma)
+            hipLaunchKernelGGL(strided_rows_kernel<true>, dim3(grid), dim3(RW_THREADS), 0, s, p, (int)items);
+        else
+            hipLaunchKernelGGL(strided_rows_kernel<false>, dim3(grid), dim3(RW_THREADS), 0, s, p, (int)items);
+        return hipGetLastError();
+    }
     const size_t lds = lds_bytes(c);
     const Layout l = layout_for(c.cout);
     if (temporal) return launch_mode<0, 64>(p, l, blocks, lds, s);
