@@ -619,8 +619,9 @@ def wl_downsample():
                         "height": h, "width": w, "out_frames": sum(touts), "out_height": ho,
                         "out_width": wo, "chunks": sizes, "batch": n, "fused_norm": FUSE_NORM},
                 kernel=kernel,
-                kernel_name=("strided_kernel<1, 64, 3, 2, 2, 12, true>" if FUSE_NORM
-                             else "strided_kernel<1, 64, 3, 2, 2, 12, false>"),
+                kernel_name=(L.wvc_conv3d_kernel_name(L.conv_desc(tuple(xs[1].shape), tuple(p["w_s"].shape),
+                                                                  L.WVC_BF16, **{k: v for k, v in sp_kw.items()}))
+                             .replace("<false>", "<true>" if FUSE_NORM else "<false>")),
                 kernel_units=k_bytes, kernel_bound="hbm", kernel_bytes=k_bytes,
                 kernel_flops=2 * 9 * c * c * 4 * ho * wo)
     return step, info

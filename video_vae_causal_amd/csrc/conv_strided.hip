@@ -857,6 +857,12 @@ bool strided_supports(const ConvCall &c) {
     return (size_t)c.cout * k_total(c) * 2 < ((size_t)1 << 31);
 }
 
+const char *strided_kernel_name(const ConvCall &c, bool norm) {
+    if (rows_route(c)) return norm ? "strided_rows_kernel<true>" : "strided_rows_kernel<false>";
+    if (is_temporal(c)) return "strided_kernel<0, 64, ...> (temporal stride)";
+    return norm ? "strided_kernel<1, ..., true>" : "strided_kernel<1, ..., false>";
+}
+
 size_t strided_packed_weight_bytes(const ConvCall &c) { return (size_t)c.cout * k_total(c) * 2; }
 
 size_t strided_workspace_bytes(const ConvCall &c, bool packed_given) {

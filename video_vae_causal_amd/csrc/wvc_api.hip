@@ -630,7 +630,9 @@ const char *wvc_conv3d_kernel_name(const wvc_conv3d_desc *d) {
     switch (pl.route) {
         case wvc::ConvRoute::Generic: snprintf(name, sizeof(name), "direct_conv_kernel"); break;
         case wvc::ConvRoute::FastTemporal:
-        case wvc::ConvRoute::FastSpatial2: snprintf(name, sizeof(name), "strided_kernel"); break;
+        case wvc::ConvRoute::FastSpatial2:
+            snprintf(name, sizeof(name), "%s", wvc::strided_kernel_name(pl.call, false));
+            break;
         default: wvc::igemm_kernel_name(pl.call, pl.route, name, sizeof(name)); break;
     }
     return name;

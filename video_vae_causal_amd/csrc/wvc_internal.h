@@ -93,6 +93,8 @@ enum class ConvRoute { Fast3x3x3, Fast1x1x1, FastTemporal, FastSpatial2, Generic
 bool strided_supports(const ConvCall &c);
 size_t strided_workspace_bytes(const ConvCall &c, bool packed_given);
 size_t strided_packed_weight_bytes(const ConvCall &c);
+// Name of the kernel launch_conv_strided launches (norm: the fused-norm form).
+const char *strided_kernel_name(const ConvCall &c, bool norm);
 hipError_t launch_strided_pack(const ConvCall &c, const void *w, void *packed, hipStream_t s);
 hipError_t launch_conv_strided(const ConvCall &c, ConvRoute r, bool packed_given, void *ws,
                                size_t ws_bytes, hipStream_t s);
