@@ -48,7 +48,8 @@
 //               the rolling cache update costs no extra pass over the frames.
 //   mapping   : workgroup ids are remapped so each XCD (own L2) receives a
 //               contiguous run of tiles: splits and channel tiles of one
-//               spatial tile, then its neighbours, share that XCD's L2.
+//               spatial tile, then (large grids) its other output frames,
+//               then its neighbours, share that XCD's L2.
 //
 // 8-bit variant (FP8): activations, cache and weights are OCP E4M3 codes (the
 // quantised Conv3D of "Cosmos3 Wan VAE", sections 7 and 9, in the format
@@ -298,24 +299,35 @@ __device__ __forceinline__ void igemm_body(const IgParams &p) {
     int L = Lcur;
     const int s = SPLIT ? L % p.S : 0;
     if (SPLIT) L /= p.S;
-    // Order of the logical tiles: channel tile fastest (large grids: the tiles
-    // of one spatial block share its halo in L2) or slowest (small grids: each
-    // XCD then works on one channel tile, so its weight slice stays in L2).
+    // Order of the logical tiles.  Small grids: channel tile slowest (each XCD
+    // then works on one channel tile, so its weight slice stays in L2), then
+    // column, row, frame.  Large grids: channel tile fastest, then frame, then
+    // column and row: the tiles an XCD runs at one time are the channel tiles
+    // of one spatial block over consecutive output frames, which read the
+    // same input-frame halos (each input frame feeds three output frames), so
+    // those halos are fetched once into that XCD's L2.
     auto decode = [&](int l, int &ct_, int &t_, int &n_, int &h0_, int &w0_) {
+        int tw_, th_;
         if (p.co_major) {
             const int per_ct = (int)(p.total / p.S) / p.co_tiles;
             ct_ = l / per_ct;
             l -= ct_ * per_ct;
+            tw_ = l % p.tiles_w;
+            l /= p.tiles_w;
+            th_ = l % p.tiles_h;
+            l /= p.tiles_h;
+            t_ = l % p.T;
+            n_ = l / p.T;
         } else {
             ct_ = l % p.co_tiles;
             l /= p.co_tiles;
+            t_ = l % p.T;
+            l /= p.T;
+            tw_ = l % p.tiles_w;
+            l /= p.tiles_w;
+            th_ = l % p.tiles_h;
+            n_ = l / p.tiles_h;
         }
-        const int tw_ = l % p.tiles_w;
-        l /= p.tiles_w;
-        const int th_ = l % p.tiles_h;
-        l /= p.tiles_h;
-        t_ = l % p.T;
-        n_ = l / p.T;
         h0_ = th_ * G::TH;
         w0_ = tw_ * TW;
     };
