@@ -123,10 +123,7 @@ class CausalConv3d:
             self.start(n, h, w)
         cin = self.cache.cin if self.frames else None
         cout = self.cache.cout if self.frames else None
-        layout = L.WVC_WEIGHT_PACKED if self.packed is not None else L.WVC_WEIGHT_STANDARD
-        d = L.conv_desc(tuple(x.shape), tuple(self.weight.shape), L._dtype_code(x.dtype),
-                        padding=self.padding, weight_layout=layout)
-        need = L.wvc_causal_conv3d_workspace_bytes(d)
+        need = self._ws_need(x)
         if need and (self.ws is None or self.ws.numel() < need):
             self.ws = torch.empty(need, dtype=torch.uint8, device=x.device)
         y = L.wvc_causal_conv3d_fwd(x, self.weight, self.bias, cin, cout, residual, y,
@@ -135,6 +132,17 @@ class CausalConv3d:
         if self.frames:
             self.cache.flip()
         return y
+
+    def _ws_need(self, x: torch.Tensor) -> int:
+        """Workspace bytes of a chunk of x's shape (asked once per shape)."""
+        key = (x.shape, x.dtype, x.device)
+        need = self.__dict__.setdefault("_needs", {}).get(key)
+        if need is None:
+            layout = L.WVC_WEIGHT_PACKED if self.packed is not None else L.WVC_WEIGHT_STANDARD
+            d = L.conv_desc(tuple(x.shape), tuple(self.weight.shape), L._dtype_code(x.dtype),
+                            padding=self.padding, weight_layout=layout)
+            need = self._needs[key] = L.wvc_causal_conv3d_workspace_bytes(d)
+        return need
 
     def caches(self) -> List[torch.Tensor]:
         if self.cache is None:
@@ -194,11 +202,19 @@ class ResBlock:
         if not _fits(self.c1, (n, c, CACHE_T, h, w)):
             self.start(n, h, w)
 
+    def _ws_need(self, x: torch.Tensor) -> int:
+        """Workspace bytes of a chunk of x's shape (asked once per shape)."""
+        key = (x.shape, x.dtype, x.device)
+        need = self.__dict__.setdefault("_needs", {}).get(key)
+        if need is None:
+            d = L.resblock_desc(tuple(x.shape), self.p["w1"].shape[0], L._dtype_code(x.dtype),
+                                self.eps, weights_packed=self.packed is not None)
+            need = self._needs[key] = L.wvc_resblock_workspace_bytes(d)
+        return need
+
     def __call__(self, x: torch.Tensor, y: Optional[torch.Tensor] = None) -> torch.Tensor:
         self._ensure(x)
-        d = L.resblock_desc(tuple(x.shape), self.p["w1"].shape[0], L._dtype_code(x.dtype), self.eps,
-                            weights_packed=self.packed is not None)
-        need = L.wvc_resblock_workspace_bytes(d)
+        need = self._ws_need(x)
         if self.ws is None or self.ws.numel() < need:
             self.ws = torch.empty(need, dtype=torch.uint8, device=x.device)
         y = L.wvc_resblock_fwd(x, self.p, self.c1.cin, self.c1.cout, self.c2.cin, self.c2.cout,
@@ -215,9 +231,7 @@ class ResBlock:
         return [self.c1.cin, self.c2.cin]
 
     def _half_ws(self, name: str, x: torch.Tensor) -> torch.Tensor:
-        d = L.resblock_desc(tuple(x.shape), self.p["w1"].shape[0], L._dtype_code(x.dtype), self.eps,
-                            weights_packed=self.packed is not None)
-        need = L.wvc_resblock_workspace_bytes(d)
+        need = self._ws_need(x)
         ws = self.__dict__.get(name)
         if ws is None or ws.numel() < need:
             ws = torch.empty(need, dtype=torch.uint8, device=x.device)
