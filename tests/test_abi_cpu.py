@@ -490,6 +490,31 @@ def test_block_binding_refuses_mismatched_buffers(host_binding):
         L.wvc_resblock_back(x, x, p, cache2_in=cl_host(torch, (1, c, 2, 6, 9)))
 
 
+def test_block_parameter_check_is_redone_when_the_set_changes(host_binding):
+    """A block's parameter set is checked in full once; later calls with the
+    same dict only compare its fingerprint, so a tensor swapped into the dict
+    (another shape, dtype or layout) is caught on the next call."""
+    torch = host_binding
+    c = 32
+    x = cl_host(torch, (1, c, 1, 6, 10))
+    vec = lambda n, dt=torch.bfloat16: torch.zeros(n, dtype=dt)
+    p = {"gamma1": vec(c), "w1": cl_host(torch, (c, c, 3, 3, 3)), "b1": vec(c), "gamma2": vec(c),
+         "w2": cl_host(torch, (c, c, 3, 3, 3)), "b2": vec(c)}
+    for _ in range(2):  # checked in full, then by fingerprint: both reach the launch
+        with pytest.raises(AssertionError, match="reached a launch"):
+            L.wvc_resblock_fwd(x, p)
+    for k, bad in (("w2", cl_host(torch, (c, c // 2, 3, 3, 3))),
+                   ("b1", vec(c, torch.float32)),
+                   ("w1", torch.zeros((c, c, 3, 3, 3), dtype=torch.bfloat16))):  # not channels-last
+        good = p[k]
+        p[k] = bad
+        with pytest.raises((ValueError, TypeError)):
+            L.wvc_resblock_fwd(x, p)
+        p[k] = good
+    with pytest.raises(AssertionError, match="reached a launch"):
+        L.wvc_resblock_fwd(x, p)
+
+
 def test_norm_upsample_e4m3_bindings_refuse_mismatched_buffers(host_binding):
     torch = host_binding
     x = cl_host(torch, (1, 32, 2, 6, 10))
