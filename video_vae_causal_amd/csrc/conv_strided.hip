@@ -410,10 +410,13 @@ __global__ void __launch_bounds__(256) strided_kernel(SParams p) {
 // Staging: before an item's MFMAs, the loads of the next item's two input
 // rows are issued (each row a contiguous run of 127 positions x 192 bytes in
 // memory; thread t loads 16-byte chunks t, t + 512, ...: coalesced).  After
-// the K loop they go to the ring rows the current item was the last to read;
-// with the fused norm, the staged positions are then normalised in place,
-// two threads per position (sum of squares with v_dot2_f32_bf16,
-// gamma/beta, SiLU, one rounding to bf16).  A strip's first item stages all three rows before its K loop.
+// the K loop they go to the ring rows the current item was the last to read.
+// With the fused norm, two threads share a position instead (48 channels
+// each) and normalise it in registers during the last K-steps of the current
+// item, between its MFMAs (sum of squares with v_dot2_f32_bf16 over the lane
+// pair, gamma/beta, SiLU, one rounding to bf16): the norm's VALU work runs
+// beside the matrix work, and the ring receives normalised values only.  A
+// strip's first item stages all three rows before its K loop.
 //
 // LDS row layout: the even input columns of a row at entries 13 s (s = column
 // / 2), the odd ones from entry 840 on.  A B-fragment read (16 consecutive
@@ -464,10 +467,13 @@ __global__ void __launch_bounds__(RW_THREADS) strided_rows_kernel(SParams p, int
         const uint4 bq = p.beta ? reinterpret_cast<const uint4 *>(p.beta)[tid >> 1] : make_uint4(0, 0, 0, 0);
         const uint32_t g0 = (tid & 1) ? gq.z : gq.x, g1 = (tid & 1) ? gq.w : gq.y;
         const uint32_t b0 = (tid & 1) ? bq.z : bq.x, b1 = (tid & 1) ? bq.w : bq.y;
-        gam_s[tid] = make_float4(bf16_to_f32(g0 & 0xffffu), bf16_to_f32(g0 >> 16), bf16_to_f32(g1 & 0xffffu),
-                                 bf16_to_f32(g1 >> 16));
-        bet_s[tid] = make_float4(bf16_to_f32(b0 & 0xffffu), bf16_to_f32(b0 >> 16), bf16_to_f32(b1 & 0xffffu),
-                                 bf16_to_f32(b1 >> 16));
+        // gamma and beta times -log2(e): the norm works on t = -log2(e) u
+        // (see norm_chunk)
+        constexpr float NL2E = -1.4426950408889634f;
+        gam_s[tid] = make_float4(NL2E * bf16_to_f32(g0 & 0xffffu), NL2E * bf16_to_f32(g0 >> 16),
+                                 NL2E * bf16_to_f32(g1 & 0xffffu), NL2E * bf16_to_f32(g1 >> 16));
+        bet_s[tid] = make_float4(NL2E * bf16_to_f32(b0 & 0xffffu), NL2E * bf16_to_f32(b0 >> 16),
+                                 NL2E * bf16_to_f32(b1 & 0xffffu), NL2E * bf16_to_f32(b1 >> 16));
     }
 
     // ---- weights: this wave's A fragments, loaded once
@@ -519,60 +525,89 @@ __global__ void __launch_bounds__(RW_THREADS) strided_rows_kernel(SParams p, int
         for (int k = 0; k < RW_PER; ++k)
             if (dst[k] >= 0) ring[dst[k]] = raw[k];
     };
-    // Fused norm of the staged positions, rows hs0 .. hs0 + rows - 1, in place
-    // in the ring: two threads per position (6 chunks = 48 channels each),
-    // their sums of squares combined across the lane pair.
-    auto normalise = [&](int hs0, int rows, int col0) __attribute__((always_inline)) {
-        if constexpr (NORM) {
-            typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-            constexpr int H8 = RW_C8 / 2;
-            for (int t2 = tid; t2 < 2 * rows * RW_COLS; t2 += RW_THREADS) {
-                const int pos = t2 >> 1, half = t2 & 1;
-                const int row = pos / RW_COLS, col = pos - row * RW_COLS;
-                const int hs = hs0 + row, ws = col0 + col;
-                const bool in = (unsigned)hs < (unsigned)p.h && (unsigned)ws < (unsigned)p.w;
-                uint4 *e = ring + ((hs + 3) % 3) * RW_ROW + rw_entry(col) + half * H8;
-                uint4 v[H8];
-                float ss = 0.f;
+    // NORM staging: two threads per position, thread t taking half h = t & 1
+    // of position pbase + t/2 (chunks 6h .. 6h+5 = channels 48h .. 48h+47),
+    // so that the norm's sum of squares needs only the lane pair and the
+    // staged values are normalised in registers before their one store to
+    // the ring.  A wave's load k then reads 16 of every 96 bytes of a
+    // contiguous run; its six loads together read the run whole.
+    constexpr int H8 = RW_C8 / 2;
+    const int half = tid & 1;
+    int ndst = -1;       // ring entry of this thread's first chunk, -1 when idle
+    bool nin = false;    // the position lies inside the frame
+    float nr = 0.f;      // its scale sqrt(C) / max(||v||, eps)
+    auto issue_pos = [&](int n_, int j_, int hs0, int col0, int pbase, int pend) __attribute__((always_inline)) {
+        const __amdgpu_buffer_rsrc_t fr = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint16_t *>(p.x + ((size_t)n_ * p.t + j_) * frame), (short)0, frame_bytes, 0x00020000);
+        int pos = pbase + (tid >> 1);
+        asm volatile("" : "+v"(pos));
+        const int row = pos / RW_COLS, col = pos - row * RW_COLS;
+        const int hs = hs0 + row, ws = col0 + col;
+        nin = pos < pend && (unsigned)hs < (unsigned)p.h && (unsigned)ws < (unsigned)p.w;
+        const uint32_t base = nin ? (uint32_t)(hs * p.w + ws) * 192u + (uint32_t)half * 96u : 0x80000000u;
 #pragma unroll
-                for (int k = 0; k < H8; ++k) {
-                    v[k] = e[k];
-                    ss = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, v[k].x),
-                                                         __builtin_bit_cast(bf16x2, v[k].x), ss, false);
-                    ss = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, v[k].y),
-                                                         __builtin_bit_cast(bf16x2, v[k].y), ss, false);
-                    ss = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, v[k].z),
-                                                         __builtin_bit_cast(bf16x2, v[k].z), ss, false);
-                    ss = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, v[k].w),
-                                                         __builtin_bit_cast(bf16x2, v[k].w), ss, false);
-                }
-                // lane pairs (2m, 2m+1) hold the two halves; both add in the
-                // same order (half 0 + half 1), so both get the same bits
-                const float other = __shfl_xor(ss, 1);
-                const float tot = half ? other + ss : ss + other;
-                const float r = p.norm_scale / fmaxf(sqrtf(tot), p.eps);
+        for (int k = 0; k < H8; ++k) {
+            const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(fr, (int)(base + 16u * k), 0, 0);
+            raw[k] = make_uint4(v.x, v.y, v.z, v.w);
+        }
+        ndst = pos < pend ? ((hs + 3) % 3) * RW_ROW + rw_entry(col) + half * H8 : -1;
+    };
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    auto norm_sum = [&]() __attribute__((always_inline)) {
+        float ss = 0.f;
 #pragma unroll
-                for (int k = 0; k < H8; ++k) {
-                    const float4 g0 = gam_s[2 * (half * H8 + k)], g1 = gam_s[2 * (half * H8 + k) + 1];
-                    const float4 b0 = bet_s[2 * (half * H8 + k)], b1 = bet_s[2 * (half * H8 + k) + 1];
-                    const float gg[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
-                    const float bb[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
-                    const uint32_t wd[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
-                    uint32_t o[4];
+        for (int k = 0; k < H8; ++k) {
+            ss = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, raw[k].x),
+                                                 __builtin_bit_cast(bf16x2, raw[k].x), ss, false);
+            ss = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, raw[k].y),
+                                                 __builtin_bit_cast(bf16x2, raw[k].y), ss, false);
+            ss = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, raw[k].z),
+                                                 __builtin_bit_cast(bf16x2, raw[k].z), ss, false);
+            ss = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, raw[k].w),
+                                                 __builtin_bit_cast(bf16x2, raw[k].w), ss, false);
+        }
+        // both lanes of the pair add half 0 + half 1, so both get the same bits
+        const float other = __shfl_xor(ss, 1);
+        const float tot = half ? other + ss : ss + other;
+        nr = p.norm_scale / fmaxf(sqrtf(tot), p.eps);
+    };
+    // Chunk k of this thread: gamma, beta, SiLU, one rounding.  With
+    // u = x r gamma + beta and t = -log2(e) u (gamma and beta are stored
+    // pre-scaled), SiLU(u) = u / (1 + e^-u) = t / (-log2(e) (1 + 2^t)): one
+    // fma, one exp2, one fma, one reciprocal and one multiply per element.
+    // Positions outside the frame are zeroed at the store (the conv's zero
+    // padding applies to the norm's output).
+    auto norm_chunk = [&](auto k_tag) __attribute__((always_inline)) {
+        constexpr int k = decltype(k_tag)::value;
+        const int c = half * H8 + k;
+        const float4 g0 = gam_s[2 * c], g1 = gam_s[2 * c + 1];
+        const float4 b0 = bet_s[2 * c], b1 = bet_s[2 * c + 1];
+        const float gg[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+        const float bb[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+        const uint32_t wd[4] = {raw[k].x, raw[k].y, raw[k].z, raw[k].w};
+        uint32_t o[4];
+        constexpr float NL2E = -1.4426950408889634f;
 #pragma unroll
-                    for (int d = 0; d < 4; ++d) {
-                        const float u0 = fmaf(bf16_to_f32(wd[d] & 0xffffu) * r, gg[2 * d], bb[2 * d]);
-                        const float u1 = fmaf(__uint_as_float(wd[d] & 0xffff0000u) * r, gg[2 * d + 1], bb[2 * d + 1]);
-                        o[d] = pack2_bf16(u0 * __builtin_amdgcn_rcpf(1.f + __expf(-u0)),
-                                          u1 * __builtin_amdgcn_rcpf(1.f + __expf(-u1)));
-                    }
-                    e[k] = in ? make_uint4(o[0], o[1], o[2], o[3]) : make_uint4(0u, 0u, 0u, 0u);
-                    __builtin_amdgcn_sched_barrier(0);  // one chunk at a time: few live values
-                }
+        for (int d = 0; d < 4; ++d) {
+            const float t0 = fmaf(bf16_to_f32(wd[d] & 0xffffu) * nr, gg[2 * d], bb[2 * d]);
+            const float t1 = fmaf(__uint_as_float(wd[d] & 0xffff0000u) * nr, gg[2 * d + 1], bb[2 * d + 1]);
+            const float d0 = fmaf(__builtin_amdgcn_exp2f(t0), NL2E, NL2E);
+            const float d1 = fmaf(__builtin_amdgcn_exp2f(t1), NL2E, NL2E);
+            o[d] = pack2_bf16(t0 * __builtin_amdgcn_rcpf(d0), t1 * __builtin_amdgcn_rcpf(d1));
+        }
+        raw[k] = make_uint4(o[0], o[1], o[2], o[3]);
+    };
+    auto store_pos = [&]() __attribute__((always_inline)) {
+        if (ndst >= 0) {
+            if (nin) {
+#pragma unroll
+                for (int k = 0; k < H8; ++k) ring[ndst + k] = raw[k];
+            } else {
+#pragma unroll
+                for (int k = 0; k < H8; ++k) ring[ndst + k] = make_uint4(0u, 0u, 0u, 0u);
             }
         }
     };
-
     // Epilogue of an item, finished one item late, during the next item's
     // MFMAs: block wq of the finished item, the four quarters' partial sums
     // in quarter order (its own from registers), + bias, + residual (loaded
@@ -625,19 +660,29 @@ __global__ void __launch_bounds__(RW_THREADS) strided_rows_kernel(SParams p, int
                 prev_res[f] = *reinterpret_cast<const uint2 *>(p.res + prev_obase + wc * 48 + f * 16 + lg * 4);
         }
         if (fresh) {  // all three rows, in two batches of loads
-            for (int qb = 0; qb < 3 * RW_ROWCH; qb += RW_THREADS * RW_PER) {
-                issue(n, j, r0, col0, qb, 3 * RW_ROWCH);
-                store();
-            }
-            if (NORM) {
-                __syncthreads();
-                normalise(r0, 3, col0);
+            if constexpr (NORM) {
+                for (int pb = 0; pb < 3 * RW_COLS; pb += RW_THREADS / 2) {
+                    issue_pos(n, j, r0, col0, pb, 3 * RW_COLS);
+                    norm_sum();
+                    static_for<H8>([&](auto k) { norm_chunk(k); });
+                    store_pos();
+                }
+            } else {
+                for (int qb = 0; qb < 3 * RW_ROWCH; qb += RW_THREADS * RW_PER) {
+                    issue(n, j, r0, col0, qb, 3 * RW_ROWCH);
+                    store();
+                }
             }
             __syncthreads();
         }
         // next item continues this strip: its two new rows r0+3, r0+4
         const bool next = i + 1 < i_end && oh + 1 < p.ho;
-        if (next) issue(n, j, r0 + 3, col0, 0, 2 * RW_ROWCH);
+        if (next) {
+            if constexpr (NORM)
+                issue_pos(n, j, r0 + 3, col0, 0, 2 * RW_COLS);
+            else
+                issue(n, j, r0 + 3, col0, 0, 2 * RW_ROWCH);
+        }
 
         // ---- K loop over this wave's quarter.  Each quarter is its own
         // compile-time instance, so every B-fragment address is one of three
@@ -677,8 +722,8 @@ __global__ void __launch_bounds__(RW_THREADS) strided_rows_kernel(SParams p, int
 #pragma unroll
                     for (int f = 0; f < 3; ++f)
                         acc[f][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[m][f], B[cur][b], acc[f][b], 0, 0, 0);
-                if constexpr (m >= 1 && m <= 3) {
-                    if (epi) epi_piece(m - 1);
+                if constexpr (m <= 2) {
+                    if (epi) epi_piece(m);
                 }
                 __builtin_amdgcn_sched_barrier(0);
             });
@@ -688,6 +733,15 @@ __global__ void __launch_bounds__(RW_THREADS) strided_rows_kernel(SParams p, int
             case 1: kloop(Int<1>{}); break;
             case 2: kloop(Int<2>{}); break;
             default: kloop(Int<3>{}); break;
+        }
+        // NORM: the next item's positions, normalised in registers before the
+        // barrier, so that a wave done with its K-steps runs this VALU work
+        // while the waves still in theirs keep the matrix pipe busy
+        if constexpr (NORM) {
+            if (next) {
+                norm_sum();
+                static_for<H8>([&](auto k) { norm_chunk(k); });
+            }
         }
         __syncthreads();  // K loops and the previous epilogue done: red free, ring rows r0, r0+1 free
         // partial sums of the blocks other waves finish
@@ -704,10 +758,10 @@ __global__ void __launch_bounds__(RW_THREADS) strided_rows_kernel(SParams p, int
         prev_st = pp_mine < RW_PT && ct * RW_PT + pp_mine < p.wo;
         have_prev = true;
         if (next) {
-            store();
-            if (NORM) {
-                __syncthreads();
-                normalise(r0 + 3, 2, col0);
+            if constexpr (NORM) {
+                store_pos();
+            } else {
+                store();
             }
         }
         __syncthreads();  // new rows and partial sums in
