@@ -99,7 +99,7 @@ def parse():
                     help="only run 5 plain device copies of MIB MiB (bf16) and exit: the known-size "
                          "kernel that scales rocprofv3's FETCH_SIZE / WRITE_SIZE counters")
     ap.add_argument("--operands", choices=("random", "zero"), default="random",
-                    help="zero: layer_384_240x416 only, with all-zero input and weights -- a diagnostic "
+                    help="zero: layer_384_240x416 and layer_96_480x832 only, with all-zero input and weights -- a diagnostic "
                          "that keeps every instruction, address and wait of the conv and removes the "
                          "operands' bit toggling, to separate the chip's clock response from the "
                          "schedule; its numbers are not the metric")
@@ -418,6 +418,9 @@ def wl_layer96():
     ys = [y[:, :, s:s + k] for s, k in zip(starts, sizes)]
 
     wss = [conv_workspace(hs[i], wt, packed=True) for i in range(len(sizes))]
+    if OPERANDS == "zero":
+        for a in (x, g, wt, b, hbuf):
+            a.zero_()
     wtp = L.wvc_conv3d_pack_weights(wt)
 
     def step():
@@ -438,7 +441,8 @@ def wl_layer96():
 
     info = dict(workload="layer_96_480x832", conv_flops=conv_flops, latent_frames=t,
                 config={"workload": "layer_96_480x832", "channels": c, "frames": t,
-                        "height": h, "width": w, "chunks": sizes, "batch": n},
+                        "height": h, "width": w, "chunks": sizes, "batch": n,
+                        **({"operands": "zero (diagnostic)"} if OPERANDS == "zero" else {})},
                 kernel=kernel, kernel_name=conv_kernel_name(hs[1], wt),
                 kernel_units=acc.conv_flops(n, 4, h, w, c, c), kernel_bound="mfma",
                 kernel_bytes=acc.conv_launch_bytes(n, 4, h, w, c, c),
@@ -1030,8 +1034,9 @@ def main():
               "(the library runs on one GPU and has no multi-GPU sharding)", file=sys.stderr)
         sys.exit(2)
     if args.operands == "zero":
-        if args.workload != "layer_384_240x416":
-            print("--operands zero is a diagnostic of the layer_384_240x416 workload only", file=sys.stderr)
+        if args.workload not in ("layer_384_240x416", "layer_96_480x832"):
+            print("--operands zero is a diagnostic of the layer_384_240x416 and layer_96_480x832 "
+                  "workloads only", file=sys.stderr)
             sys.exit(2)
         args.no_cpu_baseline = True  # the oracle's sample is random data
     if args.pipeline == "auto":

@@ -181,6 +181,33 @@ int wvc_causal_conv3d_fwd_noalloc(const wvc_conv3d_desc *d, const void *x, const
 size_t wvc_causal_conv3d_workspace_bytes(const wvc_conv3d_desc *d);
 
 /*
+ * A causal conv followed by the RMS norm + SiLU of the layer it feeds
+ * ([P1] 10.3 for the conv and the residual block, 10.2 and 10.4 for the norm
+ * and SiLU: a block's conv1 feeds norm2, its conv2 plus the shortcut feeds
+ * the next block's norm1):
+ *   y = round_bf16(conv_d(x | cache_in) + bias + residual)   (C_out channels)
+ *   h = round_bf16(silu(rmsnorm(y; gamma, beta, eps)))
+ * y is bit for bit what wvc_causal_conv3d_fwd stores and h what
+ * wvc_rmsnorm_silu stores for that y.  Arguments as for wvc_causal_conv3d_fwd,
+ * plus gamma [C_out], beta [C_out] or NULL, eps > 0 and the output
+ * h [N, C_out, t_out, h_out, w_out]; y may be NULL when only h is wanted.
+ * When the conv's plan splits K, its split sums go straight into the norm
+ * kernel, which adds them in split order, then the bias and the residual,
+ * rounds y once (storing it when y is given) and normalises it: the split-K
+ * reduce and the norm are one kernel.  bf16 only, C_out % 8 == 0 and
+ * C_out <= 2048 (WVC_ERR_UNSUPPORTED otherwise).  The workspace must hold
+ * wvc_causal_conv3d_norm_workspace_bytes(d) bytes (the conv's workspace plus
+ * room for y); its contents on entry do not matter.  Written buffers (y, h,
+ * cache_out, workspace) may not overlap the others (WVC_ERR_ALIAS).
+ */
+int wvc_causal_conv3d_norm_fwd(const wvc_conv3d_desc *d, const void *x, const void *cache_in,
+                               void *cache_out, const void *weight, const void *bias,
+                               const void *residual, void *y, const void *gamma, const void *beta,
+                               float eps, void *h, void *workspace, size_t workspace_bytes,
+                               void *stream);
+size_t wvc_causal_conv3d_norm_workspace_bytes(const wvc_conv3d_desc *d);
+
+/*
  * Weights in MFMA fragment order.  The fast routes read each wave's weight
  * fragment (M output channels x one MFMA K-step, M = 32 or 16 by C_out) as
  * one contiguous 1 KiB block; wvc_conv3d_pack_weights writes that order once,

@@ -41,6 +41,7 @@ EXPORTED = (
     "wvc_causal_conv3d_e4m3_fwd", "wvc_quantize_e4m3", "wvc_quantize_rows_e4m3",
     "wvc_rmsnorm_silu_e4m3", "wvc_rmsnorm_silu_conv3d_fwd", "wvc_resblock_e4m3_fwd",
     "wvc_resblock_e4m3_workspace_bytes", "wvc_conv3d_kernel_name", "wvc_causal_conv3d_fwd_noalloc",
+    "wvc_causal_conv3d_norm_fwd", "wvc_causal_conv3d_norm_workspace_bytes",
 )
 
 
@@ -106,6 +107,11 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.wvc_causal_conv3d_fwd_noalloc.restype = i
     lib.wvc_causal_conv3d_workspace_bytes.argtypes = [dptr]
     lib.wvc_causal_conv3d_workspace_bytes.restype = sz
+    lib.wvc_causal_conv3d_norm_fwd.argtypes = [dptr, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                               ctypes.c_float, vp, vp, sz, vp]
+    lib.wvc_causal_conv3d_norm_fwd.restype = i
+    lib.wvc_causal_conv3d_norm_workspace_bytes.argtypes = [dptr]
+    lib.wvc_causal_conv3d_norm_workspace_bytes.restype = sz
     lib.wvc_conv3d_kernel_name.argtypes = [dptr]
     lib.wvc_conv3d_kernel_name.restype = ctypes.c_char_p
     lib.wvc_conv3d_cache_frames.argtypes = [dptr]
@@ -350,6 +356,14 @@ def wvc_conv3d_packed_weight_bytes(w_shape, dtype=torch.bfloat16, padding=(1, 1)
 _packed_bytes_shared = _memo(wvc_conv3d_packed_weight_bytes)
 
 
+@_memo
+def _norm_ws_shared(x_shape, w_shape, code, padding, layout, device) -> int:
+    """wvc_causal_conv3d_norm_workspace_bytes of a unit-stride conv, asked once
+    per shape and device (the size depends on the device's CU count)."""
+    return wvc_causal_conv3d_norm_workspace_bytes(
+        conv_desc(x_shape, w_shape, code, padding=padding, weight_layout=layout))
+
+
 def wvc_conv3d_pack_weights(weight: torch.Tensor, padding=(1, 1), stride=(1, 1, 1),
                             pad_extra=(0, 0)) -> torch.Tensor:
     """Weights [C_out, C_in, kT, kH, kW] (channels_last_3d) -> their packed MFMA
@@ -399,6 +413,49 @@ def wvc_causal_conv3d_fwd(x: torch.Tensor, weight: torch.Tensor, bias: Optional[
                                       _ptr(wsrc), _ptr(bias), _ptr(residual), _ptr(y),
                                       _ptr(workspace), ws_bytes, _stream(x)))
     return y
+
+
+def wvc_causal_conv3d_norm_workspace_bytes(d: ConvDesc) -> int:
+    v = load().wvc_causal_conv3d_norm_workspace_bytes(ctypes.byref(d))
+    if v == ctypes.c_size_t(-1).value:
+        raise WvcError(WVC_ERR_ARG, load().wvc_last_error().decode())
+    return v
+
+
+def wvc_causal_conv3d_norm_fwd(x: torch.Tensor, weight: torch.Tensor, gamma: torch.Tensor,
+                               bias: Optional[torch.Tensor] = None,
+                               beta: Optional[torch.Tensor] = None, eps: float = 1e-12,
+                               cache_in: Optional[torch.Tensor] = None,
+                               cache_out: Optional[torch.Tensor] = None,
+                               residual: Optional[torch.Tensor] = None,
+                               y: Optional[torch.Tensor] = None, h: Optional[torch.Tensor] = None,
+                               padding=(1, 1), workspace: Optional[torch.Tensor] = None,
+                               packed_weight: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Conv, then the RMS norm + SiLU of the layer it feeds (see
+    wvc_causal_conv3d_norm_fwd in include/wvc.h): y = conv(x) + bias + residual
+    (stored only when ``y`` is given), h = SiLU(norm(y)).  Returns h
+    (allocated if not given)."""
+    d, out_shape, wsrc = _conv_checks(x, weight, bias, cache_in, cache_out, residual, y, (1, 1, 1),
+                                      padding, (1, 1, 1), 1, packed_weight, (0, 0), 0)
+    c_out = out_shape[1]
+    _need_exact(gamma, "gamma", (c_out,), x.dtype, x.device)
+    if gamma is None:
+        raise ValueError("gamma must be given")
+    _need_exact(beta, "beta", (c_out,), x.dtype, x.device)
+    _need_exact(h, "h", out_shape, x.dtype, x.device)
+    if h is None:
+        h = empty_cl(out_shape, x.dtype, x.device)
+    if workspace is None:
+        need = _norm_ws_shared(tuple(x.shape), tuple(weight.shape), _dtype_code(x.dtype),
+                               tuple(padding), d.weight_layout, x.device)
+    if workspace is None and need:  # contents on entry do not matter
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(load().wvc_causal_conv3d_norm_fwd(ctypes.byref(d), _ptr(x), _ptr(cache_in),
+                                             _ptr(cache_out), _ptr(wsrc), _ptr(bias), _ptr(residual),
+                                             _ptr(y), _ptr(gamma), _ptr(beta), float(eps), _ptr(h),
+                                             _ptr(workspace), ws_bytes, _stream(x)))
+    return h
 
 
 def wvc_causal_conv3d_fwd_noalloc(x: torch.Tensor, weight: torch.Tensor, y: torch.Tensor,

@@ -90,11 +90,14 @@ struct Partials {
     const uint4 *bias;  // [C] bf16, or nullptr
     const float4 *wscale = nullptr;  // 8-bit conv: [C] weight scales (sum *= xscale * wscale)
     float xscale = 1.f;
+    const uint4 *res = nullptr;  // [positions * C] bf16 residual added after the bias, or nullptr
+    uint4 *xstore = nullptr;     // where the rounded x is also stored, or nullptr
 };
 
 // FROM_PARTS: the input chunk is not read from x but built from partial sums,
-// x = round_bf16(sum over splits in order + bias), bit for bit what the
-// split-K reduce kernel stores (bf16 only).
+// x = round_bf16(sum over splits in order + bias + residual), bit for bit
+// what the split-K reduce kernel stores (bf16 only); pp.xstore receives that
+// x as well when given.
 // OUT8: the result is stored as E4M3 codes of fl32(y * qr), 8 bytes per chunk
 // of 8 channels (bf16 input only): the quantised conv's input written by the
 // norm itself, half the bytes of a bf16 store.
@@ -173,7 +176,14 @@ __global__ void __launch_bounds__(256) rmsnorm_flat_kernel(const uint4 *__restri
 #pragma unroll
                     for (int e = 0; e < 8; ++e) v[e] += bb[e];
                 }
+                if (pp.res) {
+                    float rr[8];
+                    V::unpack(pp.res[pos0 * cpp + f], rr);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) v[e] += rr[e];
+                }
                 raw[k] = V::pack(v);
+                if (pp.xstore) pp.xstore[pos0 * cpp + f] = raw[k];
             }
         }
     } else {
@@ -330,7 +340,7 @@ hipError_t launch_rmsnorm_silu_from_partials(const ConvPartials &pp, const void 
                                              const void *gamma, const void *beta, void *y,
                                              long positions, int c, float eps, int apply_silu,
                                              hipStream_t s, const float *wscale, float xscale,
-                                             float out_qr) {
+                                             float out_qr, const void *residual, void *xstore) {
     if (positions <= 0) return hipSuccess;
     const int cpp = c / 8;
     if (c % 8 != 0 || cpp > FLAT_MAX_CPP || pp.S < 1) return hipErrorInvalidValue;
@@ -340,7 +350,8 @@ hipError_t launch_rmsnorm_silu_from_partials(const ConvPartials &pp, const void 
     const long blocks = (positions + P - 1) / P;
     if (blocks > 0x7fffffffL) return hipErrorInvalidValue;
     const Partials q{pp.part, pp.stride, pp.S, static_cast<const uint4 *>(bias),
-                     reinterpret_cast<const float4 *>(wscale), xscale};
+                     reinterpret_cast<const float4 *>(wscale), xscale,
+                     static_cast<const uint4 *>(residual), static_cast<uint4 *>(xstore)};
     if (out_qr > 0.f)  // 8-bit output: codes of fl32(y * out_qr)
         hipLaunchKernelGGL((rmsnorm_flat_kernel<true, 1, false, true, true>), dim3((unsigned)blocks),
                            dim3(256), 0, s, nullptr, static_cast<const uint4 *>(gamma),

@@ -536,6 +536,75 @@ size_t wvc_causal_conv3d_workspace_bytes(const wvc_conv3d_desc *d) {
     return route_ws_bytes(pl, d->weight_layout == WVC_WEIGHT_PACKED);
 }
 
+// ---- conv, then the next layer's RMS norm + SiLU
+//
+// Workspace: [the conv's workspace][room for y when the caller passes none].
+size_t wvc_causal_conv3d_norm_workspace_bytes(const wvc_conv3d_desc *d) {
+    ConvPlan pl;
+    if (plan_conv(d, &pl, /*count=*/false)) return (size_t)-1;
+    return align256(route_ws_bytes(pl, d->weight_layout == WVC_WEIGHT_PACKED)) + align256(pl.y_bytes);
+}
+
+int wvc_causal_conv3d_norm_fwd(const wvc_conv3d_desc *d, const void *x, const void *cache_in,
+                               void *cache_out, const void *weight, const void *bias,
+                               const void *residual, void *y, const void *gamma, const void *beta,
+                               float eps, void *h, void *workspace, size_t workspace_bytes,
+                               void *stream) {
+    ConvPlan pl;
+    int rc = plan_conv(d, &pl, /*count=*/false);  // conv_fwd below counts the call
+    if (rc) return rc;
+    if (d->dtype != WVC_BF16) {
+        g_rejected++;
+        return fail(WVC_ERR_UNSUPPORTED, "the conv + norm call exists for WVC_BF16 only");
+    }
+    if (d->c_out % 8 != 0 || d->c_out > 2048) {
+        g_rejected++;
+        return fail(WVC_ERR_UNSUPPORTED, "the conv + norm call needs C_out %% 8 == 0 and C_out <= 2048");
+    }
+    if (!gamma) return fail(WVC_ERR_ARG, "gamma is NULL");
+    if (!(eps > 0.f)) return fail(WVC_ERR_ARG, "eps must be > 0");
+    const long positions = (long)d->n * pl.call.to * pl.call.ho * pl.call.wo;
+    if (d->t > 0 && positions > 0 && !h) return fail(WVC_ERR_ARG, "h is NULL");
+    if (!ws_ok(workspace, workspace_bytes)) return fail(WVC_ERR_ARG, "workspace is NULL but workspace_bytes > 0");
+    const size_t conv_need = align256(route_ws_bytes(pl, d->weight_layout == WVC_WEIGHT_PACKED));
+    const size_t need = conv_need + align256(pl.y_bytes);
+    if (workspace_bytes < need)
+        return fail(WVC_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, need);
+    const Buf bufs[] = {
+        {x, pl.x_bytes, false, "x"},
+        {cache_in, pl.cache_bytes, false, "cache_in"},
+        {cache_out, pl.cache_bytes, true, "cache_out"},
+        {residual, pl.y_bytes, false, "residual"},
+        {y, pl.y_bytes, true, "y"},
+        {gamma, (size_t)d->c_out * 2, false, "gamma"},
+        {beta, (size_t)d->c_out * 2, false, "beta"},
+        {h, pl.y_bytes, true, "h"},
+        {workspace, workspace_bytes, true, "workspace"},
+    };
+    rc = check_aliasing(bufs, 9);
+    if (rc) return rc;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    char *ws = static_cast<char *>(workspace);
+    void *yy = y ? y : ws + conv_need;
+    // On a split-K plan the reduce is fused into the norm: the norm kernel adds
+    // the partial sums in split order, the bias and the residual, rounds y
+    // once (storing it when y is given) and normalises that rounded value.
+    const bool fuse = aligned(gamma, 16) && aligned(beta, 16) && aligned(bias, 16) &&
+                      aligned(residual, 16) && aligned(y, 16) && aligned(h, 16);
+    wvc::ConvPartials parts;
+    if ((rc = conv_fwd(d, x, cache_in, cache_out, weight, bias, residual, yy, ws, conv_need, s,
+                       fuse ? &parts : nullptr)))
+        return rc;
+    if (parts.S > 1)
+        return hip_status(wvc::launch_rmsnorm_silu_from_partials(parts, bias, gamma, beta, h, positions,
+                                                                 d->c_out, eps, 1, s, nullptr, 1.f, 0.f,
+                                                                 residual, y),
+                          "norm launch");
+    if (d->t == 0 || positions == 0) return WVC_OK;
+    return norm_fwd(yy, gamma, beta, h, d->n, d->c_out, pl.call.to, pl.call.ho, pl.call.wo, d->dtype,
+                    eps, 1, s);
+}
+
 size_t wvc_conv3d_packed_weight_bytes(const wvc_conv3d_desc *d) {
     ConvPlan pl;
     if (plan_conv(d, &pl, /*count=*/false)) return (size_t)-1;

@@ -48,6 +48,18 @@ def _cached_buf(bufs: Dict[str, torch.Tensor], name: str, shape, like: torch.Ten
     return b
 
 
+def _norm_workspace(ws: Optional[torch.Tensor], x: torch.Tensor, weight: torch.Tensor, padding,
+                    packed: Optional[torch.Tensor]) -> torch.Tensor:
+    """A workspace for wvc_causal_conv3d_norm_fwd on chunks of x's shape:
+    ``ws`` when it is large enough, else a new one."""
+    layout = L.WVC_WEIGHT_PACKED if packed is not None else L.WVC_WEIGHT_STANDARD
+    need = L._norm_ws_shared(tuple(x.shape), tuple(weight.shape), L._dtype_code(x.dtype),
+                             tuple(padding), layout, x.device)
+    if ws is None or ws.numel() < need:
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    return ws
+
+
 class _PingPong:
     """A layer's cache pair.  After ``reset()`` the cache is *fresh*: the next
     chunk passes ``cache_in = NULL``, which the library reads as zero causal
@@ -132,6 +144,25 @@ class CausalConv3d:
         if self.frames:
             self.cache.flip()
         return y
+
+    def norm_into(self, x: torch.Tensor, y: Optional[torch.Tensor], gamma: torch.Tensor,
+                  beta: Optional[torch.Tensor], eps: float, h: torch.Tensor,
+                  residual: Optional[torch.Tensor] = None) -> torch.Tensor:
+        """The conv into y (skipped when None) and the RMS norm + SiLU of the
+        layer it feeds into h, as one library call (wvc_causal_conv3d_norm_fwd:
+        a split-K conv's reduce runs inside the norm kernel)."""
+        n, c, _, hh, ww = x.shape
+        if self.frames and not _fits(self.cache, (n, c, self.frames, hh, ww)):
+            self.start(n, hh, ww)
+        cin = self.cache.cin if self.frames else None
+        cout = self.cache.cout if self.frames else None
+        self.nws = _norm_workspace(self.__dict__.get("nws"), x, self.weight, self.padding, self.packed)
+        L.wvc_causal_conv3d_norm_fwd(x, self.weight, gamma, self.bias, beta, eps, cin, cout, residual,
+                                     y, h, padding=self.padding, workspace=self.nws,
+                                     packed_weight=self.packed)
+        if self.frames:
+            self.cache.flip()
+        return h
 
     def _ws_need(self, x: torch.Tensor) -> int:
         """Workspace bytes of a chunk of x's shape (asked once per shape)."""
@@ -253,6 +284,38 @@ class ResBlock:
             raise ValueError("back() of a chunk whose front() ran at another size")
         L.wvc_resblock_back(h2, x, self.p, self.c2.cin, self.c2.cout, y=y, eps=self.eps,
                             workspace=self._half_ws("ws_back", x), packed=self.packed)
+        self.c2.flip()
+        return y
+
+    def front_from_h1(self, h1: torch.Tensor, h2: torch.Tensor) -> torch.Tensor:
+        """First half given h1 = SiLU(norm1(x)), computed by the layer before
+        (wvc_causal_conv3d_norm_fwd): conv1 + norm2 into h2; advances cache1."""
+        self._ensure(h1)
+        p, pk = self.p, self.packed
+        self.ws_f1 = _norm_workspace(self.__dict__.get("ws_f1"), h1, p["w1"], (1, 1),
+                                     None if pk is None else pk["w1"])
+        L.wvc_causal_conv3d_norm_fwd(h1, p["w1"], p["gamma2"], p.get("b1"), p.get("beta2"), self.eps,
+                                     self.c1.cin, self.c1.cout, None, None, h2, workspace=self.ws_f1,
+                                     packed_weight=None if pk is None else pk["w1"])
+        self.c1.flip()
+        return h2
+
+    def back_norm(self, h2: torch.Tensor, x: torch.Tensor, y: torch.Tensor, gamma: torch.Tensor,
+                  beta: Optional[torch.Tensor], eps: float, h_next: torch.Tensor) -> torch.Tensor:
+        """Second half of an identity-shortcut block, y = conv2(h2) + x, and the
+        next block's norm1 + SiLU of y into h_next, in one library call;
+        advances cache2."""
+        if self.p.get("w_short") is not None:
+            raise ValueError("back_norm covers the identity-shortcut block")
+        n, _, _, hh, ww = x.shape
+        if not _fits(self.c2, (n, self.p["w1"].shape[0], CACHE_T, hh, ww)):
+            raise ValueError("back_norm() of a chunk whose front ran at another size")
+        p, pk = self.p, self.packed
+        self.ws_b1 = _norm_workspace(self.__dict__.get("ws_b1"), h2, p["w2"], (1, 1),
+                                     None if pk is None else pk["w2"])
+        L.wvc_causal_conv3d_norm_fwd(h2, p["w2"], gamma, p.get("b2"), beta, eps, self.c2.cin,
+                                     self.c2.cout, x, y, h_next, workspace=self.ws_b1,
+                                     packed_weight=None if pk is None else pk["w2"])
         self.c2.flip()
         return y
 
@@ -446,9 +509,54 @@ class DecoderStack(Stream):
         recorded graph names the same memory every time)."""
         return _cached_buf(self.__dict__.setdefault("_bufs", {}), name, shape, like)
 
+    def _fusable(self) -> bool:
+        """Every block has an identity shortcut and bf16 parameters, so each
+        conv can hand its output straight to the next norm
+        (wvc_causal_conv3d_norm_fwd)."""
+        return all(isinstance(rb, ResBlock) and rb.p.get("w_short") is None and
+                   rb.p["w1"].dtype == torch.bfloat16 for rb in self.rbs) and \
+            isinstance(self.conv_in, CausalConv3d) and isinstance(self.conv_up, CausalConv3d)
+
     def stages(self, x: torch.Tensor, out: torch.Tensor, buf) -> List[Callable[[], object]]:
         """The chunk as a list of stages (each a few library calls); the
-        intermediates come from ``buf(name, shape, like)``."""
+        intermediates come from ``buf(name, shape, like)``.
+
+        Each conv that feeds a norm computes that norm too: conv_in and conv_up
+        the first block's norm1, a block's conv1 its norm2, the first block's
+        conv2 (plus its input) the second block's norm1.  The stages are those
+        of the layer-by-layer composition, bitwise, with four norm kernels and
+        four split-K reduces fewer per chunk."""
+        if not self._fusable():
+            return self._stages_layerwise(x, out, buf)
+        n, _, t, h, w = x.shape
+        c = self.conv_in.weight.shape[0]
+        lo, hi = (n, c, t, h, w), (n, c, t, 2 * h, 2 * w)
+        a_in, a0, a1 = buf("in", lo, x), buf("rb0", lo, x), buf("rb1", lo, x)
+        up, a_up, a2 = buf("up", hi, x), buf("conv_up", hi, x), buf("rb2", hi, x)
+        h1 = [buf(f"rb{k}.h1", lo if k < 2 else hi, x) for k in range(4)]
+        h2 = [buf(f"rb{k}.h2", lo if k < 2 else hi, x) for k in range(4)]
+        rb = self.rbs
+
+        def norm1(k):
+            return rb[k].p["gamma1"], rb[k].p.get("beta1"), rb[k].eps
+
+        return [
+            lambda: self.conv_in.norm_into(x, a_in, *norm1(0), h1[0]),
+            lambda: rb[0].front_from_h1(h1[0], h2[0]),
+            lambda: rb[0].back_norm(h2[0], a_in, a0, *norm1(1), h1[1]),
+            lambda: rb[1].front_from_h1(h1[1], h2[1]),
+            lambda: rb[1].back(h2[1], a0, a1),
+            lambda: L.wvc_upsample_nearest2x(a1, y=up),
+            lambda: self.conv_up.norm_into(up, a_up, *norm1(2), h1[2]),
+            lambda: rb[2].front_from_h1(h1[2], h2[2]),
+            lambda: rb[2].back_norm(h2[2], a_up, a2, *norm1(3), h1[3]),
+            lambda: rb[3].front_from_h1(h1[3], h2[3]),
+            lambda: rb[3].back(h2[3], a2, out),
+        ]
+
+    def _stages_layerwise(self, x: torch.Tensor, out: torch.Tensor, buf) -> List[Callable[[], object]]:
+        """The chunk layer by layer: each layer's own calls (its norm1 inside
+        the block call)."""
         n, _, t, h, w = x.shape
         c = self.conv_in.weight.shape[0]
         lo, hi = (n, c, t, h, w), (n, c, t, 2 * h, 2 * w)
