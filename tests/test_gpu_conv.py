@@ -55,24 +55,27 @@ def test_conv3x3x3_bf16_vs_oracle(cin, cout, t, h, w):
 
 
 @pytest.mark.parametrize("cin,cout,t,h,w,tw", [
-    (96, 192, 3, 100, 150, 32),  # two channel tiles, ragged rows and columns
-    (64, 64, 4, 128, 200, 16),
+    (96, 192, 3, 100, 150, 32),  # two channel tiles, ragged rows and columns; 9 stages (odd)
+    (64, 64, 4, 128, 200, 16),   # 6 stages (even)
     (96, 96, 8, 2048, 8, 8),     # 8-wide tiles (one per row band), 512 tiles
     (64, 64, 8, 2048, 8, 8),
+    (32, 96, 4, 128, 256, 32),   # 3 stages: only the odd last stage
+    (48, 64, 3, 130, 260, 32),   # a half-filled channel block (channels past C_in read zero)
 ])
-def test_conv3x3x3_persistent_workgroups_vs_oracle(cin, cout, t, h, w, tw):
-    """Grids of 16x16 MFMA tiles with more tiles than CUs and no split of K run
-    persistent workgroups (several tiles each, the next tile's halo fetched
-    during the current one).  The library names the kernel it launches; the
-    case must reach the persistent kernel at the expected tile width."""
+def test_conv3x3x3_two_waves_per_simd_vs_oracle(cin, cout, t, h, w, tw):
+    """Whole-K grids of 16x16 MFMA tiles run two workgroups per CU, two waves
+    per SIMD: two weight row sets that alternate while the kernel rows cycle
+    through three (two stages per loop iteration, then an odd last stage), and
+    the B fragments in a 3-slot ring.  The library names the kernel it
+    launches; the case must reach that kernel at the expected tile width."""
     x, wt, b, cache = conv_case(cin, cout, t, h, w, seed=cin + cout + h + 1)
     d = L.conv_desc(x.shape, wt.shape, L.WVC_BF16)
     name = L.wvc_conv3d_kernel_name(d)
-    print(f"[case] conv3 persistent cin={cin} cout={cout} t={t} {h}x{w}: {name}", flush=True)
-    assert name.startswith("igemm_persist_kernel<") and name.endswith(f", 16, 2, {tw}, false>"), name
+    print(f"[case] conv3 two waves per SIMD cin={cin} cout={cout} t={t} {h}x{w}: {name}", flush=True)
+    assert name.startswith("igemm_occ2_kernel<") and name.endswith(f", 2, {tw}>"), name
     y = L.wvc_causal_conv3d_fwd(to_dev(x), to_dev(wt), to_dev(b), cache_in=to_dev(cache))
     ref = oracle.causal_conv3d(f64(x), f64(wt), f64(b), cache=f64(cache))
-    check_bf16(to_host(y), ref, f"conv3 persistent {cin}->{cout} {h}x{w}")
+    check_bf16(to_host(y), ref, f"conv3 two waves per SIMD {cin}->{cout} {h}x{w}")
 
 
 def test_split_k_workspace_reused_across_shapes():

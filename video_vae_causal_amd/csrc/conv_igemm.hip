@@ -233,8 +233,14 @@ __device__ __forceinline__ void bcol(int n, int &dr, int &c) {
 //   during the row two rows back, and the halo written at the end of a stage
 //   during that stage's first row, so every wait covers loads at least a row
 //   old.
-template <int KS, int CO_T, int M, int WAVES_CO, bool SPLIT, int TW, bool FP8, bool PERSIST>
+template <int KS, int CO_T, int M, int WAVES_CO, bool SPLIT, int TW, bool FP8, bool PERSIST,
+          bool OCC2 = false>
 __device__ __forceinline__ void igemm_body(const IgParams &p) {
+    static_assert(!OCC2 || (!PERSIST && KS == 3 && M == 16 && !FP8),
+                  "two waves per SIMD: 16x16 bf16 tiles, one tile per workgroup");
+    // Weight row sets: rows are prefetched NSETS - 1 rows ahead.  Two waves
+    // per SIMD (OCC2) keep two sets; the other wave covers the shorter lead.
+    constexpr int NSETS = OCC2 ? 2 : 3;
     static_assert(!FP8 || M == 32, "the 8-bit path uses 32x32x64 MFMAs");
     static_assert(!PERSIST || (!SPLIT && KS == 3), "persistent workgroups: whole-K 3x3x3 tiles");
     using MF = Mfma<M>;
@@ -412,8 +418,12 @@ __device__ __forceinline__ void igemm_body(const IgParams &p) {
 
     // bf16: one fragment per K-step.  8-bit: one 32-byte operand whose halves
     // are the 16-byte fragments of K-steps 0 and 1.
-    frag_t A[3][KS][FCO][KA];  // three row sets: [set][kw][co tile][K-step]
-    frag_t B[2][FPOS][KA];     // two tap sets: tap k reads B[k & 1]
+    frag_t A[NSETS][KS][FCO][KA];  // row sets: [set][kw][co tile][K-step]
+    frag_t B[OCC2 ? 1 : 2][FPOS][KA];  // two tap sets: tap k reads B[k & 1]
+    // OCC2: the B fragment of column step q = tap * FPOS + j lives in ring
+    // slot q % 3 and is read two column steps ahead (12 registers instead of
+    // 2 * FPOS * 4), which fits a wave in the 256 registers of two waves per SIMD.
+    frag_t Bq[3];
     uint4 hv[NIT];
     auto put = [](frag_t &dst, int ks, uint4 v) {
         if constexpr (FP8) {
@@ -502,6 +512,10 @@ __device__ __forceinline__ void igemm_body(const IgParams &p) {
     };
     // LDS entry offset of MFMA column tile j relative to column tile 0.
     auto offj = [](int j) { return ((j * M) / TW) * HC + (j * M) % TW; };
+    auto load_bq = [&](auto slot_tag, const uint4 *hb, int j, int kh, int kw) {
+        constexpr int SL = decltype(slot_tag)::value;
+        put(Bq[SL], 0, hb[offj(j) + kh * HC + kw]);
+    };
     auto load_b = [&](auto set_tag, const uint4 *hb, int j, int kh, int kw) {
         constexpr int BS = decltype(set_tag)::value;
 #pragma unroll
@@ -514,14 +528,14 @@ __device__ __forceinline__ void igemm_body(const IgParams &p) {
     // The prefetches are unconditional (indices clamped to the last row or
     // stage; the surplus loads at the very end are never used) so the loads
     // stay where they are issued instead of moving next to their first use.
-    auto row = [&](auto set_tag, int rho) {
+    auto row = [&](auto set_tag, auto kh_tag, int rho) {
         constexpr int SET = decltype(set_tag)::value;
-        constexpr int kh = SET % KS;  // rows are visited in groups of 3 == KS (or KS == 1)
+        constexpr int kh = decltype(kh_tag)::value;
         const int u = u0 + rho / KS;
         const int buf = (u - u0) & 1;
         const uint4 *hb = &halo[buf][bbase];
         const bool last_stage = u + 1 >= u1;
-        const int rnext = rho + 2 < R ? rho + 2 : R - 1;
+        const int rnext = rho + NSETS - 1 < R ? rho + NSETS - 1 : R - 1;
         // PERSIST: the last stage fetches the next tile's first halo (the
         // long-latency loads) instead of re-fetching its own last stage's
         const bool setup_next = PERSIST && last_stage && has_next;
@@ -543,21 +557,30 @@ __device__ __forceinline__ void igemm_body(const IgParams &p) {
                 constexpr int ks = decltype(ks_tag)::value;
                 static_for<FPOS>([&](auto j_tag) {
                     constexpr int j = decltype(j_tag)::value;
+                    if constexpr (OCC2) {
+                        constexpr int q = tp * FPOS + j, q2 = q + 2;
 #pragma unroll
-                    for (int i = 0; i < FCO; ++i) {
-                        if constexpr (FP8)
-                            acc[i][j] = mfma_e4m3(A[SET][kw][i][0], B[cur][j][0], acc[i][j]);
-                        else
-                            acc[i][j] = MF::run(A[SET][kw][i][ks], B[cur][j][ks], acc[i][j]);
+                        for (int i = 0; i < FCO; ++i)
+                            acc[i][j] = MF::run(A[SET][kw][i][0], Bq[q % 3], acc[i][j]);
+                        if constexpr (q2 < KS * KS * FPOS)
+                            load_bq(Int<q2 % 3>{}, hb, q2 % FPOS, (q2 / FPOS) / KS, (q2 / FPOS) % KS);
+                    } else {
+#pragma unroll
+                        for (int i = 0; i < FCO; ++i) {
+                            if constexpr (FP8)
+                                acc[i][j] = mfma_e4m3(A[SET][kw][i][0], B[cur][j][0], acc[i][j]);
+                            else
+                                acc[i][j] = MF::run(A[SET][kw][i][ks], B[cur][j][ks], acc[i][j]);
+                        }
+                        if (ks == 0 && next_in_stage) load_b(Int<cur ^ 1>{}, hb, j, nkh, nkw);
                     }
-                    if (ks == 0 && next_in_stage) load_b(Int<cur ^ 1>{}, hb, j, nkh, nkw);
                     // group index within the row, and the loads that fall on it
                     constexpr int NG = KS * KA * FPOS, NL = KS * FCO * KSTEPS;
                     constexpr int grp = (kw * KA + ks) * FPOS + j;
                     static_for<NL>([&](auto li) {
                         constexpr int L_ = decltype(li)::value;
                         if constexpr ((L_ * NG) / NL == grp)
-                            load_a_one(Int<(SET + 2) % 3>{}, Int<L_>{}, rnext, ct);
+                            load_a_one(Int<(SET + NSETS - 1) % NSETS>{}, Int<L_>{}, rnext, ct);
                     });
                     if constexpr (kh == 0) {
                         static_for<NIT>([&](auto hk) {
@@ -578,8 +601,13 @@ __device__ __forceinline__ void igemm_body(const IgParams &p) {
             store_halo(u + 1, buf ^ 1);
             __syncthreads();
             const uint4 *hn = &halo[buf ^ 1][bbase];
+            if constexpr (OCC2) {
+                load_bq(Int<0>{}, hn, 0, 0, 0);
+                load_bq(Int<1>{}, hn, 1 % FPOS, 1 / FPOS, 0);
+            } else {
 #pragma unroll
-            for (int j = 0; j < FPOS; ++j) load_b(Int<0>{}, hn, j, 0, 0);
+                for (int j = 0; j < FPOS; ++j) load_b(Int<0>{}, hn, j, 0, 0);
+            }
         }
     };
 
@@ -587,27 +615,50 @@ __device__ __forceinline__ void igemm_body(const IgParams &p) {
     if (R > 0) {
         load_halo(u0);
         load_row(Int<0>{}, 0, ct);
-        load_row(Int<1>{}, R > 1 ? 1 : 0, ct);
+        if constexpr (NSETS == 3) load_row(Int<1>{}, R > 1 ? 1 : 0, ct);
         store_halo(u0, 0);
         __syncthreads();
         const uint4 *h0p = &halo[0][bbase];
+        if constexpr (OCC2) {
+            load_bq(Int<0>{}, h0p, 0, 0, 0);
+            load_bq(Int<1>{}, h0p, 1 % FPOS, 1 / FPOS, 0);
+        } else {
 #pragma unroll
-        for (int j = 0; j < FPOS; ++j) load_b(Int<0>{}, h0p, j, 0, 0);
+            for (int j = 0; j < FPOS; ++j) load_b(Int<0>{}, h0p, j, 0, 0);
+        }
     }
     for (;;) {  // one pass per tile (PERSIST), else exactly one
     if (R > 0) {
-        if (KS == 3) {
+        if constexpr (OCC2) {
+            // Two row sets alternate while the kernel rows cycle through 3:
+            // two stages per iteration, then a last odd stage (R is a
+            // multiple of 3).
+            int rho = 0;
+            for (; rho + 6 <= R; rho += 6) {
+                row(Int<0>{}, Int<0>{}, rho);
+                row(Int<1>{}, Int<1>{}, rho + 1);
+                row(Int<0>{}, Int<2>{}, rho + 2);
+                row(Int<1>{}, Int<0>{}, rho + 3);
+                row(Int<0>{}, Int<1>{}, rho + 4);
+                row(Int<1>{}, Int<2>{}, rho + 5);
+            }
+            if (rho < R) {
+                row(Int<0>{}, Int<0>{}, rho);
+                row(Int<1>{}, Int<1>{}, rho + 1);
+                row(Int<0>{}, Int<2>{}, rho + 2);
+            }
+        } else if constexpr (KS == 3) {
             // R is a multiple of 3: one stage per iteration, no row guards.
             for (int rho = 0; rho < R; rho += 3) {
-                row(Int<0>{}, rho);
-                row(Int<1>{}, rho + 1);
-                row(Int<2>{}, rho + 2);
+                row(Int<0>{}, Int<0>{}, rho);
+                row(Int<1>{}, Int<1>{}, rho + 1);
+                row(Int<2>{}, Int<2>{}, rho + 2);
             }
         } else {
             for (int rho = 0; rho < R; rho += 3) {
-                row(Int<0>{}, rho);
-                if (rho + 1 < R) row(Int<1>{}, rho + 1);
-                if (rho + 2 < R) row(Int<2>{}, rho + 2);
+                row(Int<0>{}, Int<0>{}, rho);
+                if (rho + 1 < R) row(Int<1>{}, Int<0>{}, rho + 1);
+                if (rho + 2 < R) row(Int<2>{}, Int<0>{}, rho + 2);
             }
         }
     }
@@ -750,6 +801,15 @@ template <int KS, int CO_T, int M, int WAVES_CO, bool SPLIT, int TW, bool FP8 = 
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 igemm_kernel(IgParams p) {
     igemm_body<KS, CO_T, M, WAVES_CO, SPLIT, TW, FP8, false>(p);
+}
+
+// Two workgroups per CU, two waves per SIMD (whole-K 16x16 bf16 tiles): a
+// wave's stall at a stage barrier or in its epilogue is covered by the other
+// workgroup's MFMAs.
+template <int CO_T, int WAVES_CO, int TW>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+igemm_occ2_kernel(IgParams p) {
+    igemm_body<3, CO_T, 16, WAVES_CO, false, TW, false, false, true>(p);
 }
 
 // Persistent workgroups: one per CU, each through a run of whole-K tiles.
@@ -998,29 +1058,19 @@ size_t ws_bytes_for(const Plan &pl, const ConvCall &c, bool need_pack) {
 // Whole-K 3x3x3 grids of 16x16 MFMA tiles with more tiles than CUs run
 // persistent workgroups (the tile split over XCDs needs a CU count that is a
 // multiple of 8).
-bool runs_persistent(int ks, int m, int S, long total) {
-    const int cus = num_cus();
-    return ks == 3 && m == 16 && S == 1 && cus % 8 == 0 && total > cus;
-}
+// Whole-K 3x3x3 grids of 16x16 bf16 tiles run two workgroups per CU.
+bool runs_occ2(int ks, int m, int S, bool fp8) { return ks == 3 && m == 16 && S == 1 && !fp8; }
 
 template <int KS, int CO_T, int M, int WAVES_CO, int TW, bool FP8>
 hipError_t launch_tw(const IgParams &p, hipStream_t s) {
-    // Grids with more whole-K 3x3x3 tiles than CUs run persistent: one
-    // workgroup per CU, each through a run of tiles, so that a tile's first
-    // loads overlap the previous tile's epilogue.  The tile split over XCDs
-    // needs a CU count that is a multiple of 8.
-    const int cus = num_cus();
     if (p.S > 1) {
         hipLaunchKernelGGL((igemm_kernel<KS, CO_T, M, WAVES_CO, true, TW, FP8>), dim3(p.total),
                            dim3(256), 0, s, p);
         return hipGetLastError();
     }
-    if constexpr (KS == 3 && M == 16) {
-        if (runs_persistent(KS, M, p.S, p.total)) {
-            hipLaunchKernelGGL((igemm_persist_kernel<CO_T, M, WAVES_CO, TW, FP8>), dim3(cus),
-                               dim3(256), 0, s, p);
-            return hipGetLastError();
-        }
+    if constexpr (KS == 3 && M == 16 && !FP8) {
+        hipLaunchKernelGGL((igemm_occ2_kernel<CO_T, WAVES_CO, TW>), dim3(p.total), dim3(256), 0, s, p);
+        return hipGetLastError();
     }
     hipLaunchKernelGGL((igemm_kernel<KS, CO_T, M, WAVES_CO, false, TW, FP8>), dim3(p.total),
                        dim3(256), 0, s, p);
@@ -1086,8 +1136,8 @@ int igemm_kernel_name(const ConvCall &c, ConvRoute r, char *buf, size_t n) {
     if (pl.S > 1)
         return snprintf(buf, n, "igemm_kernel<%d, %d, %d, %d, true, %d, %s> + splitk_reduce_kernel",
                         ks, co_t, m, waves_co, pl.tw, f8);
-    if (runs_persistent(ks, m, pl.S, pl.tiles))
-        return snprintf(buf, n, "igemm_persist_kernel<%d, %d, %d, %d, %s>", co_t, m, waves_co, pl.tw, f8);
+    if (runs_occ2(ks, m, pl.S, fp8))
+        return snprintf(buf, n, "igemm_occ2_kernel<%d, %d, %d>", co_t, waves_co, pl.tw);
     return snprintf(buf, n, "igemm_kernel<%d, %d, %d, %d, false, %d, %s>", ks, co_t, m, waves_co,
                     pl.tw, f8);
 }
