@@ -18,7 +18,12 @@
 //   workgroup : 256 threads (4 waves), one per CU (up to 512 registers per
 //               lane), CO_T output channels x 256 output positions of one
 //               output frame; the positions form a TH x TW spatial tile chosen
-//               by the host (TH*TW == 256).
+//               by the host (TH*TW == 256).  Whole-K grids of 16x16 bf16
+//               tiles (96 and 64 channels) run two workgroups per CU instead
+//               (igemm_occ2_kernel, 256 registers per lane): the weights are
+//               prefetched one row ahead instead of two and the B fragments
+//               pass through a 3-slot ring, and each workgroup's barrier and
+//               epilogue stalls are covered by the other's MFMAs.
 //   K loop    : over work units (kt, 32-channel block).  A unit stages the
 //               halo of ONE input frame (t-2+kt: cache or chunk) for 32 input
 //               channels in LDS as [k-group(4)][(TH+2)(TW+2)][8 channels]
@@ -233,16 +238,13 @@ __device__ __forceinline__ void bcol(int n, int &dr, int &c) {
 //   during the row two rows back, and the halo written at the end of a stage
 //   during that stage's first row, so every wait covers loads at least a row
 //   old.
-template <int KS, int CO_T, int M, int WAVES_CO, bool SPLIT, int TW, bool FP8, bool PERSIST,
-          bool OCC2 = false>
+template <int KS, int CO_T, int M, int WAVES_CO, bool SPLIT, int TW, bool FP8, bool OCC2 = false>
 __device__ __forceinline__ void igemm_body(const IgParams &p) {
-    static_assert(!OCC2 || (!PERSIST && KS == 3 && M == 16 && !FP8),
-                  "two waves per SIMD: 16x16 bf16 tiles, one tile per workgroup");
+    static_assert(!OCC2 || (KS == 3 && M == 16 && !FP8), "two waves per SIMD: 16x16 bf16 tiles");
     // Weight row sets: rows are prefetched NSETS - 1 rows ahead.  Two waves
     // per SIMD (OCC2) keep two sets; the other wave covers the shorter lead.
     constexpr int NSETS = OCC2 ? 2 : 3;
     static_assert(!FP8 || M == 32, "the 8-bit path uses 32x32x64 MFMAs");
-    static_assert(!PERSIST || (!SPLIT && KS == 3), "persistent workgroups: whole-K 3x3x3 tiles");
     using MF = Mfma<M>;
     // 16x16 tiles take the bank-congruent group pitch and staging map
     constexpr bool CONG = M == 16;
@@ -286,23 +288,7 @@ __device__ __forceinline__ void igemm_body(const IgParams &p) {
     const int g = CONG ? (tid >> 4) & 3 : tid & 3;
     const int sp = CONG ? (tid & 15) + 16 * (tid >> 6) : tid >> 2;
 
-    // PERSIST: one workgroup per CU runs a sequence of tiles.  XCD k's
-    // workgroups share its contiguous slice of the logical tile order (the
-    // slice xcd_remap hands it), each taking every (workgroups per XCD)-th
-    // tile, so the XCD's L2 sees neighbouring tiles at any moment.
-    int Lcur, Lend = 0, Lstep = 0;
-    if constexpr (PERSIST) {
-        const int xcd = blockIdx.x & 7;
-        const int per = p.total >> 3, rem = p.total & 7;
-        const int start = xcd < rem ? xcd * (per + 1) : rem * (per + 1) + (xcd - rem) * per;
-        Lcur = start + (int)(blockIdx.x >> 3);
-        Lend = start + per + (xcd < rem ? 1 : 0);
-        Lstep = (int)(gridDim.x >> 3);
-        if (Lcur >= Lend) return;  // uniform per workgroup, before any barrier
-    } else {
-        Lcur = xcd_remap(blockIdx.x, p.total);
-    }
-    int L = Lcur;
+    int L = xcd_remap(blockIdx.x, p.total);
     const int s = SPLIT ? L % p.S : 0;
     if (SPLIT) L /= p.S;
     // Order of the logical tiles.  Small grids: channel tile slowest (each XCD
@@ -373,23 +359,6 @@ __device__ __forceinline__ void igemm_body(const IgParams &p) {
         }
     };
     stage_offsets(h0, w0, soff, interior);
-    // PERSIST: the workgroup's next tile, whose first halo and first two
-    // weight rows the current tile's last stage prefetches in place of the
-    // surplus loads a single tile ends with.
-    bool has_next = false;
-    int ct_n = 0, t_n = 0, n_n = 0, h0_n = 0, w0_n = 0;
-    uint32_t soff_n[NIT];
-    uint32_t interior_n = 0;
-    auto plan_next = [&]() {
-        if constexpr (PERSIST) {
-            has_next = Lcur + Lstep < Lend;
-            if (has_next) {
-                decode(Lcur + Lstep, ct_n, t_n, n_n, h0_n, w0_n);
-                stage_offsets(h0_n, w0_n, soff_n, interior_n);
-            }
-        }
-    };
-    plan_next();
     // B fragments: LDS entry of this lane's position (first MFMA column tile,
     // spatial tap (0,0), K-step 0).  Column tile j, K-step ks and tap (kh, kw)
     // add compile-time offsets.
@@ -463,24 +432,21 @@ __device__ __forceinline__ void igemm_body(const IgParams &p) {
     __amdgpu_buffer_rsrc_t hfr = rsrc(p.x, 0u);
     uint32_t hcb2 = 0;
     bool hgok = false;
-    bool hnext = false;  // PERSIST: the loads being set up are the next tile's
-    auto halo_setup = [&](int u, bool nxt) {
-        const int t_ = nxt ? t_n : t, n_ = nxt ? n_n : n;
+    auto halo_setup = [&](int u) {
         const int kt = u % KS, cb = (u / KS) * CB;
-        const int ts = t_ - (KS - 1) + kt;
+        const int ts = t - (KS - 1) + kt;
         if (ts >= 0)
-            hfr = rsrc(xb + (size_t)(n_ * p.T + ts) * p.frame_bytes, p.frame_bytes);
+            hfr = rsrc(xb + (size_t)(n * p.T + ts) * p.frame_bytes, p.frame_bytes);
         else if (p.cache)
-            hfr = rsrc(cb_base + (size_t)(n_ * p.F + p.F + ts) * p.frame_bytes, p.frame_bytes);
+            hfr = rsrc(cb_base + (size_t)(n * p.F + p.F + ts) * p.frame_bytes, p.frame_bytes);
         else
             hfr = rsrc(p.x, 0u);  // zero causal padding: every load reads zero
         hcb2 = (uint32_t)cb * ESZ;
         hgok = cb + g * CPE < p.Cin;
-        hnext = nxt;
     };
     auto halo_one = [&](auto k_tag) {
         constexpr int k = decltype(k_tag)::value;
-        const uint32_t so = (PERSIST && hnext) ? soff_n[k] : soff[k];
+        const uint32_t so = soff[k];
         hv[k] = bload(hfr, (hgok && so != OOB) ? so + hcb2 : OOB);
     };
     auto load_halo = [&](int u) {
@@ -536,10 +502,7 @@ __device__ __forceinline__ void igemm_body(const IgParams &p) {
         const uint4 *hb = &halo[buf][bbase];
         const bool last_stage = u + 1 >= u1;
         const int rnext = rho + NSETS - 1 < R ? rho + NSETS - 1 : R - 1;
-        // PERSIST: the last stage fetches the next tile's first halo (the
-        // long-latency loads) instead of re-fetching its own last stage's
-        const bool setup_next = PERSIST && last_stage && has_next;
-        if (kh == 0) halo_setup(setup_next ? 0 : (last_stage ? u : u + 1), setup_next);
+        if (kh == 0) halo_setup(last_stage ? u : u + 1);
         // Tap tp = kh*KS + kw of the stage reads B[tp & 1]; the next tap's set is
         // filled while this tap's MFMAs run, so no LDS read ever overwrites
         // registers an in-flight MFMA is still reading.  The global loads (the
@@ -627,7 +590,6 @@ __device__ __forceinline__ void igemm_body(const IgParams &p) {
             for (int j = 0; j < FPOS; ++j) load_b(Int<0>{}, h0p, j, 0, 0);
         }
     }
-    for (;;) {  // one pass per tile (PERSIST), else exactly one
     if (R > 0) {
         if constexpr (OCC2) {
             // Two row sets alternate while the kernel rows cycle through 3:
@@ -757,50 +719,13 @@ __device__ __forceinline__ void igemm_body(const IgParams &p) {
                 *reinterpret_cast<uint2 *>(p.y + obase + co) = o;
             }
     }
-    if constexpr (!PERSIST) {
-        break;
-    } else {
-        if (!has_next) break;
-        // Next tile.  Its first halo (hv) was fetched during this tile's last
-        // stage; its first two weight rows are issued now, after the stores,
-        // where the epilogue's registers are free again.  The barrier waits
-        // for every wave to finish with the halo buffers and bias_s.
-        load_row(Int<0>{}, 0, ct_n);
-        load_row(Int<1>{}, R > 1 ? 1 : 0, ct_n);
-        __syncthreads();
-        Lcur += Lstep;
-        ct = ct_n;
-        t = t_n;
-        n = n_n;
-        h0 = h0_n;
-        w0 = w0_n;
-        co0 = ct * CO_T + wco * WCO;
-#pragma unroll
-        for (int k = 0; k < NIT; ++k) soff[k] = soff_n[k];
-        interior = interior_n;
-        write_cache = KS == 3 && p.cache_out != nullptr && t == p.T - 1;
-        load_bias(ct);
-        store_halo(u0, 0);
-        __syncthreads();
-        const uint4 *h0p = &halo[0][bbase];
-#pragma unroll
-        for (int j = 0; j < FPOS; ++j) load_b(Int<0>{}, h0p, j, 0, 0);
-#pragma unroll
-        for (int i = 0; i < FCO; ++i)
-#pragma unroll
-            for (int j = 0; j < FPOS; ++j)
-#pragma unroll
-                for (int e = 0; e < ACC; ++e) acc[i][j][e] = 0.f;
-        plan_next();
-    }
-    }  // tiles
 }
 
 // One tile per workgroup (split-K partial sums when SPLIT).
 template <int KS, int CO_T, int M, int WAVES_CO, bool SPLIT, int TW, bool FP8 = false>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 igemm_kernel(IgParams p) {
-    igemm_body<KS, CO_T, M, WAVES_CO, SPLIT, TW, FP8, false>(p);
+    igemm_body<KS, CO_T, M, WAVES_CO, SPLIT, TW, FP8>(p);
 }
 
 // Two workgroups per CU, two waves per SIMD (whole-K 16x16 bf16 tiles): a
@@ -809,14 +734,7 @@ igemm_kernel(IgParams p) {
 template <int CO_T, int WAVES_CO, int TW>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 igemm_occ2_kernel(IgParams p) {
-    igemm_body<3, CO_T, 16, WAVES_CO, false, TW, false, false, true>(p);
-}
-
-// Persistent workgroups: one per CU, each through a run of whole-K tiles.
-template <int CO_T, int M, int WAVES_CO, int TW, bool FP8 = false>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
-igemm_persist_kernel(IgParams p) {
-    igemm_body<3, CO_T, M, WAVES_CO, false, TW, FP8, true>(p);
+    igemm_body<3, CO_T, 16, WAVES_CO, false, TW, false, true>(p);
 }
 
 // Split-K reduction: y = round(sum_s part[s] (in split order) + bias + residual),
@@ -1055,9 +973,6 @@ size_t ws_bytes_for(const Plan &pl, const ConvCall &c, bool need_pack) {
     return align256(part_bytes(pl, c)) + (need_pack ? align256(packed_bytes(c)) : 0);
 }
 
-// Whole-K 3x3x3 grids of 16x16 MFMA tiles with more tiles than CUs run
-// persistent workgroups (the tile split over XCDs needs a CU count that is a
-// multiple of 8).
 // Whole-K 3x3x3 grids of 16x16 bf16 tiles run two workgroups per CU.
 bool runs_occ2(int ks, int m, int S, bool fp8) { return ks == 3 && m == 16 && S == 1 && !fp8; }
 
