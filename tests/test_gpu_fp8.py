@@ -385,6 +385,53 @@ def test_decoder_stack_e4m3_streamed_vs_oracle():
     assert rel_bf <= 0.12
 
 
+def test_decoder_stack_e4m3_layer_by_layer_vs_oracle():
+    """The 8-bit decoder stack with every layer held to the single-layer bar.
+    Each layer runs on the GPU over the whole sequence, fed the previous
+    layer's GPU output, and is compared with the oracle's layer given that
+    same input: a quantiser flip in one layer cannot hide behind the
+    stack-level bar, and no error compounds between the comparisons.  The
+    chain must equal the stack itself bitwise."""
+    from video_vae_causal_amd import stream
+    lat, pd, p64 = _dec8_case(seed=28)
+    n, _, t, h, w = lat.shape
+    print(f"[case] 8-bit decoder stack layer by layer {lat.shape}, width 128", flush=True)
+    sc = DEC8_SCALES
+
+    def conv8_ref(x64, wk, bk, s):
+        wq, ws = oracle.quantize_conv_weights_e4m3(p64[wk])
+        return oracle.round_bf16(oracle.causal_conv3d_e4m3(oracle.quantize_e4m3(x64, s), s, wq, ws, p64[bk]))
+
+    x = to_dev(lat)
+    conv_in = stream.CausalConv3dE4M3(pd["w_in"], pd["b_in"], sc["in"])
+    conv_in.start(n, h, w)
+    a = conv_in(x)
+    check_e4m3_conv(to_host(a), conv8_ref(f64(lat), "w_in", "b_in", sc["in"]), "8-bit stack conv_in")
+    for k in range(4):
+        if k == 2:
+            up = L.wvc_upsample_nearest2x(a)
+            np.testing.assert_array_equal(to_host(up), oracle.upsample_nearest2x(to_host(a)))
+            conv_up = stream.CausalConv3dE4M3(pd["w_up"], pd["b_up"], sc["up"])
+            conv_up.start(n, 2 * h, 2 * w)
+            a = conv_up(up)
+            check_e4m3_conv(to_host(a), conv8_ref(f64(to_host(up)), "w_up", "b_up", sc["up"]),
+                            "8-bit stack conv_up")
+        blk = stream.ResBlockE4M3(pd[f"rb{k}"], *sc["rb"][k])
+        hh, ww = a.shape[3], a.shape[4]
+        blk.start(n, hh, ww)
+        a_in = a
+        a = blk(a_in)
+        ref = oracle.resblock_e4m3(f64(to_host(a_in)), p64[f"rb{k}"], *sc["rb"][k])
+        y = to_host(a)
+        check_bf16(y, ref, f"8-bit stack block {k}")
+        rel = oracle.rel_l2(y, ref)
+        print(f"[parity] 8-bit stack block {k} (fed the GPU's input) rel_l2={rel:.3e}", flush=True)
+        assert rel <= 5e-3, rel
+    whole = stream.DecoderStackE4M3(pd, sc).run(x, chunk_frames=t)
+    torch.cuda.synchronize()
+    assert torch.equal(whole, a)
+
+
 def test_decoder_stack_e4m3_pipeline_equals_sequential_bitwise():
     from video_vae_causal_amd import stream
     lat, pd, _ = _dec8_case(shape=(1, 48, 4, 10, 16), seed=27)
