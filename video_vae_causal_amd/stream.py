@@ -513,9 +513,11 @@ class DecoderStack(Stream):
         """Every block has an identity shortcut and bf16 parameters, so each
         conv can hand its output straight to the next norm
         (wvc_causal_conv3d_norm_fwd)."""
+        c = self.conv_in.weight.shape[0] if isinstance(self.conv_in, CausalConv3d) else 0
         return all(isinstance(rb, ResBlock) and rb.p.get("w_short") is None and
                    rb.p["w1"].dtype == torch.bfloat16 for rb in self.rbs) and \
-            isinstance(self.conv_in, CausalConv3d) and isinstance(self.conv_up, CausalConv3d)
+            isinstance(self.conv_in, CausalConv3d) and isinstance(self.conv_up, CausalConv3d) and \
+            c % 8 == 0 and c <= 2048  # the conv + norm call's channel range
 
     def stages(self, x: torch.Tensor, out: torch.Tensor, buf) -> List[Callable[[], object]]:
         """The chunk as a list of stages (each a few library calls); the
