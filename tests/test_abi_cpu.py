@@ -515,6 +515,60 @@ def test_block_parameter_check_is_redone_when_the_set_changes(host_binding):
         L.wvc_resblock_fwd(x, p)
 
 
+def test_conv_norm_binding_refuses_mismatched_buffers(host_binding):
+    """wvc_causal_conv3d_norm_fwd: the conv's buffers are checked as for the
+    conv call, and gamma, beta and h against C_out and the output shape."""
+    torch = host_binding
+    x = cl_host(torch, (1, 16, 2, 8, 12))
+    w = cl_host(torch, (32, 16, 3, 3, 3))
+    g = torch.zeros(32, dtype=torch.bfloat16)
+    h_ok = cl_host(torch, (1, 32, 2, 8, 12))
+    bad = [
+        dict(gamma=torch.zeros(16, dtype=torch.bfloat16)),           # C_in instead of C_out
+        dict(beta=torch.zeros(31, dtype=torch.bfloat16)),
+        dict(gamma=torch.zeros(32, dtype=torch.float32)),             # other dtype
+        dict(h=cl_host(torch, (1, 32, 1, 8, 12))),                    # fewer frames
+        dict(h=torch.zeros((1, 32, 2, 8, 12), dtype=torch.bfloat16)),  # not channels-last
+        dict(y=cl_host(torch, (1, 16, 2, 8, 12))),                    # C_in instead of C_out
+        dict(cache_in=cl_host(torch, (1, 16, 2, 4, 12))),
+        dict(residual=cl_host(torch, (1, 32, 2, 8, 11))),
+    ]
+    for kw in bad:
+        args = dict(gamma=g, h=h_ok)
+        args.update(kw)
+        gamma = args.pop("gamma")
+        with pytest.raises((ValueError, TypeError)):
+            L.wvc_causal_conv3d_norm_fwd(x, w, gamma, **args)
+    with pytest.raises(AssertionError, match="reached a launch"):
+        L.wvc_causal_conv3d_norm_fwd(x, w, g, h=h_ok, workspace=torch.zeros(1 << 20, dtype=torch.uint8))
+
+
+def test_conv_norm_c_abi_argument_errors(lib):
+    """The C entry point's own refusals, before anything is enqueued (no GPU):
+    a dtype it does not cover, C_out outside its range, eps <= 0, a missing
+    gamma or h, and a workspace smaller than its size query."""
+    import ctypes
+    ok = 1 << 12
+    d = L.conv_desc((1, 16, 2, 8, 12), (32, 16, 3, 3, 3), L.WVC_BF16)
+    need = L.wvc_causal_conv3d_norm_workspace_bytes(d)
+    assert need >= L.wvc_causal_conv3d_workspace_bytes(d)
+    p = ctypes.c_void_p
+    fake = lambda k: p(ok * k)   # distinct, 4 KiB-aligned, never dereferenced
+
+    def call(desc, gamma=fake(7), eps=1e-12, h=fake(9), ws_bytes=None):
+        return lib.wvc_causal_conv3d_norm_fwd(ctypes.byref(desc), fake(1), None, None, fake(3), None,
+                                              None, None, gamma, None, ctypes.c_float(eps), h,
+                                              fake(100), need if ws_bytes is None else ws_bytes, None)
+    d32 = L.conv_desc((1, 16, 2, 8, 12), (32, 16, 3, 3, 3), L.WVC_F32)
+    assert call(d32) == L.WVC_ERR_UNSUPPORTED
+    d20 = L.conv_desc((1, 16, 2, 8, 12), (20, 16, 3, 3, 3), L.WVC_BF16)
+    assert call(d20) == L.WVC_ERR_UNSUPPORTED
+    assert call(d, eps=0.0) == L.WVC_ERR_ARG
+    assert call(d, gamma=None) == L.WVC_ERR_ARG
+    assert call(d, h=None) == L.WVC_ERR_ARG
+    assert call(d, ws_bytes=need - 1) == L.WVC_ERR_WORKSPACE
+
+
 def test_norm_upsample_e4m3_bindings_refuse_mismatched_buffers(host_binding):
     torch = host_binding
     x = cl_host(torch, (1, 32, 2, 6, 10))

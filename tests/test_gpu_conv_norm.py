@@ -102,3 +102,20 @@ def test_decoder_stack_fused_equals_layerwise_bitwise(shape, width):
     y_l = layer.run(lat, chunk_frames=1)
     torch.cuda.synchronize()
     assert torch.equal(y_f, y_l)
+
+
+def test_conv_norm_empty_chunk_only_rolls_the_cache():
+    """A chunk of no frames: nothing to convolve or normalise, and cache_out
+    is cache_in (the last two frames of cache || empty chunk)."""
+    c, h, w = 64, 10, 14
+    cache = to_dev(inputs.quantize(inputs.normal((1, c, 2, h, w), 5, "cache"), "bf16"))
+    x = L.empty_cl((1, c, 0, h, w))
+    wt = to_dev(inputs.conv_weight(c, c, (3, 3, 3), 5, "w", "bf16"))
+    g = to_dev(inputs.norm_gamma(c, 5, "g", "bf16"))
+    cout = L.empty_cl((1, c, 2, h, w))
+    cout.fill_(float("nan"))
+    print("[case] conv+norm empty chunk", flush=True)
+    hh = L.wvc_causal_conv3d_norm_fwd(x, wt, g, cache_in=cache, cache_out=cout)
+    torch.cuda.synchronize()
+    assert tuple(hh.shape) == (1, c, 0, h, w)
+    assert torch.equal(cout, cache)
