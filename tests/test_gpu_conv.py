@@ -124,6 +124,25 @@ def test_conv_residual_and_no_bias():
     check_bf16(to_host(y), ref, "conv3 + residual, no bias")
 
 
+def test_conv3x3x3_two_waves_residual_no_bias_cache_out():
+    """The two-wave kernel's other epilogue and staging paths: a residual, no
+    bias, and the cache of the last two input frames written by its staging
+    (the chunk's last output frame), with and without a cache coming in."""
+    for cached in (True, False):
+        x, wt, _, cache = conv_case(96, 96, 4, 96, 160, seed=61 + cached)
+        res = inputs.quantize(inputs.normal((1, 96, 4, 96, 160), 61, "res"), "bf16")
+        d = L.conv_desc(x.shape, wt.shape, L.WVC_BF16)
+        name = L.wvc_conv3d_kernel_name(d)
+        print(f"[case] two waves, residual, no bias, cache_out, cached={cached}: {name}", flush=True)
+        assert name.startswith("igemm_occ2_kernel<"), name
+        cout = L.empty_cl((1, 96, 2, 96, 160))
+        y = L.wvc_causal_conv3d_fwd(to_dev(x), to_dev(wt), None, to_dev(cache) if cached else None, cout,
+                                    residual=to_dev(res))
+        ref = oracle.causal_conv3d(f64(x), f64(wt), None, cache=f64(cache) if cached else None) + f64(res)
+        check_bf16(to_host(y), ref, f"two waves + residual, no bias, cached={cached}")
+        np.testing.assert_array_equal(to_host(cout), oracle.next_cache(f64(cache) if cached else None, f64(x)))
+
+
 def test_cache_out_is_last_two_frames_exactly():
     for t in (1, 2, 4):
         x, wt, b, cache = conv_case(32, 32, t, 6, 10, seed=20 + t)
