@@ -128,6 +128,22 @@ def to_dev(a, dtype=None):
     return cl(t) if t.dim() == 5 else t
 
 
+def steady_cache(shape, name, e4m3_scale=None):
+    """A 2-frame cache of past activations (seeded normals, like the kernel's
+    input chunk): the state a streamed conv sees from its third chunk on.  A
+    zeroed cache (the first chunk) feeds the MFMAs zeros on two of the three
+    temporal taps, which draws less power, so the chip holds a higher clock
+    and the launch runs faster than in the steady state."""
+    import torch
+    from video_vae_causal_amd import _lib as L, inputs
+    v = to_dev(inputs.quantize(inputs.normal(tuple(shape), 6, name), "bf16"))
+    if e4m3_scale is None:
+        return v
+    q = L.empty_cl(tuple(shape), torch.uint8)
+    L.wvc_quantize_e4m3(v, e4m3_scale, q=q)
+    return q
+
+
 def conv_workspace(x, w, padding=(1, 1), packed=False):
     """Conv workspace allocated once, outside any timed region."""
     import torch
@@ -230,9 +246,8 @@ def wl_resblock():
     conv_flops = 2 * t * acc.conv_flops(n, 1, h, w, c, c)
     # dominant kernel alone: the 3x3x3 conv of one 60x104 frame with its cache
     # in and out, as the block's convs run
-    cache = L.empty_cl((n, c, 2, h, w))
+    cache = steady_cache((n, c, 2, h, w), "kernel_cache")
     cache_o = L.empty_cl((n, c, 2, h, w))
-    L.wvc_cache_reset(cache)
     ky = L.empty_cl((n, c, 1, h, w))
     kws = conv_workspace(frames[0], p["w1"], packed=True)
     w1p = L.wvc_conv3d_pack_weights(p["w1"])
@@ -274,8 +289,7 @@ def wl_resblock_e4m3():
     conv_flops = 2 * t * acc.conv_flops(n, 1, h, w, c, c)
     qx = L.empty_cl((n, c, 1, h, w), torch.uint8)
     L.wvc_quantize_e4m3(frames[0], 5.0 / 448, q=qx)
-    cache = L.empty_cl((n, c, 2, h, w), torch.uint8)
-    L.wvc_cache_reset(cache)
+    cache = steady_cache((n, c, 2, h, w), "kernel_cache", 5.0 / 448)
     ky = L.empty_cl((n, c, 1, h, w))
     wq, wsc, wqp = rb.w["w1"]
     d8 = L.conv_desc(tuple(qx.shape), tuple(wq.shape), L.WVC_E4M3, weight_layout=L.WVC_WEIGHT_PACKED)
@@ -478,9 +492,8 @@ def wl_decoder():
 
     per_frame = (acc.conv_flops(n, 1, h, w, cl_, width) + 4 * acc.conv_flops(n, 1, h, w, width, width)
                  + 5 * acc.conv_flops(n, 1, 2 * h, 2 * w, width, width))
-    cache = L.empty_cl((n, width, 2, 2 * h, 2 * w))
+    cache = steady_cache((n, width, 2, 2 * h, 2 * w), "kernel_cache")
     cache_o = L.empty_cl((n, width, 2, 2 * h, 2 * w))
-    L.wvc_cache_reset(cache)
     kx = to_dev(inputs.quantize(inputs.normal((n, width, 1, 2 * h, 2 * w), 5, "kernel_x"), "bf16"))
     ky = L.empty_cl((n, width, 1, 2 * h, 2 * w))
 
@@ -535,8 +548,7 @@ def wl_decoder_e4m3():
     kx = L.empty_cl((n, width, 1, 2 * h, 2 * w), torch.uint8)
     L.wvc_quantize_e4m3(to_dev(inputs.quantize(inputs.normal((n, width, 1, 2 * h, 2 * w), 5, "kernel_x"),
                                                "bf16")), 8.0 / 448, q=kx)
-    cache = L.empty_cl((n, width, 2, 2 * h, 2 * w), torch.uint8)
-    L.wvc_cache_reset(cache)
+    cache = steady_cache((n, width, 2, 2 * h, 2 * w), "kernel_cache", 8.0 / 448)
     ky = L.empty_cl((n, width, 1, 2 * h, 2 * w))
     cu = stack.conv_up
     d8 = L.conv_desc(tuple(kx.shape), tuple(cu.wq.shape), L.WVC_E4M3, weight_layout=L.WVC_WEIGHT_PACKED)
@@ -670,8 +682,7 @@ def wl_tiled():
     # the dominant kernel: the 3x3x3 conv on one decoded tile frame at 2x
     kx = cl(torch.randn((n, width, 1, 2 * th, 2 * tw), device="cuda").to(torch.bfloat16))
     ky = L.empty_cl(kx.shape)
-    cache = L.empty_cl((n, width, 2, 2 * th, 2 * tw))
-    L.wvc_cache_reset(cache)
+    cache = steady_cache((n, width, 2, 2 * th, 2 * tw), "kernel_cache")
     kws = conv_workspace(kx, p["w_up"], packed=True)
     wup = L.wvc_conv3d_pack_weights(p["w_up"])
 
