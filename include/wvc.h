@@ -81,6 +81,11 @@ typedef struct wvc_conv3d_desc {
                                     [P1] 10.5); 0 for the symmetric case        */
     int t_phase;                 /* sequence frames before this chunk, modulo
                                     stride_t (0 when stride_t == 1)             */
+    int upsample_in;             /* 0, or 2: the conv's input is x (and the
+                                    cache) seen through a nearest 2x spatial
+                                    upsample; h, w are then the upsampled
+                                    frame's, x and the caches hold h/2 x w/2
+                                    frames (see wvc_causal_conv3d_fwd)          */
 } wvc_conv3d_desc;
 
 /* Route counters ([P3]: counters show which route every call took). */
@@ -146,6 +151,17 @@ typedef struct wvc_counters {
  * Aliasing: y, cache_out and workspace may not overlap any other buffer of the
  * call (WVC_ERR_ALIAS); read-only buffers may overlap each other (residual ==
  * x is legal).  cache_in and cache_out must therefore be distinct buffers.
+ * Upsampled input (d->upsample_in == 2): the decoder's nearest 2x spatial
+ * upsample feeding this conv, read inside the conv's halo staging, so the
+ * upsampled frames never reach memory.  The conv computes exactly the call
+ * above on X'[.., 2i+a, 2j+b] = x[.., i, j] (a, b in {0, 1}), per frame, with
+ * the cache carrying the past input frames before the upsample: x is
+ * [N, C_in, t, h/2, w/2], cache_in / cache_out are [N, C_in, F, h/2, w/2], y
+ * and residual are [N, C_out, t, h, w].  The result is bitwise that of
+ * wvc_upsample_nearest2x followed by the conv on the upsampled frames and
+ * caches.  h and w must be even; the call must take the MFMA 3x3x3 route
+ * (bf16), else WVC_ERR_UNSUPPORTED (no other route reads through the
+ * upsample).  0 = no upsample; other values are WVC_ERR_ARG.
  */
 int wvc_causal_conv3d_fwd(const wvc_conv3d_desc *d, const void *x, const void *cache_in,
                           void *cache_out, const void *weight, const void *bias,
@@ -188,8 +204,10 @@ size_t wvc_causal_conv3d_workspace_bytes(const wvc_conv3d_desc *d);
  *   y = round_bf16(conv_d(x | cache_in) + bias + residual)   (C_out channels)
  *   h = round_bf16(silu(rmsnorm(y; gamma, beta, eps)))
  * y is bit for bit what wvc_causal_conv3d_fwd stores and h what
- * wvc_rmsnorm_silu stores for that y.  Arguments as for wvc_causal_conv3d_fwd,
- * plus gamma [C_out], beta [C_out] or NULL, eps > 0 and the output
+ * wvc_rmsnorm_silu stores for that y.  Arguments as for wvc_causal_conv3d_fwd
+ * (d->upsample_in included: the decoder's conv after its upsample feeds the
+ * next block's norm this way), plus gamma [C_out], beta [C_out] or NULL,
+ * eps > 0 and the output
  * h [N, C_out, t_out, h_out, w_out]; y may be NULL when only h is wanted.
  * When the conv's plan splits K, its split sums go straight into the norm
  * kernel, which adds them in split order, then the bias and the residual,

@@ -606,3 +606,62 @@ def test_noalloc_scratch_size_and_validation(lib):
     assert f(ctypes.byref(big), X, CIN, COUT, W, B, None, Y, None) == L.WVC_ERR_WORKSPACE
     assert "scratch" in L.wvc_last_error()
     assert L.wvc_get_counters()["fast_3x3x3"] == 0
+
+
+def test_upsampled_input_validation(lib):
+    """upsample_in = 2: the conv reads x and the caches (h/2 x w/2 frames)
+    through a nearest 2x upsample, so the conv frame h x w must be even, and
+    only the bf16 MFMA 3x3x3 route reads that way; any other value is an
+    argument error."""
+    w32 = (32, 16, 3, 3, 3)
+    d = desc(x_shape=(1, 16, 2, 8, 12), w_shape=w32)
+    d.upsample_in = 2
+    assert L.wvc_causal_conv3d_workspace_bytes(d) >= 0
+    assert L.wvc_causal_conv3d_norm_workspace_bytes(d) >= 0
+    for v in (1, 3, -2):
+        d.upsample_in = v
+        assert call(lib, d) == L.WVC_ERR_ARG and "upsample_in" in L.wvc_last_error()
+    for shape in ((1, 16, 2, 7, 12), (1, 16, 2, 8, 9)):
+        odd = desc(x_shape=shape, w_shape=w32)
+        odd.upsample_in = 2
+        assert call(lib, odd) == L.WVC_ERR_ARG and "even" in L.wvc_last_error()
+    L.wvc_reset_counters()
+    others = [desc(w_shape=(32, 16, 1, 1, 1), padding=(0, 0)),        # projection route
+              desc(w_shape=w32, dtype=L.WVC_F32),                     # direct route
+              desc(x_shape=(1, 12, 2, 8, 8), w_shape=(32, 12, 3, 3, 3))]  # C_in % 8 != 0
+    for o in others:
+        o.upsample_in = 2
+        assert call(lib, o) == L.WVC_ERR_UNSUPPORTED and "upsample_in" in L.wvc_last_error()
+    assert L.wvc_get_counters()["rejected"] == len(others)
+    e8 = desc(w_shape=w32, dtype=L.WVC_E4M3)                        # the 8-bit conv
+    e8.upsample_in = 2
+    with pytest.raises(L.WvcError, match="upsample_in"):
+        L.wvc_causal_conv3d_workspace_bytes(e8)
+    # x ends at h/2 * w/2 positions per frame: a y 16 bytes before that end
+    # overlaps it
+    u = desc(x_shape=(1, 16, 2, 8, 8), w_shape=w32)
+    u.upsample_in = 2
+    need = L.wvc_causal_conv3d_workspace_bytes(u)
+    x_bytes = 1 * 16 * 2 * 4 * 4 * 2
+    assert call(lib, u, y=X + x_bytes - 16, ws=WS, wsb=need) == L.WVC_ERR_ALIAS
+    assert "'y'" in L.wvc_last_error()
+
+
+def test_upsampled_input_binding_shapes(host_binding):
+    """The binding sizes x and the caches at the stored frame and y at twice
+    it, and refuses the other sizes before any launch."""
+    torch = host_binding
+    x = cl_host(torch, (1, 16, 2, 4, 6))
+    w = cl_host(torch, (32, 16, 3, 3, 3))
+    small = lambda: cl_host(torch, (1, 16, 2, 4, 6))
+    y = cl_host(torch, (1, 32, 2, 8, 12))
+    bad = [dict(cache_in=cl_host(torch, (1, 16, 2, 8, 12))),   # cache at the upsampled size
+           dict(y=cl_host(torch, (1, 32, 2, 4, 6))),             # y at the stored size
+           dict(upsample_in=3)]
+    for kw in bad:
+        args = dict(cache_in=small(), cache_out=small(), y=y, upsample_in=2)
+        args.update(kw)
+        with pytest.raises((ValueError, TypeError, L.WvcError)):
+            L.wvc_causal_conv3d_fwd(x, w, **args)
+    with pytest.raises(AssertionError, match="reached a launch"):
+        L.wvc_causal_conv3d_fwd(x, w, None, small(), small(), y=y, upsample_in=2)

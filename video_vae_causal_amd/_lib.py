@@ -49,7 +49,7 @@ class ConvDesc(ctypes.Structure):
     _fields_ = [(f, ctypes.c_int) for f in (
         "n", "c_in", "c_out", "t", "h", "w", "kt", "kh", "kw", "stride_t", "stride_h",
         "stride_w", "pad_h", "pad_w", "dil_t", "dil_h", "dil_w", "groups", "dtype",
-        "weight_layout", "pad_h_extra", "pad_w_extra", "t_phase")]
+        "weight_layout", "pad_h_extra", "pad_w_extra", "t_phase", "upsample_in")]
 
 
 class ResblockDesc(ctypes.Structure):
@@ -286,11 +286,16 @@ def empty_cl(shape: Sequence[int], dtype=torch.bfloat16, device="cuda") -> torch
 def conv_desc(x_shape, w_shape, dtype: int, stride=(1, 1, 1), padding=(1, 1),
               dilation=(1, 1, 1), groups: int = 1,
               weight_layout: int = WVC_WEIGHT_STANDARD, pad_extra=(0, 0),
-              t_phase: int = 0) -> ConvDesc:
+              t_phase: int = 0, upsample_in: int = 0) -> ConvDesc:
+    """Descriptor of a conv over x of shape ``x_shape``.  With upsample_in = 2
+    the conv reads x through a nearest 2x upsample: its frame (d.h, d.w) is
+    twice x's."""
     n, c, t, h, w = x_shape
     co, ci, kt, kh, kw = w_shape
+    up = 2 if upsample_in == 2 else 1
     d = ConvDesc()
-    d.n, d.c_in, d.c_out, d.t, d.h, d.w = n, ci, co, t, h, w
+    d.n, d.c_in, d.c_out, d.t, d.h, d.w = n, ci, co, t, h * up, w * up
+    d.upsample_in = upsample_in
     d.kt, d.kh, d.kw = kt, kh, kw
     d.stride_t, d.stride_h, d.stride_w = stride
     d.pad_h, d.pad_w = padding
@@ -305,11 +310,11 @@ def conv_desc(x_shape, w_shape, dtype: int, stride=(1, 1, 1), padding=(1, 1),
 
 @_memo
 def _conv_desc_shared(x_shape, w_shape, dtype, stride, padding, dilation, groups, layout,
-                      pad_extra, t_phase) -> ConvDesc:
+                      pad_extra, t_phase, upsample_in=0) -> ConvDesc:
     """conv_desc for the binding's own calls, one object per argument tuple
     (read only: the library never writes a descriptor)."""
     return conv_desc(x_shape, w_shape, dtype, stride, padding, dilation, groups, layout,
-                     pad_extra, t_phase)
+                     pad_extra, t_phase, upsample_in)
 
 
 def conv_out_hw(h, w, k, stride, padding, dilation, pad_extra=(0, 0)):
@@ -357,11 +362,12 @@ _packed_bytes_shared = _memo(wvc_conv3d_packed_weight_bytes)
 
 
 @_memo
-def _norm_ws_shared(x_shape, w_shape, code, padding, layout, device) -> int:
+def _norm_ws_shared(x_shape, w_shape, code, padding, layout, device, upsample_in=0) -> int:
     """wvc_causal_conv3d_norm_workspace_bytes of a unit-stride conv, asked once
     per shape and device (the size depends on the device's CU count)."""
     return wvc_causal_conv3d_norm_workspace_bytes(
-        conv_desc(x_shape, w_shape, code, padding=padding, weight_layout=layout))
+        conv_desc(x_shape, w_shape, code, padding=padding, weight_layout=layout,
+                  upsample_in=upsample_in))
 
 
 def wvc_conv3d_pack_weights(weight: torch.Tensor, padding=(1, 1), stride=(1, 1, 1),
@@ -390,16 +396,19 @@ def wvc_causal_conv3d_fwd(x: torch.Tensor, weight: torch.Tensor, bias: Optional[
                           dilation=(1, 1, 1), groups: int = 1,
                           workspace: Optional[torch.Tensor] = None,
                           packed_weight: Optional[torch.Tensor] = None, pad_extra=(0, 0),
-                          t_phase: int = 0) -> torch.Tensor:
+                          t_phase: int = 0, upsample_in: int = 0) -> torch.Tensor:
     """Causal Conv3D of one chunk (see wvc_causal_conv3d_fwd in include/wvc.h).
     ``weight`` gives the logical shape; when ``packed_weight`` (from
     wvc_conv3d_pack_weights) is given the call reads that instead.
     ``stride`` is (temporal, h, w); ``pad_extra`` adds zero rows below / columns
     right of the frame; ``t_phase`` is the number of sequence frames before this
-    chunk modulo the temporal stride.  Returns y (allocated if not given)."""
+    chunk modulo the temporal stride; ``upsample_in`` = 2 reads x and the
+    caches (frames of h x w) through a nearest 2x upsample, so y has frames of
+    2h x 2w.  Returns y (allocated if not given)."""
     lib = load()
     d, out_shape, wsrc = _conv_checks(x, weight, bias, cache_in, cache_out, residual, y, stride,
-                                      padding, dilation, groups, packed_weight, pad_extra, t_phase)
+                                      padding, dilation, groups, packed_weight, pad_extra, t_phase,
+                                      upsample_in)
     if y is None:
         y = empty_cl(out_shape, x.dtype, x.device)
     ws_bytes = 0
@@ -430,13 +439,14 @@ def wvc_causal_conv3d_norm_fwd(x: torch.Tensor, weight: torch.Tensor, gamma: tor
                                residual: Optional[torch.Tensor] = None,
                                y: Optional[torch.Tensor] = None, h: Optional[torch.Tensor] = None,
                                padding=(1, 1), workspace: Optional[torch.Tensor] = None,
-                               packed_weight: Optional[torch.Tensor] = None) -> torch.Tensor:
+                               packed_weight: Optional[torch.Tensor] = None,
+                               upsample_in: int = 0) -> torch.Tensor:
     """Conv, then the RMS norm + SiLU of the layer it feeds (see
     wvc_causal_conv3d_norm_fwd in include/wvc.h): y = conv(x) + bias + residual
-    (stored only when ``y`` is given), h = SiLU(norm(y)).  Returns h
-    (allocated if not given)."""
+    (stored only when ``y`` is given), h = SiLU(norm(y)); ``upsample_in`` as for
+    wvc_causal_conv3d_fwd.  Returns h (allocated if not given)."""
     d, out_shape, wsrc = _conv_checks(x, weight, bias, cache_in, cache_out, residual, y, (1, 1, 1),
-                                      padding, (1, 1, 1), 1, packed_weight, (0, 0), 0)
+                                      padding, (1, 1, 1), 1, packed_weight, (0, 0), 0, upsample_in)
     c_out = out_shape[1]
     _need_exact(gamma, "gamma", (c_out,), x.dtype, x.device)
     if gamma is None:
@@ -447,7 +457,7 @@ def wvc_causal_conv3d_norm_fwd(x: torch.Tensor, weight: torch.Tensor, gamma: tor
         h = empty_cl(out_shape, x.dtype, x.device)
     if workspace is None:
         need = _norm_ws_shared(tuple(x.shape), tuple(weight.shape), _dtype_code(x.dtype),
-                               tuple(padding), d.weight_layout, x.device)
+                               tuple(padding), d.weight_layout, x.device, upsample_in)
     if workspace is None and need:  # contents on entry do not matter
         workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
@@ -480,16 +490,19 @@ def wvc_causal_conv3d_fwd_noalloc(x: torch.Tensor, weight: torch.Tensor, y: torc
 
 
 def _conv_checks(x, weight, bias, cache_in, cache_out, residual, y, stride, padding, dilation,
-                 groups, packed_weight, pad_extra, t_phase):
+                 groups, packed_weight, pad_extra, t_phase, upsample_in=0):
     """Checks of a conv call's tensors against the descriptor built from x and
     the weight; returns (descriptor, output shape, weight pointer source)."""
     _need_cl(x, "x")
     _need_cl(weight, "weight")
     code = _dtype_code(x.dtype)
     n, c, t, h, w = x.shape
+    if upsample_in not in (0, 2):
+        raise WvcError(WVC_ERR_ARG, f"upsample_in {upsample_in} must be 0 or 2")
+    up = 2 if upsample_in == 2 else 1   # the caches keep x's frame size
     _need_exact(weight, "weight", (weight.shape[0], c) + tuple(weight.shape[2:]), x.dtype, x.device)
     _need_exact(bias, "bias", (weight.shape[0],), x.dtype, x.device)
-    ho, wo = conv_out_hw(h, w, weight.shape[2:], stride, padding, dilation, pad_extra)
+    ho, wo = conv_out_hw(h * up, w * up, weight.shape[2:], stride, padding, dilation, pad_extra)
     if ho < 1 or wo < 1:
         raise WvcError(WVC_ERR_ARG, "kernel larger than the padded frame")
     if stride[0] < 1 or not 0 <= t_phase < stride[0]:
@@ -506,7 +519,7 @@ def _conv_checks(x, weight, bias, cache_in, cache_out, residual, y, stride, padd
     stride, padding, dilation, pad_extra = tuple(stride), tuple(padding), tuple(dilation), \
         tuple(pad_extra)
     d = _conv_desc_shared(tuple(x.shape), tuple(weight.shape), code, stride, padding, dilation,
-                          groups, layout, pad_extra, t_phase)
+                          groups, layout, pad_extra, t_phase, upsample_in)
     if packed_weight is not None:
         _need_bytes(packed_weight, "packed_weight",
                     _packed_bytes_shared(tuple(weight.shape), x.dtype, padding, stride, pad_extra),

@@ -102,6 +102,8 @@ struct IgParams {
     int S, U;
     int total;
     int co_major;  // channel tile slowest in the workgroup order (small grids)
+    int up;        // 1, or 2: x and the caches hold H/2 x W/2 frames read through a
+                   // nearest 2x upsample (frame_bytes is then theirs)
     uint32_t frame_bytes, w_bytes;
 };
 
@@ -354,7 +356,11 @@ __device__ __forceinline__ void igemm_body(const IgParams &p) {
             const int r = hp / HC, c = hp - r * HC;
             const int hs = h0_ + r - PAD, ws = w0_ + c - PAD;
             const bool inframe = hp < HP && hs >= 0 && hs < p.H && ws >= 0 && ws < p.W;
-            so[k] = inframe ? (uint32_t)((hs * p.W + ws) * p.Cin * ESZ + g * 16) : OOB;
+            // upsampled input: position (hs, ws) of the conv's frame is pixel
+            // (hs/2, ws/2) of the stored one (hs, ws >= 0 when in frame)
+            const int ush = p.up >> 1;
+            const int sh = hs >> ush, sw = ws >> ush, srow = p.W >> ush;
+            so[k] = inframe ? (uint32_t)((sh * srow + sw) * p.Cin * ESZ + g * 16) : OOB;
             if (inframe && r >= PAD && r < PAD + G::TH && c >= PAD && c < PAD + TW) inner |= 1u << k;
         }
     };
@@ -1097,7 +1103,8 @@ hipError_t launch_conv_igemm(const ConvCall &c, ConvRoute r, bool packed_given, 
     p.S = pl.S;
     p.U = pl.U;
     p.co_major = pl.co_major;
-    p.frame_bytes = (uint32_t)((size_t)c.h * c.w * c.cin * act_bytes(c));
+    p.up = c.up == 2 ? 2 : 1;
+    p.frame_bytes = (uint32_t)((size_t)(c.h / p.up) * (c.w / p.up) * c.cin * act_bytes(c));
     p.w_bytes = (uint32_t)packed_bytes(c);
     if (pl.S > 1) {
         p.part = static_cast<float *>(ws);

@@ -128,6 +128,12 @@ int plan_conv(const wvc_conv3d_desc *d, ConvPlan *pl, bool count = true) {
         return fail(WVC_ERR_ARG, "bad kernel/stride/pad/dilation");
     if (d->t_phase < 0 || d->t_phase >= d->stride_t)
         return fail(WVC_ERR_ARG, "t_phase %d must lie in [0, stride_t = %d)", d->t_phase, d->stride_t);
+    if (d->upsample_in != 0 && d->upsample_in != 2)
+        return fail(WVC_ERR_ARG, "upsample_in %d must be 0 or 2", d->upsample_in);
+    // Upsampled input: x and the caches hold h/2 x w/2 frames.
+    const int up = d->upsample_in == 2 ? 2 : 1;
+    if (up == 2 && (d->h % 2 != 0 || d->w % 2 != 0))
+        return fail(WVC_ERR_ARG, "upsample_in needs an even h and w (got %d x %d)", d->h, d->w);
     // One-sided padding extends the padded frame at its far end only.
     const int ho = out_size(d->h + d->pad_h_extra, d->kh, d->stride_h, d->pad_h, d->dil_h);
     const int wo = out_size(d->w + d->pad_w_extra, d->kw, d->stride_w, d->pad_w, d->dil_w);
@@ -152,9 +158,11 @@ int plan_conv(const wvc_conv3d_desc *d, ConvPlan *pl, bool count = true) {
     c.to = to;
     c.eh = d->pad_h_extra;
     c.ew = d->pad_w_extra;
+    c.up = up;
 
     size_t plane_in, plane_out, v;
-    bool ok = mul_ok((size_t)d->h, (size_t)d->w, &plane_in) && mul_ok(plane_in, d->c_in, &plane_in);
+    bool ok = mul_ok((size_t)(d->h / up), (size_t)(d->w / up), &plane_in) &&
+              mul_ok(plane_in, d->c_in, &plane_in);
     ok = ok && mul_ok((size_t)ho, (size_t)wo, &plane_out) && mul_ok(plane_out, d->c_out, &plane_out);
     ok = ok && mul_ok(plane_in, (size_t)d->n * d->t, &v) && mul_ok(v, e, &pl->x_bytes);
     ok = ok && mul_ok(plane_in, (size_t)d->n * frames, &v) && mul_ok(v, e, &pl->cache_bytes);
@@ -193,6 +201,12 @@ int plan_conv(const wvc_conv3d_desc *d, ConvPlan *pl, bool count = true) {
                         "C_out %% 32 == 0");
         }
         pl->route = wvc::ConvRoute::Fast3x3x3;
+    }
+    if (up == 2 && (pl->route != wvc::ConvRoute::Fast3x3x3 || e4m3)) {
+        if (count) g_rejected++;
+        return fail(WVC_ERR_UNSUPPORTED,
+                    "upsample_in is read by the bf16 MFMA 3x3x3 route only (3x3x3, stride 1, pad 1, "
+                    "dilation 1, C_in %% 8 == 0, C_out %% 32 == 0)");
     }
     if (d->weight_layout == WVC_WEIGHT_PACKED) {
         if (pl->route == wvc::ConvRoute::Generic) {
@@ -246,9 +260,9 @@ int conv_fwd(const wvc_conv3d_desc *d, const void *x, const void *cache_in, void
         const bool al = aligned(x, 16) && aligned(cache_in, 16) && aligned(weight, 16) &&
                         aligned(y, 16) && aligned(residual, 16) && aligned(bias, 8);
         if (!al) {
-            if (packed || e4m3)
+            if (packed || e4m3 || pl.call.up == 2)
                 return fail(WVC_ERR_ARG, "%s need 16-byte aligned tensors",
-                            e4m3 ? "E4M3 convs" : "packed weights");
+                            e4m3 ? "E4M3 convs" : packed ? "packed weights" : "upsampled-input convs");
             pl.route = wvc::ConvRoute::Generic;
         }
     }
@@ -298,7 +312,7 @@ int conv_fwd(const wvc_conv3d_desc *d, const void *x, const void *cache_in, void
         if (err != hipSuccess) return hip_status(err, "conv launch");
     }
     if (cache_out && !cache_done) {
-        const size_t frame_elems = (size_t)d->h * d->w * d->c_in;
+        const size_t frame_elems = (size_t)(d->h / c.up) * (d->w / c.up) * d->c_in;
         err = wvc::launch_cache_update(x, cache_in, cache_out, d->n, d->t, c.frames, frame_elems,
                                        e4m3 ? 1 : elem_bytes(d->dtype), s);
         if (err != hipSuccess) return hip_status(err, "cache update launch");

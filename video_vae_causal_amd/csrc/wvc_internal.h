@@ -71,6 +71,8 @@ struct ConvCall {
     int dtype;             // WVC_F32 / WVC_BF16 / WVC_E4M3
     int st, t0, to;        // temporal stride, first anchor frame, output frames
     int eh, ew;            // extra zero rows below / columns right of the frame
+    int up;                // 2: x and the caches hold h/2 x w/2 frames, read through a
+                           // nearest 2x upsample (MFMA 3x3x3 route only); else 1
     // WVC_E4M3 calls: x, cache and weight hold E4M3 codes; bias, residual and
     // y are bf16; the sum is multiplied by xscale * wscale[co].
     float xscale;

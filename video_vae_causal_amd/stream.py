@@ -49,12 +49,12 @@ def _cached_buf(bufs: Dict[str, torch.Tensor], name: str, shape, like: torch.Ten
 
 
 def _norm_workspace(ws: Optional[torch.Tensor], x: torch.Tensor, weight: torch.Tensor, padding,
-                    packed: Optional[torch.Tensor]) -> torch.Tensor:
+                    packed: Optional[torch.Tensor], upsample_in: int = 0) -> torch.Tensor:
     """A workspace for wvc_causal_conv3d_norm_fwd on chunks of x's shape:
     ``ws`` when it is large enough, else a new one."""
     layout = L.WVC_WEIGHT_PACKED if packed is not None else L.WVC_WEIGHT_STANDARD
     need = L._norm_ws_shared(tuple(x.shape), tuple(weight.shape), L._dtype_code(x.dtype),
-                             tuple(padding), layout, x.device)
+                             tuple(padding), layout, x.device, upsample_in)
     if ws is None or ws.numel() < need:
         ws = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
     return ws
@@ -108,11 +108,15 @@ def _fits(pp: Optional[_PingPong], shape) -> bool:
 
 
 class CausalConv3d:
-    """A causal 3x3x3 conv layer with its rolling 2-frame cache."""
+    """A causal 3x3x3 conv layer with its rolling 2-frame cache.  With
+    ``upsample_in`` = 2 the layer is the decoder's nearest 2x upsample and the
+    conv after it in one call: it takes chunks of h x w frames, caches them at
+    that size and returns frames of 2h x 2w."""
 
-    def __init__(self, weight: torch.Tensor, bias: Optional[torch.Tensor]):
+    def __init__(self, weight: torch.Tensor, bias: Optional[torch.Tensor], upsample_in: int = 0):
         self.weight = weight
         self.bias = bias
+        self.upsample_in = upsample_in
         self.frames = L.wvc_conv3d_cache_frames(tuple(weight.shape))
         self.cache: Optional[_PingPong] = None
         self.ws: Optional[torch.Tensor] = None
@@ -140,7 +144,7 @@ class CausalConv3d:
             self.ws = torch.empty(need, dtype=torch.uint8, device=x.device)
         y = L.wvc_causal_conv3d_fwd(x, self.weight, self.bias, cin, cout, residual, y,
                                     padding=self.padding, workspace=self.ws if need else None,
-                                    packed_weight=self.packed)
+                                    packed_weight=self.packed, upsample_in=self.upsample_in)
         if self.frames:
             self.cache.flip()
         return y
@@ -156,10 +160,11 @@ class CausalConv3d:
             self.start(n, hh, ww)
         cin = self.cache.cin if self.frames else None
         cout = self.cache.cout if self.frames else None
-        self.nws = _norm_workspace(self.__dict__.get("nws"), x, self.weight, self.padding, self.packed)
+        self.nws = _norm_workspace(self.__dict__.get("nws"), x, self.weight, self.padding, self.packed,
+                                   self.upsample_in)
         L.wvc_causal_conv3d_norm_fwd(x, self.weight, gamma, self.bias, beta, eps, cin, cout, residual,
                                      y, h, padding=self.padding, workspace=self.nws,
-                                     packed_weight=self.packed)
+                                     packed_weight=self.packed, upsample_in=self.upsample_in)
         if self.frames:
             self.cache.flip()
         return h
@@ -171,7 +176,7 @@ class CausalConv3d:
         if need is None:
             layout = L.WVC_WEIGHT_PACKED if self.packed is not None else L.WVC_WEIGHT_STANDARD
             d = L.conv_desc(tuple(x.shape), tuple(self.weight.shape), L._dtype_code(x.dtype),
-                            padding=self.padding, weight_layout=layout)
+                            padding=self.padding, weight_layout=layout, upsample_in=self.upsample_in)
             need = self._needs[key] = L.wvc_causal_conv3d_workspace_bytes(d)
         return need
 
@@ -482,25 +487,34 @@ class Stream:
 class DecoderStack(Stream):
     """Decoder-shaped stack: conv_in (C_lat -> C) -> 2 resblocks -> nearest 2x
     upsample -> conv_up (C -> C) -> 2 resblocks, streamed chunk by chunk with one
-    2-frame cache per 3x3x3 conv (10 caches for 4 resblocks)."""
+    2-frame cache per 3x3x3 conv (10 caches for 4 resblocks).  The upsample is
+    read inside conv_up (upsample_in = 2): the upsampled frames never reach
+    memory, and conv_up caches its input frames before the upsample."""
 
-    # Pipeline cut: conv_in, both low-resolution blocks and the upsample on
-    # one stream; conv_up and the two full-resolution blocks on the other.
-    # The low-resolution convs fill fewer workgroups than there are CUs, and
-    # the other stream's convs use the rest.
-    PIPELINE_SPLIT = 6
+    # Pipeline cut: conv_in and both low-resolution blocks on one stream;
+    # conv_up (reading through the upsample) and the two full-resolution
+    # blocks on the other.  The low-resolution convs fill fewer workgroups
+    # than there are CUs, and the other stream's convs use the rest.
+    PIPELINE_SPLIT = 5
 
     def __init__(self, p: Dict, eps: float = 1e-12):
         self.conv_in = CausalConv3d(p["w_in"], p.get("b_in"))
         self.rbs = [ResBlock(p[f"rb{k}"], eps) for k in range(4)]
-        self.conv_up = CausalConv3d(p["w_up"], p.get("b_up"))
+        self.conv_up = CausalConv3d(p["w_up"], p.get("b_up"), upsample_in=2)
         super().__init__([self.conv_in] + self.rbs[:2] + [self.conv_up] + self.rbs[2:])
+
+    def _up_fused(self) -> bool:
+        """Whether conv_up reads its input through the upsample itself."""
+        return getattr(self.conv_up, "upsample_in", 0) == 2
 
     def start(self, n: int, h: int, w: int):
         self.conv_in.start(n, h, w)
         for rb in self.rbs[:2]:
             rb.start(n, h, w)
-        self.conv_up.start(n, 2 * h, 2 * w)
+        if self._up_fused():
+            self.conv_up.start(n, h, w)   # its cache holds frames before the upsample
+        else:
+            self.conv_up.start(n, 2 * h, 2 * w)
         for rb in self.rbs[2:]:
             rb.start(n, 2 * h, 2 * w)
 
@@ -534,7 +548,7 @@ class DecoderStack(Stream):
         c = self.conv_in.weight.shape[0]
         lo, hi = (n, c, t, h, w), (n, c, t, 2 * h, 2 * w)
         a_in, a0, a1 = buf("in", lo, x), buf("rb0", lo, x), buf("rb1", lo, x)
-        up, a_up, a2 = buf("up", hi, x), buf("conv_up", hi, x), buf("rb2", hi, x)
+        a_up, a2 = buf("conv_up", hi, x), buf("rb2", hi, x)
         h1 = [buf(f"rb{k}.h1", lo if k < 2 else hi, x) for k in range(4)]
         h2 = [buf(f"rb{k}.h2", lo if k < 2 else hi, x) for k in range(4)]
         rb = self.rbs
@@ -548,8 +562,7 @@ class DecoderStack(Stream):
             lambda: rb[0].back_norm(h2[0], a_in, a0, *norm1(1), h1[1]),
             lambda: rb[1].front_from_h1(h1[1], h2[1]),
             lambda: rb[1].back(h2[1], a0, a1),
-            lambda: L.wvc_upsample_nearest2x(a1, y=up),
-            lambda: self.conv_up.norm_into(up, a_up, *norm1(2), h1[2]),
+            lambda: self.conv_up.norm_into(a1, a_up, *norm1(2), h1[2]),
             lambda: rb[2].front_from_h1(h1[2], h2[2]),
             lambda: rb[2].back_norm(h2[2], a_up, a2, *norm1(3), h1[3]),
             lambda: rb[3].front_from_h1(h1[3], h2[3]),
@@ -563,7 +576,7 @@ class DecoderStack(Stream):
         c = self.conv_in.weight.shape[0]
         lo, hi = (n, c, t, h, w), (n, c, t, 2 * h, 2 * w)
         a_in, a0, a1 = buf("in", lo, x), buf("rb0", lo, x), buf("rb1", lo, x)
-        up, a_up, a2 = buf("up", hi, x), buf("conv_up", hi, x), buf("rb2", hi, x)
+        a_up, a2 = buf("conv_up", hi, x), buf("rb2", hi, x)
 
         def sub(k):
             return lambda name, shape, like: buf(f"rb{k}.{name}", shape, like)
@@ -571,8 +584,12 @@ class DecoderStack(Stream):
         st = self.conv_in.stages(x, a_in, buf)
         st += self.rbs[0].stages(a_in, a0, sub(0))
         st += self.rbs[1].stages(a0, a1, sub(1))
-        st.append(lambda: L.wvc_upsample_nearest2x(a1, y=up))
-        st += self.conv_up.stages(up, a_up, buf)
+        if self._up_fused():
+            st += self.conv_up.stages(a1, a_up, buf)
+        else:
+            up = buf("up", hi, x)
+            st.append(lambda: L.wvc_upsample_nearest2x(a1, y=up))
+            st += self.conv_up.stages(up, a_up, buf)
         st += self.rbs[2].stages(a_up, a2, sub(2))
         st += self.rbs[3].stages(a2, out, sub(3))
         return st
