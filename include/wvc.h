@@ -160,8 +160,9 @@ typedef struct wvc_counters {
  * and residual are [N, C_out, t, h, w].  The result is bitwise that of
  * wvc_upsample_nearest2x followed by the conv on the upsampled frames and
  * caches.  h and w must be even; the call must take the MFMA 3x3x3 route
- * (bf16), else WVC_ERR_UNSUPPORTED (no other route reads through the
- * upsample).  0 = no upsample; other values are WVC_ERR_ARG.
+ * (bf16 here, or E4M3 codes through wvc_causal_conv3d_e4m3_fwd), else
+ * WVC_ERR_UNSUPPORTED (no other route reads through the upsample).
+ * 0 = no upsample; other values are WVC_ERR_ARG.
  */
 int wvc_causal_conv3d_fwd(const wvc_conv3d_desc *d, const void *x, const void *cache_in,
                           void *cache_out, const void *weight, const void *bias,

@@ -611,8 +611,8 @@ def test_noalloc_scratch_size_and_validation(lib):
 def test_upsampled_input_validation(lib):
     """upsample_in = 2: the conv reads x and the caches (h/2 x w/2 frames)
     through a nearest 2x upsample, so the conv frame h x w must be even, and
-    only the bf16 MFMA 3x3x3 route reads that way; any other value is an
-    argument error."""
+    only the MFMA 3x3x3 route (bf16 or E4M3) reads that way; any other value
+    is an argument error."""
     w32 = (32, 16, 3, 3, 3)
     d = desc(x_shape=(1, 16, 2, 8, 12), w_shape=w32)
     d.upsample_in = 2
@@ -633,10 +633,9 @@ def test_upsampled_input_validation(lib):
         o.upsample_in = 2
         assert call(lib, o) == L.WVC_ERR_UNSUPPORTED and "upsample_in" in L.wvc_last_error()
     assert L.wvc_get_counters()["rejected"] == len(others)
-    e8 = desc(w_shape=w32, dtype=L.WVC_E4M3)                        # the 8-bit conv
+    e8 = desc(w_shape=w32, dtype=L.WVC_E4M3)   # the 8-bit conv reads through it too
     e8.upsample_in = 2
-    with pytest.raises(L.WvcError, match="upsample_in"):
-        L.wvc_causal_conv3d_workspace_bytes(e8)
+    assert L.wvc_causal_conv3d_workspace_bytes(e8) >= 0
     # x ends at h/2 * w/2 positions per frame: a y 16 bytes before that end
     # overlaps it
     u = desc(x_shape=(1, 16, 2, 8, 8), w_shape=w32)

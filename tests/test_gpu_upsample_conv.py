@@ -105,3 +105,39 @@ def test_upsampled_input_conv_norm_equals_composition():
         ref = oracle.causal_conv3d(oracle.upsample_nearest2x(f64(x)), f64(wt), f64(b),
                                    cache=oracle.upsample_nearest2x(f64(cache))) + to_host(res)
         check_bf16(to_host(y1), ref, f"upsample-in conv + residual {cin}->{cout}")
+
+
+def test_upsampled_input_e4m3_conv():
+    """The 8-bit conv reading E4M3 codes through the upsample (the decoder's
+    8-bit conv_up): bitwise the 8-bit conv over the codes of the upsampled
+    frames (the quantiser is elementwise, so those are the upsampled codes),
+    and within the 8-bit conv's bar of the oracle's conv of the decoded,
+    upsampled codes."""
+    from test_gpu_fp8 import check_e4m3_conv
+    cin, cout, t, h, w, seed = 128, 128, 2, 15, 26, 44
+    xs = 6.0 / 448
+    x = inputs.quantize(inputs.normal((1, cin, t, h, w), seed, "x"), "bf16")
+    cache = inputs.quantize(inputs.normal((1, cin, 2, h, w), seed, "cache"), "bf16")
+    wt = inputs.conv_weight(cout, cin, (3, 3, 3), seed, "w", "bf16")
+    b = inputs.conv_bias(cout, seed, "b", "bf16")
+    print(f"[case] upsample-in E4M3 conv {cin}->{cout} t={t} {h}x{w} -> {2 * h}x{2 * w}", flush=True)
+    xd, cd, bd = to_dev(x), to_dev(cache), to_dev(b)
+    xq, cq = L.wvc_quantize_e4m3(xd, xs), L.wvc_quantize_e4m3(cd, xs)
+    wq, wsc = L.wvc_quantize_rows_e4m3(to_dev(wt))
+    c_next = L.empty_cl((1, cin, 2, h, w), torch.uint8)
+    y = L.wvc_causal_conv3d_e4m3_fwd(xq, xs, wq, wsc, bd, cq, c_next, upsample_in=2)
+    assert tuple(y.shape) == (1, cout, t, 2 * h, 2 * w)
+    assert torch.equal(c_next, xq)    # t = 2: the cache is the chunk's codes, before the upsample
+    y2 = L.wvc_causal_conv3d_e4m3_fwd(L.wvc_quantize_e4m3(L.wvc_upsample_nearest2x(xd), xs), xs, wq,
+                                      wsc, bd, L.wvc_quantize_e4m3(L.wvc_upsample_nearest2x(cd), xs))
+    assert torch.equal(y, y2), "fused upsample read differs from the upsampled codes"
+
+    def codes(tq):
+        return tq.cpu().numpy()
+
+    def up_codes(c):
+        return oracle.upsample_nearest2x(c.astype(np.float64)).astype(np.uint8)
+
+    ref = oracle.causal_conv3d_e4m3(up_codes(codes(xq)), xs, codes(wq), wsc.cpu().numpy(), f64(b),
+                                    cache_q=up_codes(codes(cq)))
+    check_e4m3_conv(to_host(y), ref, "upsample-in E4M3 conv")

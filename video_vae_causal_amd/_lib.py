@@ -633,17 +633,23 @@ def wvc_causal_conv3d_e4m3_fwd(x: torch.Tensor, x_scale: float, weight: torch.Te
                                residual: Optional[torch.Tensor] = None,
                                y: Optional[torch.Tensor] = None,
                                workspace: Optional[torch.Tensor] = None,
-                               packed_weight: Optional[torch.Tensor] = None) -> torch.Tensor:
+                               packed_weight: Optional[torch.Tensor] = None,
+                               upsample_in: int = 0) -> torch.Tensor:
     """Causal 3x3x3 conv of E4M3 operands (see wvc_causal_conv3d_e4m3_fwd in
     include/wvc.h).  x, caches and weight are uint8 tensors of E4M3 codes in
     channels_last_3d; w_scale is a float32 vector [C_out]; bias, residual and
-    y are bfloat16.  Returns y (allocated if not given)."""
+    y are bfloat16.  ``upsample_in`` = 2 reads x and the caches through a
+    nearest 2x upsample (y then has frames of twice x's).  Returns y
+    (allocated if not given)."""
     lib = load()
     _need_cl(x, "x")
     _need_cl(weight, "weight")
     if x.dtype != torch.uint8 or weight.dtype != torch.uint8 or w_scale.dtype != torch.float32:
         raise TypeError("x and weight must be uint8 (E4M3 codes), w_scale float32")
     n, c, t, h, w = x.shape
+    if upsample_in not in (0, 2):
+        raise WvcError(WVC_ERR_ARG, f"upsample_in {upsample_in} must be 0 or 2")
+    up = 2 if upsample_in == 2 else 1   # the caches keep x's frame size
     co = weight.shape[0]
     _need_exact(weight, "weight", (co, c) + tuple(weight.shape[2:]), torch.uint8, x.device)
     _need_exact(bias, "bias", (co,), torch.bfloat16, x.device)
@@ -651,15 +657,16 @@ def wvc_causal_conv3d_e4m3_fwd(x: torch.Tensor, x_scale: float, weight: torch.Te
     for name, cc in (("cache_in", cache_in), ("cache_out", cache_out)):
         _need_exact(cc, name, (n, c, 2, h, w), torch.uint8, x.device)
     for name, tt in (("residual", residual), ("y", y)):
-        _need_exact(tt, name, (n, co, t, h, w), torch.bfloat16, x.device)
+        _need_exact(tt, name, (n, co, t, h * up, w * up), torch.bfloat16, x.device)
     layout = WVC_WEIGHT_STANDARD if packed_weight is None else WVC_WEIGHT_PACKED
-    d = conv_desc(tuple(x.shape), tuple(weight.shape), WVC_E4M3, weight_layout=layout)
+    d = conv_desc(tuple(x.shape), tuple(weight.shape), WVC_E4M3, weight_layout=layout,
+                  upsample_in=upsample_in)
     if packed_weight is not None:
         _need_bytes(packed_weight, "packed_weight",
                     wvc_conv3d_packed_weight_bytes(tuple(weight.shape), torch.uint8), x.device)
     wsrc = weight if packed_weight is None else packed_weight
     if y is None:
-        y = empty_cl((n, co, t, h, w), torch.bfloat16, x.device)
+        y = empty_cl((n, co, t, h * up, w * up), torch.bfloat16, x.device)
     ws_bytes = 0
     if workspace is None:
         need = wvc_causal_conv3d_workspace_bytes(d)

@@ -202,11 +202,11 @@ int plan_conv(const wvc_conv3d_desc *d, ConvPlan *pl, bool count = true) {
         }
         pl->route = wvc::ConvRoute::Fast3x3x3;
     }
-    if (up == 2 && (pl->route != wvc::ConvRoute::Fast3x3x3 || e4m3)) {
+    if (up == 2 && pl->route != wvc::ConvRoute::Fast3x3x3) {
         if (count) g_rejected++;
         return fail(WVC_ERR_UNSUPPORTED,
-                    "upsample_in is read by the bf16 MFMA 3x3x3 route only (3x3x3, stride 1, pad 1, "
-                    "dilation 1, C_in %% 8 == 0, C_out %% 32 == 0)");
+                    "upsample_in is read by the MFMA 3x3x3 route only (bf16 or E4M3; 3x3x3, stride 1, "
+                    "pad 1, dilation 1, C_in %% 8 == 0, C_out %% 32 == 0)");
     }
     if (d->weight_layout == WVC_WEIGHT_PACKED) {
         if (pl->route == wvc::ConvRoute::Generic) {

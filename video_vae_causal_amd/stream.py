@@ -336,10 +336,15 @@ class CausalConv3dE4M3:
     """A causal 3x3x3 conv on the 8-bit path whose input is not a norm output
     (the decoder's conv_in and conv_up): the bf16 chunk is quantised at the
     activation scale ``scale`` (``wvc_quantize_e4m3``), then the 8-bit conv
-    runs on the codes with its code cache; the output is bf16."""
+    runs on the codes with its code cache; the output is bf16.  With
+    ``upsample_in`` = 2 the conv reads the codes through the nearest 2x
+    upsample (the quantiser is elementwise, so quantising before the upsample
+    gives the same codes), and the chunk and cache keep the small frame."""
 
-    def __init__(self, weight: torch.Tensor, bias: Optional[torch.Tensor], scale: float):
+    def __init__(self, weight: torch.Tensor, bias: Optional[torch.Tensor], scale: float,
+                 upsample_in: int = 0):
         self.weight, self.bias, self.scale = weight, bias, float(scale)
+        self.upsample_in = upsample_in
         self.wq, self.wsc = L.wvc_quantize_rows_e4m3(weight)
         self.packed = L.wvc_conv3d_pack_weights(self.wq)
         self.cache: Optional[_PingPong] = None
@@ -372,13 +377,14 @@ class CausalConv3dE4M3:
             self.start(n, h, w)
         q = _cached_buf(self.bufs, "q", x.shape, x.new_empty(0, dtype=torch.uint8))
         L.wvc_quantize_e4m3(x, self.scale, q=q)
-        d = L.conv_desc(tuple(q.shape), tuple(self.wq.shape), L.WVC_E4M3, weight_layout=L.WVC_WEIGHT_PACKED)
+        d = L.conv_desc(tuple(q.shape), tuple(self.wq.shape), L.WVC_E4M3, weight_layout=L.WVC_WEIGHT_PACKED,
+                        upsample_in=self.upsample_in)
         need = L.wvc_causal_conv3d_workspace_bytes(d)
         if need and (self.ws is None or self.ws.numel() < need):
             self.ws = torch.empty(need, dtype=torch.uint8, device=x.device)
         y = L.wvc_causal_conv3d_e4m3_fwd(q, self.scale, self.wq, self.wsc, self.bias, self.cache.cin,
                                          self.cache.cout, None, y, workspace=self.ws if need else None,
-                                         packed_weight=self.packed)
+                                         packed_weight=self.packed, upsample_in=self.upsample_in)
         self.cache.flip()
         return y
 
@@ -623,13 +629,14 @@ class DecoderStackE4M3(DecoderStack):
     ``scales["up"]``; each residual block k quantises its two norm outputs at
     ``scales["rb"][k]`` = (s1, s2).  Activations between layers stay bf16."""
 
-    # conv_in, rb0, rb1 and the upsample on one stream; the rest on the other
-    PIPELINE_SPLIT = 4
+    # conv_in, rb0 and rb1 on one stream; conv_up (reading through the
+    # upsample) and the rest on the other
+    PIPELINE_SPLIT = 3
 
     def __init__(self, p: Dict, scales: Dict, eps: float = 1e-12):
         self.conv_in = CausalConv3dE4M3(p["w_in"], p.get("b_in"), scales["in"])
         self.rbs = [ResBlockE4M3(p[f"rb{k}"], *scales["rb"][k], eps) for k in range(4)]
-        self.conv_up = CausalConv3dE4M3(p["w_up"], p.get("b_up"), scales["up"])
+        self.conv_up = CausalConv3dE4M3(p["w_up"], p.get("b_up"), scales["up"], upsample_in=2)
         Stream.__init__(self, [self.conv_in] + self.rbs[:2] + [self.conv_up] + self.rbs[2:])
 
 
