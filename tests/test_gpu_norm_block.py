@@ -210,6 +210,34 @@ def test_decoder_stack_small_vs_oracle():
     check_bf16(to_host(out), ref, "decoder stack small")
 
 
+def test_decoder_stack_checkpoint_resume_bitwise():
+    """The decoder stack's whole resumable state is its ten caches (conv_up's
+    at the frame size before the upsample it reads through): a stack resumed
+    from a checkpoint taken after frame 2 continues bitwise as the
+    uninterrupted stream ("Cosmos3 Wan VAE", section 8.5: the cache carries
+    the past frames from chunk to chunk)."""
+    d = inputs.decoder_inputs(seed=16, shape=(1, 16, 5, 6, 9), width=64)
+    pd, lat = stack_dev(d["p"]), to_dev(d["latent"])
+    n, _, t, h, w = lat.shape
+    frames = [lat[:, :, i:i + 1].contiguous(memory_format=torch.channels_last_3d) for i in range(t)]
+    print("[case] decoder stack checkpoint after frame 2, resume", flush=True)
+    whole = stream.DecoderStack(pd)
+    whole.start(n, h, w)
+    full = [whole.chunk(f).clone() for f in frames]
+    first = stream.DecoderStack(pd)
+    first.start(n, h, w)
+    for f in frames[:3]:
+        first.chunk(f)
+    saved = first.state()
+    assert len(saved) == 10
+    assert tuple(first.conv_up.caches()[0].shape[3:]) == (h, w)
+    resumed = stream.DecoderStack(pd)
+    resumed.start(n, h, w)
+    resumed.load_state(saved)
+    for f, ref in zip(frames[3:], full[3:]):
+        assert torch.equal(resumed.chunk(f), ref)
+
+
 @pytest.mark.timeout(900)
 def test_decoder_stack_full_21_frames_vs_oracle():
     """The decoder-shaped stack at its real widths (48-ch latent, 384 ch, 30x52
