@@ -86,6 +86,14 @@ typedef struct wvc_conv3d_desc {
                                     upsample; h, w are then the upsampled
                                     frame's, x and the caches hold h/2 x w/2
                                     frames (see wvc_causal_conv3d_fwd)          */
+    int cu_limit;                /* 0, or the number of CUs to plan the grid for:
+                                    a call that shares the GPU with work on
+                                    another stream leaves the other CUs to it.
+                                    Only the split-K choice of the MFMA 3x3x3
+                                    route reads it (a different split count
+                                    adds the partial sums in another grouping,
+                                    so results may differ in the last bit);
+                                    < 0 is WVC_ERR_ARG                        */
 } wvc_conv3d_desc;
 
 /* Route counters ([P3]: counters show which route every call took). */
@@ -277,6 +285,8 @@ typedef struct wvc_resblock_desc {
     int dtype;
     float eps;          /* RMS-norm clamp, > 0 */
     int weights_packed; /* 1: w1, w2, w_short were packed by wvc_conv3d_pack_weights */
+    int cu_limit;       /* 0, or the number of CUs the block's convs plan their
+                           grids for (wvc_conv3d_desc.cu_limit); < 0 is WVC_ERR_ARG */
 } wvc_resblock_desc;
 
 /* Parameters of one residual block ([P1] 10.4).  All device pointers. */

@@ -664,3 +664,25 @@ def test_upsampled_input_binding_shapes(host_binding):
             L.wvc_causal_conv3d_fwd(x, w, **args)
     with pytest.raises(AssertionError, match="reached a launch"):
         L.wvc_causal_conv3d_fwd(x, w, None, small(), small(), y=y, upsample_in=2)
+
+
+def test_cu_limit_plans_the_split_for_fewer_cus(lib):
+    """cu_limit > 0 plans a small grid's split-K for that many CUs: the
+    384-channel 30x52 frame (24 tiles of 128 channels x 256 positions, 36
+    K units) splits K 9 ways on 256 CUs (216 workgroups) and 6 ways on 160
+    (144 workgroups), which the partial-sum workspace shows; < 0 is refused,
+    for the conv and for the block descriptor."""
+    def ws(cu):
+        d = L.conv_desc((1, 384, 1, 30, 52), (384, 384, 3, 3, 3), L.WVC_BF16,
+                        weight_layout=L.WVC_WEIGHT_PACKED, cu_limit=cu)
+        return L.wvc_causal_conv3d_workspace_bytes(d)
+    part = 1560 * 384 * 4
+    align = lambda v: (v + 255) // 256 * 256
+    assert ws(0) == align(9 * part) and ws(256) == align(9 * part)
+    assert ws(160) == align(6 * part)
+    bad = L.conv_desc((1, 384, 1, 30, 52), (384, 384, 3, 3, 3), L.WVC_BF16, cu_limit=-1)
+    assert call(lib, bad) == L.WVC_ERR_ARG and "cu_limit" in L.wvc_last_error()
+    rd = L.resblock_desc((1, 64, 1, 8, 8), 64, L.WVC_BF16)
+    assert L.wvc_resblock_workspace_bytes(rd) > 0
+    rd.cu_limit = -1
+    assert lib.wvc_resblock_workspace_bytes(ctypes.byref(rd)) == ctypes.c_size_t(-1).value

@@ -362,3 +362,18 @@ def test_strict_mode_allows_fast_route_and_refuses_generic():
         assert e.value.code == L.WVC_ERR_STRICT
     finally:
         L.wvc_set_strict(False)
+
+
+def test_conv_planned_for_fewer_cus_vs_oracle():
+    """cu_limit = 160: the 384-channel 30x52 frame splits K 6 ways instead of
+    9 (144 workgroups instead of 216, leaving CUs to another stream's work);
+    the result stays within the bf16 bar of the oracle and within rounding of
+    the full-device plan, which adds the same products in another grouping."""
+    x, wt, b, cache = conv_case(384, 384, 1, 30, 52, seed=61)
+    print("[case] conv 384 30x52 planned for 160 CUs", flush=True)
+    xd, wd, bd, cd = to_dev(x), to_dev(wt), to_dev(b), to_dev(cache)
+    y6 = L.wvc_causal_conv3d_fwd(xd, wd, bd, cache_in=cd, cu_limit=160)
+    y9 = L.wvc_causal_conv3d_fwd(xd, wd, bd, cache_in=cd)
+    ref = oracle.causal_conv3d(f64(x), f64(wt), f64(b), cache=f64(cache))
+    check_bf16(to_host(y6), ref, "conv 384 30x52, 160 CUs")
+    check_bf16(to_host(y6), to_host(y9), "conv 384 30x52, 160 CUs vs all CUs")

@@ -49,12 +49,12 @@ class ConvDesc(ctypes.Structure):
     _fields_ = [(f, ctypes.c_int) for f in (
         "n", "c_in", "c_out", "t", "h", "w", "kt", "kh", "kw", "stride_t", "stride_h",
         "stride_w", "pad_h", "pad_w", "dil_t", "dil_h", "dil_w", "groups", "dtype",
-        "weight_layout", "pad_h_extra", "pad_w_extra", "t_phase", "upsample_in")]
+        "weight_layout", "pad_h_extra", "pad_w_extra", "t_phase", "upsample_in", "cu_limit")]
 
 
 class ResblockDesc(ctypes.Structure):
     _fields_ = [(f, ctypes.c_int) for f in ("n", "c_in", "c_out", "t", "h", "w", "dtype")] + \
-        [("eps", ctypes.c_float), ("weights_packed", ctypes.c_int)]
+        [("eps", ctypes.c_float), ("weights_packed", ctypes.c_int), ("cu_limit", ctypes.c_int)]
 
 
 class ResblockParams(ctypes.Structure):
@@ -286,16 +286,17 @@ def empty_cl(shape: Sequence[int], dtype=torch.bfloat16, device="cuda") -> torch
 def conv_desc(x_shape, w_shape, dtype: int, stride=(1, 1, 1), padding=(1, 1),
               dilation=(1, 1, 1), groups: int = 1,
               weight_layout: int = WVC_WEIGHT_STANDARD, pad_extra=(0, 0),
-              t_phase: int = 0, upsample_in: int = 0) -> ConvDesc:
+              t_phase: int = 0, upsample_in: int = 0, cu_limit: int = 0) -> ConvDesc:
     """Descriptor of a conv over x of shape ``x_shape``.  With upsample_in = 2
     the conv reads x through a nearest 2x upsample: its frame (d.h, d.w) is
-    twice x's."""
+    twice x's.  cu_limit > 0 plans the grid for that many CUs."""
     n, c, t, h, w = x_shape
     co, ci, kt, kh, kw = w_shape
     up = 2 if upsample_in == 2 else 1
     d = ConvDesc()
     d.n, d.c_in, d.c_out, d.t, d.h, d.w = n, ci, co, t, h * up, w * up
     d.upsample_in = upsample_in
+    d.cu_limit = cu_limit
     d.kt, d.kh, d.kw = kt, kh, kw
     d.stride_t, d.stride_h, d.stride_w = stride
     d.pad_h, d.pad_w = padding
@@ -310,11 +311,11 @@ def conv_desc(x_shape, w_shape, dtype: int, stride=(1, 1, 1), padding=(1, 1),
 
 @_memo
 def _conv_desc_shared(x_shape, w_shape, dtype, stride, padding, dilation, groups, layout,
-                      pad_extra, t_phase, upsample_in=0) -> ConvDesc:
+                      pad_extra, t_phase, upsample_in=0, cu_limit=0) -> ConvDesc:
     """conv_desc for the binding's own calls, one object per argument tuple
     (read only: the library never writes a descriptor)."""
     return conv_desc(x_shape, w_shape, dtype, stride, padding, dilation, groups, layout,
-                     pad_extra, t_phase, upsample_in)
+                     pad_extra, t_phase, upsample_in, cu_limit)
 
 
 def conv_out_hw(h, w, k, stride, padding, dilation, pad_extra=(0, 0)):
@@ -362,12 +363,13 @@ _packed_bytes_shared = _memo(wvc_conv3d_packed_weight_bytes)
 
 
 @_memo
-def _norm_ws_shared(x_shape, w_shape, code, padding, layout, device, upsample_in=0) -> int:
+def _norm_ws_shared(x_shape, w_shape, code, padding, layout, device, upsample_in=0,
+                    cu_limit=0) -> int:
     """wvc_causal_conv3d_norm_workspace_bytes of a unit-stride conv, asked once
     per shape and device (the size depends on the device's CU count)."""
     return wvc_causal_conv3d_norm_workspace_bytes(
         conv_desc(x_shape, w_shape, code, padding=padding, weight_layout=layout,
-                  upsample_in=upsample_in))
+                  upsample_in=upsample_in, cu_limit=cu_limit))
 
 
 def wvc_conv3d_pack_weights(weight: torch.Tensor, padding=(1, 1), stride=(1, 1, 1),
@@ -396,7 +398,7 @@ def wvc_causal_conv3d_fwd(x: torch.Tensor, weight: torch.Tensor, bias: Optional[
                           dilation=(1, 1, 1), groups: int = 1,
                           workspace: Optional[torch.Tensor] = None,
                           packed_weight: Optional[torch.Tensor] = None, pad_extra=(0, 0),
-                          t_phase: int = 0, upsample_in: int = 0) -> torch.Tensor:
+                          t_phase: int = 0, upsample_in: int = 0, cu_limit: int = 0) -> torch.Tensor:
     """Causal Conv3D of one chunk (see wvc_causal_conv3d_fwd in include/wvc.h).
     ``weight`` gives the logical shape; when ``packed_weight`` (from
     wvc_conv3d_pack_weights) is given the call reads that instead.
@@ -404,11 +406,12 @@ def wvc_causal_conv3d_fwd(x: torch.Tensor, weight: torch.Tensor, bias: Optional[
     right of the frame; ``t_phase`` is the number of sequence frames before this
     chunk modulo the temporal stride; ``upsample_in`` = 2 reads x and the
     caches (frames of h x w) through a nearest 2x upsample, so y has frames of
-    2h x 2w.  Returns y (allocated if not given)."""
+    2h x 2w; ``cu_limit`` > 0 plans the grid for that many CUs (see the
+    descriptor in include/wvc.h).  Returns y (allocated if not given)."""
     lib = load()
     d, out_shape, wsrc = _conv_checks(x, weight, bias, cache_in, cache_out, residual, y, stride,
                                       padding, dilation, groups, packed_weight, pad_extra, t_phase,
-                                      upsample_in)
+                                      upsample_in, cu_limit)
     if y is None:
         y = empty_cl(out_shape, x.dtype, x.device)
     ws_bytes = 0
@@ -440,13 +443,15 @@ def wvc_causal_conv3d_norm_fwd(x: torch.Tensor, weight: torch.Tensor, gamma: tor
                                y: Optional[torch.Tensor] = None, h: Optional[torch.Tensor] = None,
                                padding=(1, 1), workspace: Optional[torch.Tensor] = None,
                                packed_weight: Optional[torch.Tensor] = None,
-                               upsample_in: int = 0) -> torch.Tensor:
+                               upsample_in: int = 0, cu_limit: int = 0) -> torch.Tensor:
     """Conv, then the RMS norm + SiLU of the layer it feeds (see
     wvc_causal_conv3d_norm_fwd in include/wvc.h): y = conv(x) + bias + residual
-    (stored only when ``y`` is given), h = SiLU(norm(y)); ``upsample_in`` as for
-    wvc_causal_conv3d_fwd.  Returns h (allocated if not given)."""
+    (stored only when ``y`` is given), h = SiLU(norm(y)); ``upsample_in`` and
+    ``cu_limit`` as for wvc_causal_conv3d_fwd.  Returns h (allocated if not
+    given)."""
     d, out_shape, wsrc = _conv_checks(x, weight, bias, cache_in, cache_out, residual, y, (1, 1, 1),
-                                      padding, (1, 1, 1), 1, packed_weight, (0, 0), 0, upsample_in)
+                                      padding, (1, 1, 1), 1, packed_weight, (0, 0), 0, upsample_in,
+                                      cu_limit)
     c_out = out_shape[1]
     _need_exact(gamma, "gamma", (c_out,), x.dtype, x.device)
     if gamma is None:
@@ -457,7 +462,7 @@ def wvc_causal_conv3d_norm_fwd(x: torch.Tensor, weight: torch.Tensor, gamma: tor
         h = empty_cl(out_shape, x.dtype, x.device)
     if workspace is None:
         need = _norm_ws_shared(tuple(x.shape), tuple(weight.shape), _dtype_code(x.dtype),
-                               tuple(padding), d.weight_layout, x.device, upsample_in)
+                               tuple(padding), d.weight_layout, x.device, upsample_in, cu_limit)
     if workspace is None and need:  # contents on entry do not matter
         workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
@@ -490,7 +495,7 @@ def wvc_causal_conv3d_fwd_noalloc(x: torch.Tensor, weight: torch.Tensor, y: torc
 
 
 def _conv_checks(x, weight, bias, cache_in, cache_out, residual, y, stride, padding, dilation,
-                 groups, packed_weight, pad_extra, t_phase, upsample_in=0):
+                 groups, packed_weight, pad_extra, t_phase, upsample_in=0, cu_limit=0):
     """Checks of a conv call's tensors against the descriptor built from x and
     the weight; returns (descriptor, output shape, weight pointer source)."""
     _need_cl(x, "x")
@@ -499,6 +504,8 @@ def _conv_checks(x, weight, bias, cache_in, cache_out, residual, y, stride, padd
     n, c, t, h, w = x.shape
     if upsample_in not in (0, 2):
         raise WvcError(WVC_ERR_ARG, f"upsample_in {upsample_in} must be 0 or 2")
+    if cu_limit < 0:
+        raise WvcError(WVC_ERR_ARG, f"cu_limit {cu_limit} must be >= 0")
     up = 2 if upsample_in == 2 else 1   # the caches keep x's frame size
     _need_exact(weight, "weight", (weight.shape[0], c) + tuple(weight.shape[2:]), x.dtype, x.device)
     _need_exact(bias, "bias", (weight.shape[0],), x.dtype, x.device)
@@ -519,7 +526,7 @@ def _conv_checks(x, weight, bias, cache_in, cache_out, residual, y, stride, padd
     stride, padding, dilation, pad_extra = tuple(stride), tuple(padding), tuple(dilation), \
         tuple(pad_extra)
     d = _conv_desc_shared(tuple(x.shape), tuple(weight.shape), code, stride, padding, dilation,
-                          groups, layout, pad_extra, t_phase, upsample_in)
+                          groups, layout, pad_extra, t_phase, upsample_in, cu_limit)
     if packed_weight is not None:
         _need_bytes(packed_weight, "packed_weight",
                     _packed_bytes_shared(tuple(weight.shape), x.dtype, padding, stride, pad_extra),
@@ -751,8 +758,9 @@ def wvc_rmsnorm_silu(x: torch.Tensor, gamma: torch.Tensor, beta: Optional[torch.
 
 
 def resblock_desc(x_shape, c_out: int, dtype: int, eps: float = 1e-12,
-                  weights_packed: bool = False) -> ResblockDesc:
+                  weights_packed: bool = False, cu_limit: int = 0) -> ResblockDesc:
     d = ResblockDesc()
+    d.cu_limit = cu_limit
     d.n, d.c_in, d.t, d.h, d.w = x_shape[0], x_shape[1], x_shape[2], x_shape[3], x_shape[4]
     d.c_out = c_out
     d.dtype = dtype
@@ -813,10 +821,10 @@ def _checked_block(x: torch.Tensor, params: dict, packed: Optional[dict]):
 
 
 @_memo
-def _block_desc_ws(x_shape, c_out, code, eps, packed, device) -> tuple:
+def _block_desc_ws(x_shape, c_out, code, eps, packed, device, cu_limit=0) -> tuple:
     """(ResblockDesc, workspace bytes) of a block call (the workspace size
     depends on the device's CU count through the split-K plan)."""
-    d = resblock_desc(x_shape, c_out, code, eps, weights_packed=packed)
+    d = resblock_desc(x_shape, c_out, code, eps, weights_packed=packed, cu_limit=cu_limit)
     return d, wvc_resblock_workspace_bytes(d)
 
 
@@ -842,10 +850,11 @@ def _check_block_params(x: torch.Tensor, params: dict, packed: Optional[dict]):
 def wvc_resblock_fwd(x: torch.Tensor, params: dict, cache1_in=None, cache1_out=None,
                      cache2_in=None, cache2_out=None, y: Optional[torch.Tensor] = None,
                      eps: float = 1e-12, workspace: Optional[torch.Tensor] = None,
-                     packed: Optional[dict] = None) -> torch.Tensor:
+                     packed: Optional[dict] = None, cu_limit: int = 0) -> torch.Tensor:
     """Wan residual block on one chunk (see wvc_resblock_fwd in include/wvc.h).
     ``params``: gamma1, beta1, w1, b1, gamma2, beta2, w2, b2[, w_short, b_short].
-    ``packed``: optional {w1, w2[, w_short]} from wvc_conv3d_pack_weights."""
+    ``packed``: optional {w1, w2[, w_short]} from wvc_conv3d_pack_weights.
+    ``cu_limit`` > 0 plans the convs' grids for that many CUs."""
     lib = load()
     c_out, p = _checked_block(x, params, packed)
     n, ci, t, h, w = x.shape
@@ -854,7 +863,7 @@ def wvc_resblock_fwd(x: torch.Tensor, params: dict, cache1_in=None, cache1_out=N
         _need_exact(cc, name, (n, ch, 2, h, w), x.dtype, x.device)
     _need_exact(y, "y", (n, c_out, t, h, w), x.dtype, x.device)
     d, need = _block_desc_ws(tuple(x.shape), c_out, _dtype_code(x.dtype), float(eps),
-                             packed is not None, x.device)
+                             packed is not None, x.device, int(cu_limit))
     if y is None:
         y = empty_cl((x.shape[0], c_out) + tuple(x.shape[2:]), x.dtype, x.device)
     if workspace is None and need:  # contents on entry do not matter
@@ -866,7 +875,7 @@ def wvc_resblock_fwd(x: torch.Tensor, params: dict, cache1_in=None, cache1_out=N
     return y
 
 
-def _block_call(x, params, packed, eps, workspace, outs):
+def _block_call(x, params, packed, eps, workspace, outs, cu_limit=0):
     """Shared marshalling of the block halves: descriptor, params struct,
     workspace (allocated when not given) and its size."""
     c_out, p = _checked_block(x, params, packed)
@@ -877,7 +886,7 @@ def _block_call(x, params, packed, eps, workspace, outs):
     for name, tt in outs:
         _need_exact(tt, name, want[name], x.dtype, x.device)
     d, need = _block_desc_ws(tuple(x.shape), c_out, _dtype_code(x.dtype), float(eps),
-                             packed is not None, x.device)
+                             packed is not None, x.device, int(cu_limit))
     if workspace is None and need:  # contents on entry do not matter
         workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
@@ -887,12 +896,12 @@ def _block_call(x, params, packed, eps, workspace, outs):
 def wvc_resblock_front(x: torch.Tensor, params: dict, cache1_in=None, cache1_out=None,
                        h2: Optional[torch.Tensor] = None, eps: float = 1e-12,
                        workspace: Optional[torch.Tensor] = None,
-                       packed: Optional[dict] = None) -> torch.Tensor:
+                       packed: Optional[dict] = None, cu_limit: int = 0) -> torch.Tensor:
     """First half of the block, h2 = SiLU(norm2(conv1(SiLU(norm1(x)))))
     (see wvc_resblock_front in include/wvc.h)."""
     d, p, c_out, workspace, ws_bytes = _block_call(
         x, params, packed, eps, workspace,
-        (("cache1_in", cache1_in), ("cache1_out", cache1_out), ("h2", h2)))
+        (("cache1_in", cache1_in), ("cache1_out", cache1_out), ("h2", h2)), cu_limit)
     if h2 is None:
         h2 = empty_cl((x.shape[0], c_out) + tuple(x.shape[2:]), x.dtype, x.device)
     _check(load().wvc_resblock_front(ctypes.byref(d), _ptr(x), _ptr(h2), ctypes.byref(p),
@@ -904,12 +913,12 @@ def wvc_resblock_front(x: torch.Tensor, params: dict, cache1_in=None, cache1_out
 def wvc_resblock_back(h2: torch.Tensor, x: torch.Tensor, params: dict, cache2_in=None,
                       cache2_out=None, y: Optional[torch.Tensor] = None, eps: float = 1e-12,
                       workspace: Optional[torch.Tensor] = None,
-                      packed: Optional[dict] = None) -> torch.Tensor:
+                      packed: Optional[dict] = None, cu_limit: int = 0) -> torch.Tensor:
     """Second half of the block, y = conv2(h2) + shortcut(x) (see
     wvc_resblock_back in include/wvc.h)."""
     d, p, c_out, workspace, ws_bytes = _block_call(
         x, params, packed, eps, workspace,
-        (("h2", h2), ("cache2_in", cache2_in), ("cache2_out", cache2_out), ("y", y)))
+        (("h2", h2), ("cache2_in", cache2_in), ("cache2_out", cache2_out), ("y", y)), cu_limit)
     if y is None:
         y = empty_cl((x.shape[0], c_out) + tuple(x.shape[2:]), x.dtype, x.device)
     _check(load().wvc_resblock_back(ctypes.byref(d), _ptr(h2), _ptr(x), _ptr(y), ctypes.byref(p),

@@ -919,11 +919,13 @@ Plan make_plan(const ConvCall &c, ConvRoute r) {
     pl.co_t = co_tile_for(c.cout, is_e4m3(c));
     pl.U = ks * ((c.cin + unit_channels(c) - 1) / unit_channels(c));
     const long spatial = (long)c.n * c.t * pl.tiles_h * pl.tiles_w;
-    const long slots = num_cus();  // one workgroup per CU
+    const long cus = num_cus();
+    // one workgroup per CU, on the CUs the call may plan for
+    const long slots = c.cu_limit > 0 && c.cu_limit < cus ? c.cu_limit : cus;
     // Small grid (fewer tiles than resident slots): order channel tiles
     // slowest, so each XCD works on (about) one channel tile and keeps that
     // slice of the weights in its L2.
-    pl.co_major = spatial * (c.cout / pl.co_t) < slots;
+    pl.co_major = spatial * (c.cout / pl.co_t) < cus;
     pl.co_tiles = c.cout / pl.co_t;
     pl.tiles = spatial * pl.co_tiles;
     // Split K when the tiles alone leave CUs idle: minimise

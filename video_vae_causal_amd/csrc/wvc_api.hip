@@ -130,6 +130,7 @@ int plan_conv(const wvc_conv3d_desc *d, ConvPlan *pl, bool count = true) {
         return fail(WVC_ERR_ARG, "t_phase %d must lie in [0, stride_t = %d)", d->t_phase, d->stride_t);
     if (d->upsample_in != 0 && d->upsample_in != 2)
         return fail(WVC_ERR_ARG, "upsample_in %d must be 0 or 2", d->upsample_in);
+    if (d->cu_limit < 0) return fail(WVC_ERR_ARG, "cu_limit %d must be >= 0", d->cu_limit);
     // Upsampled input: x and the caches hold h/2 x w/2 frames.
     const int up = d->upsample_in == 2 ? 2 : 1;
     if (up == 2 && (d->h % 2 != 0 || d->w % 2 != 0))
@@ -159,6 +160,7 @@ int plan_conv(const wvc_conv3d_desc *d, ConvPlan *pl, bool count = true) {
     c.eh = d->pad_h_extra;
     c.ew = d->pad_w_extra;
     c.up = up;
+    c.cu_limit = d->cu_limit;
 
     size_t plane_in, plane_out, v;
     bool ok = mul_ok((size_t)(d->h / up), (size_t)(d->w / up), &plane_in) &&
@@ -365,6 +367,7 @@ int plan_block(const wvc_resblock_desc *d, BlockLayout *L) {
     if (!(d->eps > 0.f)) return fail(WVC_ERR_ARG, "eps must be > 0");
     if (d->weights_packed != 0 && d->weights_packed != 1)
         return fail(WVC_ERR_ARG, "weights_packed must be 0 or 1");
+    if (d->cu_limit < 0) return fail(WVC_ERR_ARG, "cu_limit %d must be >= 0", d->cu_limit);
     const size_t pos = (size_t)d->n * d->t * d->h * d->w;
     // The convs' scratch (split-K partials, packed weights) comes first, sized
     // for the largest of the block's convs; the intermediates follow.
@@ -377,6 +380,7 @@ int plan_block(const wvc_resblock_desc *d, BlockLayout *L) {
     c.groups = 1;
     c.dtype = d->dtype;
     c.weight_layout = d->weights_packed ? WVC_WEIGHT_PACKED : WVC_WEIGHT_STANDARD;
+    c.cu_limit = d->cu_limit;
     size_t need = 0;
     for (int k = 0; k < 3; ++k) {
         if (k == 1) c.c_in = d->c_out;
@@ -766,6 +770,7 @@ int check_block(const wvc_resblock_desc *d, const wvc_resblock_params *p, bool f
     c1->groups = 1;
     c1->dtype = d->dtype;
     c1->weight_layout = d->weights_packed ? WVC_WEIGHT_PACKED : WVC_WEIGHT_STANDARD;
+    c1->cu_limit = d->cu_limit;
     *c2 = *c1;
     c2->c_in = d->c_out;
     // Validate the convs (and strict mode) before enqueueing anything.
@@ -858,6 +863,7 @@ int plan_block8(const wvc_resblock_desc *d, Block8Layout *L, wvc_conv3d_desc *c,
     c->groups = 1;
     c->dtype = WVC_E4M3;
     c->weight_layout = d->weights_packed ? WVC_WEIGHT_PACKED : WVC_WEIGHT_STANDARD;
+    c->cu_limit = d->cu_limit;
     const int rc = plan_conv(c, pl, count);
     if (rc) return rc;
     const size_t pos = (size_t)d->n * d->t * d->h * d->w;

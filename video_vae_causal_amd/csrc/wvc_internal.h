@@ -73,6 +73,7 @@ struct ConvCall {
     int eh, ew;            // extra zero rows below / columns right of the frame
     int up;                // 2: x and the caches hold h/2 x w/2 frames, read through a
                            // nearest 2x upsample (MFMA 3x3x3 route only); else 1
+    int cu_limit;          // > 0: plan the split-K grid for this many CUs
     // WVC_E4M3 calls: x, cache and weight hold E4M3 codes; bias, residual and
     // y are bf16; the sum is multiplied by xscale * wscale[co].
     float xscale;

@@ -49,12 +49,13 @@ def _cached_buf(bufs: Dict[str, torch.Tensor], name: str, shape, like: torch.Ten
 
 
 def _norm_workspace(ws: Optional[torch.Tensor], x: torch.Tensor, weight: torch.Tensor, padding,
-                    packed: Optional[torch.Tensor], upsample_in: int = 0) -> torch.Tensor:
+                    packed: Optional[torch.Tensor], upsample_in: int = 0,
+                    cu_limit: int = 0) -> torch.Tensor:
     """A workspace for wvc_causal_conv3d_norm_fwd on chunks of x's shape:
     ``ws`` when it is large enough, else a new one."""
     layout = L.WVC_WEIGHT_PACKED if packed is not None else L.WVC_WEIGHT_STANDARD
     need = L._norm_ws_shared(tuple(x.shape), tuple(weight.shape), L._dtype_code(x.dtype),
-                             tuple(padding), layout, x.device, upsample_in)
+                             tuple(padding), layout, x.device, upsample_in, cu_limit)
     if ws is None or ws.numel() < need:
         ws = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
     return ws
@@ -117,6 +118,7 @@ class CausalConv3d:
         self.weight = weight
         self.bias = bias
         self.upsample_in = upsample_in
+        self.cu_limit = 0   # > 0: plan the conv's grid for that many CUs (see set_cu_limit)
         self.frames = L.wvc_conv3d_cache_frames(tuple(weight.shape))
         self.cache: Optional[_PingPong] = None
         self.ws: Optional[torch.Tensor] = None
@@ -144,7 +146,8 @@ class CausalConv3d:
             self.ws = torch.empty(need, dtype=torch.uint8, device=x.device)
         y = L.wvc_causal_conv3d_fwd(x, self.weight, self.bias, cin, cout, residual, y,
                                     padding=self.padding, workspace=self.ws if need else None,
-                                    packed_weight=self.packed, upsample_in=self.upsample_in)
+                                    packed_weight=self.packed, upsample_in=self.upsample_in,
+                                    cu_limit=self.cu_limit)
         if self.frames:
             self.cache.flip()
         return y
@@ -161,22 +164,24 @@ class CausalConv3d:
         cin = self.cache.cin if self.frames else None
         cout = self.cache.cout if self.frames else None
         self.nws = _norm_workspace(self.__dict__.get("nws"), x, self.weight, self.padding, self.packed,
-                                   self.upsample_in)
+                                   self.upsample_in, self.cu_limit)
         L.wvc_causal_conv3d_norm_fwd(x, self.weight, gamma, self.bias, beta, eps, cin, cout, residual,
                                      y, h, padding=self.padding, workspace=self.nws,
-                                     packed_weight=self.packed, upsample_in=self.upsample_in)
+                                     packed_weight=self.packed, upsample_in=self.upsample_in,
+                                     cu_limit=self.cu_limit)
         if self.frames:
             self.cache.flip()
         return h
 
     def _ws_need(self, x: torch.Tensor) -> int:
         """Workspace bytes of a chunk of x's shape (asked once per shape)."""
-        key = (x.shape, x.dtype, x.device)
+        key = (x.shape, x.dtype, x.device, self.cu_limit)
         need = self.__dict__.setdefault("_needs", {}).get(key)
         if need is None:
             layout = L.WVC_WEIGHT_PACKED if self.packed is not None else L.WVC_WEIGHT_STANDARD
             d = L.conv_desc(tuple(x.shape), tuple(self.weight.shape), L._dtype_code(x.dtype),
-                            padding=self.padding, weight_layout=layout, upsample_in=self.upsample_in)
+                            padding=self.padding, weight_layout=layout, upsample_in=self.upsample_in,
+                            cu_limit=self.cu_limit)
             need = self._needs[key] = L.wvc_causal_conv3d_workspace_bytes(d)
         return need
 
@@ -204,6 +209,7 @@ class ResBlock:
     def __init__(self, params: Dict[str, torch.Tensor], eps: float = 1e-12):
         self.p = params
         self.eps = eps
+        self.cu_limit = 0   # > 0: plan the convs' grids for that many CUs
         self.c1: Optional[_PingPong] = None
         self.c2: Optional[_PingPong] = None
         self.ws: Optional[torch.Tensor] = None
@@ -240,11 +246,12 @@ class ResBlock:
 
     def _ws_need(self, x: torch.Tensor) -> int:
         """Workspace bytes of a chunk of x's shape (asked once per shape)."""
-        key = (x.shape, x.dtype, x.device)
+        key = (x.shape, x.dtype, x.device, self.cu_limit)
         need = self.__dict__.setdefault("_needs", {}).get(key)
         if need is None:
             d = L.resblock_desc(tuple(x.shape), self.p["w1"].shape[0], L._dtype_code(x.dtype),
-                                self.eps, weights_packed=self.packed is not None)
+                                self.eps, weights_packed=self.packed is not None,
+                                cu_limit=self.cu_limit)
             need = self._needs[key] = L.wvc_resblock_workspace_bytes(d)
         return need
 
@@ -254,7 +261,8 @@ class ResBlock:
         if self.ws is None or self.ws.numel() < need:
             self.ws = torch.empty(need, dtype=torch.uint8, device=x.device)
         y = L.wvc_resblock_fwd(x, self.p, self.c1.cin, self.c1.cout, self.c2.cin, self.c2.cout,
-                               y=y, eps=self.eps, workspace=self.ws, packed=self.packed)
+                               y=y, eps=self.eps, workspace=self.ws, packed=self.packed,
+                               cu_limit=self.cu_limit)
         self.c1.flip()
         self.c2.flip()
         return y
@@ -278,7 +286,8 @@ class ResBlock:
         """First half (norm1, conv1, norm2) into h2; advances cache1."""
         self._ensure(x)
         L.wvc_resblock_front(x, self.p, self.c1.cin, self.c1.cout, h2=h2, eps=self.eps,
-                             workspace=self._half_ws("ws_front", x), packed=self.packed)
+                             workspace=self._half_ws("ws_front", x), packed=self.packed,
+                             cu_limit=self.cu_limit)
         self.c1.flip()
         return h2
 
@@ -288,7 +297,8 @@ class ResBlock:
         if not _fits(self.c2, (n, self.p["w1"].shape[0], CACHE_T, h, w)):
             raise ValueError("back() of a chunk whose front() ran at another size")
         L.wvc_resblock_back(h2, x, self.p, self.c2.cin, self.c2.cout, y=y, eps=self.eps,
-                            workspace=self._half_ws("ws_back", x), packed=self.packed)
+                            workspace=self._half_ws("ws_back", x), packed=self.packed,
+                            cu_limit=self.cu_limit)
         self.c2.flip()
         return y
 
@@ -298,10 +308,11 @@ class ResBlock:
         self._ensure(h1)
         p, pk = self.p, self.packed
         self.ws_f1 = _norm_workspace(self.__dict__.get("ws_f1"), h1, p["w1"], (1, 1),
-                                     None if pk is None else pk["w1"])
+                                     None if pk is None else pk["w1"], cu_limit=self.cu_limit)
         L.wvc_causal_conv3d_norm_fwd(h1, p["w1"], p["gamma2"], p.get("b1"), p.get("beta2"), self.eps,
                                      self.c1.cin, self.c1.cout, None, None, h2, workspace=self.ws_f1,
-                                     packed_weight=None if pk is None else pk["w1"])
+                                     packed_weight=None if pk is None else pk["w1"],
+                                     cu_limit=self.cu_limit)
         self.c1.flip()
         return h2
 
@@ -317,10 +328,11 @@ class ResBlock:
             raise ValueError("back_norm() of a chunk whose front ran at another size")
         p, pk = self.p, self.packed
         self.ws_b1 = _norm_workspace(self.__dict__.get("ws_b1"), h2, p["w2"], (1, 1),
-                                     None if pk is None else pk["w2"])
+                                     None if pk is None else pk["w2"], cu_limit=self.cu_limit)
         L.wvc_causal_conv3d_norm_fwd(h2, p["w2"], gamma, p.get("b2"), beta, eps, self.c2.cin,
                                      self.c2.cout, x, y, h_next, workspace=self.ws_b1,
-                                     packed_weight=None if pk is None else pk["w2"])
+                                     packed_weight=None if pk is None else pk["w2"],
+                                     cu_limit=self.cu_limit)
         self.c2.flip()
         return y
 
@@ -513,7 +525,23 @@ class DecoderStack(Stream):
         """Whether conv_up reads its input through the upsample itself."""
         return getattr(self.conv_up, "upsample_in", 0) == 2
 
+    # The low-resolution convs plan their grids for this share of the CUs
+    # (their split-K count drops), which leaves CUs to the other stream's
+    # full-resolution convs when the stack runs in the two-stream pipeline.
+    # Sequential runs use the same plans, so both give the same bits.
+    LOW_RES_CU_SHARE = (5, 8)
+
+    def set_cu_limit(self, cus: int):
+        """Plan the low-resolution layers' grids for ``cus`` CUs (0: all)."""
+        for layer in [self.conv_in] + self.rbs[:2]:
+            if hasattr(layer, "cu_limit"):
+                layer.cu_limit = cus
+
     def start(self, n: int, h: int, w: int):
+        num, den = self.LOW_RES_CU_SHARE
+        dev = self.conv_in.weight.device
+        if dev.type == "cuda":
+            self.set_cu_limit(torch.cuda.get_device_properties(dev).multi_processor_count * num // den)
         self.conv_in.start(n, h, w)
         for rb in self.rbs[:2]:
             rb.start(n, h, w)
