@@ -90,9 +90,12 @@ def parse():
                          "the second part of frame i runs next to the first part of frame i+1 "
                          "(auto: on for the decoder stack, where it is faster; off for the single "
                          "residual block, where it is not)")
-    ap.add_argument("--graph", choices=("on", "off"), default="off",
-                    help="replay the whole step as one recorded HIP graph (after the eager "
-                         "warm-up) instead of enqueuing its launches one by one")
+    ap.add_argument("--graph", choices=("auto", "on", "off"), default="auto",
+                    help="replay recorded HIP graphs instead of enqueuing the launches one by one: "
+                         "the whole step as one graph (after the eager warm-up), or with the "
+                         "two-stream pipeline each frame's two parts as graphs (auto: on for the "
+                         "8-bit decoder stack, whose eager launches the host cannot issue as fast "
+                         "as the GPU runs them; off elsewhere)")
     ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "traffic.json"),
                     help="measured HBM bytes per launch (from rocprofv3 --pmc), if present")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -111,9 +114,20 @@ def parse():
 
 
 PIPELINE = False  # set from --pipeline in main()
+PIPE_GRAPH = False  # --pipeline on with --graph on: each chunk's two parts replayed as graphs
 OPERANDS = "random"  # set from --operands in main()
 PIPELINED = ("resblock_384_60x104", "decoder_stack_48_30x52", "decoder_stack_48_30x52_e4m3")
 PIPELINE_AUTO = ("decoder_stack_48_30x52", "decoder_stack_48_30x52_e4m3")  # where it measured faster
+GRAPH_AUTO = ("decoder_stack_48_30x52_e4m3",)  # where graph replay measured faster
+
+
+def make_pipe(stack, chunk_shape):
+    """The two-stream pipeline over ``stack``: eager launches, or with
+    PIPE_GRAPH each chunk's two parts replayed as recorded graphs."""
+    from video_vae_causal_amd import stream
+    if PIPE_GRAPH:
+        return stream.PipelineGraph(stack, tuple(chunk_shape))
+    return stream.Pipeline(stack)
 
 
 def cl(t):
@@ -233,7 +247,7 @@ def wl_resblock():
     rb = stream.ResBlock(p)
     rb.start(n, h, w)
 
-    pipe = stream.Pipeline(rb) if PIPELINE else None
+    pipe = make_pipe(rb, frames[0].shape) if PIPELINE else None
 
     def step():
         rb.reset()
@@ -480,7 +494,7 @@ def wl_decoder():
     out = L.empty_cl((n, width, t, 2 * h, 2 * w))
     outs = [out[:, :, i:i + 1] for i in range(t)]
 
-    pipe = stream.Pipeline(stack) if PIPELINE else None
+    pipe = make_pipe(stack, frames[0].shape) if PIPELINE else None
 
     def step():
         stack.reset()
@@ -533,7 +547,7 @@ def wl_decoder_e4m3():
     stack.start(n, h, w)
     out = L.empty_cl((n, width, t, 2 * h, 2 * w))
     outs = [out[:, :, i:i + 1] for i in range(t)]
-    pipe = stream.Pipeline(stack) if PIPELINE else None
+    pipe = make_pipe(stack, frames[0].shape) if PIPELINE else None
 
     def step():
         stack.reset()
@@ -1051,11 +1065,9 @@ def main():
             sys.exit(2)
         args.no_cpu_baseline = True  # the oracle's sample is random data
     if args.pipeline == "auto":
-        args.pipeline = "on" if args.workload in PIPELINE_AUTO and args.graph == "off" else "off"
-    if args.pipeline == "on" and args.graph == "on":
-        print("--pipeline on runs two streams, which are not recorded into a graph; "
-              "use one of the two", file=sys.stderr)
-        sys.exit(2)
+        args.pipeline = "on" if args.workload in PIPELINE_AUTO else "off"
+    if args.graph == "auto":
+        args.graph = "on" if args.workload in GRAPH_AUTO else "off"
     import torch
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
@@ -1067,14 +1079,17 @@ def main():
     L.load()
     torch.cuda.set_device(0)
 
-    global PIPELINE, TILING, FUSE_NORM, OPERANDS
+    global PIPELINE, PIPE_GRAPH, TILING, FUSE_NORM, OPERANDS
     OPERANDS = args.operands
     PIPELINE = args.pipeline == "on"
+    # two streams are not recorded into one graph: with the pipeline, --graph
+    # records each chunk's two parts (stream.PipelineGraph) instead of the step
+    PIPE_GRAPH = PIPELINE and args.graph == "on" and args.workload in PIPELINED
     FUSE_NORM = args.fuse_norm == "on"
     TILING = args.tiling
     step, info = WORKLOADS[args.workload]()
     timed = step
-    if args.graph == "on":
+    if args.graph == "on" and not PIPE_GRAPH:
         # The eager warm-up sizes every workspace and buffer; the graph then
         # records one whole step (cache resets included) and each timed call
         # replays it.

@@ -545,11 +545,13 @@ def wvc_resblock_e4m3_workspace_bytes(d: ResblockDesc) -> int:
 def wvc_resblock_e4m3_fwd(x: torch.Tensor, params: dict, s1: float, s2: float, cache1_in=None,
                           cache1_out=None, cache2_in=None, cache2_out=None,
                           y: Optional[torch.Tensor] = None, eps: float = 1e-12,
-                          workspace: Optional[torch.Tensor] = None, packed: bool = False) -> torch.Tensor:
+                          workspace: Optional[torch.Tensor] = None, packed: bool = False,
+                          cu_limit: int = 0) -> torch.Tensor:
     """The residual block on the 8-bit path (see wvc_resblock_e4m3_fwd in
     include/wvc.h).  ``params`` holds gamma1, beta1, gamma2, beta2, b1, b2
     (bf16 vectors), w1, w2 (uint8 E4M3 codes, packed when ``packed``) and
-    w1_scale, w2_scale (float32 [C]).  Caches are uint8 codes."""
+    w1_scale, w2_scale (float32 [C]).  Caches are uint8 codes.  ``cu_limit``
+    > 0 plans the convs' split-K grids for that many CUs."""
     lib = load()
     _need_cl(x, "x")
     n, c, t, h, w = x.shape
@@ -568,7 +570,7 @@ def wvc_resblock_e4m3_fwd(x: torch.Tensor, params: dict, s1: float, s2: float, c
         if params.get(k) is None or params[k].numel() * params[k].element_size() != wbytes \
                 or params[k].dtype != torch.uint8 or params[k].device != x.device:
             raise ValueError(f"{k} must be {wbytes} bytes of E4M3 codes (uint8) on {x.device}")
-    d = resblock_desc(tuple(x.shape), c, WVC_BF16, eps, weights_packed=packed)
+    d = resblock_desc(tuple(x.shape), c, WVC_BF16, eps, weights_packed=packed, cu_limit=cu_limit)
     if y is None:
         y = empty_cl(x.shape, x.dtype, x.device)
     if workspace is None:
@@ -641,13 +643,14 @@ def wvc_causal_conv3d_e4m3_fwd(x: torch.Tensor, x_scale: float, weight: torch.Te
                                y: Optional[torch.Tensor] = None,
                                workspace: Optional[torch.Tensor] = None,
                                packed_weight: Optional[torch.Tensor] = None,
-                               upsample_in: int = 0) -> torch.Tensor:
+                               upsample_in: int = 0, cu_limit: int = 0) -> torch.Tensor:
     """Causal 3x3x3 conv of E4M3 operands (see wvc_causal_conv3d_e4m3_fwd in
     include/wvc.h).  x, caches and weight are uint8 tensors of E4M3 codes in
     channels_last_3d; w_scale is a float32 vector [C_out]; bias, residual and
     y are bfloat16.  ``upsample_in`` = 2 reads x and the caches through a
-    nearest 2x upsample (y then has frames of twice x's).  Returns y
-    (allocated if not given)."""
+    nearest 2x upsample (y then has frames of twice x's); ``cu_limit`` > 0
+    plans the split-K grid for that many CUs.  Returns y (allocated if not
+    given)."""
     lib = load()
     _need_cl(x, "x")
     _need_cl(weight, "weight")
@@ -667,7 +670,7 @@ def wvc_causal_conv3d_e4m3_fwd(x: torch.Tensor, x_scale: float, weight: torch.Te
         _need_exact(tt, name, (n, co, t, h * up, w * up), torch.bfloat16, x.device)
     layout = WVC_WEIGHT_STANDARD if packed_weight is None else WVC_WEIGHT_PACKED
     d = conv_desc(tuple(x.shape), tuple(weight.shape), WVC_E4M3, weight_layout=layout,
-                  upsample_in=upsample_in)
+                  upsample_in=upsample_in, cu_limit=cu_limit)
     if packed_weight is not None:
         _need_bytes(packed_weight, "packed_weight",
                     wvc_conv3d_packed_weight_bytes(tuple(weight.shape), torch.uint8), x.device)

@@ -357,6 +357,7 @@ class CausalConv3dE4M3:
                  upsample_in: int = 0):
         self.weight, self.bias, self.scale = weight, bias, float(scale)
         self.upsample_in = upsample_in
+        self.cu_limit = 0   # > 0: plan the conv's grid for that many CUs
         self.wq, self.wsc = L.wvc_quantize_rows_e4m3(weight)
         self.packed = L.wvc_conv3d_pack_weights(self.wq)
         self.cache: Optional[_PingPong] = None
@@ -390,13 +391,14 @@ class CausalConv3dE4M3:
         q = _cached_buf(self.bufs, "q", x.shape, x.new_empty(0, dtype=torch.uint8))
         L.wvc_quantize_e4m3(x, self.scale, q=q)
         d = L.conv_desc(tuple(q.shape), tuple(self.wq.shape), L.WVC_E4M3, weight_layout=L.WVC_WEIGHT_PACKED,
-                        upsample_in=self.upsample_in)
+                        upsample_in=self.upsample_in, cu_limit=self.cu_limit)
         need = L.wvc_causal_conv3d_workspace_bytes(d)
         if need and (self.ws is None or self.ws.numel() < need):
             self.ws = torch.empty(need, dtype=torch.uint8, device=x.device)
         y = L.wvc_causal_conv3d_e4m3_fwd(q, self.scale, self.wq, self.wsc, self.bias, self.cache.cin,
                                          self.cache.cout, None, y, workspace=self.ws if need else None,
-                                         packed_weight=self.packed, upsample_in=self.upsample_in)
+                                         packed_weight=self.packed, upsample_in=self.upsample_in,
+                                         cu_limit=self.cu_limit)
         self.cache.flip()
         return y
 
@@ -429,6 +431,7 @@ class ResBlockE4M3:
         self.c1: Optional[_PingPong] = None
         self.c2: Optional[_PingPong] = None
         self.ws: Optional[torch.Tensor] = None
+        self.cu_limit = 0   # > 0: plan the convs' grids for that many CUs
 
     def start(self, n: int, h: int, w: int):
         c = self.p["w1"].shape[0]
@@ -459,13 +462,14 @@ class ResBlockE4M3:
         n, c, _, h, w = x.shape
         if not _fits(self.c1, (n, c, CACHE_T, h, w)):
             self.start(n, h, w)
-        d = L.resblock_desc(tuple(x.shape), x.shape[1], L.WVC_BF16, self.eps, weights_packed=True)
+        d = L.resblock_desc(tuple(x.shape), x.shape[1], L.WVC_BF16, self.eps, weights_packed=True,
+                            cu_limit=self.cu_limit)
         need = L.wvc_resblock_e4m3_workspace_bytes(d)
         if self.ws is None or self.ws.numel() < need:
             self.ws = torch.empty(max(1, need), dtype=torch.uint8, device=x.device)
         y = L.wvc_resblock_e4m3_fwd(x, self.q8, self.s1, self.s2, self.c1.cin, self.c1.cout,
                                     self.c2.cin, self.c2.cout, y=y, eps=self.eps, workspace=self.ws,
-                                    packed=True)
+                                    packed=True, cu_limit=self.cu_limit)
         self.c1.flip()
         self.c2.flip()
         return y
@@ -837,6 +841,134 @@ class Pipeline:
         for ev, st in zip(self._ev_join, (sa, sb)):
             ev.record(st)
             main.wait_event(ev)
+
+
+
+class PipelineGraph:
+    """The two-stream pipeline of ``Pipeline`` with each chunk's two parts
+    replayed as HIP graphs, so the host enqueues two graph launches, two
+    copies and four event operations per chunk instead of every library call.
+
+    Each part is recorded alone on one stream (a recording holds no
+    dependency between streams); the replays go to streams A and B with the
+    events of ``Pipeline.run`` between them.  A recording names fixed
+    buffers: buffer set k has its own input chunk ``x[k]`` and output chunk
+    ``y[k]``, and ``run`` copies each chunk into ``x[k]`` on A before the
+    first part and ``y[k]`` into the caller's output on B after the second.
+    Chunk i reads the caches chunk i-1 wrote, so the two buffers of every
+    ping-pong swap roles from chunk to chunk; with ``slots`` buffer sets the
+    (buffer set, cache parity) pairs repeat every lcm(slots, 2) chunks, and
+    that many chunks are recorded.  The replays make the calls the eager
+    pipeline makes, on the same buffers' contents, so the outputs are bitwise
+    those of ``Pipeline.run`` and of the sequential loop.
+
+    The stack's ping-pong state follows the replays (as for ``FrameGraph``),
+    so eager chunks, checkpoints and replays can be mixed; ``reset()`` starts
+    a new sequence."""
+
+    def __init__(self, stack, x_shape: Sequence[int], split: Optional[int] = None, slots: int = 3,
+                 dtype=torch.bfloat16, device=None):
+        dev = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
+        self.stack, self.device, self.slots = stack, dev, slots
+        self.split = split if split is not None else getattr(stack, "PIPELINE_SPLIT", 1)
+        self.period = slots if slots % 2 == 0 else 2 * slots
+        n, c, t, h, w = x_shape
+        run1 = stack.chunk if hasattr(stack, "chunk") else (lambda x, out=None: stack(x, y=out))
+        self.x = [L.empty_cl(tuple(x_shape), dtype, dev) for _ in range(slots)]
+        for xb in self.x:
+            L.wvc_cache_reset(xb)
+        stack.start(n, h, w)
+        y0 = run1(self.x[0])             # an eager chunk gives the output shape
+        self.y = [L.empty_cl(tuple(y0.shape), y0.dtype, dev) for _ in range(slots)]
+        self._bufs = [{} for _ in range(slots)]
+        self._pps = stack.pingpongs()
+        # an eager pass over one period sizes every buffer and workspace
+        for r in range(self.period):
+            stages = self._stages(r)
+            if not 0 < self.split < len(stages):
+                raise ValueError(f"split {self.split} must cut the {len(stages)} stages in two")
+            for stage in stages:
+                stage()
+        self._materialize()
+        self.graphs = []
+        for r in range(self.period):
+            stages = self._stages(r)
+            ga = capture(lambda: [st() for st in stages[:self.split]], dev)
+            gb = capture(lambda: [st() for st in stages[self.split:]], dev)
+            self.graphs.append((ga, gb))
+        # every layer flipped its caches once per recorded chunk, an even
+        # number of times: the parity is back where the recording started
+        self.streams = [torch.cuda.Stream(dev), torch.cuda.Stream(dev)]
+        self._ev_a = [torch.cuda.Event() for _ in range(slots)]
+        self._ev_b = [torch.cuda.Event() for _ in range(slots)]
+        self._ev_fork = torch.cuda.Event()
+        self._ev_join = [torch.cuda.Event(), torch.cuda.Event()]
+        self.reset()
+
+    def _stages(self, r: int):
+        k = r % self.slots
+        bufs = self._bufs[k]
+        return self.stack.stages(self.x[k], self.y[k],
+                                 lambda name, shape, like: _cached_buf(bufs, name, shape, like))
+
+    def _materialize(self):
+        """Recorded calls name both buffers of every ping-pong: a fresh cache
+        is written as zeros instead of passed as NULL."""
+        self.stack.reset()
+        for pp in self._pps:
+            pp.materialize()
+
+    def reset(self):
+        """A new sequence: zero caches, recording 0 next."""
+        self._materialize()
+        self.next = 0
+
+    def run(self, chunks: Sequence[torch.Tensor], outs: Sequence[torch.Tensor]):
+        """Run every chunk in order (chunks[i] -> outs[i]) from the stack's
+        current cache state; the current stream waits for all of it before
+        this returns.  Each chunk must have the recorded shape and each
+        output the shape of the stack's output chunk."""
+        if torch.cuda.is_current_stream_capturing():
+            raise RuntimeError("PipelineGraph.run replays graphs on two streams and cannot itself "
+                               "be recorded into a graph")
+        for pp in self._pps:
+            pp.materialize()    # eager chunks since reset() may have left a fresh cache
+        r = self.next
+        if self._pps and r % 2 != self._pps[0].cur:
+            r = (r + 1) % self.period    # eager chunks moved the parity
+        main = torch.cuda.current_stream(self.device)
+        sa, sb = self.streams
+        self._ev_fork.record(main)
+        sa.wait_event(self._ev_fork)
+        sb.wait_event(self._ev_fork)
+        for i, (x, y) in enumerate(zip(chunks, outs)):
+            k = r % self.slots
+            ga, gb = self.graphs[r]
+            with torch.cuda.stream(sa):
+                if i >= self.slots:
+                    sa.wait_event(self._ev_b[k])   # B is done with this buffer set
+                self.x[k].copy_(x)
+                ga.launch(sa)
+                self._ev_a[k].record(sa)
+            with torch.cuda.stream(sb):
+                sb.wait_event(self._ev_a[k])
+                gb.launch(sb)
+                y.copy_(self.y[k])
+                self._ev_b[k].record(sb)
+            x.record_stream(sa)
+            y.record_stream(sb)
+            for pp in self._pps:
+                pp.flip()
+            r = (r + 1) % self.period
+        self.next = r
+        for ev, st in zip(self._ev_join, (sa, sb)):
+            ev.record(st)
+            main.wait_event(ev)
+
+    def close(self):
+        for ga, gb in self.graphs:
+            ga.close()
+            gb.close()
 
 
 def tile_origins(size: int, tile: int, stride: int) -> List[int]:
