@@ -123,10 +123,11 @@ GRAPH_AUTO = ("decoder_stack_48_30x52_e4m3",)  # where graph replay measured fas
 
 def make_pipe(stack, chunk_shape):
     """The two-stream pipeline over ``stack``: eager launches, or with
-    PIPE_GRAPH each chunk's two parts replayed as recorded graphs."""
+    PIPE_GRAPH each chunk's two parts replayed as recorded graphs, bound to
+    the step's own chunk and output tensors (no copies)."""
     from video_vae_causal_amd import stream
     if PIPE_GRAPH:
-        return stream.PipelineGraph(stack, tuple(chunk_shape))
+        return stream.PipelineGraph(stack, tuple(chunk_shape), bind=True)
     return stream.Pipeline(stack)
 
 

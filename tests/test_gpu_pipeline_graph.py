@@ -8,7 +8,8 @@ comparison here is bitwise against the sequential chunk loop, which the
 stack tests hold to the oracle.  Definitions: "Cosmos3 Wan VAE -- engine size
 vs runtime context memory", sections 8.5 (per-layer cache) and 10.4
 (residual block).  Every test replays several times with eager work and
-synchronisations in between.
+synchronisations in between; the bound mode (recordings that read and write
+the caller's tensors, no copies) is held to the same comparisons.
 """
 import pytest
 import torch
@@ -37,17 +38,18 @@ def run_passes(stack, pipe, frames, outs, out, seq, what, reps=3, between=None):
             torch.cuda.synchronize()
 
 
-@pytest.mark.parametrize("t,slots", [(7, 3), (5, 2), (2, 3)])
-def test_small_decoder_graph_pipeline_equals_sequential(t, slots):
+@pytest.mark.parametrize("t,slots,bind", [(7, 3, False), (5, 2, False), (2, 3, False), (7, 3, True),
+                                          (5, 2, True)])
+def test_small_decoder_graph_pipeline_equals_sequential(t, slots, bind):
     d = inputs.decoder_inputs(seed=17, shape=(1, 16, t, 6, 9), width=64)
     pd, lat = stack_dev(d["p"]), to_dev(d["latent"])
-    print(f"[case] graph-replayed pipeline, small decoder t={t} slots={slots}", flush=True)
+    print(f"[case] graph-replayed pipeline, small decoder t={t} slots={slots} bind={bind}", flush=True)
     seq = stream.DecoderStack(pd).run(lat, chunk_frames=1)
     stack = stream.DecoderStack(pd)
     frames = [cl(lat[:, :, i:i + 1]) for i in range(t)]
     out = L.empty_cl(seq.shape)
     outs = [out[:, :, i:i + 1] for i in range(t)]
-    pipe = stream.PipelineGraph(stack, frames[0].shape, slots=slots)
+    pipe = stream.PipelineGraph(stack, frames[0].shape, slots=slots, bind=bind)
     try:
         other_ref = stream.DecoderStack(pd).run(lat, chunk_frames=t)
 
@@ -70,24 +72,31 @@ def test_small_decoder_graph_pipeline_equals_sequential(t, slots):
             pipe.run(frames[1:], outs[1:])
             torch.cuda.synchronize()
             assert torch.equal(out, seq), "a sequence split over two run() calls differs"
+        if bind:
+            # every (recording, chunk, output) triple met so far has its pair
+            # of graphs; a repeated pass records nothing new
+            n = len(pipe._bound)
+            run_passes(stack, pipe, frames, outs, out, seq, "bound, repeated", reps=1)
+            assert len(pipe._bound) == n
     finally:
         torch.cuda.synchronize()
         pipe.close()
 
 
-def test_decoder_21_frames_graph_pipeline_equals_sequential():
+@pytest.mark.parametrize("bind", [False, True])
+def test_decoder_21_frames_graph_pipeline_equals_sequential(bind):
     """Full-width decoder stack (48-ch latent, 384 ch, 30x52 -> 60x104), 21
     latent frames, the shape the decoder measurement streams."""
     d = inputs.decoder_inputs(seed=5)
     pd, lat = stack_dev(d["p"]), to_dev(d["latent"])
     t = lat.shape[2]
-    print("[case] graph-replayed pipeline, decoder 21 frames", flush=True)
+    print(f"[case] graph-replayed pipeline, decoder 21 frames, bind={bind}", flush=True)
     seq = stream.DecoderStack(pd).run(lat, chunk_frames=1)
     stack = stream.DecoderStack(pd)
     frames = [cl(lat[:, :, i:i + 1]) for i in range(t)]
     out = L.empty_cl(seq.shape)
     outs = [out[:, :, i:i + 1] for i in range(t)]
-    pipe = stream.PipelineGraph(stack, frames[0].shape)
+    pipe = stream.PipelineGraph(stack, frames[0].shape, bind=bind)
     try:
         run_passes(stack, pipe, frames, outs, out, seq, "decoder 21 frames", reps=2)
     finally:
@@ -95,7 +104,8 @@ def test_decoder_21_frames_graph_pipeline_equals_sequential():
         pipe.close()
 
 
-def test_e4m3_decoder_graph_pipeline_equals_sequential():
+@pytest.mark.parametrize("bind", [False, True])
+def test_e4m3_decoder_graph_pipeline_equals_sequential(bind):
     from test_gpu_fp8 import DEC8_SCALES
     d = inputs.decoder_inputs(seed=27, shape=(1, 48, 5, 10, 16), width=128)
     pd, lat = stack_dev(d["p"]), to_dev(d["latent"])
@@ -108,7 +118,7 @@ def test_e4m3_decoder_graph_pipeline_equals_sequential():
     stack = stream.DecoderStackE4M3(pd, DEC8_SCALES)
     out = L.empty_cl(seq.shape)
     outs = [out[:, :, i:i + 1] for i in range(t)]
-    pipe = stream.PipelineGraph(stack, frames[0].shape)
+    pipe = stream.PipelineGraph(stack, frames[0].shape, bind=bind)
     try:
         run_passes(stack, pipe, frames, outs, out, seq, "8-bit decoder")
     finally:

@@ -864,12 +864,23 @@ class PipelineGraph:
 
     The stack's ping-pong state follows the replays (as for ``FrameGraph``),
     so eager chunks, checkpoints and replays can be mixed; ``reset()`` starts
-    a new sequence."""
+    a new sequence.
+
+    With ``bind=True`` the recordings read the caller's chunk and write the
+    caller's output tensor themselves, with no copies: a pair of graphs is
+    recorded the first time a (recording, chunk tensor, output tensor)
+    combination is run and replayed after that.  This suits callers that pass
+    the same tensors on every pass (a preallocated sequence); at most
+    ``MAX_BOUND`` pairs are kept, the oldest released first.  The tensors
+    must stay unchanged and alive until the pass has finished."""
+
+    MAX_BOUND = 512
 
     def __init__(self, stack, x_shape: Sequence[int], split: Optional[int] = None, slots: int = 3,
-                 dtype=torch.bfloat16, device=None):
+                 dtype=torch.bfloat16, device=None, bind: bool = False):
         dev = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
-        self.stack, self.device, self.slots = stack, dev, slots
+        self.stack, self.device, self.slots, self.bind = stack, dev, slots, bind
+        self._bound: Dict[tuple, tuple] = {}
         self.split = split if split is not None else getattr(stack, "PIPELINE_SPLIT", 1)
         self.period = slots if slots % 2 == 0 else 2 * slots
         n, c, t, h, w = x_shape
@@ -905,11 +916,39 @@ class PipelineGraph:
         self._ev_join = [torch.cuda.Event(), torch.cuda.Event()]
         self.reset()
 
-    def _stages(self, r: int):
+    def _stages(self, r: int, x=None, y=None):
         k = r % self.slots
         bufs = self._bufs[k]
-        return self.stack.stages(self.x[k], self.y[k],
+        return self.stack.stages(self.x[k] if x is None else x, self.y[k] if y is None else y,
                                  lambda name, shape, like: _cached_buf(bufs, name, shape, like))
+
+    @staticmethod
+    def _key(r: int, x: torch.Tensor, y: torch.Tensor) -> tuple:
+        return (r, x.data_ptr(), tuple(x.shape), x.stride(), x.dtype,
+                y.data_ptr(), tuple(y.shape), y.stride(), y.dtype)
+
+    def _record_bound(self, todo: List[tuple]):
+        """Record the graph pairs of (r, chunk, output) triples that have none:
+        each at cache parity r % 2, then the stack's cache state as it was."""
+        saved = [(pp.cur, pp.fresh) for pp in self._pps]
+        try:
+            for r, x, y in todo:
+                if tuple(x.shape) != tuple(self.x[0].shape) or tuple(y.shape) != tuple(self.y[0].shape):
+                    raise ValueError(f"chunk {tuple(x.shape)} / output {tuple(y.shape)} differ from the "
+                                     f"recorded {tuple(self.x[0].shape)} / {tuple(self.y[0].shape)}")
+                for pp in self._pps:
+                    pp.cur, pp.fresh = r % 2, False
+                stages = self._stages(r, x, y)
+                ga = capture(lambda: [st() for st in stages[:self.split]], self.device)
+                gb = capture(lambda: [st() for st in stages[self.split:]], self.device)
+                while len(self._bound) >= self.MAX_BOUND:
+                    old = self._bound.pop(next(iter(self._bound)))
+                    old[0].close()
+                    old[1].close()
+                self._bound[self._key(r, x, y)] = (ga, gb)
+        finally:
+            for pp, (cur, fresh) in zip(self._pps, saved):
+                pp.cur, pp.fresh = cur, fresh
 
     def _materialize(self):
         """Recorded calls name both buffers of every ping-pong: a fresh cache
@@ -936,6 +975,12 @@ class PipelineGraph:
         r = self.next
         if self._pps and r % 2 != self._pps[0].cur:
             r = (r + 1) % self.period    # eager chunks moved the parity
+        if self.bind:
+            rs = [(r + i) % self.period for i in range(len(chunks))]
+            todo = [(ri, x, y) for ri, x, y in zip(rs, chunks, outs)
+                    if self._key(ri, x, y) not in self._bound]
+            if todo:
+                self._record_bound(todo)
         main = torch.cuda.current_stream(self.device)
         sa, sb = self.streams
         self._ev_fork.record(main)
@@ -943,17 +988,19 @@ class PipelineGraph:
         sb.wait_event(self._ev_fork)
         for i, (x, y) in enumerate(zip(chunks, outs)):
             k = r % self.slots
-            ga, gb = self.graphs[r]
+            ga, gb = self._bound[self._key(r, x, y)] if self.bind else self.graphs[r]
             with torch.cuda.stream(sa):
                 if i >= self.slots:
                     sa.wait_event(self._ev_b[k])   # B is done with this buffer set
-                self.x[k].copy_(x)
+                if not self.bind:
+                    self.x[k].copy_(x)
                 ga.launch(sa)
                 self._ev_a[k].record(sa)
             with torch.cuda.stream(sb):
                 sb.wait_event(self._ev_a[k])
                 gb.launch(sb)
-                y.copy_(self.y[k])
+                if not self.bind:
+                    y.copy_(self.y[k])
                 self._ev_b[k].record(sb)
             x.record_stream(sa)
             y.record_stream(sb)
@@ -966,9 +1013,10 @@ class PipelineGraph:
             main.wait_event(ev)
 
     def close(self):
-        for ga, gb in self.graphs:
+        for ga, gb in self.graphs + list(self._bound.values()):
             ga.close()
             gb.close()
+        self._bound.clear()
 
 
 def tile_origins(size: int, tile: int, stride: int) -> List[int]:
