@@ -204,7 +204,7 @@ def test_direct_route_stride_pad_dilation(k, stride, pad, dil, dtype):
 @pytest.mark.parametrize("cin,cout,t,h,w", [(64, 64, 2, 11, 19),      # one launch, no split
                                              (384, 384, 1, 30, 52),   # split-K + reduce
                                              (96, 96, 3, 5, 9),
-                                             (96, 96, 4, 120, 160)])  # persistent workgroups
+                                             (96, 96, 4, 120, 160)])  # whole K, 16x16 tiles: two workgroups per CU
 def test_conv3x3x3_batch2_with_cache_out(cin, cout, t, h, w):
     """N = 2: both batch items through the MFMA route in one call, each with
     its own cache frames in and out."""
