@@ -473,6 +473,34 @@ int wvc_causal_conv3d_e4m3_fwd(const wvc_conv3d_desc *d, const void *x, float x_
                                void *y, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * wvc_causal_conv3d_e4m3_norm_fwd: the 8-bit conv followed by the RMS norm +
+ * SiLU of the layer it feeds, that result stored as codes ([P1] 10.2-10.4
+ * for the conv, the norm and the block; the 8-bit counterpart of
+ * wvc_causal_conv3d_norm_fwd):
+ *   y = round_bf16(x_scale * w_scale[co] * S + b[co] + residual)
+ *   q = E4M3(silu(rmsnorm(y; gamma, beta, eps)) / q_scale)
+ * y is bit for bit what wvc_causal_conv3d_e4m3_fwd stores, q what
+ * wvc_rmsnorm_silu_e4m3 stores for that y at scale q_scale.  Arguments as for
+ * wvc_causal_conv3d_e4m3_fwd (d->upsample_in included), plus gamma [C_out]
+ * bf16, beta [C_out] bf16 or NULL, eps > 0, q_scale (finite, > 0) and q
+ * [N, C_out, t_out, h_out, w_out] channels-last bytes; y may be NULL when
+ * only q is wanted.  On a split-K plan the split sums go straight into the
+ * norm kernel (split order, the scales, the bias, the residual, one bf16
+ * rounding, stored as y when given), so the reduce and the norm are one
+ * kernel.  C_out % 8 == 0 and C_out <= 2048 (WVC_ERR_UNSUPPORTED otherwise).
+ * Workspace: wvc_causal_conv3d_e4m3_norm_workspace_bytes(d) bytes (the conv's
+ * workspace plus room for y), contents on entry irrelevant.  Written buffers
+ * (y, q, cache_out, workspace) may not overlap the others (WVC_ERR_ALIAS).
+ */
+int wvc_causal_conv3d_e4m3_norm_fwd(const wvc_conv3d_desc *d, const void *x, float x_scale,
+                                    const void *cache_in, void *cache_out, const void *weight,
+                                    const float *w_scale, const void *bias, const void *residual,
+                                    void *y, const void *gamma, const void *beta, float eps,
+                                    float q_scale, void *q, void *workspace,
+                                    size_t workspace_bytes, void *stream);
+size_t wvc_causal_conv3d_e4m3_norm_workspace_bytes(const wvc_conv3d_desc *d);
+
+/*
  * The residual block of wvc_resblock_fwd on the 8-bit path (identity
  * shortcut, C_in == C_out): norm1 + SiLU stored as codes at activation scale
  * s1, the 8-bit conv1 (bf16 result), norm2 + SiLU as codes at s2, the 8-bit

@@ -447,3 +447,42 @@ def test_decoder_stack_e4m3_pipeline_equals_sequential_bitwise():
     torch.cuda.synchronize()
     for a, b in zip(seq, outs):
         assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("cin,cout,t,h,w,up,with_res", [
+    (384, 384, 1, 30, 52, 0, True),     # split K: the reduce runs inside the norm
+    (48, 384, 1, 30, 52, 0, False),     # the decoder's conv_in shape
+    (64, 64, 2, 6, 9, 0, True),         # whole K: conv, then the norm kernel
+    (384, 384, 1, 30, 52, 2, False),    # conv_up: read through the upsample, 60x104 out
+])
+def test_e4m3_conv_norm_equals_composition(cin, cout, t, h, w, up, with_res):
+    """wvc_causal_conv3d_e4m3_norm_fwd stores y bitwise as the 8-bit conv does
+    and q bitwise as the norm-to-codes kernel does on that y ([P1] 10.2-10.4:
+    a conv feeding the next layer's norm + SiLU)."""
+    seed = cin + h + up
+    xs, qs = 6.0 / 448, 5.0 / 448
+    x = I.quantize(I.normal((1, cin, t, h, w), seed, "x"), "bf16")
+    cache = I.quantize(I.normal((1, cin, 2, h, w), seed, "cache"), "bf16")
+    wt = to_dev(I.conv_weight(cout, cin, (3, 3, 3), seed, "w", "bf16"))
+    b = to_dev(I.conv_bias(cout, seed, "b", "bf16"))
+    g = to_dev(I.norm_gamma(cout, seed, "g", "bf16"))
+    be = to_dev(I.norm_beta(cout, seed, "be", "bf16"))
+    ho, wo = (2 * h, 2 * w) if up else (h, w)
+    res = to_dev(I.quantize(I.normal((1, cout, t, ho, wo), seed, "r"), "bf16")) if with_res else None
+    print(f"[case] 8-bit conv + norm {cin}->{cout} t={t} {h}x{w} up={up} res={with_res}", flush=True)
+    xq, cq = L.wvc_quantize_e4m3(to_dev(x), xs), L.wvc_quantize_e4m3(to_dev(cache), xs)
+    wq, wsc = L.wvc_quantize_rows_e4m3(wt)
+    pk = L.wvc_conv3d_pack_weights(wq)
+    c1, c2 = L.empty_cl((1, cin, 2, h, w), torch.uint8), L.empty_cl((1, cin, 2, h, w), torch.uint8)
+    y1 = L.empty_cl((1, cout, t, ho, wo))
+    q1 = L.wvc_causal_conv3d_e4m3_norm_fwd(xq, xs, wq, wsc, g, qs, b, be, 1e-12, cq, c1, res, y1,
+                                           packed_weight=pk, upsample_in=up)
+    y2 = L.wvc_causal_conv3d_e4m3_fwd(xq, xs, wq, wsc, b, cq, c2, res, packed_weight=pk, upsample_in=up)
+    q2 = L.wvc_rmsnorm_silu_e4m3(y2, g, qs, beta=be)
+    assert torch.equal(y1, y2), "y differs from the 8-bit conv's"
+    assert torch.equal(q1, q2), "q differs from the norm-to-codes kernel on the conv's y"
+    assert torch.equal(c1, c2)
+    # without y (only the codes wanted) the codes are the same
+    q3 = L.wvc_causal_conv3d_e4m3_norm_fwd(xq, xs, wq, wsc, g, qs, b, be, 1e-12, cq, None, res, None,
+                                           packed_weight=pk, upsample_in=up)
+    assert torch.equal(q3, q1)

@@ -42,6 +42,7 @@ EXPORTED = (
     "wvc_rmsnorm_silu_e4m3", "wvc_rmsnorm_silu_conv3d_fwd", "wvc_resblock_e4m3_fwd",
     "wvc_resblock_e4m3_workspace_bytes", "wvc_conv3d_kernel_name", "wvc_causal_conv3d_fwd_noalloc",
     "wvc_causal_conv3d_norm_fwd", "wvc_causal_conv3d_norm_workspace_bytes",
+    "wvc_causal_conv3d_e4m3_norm_fwd", "wvc_causal_conv3d_e4m3_norm_workspace_bytes",
 )
 
 
@@ -172,6 +173,11 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.wvc_rmsnorm_silu_conv3d_fwd.restype = i
     lib.wvc_causal_conv3d_e4m3_fwd.argtypes = [dptr, vp, f, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.wvc_causal_conv3d_e4m3_fwd.restype = i
+    lib.wvc_causal_conv3d_e4m3_norm_fwd.argtypes = [dptr, vp, f, vp, vp, vp, vp, vp, vp, vp, vp, vp, f,
+                                                    f, vp, vp, sz, vp]
+    lib.wvc_causal_conv3d_e4m3_norm_fwd.restype = i
+    lib.wvc_causal_conv3d_e4m3_norm_workspace_bytes.argtypes = [dptr]
+    lib.wvc_causal_conv3d_e4m3_norm_workspace_bytes.restype = sz
     i64 = ctypes.c_int64
     lib.wvc_quantize_e4m3.argtypes = [vp, i, i64, f, vp, vp]
     lib.wvc_quantize_e4m3.restype = i
@@ -689,6 +695,73 @@ def wvc_causal_conv3d_e4m3_fwd(x: torch.Tensor, x_scale: float, weight: torch.Te
                                            _ptr(residual), _ptr(y), _ptr(workspace), ws_bytes,
                                            _stream(x)))
     return y
+
+
+def wvc_causal_conv3d_e4m3_norm_workspace_bytes(d: ConvDesc) -> int:
+    v = load().wvc_causal_conv3d_e4m3_norm_workspace_bytes(ctypes.byref(d))
+    if v == ctypes.c_size_t(-1).value:
+        raise WvcError(WVC_ERR_ARG, load().wvc_last_error().decode())
+    return v
+
+
+def wvc_causal_conv3d_e4m3_norm_fwd(x: torch.Tensor, x_scale: float, weight: torch.Tensor,
+                                    w_scale: torch.Tensor, gamma: torch.Tensor, q_scale: float,
+                                    bias: Optional[torch.Tensor] = None,
+                                    beta: Optional[torch.Tensor] = None, eps: float = 1e-12,
+                                    cache_in: Optional[torch.Tensor] = None,
+                                    cache_out: Optional[torch.Tensor] = None,
+                                    residual: Optional[torch.Tensor] = None,
+                                    y: Optional[torch.Tensor] = None,
+                                    q: Optional[torch.Tensor] = None,
+                                    workspace: Optional[torch.Tensor] = None,
+                                    packed_weight: Optional[torch.Tensor] = None,
+                                    upsample_in: int = 0, cu_limit: int = 0) -> torch.Tensor:
+    """The 8-bit conv, then the RMS norm + SiLU of the layer it feeds stored as
+    E4M3 codes at ``q_scale`` (see wvc_causal_conv3d_e4m3_norm_fwd in
+    include/wvc.h): y = the 8-bit conv's bf16 output (stored only when ``y``
+    is given), q = codes of SiLU(norm(y)).  Operands as for
+    wvc_causal_conv3d_e4m3_fwd.  Returns q (uint8, allocated if not given)."""
+    lib = load()
+    _need_cl(x, "x")
+    _need_cl(weight, "weight")
+    if x.dtype != torch.uint8 or weight.dtype != torch.uint8 or w_scale.dtype != torch.float32:
+        raise TypeError("x and weight must be uint8 (E4M3 codes), w_scale float32")
+    n, c, t, h, w = x.shape
+    if upsample_in not in (0, 2):
+        raise WvcError(WVC_ERR_ARG, f"upsample_in {upsample_in} must be 0 or 2")
+    up = 2 if upsample_in == 2 else 1
+    co = weight.shape[0]
+    out_shape = (n, co, t, h * up, w * up)
+    _need_exact(weight, "weight", (co, c) + tuple(weight.shape[2:]), torch.uint8, x.device)
+    for name, v in (("bias", bias), ("gamma", gamma), ("beta", beta)):
+        _need_exact(v, name, (co,), torch.bfloat16, x.device)
+    if gamma is None:
+        raise ValueError("gamma must be given")
+    _need_exact(w_scale, "w_scale", (co,), torch.float32, x.device)
+    for name, cc in (("cache_in", cache_in), ("cache_out", cache_out)):
+        _need_exact(cc, name, (n, c, 2, h, w), torch.uint8, x.device)
+    for name, tt in (("residual", residual), ("y", y)):
+        _need_exact(tt, name, out_shape, torch.bfloat16, x.device)
+    _need_exact(q, "q", out_shape, torch.uint8, x.device)
+    layout = WVC_WEIGHT_STANDARD if packed_weight is None else WVC_WEIGHT_PACKED
+    d = conv_desc(tuple(x.shape), tuple(weight.shape), WVC_E4M3, weight_layout=layout,
+                  upsample_in=upsample_in, cu_limit=cu_limit)
+    if packed_weight is not None:
+        _need_bytes(packed_weight, "packed_weight",
+                    wvc_conv3d_packed_weight_bytes(tuple(weight.shape), torch.uint8), x.device)
+    wsrc = weight if packed_weight is None else packed_weight
+    if q is None:
+        q = empty_cl(out_shape, torch.uint8, x.device)
+    if workspace is None:
+        workspace = torch.empty(max(1, wvc_causal_conv3d_e4m3_norm_workspace_bytes(d)), dtype=torch.uint8,
+                                device=x.device)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(lib.wvc_causal_conv3d_e4m3_norm_fwd(ctypes.byref(d), _ptr(x), float(x_scale), _ptr(cache_in),
+                                                _ptr(cache_out), _ptr(wsrc), _ptr(w_scale), _ptr(bias),
+                                                _ptr(residual), _ptr(y), _ptr(gamma), _ptr(beta),
+                                                float(eps), float(q_scale), _ptr(q), _ptr(workspace),
+                                                ws_bytes, _stream(x)))
+    return q
 
 
 def wvc_quantize_e4m3(x: torch.Tensor, scale: float, q: Optional[torch.Tensor] = None) -> torch.Tensor:

@@ -623,6 +623,80 @@ int wvc_causal_conv3d_norm_fwd(const wvc_conv3d_desc *d, const void *x, const vo
                     eps, 1, s);
 }
 
+// ---- the 8-bit conv, then the next layer's RMS norm + SiLU stored as codes
+//
+// Workspace: [the conv's workspace][room for y when the caller passes none].
+size_t wvc_causal_conv3d_e4m3_norm_workspace_bytes(const wvc_conv3d_desc *d) {
+    if (d && d->dtype != WVC_E4M3) {
+        fail(WVC_ERR_ARG, "the 8-bit conv + norm call needs d->dtype == WVC_E4M3");
+        return (size_t)-1;
+    }
+    return wvc_causal_conv3d_norm_workspace_bytes(d);
+}
+
+int wvc_causal_conv3d_e4m3_norm_fwd(const wvc_conv3d_desc *d, const void *x, float x_scale,
+                                    const void *cache_in, void *cache_out, const void *weight,
+                                    const float *w_scale, const void *bias, const void *residual,
+                                    void *y, const void *gamma, const void *beta, float eps,
+                                    float q_scale, void *q, void *workspace,
+                                    size_t workspace_bytes, void *stream) {
+    if (!d) return fail(WVC_ERR_ARG, "conv descriptor is NULL");
+    if (d->dtype != WVC_E4M3)
+        return fail(WVC_ERR_ARG, "wvc_causal_conv3d_e4m3_norm_fwd needs d->dtype == WVC_E4M3");
+    ConvPlan pl;
+    int rc = plan_conv(d, &pl, /*count=*/false);  // conv_fwd below counts the call
+    if (rc) return rc;
+    if (d->c_out % 8 != 0 || d->c_out > 2048) {
+        g_rejected++;
+        return fail(WVC_ERR_UNSUPPORTED, "the conv + norm call needs C_out %% 8 == 0 and C_out <= 2048");
+    }
+    if (!gamma) return fail(WVC_ERR_ARG, "gamma is NULL");
+    if (!(eps > 0.f)) return fail(WVC_ERR_ARG, "eps must be > 0");
+    if (!(q_scale > 0.f) || !(q_scale < INFINITY))
+        return fail(WVC_ERR_ARG, "q_scale must be finite and > 0");
+    const long positions = (long)d->n * pl.call.to * pl.call.ho * pl.call.wo;
+    if (d->t > 0 && positions > 0 && !q) return fail(WVC_ERR_ARG, "q is NULL");
+    if (!ws_ok(workspace, workspace_bytes)) return fail(WVC_ERR_ARG, "workspace is NULL but workspace_bytes > 0");
+    const size_t conv_need = align256(route_ws_bytes(pl, d->weight_layout == WVC_WEIGHT_PACKED));
+    const size_t need = conv_need + align256(pl.y_bytes);
+    if (workspace_bytes < need)
+        return fail(WVC_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, need);
+    const Buf bufs[] = {
+        {x, pl.x_bytes, false, "x"},
+        {cache_in, pl.cache_bytes, false, "cache_in"},
+        {cache_out, pl.cache_bytes, true, "cache_out"},
+        {residual, pl.y_bytes, false, "residual"},
+        {y, pl.y_bytes, true, "y"},
+        {gamma, (size_t)d->c_out * 2, false, "gamma"},
+        {beta, (size_t)d->c_out * 2, false, "beta"},
+        {q, pl.y_bytes / 2, true, "q"},
+        {workspace, workspace_bytes, true, "workspace"},
+    };
+    rc = check_aliasing(bufs, 9);
+    if (rc) return rc;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    char *ws = static_cast<char *>(workspace);
+    void *yy = y ? y : ws + conv_need;
+    // On a split-K plan the reduce is fused into the norm, as in the bf16
+    // call; the norm kernel also applies the two scales in the reduce's order.
+    const bool fuse = aligned(gamma, 16) && aligned(beta, 16) && aligned(bias, 16) &&
+                      aligned(residual, 16) && aligned(y, 16) && aligned(w_scale, 16) &&
+                      aligned(q, 16);
+    wvc::ConvPartials parts;
+    if ((rc = conv_fwd(d, x, cache_in, cache_out, weight, bias, residual, yy, ws, conv_need, s,
+                       fuse ? &parts : nullptr, x_scale, w_scale)))
+        return rc;
+    if (parts.S > 1)
+        return hip_status(wvc::launch_rmsnorm_silu_from_partials(parts, bias, gamma, beta, q, positions,
+                                                                 d->c_out, eps, 1, s, w_scale, x_scale,
+                                                                 1.f / q_scale, residual, y),
+                          "norm launch");
+    if (d->t == 0 || positions == 0) return WVC_OK;
+    return hip_status(wvc::launch_rmsnorm_silu_e4m3(yy, gamma, beta, q, positions, d->c_out, eps, 1,
+                                                    1.f / q_scale, s),
+                      "norm launch");
+}
+
 size_t wvc_conv3d_packed_weight_bytes(const wvc_conv3d_desc *d) {
     ConvPlan pl;
     if (plan_conv(d, &pl, /*count=*/false)) return (size_t)-1;

@@ -402,6 +402,30 @@ class CausalConv3dE4M3:
         self.cache.flip()
         return y
 
+    def norm_into(self, x: torch.Tensor, y: Optional[torch.Tensor], gamma: torch.Tensor,
+                  beta: Optional[torch.Tensor], eps: float, q_scale: float, q: torch.Tensor) -> torch.Tensor:
+        """This conv on the chunk, then the next layer's norm + SiLU stored as
+        codes at ``q_scale`` in ``q`` (one wvc_causal_conv3d_e4m3_norm_fwd
+        call after the quantiser); the conv's bf16 output goes to ``y`` when
+        given (a block's shortcut needs it)."""
+        n, c, _, h, w = x.shape
+        if not _fits(self.cache, (n, c, CACHE_T, h, w)):
+            self.start(n, h, w)
+        qx = _cached_buf(self.bufs, "q", x.shape, x.new_empty(0, dtype=torch.uint8))
+        L.wvc_quantize_e4m3(x, self.scale, q=qx)
+        d = L.conv_desc(tuple(qx.shape), tuple(self.wq.shape), L.WVC_E4M3, weight_layout=L.WVC_WEIGHT_PACKED,
+                        upsample_in=self.upsample_in, cu_limit=self.cu_limit)
+        need = L.wvc_causal_conv3d_e4m3_norm_workspace_bytes(d)
+        ws = self.__dict__.get("ws_n")
+        if ws is None or ws.numel() < need:
+            ws = self.ws_n = torch.empty(max(1, need), dtype=torch.uint8, device=x.device)
+        L.wvc_causal_conv3d_e4m3_norm_fwd(qx, self.scale, self.wq, self.wsc, gamma, q_scale, self.bias, beta,
+                                          eps, self.cache.cin, self.cache.cout, None, y, q, workspace=ws,
+                                          packed_weight=self.packed, upsample_in=self.upsample_in,
+                                          cu_limit=self.cu_limit)
+        self.cache.flip()
+        return q
+
     def stages(self, x: torch.Tensor, y: torch.Tensor, buf) -> List[Callable[[], object]]:
         return [lambda: self(x, y=y)]
 
@@ -471,6 +495,54 @@ class ResBlockE4M3:
                                     self.c2.cin, self.c2.cout, y=y, eps=self.eps, workspace=self.ws,
                                     packed=True, cu_limit=self.cu_limit)
         self.c1.flip()
+        self.c2.flip()
+        return y
+
+    def _ws8(self, name: str, q: torch.Tensor, norm: bool) -> torch.Tensor:
+        d = L.conv_desc(tuple(q.shape), tuple(self.w["w1"][0].shape), L.WVC_E4M3,
+                        weight_layout=L.WVC_WEIGHT_PACKED, cu_limit=self.cu_limit)
+        need = (L.wvc_causal_conv3d_e4m3_norm_workspace_bytes(d) if norm
+                else L.wvc_causal_conv3d_workspace_bytes(d))
+        ws = self.__dict__.get(name)
+        if ws is None or ws.numel() < need:
+            ws = torch.empty(max(1, need), dtype=torch.uint8, device=q.device)
+            setattr(self, name, ws)
+        return ws
+
+    def front_from_q1(self, q1: torch.Tensor, q2: torch.Tensor) -> torch.Tensor:
+        """The block's first half from the codes of norm1(x) (at scale s1),
+        which the previous layer's conv + norm call wrote: conv1, then norm2 +
+        SiLU as codes at s2 in ``q2``; the calls the block call makes after
+        its norm1."""
+        n, c, _, h, w = q1.shape
+        if not _fits(self.c1, (n, c, CACHE_T, h, w)):
+            self.start(n, h, w)
+        wq, sc, pk = self.w["w1"]
+        L.wvc_causal_conv3d_e4m3_norm_fwd(q1, self.s1, wq, sc, self.p["gamma2"], self.s2, self.p.get("b1"),
+                                          self.p.get("beta2"), self.eps, self.c1.cin, self.c1.cout, q=q2,
+                                          workspace=self._ws8("ws_f8", q1, True), packed_weight=pk,
+                                          cu_limit=self.cu_limit)
+        self.c1.flip()
+        return q2
+
+    def back(self, q2: torch.Tensor, x: torch.Tensor, y: torch.Tensor) -> torch.Tensor:
+        """conv2 on the codes of norm2 plus the shortcut x into y."""
+        wq, sc, pk = self.w["w2"]
+        L.wvc_causal_conv3d_e4m3_fwd(q2, self.s2, wq, sc, self.p.get("b2"), self.c2.cin, self.c2.cout, x, y,
+                                     workspace=self._ws8("ws_b8", q2, False), packed_weight=pk,
+                                     cu_limit=self.cu_limit)
+        self.c2.flip()
+        return y
+
+    def back_norm(self, q2: torch.Tensor, x: torch.Tensor, y: torch.Tensor, gamma: torch.Tensor,
+                  beta: Optional[torch.Tensor], eps: float, q_scale: float, q_next: torch.Tensor) -> torch.Tensor:
+        """conv2 plus the shortcut into y, and the next block's norm1 + SiLU
+        as codes at ``q_scale`` in ``q_next``, in one conv + norm call."""
+        wq, sc, pk = self.w["w2"]
+        L.wvc_causal_conv3d_e4m3_norm_fwd(q2, self.s2, wq, sc, gamma, q_scale, self.p.get("b2"), beta, eps,
+                                          self.c2.cin, self.c2.cout, x, y, q_next,
+                                          workspace=self._ws8("ws_bn8", q2, True), packed_weight=pk,
+                                          cu_limit=self.cu_limit)
         self.c2.flip()
         return y
 
@@ -661,15 +733,60 @@ class DecoderStackE4M3(DecoderStack):
     ``scales["up"]``; each residual block k quantises its two norm outputs at
     ``scales["rb"][k]`` = (s1, s2).  Activations between layers stay bf16."""
 
-    # conv_in, rb0 and rb1 on one stream; conv_up (reading through the
-    # upsample) and the rest on the other
-    PIPELINE_SPLIT = 3
-
     def __init__(self, p: Dict, scales: Dict, eps: float = 1e-12):
         self.conv_in = CausalConv3dE4M3(p["w_in"], p.get("b_in"), scales["in"])
         self.rbs = [ResBlockE4M3(p[f"rb{k}"], *scales["rb"][k], eps) for k in range(4)]
         self.conv_up = CausalConv3dE4M3(p["w_up"], p.get("b_up"), scales["up"], upsample_in=2)
         Stream.__init__(self, [self.conv_in] + self.rbs[:2] + [self.conv_up] + self.rbs[2:])
+
+    @property
+    def PIPELINE_SPLIT(self) -> int:
+        """The pipeline's cut, before conv_up: conv_in and the first two
+        blocks on one stream (5 fused stages, or 3 layers), the rest on the
+        other."""
+        return 5 if self._fusable() else 3
+
+    def _fusable(self) -> bool:
+        """Every conv that feeds a norm can compute that norm too
+        (wvc_causal_conv3d_e4m3_norm_fwd): the channel count fits the call."""
+        c = self.conv_in.weight.shape[0]
+        return c % 8 == 0 and c <= 2048 and all(isinstance(rb, ResBlockE4M3) for rb in self.rbs)
+
+    def stages(self, x: torch.Tensor, out: torch.Tensor, buf) -> List[Callable[[], object]]:
+        """The chunk as 10 stages.  Each conv that feeds a block's norm
+        computes that norm too and stores it as the block's codes: conv_in
+        and conv_up the next block's norm1, a block's conv1 its norm2, the
+        first block's conv2 (plus its input) the second block's norm1.  The
+        calls are those of the layer-by-layer composition with the norm folded
+        into the conv before it, bitwise the same codes and outputs, with four
+        norm kernels and four split-K reduces fewer per chunk."""
+        if not self._fusable():
+            return self._stages_layerwise(x, out, buf)
+        n, _, t, h, w = x.shape
+        c = self.conv_in.weight.shape[0]
+        lo, hi = (n, c, t, h, w), (n, c, t, 2 * h, 2 * w)
+        u8 = x.new_empty(0, dtype=torch.uint8)
+        a_in, a0, a1 = buf("in", lo, x), buf("rb0", lo, x), buf("rb1", lo, x)
+        a_up, a2 = buf("conv_up", hi, x), buf("rb2", hi, x)
+        q1 = [buf(f"rb{k}.q1", lo if k < 2 else hi, u8) for k in range(4)]
+        q2 = [buf(f"rb{k}.q2", lo if k < 2 else hi, u8) for k in range(4)]
+        rb = self.rbs
+
+        def norm1(k):
+            return rb[k].p["gamma1"], rb[k].p.get("beta1"), rb[k].eps, rb[k].s1
+
+        return [
+            lambda: self.conv_in.norm_into(x, a_in, *norm1(0), q1[0]),
+            lambda: rb[0].front_from_q1(q1[0], q2[0]),
+            lambda: rb[0].back_norm(q2[0], a_in, a0, *norm1(1), q1[1]),
+            lambda: rb[1].front_from_q1(q1[1], q2[1]),
+            lambda: rb[1].back(q2[1], a0, a1),
+            lambda: self.conv_up.norm_into(a1, a_up, *norm1(2), q1[2]),
+            lambda: rb[2].front_from_q1(q1[2], q2[2]),
+            lambda: rb[2].back_norm(q2[2], a_up, a2, *norm1(3), q1[3]),
+            lambda: rb[3].front_from_q1(q1[3], q2[3]),
+            lambda: rb[3].back(q2[3], a2, out),
+        ]
 
 
 def run_chunked(layer, x: torch.Tensor, sizes: Sequence[int]) -> torch.Tensor:
