@@ -686,3 +686,20 @@ def test_cu_limit_plans_the_split_for_fewer_cus(lib):
     assert L.wvc_resblock_workspace_bytes(rd) > 0
     rd.cu_limit = -1
     assert lib.wvc_resblock_workspace_bytes(ctypes.byref(rd)) == ctypes.c_size_t(-1).value
+
+
+def test_e4m3_conv_norm_workspace_query():
+    """The 8-bit conv + norm call's workspace is the 8-bit conv's plus room
+    for y, and the query refuses a bf16 descriptor (no GPU needed)."""
+    from video_vae_causal_amd import _lib as L
+    d8 = L.conv_desc((1, 384, 1, 30, 52), (384, 384, 3, 3, 3), L.WVC_E4M3,
+                     weight_layout=L.WVC_WEIGHT_PACKED)
+    conv = L.wvc_causal_conv3d_workspace_bytes(d8)
+    y_bytes = 1 * 384 * 1 * 30 * 52 * 2
+
+    def align(v):
+        return (v + 255) // 256 * 256
+    assert L.wvc_causal_conv3d_e4m3_norm_workspace_bytes(d8) == align(conv) + align(y_bytes)
+    dbf = L.conv_desc((1, 384, 1, 30, 52), (384, 384, 3, 3, 3), L.WVC_BF16)
+    with pytest.raises(L.WvcError, match="WVC_E4M3"):
+        L.wvc_causal_conv3d_e4m3_norm_workspace_bytes(dbf)
