@@ -162,3 +162,38 @@ def test_graph_pipeline_refuses_to_be_recorded(monkeypatch):
     finally:
         monkeypatch.undo()
         pipe.close()
+
+
+def test_bound_recordings_are_released_oldest_first():
+    """With room for 4 bound pairs: passes over two different output tensors
+    release each other's recordings and re-record them, every pass bitwise
+    the sequential loop; a pass needing more pairs than the limit is refused
+    before it records or replays anything."""
+    d = inputs.decoder_inputs(seed=18, shape=(1, 16, 3, 6, 9), width=64)
+    pd, lat = stack_dev(d["p"]), to_dev(d["latent"])
+    t = lat.shape[2]
+    print("[case] bound recordings, release and refusal", flush=True)
+    seq = stream.DecoderStack(pd).run(lat, chunk_frames=1)
+    stack = stream.DecoderStack(pd)
+    frames = [cl(lat[:, :, i:i + 1]) for i in range(t)]
+    pipe = stream.PipelineGraph(stack, frames[0].shape, bind=True)
+    pipe.MAX_BOUND = 4
+    try:
+        outs_ab = [L.empty_cl(seq.shape) for _ in range(2)]
+        for rep in range(4):
+            out = outs_ab[rep % 2]
+            out.fill_(float("nan"))
+            stack.reset()
+            pipe.run(frames, [out[:, :, i:i + 1] for i in range(t)])
+            torch.cuda.synchronize()
+            assert torch.equal(out, seq), f"pass {rep} differs from the sequential loop"
+            assert len(pipe._bound) <= 4
+        long_lat = to_dev(inputs.decoder_inputs(seed=18, shape=(1, 16, 5, 6, 9), width=64)["latent"])
+        long_frames = [cl(long_lat[:, :, i:i + 1]) for i in range(5)]
+        long_out = L.empty_cl((1, 64, 5, 12, 18))
+        stack.reset()
+        with pytest.raises(ValueError, match="exceeds"):
+            pipe.run(long_frames, [long_out[:, :, i:i + 1] for i in range(5)])
+    finally:
+        torch.cuda.synchronize()
+        pipe.close()

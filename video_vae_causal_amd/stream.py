@@ -993,7 +993,8 @@ class PipelineGraph:
     recorded the first time a (recording, chunk tensor, output tensor)
     combination is run and replayed after that.  This suits callers that pass
     the same tensors on every pass (a preallocated sequence); at most
-    ``MAX_BOUND`` pairs are kept, the oldest released first.  The tensors
+    ``MAX_BOUND`` pairs are kept, the oldest released first (never one the
+    pass in hand needs; a pass needing more is refused).  The tensors
     must stay unchanged and alive until the pass has finished."""
 
     MAX_BOUND = 512
@@ -1049,9 +1050,13 @@ class PipelineGraph:
         return (r, x.data_ptr(), tuple(x.shape), x.stride(), x.dtype,
                 y.data_ptr(), tuple(y.shape), y.stride(), y.dtype)
 
-    def _record_bound(self, todo: List[tuple]):
+    def _record_bound(self, todo: List[tuple], needed: set):
         """Record the graph pairs of (r, chunk, output) triples that have none:
-        each at cache parity r % 2, then the stack's cache state as it was."""
+        each at cache parity r % 2, then the stack's cache state as it was.
+        Pairs the pass in hand needs (``needed``) are never released."""
+        if len(needed) > self.MAX_BOUND:
+            raise ValueError(f"a pass over {len(needed)} distinct chunk/output pairs exceeds the "
+                             f"{self.MAX_BOUND} bound recordings kept; use bind=False")
         saved = [(pp.cur, pp.fresh) for pp in self._pps]
         try:
             for r, x, y in todo:
@@ -1064,7 +1069,8 @@ class PipelineGraph:
                 ga = capture(lambda: [st() for st in stages[:self.split]], self.device)
                 gb = capture(lambda: [st() for st in stages[self.split:]], self.device)
                 while len(self._bound) >= self.MAX_BOUND:
-                    old = self._bound.pop(next(iter(self._bound)))
+                    oldest = next(k for k in self._bound if k not in needed)
+                    old = self._bound.pop(oldest)
                     old[0].close()
                     old[1].close()
                 self._bound[self._key(r, x, y)] = (ga, gb)
@@ -1099,10 +1105,10 @@ class PipelineGraph:
             r = (r + 1) % self.period    # eager chunks moved the parity
         if self.bind:
             rs = [(r + i) % self.period for i in range(len(chunks))]
-            todo = [(ri, x, y) for ri, x, y in zip(rs, chunks, outs)
-                    if self._key(ri, x, y) not in self._bound]
+            keys = [self._key(ri, x, y) for ri, x, y in zip(rs, chunks, outs)]
+            todo = [(ri, x, y) for ri, x, y, k in zip(rs, chunks, outs, keys) if k not in self._bound]
             if todo:
-                self._record_bound(todo)
+                self._record_bound(todo, set(keys))
         main = torch.cuda.current_stream(self.device)
         sa, sb = self.streams
         self._ev_fork.record(main)
